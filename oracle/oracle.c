@@ -1,0 +1,192 @@
+/*
+ * oracle.c -- plain, slow CPU reference for the skinny decode projection.
+ *
+ * TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT: only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg load it.  It shares no
+ * code with the HIP library.  Declarations and the page citations are in
+ * oracle.h; each definition below restates the reading it follows.
+ *
+ * Deliberately naive: one loop nest per definition, double accumulation,
+ * no blocking, no threads, no reordering.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <string.h>
+
+double oracle_bf16_to_f64(uint16_t bits)
+{
+    /* bfloat16 is the upper 16 bits of an IEEE-754 binary32: widen by
+     * appending 16 zero fraction bits, then read the binary32 exactly. */
+    uint32_t word = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &word, sizeof f);
+    return (double)f;
+}
+
+uint16_t oracle_f64_to_bf16(double v)
+{
+    const uint16_t sign = signbit(v) ? 0x8000u : 0x0000u;
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7FC0u);
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7F80u);
+
+    /* a lies in [2^E, 2^(E+1)).  bf16 keeps 8 significant bits, so the
+     * spacing of representable values there is 2^(E-7); below the smallest
+     * normal 2^-126 the spacing is fixed at 2^-133 (subnormals). */
+    int e2;
+    (void)frexp(a, &e2); /* a = f * 2^e2 with f in [0.5, 1), so E = e2 - 1 */
+    int E = e2 - 1;
+    int spacing_exp = (E < -126) ? -133 : E - 7;
+    double q = ldexp(1.0, spacing_exp);
+
+    /* a / q is exact (power-of-two scale).  Round it to an integer, ties
+     * to even. */
+    double n = a / q;
+    double lo = floor(n);
+    double frac = n - lo;
+    double r = lo;
+    if (frac > 0.5 || (frac == 0.5 && fmod(lo, 2.0) != 0.0))
+        r = lo + 1.0;
+    double rounded = r * q; /* exact: r <= 256 */
+
+    /* Largest finite bf16 is (2 - 2^-7) * 2^127; anything that rounded
+     * beyond it overflows to infinity. */
+    if (rounded > ldexp(2.0 - ldexp(1.0, -7), 127))
+        return (uint16_t)(sign | 0x7F80u);
+
+    float f = (float)rounded; /* exact: a bf16 value is a binary32 value */
+    uint32_t word;
+    memcpy(&word, &f, sizeof word);
+    return (uint16_t)(sign | (word >> 16));
+}
+
+void oracle_encode_bf16(int64_t n, const double* v, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f64_to_bf16(v[i]);
+}
+
+void oracle_projection(int64_t M, int64_t N, int64_t K,
+                       const uint16_t* x, const uint16_t* W,
+                       double* y, double* abs_scale)
+{
+    /* y = x W^T with W stored [N, K]: output (m, n) is the dot product of
+     * row m of x with row n of W, summed over k in ascending order. */
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0;
+            double abs_sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double term = oracle_bf16_to_f64(x[m * K + k]) *
+                              oracle_bf16_to_f64(W[n * K + k]);
+                sum += term;
+                abs_sum += fabs(term);
+            }
+            y[m * N + n] = sum;
+            if (abs_scale)
+                abs_scale[m * N + n] = abs_sum;
+        }
+    }
+}
+
+void oracle_splitk_partials(int64_t M, int64_t N, int64_t K, int64_t S,
+                            const uint16_t* x, const uint16_t* W, double* P)
+{
+    /* The accumulation dimension is cut into S contiguous chunks of
+     * ceil(K/S) (the last one shorter, or empty).  Each chunk is an
+     * ordinary projection over its k range. */
+    int64_t chunk = (K + S - 1) / S;
+    for (int64_t s = 0; s < S; ++s) {
+        int64_t k_begin = s * chunk;
+        int64_t k_end = (s + 1) * chunk < K ? (s + 1) * chunk : K;
+        for (int64_t m = 0; m < M; ++m) {
+            for (int64_t n = 0; n < N; ++n) {
+                double sum = 0.0;
+                for (int64_t k = k_begin; k < k_end; ++k)
+                    sum += oracle_bf16_to_f64(x[m * K + k]) *
+                           oracle_bf16_to_f64(W[n * K + k]);
+                P[(s * M + m) * N + n] = sum;
+            }
+        }
+    }
+}
+
+void oracle_splitk_sum(int64_t S, int64_t MN, const double* P, double* y)
+{
+    for (int64_t i = 0; i < MN; ++i) {
+        double sum = 0.0;
+        for (int64_t s = 0; s < S; ++s)
+            sum += P[s * MN + i];
+        y[i] = sum;
+    }
+}
+
+void oracle_residual(int64_t MN, const uint16_t* r, const double* y, double* out)
+{
+    for (int64_t i = 0; i < MN; ++i)
+        out[i] = oracle_bf16_to_f64(r[i]) + y[i];
+}
+
+int64_t oracle_moe_table(int64_t T, int64_t topk, int64_t E, const int32_t* ids,
+                         int32_t* counts, int32_t* offsets, int32_t* sorted_pairs)
+{
+    int64_t pairs = T * topk;
+    int64_t invalid = 0;
+
+    for (int64_t e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (int64_t p = 0; p < pairs; ++p) {
+        int32_t e = ids[p];
+        if (e < 0 || e >= E)
+            ++invalid;
+        else
+            ++counts[e];
+    }
+
+    offsets[0] = 0;
+    for (int64_t e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + counts[e];
+
+    /* Expert by expert in ascending order, list that expert's pairs in
+     * ascending p starting at its offset; unused tail slots stay -1. */
+    for (int64_t p = 0; p < pairs; ++p)
+        sorted_pairs[p] = -1;
+    for (int64_t e = 0; e < E; ++e) {
+        int32_t slot = offsets[e];
+        for (int64_t p = 0; p < pairs; ++p) {
+            if (ids[p] == e)
+                sorted_pairs[slot++] = (int32_t)p;
+        }
+    }
+    return invalid;
+}
+
+void oracle_grouped(int64_t T, int64_t topk, int64_t E, int64_t N, int64_t K,
+                    const uint16_t* x, const uint16_t* W, const int32_t* ids,
+                    double* out, double* abs_scale)
+{
+    /* Each (token, choice) pair is a one-row projection against its chosen
+     * expert's weight; a pair with an out-of-range id yields zeros. */
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t j = 0; j < topk; ++j) {
+            int64_t p = t * topk + j;
+            int32_t e = ids[p];
+            double* o = out + p * N;
+            double* a = abs_scale ? abs_scale + p * N : 0;
+            if (e < 0 || e >= E) {
+                for (int64_t n = 0; n < N; ++n) {
+                    o[n] = 0.0;
+                    if (a)
+                        a[n] = 0.0;
+                }
+                continue;
+            }
+            oracle_projection(1, N, K, x + t * K, W + (int64_t)e * N * K, o, a);
+        }
+    }
+}

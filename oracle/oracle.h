@@ -1,0 +1,93 @@
+/*
+ * oracle.h -- plain, slow CPU reference for the skinny decode projection.
+ *
+ * TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.  Only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg may load this library.
+ * It shares no code, header, table or helper with the HIP library, and
+ * neither side includes or links the other.
+ *
+ * What it computes follows the method pages:
+ *   - "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly"
+ *     (deepnotes summary page), Method details §1 "Tune shapes for the
+ *     workload": decode-time input projections, a small-matrix kernel at
+ *     batch 1-2 and a split-K kernel (accumulation dimension split over more
+ *     workers) at larger batch;
+ *   - same page, Method details §2: the output projection fused with the
+ *     attention residual add;
+ *   - same page, Method details §3, and the French translation ("Hyper
+ *     optimisation de Kimi K3 dans vLLM"), Partie 2 §4: routed experts, where
+ *     expert selection decides which weights are read.
+ * The pages give the operation, not its arithmetic; every reading taken where
+ * they are silent is listed in the design doc and restated at each function.
+ *
+ * Conventions
+ *   bf16 values travel as raw 16-bit patterns (uint16_t), the upper half of
+ *   an IEEE-754 binary32.  All arithmetic is IEEE double, summed in the
+ *   order each comment states.  Matrices are dense and row-major:
+ *   x [M,K], W [N,K] (the nn.Linear weight layout), y [M,N], so y = x W^T.
+ *
+ * Parity pins: every function here is pinned by CPU tests against
+ * something other than itself (exact rational brute force, closed forms,
+ * library routines, invariants).  The oracle has no function whose parity is
+ * unpinned.
+ */
+#ifndef SKINNY_GEMM_ORACLE_H
+#define SKINNY_GEMM_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exact value of a bf16 bit pattern (sign, 8-bit exponent, 7-bit fraction). */
+double oracle_bf16_to_f64(uint16_t bits);
+
+/* Round a double to the nearest bf16, ties to even; overflow gives +-inf,
+ * NaN gives a quiet NaN with the input's sign. */
+uint16_t oracle_f64_to_bf16(double v);
+
+/* Element-wise oracle_f64_to_bf16 over n values. */
+void oracle_encode_bf16(int64_t n, const double* v, uint16_t* out);
+
+/* Projection y[m,n] = sum_k x[m,k] * W[n,k], k ascending, in double.
+ * abs_scale[m,n] = sum_k |x[m,k] * W[n,k]| (the tolerance scale); may be NULL. */
+void oracle_projection(int64_t M, int64_t N, int64_t K,
+                       const uint16_t* x, const uint16_t* W,
+                       double* y, double* abs_scale);
+
+/* Split-K partial sums.  Chunk s covers k in [s*c, min(K, (s+1)*c)) with
+ * c = ceil(K/S); P[s,m,n] = sum over that chunk, k ascending.  A chunk that
+ * starts at or past K is empty and holds 0. */
+void oracle_splitk_partials(int64_t M, int64_t N, int64_t K, int64_t S,
+                            const uint16_t* x, const uint16_t* W, double* P);
+
+/* y[i] = P[0,i] + P[1,i] + ... + P[S-1,i], s ascending, over MN elements. */
+void oracle_splitk_sum(int64_t S, int64_t MN, const double* P, double* y);
+
+/* Residual add out[i] = r[i] + y[i] (r a bf16 pattern), in double. */
+void oracle_residual(int64_t MN, const uint16_t* r, const double* y, double* out);
+
+/* Per-expert token table for topk_ids [T, topk] over E experts.
+ * Pair p = t*topk + j routes token t's j-th choice to expert ids[p].
+ * counts[e]       = number of pairs with ids[p] == e                [E]
+ * offsets[e]      = counts[0] + ... + counts[e-1], offsets[0] = 0   [E+1]
+ * sorted_pairs    = the valid pairs grouped by expert, ascending e, and
+ *                   ascending p inside each expert's segment; slots from
+ *                   offsets[E] to T*topk-1 hold -1                  [T*topk]
+ * Returns the number of pairs whose id lies outside [0, E). */
+int64_t oracle_moe_table(int64_t T, int64_t topk, int64_t E, const int32_t* ids,
+                         int32_t* counts, int32_t* offsets, int32_t* sorted_pairs);
+
+/* Grouped projection over routed experts: W is [E, N, K].
+ * out[t,j,n] = sum_k x[t,k] * W[ids[t*topk+j], n, k] for a valid id, and 0
+ * for an id outside [0, E).  abs_scale likewise (may be NULL). */
+void oracle_grouped(int64_t T, int64_t topk, int64_t E, int64_t N, int64_t K,
+                    const uint16_t* x, const uint16_t* W, const int32_t* ids,
+                    double* out, double* abs_scale);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,516 @@
+"""Pins for the CPU oracle: each check compares the oracle with something that
+is not the oracle -- hand-derived fixtures (tests/golden), exact rational
+brute force, closed forms, invariants, and library routines (torch's bf16
+conversions, numpy's float64/int64 matmul, Python's sorted()).
+
+Every check takes an ``oracle.Oracle`` and raises AssertionError on a
+mismatch.  The same checks run against deliberately broken copies of the
+oracle source (tests/test_oracle_mutations.py), which shows that a plausible
+slip in the oracle -- a transposed operand, a dropped term, a wrong rounding
+tie, an unstable ordering -- fails at least one of them.
+"""
+from __future__ import annotations
+
+import ast
+import bisect
+import math
+import operator
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+# ---------------------------------------------------------------- helpers
+
+
+def exact(expr: str) -> Fraction:
+    """Parse an exact arithmetic expression ('1+3*2^-8', '201/64') into a Fraction."""
+    ops = {ast.Add: operator.add, ast.Sub: operator.sub, ast.Mult: operator.mul,
+           ast.Div: operator.truediv, ast.Pow: operator.pow}
+
+    def ev(node):
+        if isinstance(node, ast.Expression):
+            return ev(node.body)
+        if isinstance(node, ast.Constant) and isinstance(node.value, int):
+            return Fraction(node.value)
+        if isinstance(node, ast.UnaryOp) and isinstance(node.op, ast.USub):
+            return -ev(node.operand)
+        if isinstance(node, ast.BinOp) and type(node.op) in ops:
+            left, right = ev(node.left), ev(node.right)
+            if isinstance(node.op, ast.Pow):
+                assert right.denominator == 1
+                return left ** int(right)
+            return ops[type(node.op)](left, right)
+        raise ValueError(f"unsupported expression {expr!r}")
+
+    return ev(ast.parse(expr.replace("^", "**"), mode="eval"))
+
+
+def read_table(name: str):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def torch_bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Library decode: torch's bfloat16 -> float64 conversion."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def torch_f32_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """Library rounding: torch's float32 -> bfloat16 conversion (round to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bits_of(values, dtype=torch.float32) -> np.ndarray:
+    """bf16 bit patterns of exactly representable values (library conversion)."""
+    t = torch.tensor(values, dtype=dtype).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def random_bf16(shape, seed: int, sigma: float = 1.0) -> np.ndarray:
+    g = torch.Generator().manual_seed(seed)
+    v = torch.randn(tuple(shape), generator=g) * sigma
+    return v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def random_int_bf16(shape, seed: int, lo: int = -4, hi: int = 4) -> np.ndarray:
+    g = torch.Generator().manual_seed(seed)
+    v = torch.randint(lo, hi + 1, tuple(shape), generator=g).to(torch.float32)
+    return v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def values(bits: np.ndarray) -> np.ndarray:
+    return torch_bf16_to_f64(bits)
+
+
+_FINITE_POS = None
+
+
+def finite_positive_bf16():
+    """(exact Fraction values, bit patterns) of all finite bf16 >= 0, ascending."""
+    global _FINITE_POS
+    if _FINITE_POS is None:
+        bits = np.arange(0, 0x7F80, dtype=np.uint16)  # 0 .. largest finite
+        vals = torch_bf16_to_f64(bits)
+        _FINITE_POS = ([Fraction(float(v)) for v in vals], [int(b) for b in bits])
+    return _FINITE_POS
+
+
+def brute_round_bf16(v: Fraction) -> int:
+    """Nearest bf16 to an exact value, ties to the even pattern, by search over all values."""
+    if v < 0:
+        return 0x8000 | brute_round_bf16(-v)
+    vals, bits = finite_positive_bf16()
+    top = vals[-1]
+    # beyond the midpoint of the largest finite value and 2^128: infinity (the even neighbour)
+    if v >= (top + Fraction(2) ** 128) / 2:
+        return 0x7F80
+    i = bisect.bisect_left(vals, v)
+    if i < len(vals) and vals[i] == v:
+        return bits[i]
+    lo, hi = i - 1, i
+    if hi >= len(vals):
+        return bits[lo]
+    d_lo, d_hi = v - vals[lo], vals[hi] - v
+    if d_lo < d_hi:
+        return bits[lo]
+    if d_hi < d_lo:
+        return bits[hi]
+    return bits[lo] if bits[lo] % 2 == 0 else bits[hi]
+
+
+def exact_projection(x_bits, W_bits):
+    """Exact rational y and A by brute force over Fractions."""
+    xv = [[Fraction(float(v)) for v in row] for row in values(x_bits)]
+    wv = [[Fraction(float(v)) for v in row] for row in values(W_bits)]
+    M, N = len(xv), len(wv)
+    y = [[sum((a * b for a, b in zip(xv[m], wv[n])), Fraction(0)) for n in range(N)] for m in range(M)]
+    A = [[sum((abs(a * b) for a, b in zip(xv[m], wv[n])), Fraction(0)) for n in range(N)]
+         for m in range(M)]
+    return y, A
+
+
+def close(a, b, scale, rel, what):
+    a, b, scale = np.asarray(a), np.asarray(b), np.asarray(scale)
+    err = np.abs(a - b)
+    bound = rel * scale
+    bad = err > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} mismatches, worst err {err.max():.3e}"
+
+
+# ---------------------------------------------------------------- bf16
+
+
+def check_bf16_decode_golden(o):
+    for row in read_table("bf16_decode.txt"):
+        bits, expect = int(row[0], 16), row[1]
+        got = o.c.oracle_bf16_to_f64(bits)
+        if expect == "nan":
+            assert math.isnan(got), (hex(bits), got)
+        elif expect in ("inf", "-inf"):
+            assert got == float(expect), (hex(bits), got)
+        elif expect == "-0":
+            assert got == 0.0 and math.copysign(1.0, got) < 0, (hex(bits), got)
+        else:
+            assert Fraction(got) == exact(expect), (hex(bits), got, expect)
+
+
+def check_bf16_decode_all_patterns(o):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = o.bf16_to_f64(bits)
+    ref = torch_bf16_to_f64(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), "NaN patterns differ"
+    assert np.array_equal(got[~nan], ref[~nan]), "decoded values differ from torch"
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan])), "signs differ"
+
+
+def check_bf16_round_golden(o):
+    for row in read_table("bf16_round.txt"):
+        expr, expect = row[0], int(row[1], 16)
+        if expr == "-0":
+            v = -0.0
+        else:
+            q = exact(expr)
+            v = float(q)
+            if Fraction(v) != q:  # not a double: only used far from a tie
+                assert expr == "314159/100000" or expr == "1/10", expr
+        got = o.c.oracle_f64_to_bf16(v)
+        assert got == expect, (expr, hex(got), hex(expect))
+
+
+def check_bf16_round_vs_torch(o):
+    rng = np.random.default_rng(11)
+    # random binary32 patterns over the whole range, plus exact ties (low half 0x8000)
+    words = rng.integers(0, 2 ** 32, size=20000, dtype=np.uint64).astype(np.uint32)
+    ties = (words & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    near = (words & np.uint32(0xFFFF0000)) | rng.integers(0x7FF0, 0x8010, size=words.size).astype(np.uint32)
+    allw = np.concatenate([words, ties, near])
+    f = allw.view(np.float32)
+    f = f[np.isfinite(f)]
+    ref = torch_f32_to_bf16_bits(f)
+    got = o.encode_bf16(f.astype(np.float64))
+    bad = got != ref
+    assert not bad.any(), f"{int(bad.sum())} float32 roundings differ from torch, e.g. {f[bad][:3]}"
+
+
+def check_bf16_round_bruteforce(o):
+    rng = np.random.default_rng(12)
+    cases = []
+    # doubles between bf16 neighbours (not float32 values), across normal and subnormal ranges
+    for e in list(range(-140, -120)) + list(range(-20, 20)) + list(range(120, 128)):
+        for _ in range(12):
+            cases.append(float(np.ldexp(rng.uniform(1.0, 2.0), e)) * (1 if rng.random() < 0.5 else -1))
+    # exact midpoints and midpoints +- one double ulp
+    vals, _ = finite_positive_bf16()
+    idx = rng.integers(1, len(vals) - 1, size=300)
+    for i in idx:
+        mid = (vals[i] + vals[i + 1]) / 2
+        m = float(mid)
+        cases += [m, math.nextafter(m, math.inf), math.nextafter(m, -math.inf)]
+    for v in cases:
+        got = o.c.oracle_f64_to_bf16(v)
+        want = brute_round_bf16(Fraction(v))
+        assert got == want, (v, hex(got), hex(want))
+
+
+# ---------------------------------------------------------------- projection
+
+
+def _golden_projection():
+    rows = {}
+    for row in read_table("projection_worked.txt"):
+        rows.setdefault(row[0].rstrip(":"), []).append([exact(t) for t in row[1:]])
+    return rows
+
+
+def check_projection_golden(o):
+    g = _golden_projection()
+    x = bits_of([[float(v) for v in r] for r in g["x"]])
+    W = bits_of([[float(v) for v in r] for r in g["W"]])
+    y, A = o.projection(x, W)
+    assert np.array_equal(y, np.array([[float(v) for v in r] for r in g["y"]])), y
+    assert np.array_equal(A, np.array([[float(v) for v in r] for r in g["A"]])), A
+    r = bits_of([[float(v) for v in row] for row in g["r"]])
+    out = o.residual(r, y)
+    assert np.array_equal(out, np.array([[float(v) for v in row] for row in g["out"]])), out
+
+
+def check_projection_exact_small(o):
+    for seed, (M, N, K) in enumerate([(1, 1, 1), (1, 3, 8), (2, 5, 16), (3, 4, 13), (2, 2, 7)]):
+        x = random_bf16((M, K), 100 + seed)
+        W = random_bf16((N, K), 200 + seed, sigma=0.02)
+        y, A = o.projection(x, W)
+        ye, Ae = exact_projection(x, W)
+        for m in range(M):
+            for n in range(N):
+                # k-ascending double accumulation: error at most K * 2^-53 * A
+                bound = Fraction(K) * Fraction(2) ** -52 * Ae[m][n]
+                assert abs(Fraction(y[m, n]) - ye[m][n]) <= bound, (M, N, K, m, n)
+                assert abs(Fraction(A[m, n]) - Ae[m][n]) <= bound, (M, N, K, m, n)
+
+
+def check_projection_integer(o):
+    for seed, (M, N, K) in enumerate([(1, 7, 64), (2, 9, 300), (5, 3, 1000)]):
+        x = random_int_bf16((M, K), 300 + seed)
+        W = random_int_bf16((N, K), 400 + seed)
+        y, A = o.projection(x, W)
+        xi = values(x).astype(np.int64)
+        wi = values(W).astype(np.int64)
+        assert np.array_equal(y, (xi @ wi.T).astype(np.float64)), (M, N, K)
+        assert np.array_equal(A, (np.abs(xi) @ np.abs(wi).T).astype(np.float64)), (M, N, K)
+
+
+def check_projection_vs_numpy(o):
+    x = random_bf16((3, 520), 501)
+    W = random_bf16((37, 520), 502, sigma=0.02)
+    y, A = o.projection(x, W)
+    xv, wv = values(x), values(W)
+    close(y, xv @ wv.T, A, 1e-12, "y vs numpy")
+    close(A, np.abs(xv) @ np.abs(wv).T, A, 1e-12, "A vs numpy")
+
+
+def check_projection_layout(o):
+    M, N, K = 2, 5, 9
+    W = random_bf16((N, K), 601)
+    for k in (0, 4, K - 1):
+        x = np.zeros((M, K), dtype=np.uint16)
+        x[:, k] = 0x3F80  # 1.0
+        y = o.projection(x, W, with_scale=False)
+        for m in range(M):
+            assert np.array_equal(y[m], values(W)[:, k]), f"one-hot x picks column {k} of W"
+    x = random_bf16((M, K), 602)
+    picks = [3, 0, 8, 8, 5]
+    Wsel = np.zeros((N, K), dtype=np.uint16)
+    for n, k in enumerate(picks):
+        Wsel[n, k] = 0x3F80
+    y = o.projection(x, Wsel, with_scale=False)
+    for n, k in enumerate(picks):
+        assert np.array_equal(y[:, n], values(x)[:, k]), f"one-hot row {n} of W picks column {k} of x"
+
+
+def check_projection_identity_zero(o):
+    K = 11
+    x = random_bf16((3, K), 701)
+    eye = np.zeros((K, K), dtype=np.uint16)
+    np.fill_diagonal(eye, 0x3F80)
+    y = o.projection(x, eye, with_scale=False)
+    assert np.array_equal(y, values(x)), "W = I gives y = x"
+    zeros = np.zeros((4, K), dtype=np.uint16)
+    assert not o.projection(x, zeros, with_scale=False).any(), "W = 0 gives 0"
+    assert not o.projection(np.zeros((2, K), dtype=np.uint16), random_bf16((4, K), 702),
+                            with_scale=False).any(), "x = 0 gives 0"
+
+
+def check_projection_linearity(o):
+    M, N, K = 2, 6, 64
+    x = random_bf16((M, K), 801)
+    W = random_bf16((N, K), 802, sigma=0.02)
+    y, A = o.projection(x, W)
+    for a in (-3, 5):
+        xs = bits_of((values(x) * 2.0 ** a).astype(np.float32))  # exact power-of-two scaling
+        ys = o.projection(xs, W, with_scale=False)
+        assert np.array_equal(ys, y * 2.0 ** a), f"y(2^{a} x) = 2^{a} y(x)"
+    mask = (np.arange(K) % 3 == 0)
+    x1 = np.where(mask, x, 0).astype(np.uint16)
+    x2 = np.where(mask, 0, x).astype(np.uint16)
+    y1 = o.projection(x1, W, with_scale=False)
+    y2 = o.projection(x2, W, with_scale=False)
+    close(y1 + y2, y, A, 1e-13, "additivity over disjoint supports")
+
+
+def check_projection_rows(o):
+    M, N, K = 8, 5, 40
+    x = random_bf16((M, K), 901)
+    W = random_bf16((N, K), 902, sigma=0.02)
+    y = o.projection(x, W, with_scale=False)
+    perm = np.array([3, 7, 0, 1, 6, 2, 5, 4])
+    yp = o.projection(x[perm], W, with_scale=False)
+    assert np.array_equal(yp, y[perm]), "permuting x rows permutes y rows"
+    y4 = o.projection(x[:4], W, with_scale=False)
+    assert np.array_equal(y4, y[:4]), "a prefix of x gives the prefix of y"
+    Wp = np.array([4, 2, 0, 1, 3])
+    yw = o.projection(x, W[Wp], with_scale=False)
+    assert np.array_equal(yw, y[:, Wp]), "permuting W rows permutes y columns"
+
+
+# ---------------------------------------------------------------- split-K
+
+
+def check_splitk(o):
+    for (M, N, K) in [(3, 5, 40), (1, 4, 7168), (2, 3, 9)]:
+        x = random_bf16((M, K), 1001 + K)
+        W = random_bf16((N, K), 1002 + K, sigma=0.02)
+        y, A = o.projection(x, W)
+        xv, wv = values(x), values(W)
+        for S in (1, 2, 3, 4, 7, 8, 16, 64):
+            P = o.splitk_partials(x, W, S)
+            assert P.shape == (S, M, N)
+            close(o.splitk_sum(P), y, A, 1e-12, f"sum of partials = y (K={K}, S={S})")
+            c = -(-K // S)
+            for s in range(S):
+                lo, hi = s * c, min(K, (s + 1) * c)
+                if lo >= hi:
+                    assert not P[s].any(), f"empty chunk {s} is 0"
+                    continue
+                ref = xv[:, lo:hi] @ wv[:, lo:hi].T
+                scale = np.abs(xv[:, lo:hi]) @ np.abs(wv[:, lo:hi]).T
+                close(P[s], ref, scale, 1e-12, f"chunk {s} of {S} covers [{lo},{hi})")
+
+
+def check_splitk_sum_order(o):
+    # 2^53 + 1 rounds back to 2^53 (tie to even), so s-ascending gives 0; any other order gives 1.
+    P = np.array([[[2.0 ** 53]], [[1.0]], [[-(2.0 ** 53)]]])
+    y = o.splitk_sum(P)
+    assert y[0, 0] == 0.0, f"partials must be added in ascending s, got {y[0, 0]}"
+
+
+# ---------------------------------------------------------------- residual
+
+
+def check_residual(o):
+    M, N, K = 3, 17, 33
+    x = random_bf16((M, K), 1101)
+    r = random_bf16((M, N), 1102)
+    zeros = np.zeros((N, K), dtype=np.uint16)
+    y = o.projection(x, zeros, with_scale=False)
+    out = o.residual(r, y)
+    assert np.array_equal(out, values(r)), "W = 0: residual passes r through"
+    assert np.array_equal(o.encode_bf16(out), r), "W = 0: bf16 output equals r bit for bit"
+    xi, wi, ri = random_int_bf16((M, K), 1103), random_int_bf16((N, K), 1104), random_int_bf16((M, N), 1105)
+    y = o.projection(xi, wi, with_scale=False)
+    ref = values(ri).astype(np.int64) + values(xi).astype(np.int64) @ values(wi).astype(np.int64).T
+    assert np.array_equal(o.residual(ri, y), ref.astype(np.float64)), "integer residual is exact"
+
+
+# ---------------------------------------------------------------- MoE table and grouped
+
+
+def _golden_moe():
+    cases, cur = [], None
+    for row in read_table("moe_table_worked.txt"):
+        if row[0] == "case":
+            cur = {kv.split("=")[0]: int(kv.split("=")[1]) for kv in row[1:]}
+            cases.append(cur)
+        else:
+            cur[row[0].rstrip(":")] = [int(v) for v in row[1:]]
+    return cases
+
+
+def brute_moe_table(ids: np.ndarray, E: int):
+    flat = [int(v) for v in ids.ravel()]
+    valid = [(e, p) for p, e in enumerate(flat) if 0 <= e < E]
+    order = sorted(valid)  # by expert, then by pair index
+    counts = [sum(1 for e, _ in valid if e == q) for q in range(E)]
+    offsets = [0]
+    for c in counts:
+        offsets.append(offsets[-1] + c)
+    pairs = [p for _, p in order] + [-1] * (len(flat) - len(order))
+    return counts, offsets, pairs, len(flat) - len(valid)
+
+
+def check_moe_golden(o):
+    for case in _golden_moe():
+        ids = np.array(case["ids"], dtype=np.int32).reshape(case["T"], case["topk"])
+        counts, offsets, pairs, invalid = o.moe_table(ids, case["E"])
+        assert list(counts) == case["counts"], (counts, case)
+        assert list(offsets) == case["offsets"], (offsets, case)
+        assert list(pairs) == case["sorted_pairs"], (pairs, case)
+        assert invalid == case["invalid"][0], (invalid, case)
+
+
+def check_moe_bruteforce(o):
+    rng = np.random.default_rng(13)
+    for T, topk, E in [(1, 8, 384), (16, 8, 384), (64, 8, 384), (5, 3, 4), (7, 2, 1)]:
+        ids = np.stack([rng.permutation(E)[:topk] if topk <= E else rng.integers(0, E, topk)
+                        for _ in range(T)]).astype(np.int32)
+        # duplicates within a token, and ids outside [0, E)
+        if T > 2:
+            ids[1, :] = ids[1, 0]
+            ids[2, 0] = -1
+            ids[2, -1] = E
+        counts, offsets, pairs, invalid = o.moe_table(ids, E)
+        bc, bo, bp, bi = brute_moe_table(ids, E)
+        assert list(counts) == bc and list(offsets) == bo, (T, topk, E)
+        assert list(pairs) == bp and invalid == bi, (T, topk, E)
+        # invariants
+        assert counts.sum() == T * topk - invalid
+        assert np.all(np.diff(offsets) >= 0)
+        flat = ids.ravel()
+        for e in range(E):
+            seg = pairs[offsets[e]:offsets[e + 1]]
+            assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+
+
+def check_grouped(o):
+    # exact rational brute force on a tiny routed problem, with an invalid id
+    T, topk, E, N, K = 2, 3, 4, 3, 8
+    x = random_bf16((T, K), 1201)
+    W = random_bf16((E, N, K), 1202, sigma=0.02)
+    ids = np.array([[2, 4, 3], [1, 2, -1]], dtype=np.int32)  # 4 == E and -1 are out of range
+    out, A = o.grouped(x, W, ids)
+    for t in range(T):
+        for j in range(topk):
+            e = ids[t, j]
+            if not 0 <= e < E:
+                assert not out[t, j].any() and not A[t, j].any(), "invalid id gives zeros"
+                continue
+            ye, Ae = exact_projection(x[t:t + 1], W[e])
+            for n in range(N):
+                bound = Fraction(K) * Fraction(2) ** -52 * Ae[0][n]
+                assert abs(Fraction(out[t, j, n]) - ye[0][n]) <= bound, (t, j, n)
+                assert abs(Fraction(A[t, j, n]) - Ae[0][n]) <= bound, (t, j, n)
+    # integer inputs: exact against numpy int64
+    T, topk, E, N, K = 5, 4, 9, 6, 96
+    x = random_int_bf16((T, K), 1203)
+    W = random_int_bf16((E, N, K), 1204)
+    rng = np.random.default_rng(14)
+    ids = np.stack([rng.permutation(E)[:topk] for _ in range(T)]).astype(np.int32)
+    out = o.grouped(x, W, ids, with_scale=False)
+    xi, wi = values(x).astype(np.int64), values(W).astype(np.int64)
+    for t in range(T):
+        for j in range(topk):
+            assert np.array_equal(out[t, j], (wi[ids[t, j]] @ xi[t]).astype(np.float64)), (t, j)
+
+
+ALL_CHECKS = [
+    check_bf16_decode_golden, check_bf16_decode_all_patterns, check_bf16_round_golden,
+    check_bf16_round_vs_torch, check_bf16_round_bruteforce,
+    check_projection_golden, check_projection_exact_small, check_projection_integer,
+    check_projection_vs_numpy, check_projection_layout, check_projection_identity_zero,
+    check_projection_linearity, check_projection_rows,
+    check_splitk, check_splitk_sum_order, check_residual,
+    check_moe_golden, check_moe_bruteforce, check_grouped,
+]
+
+
+def run_all(o) -> dict:
+    """Run every check; map check name -> None (passed) or the failure message."""
+    results = {}
+    for chk in ALL_CHECKS:
+        try:
+            chk(o)
+            results[chk.__name__] = None
+        except Exception as exc:  # noqa: BLE001 - report every failure kind
+            results[chk.__name__] = f"{type(exc).__name__}: {exc}"[:300]
+    return results
+
+
+if __name__ == "__main__":
+    # Runner used by the mutation tests: python oracle_pins.py <liboracle.so>
+    import json
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import oracle
+    res = run_all(oracle.Oracle(oracle.load(sys.argv[1])))
+    print(json.dumps(res))
