@@ -57,8 +57,9 @@ void oracle_projection(int64_t M, int64_t N, int64_t K,
                        double* y, double* abs_scale);
 
 /* Split-K partial sums.  Chunk s covers k in [s*c, min(K, (s+1)*c)) with
- * c = ceil(K/S); P[s,m,n] = sum over that chunk, k ascending.  A chunk that
- * starts at or past K is empty and holds 0. */
+ * c = 8*ceil(K/(8*S)) (ceil(K/S) rounded up to a multiple of 8);
+ * P[s,m,n] = sum over that chunk, k ascending.  A chunk that starts at or
+ * past K is empty and holds 0. */
 void oracle_splitk_partials(int64_t M, int64_t N, int64_t K, int64_t S,
                             const uint16_t* x, const uint16_t* W, double* P);
 

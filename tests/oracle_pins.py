@@ -348,7 +348,7 @@ def check_projection_rows(o):
 
 
 def check_splitk(o):
-    for (M, N, K) in [(3, 5, 40), (1, 4, 7168), (2, 3, 9)]:
+    for (M, N, K) in [(3, 5, 40), (1, 4, 7168), (2, 3, 9), (2, 3, 2056)]:
         x = random_bf16((M, K), 1001 + K)
         W = random_bf16((N, K), 1002 + K, sigma=0.02)
         y, A = o.projection(x, W)
@@ -357,7 +357,7 @@ def check_splitk(o):
             P = o.splitk_partials(x, W, S)
             assert P.shape == (S, M, N)
             close(o.splitk_sum(P), y, A, 1e-12, f"sum of partials = y (K={K}, S={S})")
-            c = -(-K // S)
+            c = 8 * -(-K // (8 * S))  # ceil(K/S) rounded up to a multiple of 8
             for s in range(S):
                 lo, hi = s * c, min(K, (s + 1) * c)
                 if lo >= hi:
