@@ -1,0 +1,492 @@
+#!/usr/bin/env python3
+"""Benchmark of the skinny decode projection on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
+
+Workload (one "step" = one pass of the hot path over one batch): the
+small-batch decode projection y = x W^T at M = 1 and M = 2 with K = 7168,
+N = 8192, bf16 x ~ N(0, 1) and W ~ N(0, 0.02^2), fp32 and bf16 outputs --
+one call of skinny_gemm per batch size, each planned by skinny_gemm_plan
+(the small-matrix kernel).  Weights already sit in HBM when timing starts.
+Each call reads the next copy of a ring of byte-identical weight copies
+larger than twice the 256 MB Infinity Cache, so every call streams its
+weights from HBM rather than from cache.
+
+Timing: W warmup steps, then synchronize and time exactly K steps; every
+launch is bracketed by HIP events on the stream it runs on (a short GPU
+sleep queued first lets the host enqueue ahead, so event gaps are GPU time).
+value = algorithmic bytes of the K steps / their GPU time (GB/s).
+
+The one JSON line also carries a sweep over the other workloads (batch
+M = 1..64, residual, MoE grouped), the roofline of the dominant kernel, and
+the CPU oracle timed on a bounded sample on this host.
+
+    python bench.py --summarize-pmc DIR     # post-process rocprofv3 --pmc CSVs
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import ctypes
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
+RING_MIN_BYTES = 2 * MALL_BYTES + 1
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "gemv_m1m2_k7168_n8192_traffic.txt")
+GEMV_SOURCES = ["skinny_gemm_projection_amd/csrc/rowdot.hip", "skinny_gemm_projection_amd/csrc/sg_device.h"]
+
+M_LIST, N_MAIN, K_MAIN = (1, 2), 8192, 7168
+
+
+def kernel_source_hash(paths=GEMV_SOURCES) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def proj_bytes(M, N, K, f32=True, bf16=True, residual=False) -> int:
+    """Algorithmic bytes of one projection: W once, x once, outputs (and r) once."""
+    b = N * K * 2 + M * K * 2
+    b += M * N * ((4 if f32 else 0) + (2 if bf16 else 0))
+    if residual:
+        b += M * N * 2
+    return b
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------- GPU timing
+
+
+class Launcher:
+    """Raw C-ABI calls with pointers resolved up front (keeps host overhead low)."""
+
+    def __init__(self, torch, sg):
+        self.torch = torch
+        self.sg = sg
+        self.c = sg._lib.load()
+        self.stream = torch.cuda.current_stream()
+        self.sp = self.stream.cuda_stream
+
+    def projection(self, plan, x, W, y32, y16, ws=None):
+        c, pp = self.c, ctypes.byref(plan)
+        args = (pp, x.data_ptr(), W.data_ptr(), y32.data_ptr() if y32 is not None else None,
+                y16.data_ptr() if y16 is not None else None,
+                ws.data_ptr() if ws is not None else None,
+                ws.numel() if ws is not None else 0, self.sp)
+
+        def go():
+            st = c.skinny_gemm(*args)
+            if st:
+                raise RuntimeError(self.sg.skinny_gemm_status_str(st))
+        return go
+
+    def residual(self, plan, x, W, r, o16, o32, ws=None):
+        c, pp = self.c, ctypes.byref(plan)
+        args = (pp, x.data_ptr(), W.data_ptr(), r.data_ptr(), o16.data_ptr(),
+                o32.data_ptr() if o32 is not None else None,
+                ws.data_ptr() if ws is not None else None,
+                ws.numel() if ws is not None else 0, self.sp)
+
+        def go():
+            st = c.skinny_gemm_residual(*args)
+            if st:
+                raise RuntimeError(self.sg.skinny_gemm_status_str(st))
+        return go
+
+    def grouped(self, x, W, ids, out, ws):
+        c = self.c
+        T, K = x.shape
+        E, N, _ = W.shape
+        topk = ids.shape[1]
+        args = (x.data_ptr(), T, W.data_ptr(), E, N, K, ids.data_ptr(), topk, out.data_ptr(),
+                None, None, None, ws.data_ptr(), ws.numel(), self.sp)
+
+        def go():
+            st = c.grouped_skinny_gemm(*args)
+            if st:
+                raise RuntimeError(self.sg.skinny_gemm_status_str(st))
+        return go
+
+
+def sleep_cycles_per_ms(torch) -> float:
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    torch.cuda._sleep(2_000_000)
+    e.record()
+    torch.cuda.synchronize()
+    return 2_000_000 / max(s.elapsed_time(e), 1e-3)
+
+
+def timed_calls(torch, calls, reps, cycles_per_ms, warmup=3):
+    """Run calls[i % len(calls)] reps times with an event pair around each call.
+
+    Returns (per-call GPU ms list, total GPU ms from first to last event)."""
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda._sleep(int(cycles_per_ms * min(50.0, 0.02 * reps + 0.5)))
+    evs[0].record()
+    for i in range(reps):
+        calls[i % len(calls)]()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
+    return per, evs[0].elapsed_time(evs[reps])
+
+
+def ring_copies(torch, W, min_bytes=RING_MIN_BYTES):
+    nbytes = W.numel() * W.element_size()
+    count = max(1, math.ceil(min_bytes / nbytes))
+    return [W] + [W.clone() for _ in range(count - 1)]
+
+
+# --------------------------------------------------------------------------- workloads
+
+
+def main_workload(torch, sg, si, L, steps, warmup, cyc):
+    dev = "cuda"
+    x = {M: si.normal_bf16((M, K_MAIN), 1.0, si.seed_for(2, si.TAG_X) + M, dev) for M in M_LIST}
+    W0 = si.normal_bf16((N_MAIN, K_MAIN), 0.02, si.seed_for(2, si.TAG_W), dev)
+    ring = ring_copies(torch, W0)
+    plans = {M: sg.skinny_gemm_plan(M, N_MAIN, K_MAIN) for M in M_LIST}
+    y32 = {M: torch.empty((M, N_MAIN), device=dev) for M in M_LIST}
+    y16 = {M: torch.empty((M, N_MAIN), device=dev, dtype=torch.bfloat16) for M in M_LIST}
+    # one launch closure per (batch size, ring copy); step i uses copies 2i, 2i+1 (mod ring)
+    R = len(ring)
+    calls = {(M, r): L.projection(plans[M], x[M], ring[r], y32[M], y16[M]) for M in M_LIST
+             for r in range(R)}
+    seq = []
+    for i in range(steps):
+        for j, M in enumerate(M_LIST):
+            seq.append((M, (len(M_LIST) * i + j) % R))
+
+    for i in range(warmup):
+        for j, M in enumerate(M_LIST):
+            calls[(M, (len(M_LIST) * i + j) % R)]()
+    torch.cuda.synchronize()
+    sg.skinny_gemm_reset_counters()
+
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)]
+    torch.cuda.synchronize()                       # barrier (one rank) + synchronize
+    t0 = time.perf_counter()
+    torch.cuda._sleep(int(cyc * min(200.0, 0.03 * len(seq) + 1.0)))
+    evs[0].record()
+    for i, key in enumerate(seq):
+        calls[key]()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(seq))]
+    total_ms = evs[0].elapsed_time(evs[-1])
+    counters = sg.skinny_gemm_get_counters()
+    assert counters[sg.SG_KERNEL_GEMV] == len(seq), counters
+
+    bytes_per = {M: proj_bytes(M, N_MAIN, K_MAIN) for M in M_LIST}
+    step_bytes = sum(bytes_per.values())
+    per_m = {M: [] for M in M_LIST}
+    for (M, _), ms in zip(seq, per):
+        per_m[M].append(ms)
+    us = {M: 1e3 * sum(v) / len(v) for M, v in per_m.items()}
+    launch_bytes = sum(bytes_per[M] for M, _ in seq)
+    achieved = launch_bytes / (sum(per) * 1e-3) / 1e9
+    ms_per_step = total_ms / steps
+    return {
+        "plans": {M: plans[M].as_dict() for M in M_LIST},
+        "ring_copies": R, "ring_bytes": R * W0.numel() * 2,
+        "ms_per_step": ms_per_step, "wall_ms_per_step": 1e3 * wall / steps,
+        "value": step_bytes * steps / (total_ms * 1e-3) / 1e9,
+        "us_per_projection": {str(M): round(us[M], 3) for M in M_LIST},
+        "gbs_per_batch": {str(M): round(bytes_per[M] / (us[M] * 1e-6) / 1e9, 1) for M in M_LIST},
+        "achieved": achieved, "avg_launch_us": 1e3 * sum(per) / len(per),
+        "bytes_per_launch": launch_bytes / len(seq),
+        "inputs": (x, W0),
+    }
+
+
+def sweep(torch, sg, si, L, cyc, reps=40):
+    dev = "cuda"
+    rows = []
+
+    def record(name, M, N, K, plan_desc, per, nbytes):
+        us = 1e3 * sum(per) / len(per)
+        rows.append({"workload": name, "M": M, "N": N, "K": K, "plan": plan_desc,
+                     "us": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "pct_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)})
+
+    def plan_desc(p):
+        return f"{sg.KERNEL_NAMES[p.kernel]} S={p.split_k}"
+
+    # single decode projection M=1, K=N=1024 (launch-bound)
+    N = K = 1024
+    x = si.normal_bf16((1, K), 0.02, si.seed_for(1, si.TAG_X), dev)
+    ring = ring_copies(torch, si.normal_bf16((N, K), 0.02, si.seed_for(1, si.TAG_W), dev))
+    p = sg.skinny_gemm_plan(1, N, K)
+    y = torch.empty((1, N), device=dev)
+    per, _ = timed_calls(torch, [L.projection(p, x, w, y, None) for w in ring], 512, cyc)
+    record("single 1024x1024", 1, N, K, plan_desc(p), per, proj_bytes(1, N, K, bf16=False))
+    del ring
+
+    # small batch M in {1,2}, K=7168, N=8192, fp32 + bf16 out
+    N, K = 8192, 7168
+    ring = ring_copies(torch, si.normal_bf16((N, K), 0.02, si.seed_for(2, si.TAG_W), dev))
+    for M in (1, 2):
+        x = si.normal_bf16((M, K), 1.0, si.seed_for(2, si.TAG_X) + M, dev)
+        p = sg.skinny_gemm_plan(M, N, K)
+        y32, y16 = torch.empty((M, N), device=dev), torch.empty((M, N), device=dev, dtype=torch.bfloat16)
+        per, _ = timed_calls(torch, [L.projection(p, x, w, y32, y16) for w in ring], reps, cyc)
+        record("small-batch 8192x7168", M, N, K, plan_desc(p), per, proj_bytes(M, N, K))
+    del ring
+
+    # split-K sweep M in {4..64}, K=7168, N=4096, fp32 out
+    N, K = 4096, 7168
+    ring = ring_copies(torch, si.normal_bf16((N, K), 0.02, si.seed_for(3, si.TAG_W), dev))
+    for M in (3, 4, 8, 12, 16, 32, 48, 64):
+        x = si.normal_bf16((M, K), 1.0, si.seed_for(3, si.TAG_X) + M, dev)
+        p = sg.skinny_gemm_plan(M, N, K)
+        y32 = torch.empty((M, N), device=dev)
+        ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        per, _ = timed_calls(torch, [L.projection(p, x, w, y32, None, ws) for w in ring], reps, cyc)
+        record("split-K 4096x7168", M, N, K, plan_desc(p), per, proj_bytes(M, N, K, bf16=False))
+    del ring
+
+    # fused output projection + residual, K=8192, N=7168, bf16 out
+    N, K = 7168, 8192
+    ring = ring_copies(torch, si.normal_bf16((N, K), 0.02, si.seed_for(4, si.TAG_W), dev))
+    for M in (1, 8, 64):
+        x = si.normal_bf16((M, K), 1.0, si.seed_for(4, si.TAG_X) + M, dev)
+        r = si.normal_bf16((M, N), 1.0, si.seed_for(4, si.TAG_R) + M, dev)
+        p = sg.skinny_gemm_plan(M, N, K)
+        o16 = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
+        ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        per, _ = timed_calls(torch, [L.residual(p, x, w, r, o16, None, ws) for w in ring], reps, cyc)
+        record("residual 7168x8192", M, N, K, plan_desc(p), per,
+               proj_bytes(M, N, K, f32=False, residual=True))
+    del ring
+    torch.cuda.empty_cache()
+
+    # MoE grouped: E=384 experts of N=2048 x K=7168, 8 distinct experts per token,
+    # a ring of 8 routing tables per batch size
+    E, N, K, topk = 384, 2048, 7168, 8
+    W = si.normal_bf16((E, N, K), 0.02, si.seed_for(5, si.TAG_W) + 100, dev)
+    for T in (1, 16, 64):
+        x = si.normal_bf16((T, K), 1.0, si.seed_for(5, si.TAG_X) + T, dev)
+        tables = [si.routing_table(T, E, topk, si.seed_for(5, si.TAG_ROUTING) + 10 * i + 1000 * T)
+                  for i in range(8)]
+        out = torch.empty((T, topk, N), device=dev)
+        ws = torch.empty(sg.grouped_skinny_gemm_workspace(T, E, topk, N, K), dtype=torch.uint8,
+                         device=dev)
+        ids_dev = [t.to(dev) for t in tables]
+        per, _ = timed_calls(torch, [L.grouped(x, W, ids, out, ws) for ids in ids_dev],
+                             max(8, reps // 4), cyc)
+        distinct = [len(set(t.view(-1).tolist())) for t in tables]
+        nbytes = []
+        for i in range(len(per)):
+            d = distinct[i % len(tables)]
+            nbytes.append(d * N * K * 2 + T * K * 2 + T * topk * N * 4 + T * topk * 4)
+        us = 1e3 * sum(per) / len(per)
+        gbs = sum(nbytes) / (sum(per) * 1e-3) / 1e9
+        rows.append({"workload": "MoE grouped E=384 2048x7168 top8", "M": T, "N": N, "K": K,
+                     "plan": "moe_table+grouped", "us": round(us, 3), "GBps": round(gbs, 1),
+                     "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                     "distinct_experts_mean": round(sum(distinct) / len(distinct), 1)})
+    del W
+    torch.cuda.empty_cache()
+    return rows
+
+
+# --------------------------------------------------------------------------- CPU baseline
+
+
+def cpu_baseline(si, inputs, budget_s=10.0):
+    """The fp64 oracle, as it stands, on full projections of the same workload."""
+    import oracle
+    o = oracle.Oracle()
+    x, W0 = inputs
+    Wb = si.bits(W0)
+    xb = {M: si.bits(x[M]) for M in M_LIST}
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        for M in M_LIST:
+            o.projection(xb[M], Wb)
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    elapsed = time.perf_counter() - t0
+    step_bytes = sum(proj_bytes(M, N_MAIN, K_MAIN) for M in M_LIST)
+    return {"value": round(step_bytes * steps / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{steps} full steps (M=1 and M=2 projections, K=7168, N=8192, fp64 "
+                      f"single-threaded C) in {elapsed:.1f} s"}
+
+
+# --------------------------------------------------------------------------- traffic (PMC)
+
+
+def read_traffic():
+    """HBM traffic per GEMV launch from the committed rocprofv3 counter summary, or None
+    when the summary is missing or the kernel source changed since it was taken."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    vals = {}
+    with open(PROFILE_TRAFFIC) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_pmc(directory: str) -> None:
+    """Turn rocprofv3 --pmc counter_collection CSVs (FETCH_SIZE, WRITE_SIZE) into the
+    per-dispatch figures committed under profiles/ (printed to stdout)."""
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    agg = {}
+    for r in rows:
+        name = r.get("Kernel_Name", r.get("Kernel-Name", ""))
+        counter = r.get("Counter_Name", r.get("Counter-Name", ""))
+        val = float(r.get("Counter_Value", r.get("Counter-Value", "0")))
+        disp = r.get("Dispatch_Id", r.get("Dispatch-Id", ""))
+        agg.setdefault((name, counter), {}).setdefault(disp, 0.0)
+        agg[(name, counter)][disp] += val
+    for (name, counter), per in sorted(agg.items()):
+        vals = list(per.values())
+        print(f"{counter} | {name[:90]} | dispatches {len(vals)} | mean KiB/dispatch "
+              f"{sum(vals) / len(vals):.1f}")
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=3):
+    """A plain element-wise copy of known size (reads nbytes, writes nbytes) for scaling
+    the FETCH_SIZE / WRITE_SIZE counters."""
+    src = torch.ones(nbytes // 4, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} element-wise copies of {nbytes} bytes")
+
+
+# --------------------------------------------------------------------------- main
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-pmc", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(collectives are out of scope), so --gpus must be 1", file=sys.stderr)
+        raise SystemExit(2)
+
+    import torch
+
+    import seeded_inputs as si
+    import skinny_gemm_projection_amd as sg
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs an MI355X (no GPU visible)")
+    torch.cuda.set_device(0)
+    L = Launcher(torch, sg)
+    cyc = sleep_cycles_per_ms(torch)
+    if args.copy_calibration:
+        copy_calibration(torch)
+
+    log(f"main workload: M in {M_LIST}, K={K_MAIN}, N={N_MAIN}, steps={args.steps}, "
+        f"warmup={args.warmup}")
+    res = main_workload(torch, sg, si, L, args.steps, args.warmup, cyc)
+    log(f"value {res['value']:.1f} GB/s, {res['ms_per_step'] * 1e3:.2f} us/step, "
+        f"per projection {res['us_per_projection']}")
+
+    sweep_rows = None
+    if not args.no_sweep:
+        log("sweep over batch sizes and workloads")
+        sweep_rows = sweep(torch, sg, si, L, cyc)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: the fp64 oracle on this host")
+        cpu = cpu_baseline(si, res["inputs"])
+
+    traffic = read_traffic()
+    line = {
+        "metric": "µs/projection and achieved HBM GB/s (% of peak) vs batch M=1..64",
+        "value": round(res["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "accumulate": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": "small-batch decode projection y = x W^T, M in {1,2}, K=7168, N=8192, "
+                        "bf16 x~N(0,1), W~N(0,0.02^2), fp32+bf16 outputs; one step = the M=1 "
+                        "and the M=2 call",
+            "M": list(M_LIST), "N": N_MAIN, "K": K_MAIN,
+            "weight_ring_copies": res["ring_copies"], "weight_ring_bytes": res["ring_bytes"],
+            "parallelism": "single GPU",
+        },
+        "us_per_projection": res["us_per_projection"],
+        "GBps_per_batch": res["gbs_per_batch"],
+        "pct_of_peak": round(100.0 * res["value"] / HBM_PEAK_GBS, 1),
+        "wall_ms_per_step": round(res["wall_ms_per_step"], 6),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "rowdot_kernel (small-matrix path, M=1 and M=2)",
+            "achieved": round(res["achieved"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(res["achieved"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": round(res["bytes_per_launch"]),
+            "avg_launch_us": round(res["avg_launch_us"], 3),
+        },
+        "cpu_baseline": cpu,
+    }
+    if sweep_rows is not None:
+        line["sweep"] = sweep_rows
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

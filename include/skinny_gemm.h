@@ -1,0 +1,178 @@
+/*
+ * skinny_gemm.h -- C ABI of libskinny_gemm.so: the batch-1..64 decode linear
+ * projection y = x W^T (+ fused residual add) and its routed-expert (MoE)
+ * variant, as hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (method pages):
+ *   [P] "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly"
+ *       (deepnotes summary page), Method details:
+ *       §1 "Tune shapes for the workload" -- decode input projections use a
+ *          dedicated small-matrix kernel at batch 1-2 and a split-K kernel
+ *          (the accumulation dimension spread over more compute units) at
+ *          larger batch; every projection is tuned to a kernel size that
+ *          fills the GPU;
+ *       §2 "Overlap computation and communication" -- the output projection
+ *          is fused with the attention residual add;
+ *       §3 "Improve MoE scheduling and overlap" -- routed experts;
+ *       §4 "Prefetching upcoming weights into cache" -- a side-stream kernel
+ *          warms the next weights while memory bandwidth is idle.
+ *   [F] "Hyper optimisation de Kimi K3 dans vLLM : aller vite et
+ *       responsablement" (French translation of the same post): Partie 1
+ *       §1-§4 (same four techniques); Partie 2 §1 (the selected path and the
+ *       way back to the standard path must be observable); Partie 2 §3 (an
+ *       early load may only read static weights); Partie 2 §4 (expert
+ *       selection decides which weights are read).
+ *   [D] "Qu'est-ce qui va suivre" on [F] and "Supplementary details" on [P]:
+ *       prefill and mixed batches fall back transparently to the standard
+ *       path; the specialised decode path covers up to 64 concurrent requests.
+ *
+ * Conventions shared by every call
+ *   - sg_bf16 is a raw bfloat16 bit pattern.  All matrices are dense,
+ *     row-major, contiguous, in device memory:
+ *       x [M, K], W [N, K] (the nn.Linear weight layout), y/out/r [M, N].
+ *     y[m, n] = sum_k x[m, k] * W[n, k], accumulated in fp32.
+ *   - Every device pointer must be 16-byte aligned and K a multiple of 8
+ *     (rows are read with 16-byte loads); otherwise SG_ERR_ALIGN.
+ *   - Ownership: the caller allocates and owns every buffer, including the
+ *     workspace.  The library allocates no device memory, holds no
+ *     per-call state beyond atomic launch counters, never synchronises the
+ *     device, and is safe to call from several host threads.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
+ *     null stream) and may be captured into a HIP graph.
+ *   - Errors: every problem the host can see is reported before anything is
+ *     launched; a launch failure returns SG_ERR_HIP.  No C++ exception
+ *     crosses this interface.  Data errors found on the device (an expert id
+ *     outside [0, E)) never trap: they are counted and their outputs zeroed.
+ */
+#ifndef SKINNY_GEMM_H
+#define SKINNY_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t sg_bf16;
+
+typedef enum {
+    SG_OK = 0,
+    SG_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    SG_ERR_SHAPE = 2,       /* a negative or over-limit size                      */
+    SG_ERR_UNSUPPORTED = 3, /* outside the decode path (M > 64): caller falls back */
+    SG_ERR_ALIGN = 4,       /* K % 8 != 0 or a pointer not 16-byte aligned       */
+    SG_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required         */
+    SG_ERR_PLAN = 6,        /* plan does not describe this problem, or bad choice */
+    SG_ERR_HIP = 7          /* the HIP runtime refused a launch                   */
+} sg_status;
+
+/* Kernel identifiers; also the indices of the launch counters. */
+typedef enum {
+    SG_KERNEL_NONE = 0,         /* empty problem (M == 0 or N == 0): nothing runs  */
+    SG_KERNEL_GEMV = 1,         /* small-matrix kernel, M <= 2                     */
+    SG_KERNEL_SPLITK_VALU = 2,  /* split-K partial, vector-ALU dot, 3 <= M <= 15   */
+    SG_KERNEL_SPLITK_MFMA = 3,  /* split-K partial, bf16 matrix cores, M >= 16     */
+    SG_KERNEL_REDUCE = 4,       /* split-K deterministic reduction + epilogue      */
+    SG_KERNEL_MOE_TABLE = 5,    /* per-expert token table                          */
+    SG_KERNEL_GROUPED = 6,      /* grouped per-expert projection                   */
+    SG_KERNEL_PREFETCH = 7      /* side-stream weight prefetch                     */
+} sg_kernel;
+
+#define SG_NUM_COUNTERS 8
+#define SG_MAX_M 64
+
+/* Launch decision for one projection shape.  Produced by skinny_gemm_plan
+ * (or skinny_gemm_plan_force) and passed unchanged to skinny_gemm /
+ * skinny_gemm_residual. */
+typedef struct {
+    int32_t M, N, K;
+    int32_t kernel;   /* sg_kernel of the main (first) launch                  */
+    int32_t split_k;  /* S: number of K chunks; 1 = no split, no reduction     */
+    int32_t k_chunk;  /* elements per K chunk: ceil(K/S) rounded up to a
+                         multiple of 8; chunk s covers [s*k_chunk,
+                         min(K, (s+1)*k_chunk))                             */
+    int32_t tile_n;   /* rows of W per workgroup work item                      */
+    int32_t grid;     /* workgroups of the main launch                          */
+    size_t workspace_bytes; /* device workspace the call needs (0 if none)      */
+} sg_plan;
+
+/* plan(M, N, K) -- pick the kernel and its tiling for y[M,N] = x[M,K] W[N,K]^T
+ * ([P] Method details §1).  0 <= M <= 64: M <= 2 small-matrix kernel; larger
+ * M split-K, on the vector ALU below 16 rows and on bf16 matrix cores from 16
+ * rows; the split factor comes from a table tuned on MI355X.  M > 64 returns
+ * SG_ERR_UNSUPPORTED (prefill-sized batches fall back, [D]); M == 0 or
+ * N == 0 gives kernel SG_KERNEL_NONE.  Host-only: touches no GPU state.
+ * Limits: 0 <= N <= 1<<20, 0 <= K <= 1<<20 (else SG_ERR_SHAPE). */
+sg_status skinny_gemm_plan(int32_t M, int32_t N, int32_t K, sg_plan* out);
+
+/* Same, but with the kernel and split factor chosen by the caller (sweeps
+ * and tests).  split_k <= 0 lets the library choose.  SG_ERR_PLAN when the
+ * kernel cannot run this shape (GEMV with M > 2, VALU split-K with M > 15 or
+ * with a chunk whose x rows do not fit its registers) or split_k > 64.  A
+ * forced split may leave trailing chunks empty; their partials are 0. */
+sg_status skinny_gemm_plan_force(int32_t M, int32_t N, int32_t K, int32_t kernel,
+                                 int32_t split_k, sg_plan* out);
+
+/* y = x W^T ([P] Method details §1).  Writes y_f32 [M,N] (fp32) and/or
+ * y_bf16 [M,N] (the same fp32 value rounded to nearest even); at least one
+ * must be non-NULL.  workspace: at least plan->workspace_bytes bytes, may be
+ * NULL when that is 0; the split-K partial sums P[S,M,N] (fp32) occupy its
+ * first S*M*N*4 bytes.  Output buffers must not overlap the inputs. */
+sg_status skinny_gemm(const sg_plan* plan, const sg_bf16* x, const sg_bf16* W,
+                      float* y_f32, sg_bf16* y_bf16,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused residual epilogue ([P] Method details §2): out = r + x W^T, with the
+ * fp32 accumulator added to r in fp32 and rounded once.  out_bf16 [M,N]
+ * and/or out_f32 [M,N]; out_bf16 may be the same pointer as r (in place;
+ * any other overlap is undefined).  Workspace as for skinny_gemm. */
+sg_status skinny_gemm_residual(const sg_plan* plan, const sg_bf16* x, const sg_bf16* W,
+                               const sg_bf16* r, sg_bf16* out_bf16, float* out_f32,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes grouped_skinny_gemm needs for this problem size. */
+size_t grouped_skinny_gemm_workspace(int32_t T, int32_t E, int32_t topk, int32_t N, int32_t K);
+
+/* Routed-expert projection for MoE decode ([P] Method details §3, [F]
+ * Partie 2 §4).  x [T,K] bf16, W [E,N,K] bf16 (expert e at W + e*N*K),
+ * topk_ids [T,topk] int32.  Pair p = t*topk + j sends token t to expert
+ * ids[p]; out [T,topk,N] fp32 gets out[t,j,n] = sum_k x[t,k] W[ids[p],n,k].
+ * Each selected expert's weights are read once per call however many tokens
+ * chose it.  Optional outputs (NULL to skip), computed on the device:
+ *   expert_offsets [E+1]: offsets[e] = number of valid pairs routed to
+ *                         experts below e;
+ *   sorted_pairs [T*topk]: valid pairs grouped by expert in ascending id,
+ *                         ascending p inside a group, -1 after the last;
+ *   invalid_count [1]:    pairs whose id is outside [0, E) -- their
+ *                         out rows are zero-filled.
+ * Limits: 0 <= T <= 256, 1 <= topk <= 32, T*topk <= 4096, 1 <= E <= 4096,
+ * 0 <= N <= 1<<20, 0 <= K <= 8192 (else SG_ERR_SHAPE). */
+sg_status grouped_skinny_gemm(const sg_bf16* x, int32_t T, const sg_bf16* W, int32_t E,
+                              int32_t N, int32_t K, const int32_t* topk_ids, int32_t topk,
+                              float* out, int32_t* expert_offsets, int32_t* sorted_pairs,
+                              int32_t* invalid_count,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Side-stream weight prefetch ([P] Method details §4): reads
+ * [W, W + bytes) so that a following projection finds it in the GPU's
+ * caches (MI355X: 4 MB L2 per XCD, 256 MB Infinity Cache).  Reads only the
+ * given static-weight range and writes nothing ([F] Partie 2 §3); the
+ * caller orders it against other streams with events.  W 16-byte aligned,
+ * bytes a multiple of 16. */
+sg_status skinny_gemm_prefetch(const void* W, size_t bytes, void* stream);
+
+/* Text for a status code (static storage). */
+const char* skinny_gemm_status_str(sg_status status);
+
+/* Launch counters, indexed by sg_kernel: how many times each kernel was
+ * launched since load or the last reset ([F] Partie 2 §1: which path ran
+ * must be observable).  Process-wide, atomic. */
+void skinny_gemm_get_counters(uint64_t launches[SG_NUM_COUNTERS]);
+void skinny_gemm_reset_counters(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKINNY_GEMM_H */

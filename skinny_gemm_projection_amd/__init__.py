@@ -1,0 +1,194 @@
+"""Python binding of libskinny_gemm.so: the batch-1..64 decode projection
+y = x W^T (+ fused residual) and its routed-expert variant on MI355X.
+
+Each function has the name of the C entry point it calls (include/
+skinny_gemm.h) and only marshals arguments: torch tensors become device
+pointers, the current torch stream becomes the hipStream_t, and a missing
+workspace is allocated with torch (PyTorch provides memory and streams; every
+step of the computation runs in the library's HIP kernels).  A non-SG_OK
+status raises SkinnyGemmError.  There is no fallback: if the library is not
+built, importing it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (KERNEL_NAMES, SG_KERNEL_GEMV, SG_KERNEL_GROUPED, SG_KERNEL_MOE_TABLE,
+                   SG_KERNEL_NONE, SG_KERNEL_PREFETCH, SG_KERNEL_REDUCE, SG_KERNEL_SPLITK_MFMA,
+                   SG_KERNEL_SPLITK_VALU, SG_NUM_COUNTERS, SgPlan, SkinnyGemmError)
+
+__all__ = [
+    "skinny_gemm_plan", "skinny_gemm_plan_force", "skinny_gemm", "skinny_gemm_residual",
+    "grouped_skinny_gemm_workspace", "grouped_skinny_gemm", "skinny_gemm_prefetch",
+    "skinny_gemm_status_str", "skinny_gemm_get_counters", "skinny_gemm_reset_counters",
+    "SgPlan", "SkinnyGemmError", "KERNEL_NAMES", "SG_KERNEL_NONE", "SG_KERNEL_GEMV",
+    "SG_KERNEL_SPLITK_VALU", "SG_KERNEL_SPLITK_MFMA", "SG_KERNEL_REDUCE", "SG_KERNEL_MOE_TABLE",
+    "SG_KERNEL_GROUPED", "SG_KERNEL_PREFETCH", "SG_NUM_COUNTERS", "library_path",
+]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _c():
+    return _lib.load()
+
+
+def _ptr(t, dtype, name, device=None):
+    """Device pointer of a contiguous tensor of the expected dtype (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _shape(t, shape, name):
+    """The C ABI cannot see buffer sizes: refuse tensors whose shape disagrees with the plan."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} does not match the plan's {tuple(shape)}")
+
+
+def _at_least(t, count, name):
+    if t is not None and t.numel() < count:
+        raise ValueError(f"{name}: needs at least {count} elements, has {t.numel()}")
+
+
+def _workspace(nbytes: int, workspace, device):
+    if nbytes == 0:
+        return workspace, (workspace.numel() if workspace is not None else 0)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise TypeError("workspace: expected a device tensor")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def skinny_gemm_plan(M: int, N: int, K: int) -> SgPlan:
+    """plan(M, N, K): kernel, split factor and workspace for y[M,N] = x[M,K] W[N,K]^T."""
+    plan = SgPlan()
+    _lib.check(_c().skinny_gemm_plan(M, N, K, ctypes.byref(plan)))
+    return plan
+
+
+def skinny_gemm_plan_force(M: int, N: int, K: int, kernel: int, split_k: int = 0) -> SgPlan:
+    """plan with the kernel (SG_KERNEL_*) and split factor chosen by the caller."""
+    plan = SgPlan()
+    _lib.check(_c().skinny_gemm_plan_force(M, N, K, kernel, split_k, ctypes.byref(plan)))
+    return plan
+
+
+def skinny_gemm(plan: SgPlan, x: torch.Tensor, W: torch.Tensor, y_f32=None, y_bf16=None,
+                workspace=None, stream=None):
+    """y = x W^T into y_f32 (float32 [M,N]) and/or y_bf16 (bfloat16 [M,N])."""
+    dev = x.device
+    M, N, K = plan.M, plan.N, plan.K
+    _shape(x, (M, K), "x"), _shape(W, (N, K), "W")
+    _shape(y_f32, (M, N), "y_f32"), _shape(y_bf16, (M, N), "y_bf16")
+    ws, ws_bytes = _workspace(plan.workspace_bytes, workspace, dev)
+    st = _c().skinny_gemm(ctypes.byref(plan), _ptr(x, torch.bfloat16, "x", dev),
+                          _ptr(W, torch.bfloat16, "W", dev),
+                          _ptr(y_f32, torch.float32, "y_f32", dev),
+                          _ptr(y_bf16, torch.bfloat16, "y_bf16", dev),
+                          _ptr(ws, torch.uint8, "workspace", dev) if ws is not None else None,
+                          ws_bytes, _stream(stream))
+    _lib.check(st)
+    return ws
+
+
+def skinny_gemm_residual(plan: SgPlan, x: torch.Tensor, W: torch.Tensor, r: torch.Tensor,
+                         out_bf16=None, out_f32=None, workspace=None, stream=None):
+    """out = r + x W^T (one rounding) into out_bf16 (may be r itself) and/or out_f32."""
+    dev = x.device
+    M, N, K = plan.M, plan.N, plan.K
+    _shape(x, (M, K), "x"), _shape(W, (N, K), "W"), _shape(r, (M, N), "r")
+    _shape(out_f32, (M, N), "out_f32"), _shape(out_bf16, (M, N), "out_bf16")
+    ws, ws_bytes = _workspace(plan.workspace_bytes, workspace, dev)
+    st = _c().skinny_gemm_residual(ctypes.byref(plan), _ptr(x, torch.bfloat16, "x", dev),
+                                   _ptr(W, torch.bfloat16, "W", dev),
+                                   _ptr(r, torch.bfloat16, "r", dev),
+                                   _ptr(out_bf16, torch.bfloat16, "out_bf16", dev),
+                                   _ptr(out_f32, torch.float32, "out_f32", dev),
+                                   _ptr(ws, torch.uint8, "workspace", dev) if ws is not None else None,
+                                   ws_bytes, _stream(stream))
+    _lib.check(st)
+    return ws
+
+
+def grouped_skinny_gemm_workspace(T: int, E: int, topk: int, N: int, K: int) -> int:
+    return int(_c().grouped_skinny_gemm_workspace(T, E, topk, N, K))
+
+
+def grouped_skinny_gemm(x: torch.Tensor, W: torch.Tensor, topk_ids: torch.Tensor, out: torch.Tensor,
+                        expert_offsets=None, sorted_pairs=None, invalid_count=None,
+                        workspace=None, stream=None):
+    """out[t,j,:] = W[topk_ids[t,j]] @ x[t] for x [T,K], W [E,N,K], topk_ids [T,topk] int32."""
+    dev = x.device
+    T, K = x.shape
+    E, N, K2 = W.shape
+    if K2 != K or topk_ids.dim() != 2 or topk_ids.shape[0] != T:
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, W {tuple(W.shape)}, "
+                         f"topk_ids {tuple(topk_ids.shape)}")
+    topk = topk_ids.shape[1]
+    _shape(out, (T, topk, N), "out")
+    _at_least(expert_offsets, E + 1, "expert_offsets")
+    _at_least(sorted_pairs, T * topk, "sorted_pairs")
+    _at_least(invalid_count, 1, "invalid_count")
+    need = grouped_skinny_gemm_workspace(T, E, topk, N, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _c().grouped_skinny_gemm(
+        _ptr(x, torch.bfloat16, "x", dev), T, _ptr(W, torch.bfloat16, "W", dev), E, N, K,
+        _ptr(topk_ids, torch.int32, "topk_ids", dev), topk, _ptr(out, torch.float32, "out", dev),
+        _ptr(expert_offsets, torch.int32, "expert_offsets", dev),
+        _ptr(sorted_pairs, torch.int32, "sorted_pairs", dev),
+        _ptr(invalid_count, torch.int32, "invalid_count", dev),
+        _ptr(workspace, torch.uint8, "workspace", dev), ws_bytes, _stream(stream))
+    _lib.check(st)
+    return workspace
+
+
+def skinny_gemm_prefetch(W: torch.Tensor, nbytes: int | None = None, stream=None) -> None:
+    """Warm [W, W + nbytes) into the GPU caches on `stream` (static weights only)."""
+    if not W.is_cuda or not W.is_contiguous():
+        raise ValueError("W: must be a contiguous device tensor")
+    total = W.numel() * W.element_size()
+    nbytes = total if nbytes is None else int(nbytes)
+    if nbytes > total:
+        raise ValueError("nbytes exceeds the tensor")
+    _lib.check(_c().skinny_gemm_prefetch(W.data_ptr() or None, nbytes, _stream(stream)))
+
+
+def skinny_gemm_status_str(status: int) -> str:
+    return _c().skinny_gemm_status_str(status).decode()
+
+
+def skinny_gemm_get_counters() -> list[int]:
+    arr = (ctypes.c_uint64 * SG_NUM_COUNTERS)()
+    _c().skinny_gemm_get_counters(arr)
+    return list(arr)
+
+
+def skinny_gemm_reset_counters() -> None:
+    _c().skinny_gemm_reset_counters()

@@ -1,0 +1,64 @@
+// launch.h -- host-side launchers of the gfx950 kernels (internal to the
+// library; the public interface is include/skinny_gemm.h).  Each launcher
+// checks nothing: the C-ABI layer has validated every argument before.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sg_device.h"
+
+namespace sg {
+
+// Largest chunk count (x registers: M * nch * 4 VGPRs) the row-streaming
+// VALU kernel is instantiated for at a given M; nch = ceil(k_chunk / 512).
+int rowdot_nch_cap(int M);
+// Rows each wavefront handles per iteration in the row-streaming kernel.
+int rowdot_rows_per_iter(int M, int nch);
+// Wavefront slots the row-streaming kernel aims to keep resident.
+int rowdot_resident_waves(int M, int nch);
+
+// Row-streaming VALU kernel (small-matrix path and VALU split-K partials).
+// x [M, K], W [N, K]; split s covers pieces [s*chunk8, min(K8, (s+1)*chunk8)).
+hipError_t launch_rowdot(int M, int N, int K, int S, int k_chunk, int grid,
+                         const void* x, const void* W, const Epilogue& ep,
+                         hipStream_t stream);
+int rowdot_grid(int M, int N, int K, int S, int k_chunk);
+
+// bf16 matrix-core split-K kernel (16 <= M <= 64, any M >= 1 when forced).
+constexpr int kMfmaTileN = 64;  // W rows per workgroup (4 waves x 16)
+hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk,
+                              const void* x, const void* W, const Epilogue& ep,
+                              hipStream_t stream);
+
+// Deterministic split-K reduction: y[i] = P[0,i] + ... + P[S-1,i] (s
+// ascending, fp32), then the final epilogue.
+hipError_t launch_reduce(const float* P, int S, int64_t MN, const Epilogue& ep,
+                         hipStream_t stream);
+
+// Per-expert token table.  ws points at the grouped workspace (layout in
+// GroupedWorkspace).
+struct GroupedWorkspace {
+    int32_t* counts;       // [E]
+    int32_t* offsets;      // [E+1]
+    int32_t* sorted;       // [P]
+    int32_t* invalid;      // [1]
+    int32_t* active;       // [E]   experts with counts > 0, ascending
+    int32_t* num_active;   // [1]
+};
+GroupedWorkspace grouped_workspace_layout(void* ws, int E, int P);
+size_t grouped_workspace_bytes(int E, int P);
+
+hipError_t launch_moe_table(const int32_t* ids, int T, int topk, int E, int N,
+                            const GroupedWorkspace& g, int32_t* user_offsets,
+                            int32_t* user_sorted, int32_t* user_invalid, float* out,
+                            hipStream_t stream);
+
+constexpr int kGroupedRowsPerWave = 4;
+constexpr int kGroupedTileN = kGroupedRowsPerWave * kWavesPerBlock;  // 16 rows per item
+hipError_t launch_grouped(const void* x, int T, const void* W, int E, int N, int K, int topk,
+                          const GroupedWorkspace& g, float* out, hipStream_t stream);
+
+hipError_t launch_prefetch(const void* W, size_t bytes, hipStream_t stream);
+
+}  // namespace sg

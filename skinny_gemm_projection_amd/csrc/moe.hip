@@ -1,0 +1,262 @@
+// moe.hip -- routed-expert (MoE) decode: per-expert token table and the
+// grouped per-expert projection, for gfx950.
+//
+// The pages replace the stock MoE GEMMs with custom low-latency kernels and
+// note that expert selection decides which weights get read ("Hyper
+// Optimizing Kimi K3 in vLLM" deepnotes page, Method details §3 and
+// Supplementary details §1; French translation, Partie 2 §4).  Here the
+// selection is turned into a table on the device, and every selected
+// expert's weight matrix is then streamed from HBM once per call, however
+// many tokens chose it.  No host synchronisation: the number of active
+// experts is only known on the device, so the grouped kernel reads it there.
+#include "launch.h"
+
+namespace sg {
+
+namespace {
+
+constexpr int kTableThreads = 1024;
+constexpr int kMaxPairs = 4096;
+constexpr int kMaxExperts = 4096;
+
+// One workgroup.  counts[e] by LDS integer atomics; offsets and the list of
+// active experts by one block-wide scan; then each valid pair p lands at
+// offsets[e] + (number of earlier pairs with the same expert), which keeps
+// every expert's segment in ascending p.  Pairs with an id outside [0, E)
+// are counted and their output rows zero-filled.
+__global__ __launch_bounds__(kTableThreads) void moe_table_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int N, GroupedWorkspace g,
+    int32_t* user_offsets, int32_t* user_sorted, int32_t* user_invalid, float* out) {
+    __shared__ int32_t s_ids[kMaxPairs];
+    __shared__ int32_t s_off[kMaxExperts];
+    __shared__ int32_t s_scan_c[kTableThreads];
+    __shared__ int32_t s_scan_a[kTableThreads];
+    __shared__ int32_t s_inv;
+
+    const int tid = threadIdx.x;
+    for (int p = tid; p < P; p += kTableThreads) s_ids[p] = ids[p];
+    for (int e = tid; e < E; e += kTableThreads) s_off[e] = 0;
+    if (tid == 0) s_inv = 0;
+    __syncthreads();
+
+    for (int p = tid; p < P; p += kTableThreads) {
+        const int e = s_ids[p];
+        if (e >= 0 && e < E)
+            atomicAdd(&s_off[e], 1);
+        else
+            atomicAdd(&s_inv, 1);
+    }
+    __syncthreads();
+
+    // Thread t owns experts 4t .. 4t+3 (E <= 4096).
+    int c[4];
+    int sum_c = 0, sum_a = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * tid + j;
+        c[j] = (e < E) ? s_off[e] : 0;
+        sum_c += c[j];
+        sum_a += c[j] > 0;
+    }
+    s_scan_c[tid] = sum_c;
+    s_scan_a[tid] = sum_a;
+    __syncthreads();
+    for (int off = 1; off < kTableThreads; off <<= 1) {
+        const int vc = tid >= off ? s_scan_c[tid - off] : 0;
+        const int va = tid >= off ? s_scan_a[tid - off] : 0;
+        __syncthreads();
+        s_scan_c[tid] += vc;
+        s_scan_a[tid] += va;
+        __syncthreads();
+    }
+    int pc = s_scan_c[tid] - sum_c;  // exclusive prefix of counts
+    int pa = s_scan_a[tid] - sum_a;  // exclusive prefix of active flags
+    const int total = s_scan_c[kTableThreads - 1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * tid + j;
+        if (e < E) {
+            g.counts[e] = c[j];
+            g.offsets[e] = pc;
+            if (user_offsets) user_offsets[e] = pc;
+            s_off[e] = pc;
+            if (c[j] > 0) g.active[pa++] = e;
+            pc += c[j];
+        }
+    }
+    if (tid == 0) {
+        g.offsets[E] = total;
+        if (user_offsets) user_offsets[E] = total;
+        *g.num_active = s_scan_a[kTableThreads - 1];
+        *g.invalid = s_inv;
+        if (user_invalid) *user_invalid = s_inv;
+    }
+    __syncthreads();
+
+    for (int p = tid; p < P; p += kTableThreads) {
+        const int e = s_ids[p];
+        if (e >= 0 && e < E) {
+            int rank = 0;
+            for (int q = 0; q < p; ++q) rank += (s_ids[q] == e);
+            g.sorted[s_off[e] + rank] = p;
+            if (user_sorted) user_sorted[s_off[e] + rank] = p;
+        }
+    }
+    for (int i = total + tid; i < P; i += kTableThreads) {
+        g.sorted[i] = -1;
+        if (user_sorted) user_sorted[i] = -1;
+    }
+
+    if (s_inv > 0) {  // rare: zero-fill the output rows of out-of-range ids
+        for (int p = 0; p < P; ++p) {
+            const int e = s_ids[p];
+            if (e < 0 || e >= E)
+                for (int n = tid; n < N; n += kTableThreads) out[(int64_t)p * N + n] = 0.0f;
+        }
+    }
+}
+
+// A whole row (K8 16-byte pieces) as NCH lane-pieces; pieces past the row
+// read as zero through the buffer bounds, and only the wave-uniform chunk
+// count guards the loads.
+template <int NCH>
+__device__ __forceinline__ void load_row(uint4 (&dst)[NCH], const uint4* __restrict__ src,
+                                         int K8, int lane) {
+    const rsrc_t r = make_rsrc(src, (uint32_t)K8 * 16u);
+    const int nch = (K8 + kWave - 1) / kWave;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        dst[c] = make_uint4(0, 0, 0, 0);
+        if (c < nch) dst[c] = load16(r, (uint32_t)(c * kWave + lane) * 16u);
+    }
+}
+
+template <int NCH>
+__device__ __forceinline__ float dot_row(const uint4 (&a)[NCH], const uint4 (&b)[NCH]) {
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) s = dot8(a[c], b[c], s);
+    return s;
+}
+
+// Persistent grid over work items (active expert, 16-row tile of its W).
+// Each wave streams 4 rows of the expert's weights, one whole row (K <= 8192,
+// up to 16 x 1 KB loads) at a time, like the small-matrix kernel, and
+// multiplies it with the gathered x rows of the tokens routed there, two at
+// a time.  With one or two tokens (the common case) their x rows are loaded
+// once per item; with more, the weight row stays in registers while token
+// pairs stream past it, so each weight byte is still fetched once.
+template <int NCH>
+__global__ __launch_bounds__(kBlock) void grouped_kernel(const uint4* __restrict__ x,
+                                                         const uint4* __restrict__ W, int N,
+                                                         int K8, int topk, int tiles,
+                                                         GroupedWorkspace g,
+                                                         float* __restrict__ out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = wave_id_in_block();
+    const int items = *g.num_active * tiles;
+
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int e = g.active[item / tiles];
+        const int tile = item - (item / tiles) * tiles;
+        const int seg = g.offsets[e];
+        const int cnt = g.offsets[e + 1] - seg;
+        const uint4* __restrict__ We = W + (int64_t)e * N * K8;
+        const int nbase = tile * kGroupedTileN + wv * kGroupedRowsPerWave;
+
+        uint4 xa[NCH], xb[NCH], wr[NCH];
+        if (cnt <= 2) {
+            const int pa = g.sorted[seg];
+            const int pb = cnt > 1 ? g.sorted[seg + 1] : pa;
+            load_row<NCH>(xa, x + (int64_t)(pa / topk) * K8, K8, lane);
+            load_row<NCH>(xb, x + (int64_t)(pb / topk) * K8, K8, lane);
+#pragma unroll 1
+            for (int i = 0; i < kGroupedRowsPerWave; ++i) {
+                const int n = nbase + i;
+                if (n >= N) break;
+                load_row<NCH>(wr, We + (int64_t)n * K8, K8, lane);
+                const float ta = wave_sum(dot_row<NCH>(xa, wr));
+                const float tb = wave_sum(dot_row<NCH>(xb, wr));
+                if (lane == 0) out[(int64_t)pa * N + n] = ta;
+                if (lane == 1 && cnt > 1) out[(int64_t)pb * N + n] = tb;
+            }
+        } else {
+#pragma unroll 1
+            for (int i = 0; i < kGroupedRowsPerWave; ++i) {
+                const int n = nbase + i;
+                if (n >= N) break;
+                load_row<NCH>(wr, We + (int64_t)n * K8, K8, lane);
+#pragma unroll 1
+                for (int c0 = 0; c0 < cnt; c0 += 2) {
+                    const int pa = g.sorted[seg + c0];
+                    const int pb = c0 + 1 < cnt ? g.sorted[seg + c0 + 1] : pa;
+                    load_row<NCH>(xa, x + (int64_t)(pa / topk) * K8, K8, lane);
+                    load_row<NCH>(xb, x + (int64_t)(pb / topk) * K8, K8, lane);
+                    const float ta = wave_sum(dot_row<NCH>(xa, wr));
+                    const float tb = wave_sum(dot_row<NCH>(xb, wr));
+                    if (lane == 0) out[(int64_t)pa * N + n] = ta;
+                    if (lane == 1 && c0 + 1 < cnt) out[(int64_t)pb * N + n] = tb;
+                }
+            }
+        }
+    }
+}
+
+int next_pow2(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+}  // namespace
+
+size_t grouped_workspace_bytes(int E, int P) {
+    const size_t ints = (size_t)E + (E + 1) + P + 1 + E + 1;
+    return (ints * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+GroupedWorkspace grouped_workspace_layout(void* ws, int E, int P) {
+    int32_t* base = static_cast<int32_t*>(ws);
+    GroupedWorkspace g;
+    g.counts = base;
+    g.offsets = g.counts + E;
+    g.sorted = g.offsets + E + 1;
+    g.invalid = g.sorted + P;
+    g.active = g.invalid + 1;
+    g.num_active = g.active + E;
+    return g;
+}
+
+hipError_t launch_moe_table(const int32_t* ids, int T, int topk, int E, int N,
+                            const GroupedWorkspace& g, int32_t* user_offsets,
+                            int32_t* user_sorted, int32_t* user_invalid, float* out,
+                            hipStream_t stream) {
+    moe_table_kernel<<<1, kTableThreads, 0, stream>>>(ids, T * topk, E, N, g, user_offsets,
+                                                      user_sorted, user_invalid, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped(const void* x, int T, const void* W, int E, int N, int K, int topk,
+                          const GroupedWorkspace& g, float* out, hipStream_t stream) {
+    const int K8 = K / kPiece;
+    const int tiles = (N + kGroupedTileN - 1) / kGroupedTileN;
+    const int max_active = E < T * topk ? E : T * topk;
+    const int64_t max_items = (int64_t)max_active * tiles;
+    const int resident = 512;  // 256 CUs x 2 workgroups
+    const int grid = (int)(max_items < resident ? max_items : resident);
+    if (grid <= 0) return hipSuccess;
+    const uint4* xp = static_cast<const uint4*>(x);
+    const uint4* wp = static_cast<const uint4*>(W);
+    const int nch = (K + kLaneSpan - 1) / kLaneSpan;
+    switch (next_pow2(nch < 1 ? 1 : nch)) {
+        case 1: grouped_kernel<1><<<grid, kBlock, 0, stream>>>(xp, wp, N, K8, topk, tiles, g, out); break;
+        case 2: grouped_kernel<2><<<grid, kBlock, 0, stream>>>(xp, wp, N, K8, topk, tiles, g, out); break;
+        case 4: grouped_kernel<4><<<grid, kBlock, 0, stream>>>(xp, wp, N, K8, topk, tiles, g, out); break;
+        case 8: grouped_kernel<8><<<grid, kBlock, 0, stream>>>(xp, wp, N, K8, topk, tiles, g, out); break;
+        case 16: grouped_kernel<16><<<grid, kBlock, 0, stream>>>(xp, wp, N, K8, topk, tiles, g, out); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sg

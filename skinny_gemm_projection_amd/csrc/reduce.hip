@@ -1,0 +1,60 @@
+// reduce.hip -- deterministic second pass of split-K.
+//
+// y[i] = P[0, i] + P[1, i] + ... + P[S-1, i], added in ascending s in fp32 (no
+// atomics, so every run gives the same bits), followed by the final
+// epilogue: optional residual add (fp32(r) + y, rounded once to bf16 -- the
+// output projection fused with the residual, "Hyper Optimizing Kimi K3 in
+// vLLM" deepnotes page, Method details §2) and fp32 and/or bf16 stores.
+// Each thread owns 4 consecutive outputs (16-byte partial loads when the
+// row-major M*N plane keeps them aligned).
+#include "launch.h"
+
+namespace sg {
+
+namespace {
+
+__global__ __launch_bounds__(kBlock) void splitk_reduce_kernel(const float* __restrict__ P, int S,
+                                                               int64_t MN, Epilogue ep) {
+    const int64_t i0 = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * 4;
+    if (i0 >= MN) return;
+    float acc[4];
+    if ((MN & 3) == 0) {
+        float4 a = reinterpret_cast<const float4*>(P + i0)[0];
+        for (int s = 1; s < S; ++s) {
+            const float4 b = reinterpret_cast<const float4*>(P + (int64_t)s * MN + i0)[0];
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        acc[0] = a.x;
+        acc[1] = a.y;
+        acc[2] = a.z;
+        acc[3] = a.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float a = 0.0f;
+            if (i0 + j < MN) {
+                a = P[i0 + j];
+                for (int s = 1; s < S; ++s) a += P[(int64_t)s * MN + i0 + j];
+            }
+            acc[j] = a;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (i0 + j < MN) store_final(ep, i0 + j, acc[j]);
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const float* P, int S, int64_t MN, const Epilogue& ep,
+                         hipStream_t stream) {
+    const int64_t threads = (MN + 3) / 4;
+    const int64_t grid = (threads + kBlock - 1) / kBlock;
+    splitk_reduce_kernel<<<dim3((unsigned)grid), kBlock, 0, stream>>>(P, S, MN, ep);
+    return hipGetLastError();
+}
+
+}  // namespace sg

@@ -1,0 +1,217 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function include/skinny_gemm.h declares, plans shapes as documented, and
+rejects bad calls before touching the device.
+
+Calls with made-up device pointers only run on a host without a GPU: there
+any accidental launch fails harmlessly instead of reading a stray address.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import skinny_gemm_projection_amd as sg
+from skinny_gemm_projection_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "skinny_gemm.h")
+
+no_gpu_only = pytest.mark.skipif(torch.cuda.is_available(),
+                                 reason="fake device pointers are only passed on a host without a GPU")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s+(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if not n.startswith("SG_")))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("skinny_gemm_plan", "skinny_gemm_plan_force", "skinny_gemm", "skinny_gemm_residual",
+                 "grouped_skinny_gemm_workspace", "grouped_skinny_gemm", "skinny_gemm_prefetch",
+                 "skinny_gemm_status_str", "skinny_gemm_get_counters", "skinny_gemm_reset_counters"):
+        assert want in names, want
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(sg.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", sg.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, f"{name} missing from the dynamic symbol table"
+
+
+def test_python_binding_has_the_same_names():
+    for name in declared_functions():
+        assert callable(getattr(sg, name)), name
+
+
+def test_status_strings():
+    for code, name in _lib.STATUS_NAMES.items():
+        assert sg.skinny_gemm_status_str(code).startswith(name)
+    assert "unknown" in sg.skinny_gemm_status_str(99)
+
+
+# ------------------------------------------------------------------ planner
+
+
+def test_plan_kernel_by_batch():
+    for M in range(1, 65):
+        p = sg.skinny_gemm_plan(M, 4096, 7168)
+        want = (sg.SG_KERNEL_GEMV if M <= 2 else
+                sg.SG_KERNEL_SPLITK_VALU if M < 16 else sg.SG_KERNEL_SPLITK_MFMA)
+        assert p.kernel == want, (M, p)
+        assert (p.M, p.N, p.K) == (M, 4096, 7168)
+
+
+def test_plan_rejects():
+    cases = [((65, 16, 16), 3), ((1000, 16, 16), 3), ((-1, 16, 16), 2), ((1, -1, 16), 2),
+             ((1, 16, -8), 2), ((1, (1 << 20) + 1, 16), 2), ((1, 16, 12), 4), ((1, 16, 7), 4)]
+    for (M, N, K), code in cases:
+        with pytest.raises(sg.SkinnyGemmError) as e:
+            sg.skinny_gemm_plan(M, N, K)
+        assert e.value.status == code, (M, N, K, e.value.status)
+
+
+def test_plan_empty_problems():
+    for M, N, K in [(0, 16, 16), (4, 0, 16), (0, 0, 0)]:
+        p = sg.skinny_gemm_plan(M, N, K)
+        assert p.kernel == sg.SG_KERNEL_NONE and p.workspace_bytes == 0
+    p = sg.skinny_gemm_plan(3, 16, 0)  # K = 0: the empty sum, still written
+    assert p.kernel == sg.SG_KERNEL_SPLITK_VALU and p.k_chunk == 0
+
+
+@pytest.mark.parametrize("N,K", [(1024, 1024), (8192, 7168), (4096, 7168), (7168, 8192),
+                                 (2048, 7168), (384, 7168), (100, 136), (33, 8), (4096, 16384)])
+def test_plan_invariants(N, K):
+    for M in range(1, 65):
+        p = sg.skinny_gemm_plan(M, N, K)
+        S, c = p.split_k, p.k_chunk
+        assert S >= 1 and c % 8 == 0
+        assert c == 8 * -(-K // (8 * S)), "chunk is ceil(K / S) rounded up to a multiple of 8"
+        assert (S - 1) * c < K or K == 0, "no empty chunk in an automatic plan"
+        if S > 1:
+            assert p.workspace_bytes >= S * M * N * 4 and p.workspace_bytes % 256 == 0
+        else:
+            assert p.workspace_bytes == 0
+        if p.kernel in (sg.SG_KERNEL_GEMV, sg.SG_KERNEL_SPLITK_VALU):
+            nch = -(-c // 512)
+            cap = 16 if M <= 2 else 8 if M <= 4 else 4 if M <= 8 else 2
+            assert nch <= cap, (M, N, K, p)
+        assert p.grid >= 1
+        assert sg.skinny_gemm_plan(M, N, K).as_dict() == p.as_dict(), "deterministic"
+
+
+def test_plan_small_matrix_kernel_has_no_split_up_to_8192():
+    for K in (1024, 7168, 8192):
+        for M in (1, 2):
+            assert sg.skinny_gemm_plan(M, 8192, K).split_k == 1
+
+
+def test_plan_force():
+    G, V, F = sg.SG_KERNEL_GEMV, sg.SG_KERNEL_SPLITK_VALU, sg.SG_KERNEL_SPLITK_MFMA
+    p = sg.skinny_gemm_plan_force(8, 4096, 7168, F, 2)
+    assert p.kernel == F and p.split_k == 2 and p.k_chunk == 3584
+    p = sg.skinny_gemm_plan_force(1, 4096, 7168, V, 14)
+    assert p.kernel == V and p.k_chunk == 512
+    p = sg.skinny_gemm_plan_force(4, 4096, 7168, F, 3)
+    assert p.k_chunk == 2392 and 2 * 2392 < 7168 <= 3 * 2392
+    p = sg.skinny_gemm_plan_force(5, 1000, 2056, V, 2)
+    assert p.k_chunk == 1032
+    for args in [(3, 64, 64, G, 1), (16, 64, 64, V, 1), (4, 4096, 7168, F, 65),
+                 (4, 4096, 7168, 9, 1), (8, 4096, 7168, V, 1), (8, 4096, 7168, V, 2)]:
+        with pytest.raises(sg.SkinnyGemmError) as e:
+            sg.skinny_gemm_plan_force(*args)
+        assert e.value.status == 6, args
+
+
+def test_grouped_workspace_size():
+    assert sg.grouped_skinny_gemm_workspace(64, 384, 8, 2048, 7168) >= 4 * (3 * 384 + 512 + 3)
+    assert sg.grouped_skinny_gemm_workspace(257, 384, 8, 2048, 7168) == 0
+    assert sg.grouped_skinny_gemm_workspace(4, 384, 8, 2048, 8200) == 0
+
+
+# ------------------------------------------------------------------ host-rejected calls
+
+
+def _raw():
+    return _lib.load()
+
+
+@no_gpu_only
+def test_projection_errors_return_before_launch():
+    c = _raw()
+    sg.skinny_gemm_reset_counters()
+    p = sg.skinny_gemm_plan(8, 4096, 7168)  # split-K: needs a workspace
+    bp = ctypes.byref(p)
+    A = 0x10000  # aligned, never dereferenced
+    ws = p.workspace_bytes
+    assert c.skinny_gemm(None, A, A, A, None, A, ws, None) == 1
+    assert c.skinny_gemm(bp, None, A, A, None, A, ws, None) == 1
+    assert c.skinny_gemm(bp, A, A, None, None, A, ws, None) == 1
+    assert c.skinny_gemm(bp, A + 8, A, A, None, A, ws, None) == 4
+    assert c.skinny_gemm(bp, A, A, A + 4, None, A, ws, None) == 4
+    assert c.skinny_gemm(bp, A, A, A, None, None, ws, None) == 5
+    assert c.skinny_gemm(bp, A, A, A, None, A, ws - 1, None) == 5
+    assert c.skinny_gemm(bp, A, A, A, None, A + 8, ws, None) == 4
+    bad = _lib.SgPlan.from_buffer_copy(p)
+    bad.grid += 1
+    assert c.skinny_gemm(ctypes.byref(bad), A, A, A, None, A, ws, None) == 6
+    bad = _lib.SgPlan.from_buffer_copy(p)
+    bad.N = 4097
+    assert c.skinny_gemm(ctypes.byref(bad), A, A, A, None, A, ws, None) == 6
+    assert c.skinny_gemm_residual(bp, A, A, None, A, None, A, ws, None) == 1
+    assert c.skinny_gemm_residual(bp, A, A, A, None, None, A, ws, None) == 1
+    assert c.skinny_gemm_residual(bp, A, A, A + 2, A, None, A, ws, None) == 4
+    assert sum(sg.skinny_gemm_get_counters()) == 0, "nothing may launch on a rejected call"
+
+
+@no_gpu_only
+def test_empty_projection_launches_nothing():
+    c = _raw()
+    sg.skinny_gemm_reset_counters()
+    p = sg.skinny_gemm_plan(0, 4096, 7168)
+    assert c.skinny_gemm(ctypes.byref(p), None, None, None, None, None, 0, None) == 0
+    assert sum(sg.skinny_gemm_get_counters()) == 0
+
+
+@no_gpu_only
+def test_grouped_and_prefetch_errors_return_before_launch():
+    c = _raw()
+    sg.skinny_gemm_reset_counters()
+    A = 0x10000
+    ws = sg.grouped_skinny_gemm_workspace(4, 384, 8, 2048, 7168)
+    args = dict(x=A, T=4, W=A, E=384, N=2048, K=7168, ids=A, topk=8, out=A, off=None, sp=None,
+                inv=None, ws=A, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return c.grouped_skinny_gemm(a["x"], a["T"], a["W"], a["E"], a["N"], a["K"], a["ids"],
+                                     a["topk"], a["out"], a["off"], a["sp"], a["inv"], a["ws"],
+                                     a["wsb"], None)
+
+    assert call(T=257) == 2
+    assert call(topk=0) == 2
+    assert call(E=0) == 2
+    assert call(K=8200) == 2
+    assert call(K=7164) == 4
+    assert call(ids=None) == 1
+    assert call(out=None) == 1
+    assert call(x=None) == 1
+    assert call(W=A + 4) == 4
+    assert call(off=A + 4) == 4
+    assert call(ws=None) == 5
+    assert call(wsb=ws - 4) == 5
+    assert c.skinny_gemm_prefetch(None, 16, None) == 1
+    assert c.skinny_gemm_prefetch(A, 24, None) == 4
+    assert c.skinny_gemm_prefetch(A + 8, 32, None) == 4
+    assert c.skinny_gemm_prefetch(A, 0, None) == 0
+    assert sum(sg.skinny_gemm_get_counters()) == 0
