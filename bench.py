@@ -12,9 +12,12 @@ Each call reads the next copy of a ring of byte-identical weight copies
 larger than twice the 256 MB Infinity Cache, so every call streams its
 weights from HBM rather than from cache.
 
-Timing: W warmup steps, then synchronize and time exactly K steps; every
-launch is bracketed by HIP events on the stream it runs on (a short GPU
-sleep queued first lets the host enqueue ahead, so event gaps are GPU time).
+Timing: W warmup steps, then synchronize and time exactly K steps between
+two HIP events recorded on the stream the kernels run on.  A short GPU sleep
+queued first lets the host enqueue the whole region ahead, so the kernels run
+back to back and the events see GPU time only; no event sits between two
+launches (on this GPU an event between kernels adds several microseconds of
+gap).  The average launch duration is the region's time over its launches.
 value = algorithmic bytes of the K steps / their GPU time (GB/s).
 
 The one JSON line also carries a sweep over the other workloads (batch
@@ -135,21 +138,22 @@ def sleep_cycles_per_ms(torch) -> float:
 
 
 def timed_calls(torch, calls, reps, cycles_per_ms, warmup=3):
-    """Run calls[i % len(calls)] reps times with an event pair around each call.
+    """Run calls[i % len(calls)] reps times back to back between one event pair.
 
-    Returns (per-call GPU ms list, total GPU ms from first to last event)."""
+    No event sits between two calls (an event between kernels adds a gap of
+    several microseconds on this GPU), so the average is the steady-state time
+    of one call as the stream sees it.  Returns the average GPU ms per call."""
     for i in range(warmup):
         calls[i % len(calls)]()
     torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    torch.cuda._sleep(int(cycles_per_ms * min(50.0, 0.02 * reps + 0.5)))
-    evs[0].record()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(cycles_per_ms * min(50.0, 0.03 * reps + 0.5)))
+    start.record()
     for i in range(reps):
         calls[i % len(calls)]()
-        evs[i + 1].record()
+    stop.record()
     torch.cuda.synchronize()
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
-    return per, evs[0].elapsed_time(evs[reps])
+    return start.elapsed_time(stop) / reps
 
 
 def ring_copies(torch, W, min_bytes=RING_MIN_BYTES):
@@ -184,29 +188,33 @@ def main_workload(torch, sg, si, L, steps, warmup, cyc):
     torch.cuda.synchronize()
     sg.skinny_gemm_reset_counters()
 
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()                       # barrier (one rank) + synchronize
     t0 = time.perf_counter()
-    torch.cuda._sleep(int(cyc * min(200.0, 0.03 * len(seq) + 1.0)))
-    evs[0].record()
-    for i, key in enumerate(seq):
+    # a short GPU sleep lets the host queue the whole region before the GPU reaches it, so
+    # kernels run back to back and the two events measure GPU time only
+    torch.cuda._sleep(int(cyc * min(200.0, 0.02 * len(seq) + 1.0)))
+    start.record()
+    for key in seq:
         calls[key]()
-        evs[i + 1].record()
+    stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(seq))]
-    total_ms = evs[0].elapsed_time(evs[-1])
+    total_ms = start.elapsed_time(stop)
     counters = sg.skinny_gemm_get_counters()
     assert counters[sg.SG_KERNEL_GEMV] == len(seq), counters
+    # per batch size: the same ring, each size alone, for the us/projection breakdown
+    per_m_ms = {}
+    for M in M_LIST:
+        per_m_ms[M] = timed_calls(torch, [calls[(M, r)] for r in range(R)], 200, cyc)
 
     bytes_per = {M: proj_bytes(M, N_MAIN, K_MAIN) for M in M_LIST}
     step_bytes = sum(bytes_per.values())
-    per_m = {M: [] for M in M_LIST}
-    for (M, _), ms in zip(seq, per):
-        per_m[M].append(ms)
-    us = {M: 1e3 * sum(v) / len(v) for M, v in per_m.items()}
-    launch_bytes = sum(bytes_per[M] for M, _ in seq)
-    achieved = launch_bytes / (sum(per) * 1e-3) / 1e9
+    us = {M: 1e3 * per_m_ms[M] for M in M_LIST}
+    launches = len(seq)
+    avg_launch_ms = total_ms / launches
+    launch_bytes = sum(bytes_per[M] for M, _ in seq) / launches
+    achieved = launch_bytes / (avg_launch_ms * 1e-3) / 1e9
     ms_per_step = total_ms / steps
     return {
         "plans": {M: plans[M].as_dict() for M in M_LIST},
@@ -215,8 +223,8 @@ def main_workload(torch, sg, si, L, steps, warmup, cyc):
         "value": step_bytes * steps / (total_ms * 1e-3) / 1e9,
         "us_per_projection": {str(M): round(us[M], 3) for M in M_LIST},
         "gbs_per_batch": {str(M): round(bytes_per[M] / (us[M] * 1e-6) / 1e9, 1) for M in M_LIST},
-        "achieved": achieved, "avg_launch_us": 1e3 * sum(per) / len(per),
-        "bytes_per_launch": launch_bytes / len(seq),
+        "achieved": achieved, "avg_launch_us": 1e3 * avg_launch_ms,
+        "bytes_per_launch": launch_bytes,
         "inputs": (x, W0),
     }
 
@@ -225,8 +233,8 @@ def sweep(torch, sg, si, L, cyc, reps=40):
     dev = "cuda"
     rows = []
 
-    def record(name, M, N, K, plan_desc, per, nbytes):
-        us = 1e3 * sum(per) / len(per)
+    def record(name, M, N, K, plan_desc, ms, nbytes):
+        us = 1e3 * ms
         rows.append({"workload": name, "M": M, "N": N, "K": K, "plan": plan_desc,
                      "us": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                      "pct_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)})
@@ -240,7 +248,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
     ring = ring_copies(torch, si.normal_bf16((N, K), 0.02, si.seed_for(1, si.TAG_W), dev))
     p = sg.skinny_gemm_plan(1, N, K)
     y = torch.empty((1, N), device=dev)
-    per, _ = timed_calls(torch, [L.projection(p, x, w, y, None) for w in ring], 512, cyc)
+    per = timed_calls(torch, [L.projection(p, x, w, y, None) for w in ring], 512, cyc)
     record("single 1024x1024", 1, N, K, plan_desc(p), per, proj_bytes(1, N, K, bf16=False))
     del ring
 
@@ -251,7 +259,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
         x = si.normal_bf16((M, K), 1.0, si.seed_for(2, si.TAG_X) + M, dev)
         p = sg.skinny_gemm_plan(M, N, K)
         y32, y16 = torch.empty((M, N), device=dev), torch.empty((M, N), device=dev, dtype=torch.bfloat16)
-        per, _ = timed_calls(torch, [L.projection(p, x, w, y32, y16) for w in ring], reps, cyc)
+        per = timed_calls(torch, [L.projection(p, x, w, y32, y16) for w in ring], reps, cyc)
         record("small-batch 8192x7168", M, N, K, plan_desc(p), per, proj_bytes(M, N, K))
     del ring
 
@@ -263,7 +271,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
         p = sg.skinny_gemm_plan(M, N, K)
         y32 = torch.empty((M, N), device=dev)
         ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
-        per, _ = timed_calls(torch, [L.projection(p, x, w, y32, None, ws) for w in ring], reps, cyc)
+        per = timed_calls(torch, [L.projection(p, x, w, y32, None, ws) for w in ring], reps, cyc)
         record("split-K 4096x7168", M, N, K, plan_desc(p), per, proj_bytes(M, N, K, bf16=False))
     del ring
 
@@ -276,7 +284,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
         p = sg.skinny_gemm_plan(M, N, K)
         o16 = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
         ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
-        per, _ = timed_calls(torch, [L.residual(p, x, w, r, o16, None, ws) for w in ring], reps, cyc)
+        per = timed_calls(torch, [L.residual(p, x, w, r, o16, None, ws) for w in ring], reps, cyc)
         record("residual 7168x8192", M, N, K, plan_desc(p), per,
                proj_bytes(M, N, K, f32=False, residual=True))
     del ring
@@ -294,15 +302,14 @@ def sweep(torch, sg, si, L, cyc, reps=40):
         ws = torch.empty(sg.grouped_skinny_gemm_workspace(T, E, topk, N, K), dtype=torch.uint8,
                          device=dev)
         ids_dev = [t.to(dev) for t in tables]
-        per, _ = timed_calls(torch, [L.grouped(x, W, ids, out, ws) for ids in ids_dev],
-                             max(8, reps // 4), cyc)
+        per = timed_calls(torch, [L.grouped(x, W, ids, out, ws) for ids in ids_dev],
+                             8 * max(1, reps // 32), cyc)
         distinct = [len(set(t.view(-1).tolist())) for t in tables]
-        nbytes = []
-        for i in range(len(per)):
-            d = distinct[i % len(tables)]
-            nbytes.append(d * N * K * 2 + T * K * 2 + T * topk * N * 4 + T * topk * 4)
-        us = 1e3 * sum(per) / len(per)
-        gbs = sum(nbytes) / (sum(per) * 1e-3) / 1e9
+        # the timed calls cycle the tables evenly (reps is a multiple of 8)
+        nbytes = sum(d * N * K * 2 + T * K * 2 + T * topk * N * 4 + T * topk * 4
+                     for d in distinct) / len(distinct)
+        us = 1e3 * per
+        gbs = nbytes / (per * 1e-3) / 1e9
         rows.append({"workload": "MoE grouped E=384 2048x7168 top8", "M": T, "N": N, "K": K,
                      "plan": "moe_table+grouped", "us": round(us, 3), "GBps": round(gbs, 1),
                      "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kTableThreads) void moe_table_kernel(
 // A whole row (K8 16-byte pieces) as NCH lane-pieces; pieces past the row
 // read as zero through the buffer bounds, and only the wave-uniform chunk
 // count guards the loads.
-template <int NCH>
+template <int NCH, int POLICY>
 __device__ __forceinline__ void load_row(uint4 (&dst)[NCH], const uint4* __restrict__ src,
                                          int K8, int lane) {
     const rsrc_t r = make_rsrc(src, (uint32_t)K8 * 16u);
@@ -127,7 +127,7 @@ __device__ __forceinline__ void load_row(uint4 (&dst)[NCH], const uint4* __restr
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         dst[c] = make_uint4(0, 0, 0, 0);
-        if (c < nch) dst[c] = load16(r, (uint32_t)(c * kWave + lane) * 16u);
+        if (c < nch) dst[c] = load16<POLICY>(r, (uint32_t)(c * kWave + lane) * 16u);
     }
 }
 
@@ -168,13 +168,13 @@ __global__ __launch_bounds__(kBlock) void grouped_kernel(const uint4* __restrict
         if (cnt <= 2) {
             const int pa = g.sorted[seg];
             const int pb = cnt > 1 ? g.sorted[seg + 1] : pa;
-            load_row<NCH>(xa, x + (int64_t)(pa / topk) * K8, K8, lane);
-            load_row<NCH>(xb, x + (int64_t)(pb / topk) * K8, K8, lane);
+            load_row<NCH, kCached>(xa, x + (int64_t)(pa / topk) * K8, K8, lane);
+            load_row<NCH, kCached>(xb, x + (int64_t)(pb / topk) * K8, K8, lane);
 #pragma unroll 1
             for (int i = 0; i < kGroupedRowsPerWave; ++i) {
                 const int n = nbase + i;
                 if (n >= N) break;
-                load_row<NCH>(wr, We + (int64_t)n * K8, K8, lane);
+                load_row<NCH, kStream>(wr, We + (int64_t)n * K8, K8, lane);
                 const float ta = wave_sum(dot_row<NCH>(xa, wr));
                 const float tb = wave_sum(dot_row<NCH>(xb, wr));
                 if (lane == 0) out[(int64_t)pa * N + n] = ta;
@@ -185,13 +185,13 @@ __global__ __launch_bounds__(kBlock) void grouped_kernel(const uint4* __restrict
             for (int i = 0; i < kGroupedRowsPerWave; ++i) {
                 const int n = nbase + i;
                 if (n >= N) break;
-                load_row<NCH>(wr, We + (int64_t)n * K8, K8, lane);
+                load_row<NCH, kStream>(wr, We + (int64_t)n * K8, K8, lane);
 #pragma unroll 1
                 for (int c0 = 0; c0 < cnt; c0 += 2) {
                     const int pa = g.sorted[seg + c0];
                     const int pb = c0 + 1 < cnt ? g.sorted[seg + c0 + 1] : pa;
-                    load_row<NCH>(xa, x + (int64_t)(pa / topk) * K8, K8, lane);
-                    load_row<NCH>(xb, x + (int64_t)(pb / topk) * K8, K8, lane);
+                    load_row<NCH, kCached>(xa, x + (int64_t)(pa / topk) * K8, K8, lane);
+                    load_row<NCH, kCached>(xb, x + (int64_t)(pb / topk) * K8, K8, lane);
                     const float ta = wave_sum(dot_row<NCH>(xa, wr));
                     const float tb = wave_sum(dot_row<NCH>(xb, wr));
                     if (lane == 0) out[(int64_t)pa * N + n] = ta;

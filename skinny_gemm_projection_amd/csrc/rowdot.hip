@@ -25,12 +25,12 @@ namespace {
 // Lane `lane` loads pieces c*64 + lane (c < nch) of a buffer of `bytes`
 // bytes; pieces past the end read as zero.  `nch` is wave-uniform, so the
 // guards are scalar branches and all loads of a row issue back to back.
-template <int NCH>
+template <int NCH, int POLICY>
 __device__ __forceinline__ void load_pieces(uint4 (&dst)[NCH], rsrc_t r, int nch, int lane) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         dst[c] = make_uint4(0, 0, 0, 0);
-        if (c < nch) dst[c] = load16(r, (uint32_t)(c * kWave + lane) * 16u);
+        if (c < nch) dst[c] = load16<POLICY>(r, (uint32_t)(c * kWave + lane) * 16u);
     }
 }
 
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kBlock) void rowdot_kernel(const uint4* __restrict_
     uint4 xr[M][NCH];
 #pragma unroll
     for (int m = 0; m < M; ++m)
-        load_pieces<NCH>(xr[m], make_rsrc(x + (int64_t)m * K8 + k0, bytes), nch, lane);
+        load_pieces<NCH, kCached>(xr[m], make_rsrc(x + (int64_t)m * K8 + k0, bytes), nch, lane);
 
     for (int n0 = q * R; n0 < N; n0 += waves_per_split * R) {
         uint4 wr[R][NCH];
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kBlock) void rowdot_kernel(const uint4* __restrict_
         for (int r = 0; r < R; ++r) {
             const int n = n0 + r;
             const rsrc_t rs = make_rsrc(W + (int64_t)min(n, N - 1) * K8 + k0, n < N ? bytes : 0u);
-            load_pieces<NCH>(wr[r], rs, nch, lane);
+            load_pieces<NCH, kStream>(wr[r], rs, nch, lane);
         }
         float acc[R][M];
 #pragma unroll
@@ -101,7 +101,7 @@ int next_pow2(int v) {
 
 // Two rows in flight per wave unless that pushes the wave past 256 VGPRs
 // (occupancy below 2 waves per SIMD): (M=2, 16 chunks) and M >= 9.
-constexpr int rows_per_iter(int M, int NCH) { return (M >= 9 || (M == 2 && NCH == 16)) ? 1 : 2; }
+constexpr int rows_per_iter(int M, int NCH) { return (M >= 9 || (M == 2 && NCH > 8)) ? 1 : 2; }
 
 }  // namespace
 
@@ -113,7 +113,10 @@ int rowdot_nch_cap(int M) {
     return 2;
 }
 
-int rowdot_rows_per_iter(int M, int nch) { return rows_per_iter(M, next_pow2(nch < 1 ? 1 : nch)); }
+int rowdot_rows_per_iter(int M, int nch) {
+    const int c = nch < 1 ? 1 : nch;
+    return rows_per_iter(M, M <= 2 ? c : next_pow2(c));
+}
 
 int rowdot_resident_waves(int, int) { return 2048; }  // 256 CUs x 8 waves
 
@@ -143,6 +146,17 @@ static hipError_t launch_mn(int N, int K, int S, int k_chunk, int grid, const vo
 template <int M>
 static hipError_t launch_m(int nch, int N, int K, int S, int k_chunk, int grid, const void* x,
                            const void* W, const Epilogue& ep, hipStream_t stream) {
+    if constexpr (M <= 2) {
+        // The small-matrix path gets an exact chunk count: no guarded loads.
+        switch (nch < 1 ? 1 : nch) {
+#define SG_NCH(c) \
+    case c: return launch_mn<M, c>(N, K, S, k_chunk, grid, x, W, ep, stream);
+            SG_NCH(1) SG_NCH(2) SG_NCH(3) SG_NCH(4) SG_NCH(5) SG_NCH(6) SG_NCH(7) SG_NCH(8)
+            SG_NCH(9) SG_NCH(10) SG_NCH(11) SG_NCH(12) SG_NCH(13) SG_NCH(14) SG_NCH(15) SG_NCH(16)
+#undef SG_NCH
+            default: return hipErrorInvalidValue;
+        }
+    }
     const int NCH = next_pow2(nch < 1 ? 1 : nch);
     switch (NCH) {
         case 1: return launch_mn<M, 1>(N, K, S, k_chunk, grid, x, W, ep, stream);

