@@ -94,6 +94,9 @@ typedef struct {
                          min(K, (s+1)*k_chunk))                             */
     int32_t tile_n;   /* rows of W per workgroup work item                      */
     int32_t grid;     /* workgroups of the main launch                          */
+    int32_t two_pass; /* 1: the S partials go through the workspace to a second,
+                         reduction kernel; 0: they are added inside the main
+                         kernel (S waves of one workgroup), or S == 1        */
     size_t workspace_bytes; /* device workspace the call needs (0 if none)      */
 } sg_plan;
 
@@ -106,19 +109,24 @@ typedef struct {
  * Limits: 0 <= N <= 1<<20, 0 <= K <= 1<<20 (else SG_ERR_SHAPE). */
 sg_status skinny_gemm_plan(int32_t M, int32_t N, int32_t K, sg_plan* out);
 
-/* Same, but with the kernel and split factor chosen by the caller (sweeps
- * and tests).  split_k <= 0 lets the library choose.  SG_ERR_PLAN when the
- * kernel cannot run this shape (GEMV with M > 2, VALU split-K with M > 15 or
- * with a chunk whose x rows do not fit its registers) or split_k > 64.  A
- * forced split may leave trailing chunks empty; their partials are 0. */
+/* Same, but with the kernel, split factor and reduction mode chosen by the
+ * caller (sweeps and tests).  kernel <= 0 and split_k <= 0 let the library
+ * choose; two_pass: 0 reduce inside the main kernel, 1 second-pass
+ * reduction through the workspace, < 0 let the library choose.  SG_ERR_PLAN
+ * when the kernel cannot run this shape (GEMV with M > 2, VALU split-K with
+ * M > 15 or with a chunk whose x rows do not fit its registers), when the
+ * split cannot be reduced in the requested mode, or split_k > 64.  A forced
+ * split may leave trailing chunks empty; their partials are 0. */
 sg_status skinny_gemm_plan_force(int32_t M, int32_t N, int32_t K, int32_t kernel,
-                                 int32_t split_k, sg_plan* out);
+                                 int32_t split_k, int32_t two_pass, sg_plan* out);
 
 /* y = x W^T ([P] Method details §1).  Writes y_f32 [M,N] (fp32) and/or
  * y_bf16 [M,N] (the same fp32 value rounded to nearest even); at least one
  * must be non-NULL.  workspace: at least plan->workspace_bytes bytes, may be
- * NULL when that is 0; the split-K partial sums P[S,M,N] (fp32) occupy its
- * first S*M*N*4 bytes.  Output buffers must not overlap the inputs. */
+ * NULL when that is 0; in two-pass plans the split-K partial sums P[S,M,N]
+ * (fp32) occupy its first S*M*N*4 bytes.  Split partials are always added
+ * in ascending split order in fp32, without atomics: repeated calls give
+ * identical bits.  Output buffers must not overlap the inputs. */
 sg_status skinny_gemm(const sg_plan* plan, const sg_bf16* x, const sg_bf16* W,
                       float* y_f32, sg_bf16* y_bf16,
                       void* workspace, size_t workspace_bytes, void* stream);

@@ -91,10 +91,12 @@ def skinny_gemm_plan(M: int, N: int, K: int) -> SgPlan:
     return plan
 
 
-def skinny_gemm_plan_force(M: int, N: int, K: int, kernel: int, split_k: int = 0) -> SgPlan:
-    """plan with the kernel (SG_KERNEL_*) and split factor chosen by the caller."""
+def skinny_gemm_plan_force(M: int, N: int, K: int, kernel: int, split_k: int = 0,
+                           two_pass: int = -1) -> SgPlan:
+    """plan with the kernel (SG_KERNEL_*), split factor and reduction mode
+    (0 in-kernel, 1 second pass, -1 library's choice) chosen by the caller."""
     plan = SgPlan()
-    _lib.check(_c().skinny_gemm_plan_force(M, N, K, kernel, split_k, ctypes.byref(plan)))
+    _lib.check(_c().skinny_gemm_plan_force(M, N, K, kernel, split_k, two_pass, ctypes.byref(plan)))
     return plan
 
 

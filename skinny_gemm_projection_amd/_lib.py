@@ -33,7 +33,8 @@ class SgPlan(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
                 ("kernel", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("k_chunk", ctypes.c_int32), ("tile_n", ctypes.c_int32),
-                ("grid", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+                ("grid", ctypes.c_int32), ("two_pass", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -67,7 +68,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     i32, p, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
     P = ctypes.POINTER(SgPlan)
     lib.skinny_gemm_plan.argtypes = [i32, i32, i32, P]
-    lib.skinny_gemm_plan_force.argtypes = [i32, i32, i32, i32, i32, P]
+    lib.skinny_gemm_plan_force.argtypes = [i32, i32, i32, i32, i32, i32, P]
     lib.skinny_gemm.argtypes = [P, p, p, p, p, p, sz, p]
     lib.skinny_gemm_residual.argtypes = [P, p, p, p, p, p, p, sz, p]
     lib.grouped_skinny_gemm_workspace.argtypes = [i32, i32, i32, i32, i32]

@@ -68,7 +68,7 @@ sg_status projection(const sg_plan* p, const sg_bf16* x, const sg_bf16* W, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // start from a clean error state
     const sg::Epilogue fin{nullptr, y_f32, y_bf16, r};
-    const bool split = p->split_k > 1;
+    const bool split = p->two_pass != 0;
     const sg::Epilogue main_ep =
         split ? sg::Epilogue{static_cast<float*>(ws), nullptr, nullptr, nullptr} : fin;
 
@@ -76,7 +76,8 @@ sg_status projection(const sg_plan* p, const sg_bf16* x, const sg_bf16* W, const
     if (p->kernel == SG_KERNEL_SPLITK_MFMA)
         err = sg::launch_splitk_mfma(p->M, p->N, p->K, p->split_k, p->k_chunk, x, W, main_ep, s);
     else
-        err = sg::launch_rowdot(p->M, p->N, p->K, p->split_k, p->k_chunk, p->grid, x, W, main_ep, s);
+        err = sg::launch_rowdot(p->M, p->N, p->K, p->split_k, p->k_chunk, p->grid, split, x, W,
+                                main_ep, s);
     if (err != hipSuccess) return SG_ERR_HIP;
     count(p->kernel);
     if (split) {
@@ -89,7 +90,8 @@ sg_status projection(const sg_plan* p, const sg_bf16* x, const sg_bf16* W, const
         std::fprintf(stderr,
                      "[skinny_gemm] M=%d N=%d K=%d kernel=%s split_k=%d k_chunk=%d grid=%d%s%s\n",
                      p->M, p->N, p->K, kernel_name(p->kernel), p->split_k, p->k_chunk, p->grid,
-                     split ? " +reduce" : "", residual ? " residual" : "");
+                     split ? " +reduce pass" : (p->split_k > 1 ? " in-workgroup reduce" : ""),
+                     residual ? " residual" : "");
     return SG_OK;
 }
 

@@ -18,12 +18,19 @@ int rowdot_rows_per_iter(int M, int nch);
 // Wavefront slots the row-streaming kernel aims to keep resident.
 int rowdot_resident_waves(int M, int nch);
 
-// Row-streaming VALU kernel (small-matrix path and VALU split-K partials).
+// Whether an S-way split can be reduced inside one workgroup (a team of S
+// waves) by the row-streaming kernel at batch size M.
+bool rowdot_team_split_ok(int M, int S);
+int rowdot_block_threads(int S, bool two_pass);
+
+// Row-streaming VALU kernel (small-matrix path and VALU split-K).
 // x [M, K], W [N, K]; split s covers pieces [s*chunk8, min(K8, (s+1)*chunk8)).
-hipError_t launch_rowdot(int M, int N, int K, int S, int k_chunk, int grid,
+// two_pass: write split partials to ep.partial ([S, M, N]) instead of
+// reducing them inside the workgroup.
+hipError_t launch_rowdot(int M, int N, int K, int S, int k_chunk, int grid, bool two_pass,
                          const void* x, const void* W, const Epilogue& ep,
                          hipStream_t stream);
-int rowdot_grid(int M, int N, int K, int S, int k_chunk);
+int rowdot_grid(int M, int N, int K, int S, int k_chunk, bool two_pass);
 
 // bf16 matrix-core split-K kernel (16 <= M <= 64, any M >= 1 when forced).
 constexpr int kMfmaTileN = 64;  // W rows per workgroup (4 waves x 16)

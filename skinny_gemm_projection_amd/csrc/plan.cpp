@@ -48,11 +48,18 @@ bool no_empty_chunk(int32_t K, int32_t S) { return K == 0 || (int64_t)(S - 1) * 
 
 int nch_of(int32_t chunk) { return (chunk + sg::kLaneSpan - 1) / sg::kLaneSpan; }
 
-// Smallest split that keeps the rowdot x registers within the cap for M.
+bool rowdot_fits(int32_t M, int32_t K, int32_t S) {
+    return nch_of(chunk_of(K, S)) <= sg::rowdot_nch_cap(M);
+}
+
+// Smallest split that keeps the rowdot x registers within the cap for M,
+// preferring one a workgroup can reduce by itself (no second pass).
 int32_t rowdot_split(int32_t M, int32_t K) {
-    const int cap = sg::rowdot_nch_cap(M);
+    for (int32_t S = 1; S <= 8; S *= 2)
+        if (sg::rowdot_team_split_ok(M, S) && no_empty_chunk(K, S) && rowdot_fits(M, K, S))
+            return S;
     for (int32_t S = 1; S <= kMaxSplit; ++S)
-        if (no_empty_chunk(K, S) && nch_of(chunk_of(K, S)) <= cap) return S;
+        if (no_empty_chunk(K, S) && rowdot_fits(M, K, S)) return S;
     return -1;
 }
 
@@ -78,7 +85,7 @@ int32_t tuned_split(int32_t M, int32_t N, int32_t K) {
 namespace sg {
 
 sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t split_k,
-                    sg_plan* out) {
+                    int32_t two_pass, sg_plan* out) {
     if (!out) return SG_ERR_NULL;
     if (M < 0 || N < 0 || K < 0 || N > kMaxNK || K > kMaxNK) return SG_ERR_SHAPE;
     if (M > SG_MAX_M) return SG_ERR_UNSUPPORTED;
@@ -93,6 +100,7 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
         p.kernel = SG_KERNEL_NONE;
         p.split_k = 1;
         p.k_chunk = K;
+        p.two_pass = 0;
         *out = p;
         return SG_OK;
     }
@@ -110,16 +118,23 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
             if (M > 15) return SG_ERR_PLAN;
             if (split_k <= 0) split_k = rowdot_split(M, K);
             if (!split_ok(split_k)) return SG_ERR_PLAN;
-            if (nch_of(chunk_of(K, split_k)) > rowdot_nch_cap(M)) return SG_ERR_PLAN;
+            if (!rowdot_fits(M, K, split_k)) return SG_ERR_PLAN;
+            const bool team_ok = rowdot_team_split_ok(M, split_k);
+            if (two_pass < 0) two_pass = (split_k > 1 && !team_ok) ? 1 : 0;
+            if (two_pass == 0 && !team_ok) return SG_ERR_PLAN;
+            if (split_k == 1) two_pass = 0;
             p.k_chunk = chunk_of(K, split_k);
             const int R = rowdot_rows_per_iter(M, nch_of(p.k_chunk));
-            p.tile_n = R * kWavesPerBlock;
-            p.grid = rowdot_grid(M, N, K, split_k, p.k_chunk);
+            p.tile_n = R;
+            p.grid = rowdot_grid(M, N, K, split_k, p.k_chunk, two_pass != 0);
             break;
         }
         case SG_KERNEL_SPLITK_MFMA: {
             if (split_k <= 0) split_k = mfma_split(N, K);
             if (!split_ok(split_k)) return SG_ERR_PLAN;
+            // partials of a multi-workgroup split always take the second pass
+            if (two_pass == 0 && split_k > 1) return SG_ERR_PLAN;
+            two_pass = split_k > 1 ? 1 : 0;
             p.k_chunk = chunk_of(K, split_k);
             p.tile_n = kMfmaTileN;
             p.grid = ((N + kMfmaTileN - 1) / kMfmaTileN) * split_k;
@@ -130,27 +145,30 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
     }
     p.kernel = kernel;
     p.split_k = split_k;
+    p.two_pass = two_pass;
     p.workspace_bytes =
-        split_k > 1 ? ((size_t)split_k * M * N * sizeof(float) + 255) / 256 * 256 : 0;
+        two_pass ? ((size_t)split_k * M * N * sizeof(float) + 255) / 256 * 256 : 0;
     *out = p;
     return SG_OK;
 }
 
 bool plan_matches(const sg_plan* p) {
     sg_plan q;
-    if (make_plan(p->M, p->N, p->K, p->kernel, p->split_k, &q) != SG_OK) return false;
+    if (make_plan(p->M, p->N, p->K, p->kernel, p->split_k, p->two_pass, &q) != SG_OK)
+        return false;
     return q.kernel == p->kernel && q.split_k == p->split_k && q.k_chunk == p->k_chunk &&
-           q.tile_n == p->tile_n && q.grid == p->grid && q.workspace_bytes == p->workspace_bytes;
+           q.tile_n == p->tile_n && q.grid == p->grid && q.two_pass == p->two_pass &&
+           q.workspace_bytes == p->workspace_bytes;
 }
 
 }  // namespace sg
 
 extern "C" sg_status skinny_gemm_plan(int32_t M, int32_t N, int32_t K, sg_plan* out) {
-    return sg::make_plan(M, N, K, 0, 0, out);
+    return sg::make_plan(M, N, K, 0, 0, -1, out);
 }
 
 extern "C" sg_status skinny_gemm_plan_force(int32_t M, int32_t N, int32_t K, int32_t kernel,
-                                            int32_t split_k, sg_plan* out) {
-    if (kernel <= 0) return sg::make_plan(M, N, K, 0, split_k, out);
-    return sg::make_plan(M, N, K, kernel, split_k, out);
+                                            int32_t split_k, int32_t two_pass, sg_plan* out) {
+    return sg::make_plan(M, N, K, kernel <= 0 ? 0 : kernel, split_k, two_pass < 0 ? -1 : two_pass,
+                         out);
 }

@@ -1,93 +1,189 @@
 // rowdot.hip -- row-streaming vector-ALU projection kernel for gfx950.
 //
 // Serves the small-matrix path (M <= 2, "Hyper Optimizing Kimi K3 in vLLM"
-// deepnotes page, Method details §1: a dedicated kernel at batch 1-2) and the
-// split-K partials for 3 <= M <= 15 (same section: the accumulation dimension
-// is spread over more compute units), where the batch is too small for a
+// deepnotes page, Method details §1: a dedicated kernel at batch 1-2) and
+// split-K for 3 <= M <= 15 (same section: the accumulation dimension is
+// spread over more compute units), where the batch is too small for a
 // matrix-core tile to be a real dense contraction.
 //
-// Mapping (MI355X, wave64): one wavefront owns one K chunk of whole W rows.
-// Lane l reads the 16-byte pieces c*64 + l (c = 0..nch-1) of the chunk, so
-// every load instruction of the wave covers 1 KB of contiguous weights and a
-// row's chunk is fully in flight after nch instructions.  The matching x
-// pieces for all M activation rows stay in registers for the wave's whole
-// life; each weight byte is fetched from HBM exactly once.  A lane multiplies
-// its pieces with v_dot2c_f32_bf16 (exact bf16 products, fp32 accumulation),
-// and the 64 lane partials of a row are summed with DPP row steps plus four
-// cross-row reads.  Waves stride over rows R at a time, persistent-style,
-// with the grid sized to the resident wave slots of the chip.
+// Mapping (MI355X, wave64).  A wave owns one K chunk of whole W rows: lane l
+// reads the 16-byte pieces c*64 + l (c < nch) of the chunk, so each load
+// instruction covers 1 KB of contiguous weights; loads are raw buffer loads
+// with the non-temporal hint (ragged tails read zero in hardware).  The
+// matching x pieces of all M activation rows stay in registers for the
+// wave's life, so each weight byte is fetched from HBM exactly once.  Lanes
+// multiply with v_dot2c_f32_bf16 (exact bf16 products, fp32 sums).
+//
+// The R*M lane partials of one iteration are reduced together by a
+// reduce-scatter: v_permlane32_swap and v_permlane16_swap halve the set
+// twice and four DPP steps finish inside 16-lane rows -- about 2.5 VALU ops
+// per output instead of 11 for one full reduction per output.
+//
+// Split-K inside a workgroup.  S waves form a team: they take the same rows,
+// each its own K chunk, and after each iteration the S partial sums of every
+// output are added in LDS in ascending chunk order (a fixed order: identical
+// bits on every run) by the team's first wave, which then runs the epilogue.
+// Teams stride over row groups persistent-style, the grid sized to the
+// chip's resident wave slots.  A plan may instead send the S partials
+// through a workspace to the separate reduction kernel (two-pass mode).
 #include "launch.h"
 
 namespace sg {
 
 namespace {
 
-// Lane `lane` loads pieces c*64 + lane (c < nch) of a buffer of `bytes`
-// bytes; pieces past the end read as zero.  `nch` is wave-uniform, so the
-// guards are scalar branches and all loads of a row issue back to back.
-template <int NCH, int POLICY>
+template <int NCH, int POLICY, bool GUARD>
 __device__ __forceinline__ void load_pieces(uint4 (&dst)[NCH], rsrc_t r, int nch, int lane) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-        dst[c] = make_uint4(0, 0, 0, 0);
-        if (c < nch) dst[c] = load16<POLICY>(r, (uint32_t)(c * kWave + lane) * 16u);
+        if (!GUARD) {
+            dst[c] = load16<POLICY>(r, (uint32_t)(c * kWave + lane) * 16u);
+        } else {
+            dst[c] = make_uint4(0, 0, 0, 0);
+            if (c < nch) dst[c] = load16<POLICY>(r, (uint32_t)(c * kWave + lane) * 16u);
+        }
     }
 }
 
-template <int M, int NCH, int R>
-__global__ __launch_bounds__(kBlock) void rowdot_kernel(const uint4* __restrict__ x,
-                                                        const uint4* __restrict__ W, int N,
-                                                        int K8, int S, int chunk8,
-                                                        int waves_per_split, Epilogue ep) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = blockIdx.x * kWavesPerBlock + wave_id_in_block();
-    const int s = wave % S;
-    const int q = wave / S;
-    if (q >= waves_per_split) return;
+__device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
 
-    const int k0 = s * chunk8;                     // first piece of this chunk
-    const int len = max(0, min(K8 - k0, chunk8));  // pieces in the chunk
-    const int nch = (len + kWave - 1) / kWave;     // lane-pieces per row
+// Sum of v over the 16 lanes of its DPP row; every lane of the row gets it.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x140>(v);  // row_mirror
+    return v;
+}
+
+// Reduce-scatter of V values (V % 4 == 0) over the 64 lanes of a wave.
+// Returns, in lane q*16 + i (i < V/4), the wave-wide sum of value
+// q*V/4 + i; other lanes return a value of no meaning.
+template <int V>
+__device__ __forceinline__ float reduce_scatter(const float (&a)[V], int lane) {
+    static_assert(V % 4 == 0, "pad V to a multiple of 4");
+    constexpr int H = V / 2, Q = V / 4;
+    float b[H];
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+        // lanes 0-31 keep value j summed over lanes l and l+32, lanes 32-63 value j+H
+        const auto p = __builtin_amdgcn_permlane32_swap(as_u(a[j]), as_u(a[j + H]), false, false);
+        b[j] = as_f(p[0]) + as_f(p[1]);
+    }
+    float c[Q];
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+        // rows 0 and 2 keep b[j], rows 1 and 3 keep b[j+Q], each summed over a row pair
+        const auto p = __builtin_amdgcn_permlane16_swap(as_u(b[j]), as_u(b[j + Q]), false, false);
+        c[j] = row16_sum(as_f(p[0]) + as_f(p[1]));
+    }
+    const int i = lane & 15;
+    float out = c[0];
+#pragma unroll
+    for (int j = 1; j < Q; ++j) out = (i == j) ? c[j] : out;
+    return out;
+}
+
+// Value index held by a lane after reduce_scatter<V>, or -1.
+template <int V>
+__device__ __forceinline__ int scatter_index(int lane) {
+    constexpr int Q = V / 4;
+    const int i = lane & 15;
+    return i < Q ? (lane >> 4) * Q + i : -1;
+}
+
+constexpr int pad4(int v) { return (v + 3) / 4 * 4; }
+constexpr int block_waves(int S) { return S > kWavesPerBlock ? S : kWavesPerBlock; }
+
+template <int M, int NCH, int R, int S, bool GUARD, bool TWO_PASS>
+__global__ __launch_bounds__(kWave * block_waves(S)) void rowdot_kernel(
+    const uint4* __restrict__ x, const uint4* __restrict__ W, int N, int K8, int splits,
+    int chunk8, int iters, Epilogue ep) {
+    // Teams of S waves (S == 1 in two-pass mode, where a wave's chunk comes
+    // from its global index instead).
+    constexpr int kWaves = block_waves(S);
+    constexpr int kTeams = kWaves / S;
+    constexpr int V = pad4(R * M);
+    __shared__ float red[2][kTeams][S][V];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wib = wave_id_in_block();
+    const int team_in_block = wib / S;
+    const int member = wib % S;
+    int chunk, team, teams;
+    if (TWO_PASS) {
+        const int wave = blockIdx.x * kWaves + wib;
+        chunk = wave % splits;
+        team = wave / splits;
+        teams = (gridDim.x * kWaves) / splits;
+        if (team >= teams) return;  // remainder waves; this mode has no barriers
+    } else {
+        chunk = member;
+        team = blockIdx.x * kTeams + team_in_block;
+        teams = gridDim.x * kTeams;
+    }
+
+    const int k0 = chunk * chunk8;
+    const int len = max(0, min(K8 - k0, chunk8));
+    const int nch = (len + kWave - 1) / kWave;
     const uint32_t bytes = (uint32_t)len * 16u;
 
     uint4 xr[M][NCH];
 #pragma unroll
     for (int m = 0; m < M; ++m)
-        load_pieces<NCH, kCached>(xr[m], make_rsrc(x + (int64_t)m * K8 + k0, bytes), nch, lane);
+        load_pieces<NCH, kCached, GUARD>(xr[m], make_rsrc(x + (int64_t)m * K8 + k0, bytes), nch,
+                                         lane);
 
-    for (int n0 = q * R; n0 < N; n0 += waves_per_split * R) {
-        uint4 wr[R][NCH];
+    const int groups = (N + R - 1) / R;
+    // Every wave of a block runs the same number of iterations (the team
+    // barrier below needs it); a group past the end contributes nothing.
+    for (int it = 0; it < iters; ++it) {
+        const int g = team + it * teams;
+        const int n0 = g * R;
+        float acc[V];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int n = n0 + r;
-            const rsrc_t rs = make_rsrc(W + (int64_t)min(n, N - 1) * K8 + k0, n < N ? bytes : 0u);
-            load_pieces<NCH, kStream>(wr[r], rs, nch, lane);
-        }
-        float acc[R][M];
+        for (int v = 0; v < V; ++v) acc[v] = 0.0f;
+        if (g < groups) {
+            uint4 wr[R][NCH];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float a = 0.0f;
-#pragma unroll
-                for (int c = 0; c < NCH; ++c)
-                    if (c < nch) a = dot8(xr[m][c], wr[r][c], a);
-                acc[r][m] = wave_sum(a);
+            for (int r = 0; r < R; ++r) {
+                const int n = n0 + r;
+                const rsrc_t rs =
+                    make_rsrc(W + (int64_t)min(n, N - 1) * K8 + k0, n < N ? bytes : 0u);
+                load_pieces<NCH, kStream, GUARD>(wr[r], rs, nch, lane);
             }
-        }
-        // Lane r*M + m stores output (m, n0 + r); the totals are wave-uniform.
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int n = n0 + r;
-            if (n >= N) break;
+            for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                if (lane == r * M + m) {
-                    if (ep.partial)
-                        ep.partial[((int64_t)s * M + m) * N + n] = acc[r][m];
-                    else
-                        store_final(ep, (int64_t)m * N + n, acc[r][m]);
+                for (int m = 0; m < M; ++m) {
+                    float a = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c) a = dot8(xr[m][c], wr[r][c], a);
+                    acc[r * M + m] = a;
                 }
+        }
+        const float total = reduce_scatter<V>(acc, lane);
+        const int v = scatter_index<V>(lane);
+        const bool mine = v >= 0 && v < R * M;
+        const int r = mine ? v / M : 0;
+        const int m = mine ? v - r * M : 0;
+        const int n = n0 + r;
+        const bool live = mine && g < groups && n < N;
+        if (TWO_PASS) {
+            if (live) ep.partial[((int64_t)chunk * M + m) * N + n] = total;
+        } else if (S == 1) {
+            if (live) store_final(ep, (int64_t)m * N + n, total);
+        } else {
+            // Team reduction in LDS: the S chunk partials added in ascending order.
+            const int buf = it & 1;
+            if (mine) red[buf][team_in_block][member][v] = total;
+            __syncthreads();
+            if (member == 0 && live) {
+                float sum = red[buf][team_in_block][0][v];
+#pragma unroll
+                for (int s = 1; s < S; ++s) sum += red[buf][team_in_block][s][v];
+                store_final(ep, (int64_t)m * N + n, sum);
             }
         }
     }
@@ -99,9 +195,9 @@ int next_pow2(int v) {
     return p;
 }
 
-// Two rows in flight per wave unless that pushes the wave past 256 VGPRs
-// (occupancy below 2 waves per SIMD): (M=2, 16 chunks) and M >= 9.
-constexpr int rows_per_iter(int M, int NCH) { return (M >= 9 || (M == 2 && NCH > 8)) ? 1 : 2; }
+// Two rows in flight per wave, except M=2 with more than 8 chunks, where the
+// second row's registers would cut occupancy below 3 waves per SIMD.
+constexpr int rows_per_iter(int M, int NCH) { return (M == 2 && NCH > 8) ? 1 : 2; }
 
 }  // namespace
 
@@ -118,71 +214,123 @@ int rowdot_rows_per_iter(int M, int nch) {
     return rows_per_iter(M, M <= 2 ? c : next_pow2(c));
 }
 
-int rowdot_resident_waves(int, int) { return 2048; }  // 256 CUs x 8 waves
+bool rowdot_team_split_ok(int M, int S) { return S == 1 || S == 2 || S == 4 || (S == 8 && M >= 5); }
 
-int rowdot_grid(int M, int N, int K, int S, int k_chunk) {
-    const int nch = (k_chunk + kLaneSpan - 1) / kLaneSpan;
-    const int R = rowdot_rows_per_iter(M, nch);
-    const int want = (N + R - 1) / R;
-    const int cap = (rowdot_resident_waves(M, nch) + S - 1) / S;
-    const int Q = want < cap ? want : cap;
-    (void)K;
-    return (S * Q + kWavesPerBlock - 1) / kWavesPerBlock;
+int rowdot_block_threads(int S, bool two_pass) {
+    return kWave * (two_pass ? kWavesPerBlock : block_waves(S));
 }
 
-template <int M, int NCH>
-static hipError_t launch_mn(int N, int K, int S, int k_chunk, int grid, const void* x,
-                            const void* W, const Epilogue& ep, hipStream_t stream) {
+int rowdot_resident_waves(int, int) { return 2048; }  // 256 CUs x 8 waves
+
+int rowdot_grid(int M, int N, int K, int S, int k_chunk, bool two_pass) {
+    (void)K;
+    const int nch = (k_chunk + kLaneSpan - 1) / kLaneSpan;
+    const int R = rowdot_rows_per_iter(M, nch);
+    const int groups = (N + R - 1) / R;
+    const int resident = rowdot_resident_waves(M, nch);
+    if (two_pass) {
+        const int cap = (resident + S - 1) / S;
+        const int Q = groups < cap ? groups : cap;
+        return (S * Q + kWavesPerBlock - 1) / kWavesPerBlock;
+    }
+    const int teams_per_block = block_waves(S) / S;
+    const int cap_teams = resident / S;
+    const int teams = groups < cap_teams ? groups : cap_teams;
+    return (teams + teams_per_block - 1) / teams_per_block;
+}
+
+template <int M, int NCH, int S, bool GUARD>
+static hipError_t launch_mns(int N, int K, int splits, int k_chunk, int grid, bool two_pass,
+                             const void* x, const void* W, const Epilogue& ep,
+                             hipStream_t stream) {
     const int K8 = K / kPiece;
     const int chunk8 = k_chunk / kPiece;
     constexpr int R = rows_per_iter(M, NCH);
-    const int waves_per_split = (grid * kWavesPerBlock) / S;
-    rowdot_kernel<M, NCH, R><<<grid, kBlock, 0, stream>>>(static_cast<const uint4*>(x),
-                                                         static_cast<const uint4*>(W), N, K8, S,
-                                                         chunk8, waves_per_split, ep);
+    const int groups = (N + R - 1) / R;
+    const uint4* xp = static_cast<const uint4*>(x);
+    const uint4* wp = static_cast<const uint4*>(W);
+    if (two_pass) {
+        const int teams = (grid * kWavesPerBlock) / splits;
+        const int iters = (groups + teams - 1) / teams;
+        rowdot_kernel<M, NCH, R, 1, GUARD, true><<<grid, kWave * kWavesPerBlock, 0, stream>>>(
+            xp, wp, N, K8, splits, chunk8, iters, ep);
+    } else {
+        const int teams = grid * (block_waves(S) / S);
+        const int iters = (groups + teams - 1) / teams;
+        rowdot_kernel<M, NCH, R, S, GUARD, false><<<grid, kWave * block_waves(S), 0, stream>>>(
+            xp, wp, N, K8, S, chunk8, iters, ep);
+    }
     return hipGetLastError();
 }
 
+// Team splits compiled per batch size: up to 8 waves per team (a 512-thread
+// workgroup keeps 256 VGPRs per lane); larger splits use the two-pass mode.
 template <int M>
-static hipError_t launch_m(int nch, int N, int K, int S, int k_chunk, int grid, const void* x,
-                           const void* W, const Epilogue& ep, hipStream_t stream) {
-    if constexpr (M <= 2) {
-        // The small-matrix path gets an exact chunk count: no guarded loads.
-        switch (nch < 1 ? 1 : nch) {
-#define SG_NCH(c) \
-    case c: return launch_mn<M, c>(N, K, S, k_chunk, grid, x, W, ep, stream);
-            SG_NCH(1) SG_NCH(2) SG_NCH(3) SG_NCH(4) SG_NCH(5) SG_NCH(6) SG_NCH(7) SG_NCH(8)
-            SG_NCH(9) SG_NCH(10) SG_NCH(11) SG_NCH(12) SG_NCH(13) SG_NCH(14) SG_NCH(15) SG_NCH(16)
-#undef SG_NCH
-            default: return hipErrorInvalidValue;
-        }
-    }
-    const int NCH = next_pow2(nch < 1 ? 1 : nch);
-    switch (NCH) {
-        case 1: return launch_mn<M, 1>(N, K, S, k_chunk, grid, x, W, ep, stream);
-        case 2: return launch_mn<M, 2>(N, K, S, k_chunk, grid, x, W, ep, stream);
-        case 4:
-            if constexpr (M <= 8) return launch_mn<M, 4>(N, K, S, k_chunk, grid, x, W, ep, stream);
-            break;
+constexpr bool team_split_compiled(int S) {
+    return S == 1 || S == 2 || S == 4 || (S == 8 && M >= 5);
+}
+
+template <int M, int NCH, bool GUARD>
+static hipError_t launch_mn(int N, int K, int S, int k_chunk, int grid, bool two_pass,
+                            const void* x, const void* W, const Epilogue& ep, hipStream_t stream) {
+    if (two_pass)
+        return launch_mns<M, NCH, 1, GUARD>(N, K, S, k_chunk, grid, true, x, W, ep, stream);
+    switch (S) {
+        case 1: return launch_mns<M, NCH, 1, GUARD>(N, K, 1, k_chunk, grid, false, x, W, ep, stream);
+        case 2: return launch_mns<M, NCH, 2, GUARD>(N, K, 2, k_chunk, grid, false, x, W, ep, stream);
+        case 4: return launch_mns<M, NCH, 4, GUARD>(N, K, 4, k_chunk, grid, false, x, W, ep, stream);
         case 8:
-            if constexpr (M <= 4) return launch_mn<M, 8>(N, K, S, k_chunk, grid, x, W, ep, stream);
-            break;
-        case 16:
-            if constexpr (M <= 2) return launch_mn<M, 16>(N, K, S, k_chunk, grid, x, W, ep, stream);
+            if constexpr (team_split_compiled<M>(8))
+                return launch_mns<M, NCH, 8, GUARD>(N, K, 8, k_chunk, grid, false, x, W, ep, stream);
             break;
         default: break;
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_rowdot(int M, int N, int K, int S, int k_chunk, int grid, const void* x,
-                         const void* W, const Epilogue& ep, hipStream_t stream) {
+template <int M>
+static hipError_t launch_m(int nch, int N, int K, int S, int k_chunk, int grid, bool two_pass,
+                           const void* x, const void* W, const Epilogue& ep, hipStream_t stream) {
+    if constexpr (M <= 2) {
+        // The unsplit small-matrix path gets an exact chunk count: no guarded loads.
+        if (!two_pass && S == 1) {
+            switch (nch < 1 ? 1 : nch) {
+#define SG_NCH(c) \
+    case c: return launch_mns<M, c, 1, false>(N, K, 1, k_chunk, grid, false, x, W, ep, stream);
+                SG_NCH(1) SG_NCH(2) SG_NCH(3) SG_NCH(4) SG_NCH(5) SG_NCH(6) SG_NCH(7) SG_NCH(8)
+                SG_NCH(9) SG_NCH(10) SG_NCH(11) SG_NCH(12) SG_NCH(13) SG_NCH(14) SG_NCH(15)
+                SG_NCH(16)
+#undef SG_NCH
+                default: return hipErrorInvalidValue;
+            }
+        }
+    }
+    switch (next_pow2(nch < 1 ? 1 : nch)) {
+        case 1: return launch_mn<M, 1, true>(N, K, S, k_chunk, grid, two_pass, x, W, ep, stream);
+        case 2: return launch_mn<M, 2, true>(N, K, S, k_chunk, grid, two_pass, x, W, ep, stream);
+        case 4:
+            if constexpr (M <= 8)
+                return launch_mn<M, 4, true>(N, K, S, k_chunk, grid, two_pass, x, W, ep, stream);
+            break;
+        case 8:
+            if constexpr (M <= 4)
+                return launch_mn<M, 8, true>(N, K, S, k_chunk, grid, two_pass, x, W, ep, stream);
+            break;
+        case 16:
+            if constexpr (M <= 2)
+                return launch_mn<M, 16, true>(N, K, S, k_chunk, grid, two_pass, x, W, ep, stream);
+            break;
+        default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_rowdot(int M, int N, int K, int S, int k_chunk, int grid, bool two_pass,
+                         const void* x, const void* W, const Epilogue& ep, hipStream_t stream) {
     const int nch = (k_chunk + kLaneSpan - 1) / kLaneSpan;
-    // The waves-per-split count is derived from the grid, which the plan
-    // computed with rowdot_grid; the remainder waves of the last block exit.
     switch (M) {
 #define SG_CASE(m) \
-    case m: return launch_m<m>(nch, N, K, S, k_chunk, grid, x, W, ep, stream);
+    case m: return launch_m<m>(nch, N, K, S, k_chunk, grid, two_pass, x, W, ep, stream);
         SG_CASE(1) SG_CASE(2) SG_CASE(3) SG_CASE(4) SG_CASE(5) SG_CASE(6) SG_CASE(7) SG_CASE(8)
         SG_CASE(9) SG_CASE(10) SG_CASE(11) SG_CASE(12) SG_CASE(13) SG_CASE(14) SG_CASE(15)
 #undef SG_CASE

@@ -98,10 +98,13 @@ def test_plan_invariants(N, K):
         assert S >= 1 and c % 8 == 0
         assert c == 8 * -(-K // (8 * S)), "chunk is ceil(K / S) rounded up to a multiple of 8"
         assert (S - 1) * c < K or K == 0, "no empty chunk in an automatic plan"
-        if S > 1:
+        if p.two_pass:
+            assert S > 1
             assert p.workspace_bytes >= S * M * N * 4 and p.workspace_bytes % 256 == 0
         else:
             assert p.workspace_bytes == 0
+        if p.kernel == sg.SG_KERNEL_SPLITK_VALU and S in (1, 2, 4) and K <= 8192:
+            assert not p.two_pass, "VALU splits of 1, 2, 4 waves reduce inside the workgroup"
         if p.kernel in (sg.SG_KERNEL_GEMV, sg.SG_KERNEL_SPLITK_VALU):
             nch = -(-c // 512)
             cap = 16 if M <= 2 else 8 if M <= 4 else 4 if M <= 8 else 2
@@ -125,9 +128,18 @@ def test_plan_force():
     p = sg.skinny_gemm_plan_force(4, 4096, 7168, F, 3)
     assert p.k_chunk == 2392 and 2 * 2392 < 7168 <= 3 * 2392
     p = sg.skinny_gemm_plan_force(5, 1000, 2056, V, 2)
-    assert p.k_chunk == 1032
+    assert p.k_chunk == 1032 and not p.two_pass and p.workspace_bytes == 0
+    p = sg.skinny_gemm_plan_force(5, 1000, 2056, V, 2, two_pass=1)
+    assert p.two_pass and p.workspace_bytes >= 2 * 5 * 1000 * 4
+    p = sg.skinny_gemm_plan_force(12, 4096, 7168, V, 0)
+    assert p.split_k == 8 and not p.two_pass, "M >= 9 splits 8 ways inside a 512-thread workgroup"
+    p = sg.skinny_gemm_plan_force(4, 4096, 7168, V, 3)
+    assert p.two_pass, "a 3-way split has no in-workgroup form"
+    p = sg.skinny_gemm_plan_force(16, 4096, 7168, F, 1)
+    assert not p.two_pass and p.workspace_bytes == 0
     for args in [(3, 64, 64, G, 1), (16, 64, 64, V, 1), (4, 4096, 7168, F, 65),
-                 (4, 4096, 7168, 9, 1), (8, 4096, 7168, V, 1), (8, 4096, 7168, V, 2)]:
+                 (4, 4096, 7168, 9, 1), (8, 4096, 7168, V, 1), (8, 4096, 7168, V, 2),
+                 (4, 4096, 7168, V, 3, 0), (16, 4096, 7168, F, 4, 0), (3, 4096, 7168, V, 8, 0)]:
         with pytest.raises(sg.SkinnyGemmError) as e:
             sg.skinny_gemm_plan_force(*args)
         assert e.value.status == 6, args
@@ -150,7 +162,8 @@ def _raw():
 def test_projection_errors_return_before_launch():
     c = _raw()
     sg.skinny_gemm_reset_counters()
-    p = sg.skinny_gemm_plan(8, 4096, 7168)  # split-K: needs a workspace
+    p = sg.skinny_gemm_plan(16, 4096, 7168)  # matrix-core split-K, two-pass: needs a workspace
+    assert p.two_pass and p.workspace_bytes > 0
     bp = ctypes.byref(p)
     A = 0x10000  # aligned, never dereferenced
     ws = p.workspace_bytes

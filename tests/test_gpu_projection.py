@@ -51,9 +51,9 @@ def oracle_rows(x, W, rows=None):
     return orc().projection(bits(x), Wb)
 
 
-def plan_or_skip(M, N, K, kernel, S):
+def plan_or_skip(M, N, K, kernel, S, two_pass=-1):
     try:
-        return sg.skinny_gemm_plan_force(M, N, K, kernel, S)
+        return sg.skinny_gemm_plan_force(M, N, K, kernel, S, two_pass)
     except sg.SkinnyGemmError as e:
         assert e.status == 6
         pytest.skip(f"plan rejects kernel {kernel} with S={S} at M={M}, K={K}")
@@ -79,22 +79,23 @@ def test_small_shapes_auto_plan(M, N, K):
     y32, y16, _ = run(plan, x, W)
     d = counters_delta(before, sg.skinny_gemm_get_counters())
     assert d[plan.kernel] == 1, f"planned kernel must run: {d}"
-    assert d[sg.SG_KERNEL_REDUCE] == (1 if plan.split_k > 1 else 0)
+    assert d[sg.SG_KERNEL_REDUCE] == (1 if plan.two_pass else 0)
     y, A = oracle_rows(x, W)
     check_f32(y32, y, A, f"fp32 M={M} N={N} K={K} {plan}")
     check_bf16(y16, y, A, f"bf16 M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 7, 8, 12, 15])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 7, 8, 9, 12, 15])
 @pytest.mark.parametrize("S", [1, 2, 3, 4, 8, 16])
-def test_valu_forced_splits(M, S):
-    N, K = 300, 2112  # K/S multiples of 8 for S in 1,2,3,4,8; 16 -> 132 rejected
-    plan = plan_or_skip(M, N, K, V, S)
-    announce(f"valu forced M={M} S={S}")
+@pytest.mark.parametrize("two_pass", [0, 1])
+def test_valu_forced_splits(M, S, two_pass):
+    N, K = 300, 2112  # 264 pieces of 8: chunk widths 2112, 1056, 704, 528, 264, 136
+    plan = plan_or_skip(M, N, K, V, S, two_pass)
+    announce(f"valu forced M={M} S={S} two_pass={two_pass}")
     x, W = make(M, N, K, 7100 + M)
     y32, _, _ = run(plan, x, W, bf16=False)
     y, A = oracle_rows(x, W)
-    check_f32(y32, y, A, f"VALU M={M} S={S}")
+    check_f32(y32, y, A, f"VALU M={M} S={S} two_pass={two_pass}")
 
 
 @pytest.mark.parametrize("M", [1, 4, 16, 17, 33, 64])
@@ -113,12 +114,14 @@ def test_mfma_forced_splits(M, S):
 # ------------------------------------------------------------------ integer inputs: bit-exact
 
 
-@pytest.mark.parametrize("kernel,M,S", [(G, 1, 1), (G, 2, 1), (G, 2, 2), (V, 3, 2), (V, 4, 2), (V, 8, 4),
-                                        (V, 15, 8), (F, 16, 1), (F, 16, 4), (F, 64, 2), (F, 64, 16),
-                                        (F, 5, 2)])
-def test_integer_inputs_bit_exact(kernel, M, S):
+@pytest.mark.parametrize("kernel,M,S,tp", [(G, 1, 1, 0), (G, 2, 1, 0), (G, 2, 2, 0), (G, 2, 2, 1),
+                                           (V, 3, 2, 0), (V, 4, 2, 1), (V, 8, 4, 0), (V, 8, 4, 1),
+                                           (V, 15, 8, 0), (V, 15, 8, 1), (V, 11, 16, 1),
+                                           (F, 16, 1, 0), (F, 16, 4, 1), (F, 64, 2, 1),
+                                           (F, 64, 16, 1), (F, 5, 2, 1)])
+def test_integer_inputs_bit_exact(kernel, M, S, tp):
     N, K = 520, 8192  # |sums| <= 16 * 8192 < 2^24: every fp32 partial is exact
-    plan = plan_or_skip(M, N, K, kernel, S)
+    plan = plan_or_skip(M, N, K, kernel, S, tp)
     announce(f"integer bit-exact kernel={kernel} M={M} S={S}")
     x = si.integer_bf16((M, K), -4, 4, 8000 + M, DEV)
     W = si.integer_bf16((N, K), -4, 4, 8001 + M, DEV)
@@ -127,7 +130,7 @@ def test_integer_inputs_bit_exact(kernel, M, S):
     y, _ = oracle_rows(x, W)
     check_exact(y32, y, f"fp32 kernel={kernel} M={M} S={S}")
     assert np.array_equal(bits(y16), orc().encode_bf16(y)), "bf16 output bit-exact"
-    if S > 1:  # the fp32 partials in the workspace equal the oracle's chunk sums
+    if plan.two_pass:  # the fp32 partials in the workspace equal the oracle's chunk sums
         P = ws[: S * M * N * 4].view(torch.float32).reshape(S, M, N)
         check_exact(P, orc().splitk_partials(bits(x), bits(W), S), "split-K partials")
     o32, o16, _ = run(plan, x, W, r=r)
@@ -139,11 +142,12 @@ def test_integer_inputs_bit_exact(kernel, M, S):
 # ------------------------------------------------------------------ full workload sizes
 
 
-def _full_case(M, N, K, seed, kernel=None, S=0, rows=256, residual=False, inplace=False):
+def _full_case(M, N, K, seed, kernel=None, S=0, rows=256, residual=False, inplace=False, tp=-1):
     x, W = make(M, N, K, seed)
     r = si.normal_bf16((M, N), 1.0, seed + si.TAG_R, DEV) if residual else None
     r_before = r.clone() if r is not None else None
-    plan = sg.skinny_gemm_plan(M, N, K) if kernel is None else plan_or_skip(M, N, K, kernel, S)
+    plan = (sg.skinny_gemm_plan(M, N, K) if kernel is None
+            else plan_or_skip(M, N, K, kernel, S, tp))
     announce(f"full M={M} N={N} K={K} plan={plan} residual={residual} inplace={inplace}")
     y32, y16, _ = run(plan, x, W, r=r, inplace=inplace)
     sel = sample_rows(N, rows, seed)
@@ -176,7 +180,7 @@ def test_full_small_batch_7168x8192(M):
     assert plan.kernel == G and plan.split_k == 1
 
 
-@pytest.mark.parametrize("M", [4, 8, 16, 32, 64])
+@pytest.mark.parametrize("M", [3, 4, 8, 12, 16, 32, 64])
 def test_full_splitk_sweep_auto(M):
     plan = _full_case(M, 4096, 7168, 3000)
     assert plan.split_k > 1
@@ -184,9 +188,10 @@ def test_full_splitk_sweep_auto(M):
 
 @pytest.mark.parametrize("M", [4, 8, 16, 32, 64])
 @pytest.mark.parametrize("S", [2, 4, 8, 16])
-def test_full_splitk_sweep_forced(M, S):
+@pytest.mark.parametrize("tp", [-1, 1])
+def test_full_splitk_sweep_forced(M, S, tp):
     kernel = V if M < 16 else F
-    _full_case(M, 4096, 7168, 3000, kernel=kernel, S=S, rows=128)
+    _full_case(M, 4096, 7168, 3000, kernel=kernel, S=S, rows=128, tp=tp)
 
 
 @pytest.mark.parametrize("M", [1, 8, 64])
@@ -198,10 +203,11 @@ def test_full_residual_8192x7168(M, inplace):
 # ------------------------------------------------------------------ properties and edge cases
 
 
-@pytest.mark.parametrize("M,kernel,S", [(1, G, 1), (8, V, 4), (64, F, 8)])
-def test_repeat_runs_are_bitwise_identical(M, kernel, S):
+@pytest.mark.parametrize("M,kernel,S,tp", [(1, G, 1, 0), (8, V, 4, 0), (8, V, 4, 1), (12, V, 8, 0),
+                                           (64, F, 8, 1)])
+def test_repeat_runs_are_bitwise_identical(M, kernel, S, tp):
     N, K = 4096, 7168
-    plan = plan_or_skip(M, N, K, kernel, S)
+    plan = plan_or_skip(M, N, K, kernel, S, tp)
     announce(f"determinism M={M} {plan}")
     x, W = make(M, N, K, 5000 + M)
     a32, a16, _ = run(plan, x, W)
@@ -244,7 +250,8 @@ def test_zero_weights_pass_residual_through():
     x, _ = make(M, N, K, 5300)
     W = torch.zeros((N, K), dtype=torch.bfloat16, device=DEV)
     r = si.normal_bf16((M, N), 1.0, 5301, DEV)
-    for plan in (sg.skinny_gemm_plan(M, N, K), sg.skinny_gemm_plan_force(M, N, K, F, 3)):
+    for plan in (sg.skinny_gemm_plan(M, N, K), sg.skinny_gemm_plan_force(M, N, K, F, 3),
+                 sg.skinny_gemm_plan_force(M, N, K, V, 4, 1)):
         announce(f"zero W residual {plan}")
         o32, o16, _ = run(plan, x, W, r=r)
         assert torch.equal(o16, r)
@@ -265,7 +272,7 @@ def test_nan_propagates_to_its_row_only():
 def test_rejected_calls_on_device_buffers():
     M, N, K = 8, 256, 4096
     x, W = make(M, N, K, 5500)
-    plan = sg.skinny_gemm_plan(M, N, K)
+    plan = sg.skinny_gemm_plan_force(M, N, K, V, 2, 1)
     assert plan.workspace_bytes > 16
     y = torch.empty((M, N), device=DEV)
     announce("rejections with device buffers")
