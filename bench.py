@@ -24,7 +24,8 @@ The one JSON line also carries a sweep over the other workloads (batch
 M = 1..64, residual, MoE grouped), the roofline of the dominant kernel, and
 the CPU oracle timed on a bounded sample on this host.
 
-    python bench.py --summarize-pmc DIR     # post-process rocprofv3 --pmc CSVs
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   # rocprofv3 --pmc CSVs -> traffic
+    python bench.py --summarize-trace DIR "COMMAND"       # rocprofv3 kernel stats -> table
 """
 from __future__ import annotations
 
@@ -366,30 +367,93 @@ def read_traffic():
         return None
 
 
-def summarize_pmc(directory: str) -> None:
-    """Turn rocprofv3 --pmc counter_collection CSVs (FETCH_SIZE, WRITE_SIZE) into the
-    per-dispatch figures committed under profiles/ (printed to stdout)."""
+COPY_BYTES = 1 << 30          # the calibration copy reads and writes this many bytes
+COPY_KERNEL_TAG = "MulFunctor"  # torch.mul(src, 1.0, out=dst): a plain element-wise copy
+GEMV_KERNEL_TAGS = ("rowdot_kernel<1, 14,", "rowdot_kernel<2, 14,")
+
+
+def _pmc_dispatches(directory: str) -> list:
+    """(kernel name, counter, grid size, value in KiB) per dispatch, from the rocprofv3
+    counter_collection CSVs under directory."""
     rows = []
     for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
         with open(path) as f:
             rows += list(csv.DictReader(f))
     if not rows:
         raise SystemExit(f"no counter_collection.csv under {directory}")
-    agg = {}
+    per = {}
     for r in rows:
-        name = r.get("Kernel_Name", r.get("Kernel-Name", ""))
-        counter = r.get("Counter_Name", r.get("Counter-Name", ""))
-        val = float(r.get("Counter_Value", r.get("Counter-Value", "0")))
-        disp = r.get("Dispatch_Id", r.get("Dispatch-Id", ""))
-        agg.setdefault((name, counter), {}).setdefault(disp, 0.0)
-        agg[(name, counter)][disp] += val
-    for (name, counter), per in sorted(agg.items()):
-        vals = list(per.values())
-        print(f"{counter} | {name[:90]} | dispatches {len(vals)} | mean KiB/dispatch "
-              f"{sum(vals) / len(vals):.1f}")
+        key = (r["Kernel_Name"], r["Counter_Name"], int(r["Grid_Size"]), r["Dispatch_Id"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return [(name, c, grid, v) for (name, c, grid, _), v in per.items()]
 
 
-def copy_calibration(torch, nbytes=1 << 30, reps=3):
+def summarize_pmc(fetch_dir: str, write_dir: str) -> None:
+    """Print the HBM-traffic summary of the small-matrix kernel (committed under profiles/):
+    FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the same counter reads
+    for the calibration copy of known size."""
+    fetch, write = _pmc_dispatches(fetch_dir), _pmc_dispatches(write_dir)
+
+    def pick(table, counter, tags, largest_grid=False):
+        hits = [(name, grid, v) for name, c, grid, v in table
+                if c == counter and any(t in name for t in tags)]
+        if largest_grid:  # the calibration copy is the largest launch of its kernel
+            top = max(grid for _, grid, _ in hits) if hits else 0
+            hits = [h for h in hits if h[1] == top]
+        if not hits:
+            raise SystemExit(f"no {counter} samples for {tags}")
+        return (sum(v for _, _, v in hits) / len(hits), len(hits),
+                sorted({name[:80] for name, _, _ in hits}))
+
+    cf, _, _ = pick(fetch, "FETCH_SIZE", (COPY_KERNEL_TAG,), largest_grid=True)
+    cw, _, _ = pick(write, "WRITE_SIZE", (COPY_KERNEL_TAG,), largest_grid=True)
+    gf, nf, names = pick(fetch, "FETCH_SIZE", GEMV_KERNEL_TAGS)
+    gw, nw, _ = pick(write, "WRITE_SIZE", GEMV_KERNEL_TAGS)
+    fetch_factor = cf * 1024 / COPY_BYTES
+    write_factor = cw * 1024 / COPY_BYTES
+    traffic = gf * 1024 / fetch_factor + gw * 1024 / write_factor
+    algo = sum(proj_bytes(M, N_MAIN, K_MAIN) for M in M_LIST) / len(M_LIST)
+    print("# HBM traffic of the small-matrix kernel (M=1 and M=2, K=7168, N=8192), per launch")
+    print("# from two rocprofv3 --pmc passes over the benchmark (FETCH_SIZE, then WRITE_SIZE),")
+    print("# each counter scaled by its reading for a 1 GiB element-wise copy (torch.mul, out=).")
+    print("# commands (repository root):")
+    print("#   rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/pmc_fetch -o f -- python bench.py "
+          "--steps 10 --warmup 2 --no-sweep --no-cpu-baseline --copy-calibration")
+    print("#   rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/pmc_write -o w -- python bench.py "
+          "--steps 10 --warmup 2 --no-sweep --no-cpu-baseline --copy-calibration")
+    print("#   python bench.py --summarize-pmc OUT/pmc_fetch OUT/pmc_write")
+    print(f"kernels: {'; '.join(names)}")
+    print(f"kernel_source_sha256: {kernel_source_hash()}")
+    print(f"dispatches_fetch: {nf}")
+    print(f"dispatches_write: {nw}")
+    print(f"copy_fetch_kib_per_dispatch: {cf:.1f}")
+    print(f"copy_write_kib_per_dispatch: {cw:.1f}")
+    print(f"fetch_scale: {fetch_factor:.4f}")
+    print(f"write_scale: {write_factor:.4f}")
+    print(f"gemv_fetch_kib_per_dispatch: {gf:.1f}")
+    print(f"gemv_write_kib_per_dispatch: {gw:.1f}")
+    print(f"traffic_bytes_per_launch: {traffic:.0f}")
+    print(f"algorithmic_bytes_per_launch: {algo:.0f}")
+    print(f"traffic_over_algorithmic: {traffic / algo:.4f}")
+
+
+def summarize_trace(directory: str, command: str) -> None:
+    """Print a per-kernel duration table from a rocprofv3 --kernel-trace --stats run."""
+    paths = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_stats.csv under {directory}")
+    with open(paths[0]) as f:
+        rows = list(csv.DictReader(f))
+    print("# rocprofv3 kernel trace, per-kernel durations (us)")
+    print(f"# command (repository root): {command}")
+    print(f"# {'calls':>6} {'avg':>9} {'min':>9} {'max':>9}  kernel")
+    for r in rows:
+        name = r["Name"]
+        print(f"  {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+              f"{float(r['MaxNs']) / 1e3:9.2f}  {name[:150]}")
+
+
+def copy_calibration(torch, nbytes=COPY_BYTES, reps=3):
     """A plain element-wise copy of known size (reads nbytes, writes nbytes) for scaling
     the FETCH_SIZE / WRITE_SIZE counters."""
     src = torch.ones(nbytes // 4, device="cuda")
@@ -411,11 +475,15 @@ def main() -> None:
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "COMMAND"))
     args = ap.parse_args()
 
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc)
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

@@ -73,8 +73,10 @@ sg_status projection(const sg_plan* p, const sg_bf16* x, const sg_bf16* W, const
         split ? sg::Epilogue{static_cast<float*>(ws), nullptr, nullptr, nullptr} : fin;
 
     hipError_t err;
-    if (p->kernel == SG_KERNEL_SPLITK_MFMA)
+    if (p->kernel == SG_KERNEL_SPLITK_MFMA && p->tile_n == sg::kMfmaTileN)
         err = sg::launch_splitk_mfma(p->M, p->N, p->K, p->split_k, p->k_chunk, x, W, main_ep, s);
+    else if (p->kernel == SG_KERNEL_SPLITK_MFMA)
+        err = sg::launch_mfma_team(p->M, p->N, p->K, p->split_k, p->k_chunk, x, W, main_ep, s);
     else
         err = sg::launch_rowdot(p->M, p->N, p->K, p->split_k, p->k_chunk, p->grid, split, x, W,
                                 main_ep, s);

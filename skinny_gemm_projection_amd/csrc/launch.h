@@ -32,8 +32,19 @@ hipError_t launch_rowdot(int M, int N, int K, int S, int k_chunk, int grid, bool
                          hipStream_t stream);
 int rowdot_grid(int M, int N, int K, int S, int k_chunk, bool two_pass);
 
-// bf16 matrix-core split-K kernel (16 <= M <= 64, any M >= 1 when forced).
-constexpr int kMfmaTileN = 64;  // W rows per workgroup (4 waves x 16)
+// bf16 matrix-core split-K (16 <= M <= 64, any M >= 1 when forced).
+// Team kernel: S waves (S in {1,2,4,8}) of one workgroup split K over a
+// 16-row tile and add their partials in LDS; grid ceil(N/16).
+constexpr int kMfmaTeamTileN = 16;
+bool mfma_team_split_ok(int S);
+hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void* x,
+                            const void* W, const Epilogue& ep, hipStream_t stream);
+// Chunk kernel: workgroups of 128 rows x one K chunk with the x chunk
+// staged in LDS; partials to ep.partial ([S, M, N]) for the reduction kernel
+// when S > 1; grid (ceil(N/128), S).
+constexpr int kMfmaTileN = 128;  // W rows per workgroup (8 waves x 16)
+constexpr size_t kMfmaMaxLds = 160 * 1024;
+size_t mfma_chunk_lds_bytes(int M, int k_chunk);
 hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk,
                               const void* x, const void* W, const Epilogue& ep,
                               hipStream_t stream);

@@ -63,11 +63,18 @@ int32_t rowdot_split(int32_t M, int32_t K) {
     return -1;
 }
 
-int32_t mfma_split(int32_t N, int32_t K) {
+bool mfma_chunk_fits(int32_t M, int32_t K, int32_t S) {
+    return sg::mfma_chunk_lds_bytes(M, chunk_of(K, S)) <= sg::kMfmaMaxLds;
+}
+
+// Split for the matrix-core chunk kernel: the smallest S whose x chunk fits
+// in LDS and whose ceil(N/128) x S workgroups cover the 256 compute units.
+int32_t mfma_split(int32_t M, int32_t N, int32_t K) {
     const int64_t tiles = (N + sg::kMfmaTileN - 1) / sg::kMfmaTileN;
-    int32_t best = 1;
-    for (int32_t S = 1; S <= 16; ++S) {
+    int32_t best = -1;
+    for (int32_t S = 1; S <= kMaxSplit; ++S) {
         if (!no_empty_chunk(K, S)) break;
+        if (!mfma_chunk_fits(M, K, S)) continue;
         best = S;
         if (tiles * S >= kComputeUnits) break;
     }
@@ -130,10 +137,30 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
             break;
         }
         case SG_KERNEL_SPLITK_MFMA: {
-            if (split_k <= 0) split_k = mfma_split(N, K);
+            // Default: the chunk kernel, its S partials summed by the second
+            // pass.  two_pass == 0 asks for the team kernel (S in 1, 2, 4, 8
+            // reduced inside the workgroup).
+            if (two_pass == 0) {
+                if (split_k <= 0) split_k = 8;
+                while (split_k > 1 && !no_empty_chunk(K, split_k)) split_k /= 2;
+                if (!mfma_team_split_ok(split_k)) return SG_ERR_PLAN;
+                p.k_chunk = chunk_of(K, split_k);
+                p.tile_n = kMfmaTeamTileN;
+                p.grid = (N + kMfmaTeamTileN - 1) / kMfmaTeamTileN;
+                two_pass = 0;
+                break;
+            }
+            if (split_k <= 0) split_k = mfma_split(M, N, K);
             if (!split_ok(split_k)) return SG_ERR_PLAN;
-            // partials of a multi-workgroup split always take the second pass
-            if (two_pass == 0 && split_k > 1) return SG_ERR_PLAN;
+            if (!mfma_chunk_fits(M, K, split_k)) {
+                // x chunk too large for LDS: the team kernel, if allowed
+                if (two_pass > 0 || !mfma_team_split_ok(split_k)) return SG_ERR_PLAN;
+                p.k_chunk = chunk_of(K, split_k);
+                p.tile_n = kMfmaTeamTileN;
+                p.grid = (N + kMfmaTeamTileN - 1) / kMfmaTeamTileN;
+                two_pass = 0;
+                break;
+            }
             two_pass = split_k > 1 ? 1 : 0;
             p.k_chunk = chunk_of(K, split_k);
             p.tile_n = kMfmaTileN;
@@ -153,9 +180,12 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
 }
 
 bool plan_matches(const sg_plan* p) {
+    // The matrix-core path has two kernels; the plan's tile width says which
+    // one it was made for (the team kernel is requested with two_pass == 0).
+    int32_t request = p->two_pass;
+    if (p->kernel == SG_KERNEL_SPLITK_MFMA) request = p->tile_n == kMfmaTileN ? 1 : 0;
     sg_plan q;
-    if (make_plan(p->M, p->N, p->K, p->kernel, p->split_k, p->two_pass, &q) != SG_OK)
-        return false;
+    if (make_plan(p->M, p->N, p->K, p->kernel, p->split_k, request, &q) != SG_OK) return false;
     return q.kernel == p->kernel && q.split_k == p->split_k && q.k_chunk == p->k_chunk &&
            q.tile_n == p->tile_n && q.grid == p->grid && q.two_pass == p->two_pass &&
            q.workspace_bytes == p->workspace_bytes;

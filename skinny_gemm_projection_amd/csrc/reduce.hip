@@ -13,24 +13,38 @@ namespace sg {
 
 namespace {
 
+// All S partial loads of a thread are issued before any is added (S <= 64,
+// in batches of 16), so the pass costs about one memory round trip.
 __global__ __launch_bounds__(kBlock) void splitk_reduce_kernel(const float* __restrict__ P, int S,
                                                                int64_t MN, Epilogue ep) {
+    constexpr int kBatch = 16;
     const int64_t i0 = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * 4;
     if (i0 >= MN) return;
-    float acc[4];
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if ((MN & 3) == 0) {
-        float4 a = reinterpret_cast<const float4*>(P + i0)[0];
-        for (int s = 1; s < S; ++s) {
-            const float4 b = reinterpret_cast<const float4*>(P + (int64_t)s * MN + i0)[0];
-            a.x += b.x;
-            a.y += b.y;
-            a.z += b.z;
-            a.w += b.w;
+        for (int s0 = 0; s0 < S; s0 += kBatch) {
+            float4 part[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                if (s0 + j < S)
+                    part[j] = reinterpret_cast<const float4*>(P + (int64_t)(s0 + j) * MN + i0)[0];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (s0 + j < S) {
+                    if (s0 + j == 0) {
+                        acc[0] = part[j].x;
+                        acc[1] = part[j].y;
+                        acc[2] = part[j].z;
+                        acc[3] = part[j].w;
+                    } else {
+                        acc[0] += part[j].x;
+                        acc[1] += part[j].y;
+                        acc[2] += part[j].z;
+                        acc[3] += part[j].w;
+                    }
+                }
+            }
         }
-        acc[0] = a.x;
-        acc[1] = a.y;
-        acc[2] = a.z;
-        acc[3] = a.w;
     } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

@@ -137,9 +137,18 @@ def test_plan_force():
     assert p.two_pass, "a 3-way split has no in-workgroup form"
     p = sg.skinny_gemm_plan_force(16, 4096, 7168, F, 1)
     assert not p.two_pass and p.workspace_bytes == 0
+    p = sg.skinny_gemm_plan(64, 4096, 7168)
+    assert p.split_k == 8 and p.two_pass and p.grid == 32 * 8 and p.tile_n == 128
+    p = sg.skinny_gemm_plan_force(32, 4096, 7168, F, 3)
+    assert p.two_pass and p.grid == 32 * 3
+    p = sg.skinny_gemm_plan_force(64, 4096, 7168, F, 4, 0)
+    assert not p.two_pass and p.tile_n == 16 and p.grid == 256, "team kernel"
+    p = sg.skinny_gemm_plan_force(64, 4096, 7168, F, 2)
+    assert not p.two_pass and p.tile_n == 16, "x chunk too big for LDS: team kernel"
     for args in [(3, 64, 64, G, 1), (16, 64, 64, V, 1), (4, 4096, 7168, F, 65),
                  (4, 4096, 7168, 9, 1), (8, 4096, 7168, V, 1), (8, 4096, 7168, V, 2),
-                 (4, 4096, 7168, V, 3, 0), (16, 4096, 7168, F, 4, 0), (3, 4096, 7168, V, 8, 0)]:
+                 (4, 4096, 7168, V, 3, 0), (16, 4096, 7168, F, 3, 0), (3, 4096, 7168, V, 8, 0),
+                 (16, 4096, 7168, F, 16, 0), (64, 4096, 7168, F, 3, 1)]:
         with pytest.raises(sg.SkinnyGemmError) as e:
             sg.skinny_gemm_plan_force(*args)
         assert e.value.status == 6, args
@@ -162,7 +171,7 @@ def _raw():
 def test_projection_errors_return_before_launch():
     c = _raw()
     sg.skinny_gemm_reset_counters()
-    p = sg.skinny_gemm_plan(16, 4096, 7168)  # matrix-core split-K, two-pass: needs a workspace
+    p = sg.skinny_gemm_plan_force(16, 4096, 7168, sg.SG_KERNEL_SPLITK_MFMA, 4, 1)  # two-pass
     assert p.two_pass and p.workspace_bytes > 0
     bp = ctypes.byref(p)
     A = 0x10000  # aligned, never dereferenced

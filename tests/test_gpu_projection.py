@@ -98,12 +98,13 @@ def test_valu_forced_splits(M, S, two_pass):
     check_f32(y32, y, A, f"VALU M={M} S={S} two_pass={two_pass}")
 
 
-@pytest.mark.parametrize("M", [1, 4, 16, 17, 33, 64])
+@pytest.mark.parametrize("M", [1, 4, 16, 17, 33, 48, 64])
 @pytest.mark.parametrize("S", [1, 2, 3, 4, 8])
-def test_mfma_forced_splits(M, S):
+@pytest.mark.parametrize("two_pass", [0, 1])
+def test_mfma_forced_splits(M, S, two_pass):
     N, K = 200, 2112
-    plan = plan_or_skip(M, N, K, F, S)
-    announce(f"mfma forced M={M} S={S}")
+    plan = plan_or_skip(M, N, K, F, S, two_pass)
+    announce(f"mfma forced M={M} S={S} two_pass={two_pass}")
     x, W = make(M, N, K, 7200 + M)
     y32, y16, _ = run(plan, x, W)
     y, A = oracle_rows(x, W)
@@ -117,8 +118,9 @@ def test_mfma_forced_splits(M, S):
 @pytest.mark.parametrize("kernel,M,S,tp", [(G, 1, 1, 0), (G, 2, 1, 0), (G, 2, 2, 0), (G, 2, 2, 1),
                                            (V, 3, 2, 0), (V, 4, 2, 1), (V, 8, 4, 0), (V, 8, 4, 1),
                                            (V, 15, 8, 0), (V, 15, 8, 1), (V, 11, 16, 1),
-                                           (F, 16, 1, 0), (F, 16, 4, 1), (F, 64, 2, 1),
-                                           (F, 64, 16, 1), (F, 5, 2, 1)])
+                                           (F, 16, 1, 0), (F, 16, 4, 1), (F, 16, 8, 0),
+                                           (F, 64, 2, 1), (F, 64, 8, 0), (F, 64, 16, 1),
+                                           (F, 5, 2, 1), (F, 37, 4, 0)])
 def test_integer_inputs_bit_exact(kernel, M, S, tp):
     N, K = 520, 8192  # |sums| <= 16 * 8192 < 2^24: every fp32 partial is exact
     plan = plan_or_skip(M, N, K, kernel, S, tp)
@@ -204,7 +206,7 @@ def test_full_residual_8192x7168(M, inplace):
 
 
 @pytest.mark.parametrize("M,kernel,S,tp", [(1, G, 1, 0), (8, V, 4, 0), (8, V, 4, 1), (12, V, 8, 0),
-                                           (64, F, 8, 1)])
+                                           (64, F, 8, 1), (64, F, 8, 0)])
 def test_repeat_runs_are_bitwise_identical(M, kernel, S, tp):
     N, K = 4096, 7168
     plan = plan_or_skip(M, N, K, kernel, S, tp)
