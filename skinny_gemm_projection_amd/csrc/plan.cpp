@@ -67,16 +67,26 @@ bool mfma_chunk_fits(int32_t M, int32_t K, int32_t S) {
     return sg::mfma_chunk_lds_bytes(M, chunk_of(K, S)) <= sg::kMfmaMaxLds;
 }
 
-// Split for the matrix-core chunk kernel: the smallest S whose x chunk fits
-// in LDS and whose ceil(N/128) x S workgroups cover the 256 compute units.
+// Split for the matrix-core chunk kernel.  Cost model in bytes per compute
+// unit: the weight bytes of the busiest unit -- ceil(tiles*S / 256) workgroups
+// of 128 rows x K/S each -- plus the partials written and read back
+// (2 * S*M*N*4 bytes spread over the 256 units).  Among the splits whose x
+// chunk fits in LDS, the cheapest wins (ties: the smaller split).
 int32_t mfma_split(int32_t M, int32_t N, int32_t K) {
     const int64_t tiles = (N + sg::kMfmaTileN - 1) / sg::kMfmaTileN;
     int32_t best = -1;
+    int64_t best_cost = 0;
     for (int32_t S = 1; S <= kMaxSplit; ++S) {
         if (!no_empty_chunk(K, S)) break;
         if (!mfma_chunk_fits(M, K, S)) continue;
-        best = S;
-        if (tiles * S >= kComputeUnits) break;
+        const int64_t per_unit = (tiles * S + kComputeUnits - 1) / kComputeUnits;
+        const int64_t w_bytes = per_unit * sg::kMfmaTileN * 2 * (int64_t)chunk_of(K, S);
+        const int64_t p_bytes = 8 * (int64_t)S * M * N / kComputeUnits;
+        const int64_t cost = w_bytes + p_bytes;
+        if (best < 0 || cost < best_cost) {
+            best = S;
+            best_cost = cost;
+        }
     }
     return best;
 }

@@ -7,17 +7,24 @@
 // compute units).
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16: lane (col = lane % 16,
-// grp = lane / 16) supplies 8 consecutive k of one row of each operand, so a
-// 32-wide k step of a 16-row W tile is one 16-byte load per lane (16 rows x
-// 64 contiguous bytes per instruction) and D = A * B leaves lane (col, grp)
-// the outputs (m = 16*mt + 4*grp + v, n = n0 + col), v = 0..3.  M is padded
-// to 16*MT rows of x with zeros.
+// grp = lane / 16) supplies 8 consecutive k of one row of each operand, and
+// D = A * B leaves lane (col, grp) the outputs (m = 16*mt + 4*grp + v,
+// n = n0 + col), v = 0..3.  M is padded to 16*MT rows of x with zeros.  The
+// k order inside a 32-wide step is free (the sum is over k), so A and B only
+// have to agree on which 8 k values each lane group supplies.
 //
-// Two kernels share that inner step:
+// Two kernels:
 //  * chunk kernel (default): a workgroup of 8 waves owns 128 rows of W and
-//    one K chunk; the x chunk is staged in LDS once, then each wave streams
-//    its 16 rows barrier-free.  Partials go to the [S, M, N] workspace and
-//    the deterministic reduction kernel adds them (two-pass split-K).
+//    one K chunk; the x chunk is staged in LDS once.  Loading the B operand
+//    straight from HBM would read 16 rows x 64 bytes per instruction, which
+//    streams about 20% slower than whole 256-byte row segments, so each wave
+//    loads W as 4 rows x 256 bytes per instruction (16 pieces of 16 bytes of
+//    each of its 16 rows per "round"), writes the round to a 4 KB LDS tile
+//    of its own and reads it back in operand layout.  Slot c of row r in the
+//    tile holds piece c ^ r (an XOR swizzle), so the operand read -- 16
+//    different rows at one piece each -- hits 16 different bank groups.
+//    Partials go to the [S, M, N] workspace and the deterministic reduction
+//    kernel adds them (two-pass split-K).
 //  * team kernel: S waves of one workgroup split K over a 16-row tile, read
 //    x straight from L2, and add their S partial tiles in LDS in ascending
 //    split order (no workspace, no second pass).
@@ -28,25 +35,24 @@ namespace sg {
 
 namespace {
 
-// Chunk kernel (two-pass split-K).  A workgroup of 8 waves owns 128 rows of
-// W and one K chunk.  It first stages the x chunk of all M rows (padded to
-// 16*MT) in LDS once -- rows padded by 16 bytes against bank conflicts --
-// then each wave streams its own 16 rows with no further barrier: D k-steps
-// of its B operands stay in flight in a register ring and the A operands come
-// from LDS.  x is read from L2 once per 128 rows.  The W loads use the default
-// cache policy: each instruction covers only half of 16 cache lines (the next
-// k step covers the other half), and for that pattern it measures faster than
-// the streaming (nt) policy.
 constexpr int kChunkWaves = 8;
 constexpr int kChunkRows = 16 * kChunkWaves;
+constexpr int kRoundPieces = 16;                 // pieces of each row per round (4 k steps)
+constexpr int kTileSlots = 16 * kRoundPieces;    // 16 rows x 16 pieces = 4 KB per wave
+constexpr int kXLoadsPerThread = 16;             // x staging loads per thread (LDS bound)
 
-template <int MT, int D>
+// Row pitch (16-byte units) of the staged x chunk: whole rounds plus one, odd,
+// so the 16 rows read by one operand load fall in 16 different bank groups.
+__host__ __device__ inline int x_pitch(int chunk8) {
+    return (chunk8 + kRoundPieces - 1) / kRoundPieces * kRoundPieces + 1;
+}
+
+template <int MT, int DR>
 __global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ W, int M, int N, int K8, int chunk8,
     Epilogue ep) {
-    extern __shared__ uint4 xs[];  // [16*MT][pitch], pitch = round4(chunk8) + 1
-    constexpr uint32_t kOff = 0xFFFFFFF0u;
-    const int pitch = (chunk8 + 3) / 4 * 4 + 1;
+    extern __shared__ uint4 lds[];
+    constexpr uint32_t kOff = 0xFFFFFFF0u;  // past any descriptor range: reads zero
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wv = wave_id_in_block();
@@ -54,63 +60,108 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
     const int grp = lane >> 4;
     const int s = blockIdx.y;
     const int k0 = s * chunk8;
-    const int len = max(0, min(K8 - k0, chunk8));
-    const int lenr = (len + 3) / 4 * 4;  // whole k-steps; pieces past len staged as 0
-
+    const int len = max(0, min(K8 - k0, chunk8));  // pieces of this chunk
+    // whole rounds: x is staged as zeros past len and the weights past len
+    // load as zeros, so every k step of a round runs unconditionally
+    const int lenr = (len + kRoundPieces - 1) / kRoundPieces * kRoundPieces;
+    const int pitch = x_pitch(chunk8);
+    uint4* xs = lds;                                  // [16*MT][pitch]
+    uint4* tile = lds + 16 * MT * pitch + wv * kTileSlots;
 
     const int row0 = blockIdx.x * kChunkRows + wv * 16;
-    const int rows = max(0, min(16, N - row0));
-    const bool n_ok = col < rows;
+    // wave-uniform by construction; readfirstlane keeps the descriptor scalar
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16, N - row0)));
     const rsrc_t wrs = make_rsrc(W + (int64_t)row0 * K8, (uint32_t)rows * (uint32_t)K8 * 16u);
-    const uint32_t w_lane = ((uint32_t)col * K8 + k0 + grp) * 16u;
-    const int steps = (len + 3) / 4;
-
-    uint4 wb[D];
-    auto load_w = [&](int t) {
-        const bool ok = n_ok && (t * 4 + grp < len);
-        return load16<kCached>(wrs, ok ? w_lane + (uint32_t)t * 64u : kOff);
+    // Load i of a round reads row 4i + grp; lane slot col carries piece col ^ row.
+    uint32_t woff[4];
+    int wpiece[4];
+    bool wrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + grp;
+        wpiece[i] = col ^ r;
+        wrow[i] = r < rows;
+        woff[i] = ((uint32_t)r * K8 + k0 + wpiece[i]) * 16u;
+    }
+    auto load_round = [&](int rd, uint4 (&w)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = wrow[i] && (rd * kRoundPieces + wpiece[i] < len);
+            w[i] = load16<kStream>(wrs, ok ? woff[i] + (uint32_t)rd * (kRoundPieces * 16u) : kOff);
+        }
     };
+
+    // x loads go out first (they hit L2 and return early), then the first DR
+    // weight rounds, then the x values are written to LDS: waiting for the x
+    // loads does not wait for the weight stream.
+    const int xtotal = 16 * MT * lenr;
+    const int div = max(lenr, kRoundPieces);
+    const int step_rows = (kWave * kChunkWaves) / div;  // idx += 512 moves this many rows
+    const int step_p = (kWave * kChunkWaves) - step_rows * div;  // ... and this many pieces
+    const rsrc_t xrs = make_rsrc(x, (uint32_t)M * (uint32_t)K8 * 16u);
+    const int nx = (xtotal + kWave * kChunkWaves - 1) / (kWave * kChunkWaves);  // <= 16
+    uint4 xv[kXLoadsPerThread];
+    int xdst[kXLoadsPerThread];  // LDS slot of each staged piece, -1 if none
+    {
+        int row = tid / div;
+        int p = tid - row * div;
+#pragma unroll
+        for (int j = 0; j < kXLoadsPerThread; ++j) {
+            if (j < nx) {  // workgroup-uniform
+                const int idx = tid + j * kWave * kChunkWaves;
+                const bool ok = idx < xtotal && row < M && p < len;
+                xv[j] = load16<kCached>(xrs, ok ? ((uint32_t)row * K8 + k0 + p) * 16u : kOff);
+                xdst[j] = idx < xtotal ? row * pitch + p : -1;
+                row += step_rows;
+                p += step_p;
+                if (p >= div) {
+                    p -= div;
+                    ++row;
+                }
+            }
+        }
+    }
+    uint4 wb[DR][4];
+#pragma unroll
+    for (int d = 0; d < DR; ++d) load_round(d, wb[d]);
+#pragma unroll
+    for (int j = 0; j < kXLoadsPerThread; ++j)
+        if (j < nx && xdst[j] >= 0) xs[xdst[j]] = xv[j];  // zeros past M and len
+    __syncthreads();
+
     f32x4_t acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    // The first D weight steps go out before x is staged, so HBM streaming
-    // starts at once and overlaps the staging.
+    const int rounds = (len + kRoundPieces - 1) / kRoundPieces;
+    for (int r0 = 0; r0 < rounds; r0 += DR) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) wb[d] = load_w(d);
-
-    // Stage x[0..16*MT) x pieces [k0, k0+lenr) into LDS (zeros past M or len).
-    {
-        const rsrc_t xrs = make_rsrc(x, (uint32_t)M * (uint32_t)K8 * 16u);
-        const int total = 16 * MT * lenr;
-        for (int idx = tid; idx < total; idx += kWave * kChunkWaves) {
-            const int row = idx / lenr;
-            const int p = idx - row * lenr;
-            const uint32_t off =
-                (row < M && p < len) ? ((uint32_t)row * K8 + k0 + p) * 16u : kOff;
-            xs[row * pitch + p] = load16<kCached>(xrs, off);
-        }
-    }
-    __syncthreads();
-
-    for (int t0 = 0; t0 < steps; t0 += D) {
+        for (int d = 0; d < DR; ++d) {
+            const int rd = r0 + d;
+            if (rd < rounds) {  // wave-uniform
+                // Within one wave LDS operations run in order, so the tile can
+                // be rewritten right after the previous round's reads.
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int t = t0 + d;
-            const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, wb[d]);
-            if (t < steps) {  // wave-uniform; p < lenr < pitch stays inside the row
-                const int p = t * 4 + grp;
+                for (int i = 0; i < 4; ++i) tile[(4 * i + grp) * kRoundPieces + col] = wb[d][i];
+                __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const uint4 a = xs[(mt * 16 + col) * pitch + p];
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, a), bop, acc[mt], 0, 0, 0);
+                for (int t = 0; t < 4; ++t) {
+                    const uint4 b = tile[col * kRoundPieces + ((4 * t + grp) ^ col)];
+                    const int p = rd * kRoundPieces + 4 * t + grp;  // < lenr < pitch
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const uint4 a = xs[(mt * 16 + col) * pitch + p];
+                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                            acc[mt], 0, 0, 0);
+                    }
                 }
+                __builtin_amdgcn_wave_barrier();
             }
-            wb[d] = load_w(t + D);
+            load_round(rd + DR, wb[d]);  // past the chunk: no memory access
         }
     }
 
-    if (!n_ok) return;
+    if (col >= rows) return;
     const int n = row0 + col;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -252,8 +303,8 @@ hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void*
 
 size_t mfma_chunk_lds_bytes(int M, int k_chunk) {
     const int MT = (M + 15) / 16;
-    const int pitch = (k_chunk / kPiece + 3) / 4 * 4 + 1;
-    return (size_t)16 * MT * pitch * 16;
+    return (size_t)16 * MT * x_pitch(k_chunk / kPiece) * 16 +
+           (size_t)kChunkWaves * kTileSlots * 16;
 }
 
 hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk, const void* x,
@@ -265,14 +316,18 @@ hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk, const voi
     const uint4* wp = static_cast<const uint4*>(W);
     const int MT = (M + 15) / 16;
     const size_t lds = mfma_chunk_lds_bytes(M, k_chunk);
-    constexpr int D = 8;
+    if (lds > kMfmaMaxLds) return hipErrorInvalidValue;
+    // x staging: 16*MT*(pitch - 1) pieces at most over the workgroup's threads
+    if ((size_t)16 * MT * (x_pitch(chunk8) - 1) > (size_t)kXLoadsPerThread * kWave * kChunkWaves)
+        return hipErrorInvalidValue;
+    constexpr int DR = 2;  // weight rounds in flight per wave (8 loads)
 #define SG_CHUNK(mt) \
     if (MT == mt) { \
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&splitk_mfma_kernel<mt, D>), \
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&splitk_mfma_kernel<mt, DR>), \
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
         if (e != hipSuccess) return e; \
-        splitk_mfma_kernel<mt, D><<<grid, kWave * kChunkWaves, lds, stream>>>(xp, wp, M, N, K8, \
-                                                                             chunk8, ep); \
+        splitk_mfma_kernel<mt, DR><<<grid, kWave * kChunkWaves, lds, stream>>>(xp, wp, M, N, K8, \
+                                                                              chunk8, ep); \
         return hipGetLastError(); \
     }
     SG_CHUNK(1) SG_CHUNK(2) SG_CHUNK(3) SG_CHUNK(4)

@@ -139,8 +139,8 @@ def test_plan_force():
     assert not p.two_pass and p.workspace_bytes == 0
     p = sg.skinny_gemm_plan(64, 4096, 7168)
     assert p.split_k == 8 and p.two_pass and p.grid == 32 * 8 and p.tile_n == 128
-    p = sg.skinny_gemm_plan_force(32, 4096, 7168, F, 3)
-    assert p.two_pass and p.grid == 32 * 3
+    p = sg.skinny_gemm_plan_force(32, 4096, 7168, F, 5)
+    assert p.two_pass and p.grid == 32 * 5 and p.tile_n == 128
     p = sg.skinny_gemm_plan_force(64, 4096, 7168, F, 4, 0)
     assert not p.two_pass and p.tile_n == 16 and p.grid == 256, "team kernel"
     p = sg.skinny_gemm_plan_force(64, 4096, 7168, F, 2)
