@@ -83,8 +83,12 @@ sg_status projection(const sg_plan* p, const sg_bf16* x, const sg_bf16* W, const
     if (err != hipSuccess) return SG_ERR_HIP;
     count(p->kernel);
     if (split) {
-        err = sg::launch_reduce(static_cast<const float*>(ws), p->split_k, (int64_t)p->M * p->N,
-                                fin, s);
+        if (p->kernel == SG_KERNEL_SPLITK_MFMA && p->tile_n == sg::kMfmaTileN)
+            err = sg::launch_reduce_tiles(static_cast<const float*>(ws), p->split_k, p->M, p->N,
+                                          fin, s);
+        else
+            err = sg::launch_reduce(static_cast<const float*>(ws), p->split_k,
+                                    (int64_t)p->M * p->N, fin, s);
         if (err != hipSuccess) return SG_ERR_HIP;
         count(SG_KERNEL_REDUCE);
     }

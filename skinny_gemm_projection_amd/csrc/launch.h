@@ -44,7 +44,11 @@ hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void*
 // when S > 1; grid (ceil(N/128), S).
 constexpr int kMfmaTileN = 128;  // W rows per workgroup (8 waves x 16)
 constexpr size_t kMfmaMaxLds = 160 * 1024;
+constexpr int kXcds = 8;         // MI355X: 8 XCDs, each with its own L2
 size_t mfma_chunk_lds_bytes(int M, int k_chunk);
+// Column tiles of the chunk kernel's grid: ceil(N/128) padded to a multiple
+// of kXcds (the padding workgroups exit at once).
+int mfma_grid_tiles(int N);
 hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk,
                               const void* x, const void* W, const Epilogue& ep,
                               hipStream_t stream);
@@ -53,6 +57,11 @@ hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk,
 // ascending, fp32), then the final epilogue.
 hipError_t launch_reduce(const float* P, int S, int64_t MN, const Epilogue& ep,
                          hipStream_t stream);
+// The same sum for partials made by the chunk kernel: one workgroup per
+// (column tile, 8 rows of M), laid out so it runs on the XCD that wrote the
+// tile's partials.
+hipError_t launch_reduce_tiles(const float* P, int S, int M, int N, const Epilogue& ep,
+                               hipStream_t stream);
 
 // Per-expert token table.  ws points at the grouped workspace (layout in
 // GroupedWorkspace).

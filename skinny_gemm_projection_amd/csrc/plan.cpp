@@ -174,7 +174,7 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
             two_pass = split_k > 1 ? 1 : 0;
             p.k_chunk = chunk_of(K, split_k);
             p.tile_n = kMfmaTileN;
-            p.grid = ((N + kMfmaTileN - 1) / kMfmaTileN) * split_k;
+            p.grid = mfma_grid_tiles(N) * split_k;
             break;
         }
         default:

@@ -61,7 +61,70 @@ __global__ __launch_bounds__(kBlock) void splitk_reduce_kernel(const float* __re
         if (i0 + j < MN) store_final(ep, i0 + j, acc[j]);
 }
 
+// Tiled form: blockIdx.x is the chunk kernel's column tile (128 outputs of
+// a row), blockIdx.y a block of 8 rows; thread t owns row 8*blockIdx.y + t/32
+// and columns 4*(t%32) .. +3 of the tile.  The grid's x extent is the chunk
+// kernel's (padded to a multiple of 8), so linear workgroup ids -- and with
+// them XCDs -- match those of the workgroups that wrote the tile.
+constexpr int kReduceRows = kBlock / 32;
+
+__global__ __launch_bounds__(kBlock) void splitk_reduce_tiles_kernel(const float* __restrict__ P,
+                                                                     int S, int M, int N,
+                                                                     Epilogue ep) {
+    constexpr int kBatch = 16;
+    const int m = blockIdx.y * kReduceRows + threadIdx.x / 32;
+    const int n0 = blockIdx.x * 128 + (threadIdx.x % 32) * 4;
+    if (m >= M || n0 >= N) return;
+    const int64_t plane = (int64_t)M * N;
+    const int64_t i0 = (int64_t)m * N + n0;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if ((N & 3) == 0) {  // n0 + 3 < N and 16-byte aligned
+        for (int s0 = 0; s0 < S; s0 += kBatch) {
+            float4 part[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                if (s0 + j < S) part[j] = reinterpret_cast<const float4*>(P + (s0 + j) * plane + i0)[0];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (s0 + j < S) {
+                    if (s0 + j == 0) {
+                        acc[0] = part[j].x;
+                        acc[1] = part[j].y;
+                        acc[2] = part[j].z;
+                        acc[3] = part[j].w;
+                    } else {
+                        acc[0] += part[j].x;
+                        acc[1] += part[j].y;
+                        acc[2] += part[j].z;
+                        acc[3] += part[j].w;
+                    }
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float a = 0.0f;
+            if (n0 + j < N) {
+                a = P[i0 + j];
+                for (int s = 1; s < S; ++s) a += P[s * plane + i0 + j];
+            }
+            acc[j] = a;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (n0 + j < N) store_final(ep, i0 + j, acc[j]);
+}
+
 }  // namespace
+
+hipError_t launch_reduce_tiles(const float* P, int S, int M, int N, const Epilogue& ep,
+                               hipStream_t stream) {
+    const dim3 grid(mfma_grid_tiles(N), (M + kReduceRows - 1) / kReduceRows);
+    splitk_reduce_tiles_kernel<<<grid, kBlock, 0, stream>>>(P, S, M, N, ep);
+    return hipGetLastError();
+}
 
 hipError_t launch_reduce(const float* P, int S, int64_t MN, const Epilogue& ep,
                          hipStream_t stream) {

@@ -24,7 +24,10 @@
 //    tile holds piece c ^ r (an XOR swizzle), so the operand read -- 16
 //    different rows at one piece each -- hits 16 different bank groups.
 //    Partials go to the [S, M, N] workspace and the deterministic reduction
-//    kernel adds them (two-pass split-K).
+//    kernel adds them (two-pass split-K).  The grid's column-tile count is
+//    padded to a multiple of the 8 XCDs: workgroups are dispatched to XCDs
+//    round-robin by linear id, so all S splits of a column tile run on one
+//    XCD and the tiled reduction finds their partials in that XCD's L2.
 //  * team kernel: S waves of one workgroup split K over a 16-row tile, read
 //    x straight from L2, and add their S partial tiles in LDS in ascending
 //    split order (no workspace, no second pass).
@@ -68,6 +71,7 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
     uint4* xs = lds;                                  // [16*MT][pitch]
     uint4* tile = lds + 16 * MT * pitch + wv * kTileSlots;
 
+    if (blockIdx.x * kChunkRows >= N) return;  // padding column of the grid
     const int row0 = blockIdx.x * kChunkRows + wv * 16;
     // wave-uniform by construction; readfirstlane keeps the descriptor scalar
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16, N - row0)));
@@ -301,6 +305,11 @@ hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void*
     return hipErrorInvalidValue;
 }
 
+int mfma_grid_tiles(int N) {
+    const int tiles = (N + kChunkRows - 1) / kChunkRows;
+    return (tiles + kXcds - 1) / kXcds * kXcds;
+}
+
 size_t mfma_chunk_lds_bytes(int M, int k_chunk) {
     const int MT = (M + 15) / 16;
     return (size_t)16 * MT * x_pitch(k_chunk / kPiece) * 16 +
@@ -309,7 +318,7 @@ size_t mfma_chunk_lds_bytes(int M, int k_chunk) {
 
 hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk, const void* x,
                               const void* W, const Epilogue& ep, hipStream_t stream) {
-    const dim3 grid((N + kChunkRows - 1) / kChunkRows, S);
+    const dim3 grid(mfma_grid_tiles(N), S);
     const int K8 = K / kPiece;
     const int chunk8 = k_chunk / kPiece;
     const uint4* xp = static_cast<const uint4*>(x);
