@@ -71,8 +71,8 @@ typedef enum {
 typedef enum {
     SG_KERNEL_NONE = 0,         /* empty problem (M == 0 or N == 0): nothing runs  */
     SG_KERNEL_GEMV = 1,         /* small-matrix kernel, M <= 2                     */
-    SG_KERNEL_SPLITK_VALU = 2,  /* split-K partial, vector-ALU dot, 3 <= M <= 15   */
-    SG_KERNEL_SPLITK_MFMA = 3,  /* split-K partial, bf16 matrix cores, M >= 16     */
+    SG_KERNEL_SPLITK_VALU = 2,  /* split-K partial, vector-ALU dot, 3 <= M <= 7    */
+    SG_KERNEL_SPLITK_MFMA = 3,  /* split-K partial, bf16 matrix cores, M >= 8      */
     SG_KERNEL_REDUCE = 4,       /* split-K deterministic reduction + epilogue      */
     SG_KERNEL_MOE_TABLE = 5,    /* per-expert token table                          */
     SG_KERNEL_GROUPED = 6,      /* grouped per-expert projection                   */
@@ -90,9 +90,12 @@ typedef struct {
     int32_t kernel;   /* sg_kernel of the main (first) launch                  */
     int32_t split_k;  /* S: number of K chunks; 1 = no split, no reduction     */
     int32_t k_chunk;  /* elements per K chunk: ceil(K/S) rounded up to a
-                         multiple of 8; chunk s covers [s*k_chunk,
-                         min(K, (s+1)*k_chunk))                             */
-    int32_t tile_n;   /* rows of W per workgroup work item                      */
+                         multiple of 64 (whole 128-byte lines); chunk s
+                         covers [s*k_chunk, min(K, (s+1)*k_chunk))          */
+    int32_t tile_n;   /* rows of W per work item: small-matrix / VALU kernels,
+                         rows per wave iteration; matrix cores: 16 for the
+                         in-workgroup (team) kernel, 128 or 256 for the
+                         chunk kernel (16 or 32 rows per wave)              */
     int32_t grid;     /* workgroups of the main launch                          */
     int32_t two_pass; /* 1: the S partials go through the workspace to a second,
                          reduction kernel; 0: they are added inside the main
@@ -102,23 +105,28 @@ typedef struct {
 
 /* plan(M, N, K) -- pick the kernel and its tiling for y[M,N] = x[M,K] W[N,K]^T
  * ([P] Method details §1).  0 <= M <= 64: M <= 2 small-matrix kernel; larger
- * M split-K, on the vector ALU below 16 rows and on bf16 matrix cores from 16
- * rows; the split factor comes from a table tuned on MI355X.  M > 64 returns
+ * M split-K, on the vector ALU below 8 rows and on bf16 matrix cores from 8
+ * rows (measured crossover on MI355X); the split factor and row tiling come
+ * from a per-compute-unit byte cost model, overridable by a tuned table.  M > 64 returns
  * SG_ERR_UNSUPPORTED (prefill-sized batches fall back, [D]); M == 0 or
  * N == 0 gives kernel SG_KERNEL_NONE.  Host-only: touches no GPU state.
  * Limits: 0 <= N <= 1<<20, 0 <= K <= 1<<20 (else SG_ERR_SHAPE). */
 sg_status skinny_gemm_plan(int32_t M, int32_t N, int32_t K, sg_plan* out);
 
-/* Same, but with the kernel, split factor and reduction mode chosen by the
- * caller (sweeps and tests).  kernel <= 0 and split_k <= 0 let the library
- * choose; two_pass: 0 reduce inside the main kernel, 1 second-pass
- * reduction through the workspace, < 0 let the library choose.  SG_ERR_PLAN
- * when the kernel cannot run this shape (GEMV with M > 2, VALU split-K with
- * M > 15 or with a chunk whose x rows do not fit its registers), when the
- * split cannot be reduced in the requested mode, or split_k > 64.  A forced
- * split may leave trailing chunks empty; their partials are 0. */
+/* Same, but with the kernel, split factor, reduction mode and (matrix cores)
+ * row tiling chosen by the caller (sweeps and tests).  kernel <= 0,
+ * split_k <= 0 and tile_n <= 0 let the library choose; two_pass: 0 reduce
+ * inside the main kernel, 1 second-pass reduction through the workspace,
+ * < 0 let the library choose; tile_n (matrix cores only): 16 the team
+ * kernel, 128 or 256 the chunk kernel.  SG_ERR_PLAN when the kernel cannot
+ * run this shape (GEMV with M > 2, VALU split-K with M > 15 or with a chunk
+ * whose x rows do not fit its registers, a chunk kernel whose x chunk does
+ * not fit in LDS), when the split cannot be reduced in the requested mode,
+ * or split_k > 64.  A forced split may leave trailing chunks empty; their
+ * partials are 0. */
 sg_status skinny_gemm_plan_force(int32_t M, int32_t N, int32_t K, int32_t kernel,
-                                 int32_t split_k, int32_t two_pass, sg_plan* out);
+                                 int32_t split_k, int32_t two_pass, int32_t tile_n,
+                                 sg_plan* out);
 
 /* y = x W^T ([P] Method details §1).  Writes y_f32 [M,N] (fp32) and/or
  * y_bf16 [M,N] (the same fp32 value rounded to nearest even); at least one

@@ -98,10 +98,10 @@ void oracle_splitk_partials(int64_t M, int64_t N, int64_t K, int64_t S,
                             const uint16_t* x, const uint16_t* W, double* P)
 {
     /* The accumulation dimension is cut into S contiguous chunks of
-     * c = 8 * ceil(K / (8*S)) elements -- ceil(K/S) rounded up to whole
-     * groups of 8 (16-byte loads of bf16) -- the last one shorter, or empty.
-     * Each chunk is an ordinary projection over its k range. */
-    int64_t chunk = 8 * ((K + 8 * S - 1) / (8 * S));
+     * c = 64 * ceil(K / (64*S)) elements -- ceil(K/S) rounded up to whole
+     * groups of 64 (128-byte cache lines of bf16) -- the last one shorter,
+     * or empty.  Each chunk is an ordinary projection over its k range. */
+    int64_t chunk = 64 * ((K + 64 * S - 1) / (64 * S));
     for (int64_t s = 0; s < S; ++s) {
         int64_t k_begin = s * chunk;
         int64_t k_end = (s + 1) * chunk < K ? (s + 1) * chunk : K;

@@ -57,7 +57,8 @@ void oracle_projection(int64_t M, int64_t N, int64_t K,
                        double* y, double* abs_scale);
 
 /* Split-K partial sums.  Chunk s covers k in [s*c, min(K, (s+1)*c)) with
- * c = 8*ceil(K/(8*S)) (ceil(K/S) rounded up to a multiple of 8);
+ * c = 64*ceil(K/(64*S)) (ceil(K/S) rounded up to a multiple of 64, whole
+ * 128-byte lines of bf16);
  * P[s,m,n] = sum over that chunk, k ascending.  A chunk that starts at or
  * past K is empty and holds 0. */
 void oracle_splitk_partials(int64_t M, int64_t N, int64_t K, int64_t S,

@@ -92,11 +92,14 @@ def skinny_gemm_plan(M: int, N: int, K: int) -> SgPlan:
 
 
 def skinny_gemm_plan_force(M: int, N: int, K: int, kernel: int, split_k: int = 0,
-                           two_pass: int = -1) -> SgPlan:
-    """plan with the kernel (SG_KERNEL_*), split factor and reduction mode
-    (0 in-kernel, 1 second pass, -1 library's choice) chosen by the caller."""
+                           two_pass: int = -1, tile_n: int = 0) -> SgPlan:
+    """plan with the kernel (SG_KERNEL_*), split factor, reduction mode
+    (0 in-kernel, 1 second pass, -1 library's choice) and, on the matrix
+    cores, row tiling (16 team kernel, 128 or 256 chunk kernel, 0 library's
+    choice) chosen by the caller."""
     plan = SgPlan()
-    _lib.check(_c().skinny_gemm_plan_force(M, N, K, kernel, split_k, two_pass, ctypes.byref(plan)))
+    _lib.check(_c().skinny_gemm_plan_force(M, N, K, kernel, split_k, two_pass, tile_n,
+                                           ctypes.byref(plan)))
     return plan
 
 

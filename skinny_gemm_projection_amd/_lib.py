@@ -68,7 +68,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     i32, p, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
     P = ctypes.POINTER(SgPlan)
     lib.skinny_gemm_plan.argtypes = [i32, i32, i32, P]
-    lib.skinny_gemm_plan_force.argtypes = [i32, i32, i32, i32, i32, i32, P]
+    lib.skinny_gemm_plan_force.argtypes = [i32, i32, i32, i32, i32, i32, i32, P]
     lib.skinny_gemm.argtypes = [P, p, p, p, p, p, sz, p]
     lib.skinny_gemm_residual.argtypes = [P, p, p, p, p, p, p, sz, p]
     lib.grouped_skinny_gemm_workspace.argtypes = [i32, i32, i32, i32, i32]

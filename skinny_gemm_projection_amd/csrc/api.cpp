@@ -73,8 +73,10 @@ sg_status projection(const sg_plan* p, const sg_bf16* x, const sg_bf16* W, const
         split ? sg::Epilogue{static_cast<float*>(ws), nullptr, nullptr, nullptr} : fin;
 
     hipError_t err;
-    if (p->kernel == SG_KERNEL_SPLITK_MFMA && p->tile_n == sg::kMfmaTileN)
-        err = sg::launch_splitk_mfma(p->M, p->N, p->K, p->split_k, p->k_chunk, x, W, main_ep, s);
+    const bool chunk = p->kernel == SG_KERNEL_SPLITK_MFMA && p->tile_n >= sg::kMfmaTileN;
+    if (chunk)
+        err = sg::launch_splitk_mfma(p->M, p->N, p->K, p->split_k, p->k_chunk, p->tile_n, x, W,
+                                     main_ep, s);
     else if (p->kernel == SG_KERNEL_SPLITK_MFMA)
         err = sg::launch_mfma_team(p->M, p->N, p->K, p->split_k, p->k_chunk, x, W, main_ep, s);
     else
@@ -83,9 +85,9 @@ sg_status projection(const sg_plan* p, const sg_bf16* x, const sg_bf16* W, const
     if (err != hipSuccess) return SG_ERR_HIP;
     count(p->kernel);
     if (split) {
-        if (p->kernel == SG_KERNEL_SPLITK_MFMA && p->tile_n == sg::kMfmaTileN)
+        if (chunk)
             err = sg::launch_reduce_tiles(static_cast<const float*>(ws), p->split_k, p->M, p->N,
-                                          fin, s);
+                                          p->tile_n, fin, s);
         else
             err = sg::launch_reduce(static_cast<const float*>(ws), p->split_k,
                                     (int64_t)p->M * p->N, fin, s);

@@ -32,24 +32,25 @@ hipError_t launch_rowdot(int M, int N, int K, int S, int k_chunk, int grid, bool
                          hipStream_t stream);
 int rowdot_grid(int M, int N, int K, int S, int k_chunk, bool two_pass);
 
-// bf16 matrix-core split-K (16 <= M <= 64, any M >= 1 when forced).
+// bf16 matrix-core split-K (8 <= M <= 64, any M >= 1 when forced).
 // Team kernel: S waves (S in {1,2,4,8}) of one workgroup split K over a
 // 16-row tile and add their partials in LDS; grid ceil(N/16).
 constexpr int kMfmaTeamTileN = 16;
 bool mfma_team_split_ok(int S);
 hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void* x,
                             const void* W, const Epilogue& ep, hipStream_t stream);
-// Chunk kernel: workgroups of 128 rows x one K chunk with the x chunk
-// staged in LDS; partials to ep.partial ([S, M, N]) for the reduction kernel
-// when S > 1; grid (ceil(N/128), S).
-constexpr int kMfmaTileN = 128;  // W rows per workgroup (8 waves x 16)
+// Chunk kernel: workgroups of tile_n rows (128: 16 per wave, or 256: 32 per
+// wave sharing each x operand load) x one K chunk, the x chunk staged in LDS;
+// partials to ep.partial ([S, M, N]) for the reduction kernel when S > 1;
+// grid (mfma_grid_tiles(N, tile_n), S).
+constexpr int kMfmaTileN = 128;  // W rows per workgroup with 16 rows per wave
 constexpr size_t kMfmaMaxLds = 160 * 1024;
 constexpr int kXcds = 8;         // MI355X: 8 XCDs, each with its own L2
-size_t mfma_chunk_lds_bytes(int M, int k_chunk);
-// Column tiles of the chunk kernel's grid: ceil(N/128) padded to a multiple
-// of kXcds (the padding workgroups exit at once).
-int mfma_grid_tiles(int N);
-hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk,
+size_t mfma_chunk_lds_bytes(int M, int k_chunk, int tile_n);
+// Column tiles of the chunk kernel's grid: ceil(N/tile_n) padded to a
+// multiple of kXcds (the padding workgroups exit at once).
+int mfma_grid_tiles(int N, int tile_n);
+hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk, int tile_n,
                               const void* x, const void* W, const Epilogue& ep,
                               hipStream_t stream);
 
@@ -58,10 +59,10 @@ hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk,
 hipError_t launch_reduce(const float* P, int S, int64_t MN, const Epilogue& ep,
                          hipStream_t stream);
 // The same sum for partials made by the chunk kernel: one workgroup per
-// (column tile, 8 rows of M), laid out so it runs on the XCD that wrote the
-// tile's partials.
-hipError_t launch_reduce_tiles(const float* P, int S, int M, int N, const Epilogue& ep,
-                               hipStream_t stream);
+// (column tile, block of rows of M), laid out so it runs on the XCD that
+// wrote the tile's partials.
+hipError_t launch_reduce_tiles(const float* P, int S, int M, int N, int tile_n,
+                               const Epilogue& ep, hipStream_t stream);
 
 // Per-expert token table.  ws points at the grouped workspace (layout in
 // GroupedWorkspace).

@@ -6,12 +6,12 @@
 // Kimi K3 in vLLM" deepnotes page, Method details §1).  On MI355X:
 //   M <= 2        row-streaming VALU kernel, no split while the x chunk fits
 //                 in registers (K <= 8192), fused epilogue;
-//   3 <= M <= 15  the same kernel on K chunks (split-K), the split sized so
-//                 the M x-rows of a chunk fit in 128 VGPRs, then the
-//                 deterministic reduction;
-//   16 <= M <= 64 bf16 matrix-core split-K, split chosen so the grid covers
-//                 the 256 compute units without the fp32 partials growing
-//                 large next to the weights, then the reduction.
+//   3 <= M <= 7   the same kernel on K chunks (split-K), the split sized so
+//                 the M x-rows of a chunk fit in its registers, reduced
+//                 inside the workgroup when the split allows;
+//   8 <= M <= 64  bf16 matrix-core split-K; split factor and row tiling from
+//                 a per-compute-unit byte cost model; then the deterministic
+//                 reduction.
 // A small table measured on MI355X overrides the split factor for known
 // shapes.  Everything here is host arithmetic; no GPU call is made.
 #include <cstdlib>
@@ -25,22 +25,34 @@ namespace {
 constexpr int32_t kMaxNK = 1 << 20;
 constexpr int32_t kMaxSplit = 64;
 constexpr int kComputeUnits = 256;
+// Smallest batch planned on the matrix cores.  Measured on MI355X (K=7168,
+// N=4096): from M=8 up the VALU kernel's v_dot2 work per weight byte, M/2
+// instructions per bf16 pair, outgrows the weight stream (M=8: 15.0 us VALU
+// against 13.8 us MFMA; M=12: 20.7 against 14.0), while at M <= 6 the VALU
+// kernel, which needs no second pass, is faster (M=4: 12.8 against 13.8).
+constexpr int32_t kMfmaFromM = 8;
 
-// Split factors measured on MI355X (bench sweeps); {M_lo, M_hi, N, K, S}.
+// Choices measured on MI355X for known projection shapes, overriding the
+// defaults: {M_lo, M_hi, N, K, kernel (0: default), split (0: default)}.
 struct Tuned {
-    int32_t m_lo, m_hi, n, k, split;
+    int32_t m_lo, m_hi, n, k, kernel, split;
 };
 constexpr Tuned kTuned[] = {
-    {0, 0, 0, 0, 0},  // sentinel
+    // output projection 8192 -> 7168 at M = 8: the VALU kernel (23.8 us)
+    // beats the best matrix-core plan (24.9 us)
+    {8, 8, 7168, 8192, SG_KERNEL_SPLITK_VALU, 0},
 };
 
 bool split_ok(int32_t S) { return S >= 1 && S <= kMaxSplit; }
 
-// Chunk width: ceil(K / S) rounded up to whole 16-byte groups (8 bf16), so
-// every chunk starts on a 16-byte boundary; the last chunk is the shorter one.
+// Chunk width: ceil(K / S) rounded up to whole 128-byte cache lines (64
+// bf16), so every chunk starts on a line boundary of each weight row; the
+// last chunk is the shorter one.  (With 16-byte granularity a chunk edge
+// splits a line between two workgroups, often on different XCDs, and the
+// weight stream measured 20-50% more HBM traffic than the weight bytes.)
 int32_t chunk_of(int32_t K, int32_t S) {
-    const int64_t groups = ((int64_t)K / 8 + S - 1) / S;
-    return (int32_t)(8 * groups);
+    const int64_t lines = ((int64_t)K + 64 * (int64_t)S - 1) / (64 * (int64_t)S);
+    return (int32_t)(64 * lines);
 }
 
 // No chunk of an automatic plan is empty.
@@ -63,38 +75,53 @@ int32_t rowdot_split(int32_t M, int32_t K) {
     return -1;
 }
 
-bool mfma_chunk_fits(int32_t M, int32_t K, int32_t S) {
-    return sg::mfma_chunk_lds_bytes(M, chunk_of(K, S)) <= sg::kMfmaMaxLds;
+bool mfma_chunk_fits(int32_t M, int32_t K, int32_t S, int32_t tile_n) {
+    return sg::mfma_chunk_lds_bytes(M, chunk_of(K, S), tile_n) <= sg::kMfmaMaxLds;
 }
 
-// Split for the matrix-core chunk kernel.  Cost model in bytes per compute
-// unit: the weight bytes of the busiest unit -- ceil(tiles*S / 256) workgroups
-// of 128 rows x K/S each -- plus the partials written and read back
-// (2 * S*M*N*4 bytes spread over the 256 units).  Among the splits whose x
-// chunk fits in LDS, the cheapest wins (ties: the smaller split).
-int32_t mfma_split(int32_t M, int32_t N, int32_t K) {
-    const int64_t tiles = (N + sg::kMfmaTileN - 1) / sg::kMfmaTileN;
-    int32_t best = -1;
+// Cost of a chunk-kernel plan in bytes per compute unit: the weight bytes of
+// the busiest unit -- ceil(tiles*S / 256) workgroups of tile_n rows x K/S --
+// plus half the x bytes those workgroups stage from L2 into LDS, plus the
+// partials written and read back (2 * S*M*N*4 bytes over the 256 units).
+int64_t mfma_cost(int32_t M, int32_t N, int32_t K, int32_t S, int32_t tile_n) {
+    const int64_t tiles = (N + tile_n - 1) / tile_n;
+    const int64_t per_unit = (tiles * S + kComputeUnits - 1) / kComputeUnits;
+    const int64_t chunk = chunk_of(K, S);
+    const int64_t w_bytes = per_unit * tile_n * 2 * chunk;
+    const int64_t x_bytes = per_unit * M * chunk;
+    const int64_t p_bytes = 8 * (int64_t)S * M * N / kComputeUnits;
+    return w_bytes + x_bytes + p_bytes;
+}
+
+// Split and tile width for the matrix-core chunk kernel: the cheapest pair
+// whose x chunk fits in LDS (ties: the smaller split, then 128-row tiles).
+// A forced split or tile width narrows the search.  False if nothing fits.
+bool mfma_choose(int32_t M, int32_t N, int32_t K, int32_t force_split, int32_t force_tile,
+                 int32_t* split, int32_t* tile_n) {
+    bool found = false;
     int64_t best_cost = 0;
-    for (int32_t S = 1; S <= kMaxSplit; ++S) {
-        if (!no_empty_chunk(K, S)) break;
-        if (!mfma_chunk_fits(M, K, S)) continue;
-        const int64_t per_unit = (tiles * S + kComputeUnits - 1) / kComputeUnits;
-        const int64_t w_bytes = per_unit * sg::kMfmaTileN * 2 * (int64_t)chunk_of(K, S);
-        const int64_t p_bytes = 8 * (int64_t)S * M * N / kComputeUnits;
-        const int64_t cost = w_bytes + p_bytes;
-        if (best < 0 || cost < best_cost) {
-            best = S;
-            best_cost = cost;
+    for (int32_t t = sg::kMfmaTileN; t <= 2 * sg::kMfmaTileN; t *= 2) {
+        if (force_tile > 0 && t != force_tile) continue;
+        for (int32_t S = 1; S <= kMaxSplit; ++S) {
+            if (force_split > 0 && S != force_split) continue;
+            if (force_split <= 0 && !no_empty_chunk(K, S)) break;
+            if (!mfma_chunk_fits(M, K, S, t)) continue;
+            const int64_t cost = mfma_cost(M, N, K, S, t);
+            if (!found || cost < best_cost) {
+                found = true;
+                best_cost = cost;
+                *split = S;
+                *tile_n = t;
+            }
         }
     }
-    return best;
+    return found;
 }
 
-int32_t tuned_split(int32_t M, int32_t N, int32_t K) {
+const Tuned* tuned_for(int32_t M, int32_t N, int32_t K) {
     for (const Tuned& t : kTuned)
-        if (t.split > 0 && M >= t.m_lo && M <= t.m_hi && N == t.n && K == t.k) return t.split;
-    return -1;
+        if (M >= t.m_lo && M <= t.m_hi && N == t.n && K == t.k) return &t;
+    return nullptr;
 }
 
 }  // namespace
@@ -102,7 +129,7 @@ int32_t tuned_split(int32_t M, int32_t N, int32_t K) {
 namespace sg {
 
 sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t split_k,
-                    int32_t two_pass, sg_plan* out) {
+                    int32_t two_pass, int32_t tile_n, sg_plan* out) {
     if (!out) return SG_ERR_NULL;
     if (M < 0 || N < 0 || K < 0 || N > kMaxNK || K > kMaxNK) return SG_ERR_SHAPE;
     if (M > SG_MAX_M) return SG_ERR_UNSUPPORTED;
@@ -123,8 +150,12 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
     }
 
     if (kernel <= 0) {
-        kernel = M <= 2 ? SG_KERNEL_GEMV : (M < 16 ? SG_KERNEL_SPLITK_VALU : SG_KERNEL_SPLITK_MFMA);
-        if (split_k <= 0) split_k = tuned_split(M, N, K);
+        kernel = M <= 2 ? SG_KERNEL_GEMV
+                        : (M < kMfmaFromM ? SG_KERNEL_SPLITK_VALU : SG_KERNEL_SPLITK_MFMA);
+        if (const Tuned* t = tuned_for(M, N, K)) {
+            if (t->kernel > 0) kernel = t->kernel;
+            if (split_k <= 0 && t->split > 0) split_k = t->split;
+        }
     }
 
     switch (kernel) {
@@ -150,31 +181,29 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
             // Default: the chunk kernel, its S partials summed by the second
             // pass.  two_pass == 0 asks for the team kernel (S in 1, 2, 4, 8
             // reduced inside the workgroup).
-            if (two_pass == 0) {
-                if (split_k <= 0) split_k = 8;
+            const bool team_asked = two_pass == 0 || tile_n == kMfmaTeamTileN;
+            int32_t S = 0, t = 0;
+            if (!team_asked && tile_n != 0 && tile_n != kMfmaTileN && tile_n != 2 * kMfmaTileN)
+                return SG_ERR_PLAN;
+            if (!team_asked && mfma_choose(M, N, K, split_k, tile_n, &S, &t)) {
+                split_k = S;
+                two_pass = S > 1 ? 1 : 0;
+                p.k_chunk = chunk_of(K, S);
+                p.tile_n = t;
+                p.grid = mfma_grid_tiles(N, t) * S;
+                break;
+            }
+            // team kernel: asked for, or the x chunk would not fit in LDS
+            if (two_pass > 0 || (tile_n != 0 && tile_n != kMfmaTeamTileN)) return SG_ERR_PLAN;
+            if (split_k <= 0) {
+                split_k = 8;
                 while (split_k > 1 && !no_empty_chunk(K, split_k)) split_k /= 2;
-                if (!mfma_team_split_ok(split_k)) return SG_ERR_PLAN;
-                p.k_chunk = chunk_of(K, split_k);
-                p.tile_n = kMfmaTeamTileN;
-                p.grid = (N + kMfmaTeamTileN - 1) / kMfmaTeamTileN;
-                two_pass = 0;
-                break;
             }
-            if (split_k <= 0) split_k = mfma_split(M, N, K);
-            if (!split_ok(split_k)) return SG_ERR_PLAN;
-            if (!mfma_chunk_fits(M, K, split_k)) {
-                // x chunk too large for LDS: the team kernel, if allowed
-                if (two_pass > 0 || !mfma_team_split_ok(split_k)) return SG_ERR_PLAN;
-                p.k_chunk = chunk_of(K, split_k);
-                p.tile_n = kMfmaTeamTileN;
-                p.grid = (N + kMfmaTeamTileN - 1) / kMfmaTeamTileN;
-                two_pass = 0;
-                break;
-            }
-            two_pass = split_k > 1 ? 1 : 0;
+            if (!mfma_team_split_ok(split_k)) return SG_ERR_PLAN;
             p.k_chunk = chunk_of(K, split_k);
-            p.tile_n = kMfmaTileN;
-            p.grid = mfma_grid_tiles(N) * split_k;
+            p.tile_n = kMfmaTeamTileN;
+            p.grid = (N + kMfmaTeamTileN - 1) / kMfmaTeamTileN;
+            two_pass = 0;
             break;
         }
         default:
@@ -191,11 +220,16 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
 
 bool plan_matches(const sg_plan* p) {
     // The matrix-core path has two kernels; the plan's tile width says which
-    // one it was made for (the team kernel is requested with two_pass == 0).
+    // one (and which row tiling) it was made for.
     int32_t request = p->two_pass;
-    if (p->kernel == SG_KERNEL_SPLITK_MFMA) request = p->tile_n == kMfmaTileN ? 1 : 0;
+    int32_t tile = 0;
+    if (p->kernel == SG_KERNEL_SPLITK_MFMA) {
+        request = p->tile_n == kMfmaTeamTileN ? 0 : 1;
+        tile = p->tile_n;
+    }
     sg_plan q;
-    if (make_plan(p->M, p->N, p->K, p->kernel, p->split_k, request, &q) != SG_OK) return false;
+    if (make_plan(p->M, p->N, p->K, p->kernel, p->split_k, request, tile, &q) != SG_OK)
+        return false;
     return q.kernel == p->kernel && q.split_k == p->split_k && q.k_chunk == p->k_chunk &&
            q.tile_n == p->tile_n && q.grid == p->grid && q.two_pass == p->two_pass &&
            q.workspace_bytes == p->workspace_bytes;
@@ -204,11 +238,12 @@ bool plan_matches(const sg_plan* p) {
 }  // namespace sg
 
 extern "C" sg_status skinny_gemm_plan(int32_t M, int32_t N, int32_t K, sg_plan* out) {
-    return sg::make_plan(M, N, K, 0, 0, -1, out);
+    return sg::make_plan(M, N, K, 0, 0, -1, 0, out);
 }
 
 extern "C" sg_status skinny_gemm_plan_force(int32_t M, int32_t N, int32_t K, int32_t kernel,
-                                            int32_t split_k, int32_t two_pass, sg_plan* out) {
+                                            int32_t split_k, int32_t two_pass, int32_t tile_n,
+                                            sg_plan* out) {
     return sg::make_plan(M, N, K, kernel <= 0 ? 0 : kernel, split_k, two_pass < 0 ? -1 : two_pass,
-                         out);
+                         tile_n < 0 ? 0 : tile_n, out);
 }

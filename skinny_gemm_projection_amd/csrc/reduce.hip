@@ -61,19 +61,18 @@ __global__ __launch_bounds__(kBlock) void splitk_reduce_kernel(const float* __re
         if (i0 + j < MN) store_final(ep, i0 + j, acc[j]);
 }
 
-// Tiled form: blockIdx.x is the chunk kernel's column tile (128 outputs of
-// a row), blockIdx.y a block of 8 rows; thread t owns row 8*blockIdx.y + t/32
-// and columns 4*(t%32) .. +3 of the tile.  The grid's x extent is the chunk
-// kernel's (padded to a multiple of 8), so linear workgroup ids -- and with
-// them XCDs -- match those of the workgroups that wrote the tile.
-constexpr int kReduceRows = kBlock / 32;
-
+// Tiled form: blockIdx.x is the chunk kernel's column tile (tile_n outputs
+// of a row), blockIdx.y a block of rows; each thread owns 4 consecutive
+// columns of one row.  The grid's x extent is the chunk kernel's (padded to a
+// multiple of 8), so linear workgroup ids -- and with them XCDs -- match those
+// of the workgroups that wrote the tile.
 __global__ __launch_bounds__(kBlock) void splitk_reduce_tiles_kernel(const float* __restrict__ P,
                                                                      int S, int M, int N,
-                                                                     Epilogue ep) {
+                                                                     int tile_n, Epilogue ep) {
     constexpr int kBatch = 16;
-    const int m = blockIdx.y * kReduceRows + threadIdx.x / 32;
-    const int n0 = blockIdx.x * 128 + (threadIdx.x % 32) * 4;
+    const int per_row = tile_n / 4;  // threads per row of the tile
+    const int m = blockIdx.y * (kBlock / per_row) + threadIdx.x / per_row;
+    const int n0 = blockIdx.x * tile_n + (threadIdx.x % per_row) * 4;
     if (m >= M || n0 >= N) return;
     const int64_t plane = (int64_t)M * N;
     const int64_t i0 = (int64_t)m * N + n0;
@@ -119,10 +118,13 @@ __global__ __launch_bounds__(kBlock) void splitk_reduce_tiles_kernel(const float
 
 }  // namespace
 
-hipError_t launch_reduce_tiles(const float* P, int S, int M, int N, const Epilogue& ep,
-                               hipStream_t stream) {
-    const dim3 grid(mfma_grid_tiles(N), (M + kReduceRows - 1) / kReduceRows);
-    splitk_reduce_tiles_kernel<<<grid, kBlock, 0, stream>>>(P, S, M, N, ep);
+hipError_t launch_reduce_tiles(const float* P, int S, int M, int N, int tile_n,
+                               const Epilogue& ep, hipStream_t stream) {
+    if (tile_n % 4 != 0 || tile_n / 4 > kBlock || kBlock % (tile_n / 4) != 0)
+        return hipErrorInvalidValue;
+    const int rows_per_block = kBlock / (tile_n / 4);
+    const dim3 grid(mfma_grid_tiles(N, tile_n), (M + rows_per_block - 1) / rows_per_block);
+    splitk_reduce_tiles_kernel<<<grid, kBlock, 0, stream>>>(P, S, M, N, tile_n, ep);
     return hipGetLastError();
 }
 

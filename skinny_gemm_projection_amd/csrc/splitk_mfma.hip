@@ -39,21 +39,39 @@ namespace sg {
 namespace {
 
 constexpr int kChunkWaves = 8;
-constexpr int kChunkRows = 16 * kChunkWaves;
-constexpr int kRoundPieces = 16;                 // pieces of each row per round (4 k steps)
-constexpr int kTileSlots = 16 * kRoundPieces;    // 16 rows x 16 pieces = 4 KB per wave
-constexpr int kXLoadsPerThread = 16;             // x staging loads per thread (LDS bound)
+constexpr int kTileSlots = 256;       // weight tile of one wave: 4 KB
+constexpr int kXLoadsPerThread = 16;  // x staging loads per thread (LDS bound)
+
+// Geometry of the chunk kernel for NT row tiles (16 rows each) per wave: a
+// round covers 16/NT pieces of each of the wave's 16*NT rows (4 KB), loaded
+// by 4 instructions of 4*NT rows x (256/NT) bytes.
+template <int NT>
+struct ChunkGeom {
+    static constexpr int kRows = 16 * NT;                  // W rows per wave
+    static constexpr int kRoundPieces = 16 / NT;           // pieces per row per round
+    static constexpr int kSteps = kRoundPieces / 4;        // 32-wide k steps per round
+    static constexpr int kRowsPerLoad = kWave / kRoundPieces;
+    static constexpr int kWgRows = kRows * kChunkWaves;    // W rows per workgroup
+    // Tile slot of (row, piece): row-major [kRows][kRoundPieces] with the
+    // piece XOR-swizzled so that the 16 rows one operand load reads fall in
+    // 16 different 16-byte bank groups.
+    __device__ static int swz(int row) {
+        return NT == 1 ? (row & 15) : ((row >> 1) & (kRoundPieces - 1));
+    }
+};
 
 // Row pitch (16-byte units) of the staged x chunk: whole rounds plus one, odd,
 // so the 16 rows read by one operand load fall in 16 different bank groups.
-__host__ __device__ inline int x_pitch(int chunk8) {
-    return (chunk8 + kRoundPieces - 1) / kRoundPieces * kRoundPieces + 1;
+__host__ __device__ inline int x_pitch(int chunk8, int round_pieces) {
+    return (chunk8 + round_pieces - 1) / round_pieces * round_pieces + 1;
 }
 
-template <int MT, int DR>
+template <int MT, int NT, int DR>
 __global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ W, int M, int N, int K8, int chunk8,
     Epilogue ep) {
+    using G = ChunkGeom<NT>;
+    constexpr int RP = G::kRoundPieces;
     extern __shared__ uint4 lds[];
     constexpr uint32_t kOff = 0xFFFFFFF0u;  // past any descriptor range: reads zero
     const int tid = threadIdx.x;
@@ -66,32 +84,35 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
     const int len = max(0, min(K8 - k0, chunk8));  // pieces of this chunk
     // whole rounds: x is staged as zeros past len and the weights past len
     // load as zeros, so every k step of a round runs unconditionally
-    const int lenr = (len + kRoundPieces - 1) / kRoundPieces * kRoundPieces;
-    const int pitch = x_pitch(chunk8);
+    const int lenr = (len + RP - 1) / RP * RP;
+    const int pitch = x_pitch(chunk8, RP);
     uint4* xs = lds;                                  // [16*MT][pitch]
     uint4* tile = lds + 16 * MT * pitch + wv * kTileSlots;
 
-    if (blockIdx.x * kChunkRows >= N) return;  // padding column of the grid
-    const int row0 = blockIdx.x * kChunkRows + wv * 16;
+    if (blockIdx.x * G::kWgRows >= N) return;  // padding column of the grid
+    const int row0 = blockIdx.x * G::kWgRows + wv * G::kRows;
     // wave-uniform by construction; readfirstlane keeps the descriptor scalar
-    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16, N - row0)));
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(G::kRows, N - row0)));
     const rsrc_t wrs = make_rsrc(W + (int64_t)row0 * K8, (uint32_t)rows * (uint32_t)K8 * 16u);
-    // Load i of a round reads row 4i + grp; lane slot col carries piece col ^ row.
+    // Load i of a round reads row i*kRowsPerLoad + lane/RP; slot lane%RP of
+    // that row carries piece slot ^ swz(row).
+    const int lrow = lane / RP;
+    const int lslot = lane % RP;
     uint32_t woff[4];
     int wpiece[4];
     bool wrow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = 4 * i + grp;
-        wpiece[i] = col ^ r;
+        const int r = i * G::kRowsPerLoad + lrow;
+        wpiece[i] = lslot ^ G::swz(r);
         wrow[i] = r < rows;
         woff[i] = ((uint32_t)r * K8 + k0 + wpiece[i]) * 16u;
     }
     auto load_round = [&](int rd, uint4 (&w)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool ok = wrow[i] && (rd * kRoundPieces + wpiece[i] < len);
-            w[i] = load16<kStream>(wrs, ok ? woff[i] + (uint32_t)rd * (kRoundPieces * 16u) : kOff);
+            const bool ok = wrow[i] && (rd * RP + wpiece[i] < len);
+            w[i] = load16<kStream>(wrs, ok ? woff[i] + (uint32_t)rd * (RP * 16u) : kOff);
         }
     };
 
@@ -99,11 +120,11 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
     // weight rounds, then the x values are written to LDS: waiting for the x
     // loads does not wait for the weight stream.
     const int xtotal = 16 * MT * lenr;
-    const int div = max(lenr, kRoundPieces);
+    const int div = max(lenr, RP);
     const int step_rows = (kWave * kChunkWaves) / div;  // idx += 512 moves this many rows
     const int step_p = (kWave * kChunkWaves) - step_rows * div;  // ... and this many pieces
-    const rsrc_t xrs = make_rsrc(x, (uint32_t)M * (uint32_t)K8 * 16u);
     const int nx = (xtotal + kWave * kChunkWaves - 1) / (kWave * kChunkWaves);  // <= 16
+    const rsrc_t xrs = make_rsrc(x, (uint32_t)M * (uint32_t)K8 * 16u);
     uint4 xv[kXLoadsPerThread];
     int xdst[kXLoadsPerThread];  // LDS slot of each staged piece, -1 if none
     {
@@ -133,10 +154,20 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
         if (j < nx && xdst[j] >= 0) xs[xdst[j]] = xv[j];  // zeros past M and len
     __syncthreads();
 
-    f32x4_t acc[MT];
+    f32x4_t acc[NT][MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    const int rounds = (len + kRoundPieces - 1) / kRoundPieces;
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    int bslot[NT][G::kSteps];  // tile slot of this lane's B operand per (row tile, k step)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int t = 0; t < G::kSteps; ++t) {
+            const int r = 16 * nt + col;
+            bslot[nt][t] = r * RP + ((4 * t + grp) ^ G::swz(r));
+        }
+    const int rounds = (len + RP - 1) / RP;
     for (int r0 = 0; r0 < rounds; r0 += DR) {
 #pragma unroll
         for (int d = 0; d < DR; ++d) {
@@ -145,18 +176,23 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
                 // Within one wave LDS operations run in order, so the tile can
                 // be rewritten right after the previous round's reads.
 #pragma unroll
-                for (int i = 0; i < 4; ++i) tile[(4 * i + grp) * kRoundPieces + col] = wb[d][i];
+                for (int i = 0; i < 4; ++i)
+                    tile[(i * G::kRowsPerLoad + lrow) * RP + lslot] = wb[d][i];
                 __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const uint4 b = tile[col * kRoundPieces + ((4 * t + grp) ^ col)];
-                    const int p = rd * kRoundPieces + 4 * t + grp;  // < lenr < pitch
+                for (int t = 0; t < G::kSteps; ++t) {
+                    const int p = rd * RP + 4 * t + grp;  // < lenr < pitch
+                    uint4 a[MT];
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const uint4 a = xs[(mt * 16 + col) * pitch + p];
-                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                            acc[mt], 0, 0, 0);
+                    for (int mt = 0; mt < MT; ++mt) a[mt] = xs[(mt * 16 + col) * pitch + p];
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const uint4 b = tile[bslot[nt][t]];
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+                            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, a[mt]), __builtin_bit_cast(bf16x8_t, b),
+                                acc[nt][mt], 0, 0, 0);
                     }
                 }
                 __builtin_amdgcn_wave_barrier();
@@ -165,18 +201,22 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
         }
     }
 
-    if (col >= rows) return;
-    const int n = row0 + col;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    for (int nt = 0; nt < NT; ++nt) {
+        const int r = 16 * nt + col;
+        if (r >= rows) continue;
+        const int n = row0 + r;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int m = mt * 16 + grp * 4 + v;
-            if (m < M) {
-                if (ep.partial)
-                    ep.partial[((int64_t)s * M + m) * N + n] = acc[mt][v];
-                else
-                    store_final(ep, (int64_t)m * N + n, acc[mt][v]);
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = mt * 16 + grp * 4 + v;
+                if (m < M) {
+                    if (ep.partial)
+                        ep.partial[((int64_t)s * M + m) * N + n] = acc[nt][mt][v];
+                    else
+                        store_final(ep, (int64_t)m * N + n, acc[nt][mt][v]);
+                }
             }
         }
     }
@@ -305,41 +345,47 @@ hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void*
     return hipErrorInvalidValue;
 }
 
-int mfma_grid_tiles(int N) {
-    const int tiles = (N + kChunkRows - 1) / kChunkRows;
+int mfma_grid_tiles(int N, int tile_n) {
+    const int tiles = (N + tile_n - 1) / tile_n;
     return (tiles + kXcds - 1) / kXcds * kXcds;
 }
 
-size_t mfma_chunk_lds_bytes(int M, int k_chunk) {
+size_t mfma_chunk_lds_bytes(int M, int k_chunk, int tile_n) {
     const int MT = (M + 15) / 16;
-    return (size_t)16 * MT * x_pitch(k_chunk / kPiece) * 16 +
+    const int round_pieces = tile_n == 2 * kMfmaTileN ? 8 : 16;
+    return (size_t)16 * MT * x_pitch(k_chunk / kPiece, round_pieces) * 16 +
            (size_t)kChunkWaves * kTileSlots * 16;
 }
 
-hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk, const void* x,
+hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk, int tile_n, const void* x,
                               const void* W, const Epilogue& ep, hipStream_t stream) {
-    const dim3 grid(mfma_grid_tiles(N), S);
+    const int NT = tile_n / kMfmaTileN;
+    if (NT != 1 && NT != 2) return hipErrorInvalidValue;
+    const dim3 grid(mfma_grid_tiles(N, tile_n), S);
     const int K8 = K / kPiece;
     const int chunk8 = k_chunk / kPiece;
     const uint4* xp = static_cast<const uint4*>(x);
     const uint4* wp = static_cast<const uint4*>(W);
     const int MT = (M + 15) / 16;
-    const size_t lds = mfma_chunk_lds_bytes(M, k_chunk);
+    const size_t lds = mfma_chunk_lds_bytes(M, k_chunk, tile_n);
     if (lds > kMfmaMaxLds) return hipErrorInvalidValue;
     // x staging: 16*MT*(pitch - 1) pieces at most over the workgroup's threads
-    if ((size_t)16 * MT * (x_pitch(chunk8) - 1) > (size_t)kXLoadsPerThread * kWave * kChunkWaves)
+    if ((size_t)16 * MT * (x_pitch(chunk8, 16 / NT) - 1) >
+        (size_t)kXLoadsPerThread * kWave * kChunkWaves)
         return hipErrorInvalidValue;
     constexpr int DR = 2;  // weight rounds in flight per wave (8 loads)
-#define SG_CHUNK(mt) \
-    if (MT == mt) { \
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&splitk_mfma_kernel<mt, DR>), \
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+#define SG_CHUNK(mt, nt) \
+    if (MT == mt && NT == nt) { \
+        hipError_t e = hipFuncSetAttribute( \
+            reinterpret_cast<const void*>(&splitk_mfma_kernel<mt, nt, DR>), \
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
         if (e != hipSuccess) return e; \
-        splitk_mfma_kernel<mt, DR><<<grid, kWave * kChunkWaves, lds, stream>>>(xp, wp, M, N, K8, \
-                                                                              chunk8, ep); \
+        splitk_mfma_kernel<mt, nt, DR><<<grid, kWave * kChunkWaves, lds, stream>>>( \
+            xp, wp, M, N, K8, chunk8, ep); \
         return hipGetLastError(); \
     }
-    SG_CHUNK(1) SG_CHUNK(2) SG_CHUNK(3) SG_CHUNK(4)
+    SG_CHUNK(1, 1) SG_CHUNK(2, 1) SG_CHUNK(3, 1) SG_CHUNK(4, 1)
+    SG_CHUNK(1, 2) SG_CHUNK(2, 2) SG_CHUNK(3, 2) SG_CHUNK(4, 2)
 #undef SG_CHUNK
     return hipErrorInvalidValue;
 }

@@ -357,7 +357,7 @@ def check_splitk(o):
             P = o.splitk_partials(x, W, S)
             assert P.shape == (S, M, N)
             close(o.splitk_sum(P), y, A, 1e-12, f"sum of partials = y (K={K}, S={S})")
-            c = 8 * -(-K // (8 * S))  # ceil(K/S) rounded up to a multiple of 8
+            c = 64 * -(-K // (64 * S))  # ceil(K/S) rounded up to a multiple of 64
             for s in range(S):
                 lo, hi = s * c, min(K, (s + 1) * c)
                 if lo >= hi:

@@ -67,7 +67,7 @@ def test_plan_kernel_by_batch():
     for M in range(1, 65):
         p = sg.skinny_gemm_plan(M, 4096, 7168)
         want = (sg.SG_KERNEL_GEMV if M <= 2 else
-                sg.SG_KERNEL_SPLITK_VALU if M < 16 else sg.SG_KERNEL_SPLITK_MFMA)
+                sg.SG_KERNEL_SPLITK_VALU if M < 8 else sg.SG_KERNEL_SPLITK_MFMA)
         assert p.kernel == want, (M, p)
         assert (p.M, p.N, p.K) == (M, 4096, 7168)
 
@@ -96,7 +96,7 @@ def test_plan_invariants(N, K):
         p = sg.skinny_gemm_plan(M, N, K)
         S, c = p.split_k, p.k_chunk
         assert S >= 1 and c % 8 == 0
-        assert c == 8 * -(-K // (8 * S)), "chunk is ceil(K / S) rounded up to a multiple of 8"
+        assert c == 64 * -(-K // (64 * S)), "chunk is ceil(K / S) rounded up to a multiple of 64"
         assert (S - 1) * c < K or K == 0, "no empty chunk in an automatic plan"
         if p.two_pass:
             assert S > 1
@@ -109,6 +109,10 @@ def test_plan_invariants(N, K):
             nch = -(-c // 512)
             cap = 16 if M <= 2 else 8 if M <= 4 else 4 if M <= 8 else 2
             assert nch <= cap, (M, N, K, p)
+        if p.kernel == sg.SG_KERNEL_SPLITK_MFMA and p.tile_n != 16:
+            assert p.tile_n in (128, 256)
+            tiles = -(-N // p.tile_n)
+            assert p.grid == -(-tiles // 8) * 8 * S, "column tiles padded to the 8 XCDs"
         assert p.grid >= 1
         assert sg.skinny_gemm_plan(M, N, K).as_dict() == p.as_dict(), "deterministic"
 
@@ -126,9 +130,9 @@ def test_plan_force():
     p = sg.skinny_gemm_plan_force(1, 4096, 7168, V, 14)
     assert p.kernel == V and p.k_chunk == 512
     p = sg.skinny_gemm_plan_force(4, 4096, 7168, F, 3)
-    assert p.k_chunk == 2392 and 2 * 2392 < 7168 <= 3 * 2392
+    assert p.k_chunk == 2432 and 2 * 2432 < 7168 <= 3 * 2432
     p = sg.skinny_gemm_plan_force(5, 1000, 2056, V, 2)
-    assert p.k_chunk == 1032 and not p.two_pass and p.workspace_bytes == 0
+    assert p.k_chunk == 1088 and not p.two_pass and p.workspace_bytes == 0
     p = sg.skinny_gemm_plan_force(5, 1000, 2056, V, 2, two_pass=1)
     assert p.two_pass and p.workspace_bytes >= 2 * 5 * 1000 * 4
     p = sg.skinny_gemm_plan_force(12, 4096, 7168, V, 0)
@@ -139,8 +143,14 @@ def test_plan_force():
     assert not p.two_pass and p.workspace_bytes == 0
     p = sg.skinny_gemm_plan(64, 4096, 7168)
     assert p.split_k == 8 and p.two_pass and p.grid == 32 * 8 and p.tile_n == 128
-    p = sg.skinny_gemm_plan_force(32, 4096, 7168, F, 5)
+    p = sg.skinny_gemm_plan_force(32, 4096, 7168, F, 5, tile_n=128)
     assert p.two_pass and p.grid == 32 * 5 and p.tile_n == 128
+    p = sg.skinny_gemm_plan_force(32, 4096, 7168, F, 16, tile_n=256)
+    assert p.two_pass and p.grid == 16 * 16 and p.tile_n == 256
+    p = sg.skinny_gemm_plan_force(64, 7168, 8192, F, 0, tile_n=256)
+    assert p.tile_n == 256 and p.grid == 32 * p.split_k, "28 tiles padded to 32"
+    p = sg.skinny_gemm_plan_force(20, 4096, 7168, F, 4, tile_n=16)
+    assert not p.two_pass and p.tile_n == 16, "tile_n 16 asks for the team kernel"
     p = sg.skinny_gemm_plan_force(64, 4096, 7168, F, 4, 0)
     assert not p.two_pass and p.tile_n == 16 and p.grid == 256, "team kernel"
     p = sg.skinny_gemm_plan_force(64, 4096, 7168, F, 2)
@@ -148,7 +158,9 @@ def test_plan_force():
     for args in [(3, 64, 64, G, 1), (16, 64, 64, V, 1), (4, 4096, 7168, F, 65),
                  (4, 4096, 7168, 9, 1), (8, 4096, 7168, V, 1), (8, 4096, 7168, V, 2),
                  (4, 4096, 7168, V, 3, 0), (16, 4096, 7168, F, 3, 0), (3, 4096, 7168, V, 8, 0),
-                 (16, 4096, 7168, F, 16, 0), (64, 4096, 7168, F, 3, 1)]:
+                 (16, 4096, 7168, F, 16, 0), (64, 4096, 7168, F, 3, 1),
+                 (16, 4096, 7168, F, 8, 1, 64), (16, 4096, 7168, F, 8, 1, 16),
+                 (64, 4096, 7168, F, 2, -1, 256)]:
         with pytest.raises(sg.SkinnyGemmError) as e:
             sg.skinny_gemm_plan_force(*args)
         assert e.value.status == 6, args

@@ -51,9 +51,9 @@ def oracle_rows(x, W, rows=None):
     return orc().projection(bits(x), Wb)
 
 
-def plan_or_skip(M, N, K, kernel, S, two_pass=-1):
+def plan_or_skip(M, N, K, kernel, S, two_pass=-1, tile_n=0):
     try:
-        return sg.skinny_gemm_plan_force(M, N, K, kernel, S, two_pass)
+        return sg.skinny_gemm_plan_force(M, N, K, kernel, S, two_pass, tile_n)
     except sg.SkinnyGemmError as e:
         assert e.status == 6
         pytest.skip(f"plan rejects kernel {kernel} with S={S} at M={M}, K={K}")
@@ -89,7 +89,7 @@ def test_small_shapes_auto_plan(M, N, K):
 @pytest.mark.parametrize("S", [1, 2, 3, 4, 8, 16])
 @pytest.mark.parametrize("two_pass", [0, 1])
 def test_valu_forced_splits(M, S, two_pass):
-    N, K = 300, 2112  # 264 pieces of 8: chunk widths 2112, 1056, 704, 528, 264, 136
+    N, K = 300, 2112  # 264 pieces of 8: chunk widths 2112, 1088, 704, 576, 320, 192 (ragged)
     plan = plan_or_skip(M, N, K, V, S, two_pass)
     announce(f"valu forced M={M} S={S} two_pass={two_pass}")
     x, W = make(M, N, K, 7100 + M)
@@ -100,11 +100,12 @@ def test_valu_forced_splits(M, S, two_pass):
 
 @pytest.mark.parametrize("M", [1, 4, 16, 17, 33, 48, 64])
 @pytest.mark.parametrize("S", [1, 2, 3, 4, 8])
-@pytest.mark.parametrize("two_pass", [0, 1])
-def test_mfma_forced_splits(M, S, two_pass):
+@pytest.mark.parametrize("tile", [16, 128, 256])
+def test_mfma_forced_splits(M, S, tile):
+    # N = 200: one ragged 128- or 256-row tile; K = 2112 = 264 pieces: ragged rounds
     N, K = 200, 2112
-    plan = plan_or_skip(M, N, K, F, S, two_pass)
-    announce(f"mfma forced M={M} S={S} two_pass={two_pass}")
+    plan = plan_or_skip(M, N, K, F, S, 0 if tile == 16 else 1, tile)
+    announce(f"mfma forced M={M} S={S} tile={tile}")
     x, W = make(M, N, K, 7200 + M)
     y32, y16, _ = run(plan, x, W)
     y, A = oracle_rows(x, W)
@@ -120,10 +121,13 @@ def test_mfma_forced_splits(M, S, two_pass):
                                            (V, 15, 8, 0), (V, 15, 8, 1), (V, 11, 16, 1),
                                            (F, 16, 1, 0), (F, 16, 4, 1), (F, 16, 8, 0),
                                            (F, 64, 2, 1), (F, 64, 8, 0), (F, 64, 16, 1),
-                                           (F, 5, 2, 1), (F, 37, 4, 0)])
+                                           (F, 5, 2, 1), (F, 37, 4, 0), (F, 64, 9, 256),
+                                           (F, 20, 16, 256), (F, 8, 8, 128)])
 def test_integer_inputs_bit_exact(kernel, M, S, tp):
+    # tp: 0 / 1 in-kernel / second-pass reduction, or 128 / 256 the chunk kernel's tile
     N, K = 520, 8192  # |sums| <= 16 * 8192 < 2^24: every fp32 partial is exact
-    plan = plan_or_skip(M, N, K, kernel, S, tp)
+    plan = (plan_or_skip(M, N, K, kernel, S, 1, tp) if tp >= 128
+            else plan_or_skip(M, N, K, kernel, S, tp))
     announce(f"integer bit-exact kernel={kernel} M={M} S={S}")
     x = si.integer_bf16((M, K), -4, 4, 8000 + M, DEV)
     W = si.integer_bf16((N, K), -4, 4, 8001 + M, DEV)
@@ -144,12 +148,13 @@ def test_integer_inputs_bit_exact(kernel, M, S, tp):
 # ------------------------------------------------------------------ full workload sizes
 
 
-def _full_case(M, N, K, seed, kernel=None, S=0, rows=256, residual=False, inplace=False, tp=-1):
+def _full_case(M, N, K, seed, kernel=None, S=0, rows=256, residual=False, inplace=False, tp=-1,
+               tile=0):
     x, W = make(M, N, K, seed)
     r = si.normal_bf16((M, N), 1.0, seed + si.TAG_R, DEV) if residual else None
     r_before = r.clone() if r is not None else None
     plan = (sg.skinny_gemm_plan(M, N, K) if kernel is None
-            else plan_or_skip(M, N, K, kernel, S, tp))
+            else plan_or_skip(M, N, K, kernel, S, tp, tile))
     announce(f"full M={M} N={N} K={K} plan={plan} residual={residual} inplace={inplace}")
     y32, y16, _ = run(plan, x, W, r=r, inplace=inplace)
     sel = sample_rows(N, rows, seed)
@@ -192,8 +197,14 @@ def test_full_splitk_sweep_auto(M):
 @pytest.mark.parametrize("S", [2, 4, 8, 16])
 @pytest.mark.parametrize("tp", [-1, 1])
 def test_full_splitk_sweep_forced(M, S, tp):
-    kernel = V if M < 16 else F
+    kernel = V if M < 8 else F
     _full_case(M, 4096, 7168, 3000, kernel=kernel, S=S, rows=128, tp=tp)
+
+
+@pytest.mark.parametrize("M,S", [(8, 8), (16, 16), (64, 16), (64, 9)])
+def test_full_mfma_32_rows_per_wave(M, S):
+    plan = _full_case(M, 4096, 7168, 3100, kernel=F, S=S, rows=128, tp=1, tile=256)
+    assert plan.tile_n == 256
 
 
 @pytest.mark.parametrize("M", [1, 8, 64])

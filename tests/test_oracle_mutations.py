@@ -33,10 +33,12 @@ MUTANTS = [
     ("mantissa width", "? -133 : E - 7", "? -133 : E - 8"),
     ("overflow threshold", "if (rounded > ldexp(", "if (rounded >= ldexp("),
     ("decode shift", "(uint32_t)bits << 16", "(uint32_t)bits << 15"),
-    ("split-K unaligned chunk", "int64_t chunk = 8 * ((K + 8 * S - 1) / (8 * S));",
+    ("split-K unaligned chunk", "int64_t chunk = 64 * ((K + 64 * S - 1) / (64 * S));",
      "int64_t chunk = (K + S - 1) / S;"),
-    ("split-K floor chunk", "int64_t chunk = 8 * ((K + 8 * S - 1) / (8 * S));",
-     "int64_t chunk = 8 * (K / (8 * S));"),
+    ("split-K 16-byte chunk", "int64_t chunk = 64 * ((K + 64 * S - 1) / (64 * S));",
+     "int64_t chunk = 8 * ((K + 8 * S - 1) / (8 * S));"),
+    ("split-K floor chunk", "int64_t chunk = 64 * ((K + 64 * S - 1) / (64 * S));",
+     "int64_t chunk = 64 * (K / (64 * S));"),
     ("split-K chunk overlap", "int64_t k_begin = s * chunk;", "int64_t k_begin = s * chunk - (s > 0);"),
     ("split-K descending sum", "for (int64_t s = 0; s < S; ++s)\n            sum += P[s * MN + i];",
      "for (int64_t s = S - 1; s >= 0; --s)\n            sum += P[s * MN + i];"),
