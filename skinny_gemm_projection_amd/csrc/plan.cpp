@@ -9,9 +9,12 @@
 //   3 <= M <= 7   the same kernel on K chunks (split-K), the split sized so
 //                 the M x-rows of a chunk fit in its registers, reduced
 //                 inside the workgroup when the split allows;
-//   8 <= M <= 64  bf16 matrix-core split-K; split factor and row tiling from
-//                 a per-compute-unit byte cost model; then the deterministic
-//                 reduction.
+//   8 <= M <= 64  bf16 matrix-core split-K: up to 12 rows the team kernel
+//                 (K split over the waves of a workgroup, reduced in LDS)
+//                 when N/16 workgroups fill the GPU; otherwise the chunk
+//                 kernel, split factor and row tiling from a
+//                 per-compute-unit byte cost model, then the deterministic
+//                 reduction kernel.
 // A small table measured on MI355X overrides the split factor for known
 // shapes.  Everything here is host arithmetic; no GPU call is made.
 #include <cstdlib>
@@ -31,6 +34,7 @@ constexpr int kComputeUnits = 256;
 // against 13.8 us MFMA; M=12: 20.7 against 14.0), while at M <= 6 the VALU
 // kernel, which needs no second pass, is faster (M=4: 12.8 against 13.8).
 constexpr int32_t kMfmaFromM = 8;
+constexpr int32_t kTeamUpToM = 12;
 
 // Choices measured on MI355X for known projection shapes, overriding the
 // defaults: {M_lo, M_hi, N, K, kernel (0: default), split (0: default)}.
@@ -38,9 +42,7 @@ struct Tuned {
     int32_t m_lo, m_hi, n, k, kernel, split;
 };
 constexpr Tuned kTuned[] = {
-    // output projection 8192 -> 7168 at M = 8: the VALU kernel (23.8 us)
-    // beats the best matrix-core plan (24.9 us)
-    {8, 8, 7168, 8192, SG_KERNEL_SPLITK_VALU, 0},
+    {0, 0, 0, 0, 0, 0},  // none yet: the defaults are the measured best on the benchmark shapes
 };
 
 bool split_ok(int32_t S) { return S >= 1 && S <= kMaxSplit; }
@@ -181,7 +183,16 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
             // Default: the chunk kernel, its S partials summed by the second
             // pass.  two_pass == 0 asks for the team kernel (S in 1, 2, 4, 8
             // reduced inside the workgroup).
-            const bool team_asked = two_pass == 0 || tile_n == kMfmaTeamTileN;
+            // Up to 12 rows the team kernel -- no workspace, no second
+            // launch -- when its grid of N/16 workgroups fills the compute
+            // units.  It reads x from L2 once per weight byte (times the
+            // x row tiles), and on MI355X it stops paying off past M = 12
+            // (K=7168, N=4096: M=8 12.9 us against 14.1 us for the chunk
+            // kernel and its reduction, M=16 15.0 against 14.2).
+            const bool team_auto = two_pass < 0 && tile_n == 0 && M <= kTeamUpToM &&
+                                   (N + kMfmaTeamTileN - 1) / kMfmaTeamTileN >= kComputeUnits &&
+                                   (split_k <= 0 || mfma_team_split_ok(split_k));
+            const bool team_asked = two_pass == 0 || tile_n == kMfmaTeamTileN || team_auto;
             int32_t S = 0, t = 0;
             if (!team_asked && tile_n != 0 && tile_n != kMfmaTileN && tile_n != 2 * kMfmaTileN)
                 return SG_ERR_PLAN;

@@ -28,9 +28,10 @@
 //    padded to a multiple of the 8 XCDs: workgroups are dispatched to XCDs
 //    round-robin by linear id, so all S splits of a column tile run on one
 //    XCD and the tiled reduction finds their partials in that XCD's L2.
-//  * team kernel: S waves of one workgroup split K over a 16-row tile, read
-//    x straight from L2, and add their S partial tiles in LDS in ascending
-//    split order (no workspace, no second pass).
+//  * team kernel: S waves of one workgroup split K over a 16-row tile (the
+//    same weight streaming), read x straight from L2, and add their S
+//    partial tiles in LDS in ascending split order (no workspace, no second
+//    pass).
 
 #include "launch.h"
 
@@ -222,77 +223,109 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
     }
 }
 
-// Team kernel: S waves of one workgroup share a 16-row tile of W and split
-// K between them; all M rows of x (padded to 16*MT) go through each wave.
-// There is no barrier in the main loop: every wave keeps D k-steps of its W
-// operand (nt buffer loads from HBM) and of its x operands (buffer loads,
-// L2-resident) in flight in a register ring, refilling a slot right after
-// the matrix ops that consumed it.  Steps past the chunk read zeros and add
-// nothing.  At the end the S partial tiles are added in LDS in ascending
-// split order (deterministic) and wave w finishes the outputs o with
-// o % S == w.
-template <int MT, int S, int D>
+// Team kernel: the S waves of one workgroup share a 16-row tile of W and
+// split K between them (wave s streams chunk s).  The weights arrive as in
+// the chunk kernel -- 4 rows x 256 bytes per load, transposed through a
+// per-wave LDS tile -- while the x operands of each k step are loaded
+// straight from L2 into the same register ring (x is small and every
+// workgroup reads all of it; at MT row tiles that is MT times the weight
+// bytes, so the planner uses this kernel for M <= 16).  There is no barrier
+// in the main loop.  At the end the S partial tiles are added in LDS in
+// ascending split order (deterministic) and wave w finishes the outputs o
+// with o % S == w: no workspace and no second kernel.
+template <int MT, int S, int DR>
 __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __restrict__ x,
                                                               const uint4* __restrict__ W, int M,
                                                               int N, int K8, int chunk8,
                                                               Epilogue ep) {
     constexpr int OUT = MT * 4;  // accumulator floats per lane
+    constexpr int RP = 16;       // pieces per row per round
     constexpr uint32_t kOff = 0xFFFFFFF0u;  // past any descriptor range: reads zero
+    __shared__ uint4 tiles[S][kTileSlots];
     __shared__ float red[S][OUT][kWave];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int s = wave_id_in_block();
     const int col = lane & 15;
     const int grp = lane >> 4;
+    uint4* tile = tiles[s];
     const int row0 = blockIdx.x * 16;
-    const int rows = max(0, min(16, N - row0));
-    const bool n_ok = col < rows;
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16, N - row0)));
     const int k0 = s * chunk8;
     const int len = max(0, min(K8 - k0, chunk8));  // pieces of this wave's chunk
-    const int steps = (len + 3) / 4;                // 32-wide k steps
+    const int rounds = (len + RP - 1) / RP;
 
     const rsrc_t wrs = make_rsrc(W + (int64_t)row0 * K8, (uint32_t)rows * (uint32_t)K8 * 16u);
     const rsrc_t xrs = make_rsrc(x, (uint32_t)M * (uint32_t)K8 * 16u);
-    const uint32_t w_lane = ((uint32_t)col * K8 + k0 + grp) * 16u;
-    uint32_t x_lane[MT];
-    bool x_ok[MT];
+    // weights: load i of a round reads row 4i + grp, slot col = piece col ^ row
+    uint32_t woff[4];
+    int wpiece[4];
+    bool wrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + grp;
+        wpiece[i] = col ^ r;
+        wrow[i] = r < rows;
+        woff[i] = ((uint32_t)r * K8 + k0 + wpiece[i]) * 16u;
+    }
+    // x: the A operand of step t is piece 16*rd + 4t + grp of row 16*mt + col
+    uint32_t xoff[MT];
+    bool xrow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int m = mt * 16 + col;
-        x_ok[mt] = m < M;
-        x_lane[mt] = ((uint32_t)m * K8 + k0 + grp) * 16u;
+        xrow[mt] = m < M;
+        xoff[mt] = ((uint32_t)m * K8 + k0 + grp) * 16u;
     }
-
-    uint4 wb[D];
-    uint4 xb[D][MT];
-    auto load_step = [&](int t, uint4& w, uint4 (&xv)[MT]) {
-        const bool ok = t * 4 + grp < len;
-        w = load16<kStream>(wrs, (n_ok && ok) ? w_lane + (uint32_t)t * 64u : kOff);
+    auto load_round = [&](int rd, uint4 (&w)[4], uint4 (&a)[4][MT]) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            xv[mt] = load16<kCached>(xrs, (x_ok[mt] && ok) ? x_lane[mt] + (uint32_t)t * 64u : kOff);
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = wrow[i] && (rd * RP + wpiece[i] < len);
+            w[i] = load16<kStream>(wrs, ok ? woff[i] + (uint32_t)rd * (RP * 16u) : kOff);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const bool ok = xrow[mt] && (rd * RP + 4 * t + grp < len);
+                a[t][mt] = load16<kCached>(
+                    xrs, ok ? xoff[mt] + (uint32_t)(rd * RP + 4 * t) * 16u : kOff);
+            }
     };
 
+    uint4 wb[DR][4];
+    uint4 xb[DR][4][MT];
+#pragma unroll
+    for (int d = 0; d < DR; ++d) load_round(d, wb[d], xb[d]);
     f32x4_t acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int r0 = 0; r0 < rounds; r0 += DR) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) load_step(d, wb[d], xb[d]);
-    for (int t0 = 0; t0 < steps; t0 += D) {
+        for (int d = 0; d < DR; ++d) {
+            const int rd = r0 + d;
+            if (rd < rounds) {  // wave-uniform
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, wb[d]);
+                for (int i = 0; i < 4; ++i) tile[(4 * i + grp) * RP + col] = wb[d][i];
+                __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, xb[d][mt]), bop, acc[mt], 0, 0, 0);
-            load_step(t0 + d + D, wb[d], xb[d]);
+                for (int t = 0; t < 4; ++t) {
+                    const uint4 b = tile[col * RP + ((4 * t + grp) ^ col)];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, xb[d][t][mt]),
+                            __builtin_bit_cast(bf16x8_t, b), acc[mt], 0, 0, 0);
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
+            load_round(rd + DR, wb[d], xb[d]);  // past the chunk: no memory access
         }
     }
 
     const int n = row0 + col;
     if (S == 1) {
-        if (!n_ok) return;
+        if (col >= rows) return;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -307,7 +340,7 @@ __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __res
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[s][mt * 4 + v][lane] = acc[mt][v];
     __syncthreads();
-    if (!n_ok) return;
+    if (col >= rows) return;
 #pragma unroll
     for (int o = 0; o < OUT; ++o) {
         if (o % S != s) continue;
@@ -331,10 +364,10 @@ hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void*
     const uint4* xp = static_cast<const uint4*>(x);
     const uint4* wp = static_cast<const uint4*>(W);
     const int MT = (M + 15) / 16;
-    constexpr int D = 8;
+    constexpr int DR = 2;  // rounds in flight per wave
 #define SG_TEAM(mt, sp) \
     if (MT == mt && S == sp) { \
-        mfma_team_kernel<mt, sp, D><<<grid, kWave * sp, 0, stream>>>(xp, wp, M, N, K8, chunk8, ep); \
+        mfma_team_kernel<mt, sp, DR><<<grid, kWave * sp, 0, stream>>>(xp, wp, M, N, K8, chunk8, ep); \
         return hipGetLastError(); \
     }
     SG_TEAM(1, 1) SG_TEAM(1, 2) SG_TEAM(1, 4) SG_TEAM(1, 8)
