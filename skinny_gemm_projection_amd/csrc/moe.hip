@@ -16,35 +16,79 @@ namespace sg {
 namespace {
 
 constexpr int kTableThreads = 1024;
+constexpr int kTableWaves = kTableThreads / kWave;
 constexpr int kMaxPairs = 4096;
 constexpr int kMaxExperts = 4096;
 
-// One workgroup.  counts[e] by LDS integer atomics; offsets and the list of
-// active experts by one block-wide scan; then each valid pair p lands at
-// offsets[e] + (number of earlier pairs with the same expert), which keeps
-// every expert's segment in ascending p.  Pairs with an id outside [0, E)
-// are counted and their output rows zero-filled.
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int u = __shfl_up(v, d, kWave);
+        if (lane >= d) v += u;
+    }
+    return v;
+}
+
+// Exclusive prefix sums of a and b over the threads of the workgroup (in
+// thread order); *total_a / *total_b receive the sums.  Two barriers.
+__device__ __forceinline__ void block_exclusive_scan2(int a, int b, int* ex_a, int* ex_b,
+                                                      int* total_a, int* total_b,
+                                                      int (*s_wave)[kTableWaves]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int ia = wave_inclusive_scan(a);
+    const int ib = wave_inclusive_scan(b);
+    if (lane == kWave - 1) {
+        s_wave[0][wv] = ia;
+        s_wave[1][wv] = ib;
+    }
+    __syncthreads();
+    int base_a = 0, base_b = 0, ta = 0, tb = 0;
+    for (int w = 0; w < kTableWaves; ++w) {  // 16 LDS broadcast reads
+        const int va = s_wave[0][w], vb = s_wave[1][w];
+        if (w < wv) {
+            base_a += va;
+            base_b += vb;
+        }
+        ta += va;
+        tb += vb;
+    }
+    *ex_a = base_a + ia - a;
+    *ex_b = base_b + ib - b;
+    *total_a = ta;
+    *total_b = tb;
+}
+
+// One workgroup builds the table.
+//  1. counts[e] by LDS integer atomics; ids outside [0, E) are left out
+//     (their number is P minus the counts' sum);
+//  2. offsets (exclusive scan of counts) and the ascending list of active
+//     experts (exclusive scan of counts > 0), by wave-level scans;
+//  3. every valid pair p is dropped into its expert's segment at a slot
+//     taken with an LDS atomic (arbitrary order) ...
+//  4. ... and then moved to offsets[e] + (number of pairs of the segment
+//     with a smaller p), which orders every segment by ascending p.  A
+//     thread does work proportional to its segment's length.
+// Output rows of invalid pairs are zero-filled.
 __global__ __launch_bounds__(kTableThreads) void moe_table_kernel(
     const int32_t* __restrict__ ids, int P, int E, int N, GroupedWorkspace g,
     int32_t* user_offsets, int32_t* user_sorted, int32_t* user_invalid, float* out) {
     __shared__ int32_t s_ids[kMaxPairs];
+    __shared__ int32_t s_tmp[kMaxPairs];     // scan scratch first, then the unordered segments
+    __shared__ int32_t s_cnt[kMaxExperts];  // counts, then fill cursors
     __shared__ int32_t s_off[kMaxExperts];
-    __shared__ int32_t s_scan_c[kTableThreads];
-    __shared__ int32_t s_scan_a[kTableThreads];
-    __shared__ int32_t s_inv;
+    int (*s_wave)[kTableWaves] = reinterpret_cast<int (*)[kTableWaves]>(s_tmp);
 
     const int tid = threadIdx.x;
     for (int p = tid; p < P; p += kTableThreads) s_ids[p] = ids[p];
-    for (int e = tid; e < E; e += kTableThreads) s_off[e] = 0;
-    if (tid == 0) s_inv = 0;
+    for (int e = tid; e < E; e += kTableThreads) s_cnt[e] = 0;
     __syncthreads();
 
     for (int p = tid; p < P; p += kTableThreads) {
         const int e = s_ids[p];
-        if (e >= 0 && e < E)
-            atomicAdd(&s_off[e], 1);
-        else
-            atomicAdd(&s_inv, 1);
+        if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
     }
     __syncthreads();
 
@@ -54,24 +98,13 @@ __global__ __launch_bounds__(kTableThreads) void moe_table_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = 4 * tid + j;
-        c[j] = (e < E) ? s_off[e] : 0;
+        c[j] = (e < E) ? s_cnt[e] : 0;
         sum_c += c[j];
         sum_a += c[j] > 0;
     }
-    s_scan_c[tid] = sum_c;
-    s_scan_a[tid] = sum_a;
-    __syncthreads();
-    for (int off = 1; off < kTableThreads; off <<= 1) {
-        const int vc = tid >= off ? s_scan_c[tid - off] : 0;
-        const int va = tid >= off ? s_scan_a[tid - off] : 0;
-        __syncthreads();
-        s_scan_c[tid] += vc;
-        s_scan_a[tid] += va;
-        __syncthreads();
-    }
-    int pc = s_scan_c[tid] - sum_c;  // exclusive prefix of counts
-    int pa = s_scan_a[tid] - sum_a;  // exclusive prefix of active flags
-    const int total = s_scan_c[kTableThreads - 1];
+    int pc, pa, total, num_active;
+    block_exclusive_scan2(sum_c, sum_a, &pc, &pa, &total, &num_active, s_wave);
+    const int invalid = P - total;  // pairs whose id is outside [0, E)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = 4 * tid + j;
@@ -80,6 +113,7 @@ __global__ __launch_bounds__(kTableThreads) void moe_table_kernel(
             g.offsets[e] = pc;
             if (user_offsets) user_offsets[e] = pc;
             s_off[e] = pc;
+            s_cnt[e] = pc;  // fill cursor
             if (c[j] > 0) g.active[pa++] = e;
             pc += c[j];
         }
@@ -87,27 +121,34 @@ __global__ __launch_bounds__(kTableThreads) void moe_table_kernel(
     if (tid == 0) {
         g.offsets[E] = total;
         if (user_offsets) user_offsets[E] = total;
-        *g.num_active = s_scan_a[kTableThreads - 1];
-        *g.invalid = s_inv;
-        if (user_invalid) *user_invalid = s_inv;
+        *g.num_active = num_active;
+        *g.invalid = invalid;
+        if (user_invalid) *user_invalid = invalid;
     }
-    __syncthreads();
+    __syncthreads();  // every thread is past its reads of s_wave (aliasing s_tmp)
 
     for (int p = tid; p < P; p += kTableThreads) {
         const int e = s_ids[p];
-        if (e >= 0 && e < E) {
-            int rank = 0;
-            for (int q = 0; q < p; ++q) rank += (s_ids[q] == e);
-            g.sorted[s_off[e] + rank] = p;
-            if (user_sorted) user_sorted[s_off[e] + rank] = p;
-        }
+        if (e >= 0 && e < E) s_tmp[atomicAdd(&s_cnt[e], 1)] = p;
+    }
+    __syncthreads();
+
+    for (int i = tid; i < total; i += kTableThreads) {
+        const int p = s_tmp[i];
+        const int e = s_ids[p];
+        const int lo = s_off[e];
+        const int hi = s_cnt[e];  // the fill cursor stopped at the segment's end
+        int rank = 0;
+        for (int j = lo; j < hi; ++j) rank += s_tmp[j] < p;
+        g.sorted[lo + rank] = p;
+        if (user_sorted) user_sorted[lo + rank] = p;
     }
     for (int i = total + tid; i < P; i += kTableThreads) {
         g.sorted[i] = -1;
         if (user_sorted) user_sorted[i] = -1;
     }
 
-    if (s_inv > 0) {  // rare: zero-fill the output rows of out-of-range ids
+    if (invalid > 0) {  // rare: zero-fill the output rows of out-of-range ids
         for (int p = 0; p < P; ++p) {
             const int e = s_ids[p];
             if (e < 0 || e >= E)
