@@ -37,12 +37,17 @@ constexpr int32_t kMfmaFromM = 8;
 constexpr int32_t kTeamUpToM = 12;
 
 // Choices measured on MI355X for known projection shapes, overriding the
-// defaults: {M_lo, M_hi, N, K, kernel (0: default), split (0: default)}.
+// defaults: {M_lo, M_hi, N, K, kernel (0: default), split (0: default),
+// matrix-core tile width (0: default)}.
 struct Tuned {
-    int32_t m_lo, m_hi, n, k, kernel, split;
+    int32_t m_lo, m_hi, n, k, kernel, split, tile_n;
 };
 constexpr Tuned kTuned[] = {
-    {0, 0, 0, 0, 0, 0},  // none yet: the defaults are the measured best on the benchmark shapes
+    // 64-row batches on the 117 MB projections: 256-row workgroups in 8
+    // splits (32.9 us at 8192 -> 7168, 29.8 us at 7168 -> 8192) beat the
+    // cost model's pick of 9 splits (41.4 us) and 128-row tiles (35.7 us)
+    {33, 64, 7168, 8192, SG_KERNEL_SPLITK_MFMA, 8, 256},
+    {33, 64, 8192, 7168, SG_KERNEL_SPLITK_MFMA, 8, 256},
 };
 
 bool split_ok(int32_t S) { return S >= 1 && S <= kMaxSplit; }
@@ -83,41 +88,52 @@ bool mfma_chunk_fits(int32_t M, int32_t K, int32_t S, int32_t tile_n) {
 
 // Cost of a chunk-kernel plan in bytes per compute unit: the weight bytes of
 // the busiest unit -- ceil(tiles*S / 256) workgroups of tile_n rows x K/S --
-// plus half the x bytes those workgroups stage from L2 into LDS, plus the
-// partials written and read back (2 * S*M*N*4 bytes over the 256 units).
+// plus half the x bytes those workgroups stage from L2 into LDS, plus a
+// tenth of the x operand bytes read back from LDS (MT/NT per weight byte),
+// plus the partials written and read back (2 * S*M*N*4 bytes over the 256
+// units).
 int64_t mfma_cost(int32_t M, int32_t N, int32_t K, int32_t S, int32_t tile_n) {
     const int64_t tiles = (N + tile_n - 1) / tile_n;
     const int64_t per_unit = (tiles * S + kComputeUnits - 1) / kComputeUnits;
     const int64_t chunk = chunk_of(K, S);
     const int64_t w_bytes = per_unit * tile_n * 2 * chunk;
     const int64_t x_bytes = per_unit * M * chunk;
+    const int64_t mt = (M + 15) / 16, nt = tile_n / sg::kMfmaTileN;
+    const int64_t lds_bytes = w_bytes * mt / nt / 10;
     const int64_t p_bytes = 8 * (int64_t)S * M * N / kComputeUnits;
-    return w_bytes + x_bytes + p_bytes;
+    return w_bytes + x_bytes + lds_bytes + p_bytes;
 }
 
 // Split and tile width for the matrix-core chunk kernel: the cheapest pair
 // whose x chunk fits in LDS (ties: the smaller split, then 128-row tiles).
-// A forced split or tile width narrows the search.  False if nothing fits.
+// Splits that cut K into equal whole-line chunks are preferred: on MI355X a
+// ragged split measured slower than the equal split next to it despite a
+// shorter chunk (K=8192, M=16: 9 splits 26.2 us, 8 splits 25.2 us).  A
+// forced split or tile width narrows the search.  False if nothing fits.
 bool mfma_choose(int32_t M, int32_t N, int32_t K, int32_t force_split, int32_t force_tile,
                  int32_t* split, int32_t* tile_n) {
-    bool found = false;
-    int64_t best_cost = 0;
-    for (int32_t t = sg::kMfmaTileN; t <= 2 * sg::kMfmaTileN; t *= 2) {
-        if (force_tile > 0 && t != force_tile) continue;
-        for (int32_t S = 1; S <= kMaxSplit; ++S) {
-            if (force_split > 0 && S != force_split) continue;
-            if (force_split <= 0 && !no_empty_chunk(K, S)) break;
-            if (!mfma_chunk_fits(M, K, S, t)) continue;
-            const int64_t cost = mfma_cost(M, N, K, S, t);
-            if (!found || cost < best_cost) {
-                found = true;
-                best_cost = cost;
-                *split = S;
-                *tile_n = t;
+    for (int pass = 0; pass < 2; ++pass) {  // 0: equal chunks only, 1: any
+        bool found = false;
+        int64_t best_cost = 0;
+        for (int32_t t = sg::kMfmaTileN; t <= 2 * sg::kMfmaTileN; t *= 2) {
+            if (force_tile > 0 && t != force_tile) continue;
+            for (int32_t S = 1; S <= kMaxSplit; ++S) {
+                if (force_split > 0 && S != force_split) continue;
+                if (force_split <= 0 && !no_empty_chunk(K, S)) break;
+                if (pass == 0 && force_split <= 0 && K % (64 * S) != 0) continue;
+                if (!mfma_chunk_fits(M, K, S, t)) continue;
+                const int64_t cost = mfma_cost(M, N, K, S, t);
+                if (!found || cost < best_cost) {
+                    found = true;
+                    best_cost = cost;
+                    *split = S;
+                    *tile_n = t;
+                }
             }
         }
+        if (found) return true;
     }
-    return found;
+    return false;
 }
 
 const Tuned* tuned_for(int32_t M, int32_t N, int32_t K) {
@@ -157,6 +173,7 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
         if (const Tuned* t = tuned_for(M, N, K)) {
             if (t->kernel > 0) kernel = t->kernel;
             if (split_k <= 0 && t->split > 0) split_k = t->split;
+            if (tile_n <= 0 && t->tile_n > 0) tile_n = t->tile_n;
         }
     }
 

@@ -1,7 +1,7 @@
 // splitk_mfma.hip -- split-K projection on bf16 matrix cores (gfx950).
 //
-// For batches of 16 and more rows the activation tile is a real dense
-// contraction, so the partial products run on v_mfma_f32_16x16x32_bf16
+// From 8 rows of batch up the activation tile is dense enough that the
+// partial products run on v_mfma_f32_16x16x32_bf16
 // ("Hyper Optimizing Kimi K3 in vLLM" deepnotes page, Method details §1:
 // split-K at larger batch; the accumulation dimension is spread over more
 // compute units).
@@ -14,20 +14,21 @@
 // have to agree on which 8 k values each lane group supplies.
 //
 // Two kernels:
-//  * chunk kernel (default): a workgroup of 8 waves owns 128 rows of W and
-//    one K chunk; the x chunk is staged in LDS once.  Loading the B operand
-//    straight from HBM would read 16 rows x 64 bytes per instruction, which
-//    streams about 20% slower than whole 256-byte row segments, so each wave
-//    loads W as 4 rows x 256 bytes per instruction (16 pieces of 16 bytes of
-//    each of its 16 rows per "round"), writes the round to a 4 KB LDS tile
-//    of its own and reads it back in operand layout.  Slot c of row r in the
-//    tile holds piece c ^ r (an XOR swizzle), so the operand read -- 16
-//    different rows at one piece each -- hits 16 different bank groups.
-//    Partials go to the [S, M, N] workspace and the deterministic reduction
-//    kernel adds them (two-pass split-K).  The grid's column-tile count is
-//    padded to a multiple of the 8 XCDs: workgroups are dispatched to XCDs
-//    round-robin by linear id, so all S splits of a column tile run on one
-//    XCD and the tiled reduction finds their partials in that XCD's L2.
+//  * chunk kernel (default): a workgroup of 8 waves owns 128 (or 256) rows
+//    of W and one K chunk, processed in rounds; x of each round is staged in
+//    a double-buffered LDS block while the previous round is multiplied.
+//    Loading the B operand straight from HBM would read 16 rows x 64 bytes
+//    per instruction, which streams about 20% slower than whole 256-byte row
+//    segments, so each wave loads W as 4 rows x 256 bytes (or 8 x 128) per
+//    instruction, writes the round to a 4 KB LDS tile of its own and reads
+//    it back in operand layout.  Slot c of row r in the tile holds piece
+//    c ^ swz(r) (an XOR swizzle), so the operand read -- 16 different rows
+//    at one piece each -- hits 16 different bank groups.  Partials go to the
+//    [S, M, N] workspace and the deterministic reduction kernel adds them
+//    (two-pass split-K).  The grid's column-tile count is padded to a
+//    multiple of the 8 XCDs: workgroups are dispatched to XCDs round-robin
+//    by linear id, so all S splits of a column tile run on one XCD and the
+//    tiled reduction finds their partials in that XCD's L2.
 //  * team kernel: S waves of one workgroup split K over a 16-row tile (the
 //    same weight streaming), read x straight from L2, and add their S
 //    partial tiles in LDS in ascending split order (no workspace, no second
@@ -40,8 +41,8 @@ namespace sg {
 namespace {
 
 constexpr int kChunkWaves = 8;
-constexpr int kTileSlots = 256;       // weight tile of one wave: 4 KB
-constexpr int kXLoadsPerThread = 16;  // x staging loads per thread (LDS bound)
+constexpr int kChunkThreads = kWave * kChunkWaves;
+constexpr int kTileSlots = 256;  // weight tile of one wave: 4 KB
 
 // Geometry of the chunk kernel for NT row tiles (16 rows each) per wave: a
 // round covers 16/NT pieces of each of the wave's 16*NT rows (4 KB), loaded
@@ -61,18 +62,25 @@ struct ChunkGeom {
     }
 };
 
-// Row pitch (16-byte units) of the staged x chunk: whole rounds plus one, odd,
-// so the 16 rows read by one operand load fall in 16 different bank groups.
-__host__ __device__ inline int x_pitch(int chunk8, int round_pieces) {
-    return (chunk8 + round_pieces - 1) / round_pieces * round_pieces + 1;
-}
+constexpr int kXLoadsMax = 16;  // x staging loads per thread and phase
 
-template <int MT, int NT, int DR>
-__global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
+// Chunk kernel.  A workgroup of 8 waves owns 128*NT rows of W and one K
+// chunk, processed in rounds of 16/NT pieces.  Each wave streams its own
+// 16*NT weight rows, DR rounds in flight in a register ring, transposed
+// through its own LDS tile into operand layout; the waves run independently
+// except at phase boundaries.  x is staged in LDS by phases of `phase`
+// pieces: when the whole chunk fits (one phase) it is staged once before
+// the loop and the loop has no barrier at all; otherwise two phase buffers
+// alternate -- x of the next phase is loaded into registers while the
+// current phase is multiplied, written to the other buffer at its end, and
+// one barrier per phase publishes it.
+template <int MT, int NT, int DR, bool PHASED>
+__global__ __launch_bounds__(kChunkThreads) void splitk_mfma_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ W, int M, int N, int K8, int chunk8,
-    Epilogue ep) {
+    int phase, Epilogue ep) {
     using G = ChunkGeom<NT>;
     constexpr int RP = G::kRoundPieces;
+    constexpr int XROWS = 16 * MT;
     extern __shared__ uint4 lds[];
     constexpr uint32_t kOff = 0xFFFFFFF0u;  // past any descriptor range: reads zero
     const int tid = threadIdx.x;
@@ -83,12 +91,14 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
     const int s = blockIdx.y;
     const int k0 = s * chunk8;
     const int len = max(0, min(K8 - k0, chunk8));  // pieces of this chunk
-    // whole rounds: x is staged as zeros past len and the weights past len
-    // load as zeros, so every k step of a round runs unconditionally
-    const int lenr = (len + RP - 1) / RP * RP;
-    const int pitch = x_pitch(chunk8, RP);
-    uint4* xs = lds;                                  // [16*MT][pitch]
-    uint4* tile = lds + 16 * MT * pitch + wv * kTileSlots;
+    const int rounds = (len + RP - 1) / RP;        // workgroup-uniform
+    const int pr = phase / RP;                      // rounds per phase
+    // PHASED == false: the launcher made the phase cover every chunk
+    const int nphases = PHASED ? (rounds + pr - 1) / pr : 1;
+    const int xp = phase + 1;                       // odd row pitch of a phase buffer
+    const int xslots = XROWS * xp;
+    uint4* xs = lds;                                // [1 or 2][XROWS][xp]
+    uint4* tile = lds + (nphases > 1 ? 2 : 1) * xslots + wv * kTileSlots;
 
     if (blockIdx.x * G::kWgRows >= N) return;  // padding column of the grid
     const int row0 = blockIdx.x * G::kWgRows + wv * G::kRows;
@@ -117,42 +127,60 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
         }
     };
 
-    // x loads go out first (they hit L2 and return early), then the first DR
-    // weight rounds, then the x values are written to LDS: waiting for the x
-    // loads does not wait for the weight stream.
-    const int xtotal = 16 * MT * lenr;
-    const int div = max(lenr, RP);
-    const int step_rows = (kWave * kChunkWaves) / div;  // idx += 512 moves this many rows
-    const int step_p = (kWave * kChunkWaves) - step_rows * div;  // ... and this many pieces
-    const int nx = (xtotal + kWave * kChunkWaves - 1) / (kWave * kChunkWaves);  // <= 16
+    // x of a phase: thread t stages the pieces t, t+512, ... of the phase's
+    // XROWS x phase block (row = idx / phase, piece = idx % phase); past M or
+    // the chunk they are zeros.  At most kXLoadsMax per thread (the launcher
+    // sizes `phase` so).
     const rsrc_t xrs = make_rsrc(x, (uint32_t)M * (uint32_t)K8 * 16u);
-    uint4 xv[kXLoadsPerThread];
-    int xdst[kXLoadsPerThread];  // LDS slot of each staged piece, -1 if none
-    {
-        int row = tid / div;
-        int p = tid - row * div;
+    const int xtotal = XROWS * phase;
+    const int nx = (xtotal + kChunkThreads - 1) / kChunkThreads;  // workgroup-uniform
+    const int step_rows = kChunkThreads / phase;                   // idx += 512 in rows ...
+    const int step_p = kChunkThreads - step_rows * phase;          // ... and pieces
+    const int row_t = tid / phase;
+    const int p_t = tid - row_t * phase;
+    uint4 xv[kXLoadsMax];
+    auto load_x = [&](int ph) {
+        int row = row_t, p = p_t;
 #pragma unroll
-        for (int j = 0; j < kXLoadsPerThread; ++j) {
-            if (j < nx) {  // workgroup-uniform
-                const int idx = tid + j * kWave * kChunkWaves;
-                const bool ok = idx < xtotal && row < M && p < len;
-                xv[j] = load16<kCached>(xrs, ok ? ((uint32_t)row * K8 + k0 + p) * 16u : kOff);
-                xdst[j] = idx < xtotal ? row * pitch + p : -1;
+        for (int j = 0; j < kXLoadsMax; ++j) {
+            if (j < nx) {
+                const int idx = tid + j * kChunkThreads;
+                const int kp = ph * phase + p;  // piece within the chunk
+                const bool ok = idx < xtotal && row < M && kp < len;
+                xv[j] = load16<kCached>(xrs, ok ? ((uint32_t)row * K8 + k0 + kp) * 16u : kOff);
                 row += step_rows;
                 p += step_p;
-                if (p >= div) {
-                    p -= div;
+                if (p >= phase) {
+                    p -= phase;
                     ++row;
                 }
             }
         }
-    }
+    };
+    auto store_x = [&](int buf) {
+        int row = row_t, p = p_t;
+#pragma unroll
+        for (int j = 0; j < kXLoadsMax; ++j) {
+            if (j < nx) {
+                const int idx = tid + j * kChunkThreads;
+                if (idx < xtotal) xs[buf * xslots + row * xp + p] = xv[j];
+                row += step_rows;
+                p += step_p;
+                if (p >= phase) {
+                    p -= phase;
+                    ++row;
+                }
+            }
+        }
+    };
+
+    // x loads first (they hit L2 and return early), then the weight
+    // prologue, then the x stores: waiting for x does not wait for weights.
+    load_x(0);
     uint4 wb[DR][4];
 #pragma unroll
     for (int d = 0; d < DR; ++d) load_round(d, wb[d]);
-#pragma unroll
-    for (int j = 0; j < kXLoadsPerThread; ++j)
-        if (j < nx && xdst[j] >= 0) xs[xdst[j]] = xv[j];  // zeros past M and len
+    store_x(0);
     __syncthreads();
 
     f32x4_t acc[NT][MT];
@@ -168,24 +196,28 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
             const int r = 16 * nt + col;
             bslot[nt][t] = r * RP + ((4 * t + grp) ^ G::swz(r));
         }
-    const int rounds = (len + RP - 1) / RP;
     for (int r0 = 0; r0 < rounds; r0 += DR) {
 #pragma unroll
         for (int d = 0; d < DR; ++d) {
             const int rd = r0 + d;
-            if (rd < rounds) {  // wave-uniform
+            if (rd < rounds) {  // workgroup-uniform
+                const int ph = PHASED ? rd / pr : 0;
+                const int rin = rd - ph * pr;  // round within the phase
+                const bool next = PHASED && ph + 1 < nphases;
+                if (next && rin == 0) load_x(ph + 1);
                 // Within one wave LDS operations run in order, so the tile can
                 // be rewritten right after the previous round's reads.
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     tile[(i * G::kRowsPerLoad + lrow) * RP + lslot] = wb[d][i];
                 __builtin_amdgcn_wave_barrier();
+                const uint4* xb = xs + (ph & 1) * xslots + rin * RP;
 #pragma unroll
                 for (int t = 0; t < G::kSteps; ++t) {
-                    const int p = rd * RP + 4 * t + grp;  // < lenr < pitch
+                    const int p = 4 * t + grp;
                     uint4 a[MT];
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) a[mt] = xs[(mt * 16 + col) * pitch + p];
+                    for (int mt = 0; mt < MT; ++mt) a[mt] = xb[(mt * 16 + col) * xp + p];
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) {
                         const uint4 b = tile[bslot[nt][t]];
@@ -196,9 +228,14 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void splitk_mfma_kernel(
                                 acc[nt][mt], 0, 0, 0);
                     }
                 }
-                __builtin_amdgcn_wave_barrier();
+                load_round(rd + DR, wb[d]);  // past the chunk: no memory access
+                if (next && (rin == pr - 1)) {
+                    // The other buffer was last read in phase ph - 1, which
+                    // every wave finished before the previous phase barrier.
+                    store_x((ph + 1) & 1);
+                    __syncthreads();
+                }
             }
-            load_round(rd + DR, wb[d]);  // past the chunk: no memory access
         }
     }
 
@@ -383,11 +420,35 @@ int mfma_grid_tiles(int N, int tile_n) {
     return (tiles + kXcds - 1) / kXcds * kXcds;
 }
 
+// Pieces of x staged per phase for a chunk kernel launch: the whole chunk
+// (rounded to whole rounds) in one buffer when that fits in LDS and in the
+// staging registers, else the largest whole number of rounds for which two
+// buffers fit.  0 if not even one round fits.
+static int chunk_phase(int M, int k_chunk, int tile_n) {
+    const int MT = (M + 15) / 16;
+    const int xrows = 16 * MT;
+    const int rp = tile_n == 2 * kMfmaTileN ? 8 : 16;
+    const size_t budget = kMfmaMaxLds - (size_t)kChunkWaves * kTileSlots * 16;  // after W tiles
+    const int chunk8 = k_chunk / kPiece;
+    const int whole = (chunk8 + rp - 1) / rp * rp;
+    const int max_stage = kXLoadsMax * kChunkThreads / xrows;  // staging registers
+    if (whole >= rp && whole <= max_stage && (size_t)xrows * (whole + 1) * 16 <= budget)
+        return whole;
+    int ph = 0;
+    for (int p = rp; p <= whole && p <= max_stage; p += rp)
+        if ((size_t)2 * xrows * (p + 1) * 16 <= budget) ph = p;
+    return ph;
+}
+
 size_t mfma_chunk_lds_bytes(int M, int k_chunk, int tile_n) {
     const int MT = (M + 15) / 16;
-    const int round_pieces = tile_n == 2 * kMfmaTileN ? 8 : 16;
-    return (size_t)16 * MT * x_pitch(k_chunk / kPiece, round_pieces) * 16 +
-           (size_t)kChunkWaves * kTileSlots * 16;
+    const int ph = chunk_phase(M, k_chunk, tile_n);
+    if (ph == 0) return kMfmaMaxLds + 1;  // cannot run
+    const int chunk8 = k_chunk / kPiece;
+    const int rp = tile_n == 2 * kMfmaTileN ? 8 : 16;
+    const int whole = (chunk8 + rp - 1) / rp * rp;
+    const int buffers = ph >= whole ? 1 : 2;
+    return (size_t)buffers * 16 * MT * (ph + 1) * 16 + (size_t)kChunkWaves * kTileSlots * 16;
 }
 
 hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk, int tile_n, const void* x,
@@ -400,25 +461,26 @@ hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk, int tile_
     const uint4* xp = static_cast<const uint4*>(x);
     const uint4* wp = static_cast<const uint4*>(W);
     const int MT = (M + 15) / 16;
+    const int phase = chunk_phase(M, k_chunk, tile_n);
     const size_t lds = mfma_chunk_lds_bytes(M, k_chunk, tile_n);
-    if (lds > kMfmaMaxLds) return hipErrorInvalidValue;
-    // x staging: 16*MT*(pitch - 1) pieces at most over the workgroup's threads
-    if ((size_t)16 * MT * (x_pitch(chunk8, 16 / NT) - 1) >
-        (size_t)kXLoadsPerThread * kWave * kChunkWaves)
-        return hipErrorInvalidValue;
+    if (phase == 0 || lds > kMfmaMaxLds) return hipErrorInvalidValue;
     constexpr int DR = 2;  // weight rounds in flight per wave (8 loads)
-#define SG_CHUNK(mt, nt) \
-    if (MT == mt && NT == nt) { \
+    const int whole = (chunk8 + 16 / NT - 1) / (16 / NT) * (16 / NT);
+    const bool phased = phase < whole;
+#define SG_CHUNK(mt, nt, ph) \
+    if (MT == mt && NT == nt && phased == ph) { \
         hipError_t e = hipFuncSetAttribute( \
-            reinterpret_cast<const void*>(&splitk_mfma_kernel<mt, nt, DR>), \
+            reinterpret_cast<const void*>(&splitk_mfma_kernel<mt, nt, DR, ph>), \
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
         if (e != hipSuccess) return e; \
-        splitk_mfma_kernel<mt, nt, DR><<<grid, kWave * kChunkWaves, lds, stream>>>( \
-            xp, wp, M, N, K8, chunk8, ep); \
+        splitk_mfma_kernel<mt, nt, DR, ph><<<grid, kChunkThreads, lds, stream>>>( \
+            xp, wp, M, N, K8, chunk8, phase, ep); \
         return hipGetLastError(); \
     }
-    SG_CHUNK(1, 1) SG_CHUNK(2, 1) SG_CHUNK(3, 1) SG_CHUNK(4, 1)
-    SG_CHUNK(1, 2) SG_CHUNK(2, 2) SG_CHUNK(3, 2) SG_CHUNK(4, 2)
+    SG_CHUNK(1, 1, false) SG_CHUNK(2, 1, false) SG_CHUNK(3, 1, false) SG_CHUNK(4, 1, false)
+    SG_CHUNK(1, 2, false) SG_CHUNK(2, 2, false) SG_CHUNK(3, 2, false) SG_CHUNK(4, 2, false)
+    SG_CHUNK(1, 1, true) SG_CHUNK(2, 1, true) SG_CHUNK(3, 1, true) SG_CHUNK(4, 1, true)
+    SG_CHUNK(1, 2, true) SG_CHUNK(2, 2, true) SG_CHUNK(3, 2, true) SG_CHUNK(4, 2, true)
 #undef SG_CHUNK
     return hipErrorInvalidValue;
 }
