@@ -26,6 +26,8 @@ the CPU oracle timed on a bounded sample on this host.
 
     python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   # rocprofv3 --pmc CSVs -> traffic
     python bench.py --summarize-trace DIR "COMMAND"       # rocprofv3 kernel stats -> table
+    python bench.py --profile-workloads MANIFEST           # workloads for rocprofv3 --pmc
+    python bench.py --summarize-workloads MANIFEST DIR...  # per-workload counters -> table
 """
 from __future__ import annotations
 
@@ -369,6 +371,7 @@ def read_traffic():
 
 COPY_BYTES = 1 << 30          # the calibration copy reads and writes this many bytes
 COPY_KERNEL_TAG = "MulFunctor"  # torch.mul(src, 1.0, out=dst): a plain element-wise copy
+COPY_GRID = COPY_BYTES // 16    # its launch: one thread per 4 floats
 GEMV_KERNEL_TAGS = ("rowdot_kernel<1, 14,", "rowdot_kernel<2, 14,")
 
 
@@ -394,19 +397,18 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> None:
     for the calibration copy of known size."""
     fetch, write = _pmc_dispatches(fetch_dir), _pmc_dispatches(write_dir)
 
-    def pick(table, counter, tags, largest_grid=False):
+    def pick(table, counter, tags, calibration=False):
         hits = [(name, grid, v) for name, c, grid, v in table
                 if c == counter and any(t in name for t in tags)]
-        if largest_grid:  # the calibration copy is the largest launch of its kernel
-            top = max(grid for _, grid, _ in hits) if hits else 0
-            hits = [h for h in hits if h[1] == top]
+        if calibration:  # the calibration copy: its kernel at exactly its launch size
+            hits = [h for h in hits if h[1] == COPY_GRID]
         if not hits:
             raise SystemExit(f"no {counter} samples for {tags}")
         return (sum(v for _, _, v in hits) / len(hits), len(hits),
                 sorted({name[:80] for name, _, _ in hits}))
 
-    cf, _, _ = pick(fetch, "FETCH_SIZE", (COPY_KERNEL_TAG,), largest_grid=True)
-    cw, _, _ = pick(write, "WRITE_SIZE", (COPY_KERNEL_TAG,), largest_grid=True)
+    cf, _, _ = pick(fetch, "FETCH_SIZE", (COPY_KERNEL_TAG,), calibration=True)
+    cw, _, _ = pick(write, "WRITE_SIZE", (COPY_KERNEL_TAG,), calibration=True)
     gf, nf, names = pick(fetch, "FETCH_SIZE", GEMV_KERNEL_TAGS)
     gw, nw, _ = pick(write, "WRITE_SIZE", GEMV_KERNEL_TAGS)
     fetch_factor = cf * 1024 / COPY_BYTES
@@ -453,6 +455,155 @@ def summarize_trace(directory: str, command: str) -> None:
               f"{float(r['MaxNs']) / 1e3:9.2f}  {name[:150]}")
 
 
+# --------------------------------------------------------------------------- per-workload counters
+
+
+def profile_workloads(torch, sg, si, L, manifest_path, reps=3):
+    """A fixed sequence of the benchmark's workloads, reps calls each (on distinct
+    weight copies), for rocprofv3 --pmc passes; writes the manifest that maps the
+    library's kernel dispatches, in order, back to the workloads."""
+    dev = "cuda"
+    copy_calibration(torch)
+    manifest = []
+
+    def run(label, M, N, K, plan, calls, nbytes):
+        before = sg.skinny_gemm_get_counters()
+        for i in range(reps):
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        after = sg.skinny_gemm_get_counters()
+        launched = sum(a - b for a, b in zip(after, before))
+        manifest.append({"workload": label, "M": M, "N": N, "K": K, "plan": plan, "calls": reps,
+                         "dispatches": launched, "bytes_per_call": nbytes})
+        log(f"profiled {label} M={M}: {launched} dispatches")
+
+    def desc(p):
+        return f"{sg.KERNEL_NAMES[p.kernel]} S={p.split_k} tile={p.tile_n}"
+
+    shapes = [("small-batch 8192x7168", M, 8192, 7168, dict()) for M in (1, 2)]
+    shapes += [("split-K 4096x7168", M, 4096, 7168, dict(bf16=False))
+               for M in (3, 4, 8, 12, 16, 32, 48, 64)]
+    shapes += [("residual 7168x8192", M, 7168, 8192, dict(f32=False, residual=True))
+               for M in (1, 8, 64)]
+    for label, M, N, K, kind in shapes:
+        W0 = si.normal_bf16((N, K), 0.02, 11, dev)
+        ring = [W0] + [W0.clone() for _ in range(reps - 1)]
+        x = si.normal_bf16((M, K), 1.0, 12, dev)
+        p = sg.skinny_gemm_plan(M, N, K)
+        ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        if kind.get("residual"):
+            r = si.normal_bf16((M, N), 1.0, 13, dev)
+            o16 = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
+            calls = [L.residual(p, x, w, r, o16, None, ws) for w in ring]
+        else:
+            y32 = torch.empty((M, N), device=dev)
+            y16 = None if kind.get("bf16") is False else torch.empty((M, N), device=dev,
+                                                                    dtype=torch.bfloat16)
+            calls = [L.projection(p, x, w, y32, y16, ws) for w in ring]
+        run(label, M, N, K, desc(p), calls, proj_bytes(M, N, K, **kind))
+        del ring, W0
+        torch.cuda.empty_cache()
+    E, N, K, topk = 384, 2048, 7168, 8
+    W = si.normal_bf16((E, N, K), 0.02, 14, dev)
+    for T in (1, 16, 64):
+        x = si.normal_bf16((T, K), 1.0, 15, dev)
+        ids = si.routing_table(T, E, topk, 16 + T)
+        out = torch.empty((T, topk, N), device=dev)
+        ws = torch.empty(sg.grouped_skinny_gemm_workspace(T, E, topk, N, K), dtype=torch.uint8,
+                         device=dev)
+        distinct = len(set(ids.view(-1).tolist()))
+        nbytes = distinct * N * K * 2 + T * K * 2 + T * topk * N * 4 + T * topk * 4
+        run("MoE grouped E=384 2048x7168 top8", T, N, K, "moe_table+grouped",
+            [L.grouped(x, W, ids.to(dev), out, ws)], nbytes)
+    del W
+    torch.cuda.empty_cache()
+    with open(manifest_path, "w") as f:
+        json.dump(manifest, f, indent=1)
+    log(f"manifest: {manifest_path}")
+
+
+def _dispatch_counters(directory: str):
+    """Per dispatch of this library's kernels, in launch order: (kernel, {counter: value});
+    and the calibration copy's counters."""
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    disp = {}
+    for r in rows:
+        d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                   "grid": int(r["Grid_Size"]), "c": {}})
+        d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ours = [disp[k] for k in sorted(disp) if "sg::" in disp[k]["name"]]
+    calib = [d["c"] for d in disp.values()
+             if COPY_KERNEL_TAG in d["name"] and d["grid"] == COPY_GRID]
+    return ours, calib
+
+
+def summarize_workloads(manifest_path: str, dirs) -> None:
+    """Per workload and kernel: HBM bytes (FETCH_SIZE + WRITE_SIZE, each scaled by the
+    calibration copy), their ratio to the algorithmic bytes, and the utilisation
+    counters, from rocprofv3 --pmc passes over `bench.py --profile-workloads`."""
+    with open(manifest_path) as f:
+        manifest = json.load(f)
+    per = {}  # (workload index, kernel short name) -> {counter: [values]}
+    scale = {}
+    for d in dirs:
+        ours, calib = _dispatch_counters(d)
+        for c in calib:
+            for name in ("FETCH_SIZE", "WRITE_SIZE"):
+                if name in c:
+                    scale[name] = c[name] * 1024 / COPY_BYTES
+        need = sum(w["dispatches"] for w in manifest)
+        if len(ours) != need:
+            raise SystemExit(f"{d}: {len(ours)} dispatches of the library, manifest expects {need}")
+        i = 0
+        for wi, w in enumerate(manifest):
+            for _ in range(w["dispatches"]):
+                k = ours[i]
+                i += 1
+                short = k["name"].replace("void ", "").replace("sg::(anonymous namespace)::", "")
+                short = short.split("(")[0]
+                slot = per.setdefault((wi, short), {})
+                for cname, v in k["c"].items():
+                    slot.setdefault(cname, []).append(v)
+    print("# Per-workload counters of this library's kernels (rocprofv3 --pmc, one pass each)")
+    print("# commands (repository root; OUT = an output folder):")
+    print("#   rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/wl_fetch -o f -- python bench.py "
+          "--profile-workloads OUT/wl_fetch.json")
+    print("#   rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/wl_write -o w -- python bench.py "
+          "--profile-workloads OUT/wl_write.json")
+    print("#   rocprofv3 --pmc MfmaUtil LdsUtil VALUBusy -f csv -d OUT/wl_util -o u -- python "
+          "bench.py --profile-workloads OUT/wl_util.json")
+    print("#   python bench.py --summarize-workloads OUT/wl_fetch.json OUT/wl_fetch OUT/wl_write "
+          "OUT/wl_util")
+    print(f"# HBM bytes = FETCH_SIZE / {scale.get('FETCH_SIZE', float('nan')):.4f} + "
+          f"WRITE_SIZE / {scale.get('WRITE_SIZE', float('nan')):.4f} (KiB -> bytes; factors from "
+          f"a 1 GiB element-wise copy); per call = summed over the kernels of one call")
+    print(f"# {'workload':34s} {'M':>3} {'kernel':44s} {'HBM MB':>8} {'x alg':>6} "
+          f"{'Mfma%':>6} {'Lds%':>6} {'VALU%':>6}")
+    for wi, w in enumerate(manifest):
+        for (wj, short), c in per.items():
+            if wj != wi:
+                continue
+            mean = {k: sum(v) / len(v) for k, v in c.items()}
+            hbm = None
+            if "FETCH_SIZE" in mean and "WRITE_SIZE" in mean and scale:
+                hbm = (mean["FETCH_SIZE"] * 1024 / scale["FETCH_SIZE"] +
+                       mean["WRITE_SIZE"] * 1024 / scale["WRITE_SIZE"])
+            ratio = hbm / w["bytes_per_call"] if hbm is not None else float("nan")
+
+            def pct(k):
+                return f"{mean[k]:6.1f}" if k in mean else f"{'-':>6}"
+            print(f"  {w['workload'][:34]:34s} {w['M']:3d} {short[:44]:44s} "
+                  f"{(hbm or float('nan')) / 1e6:8.2f} {ratio:6.3f} "
+                  f"{pct('MfmaUtil')} {pct('LdsUtil')} {pct('VALUBusy')}")
+        print(f"  {'':34s} {'':3s} {'  algorithmic bytes per call':44s} "
+              f"{w['bytes_per_call'] / 1e6:8.2f}   plan: {w['plan']}")
+
+
 def copy_calibration(torch, nbytes=COPY_BYTES, reps=3):
     """A plain element-wise copy of known size (reads nbytes, writes nbytes) for scaling
     the FETCH_SIZE / WRITE_SIZE counters."""
@@ -477,7 +628,13 @@ def main() -> None:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "COMMAND"))
+    ap.add_argument("--profile-workloads", metavar="MANIFEST")
+    ap.add_argument("--summarize-workloads", nargs="+", metavar="MANIFEST_THEN_DIRS")
     args = ap.parse_args()
+
+    if args.summarize_workloads:
+        summarize_workloads(args.summarize_workloads[0], args.summarize_workloads[1:])
+        return
 
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
@@ -500,6 +657,9 @@ def main() -> None:
     torch.cuda.set_device(0)
     L = Launcher(torch, sg)
     cyc = sleep_cycles_per_ms(torch)
+    if args.profile_workloads:
+        profile_workloads(torch, sg, si, L, args.profile_workloads)
+        return
     if args.copy_calibration:
         copy_calibration(torch)
 
