@@ -82,8 +82,8 @@ hipError_t launch_moe_table(const int32_t* ids, int T, int topk, int E, int N,
                             int32_t* user_sorted, int32_t* user_invalid, float* out,
                             hipStream_t stream);
 
-constexpr int kGroupedRowsPerWave = 4;
-constexpr int kGroupedTileN = kGroupedRowsPerWave * kWavesPerBlock;  // 16 rows per item
+constexpr int kGroupedRowsPerWave = 8;  // even: rows go two at a time
+constexpr int kGroupedTileN = kGroupedRowsPerWave * kWavesPerBlock;  // 32 rows per item
 hipError_t launch_grouped(const void* x, int T, const void* W, int E, int N, int K, int topk,
                           const GroupedWorkspace& g, float* out, hipStream_t stream);
 

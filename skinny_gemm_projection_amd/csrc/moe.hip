@@ -180,13 +180,15 @@ __device__ __forceinline__ float dot_row(const uint4 (&a)[NCH], const uint4 (&b)
     return s;
 }
 
-// Persistent grid over work items (active expert, 16-row tile of its W).
-// Each wave streams 4 rows of the expert's weights, one whole row (K <= 8192,
-// up to 16 x 1 KB loads) at a time, like the small-matrix kernel, and
-// multiplies it with the gathered x rows of the tokens routed there, two at
-// a time.  With one or two tokens (the common case) their x rows are loaded
-// once per item; with more, the weight row stays in registers while token
-// pairs stream past it, so each weight byte is still fetched once.
+// Persistent grid over work items (active expert, tile of kGroupedTileN rows
+// of its W).  Each wave takes kGroupedRowsPerWave rows of the tile, two at a
+// time (2 x up to 16 x 1 KB loads in flight), like the small-matrix kernel,
+// and multiplies them with the gathered x row of each token routed to the
+// expert; the two sums of a (row pair, token) are reduced together by one
+// lane reduce-scatter.  With one token (the common case) its x row is loaded
+// once per item; with more, the weight rows stay in registers while the
+// tokens' x rows (L2-resident) stream past them, so each weight byte is
+// still fetched from HBM once.
 template <int NCH>
 __global__ __launch_bounds__(kBlock) void grouped_kernel(const uint4* __restrict__ x,
                                                          const uint4* __restrict__ W, int N,
@@ -196,6 +198,7 @@ __global__ __launch_bounds__(kBlock) void grouped_kernel(const uint4* __restrict
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = wave_id_in_block();
     const int items = *g.num_active * tiles;
+    const int v = scatter_index<4>(lane);  // this lane's row (0 or 1) of the sums, or -1/2/3
 
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
         const int e = g.active[item / tiles];
@@ -205,38 +208,45 @@ __global__ __launch_bounds__(kBlock) void grouped_kernel(const uint4* __restrict
         const uint4* __restrict__ We = W + (int64_t)e * N * K8;
         const int nbase = tile * kGroupedTileN + wv * kGroupedRowsPerWave;
 
-        uint4 xa[NCH], xb[NCH], wr[NCH];
-        if (cnt <= 2) {
-            const int pa = g.sorted[seg];
-            const int pb = cnt > 1 ? g.sorted[seg + 1] : pa;
-            load_row<NCH, kCached>(xa, x + (int64_t)(pa / topk) * K8, K8, lane);
-            load_row<NCH, kCached>(xb, x + (int64_t)(pb / topk) * K8, K8, lane);
+        uint4 xa[NCH], w0[NCH], w1[NCH];
+        auto load_w = [&](uint4 (&dst)[NCH], int n) {
+            const bool ok = n < N;
+            load_row<NCH, kStream>(dst, We + (int64_t)(ok ? n : 0) * K8, ok ? K8 : 0, lane);
+        };
+        auto load_x = [&](int p) {
+            load_row<NCH, kCached>(xa, x + (int64_t)(p / topk) * K8, K8, lane);
+        };
+        auto finish = [&](int n, int p) {
+            float acc[4] = {dot_row<NCH>(xa, w0), dot_row<NCH>(xa, w1), 0.0f, 0.0f};
+            const float total = reduce_scatter<4>(acc, lane);
+            if (v == 0 || v == 1) {
+                const int row = n + v;
+                if (row < N) out[(int64_t)p * N + row] = total;
+            }
+        };
+        if (cnt == 1) {
+            const int p = g.sorted[seg];
+            load_x(p);
 #pragma unroll 1
-            for (int i = 0; i < kGroupedRowsPerWave; ++i) {
+            for (int i = 0; i < kGroupedRowsPerWave; i += 2) {
                 const int n = nbase + i;
                 if (n >= N) break;
-                load_row<NCH, kStream>(wr, We + (int64_t)n * K8, K8, lane);
-                const float ta = wave_sum(dot_row<NCH>(xa, wr));
-                const float tb = wave_sum(dot_row<NCH>(xb, wr));
-                if (lane == 0) out[(int64_t)pa * N + n] = ta;
-                if (lane == 1 && cnt > 1) out[(int64_t)pb * N + n] = tb;
+                load_w(w0, n);
+                load_w(w1, n + 1);
+                finish(n, p);
             }
         } else {
 #pragma unroll 1
-            for (int i = 0; i < kGroupedRowsPerWave; ++i) {
+            for (int i = 0; i < kGroupedRowsPerWave; i += 2) {
                 const int n = nbase + i;
                 if (n >= N) break;
-                load_row<NCH, kStream>(wr, We + (int64_t)n * K8, K8, lane);
+                load_w(w0, n);
+                load_w(w1, n + 1);
 #pragma unroll 1
-                for (int c0 = 0; c0 < cnt; c0 += 2) {
-                    const int pa = g.sorted[seg + c0];
-                    const int pb = c0 + 1 < cnt ? g.sorted[seg + c0 + 1] : pa;
-                    load_row<NCH, kCached>(xa, x + (int64_t)(pa / topk) * K8, K8, lane);
-                    load_row<NCH, kCached>(xb, x + (int64_t)(pb / topk) * K8, K8, lane);
-                    const float ta = wave_sum(dot_row<NCH>(xa, wr));
-                    const float tb = wave_sum(dot_row<NCH>(xb, wr));
-                    if (lane == 0) out[(int64_t)pa * N + n] = ta;
-                    if (lane == 1 && c0 + 1 < cnt) out[(int64_t)pb * N + n] = tb;
+                for (int c = 0; c < cnt; ++c) {
+                    const int p = g.sorted[seg + c];
+                    load_x(p);
+                    finish(n, p);
                 }
             }
         }

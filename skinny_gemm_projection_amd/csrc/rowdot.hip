@@ -45,54 +45,6 @@ __device__ __forceinline__ void load_pieces(uint4 (&dst)[NCH], rsrc_t r, int nch
     }
 }
 
-__device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
-__device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
-
-// Sum of v over the 16 lanes of its DPP row; every lane of the row gets it.
-__device__ __forceinline__ float row16_sum(float v) {
-    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-    v += dpp<0x141>(v);  // row_half_mirror
-    v += dpp<0x140>(v);  // row_mirror
-    return v;
-}
-
-// Reduce-scatter of V values (V % 4 == 0) over the 64 lanes of a wave.
-// Returns, in lane q*16 + i (i < V/4), the wave-wide sum of value
-// q*V/4 + i; other lanes return a value of no meaning.
-template <int V>
-__device__ __forceinline__ float reduce_scatter(const float (&a)[V], int lane) {
-    static_assert(V % 4 == 0, "pad V to a multiple of 4");
-    constexpr int H = V / 2, Q = V / 4;
-    float b[H];
-#pragma unroll
-    for (int j = 0; j < H; ++j) {
-        // lanes 0-31 keep value j summed over lanes l and l+32, lanes 32-63 value j+H
-        const auto p = __builtin_amdgcn_permlane32_swap(as_u(a[j]), as_u(a[j + H]), false, false);
-        b[j] = as_f(p[0]) + as_f(p[1]);
-    }
-    float c[Q];
-#pragma unroll
-    for (int j = 0; j < Q; ++j) {
-        // rows 0 and 2 keep b[j], rows 1 and 3 keep b[j+Q], each summed over a row pair
-        const auto p = __builtin_amdgcn_permlane16_swap(as_u(b[j]), as_u(b[j + Q]), false, false);
-        c[j] = row16_sum(as_f(p[0]) + as_f(p[1]));
-    }
-    const int i = lane & 15;
-    float out = c[0];
-#pragma unroll
-    for (int j = 1; j < Q; ++j) out = (i == j) ? c[j] : out;
-    return out;
-}
-
-// Value index held by a lane after reduce_scatter<V>, or -1.
-template <int V>
-__device__ __forceinline__ int scatter_index(int lane) {
-    constexpr int Q = V / 4;
-    const int i = lane & 15;
-    return i < Q ? (lane >> 4) * Q + i : -1;
-}
-
 constexpr int pad4(int v) { return (v + 3) / 4 * 4; }
 constexpr int block_waves(int S) { return S > kWavesPerBlock ? S : kWavesPerBlock; }
 
