@@ -48,6 +48,8 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.oracle_moe_table.argtypes = [c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p]
     lib.oracle_moe_table.restype = c_i64
     lib.oracle_grouped.argtypes = [c_i64] * 5 + [c_p] * 5
+    lib.oracle_router_topk.argtypes = [c_i64, c_i64, c_i64, c_p, c_p, c_p]
+    lib.oracle_router_topk.restype = None
     for name in ("oracle_encode_bf16", "oracle_projection", "oracle_splitk_partials",
                  "oracle_splitk_sum", "oracle_residual", "oracle_grouped"):
         getattr(lib, name).restype = None
@@ -154,3 +156,13 @@ class Oracle:
         self.c.oracle_grouped(T, topk, E, N, K, _ptr(x), _ptr(W), _ptr(ids), _ptr(out),
                               _ptr(a) if a is not None else None)
         return (out, a) if with_scale else out
+
+    def router_topk(self, scores, k: int):
+        """ids int32 [T,k] and their scores float32 [T,k] from fp32 scores [T,E]."""
+        scores = np.ascontiguousarray(scores, dtype=np.float32)
+        T, E = scores.shape
+        assert 1 <= k <= E
+        ids = np.empty((T, k), dtype=np.int32)
+        top = np.empty((T, k), dtype=np.float32)
+        self.c.oracle_router_topk(T, E, k, _ptr(scores), _ptr(ids), _ptr(top))
+        return ids, top

@@ -12,6 +12,7 @@
 #include "oracle.h"
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 double oracle_bf16_to_f64(uint16_t bits)
@@ -190,4 +191,42 @@ void oracle_grouped(int64_t T, int64_t topk, int64_t E, int64_t N, int64_t K,
             oracle_projection(1, N, K, x + t * K, W + (int64_t)e * N * K, o, a);
         }
     }
+}
+
+/* Router top-k: true when (a, ia) ranks before (b, ib) -- the larger score
+ * first, equal scores by the lower expert id, a NaN score as -infinity. */
+static int oracle_ranks_before(float a, int64_t ia, float b, int64_t ib)
+{
+    double da = isnan(a) ? -INFINITY : (double)a;
+    double db = isnan(b) ? -INFINITY : (double)b;
+    if (da != db)
+        return da > db;
+    return ia < ib;
+}
+
+void oracle_router_topk(int64_t T, int64_t E, int64_t k, const float* scores,
+                        int32_t* ids, float* top_scores)
+{
+    /* Expert selection by router score (routed experts, Method details §3):
+     * for each token, k times, the best expert not taken yet.  The ranking
+     * is decided on the given fp32 scores. */
+    unsigned char* taken = (unsigned char*)malloc(E > 0 ? (size_t)E : 1);
+    for (int64_t t = 0; t < T; ++t) {
+        const float* s = scores + t * E;
+        memset(taken, 0, E > 0 ? (size_t)E : 1);
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                if (taken[e])
+                    continue;
+                if (best < 0 || oracle_ranks_before(s[e], e, s[best], best))
+                    best = e;
+            }
+            taken[best] = 1;
+            ids[t * k + j] = (int32_t)best;
+            if (top_scores)
+                top_scores[t * k + j] = s[best];
+        }
+    }
+    free(taken);
 }

@@ -88,6 +88,16 @@ void oracle_grouped(int64_t T, int64_t topk, int64_t E, int64_t N, int64_t K,
                     const uint16_t* x, const uint16_t* W, const int32_t* ids,
                     double* out, double* abs_scale);
 
+/* Router top-k (routed experts: "Hyper Optimizing Kimi K3 in vLLM", Method
+ * details §3 -- expert selection from the router scores decides which expert
+ * weights are read).  scores [T,E] fp32 (the router projection's output);
+ * for each token t, ids[t,j] (j < k <= E) is the expert of rank j: larger
+ * score first, equal scores by the lower expert id, a NaN score ranking as
+ * -infinity.  top_scores[t,j] = scores[t, ids[t,j]] (may be NULL).  The
+ * ranking is decided on the fp32 values as given. */
+void oracle_router_topk(int64_t T, int64_t E, int64_t k, const float* scores,
+                        int32_t* ids, float* top_scores);
+
 #ifdef __cplusplus
 }
 #endif

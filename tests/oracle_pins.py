@@ -483,6 +483,51 @@ def check_grouped(o):
             assert np.array_equal(out[t, j], (wi[ids[t, j]] @ xi[t]).astype(np.float64)), (t, j)
 
 
+def _golden_topk():
+    cases, cur = [], None
+    for row in read_table("router_topk_worked.txt"):
+        if row[0] == "case":
+            cur = {kv.split("=")[0]: int(kv.split("=")[1]) for kv in row[1:]}
+            cases.append(cur)
+        else:
+            toks = " ".join(row[1:]).split("|")
+            cur[row[0].rstrip(":")] = [t.split() for t in toks]
+    return cases
+
+
+def check_router_topk_golden(o):
+    for c in _golden_topk():
+        scores = np.array([[float(v) for v in r] for r in c["scores"]], dtype=np.float32)
+        want = np.array([[int(v) for v in r] for r in c["ids"]], dtype=np.int32)
+        assert scores.shape == (c["T"], c["E"]) and want.shape == (c["T"], c["k"])
+        ids, top = o.router_topk(scores, c["k"])
+        assert np.array_equal(ids, want), (c, ids)
+        assert np.array_equal(top.view(np.uint32),
+                              np.take_along_axis(scores, want, 1).view(np.uint32))
+
+
+def check_router_topk_vs_sort(o):
+    # numpy's stable lexicographic sort on (expert id, -score) keys, NaN as -inf
+    rng = np.random.default_rng(21)
+    for T, E, k in [(4, 384, 8), (3, 17, 17), (5, 64, 1), (2, 1000, 32)]:
+        for kind in ("normal", "ties", "special"):
+            if kind == "normal":
+                s = rng.standard_normal((T, E)).astype(np.float32)
+            elif kind == "ties":
+                s = rng.integers(-3, 4, (T, E)).astype(np.float32)
+            else:
+                s = rng.integers(-2, 3, (T, E)).astype(np.float32)
+                s[rng.random((T, E)) < 0.2] = np.nan
+                s[rng.random((T, E)) < 0.1] = -np.inf
+                s[rng.random((T, E)) < 0.05] = np.inf
+            ids, top = o.router_topk(s, k)
+            key = np.where(np.isnan(s), -np.inf, s).astype(np.float64)
+            for t in range(T):
+                order = np.lexsort((np.arange(E), -key[t]))[:k]
+                assert np.array_equal(ids[t], order), (T, E, k, kind, t)
+                assert len(set(ids[t].tolist())) == k
+
+
 ALL_CHECKS = [
     check_bf16_decode_golden, check_bf16_decode_all_patterns, check_bf16_round_golden,
     check_bf16_round_vs_torch, check_bf16_round_bruteforce,
@@ -491,6 +536,7 @@ ALL_CHECKS = [
     check_projection_linearity, check_projection_rows,
     check_splitk, check_splitk_sum_order, check_residual,
     check_moe_golden, check_moe_bruteforce, check_grouped,
+    check_router_topk_golden, check_router_topk_vs_sort,
 ]
 
 

@@ -51,6 +51,10 @@ MUTANTS = [
     ("grouped expert stride", "W + (int64_t)e * N * K", "W + (int64_t)e * K"),
     ("grouped token row", "x + t * K, W", "x + j * K, W"),
     ("grouped invalid ids kept", "if (e < 0 || e >= E) {\n                for", "if (e < 0) {\n                for"),
+    ("topk ties to higher id", "    return ia < ib;", "    return ia > ib;"),
+    ("topk ascending", "        return da > db;", "        return da < db;"),
+    ("topk nan as +inf", "isnan(a) ? -INFINITY", "isnan(a) ? INFINITY"),
+    ("topk retakes experts", "if (taken[e])", "if (0)"),
 ]
 
 
