@@ -293,6 +293,35 @@ def sweep(torch, sg, si, L, cyc, reps=40):
     del ring
     torch.cuda.empty_cache()
 
+    # router: scores y = x W_r^T (E=384 experts, K=7168, fp32) and their top-8 per token
+    E, K, k = 384, 7168, 8
+    Wr = si.normal_bf16((E, K), 0.02, si.seed_for(5, si.TAG_W) + 99, dev)
+    ring = ring_copies(torch, Wr)
+    c = L.c
+    for T in (1, 16, 64):
+        x = si.normal_bf16((T, K), 1.0, si.seed_for(5, si.TAG_X) + T, dev)
+        p = sg.skinny_gemm_plan(T, E, K)
+        scores = torch.empty((T, E), device=dev)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+
+        def router(proj, scores=scores, ids=ids, T=T):
+            def go():
+                proj()
+                st = c.skinny_gemm_router_topk(scores.data_ptr(), T, E, k, ids.data_ptr(), None,
+                                               L.sp)
+                if st:
+                    raise RuntimeError(sg.skinny_gemm_status_str(st))
+            return go
+        per = timed_calls(torch, [router(L.projection(p, x, w, scores, None, ws)) for w in ring],
+                          reps, cyc)
+        nbytes = proj_bytes(T, E, K, bf16=False) + T * E * 4 + T * k * 4
+        rows.append({"workload": "router top-8 E=384 K=7168", "M": T, "N": E, "K": K,
+                     "plan": f"{plan_desc(p)}+router_topk", "us": round(1e3 * per, 3),
+                     "GBps": round(nbytes / (per * 1e-3) / 1e9, 1),
+                     "pct_peak": round(100.0 * nbytes / (per * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)})
+    del ring, Wr
+
     # MoE grouped: E=384 experts of N=2048 x K=7168, 8 distinct experts per token,
     # a ring of 8 routing tables per batch size
     E, N, K, topk = 384, 2048, 7168, 8

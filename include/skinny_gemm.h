@@ -76,10 +76,11 @@ typedef enum {
     SG_KERNEL_REDUCE = 4,       /* split-K deterministic reduction + epilogue      */
     SG_KERNEL_MOE_TABLE = 5,    /* per-expert token table                          */
     SG_KERNEL_GROUPED = 6,      /* grouped per-expert projection                   */
-    SG_KERNEL_PREFETCH = 7      /* side-stream weight prefetch                     */
+    SG_KERNEL_PREFETCH = 7,     /* side-stream weight prefetch                     */
+    SG_KERNEL_ROUTER_TOPK = 8   /* router top-k expert selection                   */
 } sg_kernel;
 
-#define SG_NUM_COUNTERS 8
+#define SG_NUM_COUNTERS 9
 #define SG_MAX_M 64
 
 /* Launch decision for one projection shape.  Produced by skinny_gemm_plan
@@ -169,6 +170,19 @@ sg_status grouped_skinny_gemm(const sg_bf16* x, int32_t T, const sg_bf16* W, int
                               float* out, int32_t* expert_offsets, int32_t* sorted_pairs,
                               int32_t* invalid_count,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Router top-k: the experts each token is routed to ([P] Method details §3:
+ * expert selection decides which expert weights are read; the selection is
+ * the step upstream of grouped_skinny_gemm).  scores [T,E] fp32 -- the
+ * router projection, e.g. skinny_gemm with N = E -- in device memory;
+ * topk_ids [T,k] int32 receives, for each token, the experts of rank
+ * 0..k-1: the larger score first, equal scores by the lower expert id, a
+ * NaN score ranking as -infinity (a total order: the ids of a token are
+ * distinct).  topk_scores [T,k] fp32 (NULL to skip) receives the selected
+ * scores as given.  Limits: 0 <= T <= 1<<20, 1 <= E <= 4096,
+ * 1 <= k <= min(E, 32) (else SG_ERR_SHAPE); pointers 4-byte aligned. */
+sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int32_t k,
+                                  int32_t* topk_ids, float* topk_scores, void* stream);
 
 /* Side-stream weight prefetch ([P] Method details §4): reads
  * [W, W + bytes) so that a following projection finds it in the GPU's

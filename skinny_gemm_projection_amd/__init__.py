@@ -17,16 +17,19 @@ import torch
 
 from . import _lib
 from ._lib import (KERNEL_NAMES, SG_KERNEL_GEMV, SG_KERNEL_GROUPED, SG_KERNEL_MOE_TABLE,
-                   SG_KERNEL_NONE, SG_KERNEL_PREFETCH, SG_KERNEL_REDUCE, SG_KERNEL_SPLITK_MFMA,
-                   SG_KERNEL_SPLITK_VALU, SG_NUM_COUNTERS, SgPlan, SkinnyGemmError)
+                   SG_KERNEL_NONE, SG_KERNEL_PREFETCH, SG_KERNEL_REDUCE, SG_KERNEL_ROUTER_TOPK,
+                   SG_KERNEL_SPLITK_MFMA, SG_KERNEL_SPLITK_VALU, SG_NUM_COUNTERS, SgPlan,
+                   SkinnyGemmError)
 
 __all__ = [
     "skinny_gemm_plan", "skinny_gemm_plan_force", "skinny_gemm", "skinny_gemm_residual",
     "grouped_skinny_gemm_workspace", "grouped_skinny_gemm", "skinny_gemm_prefetch",
+    "skinny_gemm_router_topk", "router_topk",
     "skinny_gemm_status_str", "skinny_gemm_get_counters", "skinny_gemm_reset_counters",
     "SgPlan", "SkinnyGemmError", "KERNEL_NAMES", "SG_KERNEL_NONE", "SG_KERNEL_GEMV",
     "SG_KERNEL_SPLITK_VALU", "SG_KERNEL_SPLITK_MFMA", "SG_KERNEL_REDUCE", "SG_KERNEL_MOE_TABLE",
-    "SG_KERNEL_GROUPED", "SG_KERNEL_PREFETCH", "SG_NUM_COUNTERS", "library_path",
+    "SG_KERNEL_GROUPED", "SG_KERNEL_PREFETCH", "SG_KERNEL_ROUTER_TOPK", "SG_NUM_COUNTERS",
+    "library_path",
 ]
 
 
@@ -183,6 +186,38 @@ def skinny_gemm_prefetch(W: torch.Tensor, nbytes: int | None = None, stream=None
     if nbytes > total:
         raise ValueError("nbytes exceeds the tensor")
     _lib.check(_c().skinny_gemm_prefetch(W.data_ptr() or None, nbytes, _stream(stream)))
+
+
+def skinny_gemm_router_topk(scores: torch.Tensor, k: int, topk_ids=None, topk_scores=None,
+                            stream=None):
+    """topk_ids (int32 [T,k]) and, if given, topk_scores (float32 [T,k]) from router
+    scores (float32 [T,E]): larger score first, ties to the lower expert id, NaN as -inf."""
+    if scores.dtype != torch.float32 or scores.dim() != 2 or not scores.is_contiguous():
+        raise ValueError("scores: expected a contiguous float32 [T, E] tensor")
+    T, E = scores.shape
+    dev = scores.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _shape(topk_ids, (T, k), "topk_ids"), _shape(topk_scores, (T, k), "topk_scores")
+    st = _c().skinny_gemm_router_topk(
+        _ptr(scores, torch.float32, "scores", dev), T, E, k,
+        _ptr(topk_ids, torch.int32, "topk_ids", dev),
+        _ptr(topk_scores, torch.float32, "topk_scores", dev), _stream(stream))
+    _lib.check(st)
+    return topk_ids
+
+
+def router_topk(x: torch.Tensor, W_router: torch.Tensor, k: int, stream=None):
+    """Expert selection for MoE decode: router scores y = x W_router^T (fp32, the
+    planned skinny projection), then their top-k.  Returns (topk_ids [T,k] int32,
+    topk_scores [T,k] float32, scores [T,E] float32)."""
+    T, E = x.shape[0], W_router.shape[0]
+    plan = skinny_gemm_plan(T, E, x.shape[1])
+    scores = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    skinny_gemm(plan, x, W_router, y_f32=scores, stream=stream)
+    top = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    ids = skinny_gemm_router_topk(scores, k, topk_scores=top, stream=stream)
+    return ids, top, scores
 
 
 def skinny_gemm_status_str(status: int) -> str:

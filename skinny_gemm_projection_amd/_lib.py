@@ -23,9 +23,10 @@ SG_KERNEL_REDUCE = 4
 SG_KERNEL_MOE_TABLE = 5
 SG_KERNEL_GROUPED = 6
 SG_KERNEL_PREFETCH = 7
-SG_NUM_COUNTERS = 8
+SG_KERNEL_ROUTER_TOPK = 8
+SG_NUM_COUNTERS = 9
 KERNEL_NAMES = {0: "none", 1: "gemv", 2: "splitk_valu", 3: "splitk_mfma", 4: "reduce",
-                5: "moe_table", 6: "grouped", 7: "prefetch"}
+                5: "moe_table", 6: "grouped", 7: "prefetch", 8: "router_topk"}
 
 
 class SgPlan(ctypes.Structure):
@@ -75,6 +76,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.grouped_skinny_gemm_workspace.restype = sz
     lib.grouped_skinny_gemm.argtypes = [p, i32, p, i32, i32, i32, p, i32, p, p, p, p, p, sz, p]
     lib.skinny_gemm_prefetch.argtypes = [p, sz, p]
+    lib.skinny_gemm_router_topk.argtypes = [p, i32, i32, i32, p, p, p]
     lib.skinny_gemm_status_str.argtypes = [ctypes.c_int]
     lib.skinny_gemm_status_str.restype = ctypes.c_char_p
     lib.skinny_gemm_get_counters.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
@@ -82,7 +84,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.skinny_gemm_reset_counters.argtypes = []
     lib.skinny_gemm_reset_counters.restype = None
     for name in ("skinny_gemm_plan", "skinny_gemm_plan_force", "skinny_gemm",
-                 "skinny_gemm_residual", "grouped_skinny_gemm", "skinny_gemm_prefetch"):
+                 "skinny_gemm_residual", "grouped_skinny_gemm", "skinny_gemm_prefetch",
+                 "skinny_gemm_router_topk"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

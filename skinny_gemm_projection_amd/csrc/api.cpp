@@ -45,6 +45,7 @@ const char* kernel_name(int k) {
         case SG_KERNEL_MOE_TABLE: return "moe_table";
         case SG_KERNEL_GROUPED: return "grouped";
         case SG_KERNEL_PREFETCH: return "prefetch";
+        case SG_KERNEL_ROUTER_TOPK: return "router_topk";
         default: return "?";
     }
 }
@@ -163,6 +164,24 @@ sg_status grouped_skinny_gemm(const sg_bf16* x, int32_t T, const sg_bf16* W, int
     return SG_OK;
 }
 
+sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int32_t k,
+                                  int32_t* topk_ids, float* topk_scores, void* stream) {
+    if (T < 0 || T > (1 << 20) || E < 1 || E > 4096 || k < 1 || k > 32 || k > E)
+        return SG_ERR_SHAPE;
+    if (T == 0) return SG_OK;
+    if (!scores || !topk_ids) return SG_ERR_NULL;
+    auto aligned4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+    if (!aligned4(scores) || !aligned4(topk_ids) || !aligned4(topk_scores)) return SG_ERR_ALIGN;
+    (void)hipGetLastError();
+    if (sg::launch_router_topk(scores, T, E, k, topk_ids, topk_scores,
+                               static_cast<hipStream_t>(stream)) != hipSuccess)
+        return SG_ERR_HIP;
+    count(SG_KERNEL_ROUTER_TOPK);
+    if (log_enabled())
+        std::fprintf(stderr, "[skinny_gemm] router_topk T=%d E=%d k=%d\n", T, E, k);
+    return SG_OK;
+}
+
 sg_status skinny_gemm_prefetch(const void* W, size_t bytes, void* stream) {
     if (bytes == 0) return SG_OK;
     if (!W) return SG_ERR_NULL;
@@ -180,7 +199,7 @@ const char* skinny_gemm_status_str(sg_status status) {
         case SG_ERR_NULL: return "SG_ERR_NULL: a required pointer is NULL";
         case SG_ERR_SHAPE: return "SG_ERR_SHAPE: size negative or over the limit";
         case SG_ERR_UNSUPPORTED: return "SG_ERR_UNSUPPORTED: batch outside the decode path (M > 64)";
-        case SG_ERR_ALIGN: return "SG_ERR_ALIGN: K % 8 != 0 or pointer not 16-byte aligned";
+        case SG_ERR_ALIGN: return "SG_ERR_ALIGN: K % 8 != 0 or a pointer misaligned";
         case SG_ERR_WORKSPACE: return "SG_ERR_WORKSPACE: workspace missing or too small";
         case SG_ERR_PLAN: return "SG_ERR_PLAN: plan does not fit this problem";
         case SG_ERR_HIP: return "SG_ERR_HIP: kernel launch failed";

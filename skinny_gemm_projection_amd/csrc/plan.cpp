@@ -73,13 +73,27 @@ bool rowdot_fits(int32_t M, int32_t K, int32_t S) {
 
 // Smallest split that keeps the rowdot x registers within the cap for M,
 // preferring one a workgroup can reduce by itself (no second pass).
-int32_t rowdot_split(int32_t M, int32_t K) {
-    for (int32_t S = 1; S <= 8; S *= 2)
+int32_t rowdot_split(int32_t M, int32_t N, int32_t K) {
+    int32_t S0 = -1;
+    for (int32_t S = 1; S <= 8 && S0 < 0; S *= 2)
         if (sg::rowdot_team_split_ok(M, S) && no_empty_chunk(K, S) && rowdot_fits(M, K, S))
-            return S;
-    for (int32_t S = 1; S <= kMaxSplit; ++S)
-        if (no_empty_chunk(K, S) && rowdot_fits(M, K, S)) return S;
-    return -1;
+            S0 = S;
+    if (S0 < 0) {
+        for (int32_t S = 1; S <= kMaxSplit; ++S)
+            if (no_empty_chunk(K, S) && rowdot_fits(M, K, S)) return S;
+        return -1;
+    }
+    // Few rows (a router's 384 experts, a 1024-row matrix): the row groups
+    // alone leave most compute units idle, so split K over more waves of
+    // each team while the teams still fit the resident wave slots.
+    const int64_t groups = (N + 1) / 2;
+    for (int32_t S = 2 * S0; S <= 4; S *= 2) {
+        if (groups * S > sg::rowdot_resident_waves(M, 1)) break;
+        if (!sg::rowdot_team_split_ok(M, S) || !no_empty_chunk(K, S)) break;
+        if (groups * S0 >= kComputeUnits * 2) break;  // already two waves per CU
+        S0 = S;
+    }
+    return S0;
 }
 
 bool mfma_chunk_fits(int32_t M, int32_t K, int32_t S, int32_t tile_n) {
@@ -183,7 +197,7 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
             [[fallthrough]];
         case SG_KERNEL_SPLITK_VALU: {
             if (M > 15) return SG_ERR_PLAN;
-            if (split_k <= 0) split_k = rowdot_split(M, K);
+            if (split_k <= 0) split_k = rowdot_split(M, N, K);
             if (!split_ok(split_k)) return SG_ERR_PLAN;
             if (!rowdot_fits(M, K, split_k)) return SG_ERR_PLAN;
             const bool team_ok = rowdot_team_split_ok(M, split_k);
