@@ -9,57 +9,72 @@
 // by the lower expert id, a NaN score as -infinity -- a total order, so the
 // selected ids are unique.
 //
-// One wavefront per token.  Lane l holds the scores of experts l, l+64, ...
-// in registers.  Round j keeps, in each lane, the best of its experts that
-// rank after the round j-1 winner, then DPP and permlane exchanges find the
-// wave's best: k rounds of (E/64 compares + 6 exchanges), no LDS, no
-// sorting, and nothing to reset between tokens.
+// The order is carried by one 64-bit key per expert: the high word is the
+// score's bits mapped so that unsigned order is float order (NaN mapped to
+// -infinity first, -0 to +0), the low word is ~id, so that the lower id wins
+// a tie.  Keys are distinct, so "ranks before" is one unsigned compare and
+// the wave's first is a plain maximum.
+//
+// One wavefront per token; lane l holds the keys of experts l, l+64, ...
+// in registers.  Up to 8 keys a lane: the lane sorts them once, then each
+// of the k rounds takes the wave maximum of the lane heads (DPP and
+// permlane exchanges, no LDS) and the winning lane pops its head.  More
+// keys a lane: each round every lane rescans for its best key below the
+// previous winner.  Lane r keeps the round-r winner; the k results leave in
+// one parallel store.
 #include "launch.h"
 
 namespace sg {
 
 namespace {
 
-__device__ __forceinline__ bool ranks_before(float a, int ia, float b, int ib) {
-    return a > b || (a == b && ia < ib);
+constexpr int kSortedPerLane = 8;  // presort up to this many keys per lane
+
+__device__ __forceinline__ uint64_t rank_key(float v, int e) {
+    if (v != v) v = -__builtin_inff();  // NaN ranks as -infinity
+    if (v == 0.0f) v = 0.0f;            // -0 ties with +0
+    uint32_t u = as_u(v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
 }
 
-__device__ __forceinline__ void keep_first(float& v, int& i, float ov, int oi) {
-    if (ranks_before(ov, oi, v, i)) {
-        v = ov;
-        i = oi;
-    }
+__device__ __forceinline__ int key_id(uint64_t key) { return (int)~(uint32_t)key; }
+
+__device__ __forceinline__ uint64_t join(uint32_t hi, uint32_t lo) {
+    return ((uint64_t)hi << 32) | lo;
 }
+
+__device__ __forceinline__ uint64_t umax(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 template <int CTRL>
-__device__ __forceinline__ void dpp_step(float& v, int& i) {
-    const float ov = dpp<CTRL>(v);
-    const int oi = __builtin_amdgcn_mov_dpp(i, CTRL, 0xF, 0xF, true);
-    keep_first(v, i, ov, oi);
+__device__ __forceinline__ uint64_t dpp_max(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+    const uint32_t hi =
+        (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
+    return umax(v, join(hi, lo));
 }
 
-// Every lane receives the wave's first-ranked (v, i): DPP exchanges inside
-// 16-lane rows (partners l^1, l^2, the mirrored half row, the mirrored row),
-// then row-pair and half-wave swaps -- all VALU, no LDS round trips.
-__device__ __forceinline__ void wave_first(float& v, int& i) {
-    dpp_step<0xB1>(v, i);   // quad_perm [1,0,3,2]
-    dpp_step<0x4E>(v, i);   // quad_perm [2,3,0,1]
-    dpp_step<0x141>(v, i);  // row_half_mirror
-    dpp_step<0x140>(v, i);  // row_mirror
+// Every lane receives the wave maximum: DPP exchanges inside 16-lane rows
+// (partners l^1, l^2, the mirrored half row, the mirrored row), then
+// row-pair and half-wave swaps.
+__device__ __forceinline__ uint64_t wave_max(uint64_t v) {
+    v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max<0x141>(v);  // row_half_mirror
+    v = dpp_max<0x140>(v);  // row_mirror
     {
-        const auto pv = __builtin_amdgcn_permlane16_swap(as_u(v), as_u(v), false, false);
-        const auto pi = __builtin_amdgcn_permlane16_swap((uint32_t)i, (uint32_t)i, false, false);
-        v = as_f(pv[0]);
-        i = (int)pi[0];
-        keep_first(v, i, as_f(pv[1]), (int)pi[1]);
+        const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+        const auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+        const auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+        v = umax(join(ph[0], pl[0]), join(ph[1], pl[1]));
     }
     {
-        const auto pv = __builtin_amdgcn_permlane32_swap(as_u(v), as_u(v), false, false);
-        const auto pi = __builtin_amdgcn_permlane32_swap((uint32_t)i, (uint32_t)i, false, false);
-        v = as_f(pv[0]);
-        i = (int)pi[0];
-        keep_first(v, i, as_f(pv[1]), (int)pi[1]);
+        const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+        const auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+        const auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+        v = umax(join(ph[0], pl[0]), join(ph[1], pl[1]));
     }
+    return v;
 }
 
 template <int PER>
@@ -71,36 +86,48 @@ __global__ __launch_bounds__(kBlock) void router_topk_kernel(const float* __rest
     const int t = blockIdx.x * kWavesPerBlock + wave_id_in_block();
     if (t >= T) return;
     const float* s = scores + (int64_t)t * E;
-    float key[PER];
+    // key 0 (below every real key) pads experts past E
+    uint64_t key[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int e = j * kWave + lane;
-        const float v = e < E ? s[e] : -__builtin_inff();
-        key[j] = v != v ? -__builtin_inff() : v;  // NaN ranks as -infinity
+        const float v = s[e < E ? e : E - 1];
+        key[j] = e < E ? rank_key(v, e) : 0;
     }
-    float prev = 0.0f;
-    int prev_id = -1;  // -1: no winner yet
-    int mine = 0;      // lane r keeps the round-r winner
-    for (int r = 0; r < k; ++r) {
-        float best = -__builtin_inff();
-        int best_id = 0x7fffffff;  // ranks after every expert
+    uint64_t mine = 0;
+    if constexpr (PER <= kSortedPerLane) {
+        // odd-even transposition sort, descending
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int e = j * kWave + lane;
-            const bool after_prev = prev_id < 0 || ranks_before(prev, prev_id, key[j], e);
-            if (e < E && after_prev && ranks_before(key[j], e, best, best_id)) {
-                best = key[j];
-                best_id = e;
+        for (int r = 0; r < PER; ++r) {
+#pragma unroll
+            for (int j = r & 1; j + 1 < PER; j += 2) {
+                const uint64_t a = key[j], b = key[j + 1];
+                key[j] = umax(a, b);
+                key[j + 1] = a > b ? b : a;
             }
         }
-        wave_first(best, best_id);
-        if (lane == r) mine = best_id;
-        prev = best;
-        prev_id = best_id;
+        for (int r = 0; r < k; ++r) {
+            const uint64_t w = wave_max(key[0]);
+            if (lane == r) mine = w;
+            const uint64_t pop = key[0] == w ? ~0ull : 0;  // the winner lane shifts
+#pragma unroll
+            for (int j = 0; j + 1 < PER; ++j) key[j] = (key[j] & ~pop) | (key[j + 1] & pop);
+            key[PER - 1] &= ~pop;
+        }
+    } else {
+        uint64_t prev = ~0ull;  // ranks before every key
+        for (int r = 0; r < k; ++r) {
+            uint64_t best = 0;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) best = key[j] < prev ? umax(best, key[j]) : best;
+            prev = wave_max(best);
+            if (lane == r) mine = prev;
+        }
     }
-    if (lane < k) {  // one parallel store (and read of the score as given, NaN kept)
-        ids[(int64_t)t * k + lane] = mine;
-        if (top) top[(int64_t)t * k + lane] = s[mine];
+    if (lane < k) {
+        const int id = key_id(mine);
+        ids[(int64_t)t * k + lane] = id;
+        if (top) top[(int64_t)t * k + lane] = s[id];  // the score as given (NaN, -0 kept)
     }
 }
 
@@ -115,7 +142,8 @@ hipError_t launch_router_topk(const float* scores, int T, int E, int k, int32_t*
         router_topk_kernel<p><<<grid, kBlock, 0, stream>>>(scores, T, E, k, ids, top); \
         return hipGetLastError(); \
     }
-    SG_PER(1) SG_PER(2) SG_PER(4) SG_PER(8) SG_PER(16) SG_PER(32) SG_PER(64)
+    SG_PER(1) SG_PER(2) SG_PER(3) SG_PER(4) SG_PER(5) SG_PER(6) SG_PER(7) SG_PER(8)
+    SG_PER(16) SG_PER(32) SG_PER(64)
 #undef SG_PER
     return hipErrorInvalidValue;
 }
