@@ -129,6 +129,32 @@ class Launcher:
                 raise RuntimeError(self.sg.skinny_gemm_status_str(st))
         return go
 
+    def moe_step(self, x, Wr, We, Ws, topk, outs, ws, mode):
+        """skinny_moe_step: the shared expert fused into the router GEMM (Wr and Ws
+        adjacent, outputs in one [T, E + N_shared] buffer), on the binding's side
+        stream, or serial after the routed experts."""
+        c, sg = self.c, self.sg
+        T, K = x.shape
+        E, N, _ = We.shape
+        ids, scores, out, shared = outs
+        fused = mode == "fused"
+        step = sg.SgMoeStep(x.data_ptr(), Wr.data_ptr(), We.data_ptr(),
+                            None if fused else Ws.data_ptr(), scores.data_ptr(), ids.data_ptr(),
+                            None, out.data_ptr(), None if fused else shared.data_ptr(),
+                            T, K, E, topk, N, Ws.shape[0],
+                            sg._lib.SG_MOE_STEP_FUSED_SHARED if fused else 0)
+        side = fork = join = None
+        if mode == "side_stream":
+            s_, f_, j_ = sg._side_resources(x.device)
+            side, fork, join = s_.cuda_stream, f_.cuda_event, j_.cuda_event
+        ref = ctypes.byref(step)
+
+        def go(step=step):
+            st = c.skinny_moe_step(ref, ws.data_ptr(), ws.numel(), self.sp, side, fork, join)
+            if st:
+                raise RuntimeError(sg.skinny_gemm_status_str(st))
+        return go
+
 
 def sleep_cycles_per_ms(torch) -> float:
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -346,7 +372,46 @@ def sweep(torch, sg, si, L, cyc, reps=40):
                      "plan": "moe_table+grouped", "us": round(us, 3), "GBps": round(gbs, 1),
                      "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                      "distinct_experts_mean": round(sum(distinct) / len(distinct), 1)})
-    del W
+
+    # one MoE decode step: router scores + top-8 + table + grouped routed experts, and a
+    # shared expert of the same shape as one routed expert (N=2048, K=7168): fused into the
+    # router's GEMM, on a side stream overlapping the routing, or serial.  Rings: inputs (8)
+    # and [router; shared expert] weight pairs (> 2 x MALL).
+    Wrs = torch.cat([si.normal_bf16((E, K), 0.02, si.seed_for(5, si.TAG_W) + 99, dev),
+                     si.normal_bf16((N, K), 0.02, si.seed_for(5, si.TAG_W) + 98, dev)])
+    ring_rs = ring_copies(torch, Wrs)
+    for T in (1, 16, 64):
+        xs = [si.normal_bf16((T, K), 1.0, si.seed_for(5, si.TAG_X) + 100 * T + i, dev)
+              for i in range(8)]
+        n_calls = max(len(ring_rs), len(xs))
+        combos = [(xs[i % len(xs)], ring_rs[i % len(ring_rs)][:E], ring_rs[i % len(ring_rs)][E:])
+                  for i in range(n_calls)]
+        outs = (torch.empty((T, topk), dtype=torch.int32, device=dev),
+                torch.empty((T, E + N), device=dev), torch.empty((T, topk, N), device=dev),
+                torch.empty((T, N), device=dev))
+        ws = torch.empty(sg.skinny_moe_step_workspace(T, K, E, topk, N, N), dtype=torch.uint8,
+                         device=dev)
+        distinct = []
+        for x, wr, wsh in combos:  # the experts each call routes to (same inputs as timed)
+            L.moe_step(x, wr, W, wsh, topk, outs, ws, "serial")()
+            torch.cuda.synchronize()
+            distinct.append(len(set(outs[0].view(-1).tolist())))
+        nbytes = sum(d * N * K * 2 for d in distinct) / len(distinct) + \
+            proj_bytes(T, E, K, bf16=False) + proj_bytes(T, N, K, bf16=False) - T * K * 2 + \
+            T * topk * N * 4 + T * topk * 4
+        per = {}
+        for mode in ("serial", "side_stream", "fused"):
+            calls = [L.moe_step(x, wr, W, wsh, topk, outs, ws, mode) for x, wr, wsh in combos]
+            per[mode] = timed_calls(torch, calls, n_calls, cyc)
+        gbs = nbytes / (per["fused"] * 1e-3) / 1e9
+        rows.append({"workload": "MoE step E=384 top8 2048x7168 + shared expert", "M": T,
+                     "N": N, "K": K, "plan": "router+shared fused GEMM, top8, table, grouped",
+                     "us": round(1e3 * per["fused"], 3),
+                     "us_side_stream": round(1e3 * per["side_stream"], 3),
+                     "us_serial": round(1e3 * per["serial"], 3),
+                     "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                     "distinct_experts_mean": round(sum(distinct) / len(distinct), 1)})
+    del W, Wrs, ring_rs
     torch.cuda.empty_cache()
     return rows
 

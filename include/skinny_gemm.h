@@ -184,6 +184,63 @@ sg_status grouped_skinny_gemm(const sg_bf16* x, int32_t T, const sg_bf16* W, int
 sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int32_t k,
                                   int32_t* topk_ids, float* topk_scores, void* stream);
 
+/* One MoE decode step of a layer on one GPU, with the shared expert on its
+ * own stream ([P] Method details §3; [F] Partie 1 §3: the shared expert runs
+ * on a separate stream and its work overlaps the routing or the
+ * routed-expert computation).
+ *   on stream:       scores     = x W_router^T       (skinny_gemm, N = E)
+ *                    topk_ids, topk_scores            (skinny_gemm_router_topk)
+ *                    out        = routed projection   (grouped_skinny_gemm)
+ *   on side_stream:  shared_out = x W_shared^T       (skinny_gemm, N = N_shared)
+ * The side stream starts after the work already queued on `stream`
+ * (fork_event is recorded on stream), so the shared expert overlaps the
+ * routing phase -- router projection, top-k and token table, which leave
+ * HBM mostly idle -- and the start of the routed projection; `stream` waits
+ * for it at the end (join_event), so work queued on `stream` afterwards
+ * sees every output.  side_stream NULL (or equal to stream): everything runs
+ * on `stream` in the order above, the shared expert last.  The two events
+ * are caller-owned hipEvent_t (timing may be disabled), required with a
+ * side stream.  The outputs are identical either way.
+ * flags & SG_MOE_STEP_FUSED_SHARED: the shared expert joins the router's
+ * projection instead -- both read the same x, so they are one skinny GEMM,
+ * one weight stream and one launch ([P] Method details §3 likewise merges
+ * the projections that precede the experts into a single GEMM).  Then
+ * W_router is [E + N_shared, K] (router rows, then the shared expert's),
+ * `scores` is [T, E + N_shared] (columns [0,E) the router scores, columns
+ * [E, E+N_shared) the shared expert's output), W_shared and shared_out are
+ * ignored, and no side stream is used.  Outputs equal those of the other
+ * modes to the projection tolerance (the fused GEMM may take another plan).
+ * Shapes: x [T,K], W_router [E,K], W_experts [E,N,K], W_shared [N_shared,K]
+ * (bf16); scores [T,E], topk_scores [T,topk] (nullable), out [T,topk,N],
+ * shared_out [T,N_shared] (fp32); topk_ids [T,topk] int32.  Pointers whose
+ * extent is zero may be NULL; the others must be 16-byte aligned.
+ * Limits: T > 64 -> SG_ERR_UNSUPPORTED; 1 <= E <= 4096, 1 <= topk <=
+ * min(E, 32), 0 <= K <= 8192 (K % 8 == 0), 0 <= N, N_shared <= 1<<20 (else
+ * SG_ERR_SHAPE / SG_ERR_ALIGN).  Workspace: skinny_moe_step_workspace bytes,
+ * 16-byte aligned, used by the three projections and the token table. */
+typedef struct {
+    const sg_bf16* x;
+    const sg_bf16* W_router;
+    const sg_bf16* W_experts;
+    const sg_bf16* W_shared;
+    float* scores;
+    int32_t* topk_ids;
+    float* topk_scores;
+    float* out;
+    float* shared_out;
+    int32_t T, K, E, topk, N, N_shared;
+    int32_t flags;  /* 0, or SG_MOE_STEP_FUSED_SHARED */
+} sg_moe_step;
+
+#define SG_MOE_STEP_FUSED_SHARED 1
+
+/* Workspace bytes skinny_moe_step needs (0 if the sizes are rejected). */
+size_t skinny_moe_step_workspace(int32_t T, int32_t K, int32_t E, int32_t topk, int32_t N,
+                                 int32_t N_shared);
+
+sg_status skinny_moe_step(const sg_moe_step* step, void* workspace, size_t workspace_bytes,
+                          void* stream, void* side_stream, void* fork_event, void* join_event);
+
 /* Side-stream weight prefetch ([P] Method details §4): reads
  * [W, W + bytes) so that a following projection finds it in the GPU's
  * caches (MI355X: 4 MB L2 per XCD, 256 MB Infinity Cache).  Reads only the

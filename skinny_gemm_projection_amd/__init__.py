@@ -18,13 +18,14 @@ import torch
 from . import _lib
 from ._lib import (KERNEL_NAMES, SG_KERNEL_GEMV, SG_KERNEL_GROUPED, SG_KERNEL_MOE_TABLE,
                    SG_KERNEL_NONE, SG_KERNEL_PREFETCH, SG_KERNEL_REDUCE, SG_KERNEL_ROUTER_TOPK,
-                   SG_KERNEL_SPLITK_MFMA, SG_KERNEL_SPLITK_VALU, SG_NUM_COUNTERS, SgPlan,
-                   SkinnyGemmError)
+                   SG_KERNEL_SPLITK_MFMA, SG_KERNEL_SPLITK_VALU, SG_NUM_COUNTERS, SgMoeStep,
+                   SgPlan, SkinnyGemmError)
 
 __all__ = [
     "skinny_gemm_plan", "skinny_gemm_plan_force", "skinny_gemm", "skinny_gemm_residual",
     "grouped_skinny_gemm_workspace", "grouped_skinny_gemm", "skinny_gemm_prefetch",
-    "skinny_gemm_router_topk", "router_topk",
+    "skinny_gemm_router_topk", "router_topk", "skinny_moe_step_workspace", "skinny_moe_step",
+    "concat_router_shared", "MOE_STEP_MODES",
     "skinny_gemm_status_str", "skinny_gemm_get_counters", "skinny_gemm_reset_counters",
     "SgPlan", "SkinnyGemmError", "KERNEL_NAMES", "SG_KERNEL_NONE", "SG_KERNEL_GEMV",
     "SG_KERNEL_SPLITK_VALU", "SG_KERNEL_SPLITK_MFMA", "SG_KERNEL_REDUCE", "SG_KERNEL_MOE_TABLE",
@@ -218,6 +219,96 @@ def router_topk(x: torch.Tensor, W_router: torch.Tensor, k: int, stream=None):
     top = torch.empty((T, k), dtype=torch.float32, device=x.device)
     ids = skinny_gemm_router_topk(scores, k, topk_scores=top, stream=stream)
     return ids, top, scores
+
+
+def skinny_moe_step_workspace(T: int, K: int, E: int, topk: int, N: int, N_shared: int) -> int:
+    return int(_c().skinny_moe_step_workspace(T, K, E, topk, N, N_shared))
+
+
+_SIDE = {}  # device -> (side stream, fork event, join event), made once per device
+
+
+def _side_resources(device):
+    res = _SIDE.get(device)
+    if res is None:
+        with torch.cuda.device(device):
+            side = torch.cuda.Stream(device=device)  # default priority
+            fork, join = torch.cuda.Event(), torch.cuda.Event()
+            cur = torch.cuda.current_stream(device)
+            fork.record(cur)  # torch creates the hipEvent_t at its first record
+            join.record(cur)
+        res = (side, fork, join)
+        _SIDE[device] = res
+    return res
+
+
+def concat_router_shared(W_router: torch.Tensor, W_shared: torch.Tensor):
+    """One [E + N_shared, K] tensor holding the router rows, then the shared expert's;
+    returns its two views (W_router, W_shared) -- the weight layout the fused step reads."""
+    both = torch.cat([W_router, W_shared], dim=0).contiguous()
+    return both[:W_router.shape[0]], both[W_router.shape[0]:]
+
+
+MOE_STEP_MODES = ("fused", "side_stream", "serial")
+
+
+def skinny_moe_step(x: torch.Tensor, W_router: torch.Tensor, W_experts: torch.Tensor,
+                    W_shared, topk: int, mode: str = "fused", workspace=None, stream=None):
+    """One MoE decode step: router scores, top-k and routed-expert projection on `stream`,
+    plus the shared expert's projection (W_shared [N_shared,K], or None):
+      "fused"       -- in the router's GEMM; W_shared must be stored right after W_router
+                       (the two views concat_router_shared returns);
+      "side_stream" -- on a side stream that overlaps the routing phase;
+      "serial"      -- after the routed experts on `stream`.
+    Returns (topk_ids [T,topk] int32, topk_scores [T,topk], scores [T,E], out [T,topk,N],
+    shared_out [T,N_shared]; fp32).  In fused mode scores and shared_out are column
+    views of one [T, E + N_shared] buffer."""
+    if mode not in MOE_STEP_MODES:
+        raise ValueError(f"mode: one of {MOE_STEP_MODES}")
+    dev = x.device
+    T, K = x.shape
+    E, N, K2 = W_experts.shape
+    N_shared = 0 if W_shared is None else W_shared.shape[0]
+    if W_router.shape != (E, K) or K2 != K or (W_shared is not None and W_shared.shape[1] != K):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, W_router {tuple(W_router.shape)}, "
+                         f"W_experts {tuple(W_experts.shape)}")
+    fused = mode == "fused" and N_shared > 0
+    if fused and W_shared.data_ptr() != W_router.data_ptr() + E * K * W_router.element_size():
+        raise ValueError("fused mode: W_shared must follow W_router in memory "
+                         "(use concat_router_shared)")
+    f32 = dict(dtype=torch.float32, device=dev)
+    ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    top = torch.empty((T, topk), **f32)
+    out = torch.empty((T, topk, N), **f32)
+    if fused:
+        y = torch.empty((T, E + N_shared), **f32)
+        scores, shared_out = y[:, :E], y[:, E:]
+        w_router_ptr = _ptr(W_router, torch.bfloat16, "W_router", dev)
+        scores_ptr, shared_ptr, w_shared_ptr = y.data_ptr() or None, None, None
+    else:
+        scores, shared_out = torch.empty((T, E), **f32), torch.empty((T, N_shared), **f32)
+        w_router_ptr = _ptr(W_router, torch.bfloat16, "W_router", dev)
+        scores_ptr = _ptr(scores, torch.float32, "scores", dev)
+        shared_ptr = _ptr(shared_out, torch.float32, "shared_out", dev)
+        w_shared_ptr = _ptr(W_shared, torch.bfloat16, "W_shared", dev)
+    need = skinny_moe_step_workspace(T, K, E, topk, N, N_shared)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    step = SgMoeStep(
+        _ptr(x, torch.bfloat16, "x", dev), w_router_ptr,
+        _ptr(W_experts, torch.bfloat16, "W_experts", dev), w_shared_ptr, scores_ptr,
+        _ptr(ids, torch.int32, "topk_ids", dev), _ptr(top, torch.float32, "topk_scores", dev),
+        _ptr(out, torch.float32, "out", dev), shared_ptr, T, K, E, topk, N, N_shared,
+        _lib.SG_MOE_STEP_FUSED_SHARED if fused else 0)
+    side = fork = join = None
+    if mode == "side_stream":
+        s, f, j = _side_resources(dev)
+        side, fork, join = s.cuda_stream, f.cuda_event, j.cuda_event
+    st = _c().skinny_moe_step(ctypes.byref(step), _ptr(workspace, torch.uint8, "workspace", dev),
+                              ws_bytes, _stream(stream), side, fork, join)
+    _lib.check(st)
+    return ids, top, scores, out, shared_out
 
 
 def skinny_gemm_status_str(status: int) -> str:

@@ -46,6 +46,21 @@ class SgPlan(ctypes.Structure):
         return f"SgPlan({d})"
 
 
+class SgMoeStep(ctypes.Structure):
+    """Mirror of sg_moe_step."""
+    _fields_ = [("x", ctypes.c_void_p), ("W_router", ctypes.c_void_p),
+                ("W_experts", ctypes.c_void_p), ("W_shared", ctypes.c_void_p),
+                ("scores", ctypes.c_void_p), ("topk_ids", ctypes.c_void_p),
+                ("topk_scores", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("shared_out", ctypes.c_void_p),
+                ("T", ctypes.c_int32), ("K", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("N", ctypes.c_int32), ("N_shared", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
+
+
+SG_MOE_STEP_FUSED_SHARED = 1
+
+
 class SkinnyGemmError(RuntimeError):
     """A non-SG_OK status from the library; .status holds the code."""
 
@@ -77,6 +92,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.grouped_skinny_gemm.argtypes = [p, i32, p, i32, i32, i32, p, i32, p, p, p, p, p, sz, p]
     lib.skinny_gemm_prefetch.argtypes = [p, sz, p]
     lib.skinny_gemm_router_topk.argtypes = [p, i32, i32, i32, p, p, p]
+    lib.skinny_moe_step_workspace.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.skinny_moe_step_workspace.restype = sz
+    lib.skinny_moe_step.argtypes = [ctypes.POINTER(SgMoeStep), p, sz, p, p, p, p]
     lib.skinny_gemm_status_str.argtypes = [ctypes.c_int]
     lib.skinny_gemm_status_str.restype = ctypes.c_char_p
     lib.skinny_gemm_get_counters.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
@@ -85,7 +103,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.skinny_gemm_reset_counters.restype = None
     for name in ("skinny_gemm_plan", "skinny_gemm_plan_force", "skinny_gemm",
                  "skinny_gemm_residual", "grouped_skinny_gemm", "skinny_gemm_prefetch",
-                 "skinny_gemm_router_topk"):
+                 "skinny_gemm_router_topk", "skinny_moe_step"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -112,6 +112,29 @@ bool grouped_sizes_ok(int32_t T, int32_t E, int32_t topk, int32_t N, int32_t K) 
 
 }  // namespace
 
+namespace sg {
+
+sg_status router_topk_call(const float* scores, int64_t ld, int32_t T, int32_t E, int32_t k,
+                           int32_t* topk_ids, float* topk_scores, void* stream) {
+    if (T < 0 || T > (1 << 20) || E < 1 || E > 4096 || k < 1 || k > 32 || k > E || ld < E)
+        return SG_ERR_SHAPE;
+    if (T == 0) return SG_OK;
+    if (!scores || !topk_ids) return SG_ERR_NULL;
+    auto aligned4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+    if (!aligned4(scores) || !aligned4(topk_ids) || !aligned4(topk_scores)) return SG_ERR_ALIGN;
+    (void)hipGetLastError();
+    if (launch_router_topk(scores, ld, T, E, k, topk_ids, topk_scores,
+                           static_cast<hipStream_t>(stream)) != hipSuccess)
+        return SG_ERR_HIP;
+    count(SG_KERNEL_ROUTER_TOPK);
+    if (log_enabled())
+        std::fprintf(stderr, "[skinny_gemm] router_topk T=%d E=%d k=%d ld=%lld\n", T, E, k,
+                     (long long)ld);
+    return SG_OK;
+}
+
+}  // namespace sg
+
 extern "C" {
 
 sg_status skinny_gemm(const sg_plan* plan, const sg_bf16* x, const sg_bf16* W, float* y_f32,
@@ -166,20 +189,7 @@ sg_status grouped_skinny_gemm(const sg_bf16* x, int32_t T, const sg_bf16* W, int
 
 sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int32_t k,
                                   int32_t* topk_ids, float* topk_scores, void* stream) {
-    if (T < 0 || T > (1 << 20) || E < 1 || E > 4096 || k < 1 || k > 32 || k > E)
-        return SG_ERR_SHAPE;
-    if (T == 0) return SG_OK;
-    if (!scores || !topk_ids) return SG_ERR_NULL;
-    auto aligned4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
-    if (!aligned4(scores) || !aligned4(topk_ids) || !aligned4(topk_scores)) return SG_ERR_ALIGN;
-    (void)hipGetLastError();
-    if (sg::launch_router_topk(scores, T, E, k, topk_ids, topk_scores,
-                               static_cast<hipStream_t>(stream)) != hipSuccess)
-        return SG_ERR_HIP;
-    count(SG_KERNEL_ROUTER_TOPK);
-    if (log_enabled())
-        std::fprintf(stderr, "[skinny_gemm] router_topk T=%d E=%d k=%d\n", T, E, k);
-    return SG_OK;
+    return sg::router_topk_call(scores, E, T, E, k, topk_ids, topk_scores, stream);
 }
 
 sg_status skinny_gemm_prefetch(const void* W, size_t bytes, void* stream) {

@@ -89,9 +89,9 @@ hipError_t launch_grouped(const void* x, int T, const void* W, int E, int N, int
 
 hipError_t launch_prefetch(const void* W, size_t bytes, hipStream_t stream);
 
-// Router top-k: ids [T,k] (and their scores) from fp32 scores [T,E];
-// E <= 4096, k <= 32 (checked by the caller).
-hipError_t launch_router_topk(const float* scores, int T, int E, int k, int32_t* ids,
-                              float* top, hipStream_t stream);
+// Router top-k: ids [T,k] (and their scores) from fp32 scores, row t at
+// scores + t*ld (ld >= E); E <= 4096, k <= 32 (checked by the caller).
+hipError_t launch_router_topk(const float* scores, int64_t ld, int T, int E, int k,
+                              int32_t* ids, float* top, hipStream_t stream);
 
 }  // namespace sg

@@ -1,4 +1,4 @@
-// plan_internal.h -- planner entry points shared inside the library.
+// plan_internal.h -- planner and call entry points shared inside the library.
 #pragma once
 
 #include "skinny_gemm.h"
@@ -12,5 +12,12 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
 
 // True when *p is exactly what the planner produces for its own fields.
 bool plan_matches(const sg_plan* p);
+
+// The checked, counted and logged router top-k call behind
+// skinny_gemm_router_topk, with a row stride (ld >= E elements) for scores
+// that share their rows with other outputs (a fused router + shared-expert
+// projection).
+sg_status router_topk_call(const float* scores, int64_t ld, int32_t T, int32_t E, int32_t k,
+                           int32_t* topk_ids, float* topk_scores, void* stream);
 
 }  // namespace sg

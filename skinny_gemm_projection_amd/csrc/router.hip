@@ -79,13 +79,13 @@ __device__ __forceinline__ uint64_t wave_max(uint64_t v) {
 
 template <int PER>
 __global__ __launch_bounds__(kBlock) void router_topk_kernel(const float* __restrict__ scores,
-                                                             int T, int E, int k,
+                                                             int64_t ld, int T, int E, int k,
                                                              int32_t* __restrict__ ids,
                                                              float* __restrict__ top) {
     const int lane = threadIdx.x & (kWave - 1);
     const int t = blockIdx.x * kWavesPerBlock + wave_id_in_block();
     if (t >= T) return;
-    const float* s = scores + (int64_t)t * E;
+    const float* s = scores + t * ld;
     // key 0 (below every real key) pads experts past E
     uint64_t key[PER];
 #pragma unroll
@@ -133,13 +133,13 @@ __global__ __launch_bounds__(kBlock) void router_topk_kernel(const float* __rest
 
 }  // namespace
 
-hipError_t launch_router_topk(const float* scores, int T, int E, int k, int32_t* ids,
-                              float* top, hipStream_t stream) {
+hipError_t launch_router_topk(const float* scores, int64_t ld, int T, int E, int k,
+                              int32_t* ids, float* top, hipStream_t stream) {
     const int grid = (T + kWavesPerBlock - 1) / kWavesPerBlock;
     const int per = (E + kWave - 1) / kWave;
 #define SG_PER(p) \
     if (per <= p) { \
-        router_topk_kernel<p><<<grid, kBlock, 0, stream>>>(scores, T, E, k, ids, top); \
+        router_topk_kernel<p><<<grid, kBlock, 0, stream>>>(scores, ld, T, E, k, ids, top); \
         return hipGetLastError(); \
     }
     SG_PER(1) SG_PER(2) SG_PER(3) SG_PER(4) SG_PER(5) SG_PER(6) SG_PER(7) SG_PER(8)
