@@ -230,3 +230,49 @@ void oracle_router_topk(int64_t T, int64_t E, int64_t k, const float* scores,
     }
     free(taken);
 }
+
+double oracle_e2m1_to_f64(uint8_t code)
+{
+    /* 4-bit float: sign bit 3, 2-bit exponent (bias 1), 1-bit mantissa. */
+    const int sign = (code >> 3) & 1;
+    const int e = (code >> 1) & 3;
+    const int m = code & 1;
+    double mag;
+    if (e == 0)
+        mag = m * 0.5;                             /* subnormal: 0 or 0.5 */
+    else
+        mag = ldexp(1.0 + m * 0.5, e - 1);         /* 1, 1.5, 2, 3, 4, 6 */
+    return sign ? -mag : mag;
+}
+
+double oracle_e8m0_to_f64(uint8_t s)
+{
+    /* unsigned 8-bit exponent, no sign or mantissa; all ones is NaN */
+    if (s == 255)
+        return NAN;
+    return ldexp(1.0, (int)s - 127);
+}
+
+void oracle_projection_mxfp4(int64_t M, int64_t N, int64_t K, const uint16_t* x,
+                             const uint8_t* Wq, const uint8_t* Ws, double* y,
+                             double* abs_scale)
+{
+    /* Decode each weight from its nibble and its block's scale, then the
+     * plain projection sum, k ascending. */
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0, abs_sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const uint8_t byte = Wq[n * (K / 2) + k / 2];
+                const uint8_t code = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+                const double w = oracle_e2m1_to_f64(code) * oracle_e8m0_to_f64(Ws[n * (K / 32) + k / 32]);
+                const double term = oracle_bf16_to_f64(x[m * K + k]) * w;
+                sum += term;
+                abs_sum += fabs(term);
+            }
+            y[m * N + n] = sum;
+            if (abs_scale)
+                abs_scale[m * N + n] = abs_sum;
+        }
+    }
+}

@@ -98,6 +98,32 @@ void oracle_grouped(int64_t T, int64_t topk, int64_t E, int64_t N, int64_t K,
 void oracle_router_topk(int64_t T, int64_t E, int64_t k, const float* scores,
                         int32_t* ids, float* top_scores);
 
+/* Block-scaled 4-bit weights.  The pages' later evaluation model ships
+ * NVFP4 weights ("Hyper Optimizing Kimi K3 in vLLM", Experimental setup and
+ * Supplementary details: a 4-bit float element format with per-block
+ * scales).  The block-scaled 4-bit format MI355X handles natively is OCP
+ * MXFP4: e2m1 elements, blocks of 32 consecutive elements along K, one e8m0
+ * power-of-two scale per block.  That is the format read here.
+ *
+ * e2m1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa.  Exponent 0
+ * is subnormal (0 or 0.5); otherwise 2^(e-1) * (1 + m/2).  No Inf or NaN;
+ * the largest magnitude is 6. */
+double oracle_e2m1_to_f64(uint8_t code);
+
+/* e8m0 scale: 2^(s - 127) for s in 0..254; s == 255 is NaN. */
+double oracle_e8m0_to_f64(uint8_t s);
+
+/* Projection with MXFP4 weights (K a multiple of 32):
+ *   Wq [N, K/2] bytes: element k of row n sits in byte n*K/2 + k/2, in the
+ *                      low nibble for even k and the high nibble for odd k;
+ *   Ws [N, K/32] e8m0 scales: block b of row n covers k in [32b, 32b+32).
+ *   w[n,k] = e2m1(code[n,k]) * e8m0(Ws[n, k/32])
+ *   y[m,n] = sum_k x[m,k] * w[n,k], k ascending, in double; abs_scale the
+ *   sum of |x[m,k] * w[n,k]| (may be NULL). */
+void oracle_projection_mxfp4(int64_t M, int64_t N, int64_t K, const uint16_t* x,
+                             const uint8_t* Wq, const uint8_t* Ws, double* y,
+                             double* abs_scale);
+
 #ifdef __cplusplus
 }
 #endif

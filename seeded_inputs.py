@@ -13,7 +13,10 @@ used throughout):
   * routing: for each token in order, the first ``topk`` entries of a seeded
     random permutation of the E expert ids (distinct, uniform);
   * integer-valued tensors: uniform integers in [lo, hi] stored as bf16 (all
-    exactly representable), for the exact-sum checks.
+    exactly representable), for the exact-sum checks;
+  * MXFP4 weights: uniform random bytes (two 4-bit codes each) and uniform
+    random 8-bit block scales in a band (by default 119..121, so weights of
+    magnitude about 0.02 like the bf16 ones).
 Seeds: workload c uses base 1000*c; tags add x:+0, W:+1 (expert e: +100+e),
 r:+2, routing:+3 (routing table i of a ring: +3+10*i).
 """
@@ -59,6 +62,23 @@ def routing_table(T: int, E: int, topk: int, seed: int) -> torch.Tensor:
     if not rows:
         return torch.empty((0, topk), dtype=torch.int32)
     return torch.stack(rows).to(torch.int32)
+
+
+def random_bytes(shape, lo: int, hi: int, seed: int, device: str = "cpu") -> torch.Tensor:
+    """uint8 tensor of uniform integers in [lo, hi] (packed 4-bit codes, or scale codes)."""
+    assert 0 <= lo <= hi <= 255
+    g = _generator(seed, device)
+    return torch.randint(lo, hi + 1, tuple(shape), generator=g, device=device,
+                         dtype=torch.int32).to(torch.uint8)
+
+
+def mxfp4_weights(N: int, K: int, seed: int, device: str = "cpu", scale_lo: int = 119,
+                  scale_hi: int = 121):
+    """(codes uint8 [N, K/2], scales uint8 [N, K/32]): random 4-bit weight codes and
+    block scale codes for a [N, K] MXFP4 weight matrix (K a multiple of 32)."""
+    assert K % 32 == 0
+    return (random_bytes((N, K // 2), 0, 255, seed, device),
+            random_bytes((N, K // 32), scale_lo, scale_hi, seed + 7919, device))
 
 
 def bits(t: torch.Tensor):

@@ -528,6 +528,123 @@ def check_router_topk_vs_sort(o):
                 assert len(set(ids[t].tolist())) == k
 
 
+# ---------------------------------------------------------------- MXFP4 weights
+
+
+def _mxfp4_golden_tables():
+    """{code: Fraction or 'nan'} for e2m1 and e8m0, from tests/golden/mxfp4_decode.txt."""
+    e2m1, e8m0 = {}, {}
+    for kind, code, value in read_table("mxfp4_decode.txt"):
+        v = "nan" if value == "nan" else (exact(value.lstrip("-")) * (-1 if value.startswith("-") else 1),
+                                          value.startswith("-"))
+        (e2m1 if kind == "e2m1" else e8m0)[int(code)] = v
+    return e2m1, e8m0
+
+
+def check_mxfp4_decode_golden(o):
+    e2m1, e8m0 = _mxfp4_golden_tables()
+    assert sorted(e2m1) == list(range(16)), "all 16 e2m1 codes are listed"
+    for code, (val, neg) in e2m1.items():
+        got = o.c.oracle_e2m1_to_f64(code)
+        assert Fraction(got) == val and math.copysign(1.0, got) == (-1.0 if neg else 1.0), (code, got)
+    for code, v in e8m0.items():
+        got = o.c.oracle_e8m0_to_f64(code)
+        if v == "nan":
+            assert math.isnan(got), (code, got)
+        else:
+            assert Fraction(got) == v[0], (code, got)
+
+
+def check_mxfp4_scales_vs_ldexp(o):
+    # every finite e8m0 code against the library's power of two
+    for s in range(255):
+        assert o.c.oracle_e8m0_to_f64(s) == math.ldexp(1.0, s - 127), s
+    assert math.isnan(o.c.oracle_e8m0_to_f64(255))
+
+
+def _mxfp4_golden_projection():
+    rows = read_table("mxfp4_projection_worked.txt")
+    x_nz = {int(kv.split("=")[0]): exact(kv.split("=")[1]) for kv in rows[0][1:]}
+    Ws = [[int(v, 16) for v in r[1:]] for r in rows if r[0] == "Ws:"]
+    Wq = [[int(v, 16) for v in r[1:]] for r in rows if r[0] == "Wq:"]
+    y = [r[1:] for r in rows if r[0] == "y:"][0]
+    A = [r[1:] for r in rows if r[0] == "A:"][0]
+    return x_nz, np.array(Wq, dtype=np.uint8), np.array(Ws, dtype=np.uint8), y, A
+
+
+def check_mxfp4_projection_golden(o):
+    x_nz, Wq, Ws, y_txt, A_txt = _mxfp4_golden_projection()
+    K = 64
+    x = np.zeros((1, K), dtype=np.float32)
+    for k, v in x_nz.items():
+        x[0, k] = float(v)
+    xb = bits_of(x)
+    assert np.array_equal(values(xb), x.astype(np.float64)), "x values exact in bf16"
+    y, A = o.projection_mxfp4(xb, Wq, Ws)
+    for n, (ty, ta) in enumerate(zip(y_txt, A_txt)):
+        if ty == "nan":
+            assert math.isnan(y[0, n]) and math.isnan(A[0, n]), n
+        else:
+            assert Fraction(y[0, n]) == exact(ty) and Fraction(A[0, n]) == exact(ta), (n, y[0, n], A[0, n])
+
+
+def _mxfp4_dequant_bf16(Wq, Ws):
+    """Dequantised weights as bf16 bits, built without the oracle: nibbles unpacked with
+    numpy (element 2i low, 2i+1 high), values from the golden e2m1 table, scales by
+    math.ldexp, rounded to bf16 by torch (exact: at most 2 significant bits)."""
+    e2m1, _ = _mxfp4_golden_tables()
+    table = np.array([float(e2m1[c][0]) * (-1.0 if e2m1[c][1] and e2m1[c][0] == 0 else 1.0)
+                      for c in range(16)])
+    N = Wq.shape[0]
+    codes = np.stack([Wq & 0x0F, Wq >> 4], axis=-1).reshape(N, -1)
+    K = codes.shape[1]
+    scale = np.array([[math.ldexp(1.0, int(s) - 127) if s != 255 else math.nan for s in row]
+                      for row in Ws])
+    w = table[codes] * np.repeat(scale, 32, axis=1)[:, :K]
+    wb = bits_of(w.astype(np.float32))
+    assert np.array_equal(values(wb), w, equal_nan=True), "dequantised weights exact in bf16"
+    return wb
+
+
+def check_mxfp4_vs_bf16_projection(o):
+    # the MXFP4 projection equals the (separately pinned) bf16 projection of the
+    # dequantised weights, term for term: the same products in the same order
+    rng = np.random.default_rng(31)
+    for M, N, K in [(1, 5, 32), (3, 7, 96), (2, 16, 256)]:
+        x = random_bf16((M, K), 40 + K)
+        Wq = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+        Ws = rng.integers(110, 135, (N, K // 32)).astype(np.uint8)
+        y4, A4 = o.projection_mxfp4(x, Wq, Ws)
+        y16, A16 = o.projection(x, _mxfp4_dequant_bf16(Wq, Ws))
+        assert np.array_equal(y4, y16) and np.array_equal(A4, A16), (M, N, K)
+
+
+def check_mxfp4_exact_small(o):
+    # exact rational brute force over the dequantised weights
+    rng = np.random.default_rng(32)
+    M, N, K = 2, 3, 64
+    x = random_bf16((M, K), 77)
+    Wq = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    Ws = rng.integers(118, 132, (N, K // 32)).astype(np.uint8)
+    y, A = o.projection_mxfp4(x, Wq, Ws)
+    ye, Ae = exact_projection(x, _mxfp4_dequant_bf16(Wq, Ws))
+    for m in range(M):
+        for n in range(N):
+            assert y[m, n] == float(ye[m][n]) and A[m, n] == float(Ae[m][n]), (m, n)
+
+
+def check_mxfp4_nan_scale_rows(o):
+    # a NaN scale poisons exactly the rows that use its block
+    rng = np.random.default_rng(33)
+    M, N, K = 2, 4, 96
+    x = random_bf16((M, K), 5)
+    Wq = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    Ws = np.full((N, K // 32), 127, dtype=np.uint8)
+    Ws[2, 1] = 255
+    y = o.projection_mxfp4(x, Wq, Ws, with_scale=False)
+    assert np.isnan(y[:, 2]).all() and not np.isnan(np.delete(y, 2, axis=1)).any()
+
+
 ALL_CHECKS = [
     check_bf16_decode_golden, check_bf16_decode_all_patterns, check_bf16_round_golden,
     check_bf16_round_vs_torch, check_bf16_round_bruteforce,
@@ -537,6 +654,8 @@ ALL_CHECKS = [
     check_splitk, check_splitk_sum_order, check_residual,
     check_moe_golden, check_moe_bruteforce, check_grouped,
     check_router_topk_golden, check_router_topk_vs_sort,
+    check_mxfp4_decode_golden, check_mxfp4_scales_vs_ldexp, check_mxfp4_projection_golden,
+    check_mxfp4_vs_bf16_projection, check_mxfp4_exact_small, check_mxfp4_nan_scale_rows,
 ]
 
 

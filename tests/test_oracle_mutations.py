@@ -55,6 +55,15 @@ MUTANTS = [
     ("topk ascending", "        return da > db;", "        return da < db;"),
     ("topk nan as +inf", "isnan(a) ? -INFINITY", "isnan(a) ? INFINITY"),
     ("topk retakes experts", "if (taken[e])", "if (0)"),
+    ("mxfp4 nibble order", "(k % 2 == 0) ? (byte & 0x0F) : (byte >> 4)",
+     "(k % 2 == 0) ? (byte >> 4) : (byte & 0x0F)"),
+    ("mxfp4 one scale a row", "Ws[n * (K / 32) + k / 32]", "Ws[n * (K / 32)]"),
+    ("e2m1 exponent bias", "ldexp(1.0 + m * 0.5, e - 1)", "ldexp(1.0 + m * 0.5, e)"),
+    ("e2m1 mantissa weight", "ldexp(1.0 + m * 0.5, e - 1)", "ldexp(1.0 + m * 0.25, e - 1)"),
+    ("e2m1 subnormal", "mag = m * 0.5;", "mag = m * 1.0;"),
+    ("e2m1 sign dropped", "return sign ? -mag : mag;", "return mag;"),
+    ("e8m0 bias", "ldexp(1.0, (int)s - 127)", "ldexp(1.0, (int)s - 128)"),
+    ("e8m0 nan code finite", "if (s == 255)\n        return NAN;", "if (0)\n        return NAN;"),
 ]
 
 
