@@ -319,6 +319,43 @@ def sweep(torch, sg, si, L, cyc, reps=40):
     del ring
     torch.cuda.empty_cache()
 
+    # MXFP4 weights (e2m1 codes + e8m0 block scales): the same shapes at a quarter of the
+    # weight bytes; a ring of code/scale copies larger than 2 x MALL per shape
+    c = L.c
+    for label, Ms, N, K, residual in (("mxfp4 8192x7168", (1, 2), 8192, 7168, False),
+                                      ("mxfp4 4096x7168", (4, 8), 4096, 7168, False),
+                                      ("mxfp4 residual 7168x8192", (1, 8), 7168, 8192, True)):
+        codes, scales = si.mxfp4_weights(N, K, si.seed_for(6, si.TAG_W) + N, dev)
+        per_copy = codes.numel() + scales.numel()
+        copies = max(1, math.ceil(RING_MIN_BYTES / per_copy))
+        ring = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(copies - 1)]
+        for M in Ms:
+            x = si.normal_bf16((M, K), 1.0, si.seed_for(6, si.TAG_X) + M, dev)
+            r = si.normal_bf16((M, N), 1.0, si.seed_for(6, si.TAG_R) + M, dev) if residual else None
+            y32 = None if residual else torch.empty((M, N), device=dev)
+            y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+            def mx(cw, sw, x=x, r=r, y32=y32, y16=y16, M=M, N=N, K=K):
+                args = (M, N, K, x.data_ptr(), cw.data_ptr(), sw.data_ptr(),
+                        r.data_ptr() if r is not None else None,
+                        y32.data_ptr() if y32 is not None else None, y16.data_ptr(), L.sp)
+
+                def go():
+                    st = c.skinny_gemm_mxfp4(*args)
+                    if st:
+                        raise RuntimeError(sg.skinny_gemm_status_str(st))
+                return go
+            per = timed_calls(torch, [mx(cw, sw) for cw, sw in ring], reps, cyc)
+            nbytes = N * K // 2 + N * K // 32 + M * K * 2 + M * N * 2 * (2 if residual else 1) + \
+                (0 if residual else M * N * 4)
+            us = 1e3 * per
+            gbs = nbytes / (per * 1e-3) / 1e9
+            rows.append({"workload": label, "M": M, "N": N, "K": K, "plan": "mxfp4_rowdot",
+                         "us": round(us, 3), "GBps": round(gbs, 1),
+                         "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
+        del ring
+    torch.cuda.empty_cache()
+
     # router: scores y = x W_r^T (E=384 experts, K=7168, fp32) and their top-8 per token
     E, K, k = 384, 7168, 8
     Wr = si.normal_bf16((E, K), 0.02, si.seed_for(5, si.TAG_W) + 99, dev)

@@ -77,10 +77,11 @@ typedef enum {
     SG_KERNEL_MOE_TABLE = 5,    /* per-expert token table                          */
     SG_KERNEL_GROUPED = 6,      /* grouped per-expert projection                   */
     SG_KERNEL_PREFETCH = 7,     /* side-stream weight prefetch                     */
-    SG_KERNEL_ROUTER_TOPK = 8   /* router top-k expert selection                   */
+    SG_KERNEL_ROUTER_TOPK = 8,  /* router top-k expert selection                   */
+    SG_KERNEL_MXFP4 = 9         /* projection with block-scaled 4-bit weights      */
 } sg_kernel;
 
-#define SG_NUM_COUNTERS 9
+#define SG_NUM_COUNTERS 10
 #define SG_MAX_M 64
 
 /* Launch decision for one projection shape.  Produced by skinny_gemm_plan
@@ -183,6 +184,30 @@ sg_status grouped_skinny_gemm(const sg_bf16* x, int32_t T, const sg_bf16* W, int
  * 1 <= k <= min(E, 32) (else SG_ERR_SHAPE); pointers 4-byte aligned. */
 sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int32_t k,
                                   int32_t* topk_ids, float* topk_scores, void* stream);
+
+/* y = x W^T with block-scaled 4-bit weights.  The pages' later evaluation
+ * model ships NVFP4 weights ([P] Experimental setup and Supplementary
+ * details: 4-bit floats with per-block scales); the block-scaled 4-bit
+ * format MI355X converts in hardware is OCP MXFP4, read here:
+ *   W_codes  [N, K/2] bytes: e2m1 codes (bit 3 sign, bits 2..1 exponent with
+ *            bias 1, bit 0 mantissa: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+ *            negatives); element k of row n is in byte n*K/2 + k/2, low
+ *            nibble for even k;
+ *   W_scales [N, K/32] bytes: e8m0 scale of elements [32b, 32b+32) of row
+ *            n, 2^(s-127); s == 255 is NaN (the row's outputs become NaN).
+ *   W[n,k] = e2m1 * 2^(s-127);  y[m,n] = sum_k x[m,k] W[n,k] in fp32
+ *   (products exact), then the epilogue of skinny_gemm_residual when r is
+ *   given (out = bf16_RNE(fp32(r) + y), r may alias y_bf16) or of
+ *   skinny_gemm otherwise.  One launch, no workspace; the weight stream is a
+ *   quarter of bf16's plus 1/16 for the scales.
+ * Limits: 0 <= M <= 8 (M > 8: SG_ERR_UNSUPPORTED), 0 <= N <= 1<<20,
+ * K % 32 == 0 (SG_ERR_ALIGN), K <= 65536 at M = 1, 32768 at M = 2, 16384
+ * above (else SG_ERR_UNSUPPORTED).  x, W_codes, r and outputs 16-byte
+ * aligned; W_scales any alignment.  Scales whose weights fall below fp32's
+ * normal range may lose those products. */
+sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
+                            const uint8_t* W_codes, const uint8_t* W_scales, const sg_bf16* r,
+                            float* y_f32, sg_bf16* y_bf16, void* stream);
 
 /* One MoE decode step of a layer on one GPU, with the shared expert on its
  * own stream ([P] Method details §3; [F] Partie 1 §3: the shared expert runs

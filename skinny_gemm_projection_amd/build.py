@@ -22,7 +22,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libskinny_gemm.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "plan.cpp", "moe_step.cpp", "rowdot.hip", "splitk_mfma.hip", "reduce.hip", "moe.hip", "router.hip",
+SOURCES = ["api.cpp", "plan.cpp", "moe_step.cpp", "rowdot.hip", "splitk_mfma.hip", "reduce.hip", "moe.hip", "router.hip", "mxfp4.hip",
            "prefetch.hip"]
 
 

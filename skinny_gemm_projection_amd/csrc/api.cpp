@@ -46,6 +46,7 @@ const char* kernel_name(int k) {
         case SG_KERNEL_GROUPED: return "grouped";
         case SG_KERNEL_PREFETCH: return "prefetch";
         case SG_KERNEL_ROUTER_TOPK: return "router_topk";
+        case SG_KERNEL_MXFP4: return "mxfp4";
         default: return "?";
     }
 }
@@ -190,6 +191,32 @@ sg_status grouped_skinny_gemm(const sg_bf16* x, int32_t T, const sg_bf16* W, int
 sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int32_t k,
                                   int32_t* topk_ids, float* topk_scores, void* stream) {
     return sg::router_topk_call(scores, E, T, E, k, topk_ids, topk_scores, stream);
+}
+
+sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
+                            const uint8_t* W_codes, const uint8_t* W_scales, const sg_bf16* r,
+                            float* y_f32, sg_bf16* y_bf16, void* stream) {
+    if (M < 0 || N < 0 || N > (1 << 20) || K < 0) return SG_ERR_SHAPE;
+    if (M > sg::kMxfp4MaxM) return SG_ERR_UNSUPPORTED;
+    if (K % 32 != 0) return SG_ERR_ALIGN;
+    int nb, splits;
+    if (!sg::mxfp4_split(M, K, &nb, &splits)) return SG_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return SG_OK;
+    if (!y_f32 && !y_bf16) return SG_ERR_NULL;
+    if (K > 0 && (!x || !W_codes || !W_scales)) return SG_ERR_NULL;
+    if (!aligned16(x) || !aligned16(W_codes) || !aligned16(r) || !aligned16(y_f32) ||
+        !aligned16(y_bf16))
+        return SG_ERR_ALIGN;
+    (void)hipGetLastError();
+    const sg::Epilogue ep{nullptr, y_f32, y_bf16, r};
+    if (sg::launch_mxfp4(M, N, K, x, W_codes, W_scales, ep, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return SG_ERR_HIP;
+    count(SG_KERNEL_MXFP4);
+    if (log_enabled())
+        std::fprintf(stderr, "[skinny_gemm] mxfp4 M=%d N=%d K=%d blocks/lane=%d split_k=%d%s\n",
+                     M, N, K, nb, splits, r ? " residual" : "");
+    return SG_OK;
 }
 
 sg_status skinny_gemm_prefetch(const void* W, size_t bytes, void* stream) {

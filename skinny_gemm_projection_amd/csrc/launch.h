@@ -89,6 +89,16 @@ hipError_t launch_grouped(const void* x, int T, const void* W, int E, int N, int
 
 hipError_t launch_prefetch(const void* W, size_t bytes, hipStream_t stream);
 
+// Projection with MXFP4 weights (1 <= M <= kMxfp4MaxM, K % 32 == 0):
+// Wq [N, K/2] e2m1 codes, Ws [N, K/32] e8m0 scales.  mxfp4_split gives the
+// blocks per lane and the team split for (M, K); false when K needs more
+// than kMxfp4MaxSplit waves per row.
+constexpr int kMxfp4MaxM = 8;
+constexpr int kMxfp4MaxSplit = 8;
+bool mxfp4_split(int M, int K, int* nb, int* splits);
+hipError_t launch_mxfp4(int M, int N, int K, const void* x, const void* Wq, const uint8_t* Ws,
+                        const Epilogue& ep, hipStream_t stream);
+
 // Router top-k: ids [T,k] (and their scores) from fp32 scores, row t at
 // scores + t*ld (ld >= E); E <= 4096, k <= 32 (checked by the caller).
 hipError_t launch_router_topk(const float* scores, int64_t ld, int T, int E, int k,

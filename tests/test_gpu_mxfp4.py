@@ -1,0 +1,132 @@
+"""GPU parity of the projection with MXFP4 weights (skinny_gemm_mxfp4) through the
+C ABI, against oracle_projection_mxfp4 on the same seeded codes and scales:
+fp32 |got - ref| <= 1e-3 * A, bf16 adds 2^-8 |ref|, the residual adds 2^-23 |r + y|;
+integer-valued activations with unit scales are bit-exact (every product is a
+multiple of 1/2 and every partial sum exact in fp32)."""
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as si
+import skinny_gemm_projection_amd as sg
+from gpu_common import (DEV, announce, bits, check_bf16, check_exact, check_f32, counters_delta,
+                        orc, sample_rows)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
+
+
+def np_u8(t):
+    return t.cpu().numpy()
+
+
+def run(x, codes, scales, r=None, f32=True, bf16=True):
+    M, N = x.shape[0], codes.shape[0]
+    y32 = torch.full((M, N), -7.0, device=DEV) if f32 else None
+    y16 = torch.full((M, N), -7.0, device=DEV, dtype=torch.bfloat16) if bf16 else None
+    before = sg.skinny_gemm_get_counters()
+    sg.skinny_gemm_mxfp4(x, codes, scales, y_f32=y32, y_bf16=y16, r=r)
+    torch.cuda.synchronize()
+    d = counters_delta(before, sg.skinny_gemm_get_counters())
+    assert d[sg.SG_KERNEL_MXFP4] == (1 if M > 0 and N > 0 else 0)
+    return y32, y16
+
+
+SHAPES = [(1, 40, 32), (1, 129, 96), (1, 77, 608), (1, 65, 2080), (1, 33, 8224),
+          (2, 50, 4128), (2, 17, 8192), (3, 70, 2080), (4, 96, 4160), (5, 31, 640),
+          (6, 64, 7168), (7, 45, 2048), (8, 130, 3200), (8, 20, 16384)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_mxfp4_small(M, N, K):
+    announce(f"mxfp4 M={M} N={N} K={K}")
+    x = si.normal_bf16((M, K), 1.0, 8000 + K + M, DEV)
+    codes, scales = si.mxfp4_weights(N, K, 8100 + N + K, DEV)
+    y32, y16 = run(x, codes, scales)
+    ref, A = orc().projection_mxfp4(bits(x), np_u8(codes), np_u8(scales))
+    check_f32(y32, ref, A, f"mxfp4 fp32 M={M} N={N} K={K}")
+    check_bf16(y16, ref, A, f"mxfp4 bf16 M={M} N={N} K={K}")
+    # residual epilogue, in place on the bf16 output
+    r = si.normal_bf16((M, N), 1.0, 8200 + N, DEV)
+    out = r.clone()
+    sg.skinny_gemm_mxfp4(x, codes, scales, y_bf16=out, r=out)
+    torch.cuda.synchronize()
+    rr = orc().bf16_to_f64(bits(r)).reshape(M, N)
+    check_bf16(out, rr + ref, A, f"mxfp4 residual M={M} N={N} K={K}")
+    y32b, _ = run(x, codes, scales, bf16=False)
+    assert torch.equal(y32, y32b), "repeat runs bitwise identical"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 37, 4096), (2, 64, 7168), (8, 40, 8192), (5, 19, 96)])
+def test_mxfp4_integer_bit_exact(M, N, K):
+    announce(f"mxfp4 integer M={M} N={N} K={K}")
+    x = si.integer_bf16((M, K), -4, 4, 8300 + K, DEV)
+    codes = si.random_bytes((N, K // 2), 0, 255, 8301 + N, DEV)
+    scales = torch.full((N, K // 32), 127, dtype=torch.uint8, device=DEV)  # unit scales
+    y32, y16 = run(x, codes, scales)
+    ref = orc().projection_mxfp4(bits(x), np_u8(codes), np_u8(scales), with_scale=False)
+    check_exact(y32, ref, f"mxfp4 integer M={M}")
+    check_exact(y16.float(), orc().bf16_to_f64(orc().encode_bf16(ref)).reshape(M, N),
+                f"mxfp4 integer bf16 M={M}")
+
+
+def test_mxfp4_nan_scale_and_extremes():
+    announce("mxfp4 NaN scale, extreme scales, zero codes")
+    M, N, K = 3, 24, 512
+    x = si.normal_bf16((M, K), 1.0, 8400, DEV)
+    codes, scales = si.mxfp4_weights(N, K, 8401, DEV)
+    scales[5, 3] = 255      # NaN block: row 5 is NaN for every m
+    scales[7, :] = 200      # large scale, 2^73 (finite fp32 sums for these x)
+    scales[9, :] = 16       # small scale, 2^-111: products stay normal in fp32
+    codes[11, :] = 0        # all +0 codes
+    codes[12, :] = 0x88     # all -0 codes
+    y32, _ = run(x, codes, scales, bf16=False)
+    ref, A = orc().projection_mxfp4(bits(x), np_u8(codes), np_u8(scales))
+    y = y32.cpu().numpy()
+    assert np.isnan(y[:, 5]).all() and not np.isnan(np.delete(y, 5, axis=1)).any()
+    keep = [n for n in range(N) if n != 5]
+    check_f32(y32[:, keep], ref[:, keep], A[:, keep], "mxfp4 extremes")
+    assert (y[:, 11] == 0).all() and (y[:, 12] == 0).all()
+
+
+def test_mxfp4_empty_and_rejected():
+    announce("mxfp4 empty and rejected sizes")
+    x = si.normal_bf16((2, 64), 1.0, 1, DEV)
+    codes, scales = si.mxfp4_weights(8, 64, 2, DEV)
+    y = torch.full((2, 8), -7.0, device=DEV)
+    # K = 0: y = 0
+    sg.skinny_gemm_mxfp4(torch.empty((2, 0), dtype=torch.bfloat16, device=DEV),
+                         torch.empty((8, 0), dtype=torch.uint8, device=DEV),
+                         torch.empty((8, 0), dtype=torch.uint8, device=DEV), y_f32=y)
+    torch.cuda.synchronize()
+    assert (y == 0).all()
+    lib = sg._c()
+    y.fill_(-7.0)
+    s = torch.cuda.current_stream().cuda_stream
+    cases = [((9, 8, 64), 3),          # batch above the 4-bit path
+             ((2, 8, 48), 4),          # K not a multiple of 32
+             ((3, 8, 16416), 3),       # K over the split limit at M >= 3
+             ((2, -1, 64), 2)]
+    for (M, N, K), status in cases:
+        before = sg.skinny_gemm_get_counters()
+        st = lib.skinny_gemm_mxfp4(M, N, K, x.data_ptr(), codes.data_ptr(), scales.data_ptr(),
+                                   None, y.data_ptr(), None, s)
+        assert st == status, ((M, N, K), st)
+        assert counters_delta(before, sg.skinny_gemm_get_counters()) == [0] * sg.SG_NUM_COUNTERS
+    torch.cuda.synchronize()
+    assert (y == -7.0).all(), "a rejected call leaves the output alone"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8192, 7168), (2, 8192, 7168), (4, 4096, 7168),
+                                   (8, 4096, 7168), (1, 7168, 8192), (8, 7168, 8192)])
+def test_mxfp4_full_size(M, N, K):
+    # the benchmark's shapes: sampled output rows against the oracle
+    announce(f"mxfp4 full M={M} N={N} K={K}")
+    x = si.normal_bf16((M, K), 1.0, 8500 + M, DEV)
+    codes, scales = si.mxfp4_weights(N, K, 8600 + N, DEV)
+    y32, y16 = run(x, codes, scales)
+    rows = sample_rows(N, 96, M + N)
+    ref, A = orc().projection_mxfp4(bits(x), np_u8(codes)[rows], np_u8(scales)[rows])
+    idx = torch.as_tensor(rows, device=DEV)
+    check_f32(y32[:, idx], ref, A, f"mxfp4 full fp32 M={M}")
+    check_bf16(y16[:, idx], ref, A, f"mxfp4 full bf16 M={M}")
