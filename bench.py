@@ -323,7 +323,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
     # weight bytes; a ring of code/scale copies larger than 2 x MALL per shape
     c = L.c
     for label, Ms, N, K, residual in (("mxfp4 8192x7168", (1, 2), 8192, 7168, False),
-                                      ("mxfp4 4096x7168", (4, 8), 4096, 7168, False),
+                                      ("mxfp4 4096x7168", (4, 8, 16), 4096, 7168, False),
                                       ("mxfp4 residual 7168x8192", (1, 8), 7168, 8192, True)):
         codes, scales = si.mxfp4_weights(N, K, si.seed_for(6, si.TAG_W) + N, dev)
         per_copy = codes.numel() + scales.numel()
@@ -350,7 +350,8 @@ def sweep(torch, sg, si, L, cyc, reps=40):
                 (0 if residual else M * N * 4)
             us = 1e3 * per
             gbs = nbytes / (per * 1e-3) / 1e9
-            rows.append({"workload": label, "M": M, "N": N, "K": K, "plan": "mxfp4_rowdot",
+            rows.append({"workload": label, "M": M, "N": N, "K": K,
+                         "plan": "mxfp4_mfma" if M >= 9 else "mxfp4_rowdot",
                          "us": round(us, 3), "GBps": round(gbs, 1),
                          "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
         del ring
@@ -647,6 +648,41 @@ def profile_workloads(torch, sg, si, L, manifest_path, reps=3):
         run("MoE grouped E=384 2048x7168 top8", T, N, K, "moe_table+grouped",
             [L.grouped(x, W, ids.to(dev), out, ws)], nbytes)
     del W
+    torch.cuda.empty_cache()
+    # MXFP4 weights
+    for label, Ms, N, K in (("mxfp4 8192x7168", (1, 2), 8192, 7168),
+                            ("mxfp4 4096x7168", (4, 8, 16), 4096, 7168)):
+        codes, scales = si.mxfp4_weights(N, K, 17, dev)
+        ring = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(reps - 1)]
+        for M in Ms:
+            x = si.normal_bf16((M, K), 1.0, 18, dev)
+            y32 = torch.empty((M, N), device=dev)
+            y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+            def mx(cw, sw, x=x, y32=y32, y16=y16, M=M, N=N, K=K):
+                return lambda: sg.skinny_gemm_mxfp4(x, cw, sw, y_f32=y32, y_bf16=y16)
+            nbytes = N * K // 2 + N * K // 32 + M * K * 2 + M * N * 6
+            run(label, M, N, K, "mxfp4_mfma" if M >= 9 else "mxfp4_rowdot",
+                [mx(cw, sw) for cw, sw in ring], nbytes)
+        del ring
+    # router scores + top-8 (E = 384, K = 7168)
+    E, K, k = 384, 7168, 8
+    W0 = si.normal_bf16((E, K), 0.02, 19, dev)
+    ring = [W0] + [W0.clone() for _ in range(reps - 1)]
+    for T in (1, 64):
+        x = si.normal_bf16((T, K), 1.0, 20, dev)
+        p = sg.skinny_gemm_plan(T, E, K)
+        scores = torch.empty((T, E), device=dev)
+        ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+
+        def rt(w, x=x, p=p, scores=scores, ws=ws):
+            def go():
+                L.projection(p, x, w, scores, None, ws)()
+                sg.skinny_gemm_router_topk(scores, k)
+            return go
+        run("router top-8 E=384 K=7168", T, E, K, f"{desc(p)}+router_topk",
+            [rt(w) for w in ring], proj_bytes(T, E, K, bf16=False) + T * E * 4 + T * k * 4)
+    del ring, W0
     torch.cuda.empty_cache()
     with open(manifest_path, "w") as f:
         json.dump(manifest, f, indent=1)

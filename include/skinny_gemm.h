@@ -199,12 +199,15 @@ sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int
  *   (products exact), then the epilogue of skinny_gemm_residual when r is
  *   given (out = bf16_RNE(fp32(r) + y), r may alias y_bf16) or of
  *   skinny_gemm otherwise.  One launch, no workspace; the weight stream is a
- *   quarter of bf16's plus 1/16 for the scales.
- * Limits: 0 <= M <= 8 (M > 8: SG_ERR_UNSUPPORTED), 0 <= N <= 1<<20,
- * K % 32 == 0 (SG_ERR_ALIGN), K <= 65536 at M = 1, 32768 at M = 2, 16384
- * above (else SG_ERR_UNSUPPORTED).  x, W_codes, r and outputs 16-byte
- * aligned; W_scales any alignment.  Scales whose weights fall below fp32's
- * normal range may lose those products. */
+ *   quarter of bf16's plus 1/16 for the scales.  M <= 8 runs on the vector
+ *   ALU, 9 <= M <= 16 on bf16 matrix cores (the codes converted straight
+ *   into operand layout).
+ * Limits: 0 <= M <= 16 (M > 16: SG_ERR_UNSUPPORTED), 0 <= N <= 1<<20,
+ * 0 <= K <= 1<<20 (else SG_ERR_SHAPE), K % 32 == 0 (SG_ERR_ALIGN); K <=
+ * 65536 at M = 1, 32768 at M = 2 and 16384 for 3 <= M <= 8 (else
+ * SG_ERR_UNSUPPORTED).  x,
+ * W_codes, r and outputs 16-byte aligned; W_scales any alignment.  Scales
+ * whose weights fall below fp32's normal range may lose those products. */
 sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
                             const uint8_t* W_codes, const uint8_t* W_scales, const sg_bf16* r,
                             float* y_f32, sg_bf16* y_bf16, void* stream);

@@ -196,7 +196,7 @@ sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int
 sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
                             const uint8_t* W_codes, const uint8_t* W_scales, const sg_bf16* r,
                             float* y_f32, sg_bf16* y_bf16, void* stream) {
-    if (M < 0 || N < 0 || N > (1 << 20) || K < 0) return SG_ERR_SHAPE;
+    if (M < 0 || N < 0 || N > (1 << 20) || K < 0 || K > (1 << 20)) return SG_ERR_SHAPE;
     if (M > sg::kMxfp4MaxM) return SG_ERR_UNSUPPORTED;
     if (K % 32 != 0) return SG_ERR_ALIGN;
     int nb, splits;
@@ -214,8 +214,9 @@ sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
         return SG_ERR_HIP;
     count(SG_KERNEL_MXFP4);
     if (log_enabled())
-        std::fprintf(stderr, "[skinny_gemm] mxfp4 M=%d N=%d K=%d blocks/lane=%d split_k=%d%s\n",
-                     M, N, K, nb, splits, r ? " residual" : "");
+        std::fprintf(stderr, "[skinny_gemm] mxfp4 M=%d N=%d K=%d %s%s\n", M, N, K,
+                     M >= sg::kMxfp4MfmaFromM ? "matrix cores" : "vector ALU",
+                     r ? " residual" : "");
     return SG_OK;
 }
 

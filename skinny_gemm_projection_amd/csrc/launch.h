@@ -90,10 +90,12 @@ hipError_t launch_grouped(const void* x, int T, const void* W, int E, int N, int
 hipError_t launch_prefetch(const void* W, size_t bytes, hipStream_t stream);
 
 // Projection with MXFP4 weights (1 <= M <= kMxfp4MaxM, K % 32 == 0):
-// Wq [N, K/2] e2m1 codes, Ws [N, K/32] e8m0 scales.  mxfp4_split gives the
-// blocks per lane and the team split for (M, K); false when K needs more
-// than kMxfp4MaxSplit waves per row.
-constexpr int kMxfp4MaxM = 8;
+// Wq [N, K/2] e2m1 codes, Ws [N, K/32] e8m0 scales.  Below kMxfp4MfmaFromM
+// rows the VALU kernel runs; mxfp4_split gives its blocks per lane and team
+// split for (M, K), false when K needs more than kMxfp4MaxSplit waves per
+// row.  From kMxfp4MfmaFromM rows the matrix-core kernel runs (any K).
+constexpr int kMxfp4MaxM = 16;
+constexpr int kMxfp4MfmaFromM = 9;  // measured: the VALU kernel is faster through M = 8
 constexpr int kMxfp4MaxSplit = 8;
 bool mxfp4_split(int M, int K, int* nb, int* splits);
 hipError_t launch_mxfp4(int M, int N, int K, const void* x, const void* Wq, const uint8_t* Ws,

@@ -24,6 +24,20 @@
 // Rows are grouped R per iteration, their R*M lane partials reduced
 // together by the reduce-scatter of the bf16 kernel; S waves of a workgroup
 // split K and add their partials in LDS in ascending chunk order.
+//
+// From 9 rows of batch the VALU dots (16*M per block and row) outgrow the
+// weight stream, and a matrix-core kernel takes over (up to 16 rows of x,
+// one MFMA m-tile).  Lane (col, grp) of a wave on a 16-row tile loads block
+// grp of a 128-element window of row col -- the weights of one
+// v_mfma_f32_16x16x32_bf16 B operand per step t, as dword t of that block,
+// converted in 4 instructions straight into operand layout (no LDS
+// transpose).  The matching A operand is x[m][window + 32*grp + 8*t ..+8),
+// read from L2: inside a 32-wide step the k order is free, A and B only have
+// to agree.  S waves of a workgroup split K over the tile (8 windows in
+// flight each) and add their 16x16 tiles in LDS in ascending order.
+// Measured on MI355X it trails the VALU kernel through M = 8: its x operands
+// are four 16-byte reads per 1 KB of codes, scattered over 32 cache lines
+// per instruction, so the L1/L2 request rate -- not HBM -- sets its time.
 #include "launch.h"
 
 namespace sg {
@@ -56,13 +70,22 @@ __device__ __forceinline__ float dot_block(const uint4 (&xb)[4], const uint4 w, 
 constexpr int pad4(int v) { return (v + 3) / 4 * 4; }
 constexpr int team_waves(int S) { return S > kWavesPerBlock ? S : kWavesPerBlock; }
 
+// Rows whose M partials one lane reduce-scatter finishes (at most 64 values).
+constexpr int reduce_rows(int M, int R) {
+    int rb = 1;
+    while (rb * 2 <= R && rb * 2 * M <= 64) rb *= 2;
+    return rb;
+}
+
 template <int M, int NB, int R, int S>
 __global__ __launch_bounds__(kWave * team_waves(S)) void mxfp4_rowdot_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ Wq, const uint8_t* __restrict__ Ws,
     int N, int KB, int chunk_b, int iters, Epilogue ep) {
     constexpr int kWaves = team_waves(S);
     constexpr int kTeams = kWaves / S;
-    constexpr int V = pad4(R * M);
+    constexpr int RB = reduce_rows(M, R);  // rows per reduce-scatter
+    static_assert(R % RB == 0, "whole reduction batches");
+    constexpr int V = pad4(RB * M);
     __shared__ float red[2][kTeams][S][V];
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -92,73 +115,173 @@ __global__ __launch_bounds__(kWave * team_waves(S)) void mxfp4_rowdot_kernel(
     for (int it = 0; it < iters; ++it) {
         const int g = team + it * teams;
         const int n0 = g * R;
-        float acc[V];
+        // all R rows' codes and scales are requested with the first batch; the
+        // dots of each batch of RB rows are formed right before its reduction
+        uint4 wr[R][NB];
+        uint32_t sc[R][NB];
 #pragma unroll
-        for (int v = 0; v < V; ++v) acc[v] = 0.0f;
-        if (g < groups) {
-            uint4 wr[R][NB];
-            uint32_t sc[R][NB];
+        for (int q = 0; q < R / RB; ++q) {  // batches of RB rows
+            float part[V];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int n = n0 + r;
-                const bool ok = n < N;
-                const int64_t row = (int64_t)(ok ? n : 0) * KB + b0;
-                const rsrc_t rw = make_rsrc(Wq + row, ok ? (uint32_t)len * 16u : 0u);
-                const rsrc_t rs = make_rsrc(Ws + row, ok ? (uint32_t)len : 0u);
+            for (int v = 0; v < V; ++v) part[v] = 0.0f;
+            if (g < groups) {
+                if (q == 0) {
 #pragma unroll
-                for (int c = 0; c < NB; ++c) {
-                    wr[r][c] = load16<kStream>(rw, (uint32_t)(c * kWave + lane) * 16u);
-                    sc[r][c] = __builtin_amdgcn_raw_buffer_load_b8(
-                        rs, (uint32_t)(c * kWave + lane), 0, kStream);
+                    for (int r = 0; r < R; ++r) {
+                        const int n = n0 + r;
+                        const bool ok = n < N;
+                        const int64_t row = (int64_t)(ok ? n : 0) * KB + b0;
+                        const rsrc_t rw = make_rsrc(Wq + row, ok ? (uint32_t)len * 16u : 0u);
+                        const rsrc_t rs = make_rsrc(Ws + row, ok ? (uint32_t)len : 0u);
+#pragma unroll
+                        for (int c = 0; c < NB; ++c) {
+                            wr[r][c] = load16<kStream>(rw, (uint32_t)(c * kWave + lane) * 16u);
+                            sc[r][c] = __builtin_amdgcn_raw_buffer_load_b8(
+                                rs, (uint32_t)(c * kWave + lane), 0, kStream);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < RB; ++i) {
+                    const int r = q * RB + i;
+                    bool nan_scale = false;
+                    float scale[NB];
+#pragma unroll
+                    for (int c = 0; c < NB; ++c) {
+                        nan_scale |= sc[r][c] == 255u;
+                        scale[c] = as_f(sc[r][c] << 23);  // e8m0 code in the exponent field
+                    }
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        float a = 0.0f;
+#pragma unroll
+                        for (int c = 0; c < NB; ++c) a = dot_block(xr[m][c], wr[r][c], scale[c], a);
+                        part[i * M + m] = nan_scale ? __builtin_nanf("") : a;
+                    }
                 }
             }
+            const float total = reduce_scatter<V>(part, lane);
+            const int v = scatter_index<V>(lane);
+            const bool mine = v >= 0 && v < RB * M;
+            const int r = mine ? q * RB + v / M : 0;
+            const int m = mine ? v % M : 0;
+            const int n = n0 + r;
+            const bool live = mine && g < groups && n < N;
+            if (S == 1) {
+                if (live) store_final(ep, (int64_t)m * N + n, total);
+            } else {
+                const int buf = (it * (R / RB) + q) & 1;
+                if (mine) red[buf][team_in_block][member][v] = total;
+                __syncthreads();
+                if (member == 0 && live) {
+                    float sum = red[buf][team_in_block][0][v];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                bool nan_scale = false;
-                float scale[NB];
-#pragma unroll
-                for (int c = 0; c < NB; ++c) {
-                    nan_scale |= sc[r][c] == 255u;
-                    scale[c] = as_f(sc[r][c] << 23);  // e8m0 code in the exponent field
+                    for (int s = 1; s < S; ++s) sum += red[buf][team_in_block][s][v];
+                    store_final(ep, (int64_t)m * N + n, sum);
                 }
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    float a = 0.0f;
-#pragma unroll
-                    for (int c = 0; c < NB; ++c) a = dot_block(xr[m][c], wr[r][c], scale[c], a);
-                    acc[r * M + m] = nan_scale ? __builtin_nanf("") : a;
-                }
-            }
-        }
-        const float total = reduce_scatter<V>(acc, lane);
-        const int v = scatter_index<V>(lane);
-        const bool mine = v >= 0 && v < R * M;
-        const int r = mine ? v / M : 0;
-        const int m = mine ? v - r * M : 0;
-        const int n = n0 + r;
-        const bool live = mine && g < groups && n < N;
-        if (S == 1) {
-            if (live) store_final(ep, (int64_t)m * N + n, total);
-        } else {
-            const int buf = it & 1;
-            if (mine) red[buf][team_in_block][member][v] = total;
-            __syncthreads();
-            if (member == 0 && live) {
-                float sum = red[buf][team_in_block][0][v];
-#pragma unroll
-                for (int s = 1; s < S; ++s) sum += red[buf][team_in_block][s][v];
-                store_final(ep, (int64_t)m * N + n, sum);
             }
         }
     }
 }
 
+// Matrix-core kernel: one workgroup of S waves per 16-row tile of W; wave s
+// takes windows [s*chunk_w, (s+1)*chunk_w) of 128 elements (4 blocks), D of
+// them in flight at a time.
+constexpr int kMfmaWindows = 8;
+
+template <int S>
+__global__ __launch_bounds__(kWave * S) void mxfp4_mfma_kernel(
+    const uint4* __restrict__ x, const uint4* __restrict__ Wq, const uint8_t* __restrict__ Ws,
+    int M, int N, int KB, int chunk_w, Epilogue ep) {
+    constexpr int D = kMfmaWindows;
+    __shared__ f32x4_t red[S > 1 ? S : 1][kWave];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int col = lane & 15, grp = lane >> 4;
+    const int s = wave_id_in_block();
+    const int n0 = blockIdx.x * 16;
+    const int rows = min(16, N - n0);
+    const int K8 = KB * 4;  // 16-byte pieces of an x row
+    const int KW = (KB + 3) / 4;
+    const int w0 = s * chunk_w;
+    const int w1 = min(KW, w0 + chunk_w);
+
+    // wave-uniform descriptors over the tile's codes and scales and over x:
+    // rows past N and x rows past M read zero
+    const rsrc_t rw = make_rsrc(Wq + (int64_t)n0 * KB, (uint32_t)rows * KB * 16u);
+    const rsrc_t rs = make_rsrc(Ws + (int64_t)n0 * KB, (uint32_t)rows * KB);
+    const rsrc_t rx = make_rsrc(x, (uint32_t)M * K8 * 16u);
+    constexpr uint32_t kOut = 0xFFFFFFF0u;  // past any range: reads zero
+
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    bool nan_scale = false;
+    for (int wb = w0; wb < w1; wb += D) {
+        uint4 wv[D], xa[D][4];
+        uint32_t sc[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int w = wb + d;
+            const int b = 4 * w + grp;  // this lane's block of row col
+            const bool ok = w < w1 && b < KB;
+            wv[d] = load16<kStream>(rw, ok ? (uint32_t)(col * KB + b) * 16u : kOut);
+            sc[d] = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? (uint32_t)(col * KB + b) : kOut,
+                                                        0, kStream);
+            const uint32_t xo = ok ? (uint32_t)(col * K8 + 4 * b) * 16u : kOut;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xa[d][t] = load16<kCached>(rx, ok ? xo + 16u * t : kOut);
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            nan_scale |= sc[d] == 255u;
+            const float scale = as_f(sc[d] << 23);  // e8m0 code in the exponent field
+            const uint32_t wd[4] = {wv[d].x, wv[d].y, wv[d].z, wv[d].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint4 b = {
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[t], scale, 0)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[t], scale, 1)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[t], scale, 2)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[t], scale, 3))};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[d][t]),
+                                                              __builtin_bit_cast(bf16x8_t, b), acc,
+                                                              0, 0, 0);
+            }
+        }
+    }
+    // a NaN scale anywhere in row col's blocks of this chunk: that row is NaN
+    const uint64_t flagged = __ballot(nan_scale);
+    const uint32_t rows_nan = (uint32_t)((flagged | flagged >> 16 | flagged >> 32 | flagged >> 48) &
+                                         0xFFFFu);
+    if ((rows_nan >> col) & 1u) {
+        const float q = __builtin_nanf("");
+        acc = f32x4_t{q, q, q, q};
+    }
+    if (S > 1) {
+        red[s][lane] = acc;
+        __syncthreads();
+        if (s != 0) return;
+#pragma unroll
+        for (int j = 1; j < S; ++j) acc += red[j][lane];
+    }
+    if (col >= rows) return;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int m = 4 * grp + v;
+        if (m < M) store_final(ep, (int64_t)m * N + n0 + col, acc[v]);
+    }
+}
+
 constexpr int kResidentWaves = 2048;  // 256 CUs x 8 waves
-constexpr int kRows = 8;              // rows per wave iteration: 8 x NB KB of codes in flight
+
+// Rows per wave iteration (R * NB KB of codes in flight per wave).  Measured
+// on MI355X at K = 7168 and 8192: 8 rows at every M (4 and 16 were slower; 16
+// rows at M >= 7 also halve the resident waves).
+constexpr int mxfp4_rows(int) { return 8; }
 
 template <int M, int NB, int S>
 hipError_t launch_mns(int N, int KB, int chunk_b, const void* x, const void* Wq,
                       const uint8_t* Ws, const Epilogue& ep, hipStream_t stream) {
+    constexpr int kRows = mxfp4_rows(M);
     constexpr int kTeams = team_waves(S) / S;
     const int groups = (N + kRows - 1) / kRows;
     const int cap = kResidentWaves / S;
@@ -200,7 +323,21 @@ hipError_t launch_m(int NB, int S, int N, int KB, int chunk_b, const void* x, co
 
 }  // namespace
 
+void mxfp4_mfma_split(int N, int K, int* splits, int* chunk_w) {
+    const int KW = (K / kBlockElems + 3) / 4;
+    const int tiles = (N + 15) / 16;
+    int S = 1;
+    while (S < 8 && S < KW && tiles * S < kResidentWaves) S *= 2;
+    *splits = S;
+    *chunk_w = KW > 0 ? (KW + S - 1) / S : 0;
+}
+
 bool mxfp4_split(int M, int K, int* nb, int* splits) {
+    if (M >= kMxfp4MfmaFromM) {  // matrix-core kernel: any K (team split of windows)
+        *nb = 0;
+        *splits = 0;
+        return true;
+    }
     const int KB = K / kBlockElems;
     const int nb_max = M == 1 ? 4 : (M == 2 ? 2 : 1);
     int NB = 1;
@@ -215,6 +352,22 @@ bool mxfp4_split(int M, int K, int* nb, int* splits) {
 hipError_t launch_mxfp4(int M, int N, int K, const void* x, const void* Wq, const uint8_t* Ws,
                         const Epilogue& ep, hipStream_t stream) {
     const int KB = K / kBlockElems;
+    if (M >= kMxfp4MfmaFromM) {
+        int S, chunk_w;
+        mxfp4_mfma_split(N, K, &S, &chunk_w);
+        const int grid = (N + 15) / 16;
+        const uint4* xp = static_cast<const uint4*>(x);
+        const uint4* wp = static_cast<const uint4*>(Wq);
+        switch (S) {
+#define SG_S(v) \
+    case v: \
+        mxfp4_mfma_kernel<v><<<grid, kWave * v, 0, stream>>>(xp, wp, Ws, M, N, KB, chunk_w, ep); \
+        return hipGetLastError();
+            SG_S(1) SG_S(2) SG_S(4) SG_S(8)
+#undef SG_S
+            default: return hipErrorInvalidValue;
+        }
+    }
     int NB, S;
     if (!mxfp4_split(M, K, &NB, &S)) return hipErrorInvalidValue;
     const int chunk_b = NB * kWave;  // blocks per wave: lanes x blocks per lane

@@ -105,6 +105,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 template <int V>
 __device__ __forceinline__ float reduce_scatter(const float (&a)[V], int lane) {
     static_assert(V % 4 == 0, "pad V to a multiple of 4");
+    static_assert(V <= 4 * 16, "at most 16 values per 16-lane row");
     constexpr int H = V / 2, Q = V / 4;
     float b[H];
 #pragma unroll

@@ -34,7 +34,8 @@ def run(x, codes, scales, r=None, f32=True, bf16=True):
 
 SHAPES = [(1, 40, 32), (1, 129, 96), (1, 77, 608), (1, 65, 2080), (1, 33, 8224),
           (2, 50, 4128), (2, 17, 8192), (3, 70, 2080), (4, 96, 4160), (5, 31, 640),
-          (6, 64, 7168), (7, 45, 2048), (8, 130, 3200), (8, 20, 16384)]
+          (6, 64, 7168), (7, 45, 2048), (8, 130, 3200), (8, 20, 16384), (9, 40, 2080),
+          (12, 33, 608), (13, 70, 8224), (16, 100, 7168), (16, 17, 96), (16, 16, 32)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -57,7 +58,8 @@ def test_mxfp4_small(M, N, K):
     assert torch.equal(y32, y32b), "repeat runs bitwise identical"
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 37, 4096), (2, 64, 7168), (8, 40, 8192), (5, 19, 96)])
+@pytest.mark.parametrize("M,N,K", [(1, 37, 4096), (2, 64, 7168), (8, 40, 8192), (5, 19, 96),
+                                   (16, 48, 4096), (11, 21, 8192)])
 def test_mxfp4_integer_bit_exact(M, N, K):
     announce(f"mxfp4 integer M={M} N={N} K={K}")
     x = si.integer_bf16((M, K), -4, 4, 8300 + K, DEV)
@@ -103,9 +105,11 @@ def test_mxfp4_empty_and_rejected():
     lib = sg._c()
     y.fill_(-7.0)
     s = torch.cuda.current_stream().cuda_stream
-    cases = [((9, 8, 64), 3),          # batch above the 4-bit path
+    cases = [((17, 8, 64), 3),         # batch above the 4-bit path
              ((2, 8, 48), 4),          # K not a multiple of 32
-             ((3, 8, 16416), 3),       # K over the split limit at M >= 3
+             ((1, 8, 65568), 3),       # K over the vector-ALU split limit at M = 1
+             ((2, 8, 32800), 3),       # and at M = 2
+             ((5, 8, 16416), 3),       # and from M = 3
              ((2, -1, 64), 2)]
     for (M, N, K), status in cases:
         before = sg.skinny_gemm_get_counters()
@@ -118,7 +122,8 @@ def test_mxfp4_empty_and_rejected():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 8192, 7168), (2, 8192, 7168), (4, 4096, 7168),
-                                   (8, 4096, 7168), (1, 7168, 8192), (8, 7168, 8192)])
+                                   (8, 4096, 7168), (16, 4096, 7168), (1, 7168, 8192),
+                                   (8, 7168, 8192), (16, 7168, 8192)])
 def test_mxfp4_full_size(M, N, K):
     # the benchmark's shapes: sampled output rows against the oracle
     announce(f"mxfp4 full M={M} N={N} K={K}")
