@@ -48,10 +48,17 @@ __device__ __forceinline__ void load_pieces(uint4 (&dst)[NCH], rsrc_t r, int nch
 constexpr int pad4(int v) { return (v + 3) / 4 * 4; }
 constexpr int block_waves(int S) { return S > kWavesPerBlock ? S : kWavesPerBlock; }
 
-template <int M, int NCH, int R, int S, bool GUARD, bool TWO_PASS>
+// XS (small-matrix path: S == 1, one chunk = all of K): the workgroup stages
+// x once in LDS (dynamic, M*K8 pieces) instead of every wave reading its own
+// copy from L2 -- measured on MI355X, those per-wave x reads cost about 1 us
+// of a 117 MB projection.  Each thread loads its share of x, the first
+// group's weight loads are queued right behind, and only the x part is
+// waited for before the LDS copy and the barrier.
+template <int M, int NCH, int R, int S, bool GUARD, bool TWO_PASS, bool XS>
 __global__ __launch_bounds__(kWave * block_waves(S)) void rowdot_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ W, int N, int K8, int splits,
     int chunk8, int iters, Epilogue ep) {
+    static_assert(!XS || (S == 1 && !TWO_PASS), "x staging: one chunk per wave");
     // Teams of S waves (S == 1 in two-pass mode, where a wave's chunk comes
     // from its global index instead).
     constexpr int kWaves = block_waves(S);
@@ -81,13 +88,48 @@ __global__ __launch_bounds__(kWave * block_waves(S)) void rowdot_kernel(
     const int nch = (len + kWave - 1) / kWave;
     const uint32_t bytes = (uint32_t)len * 16u;
 
-    uint4 xr[M][NCH];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-        load_pieces<NCH, kCached, GUARD>(xr[m], make_rsrc(x + (int64_t)m * K8 + k0, bytes), nch,
-                                         lane);
-
     const int groups = (N + R - 1) / R;
+    uint4 xr[M][NCH];
+    uint4 wr[R][NCH];
+    auto load_w = [&](int g) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int n = g * R + r;
+            const rsrc_t rs = make_rsrc(W + (int64_t)min(n, N - 1) * K8 + k0, n < N ? bytes : 0u);
+            load_pieces<NCH, kStream, GUARD>(wr[r], rs, nch, lane);
+        }
+    };
+    if constexpr (XS) {
+        extern __shared__ uint4 xs[];  // x [M, K8] pieces
+        constexpr int kThreads = kWave * kWaves;
+        constexpr int kStage = (M * NCH + kWaves - 1) / kWaves;  // >= M*K8 / kThreads
+        const int total = M * K8;
+        const rsrc_t rx = make_rsrc(x, (uint32_t)total * 16u);
+        uint4 stage[kStage];
+#pragma unroll
+        for (int j = 0; j < kStage; ++j)
+            stage[j] = load16<kCached>(rx, (uint32_t)(threadIdx.x + j * kThreads) * 16u);
+        if (team < groups) load_w(team);  // the first iteration's rows, behind x
+#pragma unroll
+        for (int j = 0; j < kStage; ++j) {
+            const int i = threadIdx.x + j * kThreads;
+            if (i < total) xs[i] = stage[j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int p = c * kWave + lane;
+                xr[m][c] = p < K8 ? xs[m * K8 + p] : make_uint4(0, 0, 0, 0);
+            }
+    } else {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            load_pieces<NCH, kCached, GUARD>(xr[m], make_rsrc(x + (int64_t)m * K8 + k0, bytes),
+                                             nch, lane);
+    }
+
     // Every wave of a block runs the same number of iterations (the team
     // barrier below needs it); a group past the end contributes nothing.
     for (int it = 0; it < iters; ++it) {
@@ -97,14 +139,7 @@ __global__ __launch_bounds__(kWave * block_waves(S)) void rowdot_kernel(
 #pragma unroll
         for (int v = 0; v < V; ++v) acc[v] = 0.0f;
         if (g < groups) {
-            uint4 wr[R][NCH];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int n = n0 + r;
-                const rsrc_t rs =
-                    make_rsrc(W + (int64_t)min(n, N - 1) * K8 + k0, n < N ? bytes : 0u);
-                load_pieces<NCH, kStream, GUARD>(wr[r], rs, nch, lane);
-            }
+            if (!XS || it > 0) load_w(g);
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -191,7 +226,7 @@ int rowdot_grid(int M, int N, int K, int S, int k_chunk, bool two_pass) {
     return (teams + teams_per_block - 1) / teams_per_block;
 }
 
-template <int M, int NCH, int S, bool GUARD>
+template <int M, int NCH, int S, bool GUARD, bool XS = false>
 static hipError_t launch_mns(int N, int K, int splits, int k_chunk, int grid, bool two_pass,
                              const void* x, const void* W, const Epilogue& ep,
                              hipStream_t stream) {
@@ -204,13 +239,14 @@ static hipError_t launch_mns(int N, int K, int splits, int k_chunk, int grid, bo
     if (two_pass) {
         const int teams = (grid * kWavesPerBlock) / splits;
         const int iters = (groups + teams - 1) / teams;
-        rowdot_kernel<M, NCH, R, 1, GUARD, true><<<grid, kWave * kWavesPerBlock, 0, stream>>>(
-            xp, wp, N, K8, splits, chunk8, iters, ep);
+        rowdot_kernel<M, NCH, R, 1, GUARD, true, false>
+            <<<grid, kWave * kWavesPerBlock, 0, stream>>>(xp, wp, N, K8, splits, chunk8, iters, ep);
     } else {
         const int teams = grid * (block_waves(S) / S);
         const int iters = (groups + teams - 1) / teams;
-        rowdot_kernel<M, NCH, R, S, GUARD, false><<<grid, kWave * block_waves(S), 0, stream>>>(
-            xp, wp, N, K8, S, chunk8, iters, ep);
+        const size_t lds = XS ? (size_t)M * K8 * 16 : 0;  // staged x
+        rowdot_kernel<M, NCH, R, S, GUARD, false, XS>
+            <<<grid, kWave * block_waves(S), lds, stream>>>(xp, wp, N, K8, S, chunk8, iters, ep);
     }
     return hipGetLastError();
 }
@@ -248,7 +284,7 @@ static hipError_t launch_m(int nch, int N, int K, int S, int k_chunk, int grid, 
         if (!two_pass && S == 1) {
             switch (nch < 1 ? 1 : nch) {
 #define SG_NCH(c) \
-    case c: return launch_mns<M, c, 1, false>(N, K, 1, k_chunk, grid, false, x, W, ep, stream);
+    case c: return launch_mns<M, c, 1, false, true>(N, K, 1, k_chunk, grid, false, x, W, ep, stream);
                 SG_NCH(1) SG_NCH(2) SG_NCH(3) SG_NCH(4) SG_NCH(5) SG_NCH(6) SG_NCH(7) SG_NCH(8)
                 SG_NCH(9) SG_NCH(10) SG_NCH(11) SG_NCH(12) SG_NCH(13) SG_NCH(14) SG_NCH(15)
                 SG_NCH(16)
