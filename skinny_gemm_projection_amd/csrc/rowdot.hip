@@ -48,17 +48,17 @@ __device__ __forceinline__ void load_pieces(uint4 (&dst)[NCH], rsrc_t r, int nch
 constexpr int pad4(int v) { return (v + 3) / 4 * 4; }
 constexpr int block_waves(int S) { return S > kWavesPerBlock ? S : kWavesPerBlock; }
 
-// XS (small-matrix path: S == 1, one chunk = all of K): the workgroup stages
-// x once in LDS (dynamic, M*K8 pieces) instead of every wave reading its own
-// copy from L2 -- measured on MI355X, those per-wave x reads cost about 1 us
-// of a 117 MB projection.  Each thread loads its share of x, the first
-// group's weight loads are queued right behind, and only the x part is
-// waited for before the LDS copy and the barrier.
+// XS: the workgroup stages all of x once in LDS (dynamic, M*K8 pieces)
+// instead of every wave reading its own copy from L2 -- measured on MI355X,
+// those per-wave x reads cost 1-2 us of a 59-117 MB projection.  Each thread
+// loads its share of x, the first group's weight loads are queued right
+// behind, and only the x part is waited for before the LDS copy and the
+// barrier; each wave then reads its own chunk of x from LDS.
 template <int M, int NCH, int R, int S, bool GUARD, bool TWO_PASS, bool XS>
 __global__ __launch_bounds__(kWave * block_waves(S)) void rowdot_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ W, int N, int K8, int splits,
     int chunk8, int iters, Epilogue ep) {
-    static_assert(!XS || (S == 1 && !TWO_PASS), "x staging: one chunk per wave");
+    static_assert(!XS || !TWO_PASS, "x staging: in-workgroup teams only");
     // Teams of S waves (S == 1 in two-pass mode, where a wave's chunk comes
     // from its global index instead).
     constexpr int kWaves = block_waves(S);
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kWave * block_waves(S)) void rowdot_kernel(
     if constexpr (XS) {
         extern __shared__ uint4 xs[];  // x [M, K8] pieces
         constexpr int kThreads = kWave * kWaves;
-        constexpr int kStage = (M * NCH + kWaves - 1) / kWaves;  // >= M*K8 / kThreads
+        constexpr int kStage = (M * NCH * S + kWaves - 1) / kWaves;  // >= M*K8 / kThreads
         const int total = M * K8;
         const rsrc_t rx = make_rsrc(x, (uint32_t)total * 16u);
         uint4 stage[kStage];
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kWave * block_waves(S)) void rowdot_kernel(
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 const int p = c * kWave + lane;
-                xr[m][c] = p < K8 ? xs[m * K8 + p] : make_uint4(0, 0, 0, 0);
+                xr[m][c] = p < len ? xs[m * K8 + k0 + p] : make_uint4(0, 0, 0, 0);
             }
     } else {
 #pragma unroll
@@ -258,18 +258,30 @@ constexpr bool team_split_compiled(int S) {
     return S == 1 || S == 2 || S == 4 || (S == 8 && M >= 5);
 }
 
+// Teams stage x in LDS while it fits in kStageMax (two 4-wave workgroups of
+// a CU then still fit in its 160 KB).
+constexpr size_t kStageMax = 64 * 1024;
+
+template <int M, int NCH, int S, bool GUARD>
+static hipError_t launch_team(int N, int K, int k_chunk, int grid, const void* x, const void* W,
+                              const Epilogue& ep, hipStream_t stream) {
+    if ((size_t)M * K * 2 <= kStageMax)
+        return launch_mns<M, NCH, S, GUARD, true>(N, K, S, k_chunk, grid, false, x, W, ep, stream);
+    return launch_mns<M, NCH, S, GUARD, false>(N, K, S, k_chunk, grid, false, x, W, ep, stream);
+}
+
 template <int M, int NCH, bool GUARD>
 static hipError_t launch_mn(int N, int K, int S, int k_chunk, int grid, bool two_pass,
                             const void* x, const void* W, const Epilogue& ep, hipStream_t stream) {
     if (two_pass)
         return launch_mns<M, NCH, 1, GUARD>(N, K, S, k_chunk, grid, true, x, W, ep, stream);
     switch (S) {
-        case 1: return launch_mns<M, NCH, 1, GUARD>(N, K, 1, k_chunk, grid, false, x, W, ep, stream);
-        case 2: return launch_mns<M, NCH, 2, GUARD>(N, K, 2, k_chunk, grid, false, x, W, ep, stream);
-        case 4: return launch_mns<M, NCH, 4, GUARD>(N, K, 4, k_chunk, grid, false, x, W, ep, stream);
+        case 1: return launch_team<M, NCH, 1, GUARD>(N, K, k_chunk, grid, x, W, ep, stream);
+        case 2: return launch_team<M, NCH, 2, GUARD>(N, K, k_chunk, grid, x, W, ep, stream);
+        case 4: return launch_team<M, NCH, 4, GUARD>(N, K, k_chunk, grid, x, W, ep, stream);
         case 8:
             if constexpr (team_split_compiled<M>(8))
-                return launch_mns<M, NCH, 8, GUARD>(N, K, 8, k_chunk, grid, false, x, W, ep, stream);
+                return launch_team<M, NCH, 8, GUARD>(N, K, k_chunk, grid, x, W, ep, stream);
             break;
         default: break;
     }
