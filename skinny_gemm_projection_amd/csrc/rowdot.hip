@@ -222,7 +222,12 @@ int rowdot_grid(int M, int N, int K, int S, int k_chunk, bool two_pass) {
     }
     const int teams_per_block = block_waves(S) / S;
     const int cap_teams = resident / S;
-    const int teams = groups < cap_teams ? groups : cap_teams;
+    int teams = groups < cap_teams ? groups : cap_teams;
+    // as few teams as give every team the same number of row groups: a
+    // ragged last round leaves part of the grid idle (measured: 7168 x 8192,
+    // M = 1, 20.4 -> 19.9 us)
+    const int its = (groups + teams - 1) / teams;
+    teams = (groups + its - 1) / its;
     return (teams + teams_per_block - 1) / teams_per_block;
 }
 
