@@ -18,7 +18,7 @@
  *     optimisation de Kimi K3 dans vLLM"), Partie 2 §4: routed experts, where
  *     expert selection decides which weights are read.
  * The pages give the operation, not its arithmetic; every reading taken where
- * they are silent is listed in the design doc and restated at each function.
+ * they are silent is stated at the function it governs.
  *
  * Conventions
  *   bf16 values travel as raw 16-bit patterns (uint16_t), the upper half of
