@@ -278,7 +278,10 @@ __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __res
     constexpr int OUT = MT * 4;  // accumulator floats per lane
     constexpr int RP = 16;       // pieces per row per round
     constexpr uint32_t kOff = 0xFFFFFFF0u;  // past any descriptor range: reads zero
+    // x tiles in LDS too, where the workgroup's LDS allows (all but MT = 4, S = 8)
+    constexpr bool XT = (size_t)S * (kTileSlots * 16 * (1 + MT) + OUT * kWave * 4) <= kMfmaMaxLds;
     __shared__ uint4 tiles[S][kTileSlots];
+    __shared__ uint4 xtiles[XT ? S : 1][XT ? MT : 1][XT ? kTileSlots : 1];
     __shared__ float red[S][OUT][kWave];
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -305,15 +308,24 @@ __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __res
         wrow[i] = r < rows;
         woff[i] = ((uint32_t)r * K8 + k0 + wpiece[i]) * 16u;
     }
-    // x: the A operand of step t is piece 16*rd + 4t + grp of row 16*mt + col
-    uint32_t xoff[MT];
-    bool xrow[MT];
+    // x goes the same way as the weights: load i of a round reads row
+    // 16*mt + 4i + grp of x, slot col = piece col ^ (4i + grp), into the
+    // wave's x tile; the A operand of step t (piece 4t + grp of row
+    // 16*mt + col) is then read back like the B operand.  Whole 256-byte
+    // row segments per instruction, instead of 16 rows x 64 bytes.
+    // (Without x tiles: the A operand of step t, piece 16*rd + 4t + grp of
+    // row 16*mt + col, straight from L2.)
+    uint32_t xoff[4][MT];
+    bool xrow[4][MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 16 + col;
-        xrow[mt] = m < M;
-        xoff[mt] = ((uint32_t)m * K8 + k0 + grp) * 16u;
-    }
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = XT ? mt * 16 + 4 * i + grp : mt * 16 + col;
+            const int piece = XT ? wpiece[i] : grp + 4 * i;
+            xrow[i][mt] = m < M;
+            xoff[i][mt] = ((uint32_t)m * K8 + k0 + piece) * 16u;
+        }
     auto load_round = [&](int rd, uint4 (&w)[4], uint4 (&a)[4][MT]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -321,12 +333,12 @@ __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __res
             w[i] = load16<kStream>(wrs, ok ? woff[i] + (uint32_t)rd * (RP * 16u) : kOff);
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const bool ok = xrow[mt] && (rd * RP + 4 * t + grp < len);
-                a[t][mt] = load16<kCached>(
-                    xrs, ok ? xoff[mt] + (uint32_t)(rd * RP + 4 * t) * 16u : kOff);
+                const int piece = XT ? wpiece[i] : grp + 4 * i;
+                const bool ok = xrow[i][mt] && (rd * RP + piece < len);
+                a[i][mt] = load16<kCached>(xrs, ok ? xoff[i][mt] + (uint32_t)rd * (RP * 16u) : kOff);
             }
     };
 
@@ -343,16 +355,27 @@ __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __res
             const int rd = r0 + d;
             if (rd < rounds) {  // wave-uniform
 #pragma unroll
-                for (int i = 0; i < 4; ++i) tile[(4 * i + grp) * RP + col] = wb[d][i];
+                for (int i = 0; i < 4; ++i) {
+                    tile[(4 * i + grp) * RP + col] = wb[d][i];
+                    if constexpr (XT) {
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+                            xtiles[s][mt][(4 * i + grp) * RP + col] = xb[d][i][mt];
+                    }
+                }
                 __builtin_amdgcn_wave_barrier();
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const uint4 b = tile[col * RP + ((4 * t + grp) ^ col)];
+                    const int slot = col * RP + ((4 * t + grp) ^ col);
+                    const uint4 b = tile[slot];
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const uint4 a = XT ? xtiles[XT ? s : 0][XT ? mt : 0][XT ? slot : 0]
+                                           : xb[d][t][mt];
                         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, xb[d][t][mt]),
-                            __builtin_bit_cast(bf16x8_t, b), acc[mt], 0, 0, 0);
+                            __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                            acc[mt], 0, 0, 0);
+                    }
                 }
                 __builtin_amdgcn_wave_barrier();
             }
