@@ -34,7 +34,7 @@ constexpr int kComputeUnits = 256;
 // against 13.8 us MFMA; M=12: 20.7 against 14.0), while at M <= 6 the VALU
 // kernel, which needs no second pass, is faster (M=4: 12.8 against 13.8).
 constexpr int32_t kMfmaFromM = 8;
-constexpr int32_t kTeamUpToM = 12;
+constexpr int32_t kTeamUpToM = 16;
 
 // Choices measured on MI355X for known projection shapes, overriding the
 // defaults: {M_lo, M_hi, N, K, kernel (0: default), split (0: default),
@@ -214,12 +214,12 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
             // Default: the chunk kernel, its S partials summed by the second
             // pass.  two_pass == 0 asks for the team kernel (S in 1, 2, 4, 8
             // reduced inside the workgroup).
-            // Up to 12 rows the team kernel -- no workspace, no second
-            // launch -- when its grid of N/16 workgroups fills the compute
-            // units.  It reads x from L2 once per weight byte (times the
-            // x row tiles), and on MI355X it stops paying off past M = 12
-            // (K=7168, N=4096: M=8 12.9 us against 14.1 us for the chunk
-            // kernel and its reduction, M=16 15.0 against 14.2).
+            // Up to 16 rows (one x row tile) the team kernel -- no
+            // workspace, no second launch -- when its grid of N/16
+            // workgroups fills the compute units.  Measured on MI355X with
+            // x through the per-wave LDS tile: K=7168, N=4096, M=16 13.5 us
+            // against 14.3 us for the chunk kernel and its reduction; from
+            // M=20 (two row tiles) the chunk kernel wins (16.6 against 15.4).
             const bool team_auto = two_pass < 0 && tile_n == 0 && M <= kTeamUpToM &&
                                    (N + kMfmaTeamTileN - 1) / kMfmaTeamTileN >= kComputeUnits &&
                                    (split_k <= 0 || mfma_team_split_ok(split_k));
