@@ -195,6 +195,7 @@ __global__ __launch_bounds__(kWave * S) void mxfp4_mfma_kernel(
     int M, int N, int KB, int chunk_w, Epilogue ep) {
     constexpr int D = kMfmaWindows;
     __shared__ f32x4_t red[S > 1 ? S : 1][kWave];
+    __shared__ uint4 xtiles[S][256];  // per wave: x of one window, 16 rows x 16 pieces
 
     const int lane = threadIdx.x & (kWave - 1);
     const int col = lane & 15, grp = lane >> 4;
@@ -213,6 +214,11 @@ __global__ __launch_bounds__(kWave * S) void mxfp4_mfma_kernel(
     const rsrc_t rx = make_rsrc(x, (uint32_t)M * K8 * 16u);
     constexpr uint32_t kOut = 0xFFFFFFF0u;  // past any range: reads zero
 
+    // x of a window goes through the wave's LDS tile: load i reads row
+    // 4i + grp, piece col ^ (4i + grp) of the window (4 rows x 256 bytes per
+    // instruction), into slot col of that row; the A operand of step t,
+    // piece 4*grp + t of row col, is read back from slot (4*grp + t) ^ col.
+    uint4* xt = xtiles[s];
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     bool nan_scale = false;
     for (int wb = w0; wb < w1; wb += D) {
@@ -226,12 +232,19 @@ __global__ __launch_bounds__(kWave * S) void mxfp4_mfma_kernel(
             wv[d] = load16<kStream>(rw, ok ? (uint32_t)(col * KB + b) * 16u : kOut);
             sc[d] = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? (uint32_t)(col * KB + b) : kOut,
                                                         0, kStream);
-            const uint32_t xo = ok ? (uint32_t)(col * K8 + 4 * b) * 16u : kOut;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) xa[d][t] = load16<kCached>(rx, ok ? xo + 16u * t : kOut);
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * i + grp;
+                const int piece = 16 * w + (col ^ r);  // of the x row
+                const bool xok = w < w1 && piece < K8;
+                xa[d][i] = load16<kCached>(rx, xok ? (uint32_t)(r * K8 + piece) * 16u : kOut);
+            }
         }
 #pragma unroll
         for (int d = 0; d < D; ++d) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xt[(4 * i + grp) * 16 + col] = xa[d][i];
+            __builtin_amdgcn_wave_barrier();
             nan_scale |= sc[d] == 255u;
             const float scale = as_f(sc[d] << 23);  // e8m0 code in the exponent field
             const uint32_t wd[4] = {wv[d].x, wv[d].y, wv[d].z, wv[d].w};
@@ -242,10 +255,12 @@ __global__ __launch_bounds__(kWave * S) void mxfp4_mfma_kernel(
                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[t], scale, 1)),
                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[t], scale, 2)),
                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[t], scale, 3))};
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[d][t]),
+                const uint4 a = xt[col * 16 + ((4 * grp + t) ^ col)];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                               __builtin_bit_cast(bf16x8_t, b), acc,
                                                               0, 0, 0);
             }
+            __builtin_amdgcn_wave_barrier();
         }
     }
     // a NaN scale anywhere in row col's blocks of this chunk: that row is NaN
