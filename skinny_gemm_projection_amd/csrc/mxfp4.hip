@@ -31,13 +31,16 @@
 // grp of a 128-element window of row col -- the weights of one
 // v_mfma_f32_16x16x32_bf16 B operand per step t, as dword t of that block,
 // converted in 4 instructions straight into operand layout (no LDS
-// transpose).  The matching A operand is x[m][window + 32*grp + 8*t ..+8),
-// read from L2: inside a 32-wide step the k order is free, A and B only have
-// to agree.  S waves of a workgroup split K over the tile (8 windows in
-// flight each) and add their 16x16 tiles in LDS in ascending order.
-// Measured on MI355X it trails the VALU kernel through M = 8: its x operands
-// are four 16-byte reads per 1 KB of codes, scattered over 32 cache lines
-// per instruction, so the L1/L2 request rate -- not HBM -- sets its time.
+// transpose).  The matching A operand is x[m][window + 32*grp + 8*t ..+8):
+// inside a 32-wide step the k order is free, A and B only have to agree.
+// x of each window is loaded as 4 rows x 256 bytes per instruction into a
+// swizzled per-wave LDS tile and read back in operand layout (reading the
+// operands straight from L2, 16 rows x 64 bytes per instruction, was 10-25%
+// slower).  S waves of a workgroup split K over the tile (8 windows in
+// flight each) and add their 16x16 tiles in LDS in ascending order.  Every
+// workgroup still reads all of x from L2 -- at 16 rows four x bytes per code
+// byte -- and that traffic, not HBM, bounds the kernel; through M = 8 the
+// VALU kernel is as fast or faster.
 #include "launch.h"
 
 namespace sg {
