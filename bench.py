@@ -236,6 +236,9 @@ def main_workload(torch, sg, si, L, steps, warmup, cyc):
     per_m_ms = {}
     for M in M_LIST:
         per_m_ms[M] = timed_calls(torch, [calls[(M, r)] for r in range(R)], 200, cyc)
+    graph = graph_timing(torch, sg, lambda L2, M, r: L2.projection(plans[M], x[M], ring[r], y32[M],
+                                                                    y16[M]),
+                         M_LIST, R, y32)
 
     bytes_per = {M: proj_bytes(M, N_MAIN, K_MAIN) for M in M_LIST}
     step_bytes = sum(bytes_per.values())
@@ -254,8 +257,49 @@ def main_workload(torch, sg, si, L, steps, warmup, cyc):
         "gbs_per_batch": {str(M): round(bytes_per[M] / (us[M] * 1e-6) / 1e9, 1) for M in M_LIST},
         "achieved": achieved, "avg_launch_us": 1e3 * avg_launch_ms,
         "bytes_per_launch": launch_bytes,
+        "graph": graph,
         "inputs": (x, W0),
     }
+
+
+def graph_timing(torch, sg, make_call, m_list, R, y32, per_graph=200, replays=5):
+    """Cross-check: per batch size, `per_graph` back-to-back calls cycling the weight ring
+    captured into one HIP graph on a stream of its own (the calls are built for that
+    stream); each replay timed with one event pair.  Returns the median, min and max us
+    per projection over `replays` replays, after checking that every replay leaves the
+    same outputs as an eager call."""
+    out = {}
+    gs = torch.cuda.Stream()
+    with torch.cuda.stream(gs):
+        L2 = Launcher(torch, sg)  # its launches go to gs
+    for M in m_list:
+        calls = [make_call(L2, M, r) for r in range(R)]
+        with torch.cuda.stream(gs):
+            calls[0]()
+        torch.cuda.synchronize()
+        eager = y32[M].clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            for i in range(per_graph):
+                calls[(i + 1) % R]()  # ends on copy (per_graph % R), equal to copy 0
+        times = []
+        for _ in range(replays):
+            y32[M].fill_(float("nan"))
+            torch.cuda.synchronize()
+            start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(gs):
+                start.record()
+                g.replay()
+                stop.record()
+            torch.cuda.synchronize()
+            times.append(1e3 * start.elapsed_time(stop) / per_graph)
+            if not torch.equal(y32[M], eager):
+                raise RuntimeError(f"graph replay at M={M} differs from the eager call")
+        times.sort()
+        out[str(M)] = {"median_us": round(times[len(times) // 2], 3), "min_us": round(times[0], 3),
+                       "max_us": round(times[-1], 3)}
+        del g
+    return out
 
 
 def sweep(torch, sg, si, L, cyc, reps=40):
@@ -869,6 +913,7 @@ def main() -> None:
             "parallelism": "single GPU",
         },
         "us_per_projection": res["us_per_projection"],
+        "us_per_projection_graph": res["graph"],
         "GBps_per_batch": res["gbs_per_batch"],
         "pct_of_peak": round(100.0 * res["value"] / HBM_PEAK_GBS, 1),
         "wall_ms_per_step": round(res["wall_ms_per_step"], 6),
