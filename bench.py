@@ -334,6 +334,37 @@ def sweep(torch, sg, si, L, cyc, reps=40):
         y32, y16 = torch.empty((M, N), device=dev), torch.empty((M, N), device=dev, dtype=torch.bfloat16)
         per = timed_calls(torch, [L.projection(p, x, w, y32, y16) for w in ring], reps, cyc)
         record("small-batch 8192x7168", M, N, K, plan_desc(p), per, proj_bytes(M, N, K))
+
+    # side-stream weight prefetch on the same ring: the read of one 117 MB matrix alone, and
+    # what it buys the projection after it -- prefetch then project the same matrix (its
+    # weights now in the Infinity Cache) against prefetch one matrix and project another
+    # that was last read two pairs earlier (cold).  Both pair streams run the same kernels;
+    # their difference is the cold-minus-warm projection time.
+    nbytes = N * K * 2
+    sp = L.sp
+
+    def pf(w):
+        def go():
+            st = L.c.skinny_gemm_prefetch(w.data_ptr(), nbytes, sp)
+            if st:
+                raise RuntimeError(sg.skinny_gemm_status_str(st))
+        return go
+    x = si.normal_bf16((1, K), 1.0, si.seed_for(2, si.TAG_X) + 1, dev)
+    p = sg.skinny_gemm_plan(1, N, K)
+    y32, y16 = torch.empty((1, N), device=dev), torch.empty((1, N), device=dev, dtype=torch.bfloat16)
+    proj = [L.projection(p, x, w, y32, y16) for w in ring]
+    n = len(ring)
+    alone = timed_calls(torch, [pf(w) for w in ring], reps, cyc)
+    same = timed_calls(torch, [c for i in range(n) for c in (pf(ring[i]), proj[i])], 2 * reps, cyc)
+    other = timed_calls(torch, [c for i in range(n) for c in (pf(ring[(i + 2) % n]), proj[i])],
+                        2 * reps, cyc)
+    us = 1e3 * alone
+    rows.append({"workload": "prefetch 8192x7168 (one 117 MB matrix)", "M": 1, "N": N, "K": K,
+                 "plan": "prefetch", "us": round(us, 3),
+                 "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                 "pct_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+                 "projection_after_prefetch_us": round(2e3 * same - us, 3),
+                 "projection_cold_us": round(2e3 * other - us, 3)})
     del ring
 
     # split-K sweep M in {4..64}, K=7168, N=4096, fp32 out

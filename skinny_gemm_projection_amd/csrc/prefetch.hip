@@ -20,24 +20,35 @@ namespace sg {
 
 namespace {
 
+// Each wave reads kPrefetchUnroll consecutive 1 KB blocks per step (64 lanes
+// x 16 bytes, one buffer load each), the waves striding over the range.
+// Measured on MI355X over a 117 MB matrix: 19.1 us against 23.9 us for a
+// grid-stride loop of per-thread 16-byte loads.  The loads use the default
+// cache policy: with the non-temporal hint the data does not stay in the
+// Infinity Cache (the following projection ran no faster than on a cold
+// matrix), and warming that cache is the point.
 constexpr int kPrefetchUnroll = 8;
+constexpr uint32_t kPrefetchSpan = kPrefetchUnroll * kWave * 16;  // bytes per wave step
+constexpr int kPrefetchGrid = 1024;                                 // 256 CUs x 4 workgroups
 
-__global__ __launch_bounds__(kBlock) void prefetch_kernel(const uint4* __restrict__ src,
-                                                          int64_t n16, int never,
+__global__ __launch_bounds__(kBlock) void prefetch_kernel(const uint8_t* __restrict__ src,
+                                                          uint64_t bytes, int never,
                                                           uint32_t* __restrict__ sink) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t wave = (uint64_t)blockIdx.x * kWavesPerBlock + wave_id_in_block();
+    const uint64_t waves = (uint64_t)gridDim.x * kWavesPerBlock;
     uint32_t fold = 0;
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    for (; i + (kPrefetchUnroll - 1) * stride < n16; i += kPrefetchUnroll * stride) {
+    for (uint64_t base = wave * kPrefetchSpan; base < bytes; base += waves * kPrefetchSpan) {
+        // a descriptor per step keeps every offset 32-bit for any range size;
+        // loads past the step's end (the range's last partial step) read zero
+        const uint64_t left = bytes - base;
+        const rsrc_t r = make_rsrc(src + base, (uint32_t)(left < kPrefetchSpan ? left : kPrefetchSpan));
         uint4 v[kPrefetchUnroll];
 #pragma unroll
-        for (int u = 0; u < kPrefetchUnroll; ++u) v[u] = src[i + u * stride];
+        for (int u = 0; u < kPrefetchUnroll; ++u)
+            v[u] = load16<kCached>(r, (uint32_t)(u * kWave + lane) * 16u);
 #pragma unroll
         for (int u = 0; u < kPrefetchUnroll; ++u) fold ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-    }
-    for (; i < n16; i += stride) {
-        const uint4 v = src[i];
-        fold ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     if (never) sink[(int64_t)blockIdx.x * kBlock + threadIdx.x] = fold;
 }
@@ -45,13 +56,12 @@ __global__ __launch_bounds__(kBlock) void prefetch_kernel(const uint4* __restric
 }  // namespace
 
 hipError_t launch_prefetch(const void* W, size_t bytes, hipStream_t stream) {
-    const int64_t n16 = (int64_t)(bytes / 16);
-    if (n16 == 0) return hipSuccess;
-    const int64_t per_block = (int64_t)kBlock * kPrefetchUnroll;
-    int64_t grid = (n16 + per_block - 1) / per_block;
-    if (grid > 1024) grid = 1024;  // 256 CUs x 4 workgroups
-    prefetch_kernel<<<(unsigned)grid, kBlock, 0, stream>>>(static_cast<const uint4*>(W), n16, 0,
-                                                           nullptr);
+    if (bytes == 0) return hipSuccess;
+    const uint64_t steps = (bytes + kPrefetchSpan - 1) / kPrefetchSpan;
+    const uint64_t blocks = (steps + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int grid = blocks < (uint64_t)kPrefetchGrid ? (int)blocks : kPrefetchGrid;
+    prefetch_kernel<<<grid, kBlock, 0, stream>>>(static_cast<const uint8_t*>(W), (uint64_t)bytes,
+                                                 0, nullptr);
     return hipGetLastError();
 }
 

@@ -65,6 +65,13 @@ __global__ __launch_bounds__(kWave * block_waves(S)) void rowdot_kernel(
     constexpr int kTeams = kWaves / S;
     constexpr int V = pad4(R * M);
     __shared__ float red[2][kTeams][S][V];
+    // From M = 6 up the rows of the next group are requested as soon as the
+    // dot products have consumed this group's registers -- before the lane
+    // reduction and the team barrier -- so the wave keeps weight loads in
+    // flight across the iteration boundary.  Measured on MI355X at K=7168,
+    // N=4096: M=6 13.3 -> 12.9 us, M=7 14.2 -> 13.5 us; at M <= 5 and on the
+    // unsplit M <= 2 kernels it was neutral or slower (M=5 12.0 -> 12.4 us).
+    constexpr bool kPipe = M >= 6;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wib = wave_id_in_block();
@@ -128,6 +135,7 @@ __global__ __launch_bounds__(kWave * block_waves(S)) void rowdot_kernel(
         for (int m = 0; m < M; ++m)
             load_pieces<NCH, kCached, GUARD>(xr[m], make_rsrc(x + (int64_t)m * K8 + k0, bytes),
                                              nch, lane);
+        if (kPipe && team < groups) load_w(team);
     }
 
     // Every wave of a block runs the same number of iterations (the team
@@ -139,7 +147,7 @@ __global__ __launch_bounds__(kWave * block_waves(S)) void rowdot_kernel(
 #pragma unroll
         for (int v = 0; v < V; ++v) acc[v] = 0.0f;
         if (g < groups) {
-            if (!XS || it > 0) load_w(g);
+            if (!kPipe && (!XS || it > 0)) load_w(g);
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -150,6 +158,7 @@ __global__ __launch_bounds__(kWave * block_waves(S)) void rowdot_kernel(
                     acc[r * M + m] = a;
                 }
         }
+        if (kPipe && it + 1 < iters && g + teams < groups) load_w(g + teams);
         const float total = reduce_scatter<V>(acc, lane);
         const int v = scatter_index<V>(lane);
         const bool mine = v >= 0 && v < R * M;
@@ -207,7 +216,9 @@ int rowdot_block_threads(int S, bool two_pass) {
     return kWave * (two_pass ? kWavesPerBlock : block_waves(S));
 }
 
-int rowdot_resident_waves(int, int) { return 2048; }  // 256 CUs x 8 waves
+// 256 CUs x 8 waves.  Measured on MI355X: twice as many (a second round of
+// workgroups) was slower on every shape (7168 x 8192, M=2: 18.9 -> 20.0 us).
+int rowdot_resident_waves(int, int) { return 2048; }
 
 int rowdot_grid(int M, int N, int K, int S, int k_chunk, bool two_pass) {
     (void)K;

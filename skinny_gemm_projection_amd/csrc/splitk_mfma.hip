@@ -424,7 +424,9 @@ hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void*
     const uint4* xp = static_cast<const uint4*>(x);
     const uint4* wp = static_cast<const uint4*>(W);
     const int MT = (M + 15) / 16;
-    constexpr int DR = 2;  // rounds in flight per wave
+    // rounds in flight per wave; measured on MI355X, 3 or 4 were slower (K=7168,
+    // N=4096, M=8: 12.4 us at 2, 14.4 at 3, 15.0 at 4)
+    constexpr int DR = 2;
 #define SG_TEAM(mt, sp) \
     if (MT == mt && S == sp) { \
         mfma_team_kernel<mt, sp, DR><<<grid, kWave * sp, 0, stream>>>(xp, wp, M, N, K8, chunk8, ep); \
@@ -487,7 +489,9 @@ hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk, int tile_
     const int phase = chunk_phase(M, k_chunk, tile_n);
     const size_t lds = mfma_chunk_lds_bytes(M, k_chunk, tile_n);
     if (phase == 0 || lds > kMfmaMaxLds) return hipErrorInvalidValue;
-    constexpr int DR = 2;  // weight rounds in flight per wave (8 loads)
+    // weight rounds in flight per wave (8 loads); 3 or 4 measured slower on
+    // MI355X (K=7168, N=4096, M=64: 18.5 us at 2, 18.8 at 3, 19.6 at 4)
+    constexpr int DR = 2;
     const int whole = (chunk8 + 16 / NT - 1) / (16 / NT) * (16 / NT);
     const bool phased = phase < whole;
 #define SG_CHUNK(mt, nt, ph) \
