@@ -41,11 +41,12 @@ hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void*
                             const void* W, const Epilogue& ep, hipStream_t stream);
 // Chunk kernel: workgroups of tile_n rows (128: 16 per wave, or 256: 32 per
 // wave sharing each x operand load) x one K chunk, the x chunk staged in LDS;
-// partials to ep.partial ([S, M, N]) for the reduction kernel when S > 1;
-// grid (mfma_grid_tiles(N, tile_n), S).
+// partials to ep.partial ([S, N, mfma_partial_rows(M)], rows m >= M zero) for
+// the reduction kernel when S > 1; grid (mfma_grid_tiles(N, tile_n), S).
 constexpr int kMfmaTileN = 128;  // W rows per workgroup with 16 rows per wave
 constexpr size_t kMfmaMaxLds = 160 * 1024;
 constexpr int kXcds = 8;         // MI355X: 8 XCDs, each with its own L2
+inline int mfma_partial_rows(int M) { return 16 * ((M + 15) / 16); }
 size_t mfma_chunk_lds_bytes(int M, int k_chunk, int tile_n);
 // Column tiles of the chunk kernel's grid: ceil(N/tile_n) padded to a
 // multiple of kXcds (the padding workgroups exit at once).
@@ -58,9 +59,9 @@ hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk, int tile_
 // ascending, fp32), then the final epilogue.
 hipError_t launch_reduce(const float* P, int S, int64_t MN, const Epilogue& ep,
                          hipStream_t stream);
-// The same sum for partials made by the chunk kernel: one workgroup per
-// (column tile, block of rows of M), laid out so it runs on the XCD that
-// wrote the tile's partials.
+// The same sum for partials made by the chunk kernel ([S, N, Mp] layout):
+// one workgroup per (column tile, 16-column slice), laid out so it runs on the
+// XCD that wrote the tile's partials.
 hipError_t launch_reduce_tiles(const float* P, int S, int M, int N, int tile_n,
                                const Epilogue& ep, hipStream_t stream);
 

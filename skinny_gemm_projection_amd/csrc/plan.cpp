@@ -257,8 +257,12 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
     p.kernel = kernel;
     p.split_k = split_k;
     p.two_pass = two_pass;
+    // chunk-kernel partials are [S, N, M padded to whole 16-row tiles]; the
+    // vector-ALU kernel's are [S, M, N]
+    const bool chunk = kernel == SG_KERNEL_SPLITK_MFMA && p.tile_n >= kMfmaTileN;
+    const size_t rows = chunk ? (size_t)mfma_partial_rows(M) : (size_t)M;
     p.workspace_bytes =
-        two_pass ? ((size_t)split_k * M * N * sizeof(float) + 255) / 256 * 256 : 0;
+        two_pass ? ((size_t)split_k * rows * N * sizeof(float) + 255) / 256 * 256 : 0;
     *out = p;
     return SG_OK;
 }

@@ -61,70 +61,62 @@ __global__ __launch_bounds__(kBlock) void splitk_reduce_kernel(const float* __re
         if (i0 + j < MN) store_final(ep, i0 + j, acc[j]);
 }
 
-// Tiled form: blockIdx.x is the chunk kernel's column tile (tile_n outputs
-// of a row), blockIdx.y a block of rows; each thread owns 4 consecutive
-// columns of one row.  The grid's x extent is the chunk kernel's (padded to a
-// multiple of 8), so linear workgroup ids -- and with them XCDs -- match those
-// of the workgroups that wrote the tile.
+// Tiled form for the chunk kernel's partials, laid out [S, N, MP] (MP = 16 *
+// ceil(M/16); rows m >= M are zeros).  blockIdx.x is the chunk kernel's
+// column tile and the grid's x extent is the chunk kernel's (padded to a
+// multiple of 8), so linear workgroup ids -- and with them XCDs -- match
+// those of the workgroups that wrote the tile; blockIdx.y picks a slice of
+// kRedCols columns of the tile.  Thread (c, q) of a workgroup owns the four
+// rows 4q..4q+3 of column c: it loads that float4 of every split -- all S
+// issued before any is added (batches of 16) -- adds them in ascending s and
+// writes the four outputs; consecutive lanes take consecutive columns, so
+// each store instruction covers whole runs of a row of y.
+constexpr int kRedCols = 16;  // 256 workgroups at N = 4096 with 128-row tiles
+
 __global__ __launch_bounds__(kBlock) void splitk_reduce_tiles_kernel(const float* __restrict__ P,
-                                                                     int S, int M, int N,
+                                                                     int S, int M, int MP, int N,
                                                                      int tile_n, Epilogue ep) {
     constexpr int kBatch = 16;
-    const int per_row = tile_n / 4;  // threads per row of the tile
-    const int m = blockIdx.y * (kBlock / per_row) + threadIdx.x / per_row;
-    const int n0 = blockIdx.x * tile_n + (threadIdx.x % per_row) * 4;
-    if (m >= M || n0 >= N) return;
-    const int64_t plane = (int64_t)M * N;
-    const int64_t i0 = (int64_t)m * N + n0;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if ((N & 3) == 0) {  // n0 + 3 < N and 16-byte aligned
-        for (int s0 = 0; s0 < S; s0 += kBatch) {
-            float4 part[kBatch];
+    const int c = threadIdx.x % kRedCols;
+    const int q = threadIdx.x / kRedCols;  // float4 of the column
+    const int n = blockIdx.x * tile_n + blockIdx.y * kRedCols + c;
+    if (n >= N || 4 * q >= M) return;
+    const int64_t plane4 = (int64_t)N * (MP / 4);
+    const float4* src = reinterpret_cast<const float4*>(P) + (int64_t)n * (MP / 4) + q;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int s0 = 0; s0 < S; s0 += kBatch) {
+        float4 part[kBatch];
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j)
-                if (s0 + j < S) part[j] = reinterpret_cast<const float4*>(P + (s0 + j) * plane + i0)[0];
+        for (int j = 0; j < kBatch; ++j)
+            if (s0 + j < S) part[j] = src[(s0 + j) * plane4];
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                if (s0 + j < S) {
-                    if (s0 + j == 0) {
-                        acc[0] = part[j].x;
-                        acc[1] = part[j].y;
-                        acc[2] = part[j].z;
-                        acc[3] = part[j].w;
-                    } else {
-                        acc[0] += part[j].x;
-                        acc[1] += part[j].y;
-                        acc[2] += part[j].z;
-                        acc[3] += part[j].w;
-                    }
+        for (int j = 0; j < kBatch; ++j) {
+            if (s0 + j < S) {
+                if (s0 + j == 0) {
+                    acc = part[j];
+                } else {
+                    acc.x += part[j].x;
+                    acc.y += part[j].y;
+                    acc.z += part[j].z;
+                    acc.w += part[j].w;
                 }
             }
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float a = 0.0f;
-            if (n0 + j < N) {
-                a = P[i0 + j];
-                for (int s = 1; s < S; ++s) a += P[s * plane + i0 + j];
-            }
-            acc[j] = a;
-        }
     }
+    const float v[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        if (n0 + j < N) store_final(ep, i0 + j, acc[j]);
+    for (int i = 0; i < 4; ++i)
+        if (4 * q + i < M) store_final(ep, (int64_t)(4 * q + i) * N + n, v[i]);
 }
 
 }  // namespace
 
 hipError_t launch_reduce_tiles(const float* P, int S, int M, int N, int tile_n,
                                const Epilogue& ep, hipStream_t stream) {
-    if (tile_n % 4 != 0 || tile_n / 4 > kBlock || kBlock % (tile_n / 4) != 0)
-        return hipErrorInvalidValue;
-    const int rows_per_block = kBlock / (tile_n / 4);
-    const dim3 grid(mfma_grid_tiles(N, tile_n), (M + rows_per_block - 1) / rows_per_block);
-    splitk_reduce_tiles_kernel<<<grid, kBlock, 0, stream>>>(P, S, M, N, tile_n, ep);
+    const int MP = mfma_partial_rows(M);
+    if (tile_n % kRedCols != 0 || kRedCols * (MP / 4) > kBlock) return hipErrorInvalidValue;
+    const dim3 grid(mfma_grid_tiles(N, tile_n), tile_n / kRedCols);
+    splitk_reduce_tiles_kernel<<<grid, kBlock, 0, stream>>>(P, S, M, MP, N, tile_n, ep);
     return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@
 //    it back in operand layout.  Slot c of row r in the tile holds piece
 //    c ^ swz(r) (an XOR swizzle), so the operand read -- 16 different rows
 //    at one piece each -- hits 16 different bank groups.  Partials go to the
-//    [S, M, N] workspace and the deterministic reduction kernel adds them
+//    [S, N, 16*ceil(M/16)] workspace and the deterministic reduction kernel adds them
 //    (two-pass split-K).  The grid's column-tile count is padded to a
 //    multiple of the 8 XCDs: workgroups are dispatched to XCDs round-robin
 //    by linear id, so all S splits of a column tile run on one XCD and the
@@ -239,6 +239,22 @@ __global__ __launch_bounds__(kChunkThreads) void splitk_mfma_kernel(
         }
     }
 
+    if (ep.partial) {
+        // Partials as [S, N, 16*MT]: the 4 consecutive m a lane holds leave as
+        // one 16-byte store (rows m >= M carry the zeros of the padded x).
+        // Measured on MI355X against 4-byte stores into [S, M, N]: K=7168,
+        // N=4096, M=64 15.9 -> 15.2 us for this kernel.
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int r = 16 * nt + col;
+            if (r >= rows) continue;
+            f32x4_t* dst = reinterpret_cast<f32x4_t*>(
+                ep.partial + ((int64_t)s * N + row0 + r) * XROWS + grp * 4);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) dst[mt * 4] = acc[nt][mt];
+        }
+        return;
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int r = 16 * nt + col;
@@ -249,12 +265,7 @@ __global__ __launch_bounds__(kChunkThreads) void splitk_mfma_kernel(
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int m = mt * 16 + grp * 4 + v;
-                if (m < M) {
-                    if (ep.partial)
-                        ep.partial[((int64_t)s * M + m) * N + n] = acc[nt][mt][v];
-                    else
-                        store_final(ep, (int64_t)m * N + n, acc[nt][mt][v]);
-                }
+                if (m < M) store_final(ep, (int64_t)m * N + n, acc[nt][mt][v]);
             }
         }
     }
