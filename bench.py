@@ -710,6 +710,14 @@ def profile_workloads(torch, sg, si, L, manifest_path, reps=3):
         run(label, M, N, K, desc(p), calls, proj_bytes(M, N, K, **kind))
         del ring, W0
         torch.cuda.empty_cache()
+    # side-stream prefetch of one 117 MB matrix
+    N, K = 8192, 7168
+    W0 = si.normal_bf16((N, K), 0.02, 11, dev)
+    ring = [W0] + [W0.clone() for _ in range(reps - 1)]
+    run("prefetch 8192x7168", 1, N, K, "prefetch",
+        [(lambda w=w: sg.skinny_gemm_prefetch(w)) for w in ring], N * K * 2)
+    del ring, W0
+    torch.cuda.empty_cache()
     E, N, K, topk = 384, 2048, 7168, 8
     W = si.normal_bf16((E, N, K), 0.02, 14, dev)
     for T in (1, 16, 64):
