@@ -133,8 +133,10 @@ sg_status skinny_gemm_plan_force(int32_t M, int32_t N, int32_t K, int32_t kernel
 /* y = x W^T ([P] Method details §1).  Writes y_f32 [M,N] (fp32) and/or
  * y_bf16 [M,N] (the same fp32 value rounded to nearest even); at least one
  * must be non-NULL.  workspace: at least plan->workspace_bytes bytes, may be
- * NULL when that is 0; in two-pass plans the split-K partial sums P[S,M,N]
- * (fp32) occupy its first S*M*N*4 bytes.  Split partials are always added
+ * NULL when that is 0; in two-pass plans the fp32 split-K partial sums
+ * occupy its first bytes: P[S,M,N] for the vector-ALU kernel, P[S,N,Mp]
+ * (Mp = 16*ceil(M/16), rows m >= M zero) for the matrix-core chunk kernel
+ * (tile_n 128 or 256).  Split partials are always added
  * in ascending split order in fp32, without atomics: repeated calls give
  * identical bits.  Output buffers must not overlap the inputs. */
 sg_status skinny_gemm(const sg_plan* plan, const sg_bf16* x, const sg_bf16* W,
@@ -164,6 +166,10 @@ size_t grouped_skinny_gemm_workspace(int32_t T, int32_t E, int32_t topk, int32_t
  *                         ascending p inside a group, -1 after the last;
  *   invalid_count [1]:    pairs whose id is outside [0, E) -- their
  *                         out rows are zero-filled.
+ * With all three NULL and T*topk <= 512 the call is one launch that builds
+ * the table it needs in each workgroup (no table kernel; the workspace is
+ * not touched); otherwise a table kernel runs first.  Both give the same
+ * output bits.
  * Limits: 0 <= T <= 256, 1 <= topk <= 32, T*topk <= 4096, 1 <= E <= 4096,
  * 0 <= N <= 1<<20, 0 <= K <= 8192 (else SG_ERR_SHAPE). */
 sg_status grouped_skinny_gemm(const sg_bf16* x, int32_t T, const sg_bf16* W, int32_t E,

@@ -173,6 +173,21 @@ sg_status grouped_skinny_gemm(const sg_bf16* x, int32_t T, const sg_bf16* W, int
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
+    // No table output asked for and a small table: one fused launch builds
+    // what it needs of the table in each workgroup.
+    const bool fused = !expert_offsets && !sorted_pairs && !invalid_count &&
+                       T * topk <= sg::kFusedMaxPairs && E <= sg::kFusedMaxExperts;
+    if (fused) {
+        if (T > 0 && N > 0) {
+            if (sg::launch_grouped_fused(x, T, W, topk_ids, E, N, K, topk, out, s) != hipSuccess)
+                return SG_ERR_HIP;
+            count(SG_KERNEL_GROUPED);
+        }
+        if (log_enabled())
+            std::fprintf(stderr, "[skinny_gemm] grouped (fused table) T=%d topk=%d E=%d N=%d K=%d\n",
+                         T, topk, E, N, K);
+        return SG_OK;
+    }
     const sg::GroupedWorkspace g = sg::grouped_workspace_layout(workspace, E, T * topk);
     if (sg::launch_moe_table(topk_ids, T, topk, E, N, g, expert_offsets, sorted_pairs,
                              invalid_count, out, s) != hipSuccess)

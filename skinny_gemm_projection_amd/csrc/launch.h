@@ -85,6 +85,13 @@ hipError_t launch_moe_table(const int32_t* ids, int T, int topk, int E, int N,
 
 constexpr int kGroupedRowsPerWave = 8;  // even: rows go two at a time
 constexpr int kGroupedTileN = kGroupedRowsPerWave * kWavesPerBlock;  // 32 rows per item
+// Fused table + grouped projection for small tables when no table output is
+// asked for: P = T * topk <= kFusedMaxPairs, E <= kFusedMaxExperts (LDS:
+// (P + 2E) ints per workgroup).
+constexpr int kFusedMaxPairs = 512;
+constexpr int kFusedMaxExperts = 4096;
+hipError_t launch_grouped_fused(const void* x, int T, const void* W, const int32_t* ids, int E,
+                                int N, int K, int topk, float* out, hipStream_t stream);
 hipError_t launch_grouped(const void* x, int T, const void* W, int E, int N, int K, int topk,
                           const GroupedWorkspace& g, float* out, hipStream_t stream);
 

@@ -253,6 +253,124 @@ __global__ __launch_bounds__(kBlock) void grouped_kernel(const uint4* __restrict
     }
 }
 
+// Fused form for small routing tables (P = T * topk <= kFusedMaxPairs), used
+// when the caller asks for none of the table outputs: every workgroup builds
+// the part of the table it needs in LDS -- the ascending list of active
+// experts, from the ids -- and each wave finds an expert's pairs, in
+// ascending p, with ballots over the ids.  This drops the table kernel's
+// launch and the grouped kernel's chain of dependent reads of its output
+// (one token: 8 experts, 235 MB, the table alone was about 4 us under the
+// profiler).  Work items, per-(pair, row) arithmetic and outputs are those
+// of grouped_kernel; output rows of ids outside [0, E) are zero-filled here.
+template <int NCH>
+__global__ __launch_bounds__(kBlock) void grouped_fused_kernel(
+    const uint4* __restrict__ x, const uint4* __restrict__ W, const int32_t* __restrict__ ids,
+    int P, int E, int N, int K8, int topk, int tiles, float* __restrict__ out) {
+    extern __shared__ int32_t lds_i[];
+    int32_t* s_ids = lds_i;          // [P]
+    int32_t* s_flag = s_ids + P;     // [E]: expert e has a pair
+    int32_t* s_active = s_flag + E;  // [E]: active experts, ascending
+    __shared__ int32_t s_wave[kWavesPerBlock];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wv = wave_id_in_block();
+
+    for (int p = tid; p < P; p += kBlock) s_ids[p] = ids[p];
+    for (int e = tid; e < E; e += kBlock) s_flag[e] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += kBlock) {
+        const int e = s_ids[p];
+        if (e >= 0 && e < E) s_flag[e] = 1;  // every writer stores the same value
+    }
+    __syncthreads();
+    // thread t scans experts [t * per, (t + 1) * per)
+    const int per = (E + kBlock - 1) / kBlock;
+    const int e0 = tid * per;
+    int mine = 0;
+    for (int j = 0; j < per; ++j) mine += (e0 + j < E) ? s_flag[e0 + j] : 0;
+    const int incl = wave_inclusive_scan(mine);
+    if (lane == kWave - 1) s_wave[wv] = incl;
+    __syncthreads();
+    int base = 0, num_active = 0;
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        base += w < wv ? s_wave[w] : 0;
+        num_active += s_wave[w];
+    }
+    int pos = base + incl - mine;
+    for (int j = 0; j < per; ++j)
+        if (e0 + j < E && s_flag[e0 + j]) s_active[pos++] = e0 + j;
+    __syncthreads();
+
+    // zero-fill the output rows of out-of-range ids, spread over the workgroups
+    for (int p = blockIdx.x; p < P; p += gridDim.x) {
+        const int e = s_ids[p];
+        if (e < 0 || e >= E)
+            for (int n = tid; n < N; n += kBlock) out[(int64_t)p * N + n] = 0.0f;
+    }
+
+    const int items = num_active * tiles;
+    const int v = scatter_index<4>(lane);  // this lane's row (0 or 1) of the sums, or -1/2/3
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int e = s_active[item / tiles];
+        const int tile = item - (item / tiles) * tiles;
+        const uint4* __restrict__ We = W + (int64_t)e * N * K8;
+        const int nbase = tile * kGroupedTileN + wv * kGroupedRowsPerWave;
+        // this expert's pairs: count them, and the first (ascending p)
+        int cnt = 0, first = -1;
+        for (int b = 0; b < P; b += kWave) {
+            const uint64_t m = __ballot(b + lane < P && s_ids[b + lane] == e);
+            if (first < 0 && m) first = b + __builtin_ctzll(m);
+            cnt += __popcll(m);
+        }
+
+        uint4 xa[NCH], w0[NCH], w1[NCH];
+        auto load_w = [&](uint4 (&dst)[NCH], int n) {
+            const bool ok = n < N;
+            load_row<NCH, kStream>(dst, We + (int64_t)(ok ? n : 0) * K8, ok ? K8 : 0, lane);
+        };
+        auto load_x = [&](int p) {
+            load_row<NCH, kCached>(xa, x + (int64_t)(p / topk) * K8, K8, lane);
+        };
+        auto finish = [&](int n, int p) {
+            float acc[4] = {dot_row<NCH>(xa, w0), dot_row<NCH>(xa, w1), 0.0f, 0.0f};
+            const float total = reduce_scatter<4>(acc, lane);
+            if (v == 0 || v == 1) {
+                const int row = n + v;
+                if (row < N) out[(int64_t)p * N + row] = total;
+            }
+        };
+        if (cnt == 1) {
+            load_x(first);
+#pragma unroll 1
+            for (int i = 0; i < kGroupedRowsPerWave; i += 2) {
+                const int n = nbase + i;
+                if (n >= N) break;
+                load_w(w0, n);
+                load_w(w1, n + 1);
+                finish(n, first);
+            }
+        } else {
+#pragma unroll 1
+            for (int i = 0; i < kGroupedRowsPerWave; i += 2) {
+                const int n = nbase + i;
+                if (n >= N) break;
+                load_w(w0, n);
+                load_w(w1, n + 1);
+#pragma unroll 1
+                for (int b = 0; b < P; b += kWave) {
+                    uint64_t m = __ballot(b + lane < P && s_ids[b + lane] == e);
+                    while (m) {
+                        const int p = b + __builtin_ctzll(m);
+                        m &= m - 1;
+                        load_x(p);
+                        finish(n, p);
+                    }
+                }
+            }
+        }
+    }
+}
+
 int next_pow2(int v) {
     int p = 1;
     while (p < v) p <<= 1;
@@ -284,6 +402,33 @@ hipError_t launch_moe_table(const int32_t* ids, int T, int topk, int E, int N,
                             hipStream_t stream) {
     moe_table_kernel<<<1, kTableThreads, 0, stream>>>(ids, T * topk, E, N, g, user_offsets,
                                                       user_sorted, user_invalid, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_fused(const void* x, int T, const void* W, const int32_t* ids, int E,
+                                int N, int K, int topk, float* out, hipStream_t stream) {
+    const int P = T * topk;
+    const int K8 = K / kPiece;
+    const int tiles = (N + kGroupedTileN - 1) / kGroupedTileN;
+    const int max_active = E < P ? E : P;
+    const int64_t max_items = (int64_t)max_active * tiles;
+    const int resident = 512;  // 256 CUs x 2 workgroups
+    int grid = (int)(max_items < resident ? max_items : resident);
+    if (grid < 1) grid = 1;  // still zero-fills the rows of invalid ids
+    const size_t lds = (size_t)(P + 2 * E) * sizeof(int32_t);
+    const uint4* xp = static_cast<const uint4*>(x);
+    const uint4* wp = static_cast<const uint4*>(W);
+    const int nch = (K + kLaneSpan - 1) / kLaneSpan;
+    switch (next_pow2(nch < 1 ? 1 : nch)) {
+#define SG_FUSED(c) \
+    case c: \
+        grouped_fused_kernel<c><<<grid, kBlock, lds, stream>>>(xp, wp, ids, P, E, N, K8, topk, \
+                                                              tiles, out); \
+        break;
+        SG_FUSED(1) SG_FUSED(2) SG_FUSED(4) SG_FUSED(8) SG_FUSED(16)
+#undef SG_FUSED
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

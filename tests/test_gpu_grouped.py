@@ -69,6 +69,66 @@ def test_grouped_integer_bit_exact_with_crowded_expert():
             assert torch.equal(out.view(-1, N)[p], torch.zeros(N, device=DEV)), "invalid id: zero row"
 
 
+def run_grouped_fused(x, W, ids):
+    """The call without table outputs: the fused table + grouped launch (small tables)."""
+    T, topk = ids.shape
+    E, N, _ = W.shape
+    out = torch.full((T, topk, N), float("nan"), device=DEV)
+    before = sg.skinny_gemm_get_counters()
+    sg.grouped_skinny_gemm(x, W, ids.to(DEV), out)
+    torch.cuda.synchronize()
+    return out, counters_delta(before, sg.skinny_gemm_get_counters())
+
+
+@pytest.mark.parametrize("T,topk,E,N,K", [(1, 8, 384, 100, 1032), (5, 4, 24, 100, 1032),
+                                          (16, 8, 40, 33, 520), (64, 8, 384, 20, 264),
+                                          (3, 2, 7, 16, 8), (64, 8, 4096, 8, 64),
+                                          (1, 1, 1, 5, 8)])
+def test_grouped_fused_table(T, topk, E, N, K):
+    # no table outputs asked for: one launch, each workgroup building its table in LDS;
+    # outputs against the oracle and bit-identical to the table-kernel path
+    announce(f"grouped fused T={T} topk={topk} E={E} N={N} K={K}")
+    x = si.normal_bf16((T, K), 1.0, 9300 + T, DEV)
+    W = si.normal_bf16((E, N, K), 0.02, 9301 + T, DEV)
+    ids = si.routing_table(T, E, topk, 9302 + T)
+    out, d = run_grouped_fused(x, W, ids)
+    assert d[sg.SG_KERNEL_MOE_TABLE] == 0 and d[sg.SG_KERNEL_GROUPED] == 1
+    ref, A = orc().grouped(bits(x), bits(W), ids.numpy())
+    check_f32(out, ref, A, f"grouped fused T={T}")
+    out_t = run_grouped(x, W, ids)[0]
+    assert torch.equal(out, out_t), "fused and table paths give the same bits"
+
+
+def test_grouped_fused_integer_crowded_duplicate_invalid():
+    T, topk, E, N, K = 9, 3, 6, 40, 2056
+    x = si.integer_bf16((T, K), -4, 4, 9400, DEV)
+    W = si.integer_bf16((E, N, K), -4, 4, 9401, DEV)
+    ids = torch.tensor([[3, 1, 3], [3, 0, 5], [3, 3, 3], [2, 3, -1], [3, 6, 4], [0, 1, 2],
+                        [3, 1000, 3], [5, 4, 3], [3, 2, 1]], dtype=torch.int32)
+    announce("grouped fused integer crowded/duplicate/invalid")
+    out, d = run_grouped_fused(x, W, ids)
+    assert d[sg.SG_KERNEL_MOE_TABLE] == 0
+    ref = orc().grouped(bits(x), bits(W), ids.numpy(), with_scale=False)
+    check_exact(out, ref, "grouped fused integer")
+    flat = ids.view(-1)
+    for p in range(T * topk):
+        if not 0 <= flat[p] < E:
+            assert torch.equal(out.view(-1, N)[p], torch.zeros(N, device=DEV)), "invalid id: zero row"
+
+
+def test_grouped_large_table_keeps_table_kernel():
+    # more than 512 pairs: the table kernel runs even without table outputs
+    T, topk, E, N, K = 80, 8, 64, 24, 128
+    x = si.normal_bf16((T, K), 1.0, 9500, DEV)
+    W = si.normal_bf16((E, N, K), 0.02, 9501, DEV)
+    ids = si.routing_table(T, E, topk, 9502)
+    announce("grouped 640 pairs without table outputs")
+    out, d = run_grouped_fused(x, W, ids)
+    assert d[sg.SG_KERNEL_MOE_TABLE] == 1 and d[sg.SG_KERNEL_GROUPED] == 1
+    ref, A = orc().grouped(bits(x), bits(W), ids.numpy())
+    check_f32(out, ref, A, "grouped 640 pairs")
+
+
 def test_grouped_no_tokens():
     E, N, K = 16, 32, 64
     x = torch.empty((0, K), dtype=torch.bfloat16, device=DEV)
@@ -104,6 +164,7 @@ def test_grouped_full_size(experts_full, T):
     check_table(ids, E, off, pairs, inv)
     a, b = run_grouped(x, W, ids)[0], out
     assert torch.equal(a, b), "repeat runs bitwise identical"
+    assert torch.equal(run_grouped_fused(x, W, ids)[0], out), "fused table path, same bits"
     # sampled outputs: a spread of pairs, 96 rows each (including the last row)
     rng = np.random.default_rng(T)
     P = T * topk

@@ -71,7 +71,10 @@ def test_step_small(T, K, E, N, N_shared, topk):
         res[mode] = sg.skinny_moe_step(x, Wr, We, Ws, topk, mode=mode)
         torch.cuda.synchronize()
         d = counters_delta(before, sg.skinny_gemm_get_counters())
-        assert d[sg.SG_KERNEL_ROUTER_TOPK] == 1 and d[sg.SG_KERNEL_MOE_TABLE] == 1
+        # the step asks for no table output: up to 512 pairs the grouped launch builds
+        # its table itself (no table kernel)
+        assert d[sg.SG_KERNEL_ROUTER_TOPK] == 1
+        assert d[sg.SG_KERNEL_MOE_TABLE] == (0 if T * topk <= 512 else 1)
         assert d[sg.SG_KERNEL_GROUPED] == (1 if N > 0 else 0)
         projections = sum(d[k] for k in (sg.SG_KERNEL_GEMV, sg.SG_KERNEL_SPLITK_VALU,
                                          sg.SG_KERNEL_SPLITK_MFMA))
