@@ -482,7 +482,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
         us = 1e3 * per
         gbs = nbytes / (per * 1e-3) / 1e9
         rows.append({"workload": "MoE grouped E=384 2048x7168 top8", "M": T, "N": N, "K": K,
-                     "plan": "moe_table+grouped", "us": round(us, 3), "GBps": round(gbs, 1),
+                     "plan": "fused table+grouped", "us": round(us, 3), "GBps": round(gbs, 1),
                      "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                      "distinct_experts_mean": round(sum(distinct) / len(distinct), 1)})
 

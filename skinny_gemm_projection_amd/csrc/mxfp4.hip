@@ -329,9 +329,7 @@ template <int M>
 hipError_t launch_m(int NB, int S, int N, int KB, int chunk_b, const void* x, const void* Wq,
                     const uint8_t* Ws, const Epilogue& ep, hipStream_t stream) {
     // x registers: 16 * M * NB VGPRs, kept at 64 (128 from M = 5)
-    if (NB == 4) {
-        if constexpr (M == 1) return launch_mn<M, 4>(S, N, KB, chunk_b, x, Wq, Ws, ep, stream);
-    } else if (NB == 2) {
+    if (NB == 2) {
         if constexpr (M <= 2) return launch_mn<M, 2>(S, N, KB, chunk_b, x, Wq, Ws, ep, stream);
     } else if (NB == 1) {
         return launch_mn<M, 1>(S, N, KB, chunk_b, x, Wq, Ws, ep, stream);
@@ -357,7 +355,12 @@ bool mxfp4_split(int M, int K, int* nb, int* splits) {
         return true;
     }
     const int KB = K / kBlockElems;
-    const int nb_max = M == 1 ? 4 : (M == 2 ? 2 : 1);
+    // Blocks per lane: at most 2 for one or two rows of x, so one row's K is
+    // split over two waves of a team (2048 waves instead of 1024 at N = 8192).
+    // Measured on MI355X at M = 1 against 4 blocks a lane (K whole per wave):
+    // 8192x7168 7.65 -> 7.30 us, 4096x7168 6.41 -> 5.19 us, 7168x8192
+    // 7.64 -> 7.44 us.  At M = 2, one block a lane was slower (8.7 -> 9.2 us).
+    const int nb_max = M <= 2 ? 2 : 1;
     int NB = 1;
     while (NB < nb_max && NB * kWave < KB) NB *= 2;
     int S = 1;
