@@ -134,6 +134,27 @@ sg_status router_topk_call(const float* scores, int64_t ld, int32_t T, int32_t E
     return SG_OK;
 }
 
+bool route_grouped_ok(int32_t T, int32_t E, int32_t k, int32_t N) {
+    return T >= 1 && T <= kRouteFusedMaxT && E >= 1 && E <= kRouteFusedMaxExperts && k >= 1 &&
+           k <= 32 && k <= E && N >= 1;
+}
+
+sg_status route_grouped_call(const float* scores, int64_t ld, int32_t T, int32_t E, int32_t k,
+                             int32_t* topk_ids, float* topk_scores, const sg_bf16* x,
+                             const sg_bf16* W, int32_t N, int32_t K, float* out, void* stream) {
+    if (!route_grouped_ok(T, E, k, N) || ld < E || K < 0 || K > 8192 || K % 8 != 0)
+        return SG_ERR_UNSUPPORTED;
+    (void)hipGetLastError();
+    if (launch_route_grouped(scores, ld, T, E, k, topk_ids, topk_scores, x, W, N, K, out,
+                             static_cast<hipStream_t>(stream)) != hipSuccess)
+        return SG_ERR_HIP;
+    count(SG_KERNEL_GROUPED);
+    if (log_enabled())
+        std::fprintf(stderr, "[skinny_gemm] router top-k + grouped (one launch) T=%d E=%d k=%d N=%d K=%d\n",
+                     T, E, k, N, K);
+    return SG_OK;
+}
+
 }  // namespace sg
 
 extern "C" {

@@ -92,6 +92,15 @@ constexpr int kFusedMaxPairs = 512;
 constexpr int kFusedMaxExperts = 4096;
 hipError_t launch_grouped_fused(const void* x, int T, const void* W, const int32_t* ids, int E,
                                 int N, int K, int topk, float* out, hipStream_t stream);
+// Router top-k and the fused grouped projection in one launch, for a few
+// tokens: 1 <= T <= kRouteFusedMaxT, E <= kRouteFusedMaxExperts (at most 8
+// keys a lane), N >= 1.  ids [T, k] (and top [T, k] when non-null) are
+// written as by launch_router_topk.
+constexpr int kRouteFusedMaxT = 4;
+constexpr int kRouteFusedMaxExperts = 512;
+hipError_t launch_route_grouped(const float* scores, int64_t ld, int T, int E, int k,
+                                int32_t* ids, float* top, const void* x, const void* W, int N,
+                                int K, float* out, hipStream_t stream);
 hipError_t launch_grouped(const void* x, int T, const void* W, int E, int N, int K, int topk,
                           const GroupedWorkspace& g, float* out, hipStream_t stream);
 

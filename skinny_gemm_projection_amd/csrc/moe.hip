@@ -10,6 +10,7 @@
 // many tokens chose it.  No host synchronisation: the number of active
 // experts is only known on the device, so the grouped kernel reads it there.
 #include "launch.h"
+#include "topk_device.h"
 
 namespace sg {
 
@@ -262,20 +263,20 @@ __global__ __launch_bounds__(kBlock) void grouped_kernel(const uint4* __restrict
 // (one token: 8 experts, 235 MB, the table alone was about 4 us under the
 // profiler).  Work items, per-(pair, row) arithmetic and outputs are those
 // of grouped_kernel; output rows of ids outside [0, E) are zero-filled here.
+//
+// The body runs once the workgroup's ids are in s_ids[0, P): the caller
+// stores them, and the body's first barrier publishes them.
 template <int NCH>
-__global__ __launch_bounds__(kBlock) void grouped_fused_kernel(
-    const uint4* __restrict__ x, const uint4* __restrict__ W, const int32_t* __restrict__ ids,
-    int P, int E, int N, int K8, int topk, int tiles, float* __restrict__ out) {
-    extern __shared__ int32_t lds_i[];
-    int32_t* s_ids = lds_i;          // [P]
-    int32_t* s_flag = s_ids + P;     // [E]: expert e has a pair
-    int32_t* s_active = s_flag + E;  // [E]: active experts, ascending
-    __shared__ int32_t s_wave[kWavesPerBlock];
+__device__ __forceinline__ void grouped_lds_table(const uint4* __restrict__ x,
+                                                  const uint4* __restrict__ W,
+                                                  const int32_t* s_ids, int32_t* s_flag,
+                                                  int32_t* s_active, int32_t* s_wave, int P,
+                                                  int E, int N, int K8, int topk, int tiles,
+                                                  float* __restrict__ out) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wv = wave_id_in_block();
 
-    for (int p = tid; p < P; p += kBlock) s_ids[p] = ids[p];
     for (int e = tid; e < E; e += kBlock) s_flag[e] = 0;
     __syncthreads();
     for (int p = tid; p < P; p += kBlock) {
@@ -371,6 +372,49 @@ __global__ __launch_bounds__(kBlock) void grouped_fused_kernel(
     }
 }
 
+// LDS of the fused launches: ids [P], expert flags [E], active experts [E].
+template <int NCH>
+__global__ __launch_bounds__(kBlock) void grouped_fused_kernel(
+    const uint4* __restrict__ x, const uint4* __restrict__ W, const int32_t* __restrict__ ids,
+    int P, int E, int N, int K8, int topk, int tiles, float* __restrict__ out) {
+    extern __shared__ int32_t lds_i[];
+    __shared__ int32_t s_wave[kWavesPerBlock];
+    for (int p = threadIdx.x; p < P; p += kBlock) lds_i[p] = ids[p];
+    grouped_lds_table<NCH>(x, W, lds_i, lds_i + P, lds_i + P + E, s_wave, P, E, N, K8, topk,
+                           tiles, out);
+}
+
+// Router top-k and routed-expert projection in one launch, for a few tokens
+// (T <= kRouteFusedMaxT): every workgroup ranks the scores itself -- wave w
+// takes tokens w, w + 4, ... with the router kernel's wave_topk, so the ids
+// are the same bits -- and workgroup 0 also stores them (and the selected
+// scores).  Then the fused table and the grouped loop as above.  This drops
+// the top-k launch and the round trip of the ids through memory.
+template <int NCH, int PER>
+__global__ __launch_bounds__(kBlock) void route_grouped_kernel(
+    const float* __restrict__ scores, int64_t ld, int T, int E, int k,
+    int32_t* __restrict__ ids_out, float* __restrict__ top_out, const uint4* __restrict__ x,
+    const uint4* __restrict__ W, int N, int K8, int tiles, float* __restrict__ out) {
+    extern __shared__ int32_t lds_i[];
+    __shared__ int32_t s_wave[kWavesPerBlock];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int P = T * k;
+    for (int t = wave_id_in_block(); t < T; t += kWavesPerBlock) {
+        const float* s = scores + t * ld;
+        const uint64_t mine = wave_topk<PER>(s, E, k, lane);
+        if (lane < k) {
+            const int id = key_id(mine);
+            lds_i[t * k + lane] = id;
+            if (blockIdx.x == 0) {
+                ids_out[(int64_t)t * k + lane] = id;
+                if (top_out) top_out[(int64_t)t * k + lane] = s[id];  // as given
+            }
+        }
+    }
+    grouped_lds_table<NCH>(x, W, lds_i, lds_i + P, lds_i + P + E, s_wave, P, E, N, K8, k,
+                           tiles, out);
+}
+
 int next_pow2(int v) {
     int p = 1;
     while (p < v) p <<= 1;
@@ -430,6 +474,58 @@ hipError_t launch_grouped_fused(const void* x, int T, const void* W, const int32
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <int NCH>
+static hipError_t launch_route_nch(int per, int grid, size_t lds, hipStream_t stream,
+                             const float* scores, int64_t ld, int T, int E, int k, int32_t* ids,
+                             float* top, const uint4* xp, const uint4* wp, int N, int K8,
+                             int tiles, float* out) {
+#define SG_ROUTE(pp) \
+    if (per <= pp) { \
+        route_grouped_kernel<NCH, pp><<<grid, kBlock, lds, stream>>>( \
+            scores, ld, T, E, k, ids, top, xp, wp, N, K8, tiles, out); \
+        return hipGetLastError(); \
+    }
+    SG_ROUTE(2) SG_ROUTE(4) SG_ROUTE(6) SG_ROUTE(8)
+#undef SG_ROUTE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_route_grouped(const float* scores, int64_t ld, int T, int E, int k,
+                                int32_t* ids, float* top, const void* x, const void* W, int N,
+                                int K, float* out, hipStream_t stream) {
+    const int per = (E + kWave - 1) / kWave;
+    if (T < 1 || T > kRouteFusedMaxT || per > kSortedPerLane || N < 1) return hipErrorInvalidValue;
+    const int P = T * k;
+    const int K8 = K / kPiece;
+    const int tiles = (N + kGroupedTileN - 1) / kGroupedTileN;
+    const int max_active = E < P ? E : P;
+    const int64_t max_items = (int64_t)max_active * tiles;
+    const int resident = 512;  // 256 CUs x 2 workgroups
+    const int grid = (int)(max_items < resident ? max_items : resident);
+    const size_t lds = (size_t)(P + 2 * E) * sizeof(int32_t);
+    const uint4* xp = static_cast<const uint4*>(x);
+    const uint4* wp = static_cast<const uint4*>(W);
+    const int nch = (K + kLaneSpan - 1) / kLaneSpan;
+    switch (next_pow2(nch < 1 ? 1 : nch)) {
+        case 1:
+            return launch_route_nch<1>(per, grid, lds, stream, scores, ld, T, E, k, ids, top, xp,
+                                        wp, N, K8, tiles, out);
+        case 2:
+            return launch_route_nch<2>(per, grid, lds, stream, scores, ld, T, E, k, ids, top, xp,
+                                        wp, N, K8, tiles, out);
+        case 4:
+            return launch_route_nch<4>(per, grid, lds, stream, scores, ld, T, E, k, ids, top, xp,
+                                        wp, N, K8, tiles, out);
+        case 8:
+            return launch_route_nch<8>(per, grid, lds, stream, scores, ld, T, E, k, ids, top, xp,
+                                        wp, N, K8, tiles, out);
+        case 16:
+            return launch_route_nch<16>(per, grid, lds, stream, scores, ld, T, E, k, ids, top, xp,
+                                        wp, N, K8, tiles, out);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_grouped(const void* x, int T, const void* W, int E, int N, int K, int topk,

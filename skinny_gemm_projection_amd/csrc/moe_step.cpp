@@ -6,9 +6,12 @@
 // as the step does and run on a separate stream ("Hyper Optimizing Kimi K3 in
 // vLLM" deepnotes page, Method details §3; French translation, Partie 1 §3).
 // On one MI355X the window it fills is the routing phase: the router
-// projection is a few MB, and the top-k and token-table kernels occupy a
-// handful of CUs, so HBM is mostly idle for several microseconds before the
-// routed-expert weights start to stream.  The side stream forks from the
+// projection is a few MB, and the top-k and the start of the routed-expert
+// launch (which builds its token table in LDS) occupy a handful of CUs, so
+// HBM is mostly idle for several microseconds before the routed-expert
+// weights start to stream.  Up to 4 tokens the top-k itself runs inside the
+// routed-expert launch: every workgroup ranks the scores, so a step is two
+// launches (router projection, routed experts).  The side stream forks from the
 // caller's stream at entry and joins it at the end; the caller owns both
 // streams and both events.  Host-side composition only: every step is one of
 // the library's own calls, so the outputs are identical with and without the
@@ -118,13 +121,21 @@ sg_status skinny_moe_step(const sg_moe_step* a, void* workspace, size_t workspac
                           L.router_ws, stream)) != SG_OK)
         return st;
     const int64_t ld = fused ? (int64_t)a->E + a->N_shared : a->E;  // row stride of the scores
-    if ((st = sg::router_topk_call(a->scores, ld, a->T, a->E, a->topk, a->topk_ids,
-                                   a->topk_scores, stream)) != SG_OK)
-        return st;
-    if ((st = grouped_skinny_gemm(a->x, a->T, a->W_experts, a->E, a->N, a->K, a->topk_ids,
-                                  a->topk, a->out, nullptr, nullptr, nullptr, grouped_ws,
-                                  L.grouped_ws, stream)) != SG_OK)
-        return st;
+    if (sg::route_grouped_ok(a->T, a->E, a->topk, a->N)) {
+        // a few tokens: top-k and the routed experts in one launch
+        if ((st = sg::route_grouped_call(a->scores, ld, a->T, a->E, a->topk, a->topk_ids,
+                                         a->topk_scores, a->x, a->W_experts, a->N, a->K,
+                                         a->out, stream)) != SG_OK)
+            return st;
+    } else {
+        if ((st = sg::router_topk_call(a->scores, ld, a->T, a->E, a->topk, a->topk_ids,
+                                       a->topk_scores, stream)) != SG_OK)
+            return st;
+        if ((st = grouped_skinny_gemm(a->x, a->T, a->W_experts, a->E, a->N, a->K, a->topk_ids,
+                                      a->topk, a->out, nullptr, nullptr, nullptr, grouped_ws,
+                                      L.grouped_ws, stream)) != SG_OK)
+            return st;
+    }
     if (overlap) return hipStreamWaitEvent(main_s, join, 0) == hipSuccess ? SG_OK : SG_ERR_HIP;
     return sep ? shared_expert(stream) : SG_OK;
 }

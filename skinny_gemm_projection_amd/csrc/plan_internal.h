@@ -20,4 +20,12 @@ bool plan_matches(const sg_plan* p);
 sg_status router_topk_call(const float* scores, int64_t ld, int32_t T, int32_t E, int32_t k,
                            int32_t* topk_ids, float* topk_scores, void* stream);
 
+// Router top-k and the routed-expert projection as one launch (a few tokens,
+// E <= 512, N >= 1; see launch_route_grouped): whether it applies, and the
+// counted, logged call.  The caller has checked pointers and alignment.
+bool route_grouped_ok(int32_t T, int32_t E, int32_t k, int32_t N);
+sg_status route_grouped_call(const float* scores, int64_t ld, int32_t T, int32_t E, int32_t k,
+                             int32_t* topk_ids, float* topk_scores, const sg_bf16* x,
+                             const sg_bf16* W, int32_t N, int32_t K, float* out, void* stream);
+
 }  // namespace sg

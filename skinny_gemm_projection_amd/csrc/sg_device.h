@@ -152,7 +152,8 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 // the final epilogue: value = acc (+ r[i] when a residual is given), stored
 // as fp32 and/or bf16 (RNE of the fp32 value).
 struct Epilogue {
-    float* partial;         // [S, M, N] when split_k > 1, else nullptr
+    float* partial;         // split partials when split_k > 1 ([S, M, N] from the vector-ALU
+                            // kernel, [S, N, 16*ceil(M/16)] from the chunk kernel), else nullptr
     float* y_f32;           // nullable
     uint16_t* y_bf16;       // nullable; may equal r (in place)
     const uint16_t* r;      // residual [M, N] or nullptr

@@ -61,7 +61,10 @@ def check_step(res, x, Wr, We, Ws, topk, what, out_rows=None):
 @pytest.mark.parametrize("T,K,E,N,N_shared,topk", [(1, 1024, 64, 96, 160, 8),
                                                     (5, 520, 40, 33, 72, 6),
                                                     (64, 1032, 64, 40, 48, 8),
-                                                    (16, 256, 17, 130, 0, 3)])
+                                                    (16, 256, 17, 130, 0, 3),
+                                                    (4, 520, 384, 40, 0, 8),
+                                                    (2, 264, 500, 24, 32, 32),
+                                                    (3, 1032, 64, 0, 48, 4)])
 def test_step_small(T, K, E, N, N_shared, topk):
     x, Wr, We, Ws = weights(T, K, E, N, N_shared, 7000 + T)
     res = {}
@@ -72,8 +75,10 @@ def test_step_small(T, K, E, N, N_shared, topk):
         torch.cuda.synchronize()
         d = counters_delta(before, sg.skinny_gemm_get_counters())
         # the step asks for no table output: up to 512 pairs the grouped launch builds
-        # its table itself (no table kernel)
-        assert d[sg.SG_KERNEL_ROUTER_TOPK] == 1
+        # its table itself (no table kernel); up to 4 tokens (E <= 512) it also ranks
+        # the scores itself (no top-k kernel)
+        route_fused = 1 <= T <= 4 and E <= 512 and N > 0
+        assert d[sg.SG_KERNEL_ROUTER_TOPK] == (0 if route_fused else 1)
         assert d[sg.SG_KERNEL_MOE_TABLE] == (0 if T * topk <= 512 else 1)
         assert d[sg.SG_KERNEL_GROUPED] == (1 if N > 0 else 0)
         projections = sum(d[k] for k in (sg.SG_KERNEL_GEMV, sg.SG_KERNEL_SPLITK_VALU,
@@ -84,10 +89,12 @@ def test_step_small(T, K, E, N, N_shared, topk):
         assert torch.equal(a, b), "side-stream and serial steps bitwise identical"
 
 
-def test_step_integer_bit_exact():
-    # integer inputs: every partial sum is exact in fp32, so every output is bit-exact
-    T, K, E, N, Ns, topk = 7, 264, 24, 50, 70, 5
-    announce("moe step integer inputs")
+@pytest.mark.parametrize("T", [7, 3, 1])
+def test_step_integer_bit_exact(T):
+    # integer inputs: every partial sum is exact in fp32, so every output is bit-exact;
+    # T <= 4 takes the launch that ranks the scores itself
+    K, E, N, Ns, topk = 264, 24, 50, 70, 5
+    announce(f"moe step integer inputs T={T}")
     x = si.integer_bf16((T, K), -4, 4, 7101, DEV)
     Wr = si.integer_bf16((E, K), -4, 4, 7102, DEV)
     We = si.integer_bf16((E, N, K), -4, 4, 7103, DEV)
