@@ -72,7 +72,7 @@ typedef enum {
     SG_KERNEL_NONE = 0,         /* empty problem (M == 0 or N == 0): nothing runs  */
     SG_KERNEL_GEMV = 1,         /* small-matrix kernel, M <= 2                     */
     SG_KERNEL_SPLITK_VALU = 2,  /* split-K partial, vector-ALU dot, 3 <= M <= 7    */
-    SG_KERNEL_SPLITK_MFMA = 3,  /* split-K partial, bf16 matrix cores, M >= 8      */
+    SG_KERNEL_SPLITK_MFMA = 3,  /* split-K partial, bf16 matrix cores, M >= 6 or 8 */
     SG_KERNEL_REDUCE = 4,       /* split-K deterministic reduction + epilogue      */
     SG_KERNEL_MOE_TABLE = 5,    /* per-expert token table                          */
     SG_KERNEL_GROUPED = 6,      /* grouped per-expert projection                   */
@@ -108,7 +108,8 @@ typedef struct {
 /* plan(M, N, K) -- pick the kernel and its tiling for y[M,N] = x[M,K] W[N,K]^T
  * ([P] Method details §1).  0 <= M <= 64: M <= 2 small-matrix kernel; larger
  * M split-K, on the vector ALU below 8 rows and on bf16 matrix cores from 8
- * rows (measured crossover on MI355X); the split factor and row tiling come
+ * rows -- from 6 rows where N/16 workgroups fill the GPU (measured
+ * crossovers on MI355X); the split factor and row tiling come
  * from a per-compute-unit byte cost model, overridable by a tuned table.  M > 64 returns
  * SG_ERR_UNSUPPORTED (prefill-sized batches fall back, [D]); M == 0 or
  * N == 0 gives kernel SG_KERNEL_NONE.  Host-only: touches no GPU state.

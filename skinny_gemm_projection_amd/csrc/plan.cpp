@@ -8,8 +8,9 @@
 //                 in registers (K <= 8192), fused epilogue;
 //   3 <= M <= 7   the same kernel on K chunks (split-K), the split sized so
 //                 the M x-rows of a chunk fit in its registers, reduced
-//                 inside the workgroup when the split allows;
-//   8 <= M <= 64  bf16 matrix-core split-K: up to 12 rows the team kernel
+//                 inside the workgroup when the split allows (from M = 6 only
+//                 where the team kernel's grid does not fill the GPU);
+//   8 <= M <= 64  bf16 matrix-core split-K: up to 16 rows the team kernel
 //                 (K split over the waves of a workgroup, reduced in LDS)
 //                 when N/16 workgroups fill the GPU; otherwise the chunk
 //                 kernel, split factor and row tiling from a
@@ -35,6 +36,11 @@ constexpr int kComputeUnits = 256;
 // kernel, which needs no second pass, is faster (M=4: 12.8 against 13.8).
 constexpr int32_t kMfmaFromM = 8;
 constexpr int32_t kTeamUpToM = 16;
+// From 6 rows the matrix-core team kernel already beats the vector-ALU
+// kernel where its grid of N/16 workgroups fills the compute units
+// (interleaved A/B at K=7168, N=4096: M=6 12.3 against 12.9 us with 4 K
+// chunks, M=7 12.4 against 13.4 us; M=5 12.3 against 11.9 us).
+constexpr int32_t kTeamFromM = 6;
 
 // Choices measured on MI355X for known projection shapes, overriding the
 // defaults: {M_lo, M_hi, N, K, kernel (0: default), split (0: default),
@@ -185,8 +191,10 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
     }
 
     if (kernel <= 0) {
+        const bool team_fills = (N + kMfmaTeamTileN - 1) / kMfmaTeamTileN >= kComputeUnits;
+        const int32_t mfma_from = team_fills ? kTeamFromM : kMfmaFromM;
         kernel = M <= 2 ? SG_KERNEL_GEMV
-                        : (M < kMfmaFromM ? SG_KERNEL_SPLITK_VALU : SG_KERNEL_SPLITK_MFMA);
+                        : (M < mfma_from ? SG_KERNEL_SPLITK_VALU : SG_KERNEL_SPLITK_MFMA);
         if (const Tuned* t = tuned_for(M, N, K)) {
             if (t->kernel > 0) kernel = t->kernel;
             if (split_k <= 0 && t->split > 0) split_k = t->split;

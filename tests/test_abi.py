@@ -66,10 +66,19 @@ def test_status_strings():
 def test_plan_kernel_by_batch():
     for M in range(1, 65):
         p = sg.skinny_gemm_plan(M, 4096, 7168)
+        # the team kernel's 256 workgroups fill the GPU at N = 4096: matrix cores from M = 6
         want = (sg.SG_KERNEL_GEMV if M <= 2 else
-                sg.SG_KERNEL_SPLITK_VALU if M < 8 else sg.SG_KERNEL_SPLITK_MFMA)
+                sg.SG_KERNEL_SPLITK_VALU if M < 6 else sg.SG_KERNEL_SPLITK_MFMA)
         assert p.kernel == want, (M, p)
         assert (p.M, p.N, p.K) == (M, 4096, 7168)
+
+
+def test_plan_kernel_by_batch_few_rows():
+    # N/16 workgroups do not fill the GPU: the vector-ALU kernel up to M = 7
+    for M in range(3, 9):
+        p = sg.skinny_gemm_plan(M, 1024, 7168)
+        want = sg.SG_KERNEL_SPLITK_VALU if M < 8 else sg.SG_KERNEL_SPLITK_MFMA
+        assert p.kernel == want, (M, p)
 
 
 def test_plan_rejects():
