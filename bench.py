@@ -513,8 +513,13 @@ def sweep(torch, sg, si, L, cyc, reps=40):
             proj_bytes(T, E, K, bf16=False) + proj_bytes(T, N, K, bf16=False) - T * K * 2 + \
             T * topk * N * 4 + T * topk * 4
         per = {}
+        launches = {}
         for mode in ("serial", "side_stream", "fused"):
             calls = [L.moe_step(x, wr, W, wsh, topk, outs, ws, mode) for x, wr, wsh in combos]
+            before = sg.skinny_gemm_get_counters()
+            calls[0]()
+            torch.cuda.synchronize()
+            launches[mode] = sum(a - b for a, b in zip(sg.skinny_gemm_get_counters(), before))
             per[mode] = timed_calls(torch, calls, n_calls, cyc)
         gbs = nbytes / (per["fused"] * 1e-3) / 1e9
         rows.append({"workload": "MoE step E=384 top8 2048x7168 + shared expert", "M": T,
@@ -522,6 +527,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
                      "us": round(1e3 * per["fused"], 3),
                      "us_side_stream": round(1e3 * per["side_stream"], 3),
                      "us_serial": round(1e3 * per["serial"], 3),
+                     "launches_per_step": launches["fused"],
                      "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                      "distinct_experts_mean": round(sum(distinct) / len(distinct), 1)})
     del W, Wrs, ring_rs
