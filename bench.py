@@ -302,6 +302,40 @@ def graph_timing(torch, sg, make_call, m_list, R, y32, per_graph=200, replays=5)
     return out
 
 
+def graph_us(torch, sg, make_calls, out, per_graph=200, replays=5):
+    """Median us per call of `per_graph` back-to-back calls captured in one HIP graph on a
+    stream of its own (make_calls(launcher) builds the calls for that stream's launcher),
+    after checking that every replay leaves `out` as an eager call does."""
+    gs = torch.cuda.Stream()
+    with torch.cuda.stream(gs):
+        L2 = Launcher(torch, sg)
+    calls = make_calls(L2)
+    with torch.cuda.stream(gs):
+        calls[0]()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        for i in range(per_graph):
+            calls[(i + 1) % len(calls)]()
+    times = []
+    for _ in range(replays):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(gs):
+            start.record()
+            g.replay()
+            stop.record()
+        torch.cuda.synchronize()
+        times.append(1e3 * start.elapsed_time(stop) / per_graph)
+        if not torch.equal(out, eager):
+            raise RuntimeError("graph replay differs from the eager call")
+    del g
+    times.sort()
+    return round(times[len(times) // 2], 3)
+
+
 def sweep(torch, sg, si, L, cyc, reps=40):
     dev = "cuda"
     rows = []
@@ -377,6 +411,10 @@ def sweep(torch, sg, si, L, cyc, reps=40):
         ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
         per = timed_calls(torch, [L.projection(p, x, w, y32, None, ws) for w in ring], reps, cyc)
         record("split-K 4096x7168", M, N, K, plan_desc(p), per, proj_bytes(M, N, K, bf16=False))
+        if M in (4, 16, 32, 64):  # also as 200 calls in one HIP graph (one or two launches each)
+            rows[-1]["us_graph"] = graph_us(
+                torch, sg, lambda L2, p=p, x=x, y32=y32, ws=ws:
+                [L2.projection(p, x, w, y32, None, ws) for w in ring], y32)
     del ring
 
     # fused output projection + residual, K=8192, N=7168, bf16 out
@@ -391,6 +429,9 @@ def sweep(torch, sg, si, L, cyc, reps=40):
         per = timed_calls(torch, [L.residual(p, x, w, r, o16, None, ws) for w in ring], reps, cyc)
         record("residual 7168x8192", M, N, K, plan_desc(p), per,
                proj_bytes(M, N, K, f32=False, residual=True))
+        rows[-1]["us_graph"] = graph_us(
+            torch, sg, lambda L2, p=p, x=x, r=r, o16=o16, ws=ws:
+            [L2.residual(p, x, w, r, o16, None, ws) for w in ring], o16)
     del ring
     torch.cuda.empty_cache()
 
