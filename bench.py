@@ -240,6 +240,8 @@ def main_workload(torch, sg, si, L, steps, warmup, cyc):
                                                                     y16[M]),
                          M_LIST, R, y32)
 
+    cold = cold_latency(torch, sg, L, calls, M_LIST, ring)
+
     bytes_per = {M: proj_bytes(M, N_MAIN, K_MAIN) for M in M_LIST}
     step_bytes = sum(bytes_per.values())
     us = {M: 1e3 * per_m_ms[M] for M in M_LIST}
@@ -258,8 +260,39 @@ def main_workload(torch, sg, si, L, steps, warmup, cyc):
         "achieved": achieved, "avg_launch_us": 1e3 * avg_launch_ms,
         "bytes_per_launch": launch_bytes,
         "graph": graph,
+        "cold": cold,
         "inputs": (x, W0),
     }
+
+
+def cold_latency(torch, sg, L, calls, m_list, ring, trials=15):
+    """Secondary number: one call on its own, its weights cold.  Before each trial the
+    prefetch kernel reads every other copy of the ring (more than the 256 MB Infinity
+    Cache), then one event pair brackets the single call (launch latency included).
+    Median, min and max us per batch size."""
+    R = len(ring)
+    nbytes = ring[0].numel() * ring[0].element_size()
+    out = {}
+    for M in m_list:
+        times = []
+        for t in range(trials):
+            r = t % R
+            for o in range(R):
+                if o != r:
+                    st = L.c.skinny_gemm_prefetch(ring[o].data_ptr(), nbytes, L.sp)
+                    if st:
+                        raise RuntimeError(sg.skinny_gemm_status_str(st))
+            torch.cuda.synchronize()
+            start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record()
+            calls[(M, r)]()
+            stop.record()
+            torch.cuda.synchronize()
+            times.append(1e3 * start.elapsed_time(stop))
+        times.sort()
+        out[str(M)] = {"median_us": round(times[len(times) // 2], 3), "min_us": round(times[0], 3),
+                       "max_us": round(times[-1], 3)}
+    return out
 
 
 def graph_timing(torch, sg, make_call, m_list, R, y32, per_graph=200, replays=5):
@@ -1000,6 +1033,7 @@ def main() -> None:
         },
         "us_per_projection": res["us_per_projection"],
         "us_per_projection_graph": res["graph"],
+        "us_single_call_cold": res["cold"],
         "GBps_per_batch": res["gbs_per_batch"],
         "pct_of_peak": round(100.0 * res["value"] / HBM_PEAK_GBS, 1),
         "wall_ms_per_step": round(res["wall_ms_per_step"], 6),
