@@ -56,6 +56,10 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.oracle_e8m0_to_f64.restype = ctypes.c_double
     lib.oracle_projection_mxfp4.argtypes = [c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p]
     lib.oracle_projection_mxfp4.restype = None
+    lib.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_f64.restype = ctypes.c_double
+    lib.oracle_projection_fp8.argtypes = [c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p]
+    lib.oracle_projection_fp8.restype = None
     for name in ("oracle_encode_bf16", "oracle_projection", "oracle_splitk_partials",
                  "oracle_splitk_sum", "oracle_residual", "oracle_grouped"):
         getattr(lib, name).restype = None
@@ -180,6 +184,26 @@ class Oracle:
     def e8m0_to_f64(self, scales) -> np.ndarray:
         scales = np.asarray(scales, dtype=np.uint8).ravel()
         return np.array([self.c.oracle_e8m0_to_f64(int(s)) for s in scales], dtype=np.float64)
+
+    def e4m3_to_f64(self, codes) -> np.ndarray:
+        codes = np.asarray(codes, dtype=np.uint8).ravel()
+        return np.array([self.c.oracle_e4m3_to_f64(int(c)) for c in codes], dtype=np.float64)
+
+    def projection_fp8(self, x, Wq, Ws, with_scale: bool = True):
+        """y = x W^T for FP8 weights: Wq uint8 [N, K] (e4m3 codes), Ws float32
+        [ceil(N/128), ceil(K/128)] (one scale per 128 x 128 block)."""
+        x = _bits(x)
+        Wq = np.ascontiguousarray(Wq, dtype=np.uint8)
+        Ws = np.ascontiguousarray(Ws, dtype=np.float32)
+        M, K = x.shape
+        N = Wq.shape[0]
+        assert Wq.shape == (N, K) and Ws.shape == (-(-N // 128), -(-K // 128)), \
+            (x.shape, Wq.shape, Ws.shape)
+        y = np.empty((M, N), dtype=np.float64)
+        a = np.empty((M, N), dtype=np.float64) if with_scale else None
+        self.c.oracle_projection_fp8(M, N, K, _ptr(x), _ptr(Wq), _ptr(Ws), _ptr(y),
+                                     _ptr(a) if a is not None else None)
+        return (y, a) if with_scale else y
 
     def projection_mxfp4(self, x, Wq, Ws, with_scale: bool = True):
         """y = x W^T for MXFP4 weights: Wq uint8 [N, K/2] (two e2m1 codes a byte, low

@@ -276,3 +276,40 @@ void oracle_projection_mxfp4(int64_t M, int64_t N, int64_t K, const uint16_t* x,
         }
     }
 }
+
+double oracle_e4m3_to_f64(uint8_t code)
+{
+    /* OCP 8-bit float E4M3 (the "fn" variant: finite, no infinity): bit 7
+     * sign, bits 6..3 exponent (bias 7), bits 2..0 mantissa.  Exponent 0 is
+     * subnormal, m/8 * 2^-6; exponent 15 with mantissa 7 is NaN (either
+     * sign); every other code is the normal value 2^(e-7) * (1 + m/8). */
+    const int sign = (code >> 7) & 1;
+    const int e = (code >> 3) & 15;
+    const int m = code & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    const double mag = (e == 0) ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+void oracle_projection_fp8(int64_t M, int64_t N, int64_t K, const uint16_t* x,
+                           const uint8_t* Wq, const float* Ws, double* y, double* abs_scale)
+{
+    /* Each weight is its e4m3 code times the fp32 scale of its 128 x 128
+     * block, then the plain projection sum, k ascending. */
+    const int64_t KB = (K + 127) / 128;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0, abs_sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double w = oracle_e4m3_to_f64(Wq[n * K + k]) * (double)Ws[(n / 128) * KB + k / 128];
+                const double term = oracle_bf16_to_f64(x[m * K + k]) * w;
+                sum += term;
+                abs_sum += fabs(term);
+            }
+            y[m * N + n] = sum;
+            if (abs_scale)
+                abs_scale[m * N + n] = abs_sum;
+        }
+    }
+}

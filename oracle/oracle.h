@@ -124,6 +124,23 @@ void oracle_projection_mxfp4(int64_t M, int64_t N, int64_t K, const uint16_t* x,
                              const uint8_t* Wq, const uint8_t* Ws, double* y,
                              double* abs_scale);
 
+/* FP8 weights with block scales (the block-scaled 8-bit weight format of
+ * DeepSeek-V3-style checkpoints; a reading: the method pages name only a
+ * 4-bit format for a later model).
+ * e4m3: bit 7 sign, bits 6..3 exponent (bias 7), bits 2..0 mantissa;
+ * exponent 0 is subnormal (m/8 * 2^-6); exponent 15 with mantissa 7 is NaN;
+ * no infinity.  The largest finite magnitude is 448. */
+double oracle_e4m3_to_f64(uint8_t code);
+
+/* y = x W^T for FP8 weights:
+ *   Wq [N, K] e4m3 codes, one byte each, row-major;
+ *   Ws [ceil(N/128), ceil(K/128)] fp32 scales, row-major: block (i, j)
+ *      covers rows [128i, 128i+128) and k in [128j, 128j+128);
+ *   w[n,k] = e4m3(Wq[n,k]) * Ws[n/128, k/128], then the plain sum, k
+ *   ascending.  abs_scale (nullable) receives sum_k |x w|. */
+void oracle_projection_fp8(int64_t M, int64_t N, int64_t K, const uint16_t* x,
+                           const uint8_t* Wq, const float* Ws, double* y, double* abs_scale);
+
 #ifdef __cplusplus
 }
 #endif

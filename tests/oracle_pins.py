@@ -645,6 +645,101 @@ def check_mxfp4_nan_scale_rows(o):
     assert np.isnan(y[:, 2]).all() and not np.isnan(np.delete(y, 2, axis=1)).any()
 
 
+def _e4m3_golden():
+    """{code: (Fraction magnitude, negative) or 'nan'} from tests/golden/fp8_e4m3_decode.txt."""
+    out = {}
+    for code, value in read_table("fp8_e4m3_decode.txt"):
+        out[int(code, 16)] = "nan" if value == "nan" else (exact(value.lstrip("-")),
+                                                           value.startswith("-"))
+    return out
+
+
+def check_fp8_decode_golden(o):
+    for code, v in _e4m3_golden().items():
+        got = o.c.oracle_e4m3_to_f64(code)
+        if v == "nan":
+            assert math.isnan(got), (code, got)
+        else:
+            mag, neg = v
+            assert Fraction(abs(got)) == mag and math.copysign(1.0, got) == (-1.0 if neg else 1.0), \
+                (hex(code), got)
+
+
+def _torch_e4m3(codes: np.ndarray) -> np.ndarray:
+    """torch's float8_e4m3fn conversion of the codes, as float64 (a library routine)."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def check_fp8_decode_vs_torch(o):
+    codes = np.arange(256, dtype=np.uint8)
+    ref = _torch_e4m3(codes)
+    got = o.e4m3_to_f64(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]), "every finite e4m3 code"
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok])), "signed zeros"
+
+
+def _fp8_weights(N, K, seed, pow2_scales):
+    rng = np.random.default_rng(seed)
+    Wq = rng.integers(0, 256, (N, K)).astype(np.uint8)
+    Wq[(Wq & 0x7F) == 0x7F] = 0x38  # no NaN codes here
+    shape = (-(-N // 128), -(-K // 128))
+    if pow2_scales:
+        Ws = np.ldexp(1.0, rng.integers(-12, 4, shape)).astype(np.float32)
+    else:
+        Ws = rng.uniform(0.001, 0.05, shape).astype(np.float32)
+    return Wq, Ws
+
+
+def _fp8_dequant(Wq, Ws):
+    """Weights in float64 without the oracle: torch's e4m3 conversion times the block
+    scale, expanded over 128 x 128 blocks with numpy."""
+    N, K = Wq.shape
+    scale = np.repeat(np.repeat(Ws.astype(np.float64), 128, axis=0), 128, axis=1)[:N, :K]
+    return _torch_e4m3(Wq) * scale
+
+
+def check_fp8_projection_vs_numpy(o):
+    # numpy float64 matmul on the independently dequantised weights; shapes cross the
+    # 128-row and 128-column block edges, every block with its own scale
+    for M, N, K, seed in [(2, 200, 300, 1), (1, 130, 136, 2), (3, 5, 8, 3), (2, 257, 129, 4)]:
+        x = random_bf16((M, K), 60 + seed)
+        Wq, Ws = _fp8_weights(N, K, seed, pow2_scales=False)
+        y, A = o.projection_fp8(x, Wq, Ws)
+        w = _fp8_dequant(Wq, Ws)
+        xv = values(x)
+        ref, ref_a = xv @ w.T, np.abs(xv) @ np.abs(w).T
+        close(y, ref, ref_a, 1e-12, f"fp8 projection {M}x{N}x{K}")
+        close(A, ref_a, ref_a, 1e-12, f"fp8 scale {M}x{N}x{K}")
+
+
+def check_fp8_exact_small(o):
+    # exact rational brute force (power-of-two block scales: every double sum exact)
+    M, N, K = 2, 3, 40
+    x = random_bf16((M, K), 91)
+    Wq, Ws = _fp8_weights(N, K, 92, pow2_scales=True)
+    y, A = o.projection_fp8(x, Wq, Ws)
+    w = _fp8_dequant(Wq, Ws)
+    for m in range(M):
+        for n in range(N):
+            terms = [Fraction(float(values(x[m:m + 1, k:k + 1])[0, 0])) * Fraction(float(w[n, k]))
+                     for k in range(K)]
+            assert y[m, n] == float(sum(terms)), (m, n)
+            assert A[m, n] == float(sum(abs(t) for t in terms)), (m, n)
+
+
+def check_fp8_nan_code_rows(o):
+    # a NaN code poisons exactly its row
+    M, N, K = 2, 4, 64
+    x = random_bf16((M, K), 7)
+    Wq, Ws = _fp8_weights(N, K, 8, pow2_scales=True)
+    Wq[1, 5] = 0xFF
+    y = o.projection_fp8(x, Wq, Ws, with_scale=False)
+    assert np.isnan(y[:, 1]).all() and not np.isnan(np.delete(y, 1, axis=1)).any()
+
+
 ALL_CHECKS = [
     check_bf16_decode_golden, check_bf16_decode_all_patterns, check_bf16_round_golden,
     check_bf16_round_vs_torch, check_bf16_round_bruteforce,
@@ -656,6 +751,8 @@ ALL_CHECKS = [
     check_router_topk_golden, check_router_topk_vs_sort,
     check_mxfp4_decode_golden, check_mxfp4_scales_vs_ldexp, check_mxfp4_projection_golden,
     check_mxfp4_vs_bf16_projection, check_mxfp4_exact_small, check_mxfp4_nan_scale_rows,
+    check_fp8_decode_golden, check_fp8_decode_vs_torch, check_fp8_projection_vs_numpy,
+    check_fp8_exact_small, check_fp8_nan_code_rows,
 ]
 
 

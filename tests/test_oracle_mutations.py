@@ -62,6 +62,16 @@ MUTANTS = [
     ("e2m1 mantissa weight", "ldexp(1.0 + m * 0.5, e - 1)", "ldexp(1.0 + m * 0.25, e - 1)"),
     ("e2m1 subnormal", "mag = m * 0.5;", "mag = m * 1.0;"),
     ("e2m1 sign dropped", "return sign ? -mag : mag;", "return mag;"),
+    ("e4m3 exponent bias", "ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    ("e4m3 mantissa width", "ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 16.0, e - 7)"),
+    ("e4m3 subnormal exponent", "ldexp(m / 8.0, -6)", "ldexp(m / 8.0, -7)"),
+    ("e4m3 NaN code finite", "if (e == 15 && m == 7)\n        return NAN;", "if (0)\n        return NAN;"),
+    ("e4m3 sign dropped", "    return sign ? -mag : mag;\n}\n\nvoid oracle_projection_fp8",
+     "    return mag;\n}\n\nvoid oracle_projection_fp8"),
+    ("fp8 64-column scale blocks", "Ws[(n / 128) * KB + k / 128]", "Ws[(n / 128) * KB + k / 64 % KB]"),
+    ("fp8 scale per row block only", "Ws[(n / 128) * KB + k / 128]", "Ws[(n / 128) * KB]"),
+    ("fp8 scale blocks transposed", "Ws[(n / 128) * KB + k / 128]",
+     "Ws[((k / 128) * ((N + 127) / 128) + n / 128) % (KB * ((N + 127) / 128))]"),
     ("e8m0 bias", "ldexp(1.0, (int)s - 127)", "ldexp(1.0, (int)s - 128)"),
     ("e8m0 nan code finite", "if (s == 255)\n        return NAN;", "if (0)\n        return NAN;"),
 ]
