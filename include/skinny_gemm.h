@@ -78,10 +78,11 @@ typedef enum {
     SG_KERNEL_GROUPED = 6,      /* grouped per-expert projection                   */
     SG_KERNEL_PREFETCH = 7,     /* side-stream weight prefetch                     */
     SG_KERNEL_ROUTER_TOPK = 8,  /* router top-k expert selection                   */
-    SG_KERNEL_MXFP4 = 9         /* projection with block-scaled 4-bit weights      */
+    SG_KERNEL_MXFP4 = 9,        /* projection with block-scaled 4-bit weights      */
+    SG_KERNEL_FP8 = 10          /* projection with block-scaled 8-bit weights      */
 } sg_kernel;
 
-#define SG_NUM_COUNTERS 10
+#define SG_NUM_COUNTERS 11
 #define SG_MAX_M 64
 
 /* Launch decision for one projection shape.  Produced by skinny_gemm_plan
@@ -218,6 +219,24 @@ sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int
 sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
                             const uint8_t* W_codes, const uint8_t* W_scales, const sg_bf16* r,
                             float* y_f32, sg_bf16* y_bf16, void* stream);
+
+/* Projection with FP8 weights and block scales (low-precision weights: [P]
+ * Experimental setup and Supplementary details, the later evaluation model
+ * ships 4-bit weights; the 8-bit format read here is the block-scaled FP8 of
+ * DeepSeek-V3-style checkpoints).  W_codes [N, K] bytes, OCP E4M3 codes
+ * (bit 7 sign, bits 6..3 exponent with bias 7, bits 2..0 mantissa; exponent
+ * 0 subnormal; 0x7F and 0xFF are NaN; no infinity), row-major.  W_scales
+ * [ceil(N/128), ceil(K/128)] fp32, row-major: w[n,k] = e4m3(code[n,k]) *
+ * W_scales[n/128][k/128].  x [M, K] bf16; fp32 sums; y_f32 and/or y_bf16
+ * [M, N] (at least one); r (nullable) bf16 [M, N] gives the fused residual
+ * y = r + x W^T as for skinny_gemm_residual (y_bf16 may equal r).  A NaN
+ * code or scale makes its outputs NaN.  Limits: 0 <= M <= 4, K % 16 == 0
+ * (else SG_ERR_ALIGN), M * K <= 32768 (x is staged in LDS; else
+ * SG_ERR_UNSUPPORTED), N, K <= 1<<20.  x, W_codes, r and outputs 16-byte
+ * aligned, W_scales 4-byte aligned.  Launches one kernel; allocates nothing. */
+sg_status skinny_gemm_fp8(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
+                          const uint8_t* W_codes, const float* W_scales, const sg_bf16* r,
+                          float* y_f32, sg_bf16* y_bf16, void* stream);
 
 /* One MoE decode step of a layer on one GPU, with the shared expert on its
  * own stream ([P] Method details §3; [F] Partie 1 §3: the shared expert runs

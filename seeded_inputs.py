@@ -81,6 +81,19 @@ def mxfp4_weights(N: int, K: int, seed: int, device: str = "cpu", scale_lo: int 
             random_bytes((N, K // 32), scale_lo, scale_hi, seed + 7919, device))
 
 
+def fp8_weights(N: int, K: int, seed: int, device: str = "cpu", scale_lo: float = 2e-5,
+                scale_hi: float = 1e-4):
+    """(codes uint8 [N, K], scales float32 [ceil(N/128), ceil(K/128)]): random e4m3 weight
+    codes (the two NaN codes 0x7F and 0xFF replaced by 0x00) and uniform block scales."""
+    codes = random_bytes((N, K), 0, 255, seed, device)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    g = _generator(seed + 104729, "cpu")
+    shape = (-(-N // 128), -(-K // 128))
+    scales = (torch.rand(shape, generator=g, dtype=torch.float32) * (scale_hi - scale_lo)
+              + scale_lo).to(device)
+    return codes, scales
+
+
 def bits(t: torch.Tensor):
     """Raw uint16 bit patterns of a bf16 tensor, as a numpy array on the host."""
     assert t.dtype == torch.bfloat16

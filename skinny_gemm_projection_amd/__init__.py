@@ -17,7 +17,7 @@ import torch
 
 from . import _lib
 from ._lib import (KERNEL_NAMES, SG_KERNEL_GEMV, SG_KERNEL_GROUPED, SG_KERNEL_MOE_TABLE,
-                   SG_KERNEL_MXFP4, SG_KERNEL_NONE, SG_KERNEL_PREFETCH, SG_KERNEL_REDUCE,
+                   SG_KERNEL_FP8, SG_KERNEL_MXFP4, SG_KERNEL_NONE, SG_KERNEL_PREFETCH, SG_KERNEL_REDUCE,
                    SG_KERNEL_ROUTER_TOPK,
                    SG_KERNEL_SPLITK_MFMA, SG_KERNEL_SPLITK_VALU, SG_NUM_COUNTERS, SgMoeStep,
                    SgPlan, SkinnyGemmError)
@@ -27,6 +27,7 @@ __all__ = [
     "grouped_skinny_gemm_workspace", "grouped_skinny_gemm", "skinny_gemm_prefetch",
     "skinny_gemm_router_topk", "router_topk", "skinny_moe_step_workspace", "skinny_moe_step",
     "concat_router_shared", "MOE_STEP_MODES", "skinny_gemm_mxfp4", "SG_KERNEL_MXFP4",
+    "skinny_gemm_fp8", "SG_KERNEL_FP8",
     "skinny_gemm_status_str", "skinny_gemm_get_counters", "skinny_gemm_reset_counters",
     "SgPlan", "SkinnyGemmError", "KERNEL_NAMES", "SG_KERNEL_NONE", "SG_KERNEL_GEMV",
     "SG_KERNEL_SPLITK_VALU", "SG_KERNEL_SPLITK_MFMA", "SG_KERNEL_REDUCE", "SG_KERNEL_MOE_TABLE",
@@ -262,6 +263,31 @@ def skinny_gemm_mxfp4(x: torch.Tensor, W_codes: torch.Tensor, W_scales: torch.Te
     st = _c().skinny_gemm_mxfp4(
         M, N, K, _ptr(x, torch.bfloat16, "x", dev), _ptr(W_codes, torch.uint8, "W_codes", dev),
         _ptr(W_scales, torch.uint8, "W_scales", dev), _ptr(r, torch.bfloat16, "r", dev),
+        _ptr(y_f32, torch.float32, "y_f32", dev), _ptr(y_bf16, torch.bfloat16, "y_bf16", dev),
+        _stream(stream))
+    _lib.check(st)
+    return y_f32, y_bf16
+
+
+def skinny_gemm_fp8(x: torch.Tensor, W_codes: torch.Tensor, W_scales: torch.Tensor,
+                    y_f32=None, y_bf16=None, r=None, stream=None):
+    """y = x W^T for FP8 weights: W_codes uint8 [N, K] (OCP E4M3 codes), W_scales float32
+    [ceil(N/128), ceil(K/128)] (one scale per 128 x 128 block); x bf16 [M, K], M <= 4.
+    Writes y_f32 and/or y_bf16 [M, N]; with r (bf16 [M, N]) the fused residual
+    y = r + x W^T.  Allocates y_f32 when no output is given; returns the outputs."""
+    dev = x.device
+    M, K = x.shape
+    N = W_codes.shape[0]
+    if W_codes.shape != (N, K) or W_scales.shape != (-(-N // 128), -(-K // 128)):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, W_codes {tuple(W_codes.shape)}, "
+                         f"W_scales {tuple(W_scales.shape)}")
+    if y_f32 is None and y_bf16 is None:
+        y_f32 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    for t, name in ((y_f32, "y_f32"), (y_bf16, "y_bf16"), (r, "r")):
+        _shape(t, (M, N), name)
+    st = _c().skinny_gemm_fp8(
+        M, N, K, _ptr(x, torch.bfloat16, "x", dev), _ptr(W_codes, torch.uint8, "W_codes", dev),
+        _ptr(W_scales, torch.float32, "W_scales", dev), _ptr(r, torch.bfloat16, "r", dev),
         _ptr(y_f32, torch.float32, "y_f32", dev), _ptr(y_bf16, torch.bfloat16, "y_bf16", dev),
         _stream(stream))
     _lib.check(st)

@@ -25,9 +25,11 @@ SG_KERNEL_GROUPED = 6
 SG_KERNEL_PREFETCH = 7
 SG_KERNEL_ROUTER_TOPK = 8
 SG_KERNEL_MXFP4 = 9
-SG_NUM_COUNTERS = 10
+SG_KERNEL_FP8 = 10
+SG_NUM_COUNTERS = 11
 KERNEL_NAMES = {0: "none", 1: "gemv", 2: "splitk_valu", 3: "splitk_mfma", 4: "reduce",
-                5: "moe_table", 6: "grouped", 7: "prefetch", 8: "router_topk", 9: "mxfp4"}
+                5: "moe_table", 6: "grouped", 7: "prefetch", 8: "router_topk", 9: "mxfp4",
+                10: "fp8"}
 
 
 class SgPlan(ctypes.Structure):
@@ -94,6 +96,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.skinny_gemm_prefetch.argtypes = [p, sz, p]
     lib.skinny_gemm_router_topk.argtypes = [p, i32, i32, i32, p, p, p]
     lib.skinny_gemm_mxfp4.argtypes = [i32, i32, i32, p, p, p, p, p, p, p]
+    lib.skinny_gemm_fp8.argtypes = [i32, i32, i32, p, p, p, p, p, p, p]
     lib.skinny_moe_step_workspace.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.skinny_moe_step_workspace.restype = sz
     lib.skinny_moe_step.argtypes = [ctypes.POINTER(SgMoeStep), p, sz, p, p, p, p]
@@ -105,7 +108,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.skinny_gemm_reset_counters.restype = None
     for name in ("skinny_gemm_plan", "skinny_gemm_plan_force", "skinny_gemm",
                  "skinny_gemm_residual", "grouped_skinny_gemm", "skinny_gemm_prefetch",
-                 "skinny_gemm_router_topk", "skinny_moe_step", "skinny_gemm_mxfp4"):
+                 "skinny_gemm_router_topk", "skinny_moe_step", "skinny_gemm_mxfp4",
+                 "skinny_gemm_fp8"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

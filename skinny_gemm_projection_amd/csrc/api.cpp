@@ -45,6 +45,7 @@ const char* kernel_name(int k) {
         case SG_KERNEL_MOE_TABLE: return "moe_table";
         case SG_KERNEL_GROUPED: return "grouped";
         case SG_KERNEL_PREFETCH: return "prefetch";
+        case SG_KERNEL_FP8: return "fp8";
         case SG_KERNEL_ROUTER_TOPK: return "router_topk";
         case SG_KERNEL_MXFP4: return "mxfp4";
         default: return "?";
@@ -252,6 +253,33 @@ sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
     if (log_enabled())
         std::fprintf(stderr, "[skinny_gemm] mxfp4 M=%d N=%d K=%d %s%s\n", M, N, K,
                      M >= sg::kMxfp4MfmaFromM ? "matrix cores" : "vector ALU",
+                     r ? " residual" : "");
+    return SG_OK;
+}
+
+sg_status skinny_gemm_fp8(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
+                          const uint8_t* W_codes, const float* W_scales, const sg_bf16* r,
+                          float* y_f32, sg_bf16* y_bf16, void* stream) {
+    if (M < 0 || N < 0 || N > (1 << 20) || K < 0 || K > (1 << 20)) return SG_ERR_SHAPE;
+    if (K % 16 != 0) return SG_ERR_ALIGN;
+    if (M > sg::kFp8MaxM || (int64_t)M * K > sg::kFp8MaxMK) return SG_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return SG_OK;
+    if (!y_f32 && !y_bf16) return SG_ERR_NULL;
+    if (K > 0 && (!x || !W_codes || !W_scales)) return SG_ERR_NULL;
+    auto aligned4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+    if (!aligned16(x) || !aligned16(W_codes) || !aligned4(W_scales) || !aligned16(r) ||
+        !aligned16(y_f32) || !aligned16(y_bf16))
+        return SG_ERR_ALIGN;
+    int splits, chunk16, nch;
+    if (!sg::fp8_split(M, K, &splits, &chunk16, &nch)) return SG_ERR_UNSUPPORTED;
+    (void)hipGetLastError();
+    const sg::Epilogue ep{nullptr, y_f32, y_bf16, r};
+    if (sg::launch_fp8(M, N, K, x, W_codes, W_scales, ep, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return SG_ERR_HIP;
+    count(SG_KERNEL_FP8);
+    if (log_enabled())
+        std::fprintf(stderr, "[skinny_gemm] fp8 M=%d N=%d K=%d split_k=%d%s\n", M, N, K, splits,
                      r ? " residual" : "");
     return SG_OK;
 }

@@ -1,0 +1,250 @@
+// fp8.hip -- projection with 8-bit float (e4m3) weights and one fp32 scale per
+// 128 x 128 block of W, on gfx950.
+//
+// Small-batch decode streams every weight once, so fewer weight bytes is time
+// saved ("Hyper Optimizing Kimi K3 in vLLM" deepnotes page, Experimental setup
+// and Supplementary details: the later evaluation model ships low-precision
+// weights).  8-bit weights halve the bf16 stream.  The format read here is the
+// block-scaled FP8 of DeepSeek-V3-style checkpoints (a reading; the pages name
+// only a 4-bit format): OCP E4M3 codes, W [N, K] one byte each, and scales
+// [ceil(N/128), ceil(K/128)] fp32, w[n,k] = e4m3(code) * scale[n/128][k/128].
+//
+// Mapping (the bf16 row-streaming kernel's, with 16 codes a lane).  A wave
+// owns one K chunk of R rows: lane l loads the 16-byte units c*64 + l of the
+// chunk of each row (1 KB of one row per load instruction, non-temporal, ragged
+// tails read zero through the buffer bounds).  x is staged once per workgroup
+// in LDS and each wave keeps the 16 activations of each of its units in
+// registers.  A unit's codes become bf16 pairs with v_cvt_scalef32_pk_bf16_fp8
+// (scale 1: exact, every e4m3 value is a bf16 value) and meet their x pairs in
+// v_dot2; the unit's sum is multiplied by its block scale (a unit of 16 codes
+// never straddles a 128-column block) and accumulated in fp32.  R divides 128
+// and groups start at multiples of R, so the R rows of a group share their
+// row block of scales.  The R*M lane sums are reduced by the lane
+// reduce-scatter; a team of S waves (one K chunk each) adds its partials in
+// LDS in ascending chunk order, and the first wave runs the epilogue.
+#include "launch.h"
+
+namespace sg {
+
+namespace {
+
+constexpr int kUnitCodes = 16;  // e4m3 codes per 16-byte lane load
+constexpr int kFp8Rows = 4;     // rows per wave iteration (divides 128)
+
+constexpr int pad4(int v) { return (v + 3) / 4 * 4; }
+constexpr int team_block_waves(int S) { return S > kWavesPerBlock ? S : kWavesPerBlock; }
+
+// Sum of one 16-code unit times its 16 activations (two 16-byte pieces of x):
+// dword d of the codes holds elements 4d..4d+3, low byte first; x dword j
+// holds elements 2j, 2j+1.
+__device__ __forceinline__ float dot_unit(const uint4 w, const uint4 xa, const uint4 xb) {
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t xd[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[d], 1.0f, false);
+        const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[d], 1.0f, true);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xd[2 * d]), lo, acc,
+                                              false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xd[2 * d + 1]), hi,
+                                              acc, false);
+    }
+    return acc;
+}
+
+template <int M, int NCH, int S>
+__global__ __launch_bounds__(kWave * team_block_waves(S)) void fp8_rowdot_kernel(
+    const uint4* __restrict__ x, const uint4* __restrict__ Wq, const float* __restrict__ Ws,
+    int N, int K16, int KB, int chunk16, int iters, Epilogue ep) {
+    constexpr int R = kFp8Rows;
+    constexpr int kWaves = team_block_waves(S);
+    constexpr int kTeams = kWaves / S;
+    constexpr int V = pad4(R * M);
+    __shared__ float red[2][kTeams][S][V];
+    extern __shared__ uint4 xs[];  // x [M, 2*K16]: 16-byte pieces of 8 bf16
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wib = wave_id_in_block();
+    const int team_in_block = wib / S;
+    const int member = wib % S;
+    const int team = blockIdx.x * kTeams + team_in_block;
+    const int teams = gridDim.x * kTeams;
+    const int u0 = member * chunk16;                 // first unit of this wave's chunk
+    const int len = max(0, min(K16 - u0, chunk16));  // units in the chunk
+    const int K8 = 2 * K16;                          // x pieces per row
+
+    const int total = M * K8;
+    for (int i = threadIdx.x; i < total; i += kWave * kWaves) xs[i] = x[i];
+    __syncthreads();
+    uint4 xr[M][NCH][2];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int u = c * kWave + lane;
+            const bool in = u < len;
+            xr[m][c][0] = in ? xs[m * K8 + 2 * (u0 + u)] : make_uint4(0, 0, 0, 0);
+            xr[m][c][1] = in ? xs[m * K8 + 2 * (u0 + u) + 1] : make_uint4(0, 0, 0, 0);
+        }
+
+    const int groups = (N + R - 1) / R;
+    for (int it = 0; it < iters; ++it) {
+        const int g = team + it * teams;
+        const int n0 = g * R;
+        float acc[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] = 0.0f;
+        if (g < groups) {
+            // the group's rows share one 128-row block of scales
+            const float* __restrict__ srow = Ws + (int64_t)(n0 / 128) * KB;
+            float sc[NCH];
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int u = c * kWave + lane;
+                sc[c] = u < len ? srow[(u0 + u) / 8] : 0.0f;  // 8 units = 128 columns
+            }
+            uint4 wr[R][NCH];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int n = n0 + r;
+                const rsrc_t rs = make_rsrc(Wq + (int64_t)min(n, N - 1) * K16 + u0,
+                                            n < N ? (uint32_t)len * 16u : 0u);
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+                    wr[r][c] = load16<kStream>(rs, (uint32_t)(c * kWave + lane) * 16u);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    float a = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c)
+                        a = fmaf(dot_unit(wr[r][c], xr[m][c][0], xr[m][c][1]), sc[c], a);
+                    acc[r * M + m] = a;
+                }
+        }
+        const float tot = reduce_scatter<V>(acc, lane);
+        const int v = scatter_index<V>(lane);
+        const bool mine = v >= 0 && v < R * M;
+        const int r = mine ? v / M : 0;
+        const int m = mine ? v - r * M : 0;
+        const int n = n0 + r;
+        const bool live = mine && g < groups && n < N;
+        if (S == 1) {
+            if (live) store_final(ep, (int64_t)m * N + n, tot);
+        } else {
+            // the S chunk partials added in ascending chunk order
+            const int buf = it & 1;
+            if (mine) red[buf][team_in_block][member][v] = tot;
+            __syncthreads();
+            if (member == 0 && live) {
+                float sum = red[buf][team_in_block][0][v];
+#pragma unroll
+                for (int s = 1; s < S; ++s) sum += red[buf][team_in_block][s][v];
+                store_final(ep, (int64_t)m * N + n, sum);
+            }
+        }
+    }
+}
+
+// Lane loads per row (x registers: 8*M*NCH VGPRs) allowed at batch size M.
+constexpr int fp8_nch_cap(int M) { return M == 1 ? 8 : (M == 2 ? 4 : 2); }
+
+constexpr int kResident = 2048;  // 256 CUs x 8 waves
+
+template <int M, int NCH, int S>
+hipError_t launch_mns(int N, int K16, int chunk16, const void* x, const void* Wq,
+                      const float* Ws, const Epilogue& ep, hipStream_t stream) {
+    constexpr int kTeams = team_block_waves(S) / S;
+    const int groups = (N + kFp8Rows - 1) / kFp8Rows;
+    const int cap = kResident / S;
+    int teams = groups < cap ? groups : cap;
+    const int its = (groups + teams - 1) / teams;
+    teams = (groups + its - 1) / its;  // every team the same number of row groups
+    const int grid = (teams + kTeams - 1) / kTeams;
+    const int iters = (groups + grid * kTeams - 1) / (grid * kTeams);
+    const int KB = (K16 * kUnitCodes + 127) / 128;
+    const size_t lds = (size_t)M * 2 * K16 * 16;  // x staged: at most 64 KB
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&fp8_rowdot_kernel<M, NCH, S>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    fp8_rowdot_kernel<M, NCH, S><<<grid, kWave * team_block_waves(S), lds, stream>>>(
+        static_cast<const uint4*>(x), static_cast<const uint4*>(Wq), Ws, N, K16, KB, chunk16,
+        iters, ep);
+    return hipGetLastError();
+}
+
+template <int M, int NCH>
+hipError_t launch_mn(int S, int N, int K16, int chunk16, const void* x, const void* Wq,
+                     const float* Ws, const Epilogue& ep, hipStream_t stream) {
+    switch (S) {
+        case 1: return launch_mns<M, NCH, 1>(N, K16, chunk16, x, Wq, Ws, ep, stream);
+        case 2: return launch_mns<M, NCH, 2>(N, K16, chunk16, x, Wq, Ws, ep, stream);
+        case 4: return launch_mns<M, NCH, 4>(N, K16, chunk16, x, Wq, Ws, ep, stream);
+        case 8: return launch_mns<M, NCH, 8>(N, K16, chunk16, x, Wq, Ws, ep, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int M>
+hipError_t launch_m(int nch, int S, int N, int K16, int chunk16, const void* x, const void* Wq,
+                    const float* Ws, const Epilogue& ep, hipStream_t stream) {
+    switch (nch) {
+        case 1: return launch_mn<M, 1>(S, N, K16, chunk16, x, Wq, Ws, ep, stream);
+        case 2: return launch_mn<M, 2>(S, N, K16, chunk16, x, Wq, Ws, ep, stream);
+        case 4:
+            if constexpr (fp8_nch_cap(M) >= 4)
+                return launch_mn<M, 4>(S, N, K16, chunk16, x, Wq, Ws, ep, stream);
+            break;
+        case 8:
+            if constexpr (fp8_nch_cap(M) >= 8)
+                return launch_mn<M, 8>(S, N, K16, chunk16, x, Wq, Ws, ep, stream);
+            break;
+        default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
+int next_pow2(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+}  // namespace
+
+bool fp8_split(int M, int K, int* splits, int* chunk16, int* nch) {
+    if (M < 1 || M > kFp8MaxM || K % kUnitCodes != 0 || (int64_t)M * K > kFp8MaxMK) return false;
+    const int K16 = K / kUnitCodes;
+    for (int S = 1; S <= 8; S *= 2) {
+        // chunks of whole 128-byte lines (8 units)
+        const int c16 = (K16 + 8 * S - 1) / (8 * S) * 8;
+        const int n = next_pow2((c16 + kWave - 1) / kWave);
+        if (n <= fp8_nch_cap(M) && (S == 1 || (int64_t)(S - 1) * c16 < K16)) {
+            *splits = S;
+            *chunk16 = c16;
+            *nch = n < 1 ? 1 : n;
+            return true;
+        }
+    }
+    return false;
+}
+
+hipError_t launch_fp8(int M, int N, int K, const void* x, const void* Wq, const float* Ws,
+                      const Epilogue& ep, hipStream_t stream) {
+    int S, chunk16, nch;
+    if (!fp8_split(M, K, &S, &chunk16, &nch)) return hipErrorInvalidValue;
+    const int K16 = K / kUnitCodes;
+    switch (M) {
+        case 1: return launch_m<1>(nch, S, N, K16, chunk16, x, Wq, Ws, ep, stream);
+        case 2: return launch_m<2>(nch, S, N, K16, chunk16, x, Wq, Ws, ep, stream);
+        case 3: return launch_m<3>(nch, S, N, K16, chunk16, x, Wq, Ws, ep, stream);
+        case 4: return launch_m<4>(nch, S, N, K16, chunk16, x, Wq, Ws, ep, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace sg

@@ -106,6 +106,17 @@ hipError_t launch_grouped(const void* x, int T, const void* W, int E, int N, int
 
 hipError_t launch_prefetch(const void* W, size_t bytes, hipStream_t stream);
 
+// Projection with FP8 e4m3 weights: codes [N, K], fp32 scales [ceil(N/128),
+// ceil(K/128)] (one per 128 x 128 block).  1 <= M <= kFp8MaxM, K % 16 == 0,
+// M * K <= kFp8MaxMK (x staged in LDS).  fp8_split: the K split (S waves a
+// team, chunk in 16-code units, loads per row) the kernel runs, false if the
+// shape is outside those limits.
+constexpr int kFp8MaxM = 4;
+constexpr int64_t kFp8MaxMK = 32768;
+bool fp8_split(int M, int K, int* splits, int* chunk16, int* nch);
+hipError_t launch_fp8(int M, int N, int K, const void* x, const void* Wq, const float* Ws,
+                      const Epilogue& ep, hipStream_t stream);
+
 // Projection with MXFP4 weights (1 <= M <= kMxfp4MaxM, K % 32 == 0):
 // Wq [N, K/2] e2m1 codes, Ws [N, K/32] e8m0 scales.  Below kMxfp4MfmaFromM
 // rows the VALU kernel runs; mxfp4_split gives its blocks per lane and team

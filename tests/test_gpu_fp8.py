@@ -1,0 +1,142 @@
+"""GPU parity of the projection with FP8 weights (skinny_gemm_fp8: e4m3 codes, one fp32
+scale per 128 x 128 block) through the C ABI, against oracle_projection_fp8 on the same
+seeded codes and scales: fp32 |got - ref| <= 1e-3 * A, bf16 adds 2^-8 |ref|, the
+residual adds 2^-23 |r + y|.  Integer-valued activations and weights with power-of-two
+scales are bit-exact (every product and partial sum is exact in fp32)."""
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as si
+import skinny_gemm_projection_amd as sg
+from gpu_common import (DEV, announce, bits, check_bf16, check_exact, check_f32, counters_delta,
+                        orc, sample_rows)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def run(x, codes, scales, r=None, f32=True, bf16=True):
+    M, N = x.shape[0], codes.shape[0]
+    y32 = torch.full((M, N), -7.0, device=DEV) if f32 else None
+    y16 = torch.full((M, N), -7.0, device=DEV, dtype=torch.bfloat16) if bf16 else None
+    before = sg.skinny_gemm_get_counters()
+    sg.skinny_gemm_fp8(x, codes, scales, y_f32=y32, y_bf16=y16, r=r)
+    torch.cuda.synchronize()
+    d = counters_delta(before, sg.skinny_gemm_get_counters())
+    assert d[sg.SG_KERNEL_FP8] == (1 if M > 0 and N > 0 else 0)
+    return y32, y16
+
+
+SHAPES = [(1, 40, 16), (1, 129, 112), (1, 200, 1040), (1, 77, 8192), (1, 33, 8208),
+          (1, 300, 20000), (2, 50, 4128), (2, 130, 16384), (3, 70, 2080), (3, 129, 7168),
+          (4, 96, 4160), (4, 257, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_fp8_small(M, N, K):
+    announce(f"fp8 M={M} N={N} K={K}")
+    x = si.normal_bf16((M, K), 1.0, 8500 + K + M, DEV)
+    codes, scales = si.fp8_weights(N, K, 8600 + N + K, DEV)
+    y32, y16 = run(x, codes, scales)
+    ref, A = orc().projection_fp8(bits(x), host(codes), host(scales))
+    check_f32(y32, ref, A, f"fp8 fp32 M={M} N={N} K={K}")
+    check_bf16(y16, ref, A, f"fp8 bf16 M={M} N={N} K={K}")
+    # residual epilogue, in place on the bf16 output
+    r = si.normal_bf16((M, N), 1.0, 8700 + N, DEV)
+    out = r.clone()
+    sg.skinny_gemm_fp8(x, codes, scales, y_bf16=out, r=out)
+    torch.cuda.synchronize()
+    rr = orc().bf16_to_f64(bits(r)).reshape(M, N)
+    check_bf16(out, rr + ref, A, f"fp8 residual M={M} N={N} K={K}")
+    y32b, _ = run(x, codes, scales, bf16=False)
+    assert torch.equal(y32, y32b), "repeat runs bitwise identical"
+
+
+# e4m3 codes of the integers 1..8 (and their negatives: bit 7)
+INT_CODES = [0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50]
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 300, 4096), (2, 129, 8192), (4, 140, 2064)])
+def test_fp8_integer_bit_exact(M, N, K):
+    # integer activations and weights, power-of-two block scales: exact sums
+    announce(f"fp8 integer M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 1000 + N)
+    x = si.integer_bf16((M, K), -3, 3, 8800 + M, DEV)
+    c = np.array(INT_CODES, dtype=np.uint8)[rng.integers(0, 8, (N, K))]
+    c |= (rng.integers(0, 2, (N, K)) * 0x80).astype(np.uint8)
+    codes = torch.from_numpy(c).to(DEV)
+    scales = torch.from_numpy(np.ldexp(1.0, rng.integers(-2, 2, (-(-N // 128), -(-K // 128))))
+                              .astype(np.float32)).to(DEV)
+    y32, y16 = run(x, codes, scales)
+    ref = orc().projection_fp8(bits(x), c, host(scales), with_scale=False)
+    check_exact(y32, ref, f"fp8 integer M={M}")
+    assert np.array_equal(bits(y16), orc().encode_bf16(ref)), "bf16 output bit-exact"
+
+
+def test_fp8_nan_code_and_scale():
+    M, N, K = 2, 300, 512
+    x = si.normal_bf16((M, K), 1.0, 8900, DEV)
+    codes, scales = si.fp8_weights(N, K, 8901, DEV)
+    codes[5, 17] = 0x7F   # NaN code: row 5
+    codes[200, 300] = 0xFF  # NaN code: row 200
+    scales[2, 1] = float("nan")  # rows 256..299 (every k block 1 column)
+    announce("fp8 NaN code and scale")
+    y32, _ = run(x, codes, scales, bf16=False)
+    ref, A = orc().projection_fp8(bits(x), host(codes), host(scales))
+    nan_rows = {5, 200} | set(range(256, 300))
+    got_nan = {n for n in range(N) if torch.isnan(y32[:, n]).all()}
+    assert got_nan == nan_rows, sorted(got_nan ^ nan_rows)
+    assert set(np.where(np.isnan(ref).all(axis=0))[0].tolist()) == nan_rows
+    keep = torch.as_tensor([n for n in range(N) if n not in nan_rows], device=DEV)
+    kh = keep.cpu().numpy()
+    check_f32(y32[:, keep], ref[:, kh], A[:, kh], "fp8 rows without NaN")
+
+
+def test_fp8_rejections_touch_nothing():
+    x5 = si.normal_bf16((5, 64), 1.0, 1, DEV)
+    codes, scales = si.fp8_weights(8, 64, 2, DEV)
+    y = torch.full((5, 8), -7.0, device=DEV)
+    with pytest.raises(sg.SkinnyGemmError) as e:
+        sg.skinny_gemm_fp8(x5, codes, scales, y_f32=y)  # M > 4
+    assert e.value.status == 3
+    x = si.normal_bf16((4, 16384), 1.0, 3, DEV)
+    c2, s2 = si.fp8_weights(8, 16384, 4, DEV)
+    y4 = torch.full((4, 8), -7.0, device=DEV)
+    with pytest.raises(sg.SkinnyGemmError) as e:
+        sg.skinny_gemm_fp8(x, c2, s2, y_f32=y4)  # M * K > 32768
+    assert e.value.status == 3
+    st = sg._c().skinny_gemm_fp8(1, 8, 24, x.data_ptr(), c2.data_ptr(), s2.data_ptr(), None,
+                                 y4.data_ptr(), None, None)  # K % 16
+    assert st == 4
+    torch.cuda.synchronize()
+    assert (y == -7.0).all() and (y4 == -7.0).all(), "rejected calls write nothing"
+
+
+def test_fp8_empty():
+    x = si.normal_bf16((1, 0), 1.0, 5, DEV)
+    codes = torch.empty((10, 0), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((1, 0), dtype=torch.float32, device=DEV)
+    y32, _ = run(x, codes, scales, bf16=False)
+    assert (y32 == 0).all(), "K = 0: zero sums"
+
+
+@pytest.mark.parametrize("M,N,K,residual", [(1, 8192, 7168, False), (2, 8192, 7168, False),
+                                            (4, 4096, 7168, False), (1, 7168, 8192, True)])
+def test_fp8_full_size_sampled(M, N, K, residual):
+    announce(f"fp8 full M={M} N={N} K={K} residual={residual}")
+    x = si.normal_bf16((M, K), 1.0, 9000 + M, DEV)
+    codes, scales = si.fp8_weights(N, K, 9100 + N, DEV)
+    r = si.normal_bf16((M, N), 1.0, 9200 + M, DEV) if residual else None
+    y32, y16 = run(x, codes, scales, r=r)
+    c, s, xb = host(codes), host(scales), bits(x)
+    for n in sample_rows(N, 48, 9300 + M):
+        ref, A = orc().projection_fp8(xb, c[n:n + 1], s[n // 128:n // 128 + 1])
+        if residual:
+            ref = ref + orc().bf16_to_f64(bits(r[:, n:n + 1])).reshape(M, 1)
+        check_f32(y32[:, n:n + 1], ref, A, f"fp8 full row {n}", extra=2.0 ** -23 * np.abs(ref))
+        check_bf16(y16[:, n:n + 1], ref, A, f"fp8 full row {n} bf16")
