@@ -506,6 +506,42 @@ def sweep(torch, sg, si, L, cyc, reps=40):
         del ring
     torch.cuda.empty_cache()
 
+    # FP8 e4m3 weights with 128 x 128 fp32 block scales: half the bf16 weight bytes; a ring
+    # of code/scale copies larger than 2 x MALL per shape
+    for label, Ms, N, K, residual in (("fp8 8192x7168", (1, 2), 8192, 7168, False),
+                                      ("fp8 4096x7168", (4,), 4096, 7168, False),
+                                      ("fp8 residual 7168x8192", (1,), 7168, 8192, True)):
+        codes, scales = si.fp8_weights(N, K, si.seed_for(7, si.TAG_W) + N, dev)
+        per_copy = codes.numel() + scales.numel() * 4
+        copies = max(1, math.ceil(RING_MIN_BYTES / per_copy))
+        ring = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(copies - 1)]
+        for M in Ms:
+            x = si.normal_bf16((M, K), 1.0, si.seed_for(7, si.TAG_X) + M, dev)
+            r = si.normal_bf16((M, N), 1.0, si.seed_for(7, si.TAG_R) + M, dev) if residual else None
+            y32 = None if residual else torch.empty((M, N), device=dev)
+            y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+            def f8(cw, sw, x=x, r=r, y32=y32, y16=y16, M=M, N=N, K=K):
+                args = (M, N, K, x.data_ptr(), cw.data_ptr(), sw.data_ptr(),
+                        r.data_ptr() if r is not None else None,
+                        y32.data_ptr() if y32 is not None else None, y16.data_ptr(), L.sp)
+
+                def go():
+                    st = c.skinny_gemm_fp8(*args)
+                    if st:
+                        raise RuntimeError(sg.skinny_gemm_status_str(st))
+                return go
+            per = timed_calls(torch, [f8(cw, sw) for cw, sw in ring], reps, cyc)
+            nbytes = N * K + scales.numel() * 4 + M * K * 2 + M * N * 2 * (2 if residual else 1) + \
+                (0 if residual else M * N * 4)
+            us = 1e3 * per
+            gbs = nbytes / (per * 1e-3) / 1e9
+            rows.append({"workload": label, "M": M, "N": N, "K": K, "plan": "fp8_rowdot",
+                         "us": round(us, 3), "GBps": round(gbs, 1),
+                         "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
+        del ring
+    torch.cuda.empty_cache()
+
     # router: scores y = x W_r^T (E=384 experts, K=7168, fp32) and their top-8 per token
     E, K, k = 384, 7168, 8
     Wr = si.normal_bf16((E, K), 0.02, si.seed_for(5, si.TAG_W) + 99, dev)
@@ -827,6 +863,20 @@ def profile_workloads(torch, sg, si, L, manifest_path, reps=3):
             nbytes = N * K // 2 + N * K // 32 + M * K * 2 + M * N * 6
             run(label, M, N, K, "mxfp4_mfma" if M >= 9 else "mxfp4_rowdot",
                 [mx(cw, sw) for cw, sw in ring], nbytes)
+        del ring
+    # FP8 weights (e4m3 codes, 128 x 128 block scales)
+    for label, Ms, N, K in (("fp8 8192x7168", (1, 2), 8192, 7168), ("fp8 4096x7168", (4,), 4096, 7168)):
+        codes, scales = si.fp8_weights(N, K, 21, dev)
+        ring = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(reps - 1)]
+        for M in Ms:
+            x = si.normal_bf16((M, K), 1.0, 22, dev)
+            y32 = torch.empty((M, N), device=dev)
+            y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+            def f8(cw, sw, x=x, y32=y32, y16=y16):
+                return lambda: sg.skinny_gemm_fp8(x, cw, sw, y_f32=y32, y_bf16=y16)
+            nbytes = N * K + scales.numel() * 4 + M * K * 2 + M * N * 6
+            run(label, M, N, K, "fp8_rowdot", [f8(cw, sw) for cw, sw in ring], nbytes)
         del ring
     # router scores + top-8 (E = 384, K = 7168)
     E, K, k = 384, 7168, 8
