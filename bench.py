@@ -448,6 +448,23 @@ def sweep(torch, sg, si, L, cyc, reps=40):
             rows[-1]["us_graph"] = graph_us(
                 torch, sg, lambda L2, p=p, x=x, y32=y32, ws=ws:
                 [L2.projection(p, x, w, y32, None, ws) for w in ring], y32)
+    # the same shapes at each split factor the workload names, S in {2, 4, 8, 16} (vector ALU
+    # below 8 rows, matrix cores from 8; the library picks the reduction and the row tiling)
+    for M in (4, 8, 16, 32, 64):
+        x = si.normal_bf16((M, K), 1.0, si.seed_for(3, si.TAG_X) + M, dev)
+        y32 = torch.empty((M, N), device=dev)
+        kernel = sg.SG_KERNEL_SPLITK_VALU if M < 8 else sg.SG_KERNEL_SPLITK_MFMA
+        for S in (2, 4, 8, 16):
+            try:
+                p = sg.skinny_gemm_plan_force(M, N, K, kernel, S)
+            except sg.SkinnyGemmError:
+                continue
+            ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+            per = timed_calls(torch, [L.projection(p, x, w, y32, None, ws) for w in ring], reps,
+                              cyc)
+            record("split-K 4096x7168, forced split", M, N, K,
+                   f"{plan_desc(p)} tile={p.tile_n} two_pass={p.two_pass}", per,
+                   proj_bytes(M, N, K, bf16=False))
     del ring
 
     # fused output projection + residual, K=8192, N=7168, bf16 out
