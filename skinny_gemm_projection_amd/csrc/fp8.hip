@@ -12,9 +12,12 @@
 // Mapping (the bf16 row-streaming kernel's, with 16 codes a lane).  A wave
 // owns one K chunk of R rows: lane l loads the 16-byte units c*64 + l of the
 // chunk of each row (1 KB of one row per load instruction, non-temporal, ragged
-// tails read zero through the buffer bounds).  x is staged once per workgroup
-// in LDS and each wave keeps the 16 activations of each of its units in
-// registers.  A unit's codes become bf16 pairs with v_cvt_scalef32_pk_bf16_fp8
+// tails read zero through the buffer bounds).  Each wave keeps the 16
+// activations of each of its units in registers: at M <= 2 x is staged once
+// per workgroup in LDS and read from there, from M = 3 (K split over teams of
+// waves) each wave loads its chunk of x straight from L2, which measured
+// faster (4096 x 7168, M = 4: 9.7 -> 9.0 us; at M = 2 the LDS staging was
+// faster, 12.5 against 13.1 us at 8192 x 7168).  A unit's codes become bf16 pairs with v_cvt_scalef32_pk_bf16_fp8
 // (scale 1: exact, every e4m3 value is a bf16 value) and meet their x pairs in
 // v_dot2; the unit's sum is multiplied by its block scale (a unit of 16 codes
 // never straddles a 128-column block) and accumulated in fp32.  R divides 128
@@ -33,6 +36,8 @@ constexpr int kFp8Rows = 4;     // rows per wave iteration (divides 128)
 
 constexpr int pad4(int v) { return (v + 3) / 4 * 4; }
 constexpr int team_block_waves(int S) { return S > kWavesPerBlock ? S : kWavesPerBlock; }
+// x of the batch staged in LDS (M <= 2) or loaded by each wave from L2
+constexpr bool fp8_x_in_lds(int M) { return M <= 2; }
 
 // Sum of one 16-code unit times its 16 activations (two 16-byte pieces of x):
 // dword d of the codes holds elements 4d..4d+3, low byte first; x dword j
@@ -74,19 +79,33 @@ __global__ __launch_bounds__(kWave * team_block_waves(S)) void fp8_rowdot_kernel
     const int len = max(0, min(K16 - u0, chunk16));  // units in the chunk
     const int K8 = 2 * K16;                          // x pieces per row
 
-    const int total = M * K8;
-    for (int i = threadIdx.x; i < total; i += kWave * kWaves) xs[i] = x[i];
-    __syncthreads();
     uint4 xr[M][NCH][2];
+    if constexpr (fp8_x_in_lds(M)) {
+        const int total = M * K8;
+        for (int i = threadIdx.x; i < total; i += kWave * kWaves) xs[i] = x[i];
+        __syncthreads();
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+        for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int u = c * kWave + lane;
-            const bool in = u < len;
-            xr[m][c][0] = in ? xs[m * K8 + 2 * (u0 + u)] : make_uint4(0, 0, 0, 0);
-            xr[m][c][1] = in ? xs[m * K8 + 2 * (u0 + u) + 1] : make_uint4(0, 0, 0, 0);
+            for (int c = 0; c < NCH; ++c) {
+                const int u = c * kWave + lane;
+                const bool in = u < len;
+                xr[m][c][0] = in ? xs[m * K8 + 2 * (u0 + u)] : make_uint4(0, 0, 0, 0);
+                xr[m][c][1] = in ? xs[m * K8 + 2 * (u0 + u) + 1] : make_uint4(0, 0, 0, 0);
+            }
+    } else {
+        // the 32 bytes of x of each of the lane's units, zero past the chunk
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const rsrc_t rx = make_rsrc(x + (int64_t)m * K8 + 2 * u0, (uint32_t)len * 32u);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const uint32_t off = (uint32_t)(c * kWave + lane) * 32u;
+                xr[m][c][0] = load16<kCached>(rx, off);
+                xr[m][c][1] = load16<kCached>(rx, off + 16u);
+            }
         }
+    }
 
     const int groups = (N + R - 1) / R;
     for (int it = 0; it < iters; ++it) {
@@ -166,7 +185,7 @@ hipError_t launch_mns(int N, int K16, int chunk16, const void* x, const void* Wq
     const int grid = (teams + kTeams - 1) / kTeams;
     const int iters = (groups + grid * kTeams - 1) / (grid * kTeams);
     const int KB = (K16 * kUnitCodes + 127) / 128;
-    const size_t lds = (size_t)M * 2 * K16 * 16;  // x staged: at most 64 KB
+    const size_t lds = fp8_x_in_lds(M) ? (size_t)M * 2 * K16 * 16 : 0;  // at most 64 KB
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&fp8_rowdot_kernel<M, NCH, S>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -108,7 +108,8 @@ hipError_t launch_prefetch(const void* W, size_t bytes, hipStream_t stream);
 
 // Projection with FP8 e4m3 weights: codes [N, K], fp32 scales [ceil(N/128),
 // ceil(K/128)] (one per 128 x 128 block).  1 <= M <= kFp8MaxM, K % 16 == 0,
-// M * K <= kFp8MaxMK (x staged in LDS).  fp8_split: the K split (S waves a
+// M * K <= kFp8MaxMK (the LDS that stages x at M <= 2, the x registers of
+// a team of at most 8 waves above).  fp8_split: the K split (S waves a
 // team, chunk in 16-code units, loads per row) the kernel runs, false if the
 // shape is outside those limits.
 constexpr int kFp8MaxM = 4;
