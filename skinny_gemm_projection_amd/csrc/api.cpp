@@ -262,7 +262,7 @@ sg_status skinny_gemm_fp8(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
                           float* y_f32, sg_bf16* y_bf16, void* stream) {
     if (M < 0 || N < 0 || N > (1 << 20) || K < 0 || K > (1 << 20)) return SG_ERR_SHAPE;
     if (K % 16 != 0) return SG_ERR_ALIGN;
-    if (M > sg::kFp8MaxM || (int64_t)M * K > sg::kFp8MaxMK) return SG_ERR_UNSUPPORTED;
+    if (M > sg::kFp8MaxM || (M > 0 && !sg::fp8_size_ok(M, K))) return SG_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return SG_OK;
     if (!y_f32 && !y_bf16) return SG_ERR_NULL;
     if (K > 0 && (!x || !W_codes || !W_scales)) return SG_ERR_NULL;

@@ -235,8 +235,13 @@ int next_pow2(int v) {
 
 }  // namespace
 
+bool fp8_size_ok(int M, int K) {
+    if (M < 1 || M > kFp8MaxM || K < 0) return false;
+    return fp8_x_in_lds(M) ? (int64_t)M * K <= kFp8MaxMK : K <= kFp8MaxKRegs;
+}
+
 bool fp8_split(int M, int K, int* splits, int* chunk16, int* nch) {
-    if (M < 1 || M > kFp8MaxM || K % kUnitCodes != 0 || (int64_t)M * K > kFp8MaxMK) return false;
+    if (!fp8_size_ok(M, K) || K % kUnitCodes != 0) return false;
     const int K16 = K / kUnitCodes;
     for (int S = 1; S <= 8; S *= 2) {
         // chunks of whole 128-byte lines (8 units)

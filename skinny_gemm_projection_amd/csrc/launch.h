@@ -107,13 +107,16 @@ hipError_t launch_grouped(const void* x, int T, const void* W, int E, int N, int
 hipError_t launch_prefetch(const void* W, size_t bytes, hipStream_t stream);
 
 // Projection with FP8 e4m3 weights: codes [N, K], fp32 scales [ceil(N/128),
-// ceil(K/128)] (one per 128 x 128 block).  1 <= M <= kFp8MaxM, K % 16 == 0,
-// M * K <= kFp8MaxMK (the LDS that stages x at M <= 2, the x registers of
-// a team of at most 8 waves above).  fp8_split: the K split (S waves a
+// ceil(K/128)] (one per 128 x 128 block).  1 <= M <= kFp8MaxM, K % 16 == 0;
+// at M <= 2, M * K <= kFp8MaxMK (the LDS that stages x), from M = 3,
+// K <= kFp8MaxKRegs (x in the registers of a team of at most 8 waves).
+// fp8_split: the K split (S waves a
 // team, chunk in 16-code units, loads per row) the kernel runs, false if the
 // shape is outside those limits.
 constexpr int kFp8MaxM = 4;
 constexpr int64_t kFp8MaxMK = 32768;
+constexpr int kFp8MaxKRegs = 16384;
+bool fp8_size_ok(int M, int K);
 bool fp8_split(int M, int K, int* splits, int* chunk16, int* nch);
 hipError_t launch_fp8(int M, int N, int K, const void* x, const void* Wq, const float* Ws,
                       const Epilogue& ep, hipStream_t stream);

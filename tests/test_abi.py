@@ -257,3 +257,26 @@ def test_grouped_and_prefetch_errors_return_before_launch():
     assert c.skinny_gemm_prefetch(A + 8, 32, None) == 4
     assert c.skinny_gemm_prefetch(A, 0, None) == 0
     assert sum(sg.skinny_gemm_get_counters()) == 0
+
+
+@no_gpu_only
+def test_fp8_size_limits_return_before_launch():
+    # status 3 (unsupported) for sizes outside the kernel's x storage, 4 for K % 16;
+    # a size inside the limits gets past those checks and stops at the missing
+    # output (status 1)
+    c = _raw()
+    sg.skinny_gemm_reset_counters()
+    A = 0x10000
+
+    def call(M, K, y=None):
+        return c.skinny_gemm_fp8(M, 8, K, A, A, A, None, y, None, None)
+
+    assert call(5, 64) == 3
+    assert call(1, 32768) == 1 and call(1, 32784) == 3   # M * K <= 32768 (LDS) at M <= 2
+    assert call(2, 16384) == 1 and call(2, 16400) == 3
+    assert call(3, 16384) == 1 and call(3, 16400) == 3   # K <= 16384 (registers) at M = 3, 4
+    assert call(4, 16384) == 1 and call(4, 16400) == 3
+    assert call(1, 24) == 4
+    assert call(0, 64) == 0
+    assert call(4, 16384, y=A + 4) == 4  # misaligned output
+    assert sum(sg.skinny_gemm_get_counters()) == 0

@@ -34,7 +34,9 @@ def run(x, codes, scales, r=None, f32=True, bf16=True):
 
 SHAPES = [(1, 40, 16), (1, 129, 112), (1, 200, 1040), (1, 77, 8192), (1, 33, 8208),
           (1, 300, 20000), (2, 50, 4128), (2, 130, 16384), (3, 70, 2080), (3, 129, 7168),
-          (4, 96, 4160), (4, 257, 8192)]
+          (4, 96, 4160), (4, 257, 8192),
+          # from M = 3 x stays in registers: K up to 16384 (8-wave teams)
+          (3, 140, 12304), (4, 129, 16384), (3, 65, 16384)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -104,17 +106,23 @@ def test_fp8_rejections_touch_nothing():
     with pytest.raises(sg.SkinnyGemmError) as e:
         sg.skinny_gemm_fp8(x5, codes, scales, y_f32=y)  # M > 4
     assert e.value.status == 3
-    x = si.normal_bf16((4, 16384), 1.0, 3, DEV)
-    c2, s2 = si.fp8_weights(8, 16384, 4, DEV)
+    x = si.normal_bf16((4, 16400), 1.0, 3, DEV)
+    c2, s2 = si.fp8_weights(8, 16400, 4, DEV)
     y4 = torch.full((4, 8), -7.0, device=DEV)
     with pytest.raises(sg.SkinnyGemmError) as e:
-        sg.skinny_gemm_fp8(x, c2, s2, y_f32=y4)  # M * K > 32768
+        sg.skinny_gemm_fp8(x, c2, s2, y_f32=y4)  # K > 16384 at M = 4
+    assert e.value.status == 3
+    x2 = si.normal_bf16((2, 16400), 1.0, 5, DEV)
+    y2 = torch.full((2, 8), -7.0, device=DEV)
+    with pytest.raises(sg.SkinnyGemmError) as e:
+        sg.skinny_gemm_fp8(x2, c2, s2, y_f32=y2)  # M * K > 32768 at M = 2
     assert e.value.status == 3
     st = sg._c().skinny_gemm_fp8(1, 8, 24, x.data_ptr(), c2.data_ptr(), s2.data_ptr(), None,
                                  y4.data_ptr(), None, None)  # K % 16
     assert st == 4
     torch.cuda.synchronize()
-    assert (y == -7.0).all() and (y4 == -7.0).all(), "rejected calls write nothing"
+    assert (y == -7.0).all() and (y4 == -7.0).all() and (y2 == -7.0).all(), \
+        "rejected calls write nothing"
 
 
 def test_fp8_empty():
