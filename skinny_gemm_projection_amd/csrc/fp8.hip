@@ -14,10 +14,12 @@
 // chunk of each row (1 KB of one row per load instruction, non-temporal, ragged
 // tails read zero through the buffer bounds).  Each wave keeps the 16
 // activations of each of its units in registers: at M <= 2 x is staged once
-// per workgroup in LDS and read from there, from M = 3 (K split over teams of
+// per workgroup in LDS and read from there; from M = 3 (K split over teams of
 // waves) each wave loads its chunk of x straight from L2, which measured
 // faster (4096 x 7168, M = 4: 9.7 -> 9.0 us; at M = 2 the LDS staging was
-// faster, 12.5 against 13.1 us at 8192 x 7168).  A unit's codes become bf16 pairs with v_cvt_scalef32_pk_bf16_fp8
+// faster, 12.5 against 13.1 us at 8192 x 7168).  Except at M = 1 the first
+// row group's codes are requested right behind x.  A unit's codes become bf16
+// pairs with v_cvt_scalef32_pk_bf16_fp8
 // (scale 1: exact, every e4m3 value is a bf16 value) and meet their x pairs in
 // v_dot2; the unit's sum is multiplied by its block scale (a unit of 16 codes
 // never straddles a 128-column block) and accumulated in fp32.  R divides 128
@@ -79,11 +81,32 @@ __global__ __launch_bounds__(kWave * team_block_waves(S)) void fp8_rowdot_kernel
     const int len = max(0, min(K16 - u0, chunk16));  // units in the chunk
     const int K8 = 2 * K16;                          // x pieces per row
 
+    const int groups = (N + R - 1) / R;
+    uint4 wr[R][NCH];
+    float sc[NCH];
+    // codes and scales of the group of R rows starting at row g * R
+    auto load_group = [&](int g) {
+        const int n0 = g * R;
+        // the group's rows share one 128-row block of scales
+        const float* __restrict__ srow = Ws + (int64_t)(n0 / 128) * KB;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int u = c * kWave + lane;
+            sc[c] = u < len ? srow[(u0 + u) / 8] : 0.0f;  // 8 units = 128 columns
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int n = n0 + r;
+            const rsrc_t rs = make_rsrc(Wq + (int64_t)min(n, N - 1) * K16 + u0,
+                                        n < N ? (uint32_t)len * 16u : 0u);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+                wr[r][c] = load16<kStream>(rs, (uint32_t)(c * kWave + lane) * 16u);
+        }
+    };
+
     uint4 xr[M][NCH][2];
-    if constexpr (fp8_x_in_lds(M)) {
-        const int total = M * K8;
-        for (int i = threadIdx.x; i < total; i += kWave * kWaves) xs[i] = x[i];
-        __syncthreads();
+    auto read_x_lds = [&]() {
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -93,6 +116,34 @@ __global__ __launch_bounds__(kWave * team_block_waves(S)) void fp8_rowdot_kernel
                 xr[m][c][0] = in ? xs[m * K8 + 2 * (u0 + u)] : make_uint4(0, 0, 0, 0);
                 xr[m][c][1] = in ? xs[m * K8 + 2 * (u0 + u) + 1] : make_uint4(0, 0, 0, 0);
             }
+    };
+    if constexpr (M == 1) {
+        // x copied to LDS first, the codes requested after the barrier (the
+        // order below measured slower here: 11.2 -> 12.0 us at 8192 x 7168)
+        const int total = K8;
+        for (int i = threadIdx.x; i < total; i += kWave * kWaves) xs[i] = x[i];
+        __syncthreads();
+        read_x_lds();
+    } else if constexpr (fp8_x_in_lds(M)) {
+        // x into registers first, then the first group's codes behind it:
+        // loads return in order, so the LDS copy waits for x only
+        // (8192 x 7168, M = 2: 12.4 -> 11.8 us)
+        constexpr int kThreads = kWave * kWaves;
+        constexpr int kStage = (2 * M * NCH * S + kWaves - 1) / kWaves;  // >= M*K8 / kThreads
+        const int total = M * K8;
+        const rsrc_t rx = make_rsrc(x, (uint32_t)total * 16u);
+        uint4 stage[kStage];
+#pragma unroll
+        for (int j = 0; j < kStage; ++j)
+            stage[j] = load16<kCached>(rx, (uint32_t)(threadIdx.x + j * kThreads) * 16u);
+        if (team < groups) load_group(team);
+#pragma unroll
+        for (int j = 0; j < kStage; ++j) {
+            const int i = threadIdx.x + j * kThreads;
+            if (i < total) xs[i] = stage[j];
+        }
+        __syncthreads();
+        read_x_lds();
     } else {
         // the 32 bytes of x of each of the lane's units, zero past the chunk
 #pragma unroll
@@ -105,9 +156,9 @@ __global__ __launch_bounds__(kWave * team_block_waves(S)) void fp8_rowdot_kernel
                 xr[m][c][1] = load16<kCached>(rx, off + 16u);
             }
         }
+        if (team < groups) load_group(team);
     }
 
-    const int groups = (N + R - 1) / R;
     for (int it = 0; it < iters; ++it) {
         const int g = team + it * teams;
         const int n0 = g * R;
@@ -115,24 +166,7 @@ __global__ __launch_bounds__(kWave * team_block_waves(S)) void fp8_rowdot_kernel
 #pragma unroll
         for (int v = 0; v < V; ++v) acc[v] = 0.0f;
         if (g < groups) {
-            // the group's rows share one 128-row block of scales
-            const float* __restrict__ srow = Ws + (int64_t)(n0 / 128) * KB;
-            float sc[NCH];
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int u = c * kWave + lane;
-                sc[c] = u < len ? srow[(u0 + u) / 8] : 0.0f;  // 8 units = 128 columns
-            }
-            uint4 wr[R][NCH];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int n = n0 + r;
-                const rsrc_t rs = make_rsrc(Wq + (int64_t)min(n, N - 1) * K16 + u0,
-                                            n < N ? (uint32_t)len * 16u : 0u);
-#pragma unroll
-                for (int c = 0; c < NCH; ++c)
-                    wr[r][c] = load16<kStream>(rs, (uint32_t)(c * kWave + lane) * 16u);
-            }
+            if (M == 1 || it > 0) load_group(g);  // else requested behind x
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
