@@ -526,7 +526,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
     # FP8 e4m3 weights with 128 x 128 fp32 block scales: half the bf16 weight bytes; a ring
     # of code/scale copies larger than 2 x MALL per shape
     for label, Ms, N, K, residual in (("fp8 8192x7168", (1, 2), 8192, 7168, False),
-                                      ("fp8 4096x7168", (4,), 4096, 7168, False),
+                                      ("fp8 4096x7168", (4, 8, 16), 4096, 7168, False),
                                       ("fp8 residual 7168x8192", (1,), 7168, 8192, True)):
         codes, scales = si.fp8_weights(N, K, si.seed_for(7, si.TAG_W) + N, dev)
         per_copy = codes.numel() + scales.numel() * 4
@@ -553,7 +553,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
                 (0 if residual else M * N * 4)
             us = 1e3 * per
             gbs = nbytes / (per * 1e-3) / 1e9
-            rows.append({"workload": label, "M": M, "N": N, "K": K, "plan": "fp8_rowdot",
+            rows.append({"workload": label, "M": M, "N": N, "K": K, "plan": "fp8_mfma" if M >= 5 else "fp8_rowdot",
                          "us": round(us, 3), "GBps": round(gbs, 1),
                          "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
         del ring
@@ -882,7 +882,8 @@ def profile_workloads(torch, sg, si, L, manifest_path, reps=3):
                 [mx(cw, sw) for cw, sw in ring], nbytes)
         del ring
     # FP8 weights (e4m3 codes, 128 x 128 block scales)
-    for label, Ms, N, K in (("fp8 8192x7168", (1, 2), 8192, 7168), ("fp8 4096x7168", (4,), 4096, 7168)):
+    for label, Ms, N, K in (("fp8 8192x7168", (1, 2), 8192, 7168),
+                            ("fp8 4096x7168", (4, 8, 16), 4096, 7168)):
         codes, scales = si.fp8_weights(N, K, 21, dev)
         ring = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(reps - 1)]
         for M in Ms:
@@ -893,7 +894,7 @@ def profile_workloads(torch, sg, si, L, manifest_path, reps=3):
             def f8(cw, sw, x=x, y32=y32, y16=y16):
                 return lambda: sg.skinny_gemm_fp8(x, cw, sw, y_f32=y32, y_bf16=y16)
             nbytes = N * K + scales.numel() * 4 + M * K * 2 + M * N * 6
-            run(label, M, N, K, "fp8_rowdot", [f8(cw, sw) for cw, sw in ring], nbytes)
+            run(label, M, N, K, "fp8_mfma" if M >= 5 else "fp8_rowdot", [f8(cw, sw) for cw, sw in ring], nbytes)
         del ring
     # router scores + top-8 (E = 384, K = 7168)
     E, K, k = 384, 7168, 8

@@ -230,10 +230,14 @@ sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
  * W_scales[n/128][k/128].  x [M, K] bf16; fp32 sums; y_f32 and/or y_bf16
  * [M, N] (at least one); r (nullable) bf16 [M, N] gives the fused residual
  * y = r + x W^T as for skinny_gemm_residual (y_bf16 may equal r).  A NaN
- * code or scale makes its outputs NaN.  Limits: 0 <= M <= 4, K % 16 == 0
+ * code or scale makes its outputs NaN.  M <= 4 runs on the vector ALU,
+ * 5 <= M <= 16 on bf16 matrix cores (codes converted exactly to bf16, each
+ * 128-column window's sum scaled once).  Limits: 0 <= M <= 16, K % 16 == 0
  * (else SG_ERR_ALIGN), M * K <= 32768 at M <= 2 (x staged in LDS) and
- * K <= 16384 at M = 3, 4 (x in registers) (else SG_ERR_UNSUPPORTED), N, K <= 1<<20.  x, W_codes, r and outputs 16-byte
- * aligned, W_scales 4-byte aligned.  Launches one kernel; allocates nothing. */
+ * K <= 16384 at M = 3, 4 (x in registers), any K from M = 5 (matrix
+ * cores) (else SG_ERR_UNSUPPORTED), N, K <= 1<<20.  x, W_codes, r and
+ * outputs 16-byte aligned, W_scales 4-byte aligned.  Launches one kernel;
+ * allocates nothing. */
 sg_status skinny_gemm_fp8(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
                           const uint8_t* W_codes, const float* W_scales, const sg_bf16* r,
                           float* y_f32, sg_bf16* y_bf16, void* stream);

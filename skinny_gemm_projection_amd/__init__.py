@@ -272,7 +272,7 @@ def skinny_gemm_mxfp4(x: torch.Tensor, W_codes: torch.Tensor, W_scales: torch.Te
 def skinny_gemm_fp8(x: torch.Tensor, W_codes: torch.Tensor, W_scales: torch.Tensor,
                     y_f32=None, y_bf16=None, r=None, stream=None):
     """y = x W^T for FP8 weights: W_codes uint8 [N, K] (OCP E4M3 codes), W_scales float32
-    [ceil(N/128), ceil(K/128)] (one scale per 128 x 128 block); x bf16 [M, K], M <= 4.
+    [ceil(N/128), ceil(K/128)] (one scale per 128 x 128 block); x bf16 [M, K], M <= 16.
     Writes y_f32 and/or y_bf16 [M, N]; with r (bf16 [M, N]) the fused residual
     y = r + x W^T.  Allocates y_f32 when no output is given; returns the outputs."""
     dev = x.device

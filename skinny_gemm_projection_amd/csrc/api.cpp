@@ -271,7 +271,7 @@ sg_status skinny_gemm_fp8(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
         !aligned16(y_f32) || !aligned16(y_bf16))
         return SG_ERR_ALIGN;
     int splits, chunk16, nch;
-    if (!sg::fp8_split(M, K, &splits, &chunk16, &nch)) return SG_ERR_UNSUPPORTED;
+    if (!sg::fp8_split(M, N, K, &splits, &chunk16, &nch)) return SG_ERR_UNSUPPORTED;
     (void)hipGetLastError();
     const sg::Epilogue ep{nullptr, y_f32, y_bf16, r};
     if (sg::launch_fp8(M, N, K, x, W_codes, W_scales, ep, static_cast<hipStream_t>(stream)) !=
@@ -279,7 +279,8 @@ sg_status skinny_gemm_fp8(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
         return SG_ERR_HIP;
     count(SG_KERNEL_FP8);
     if (log_enabled())
-        std::fprintf(stderr, "[skinny_gemm] fp8 M=%d N=%d K=%d split_k=%d%s\n", M, N, K, splits,
+        std::fprintf(stderr, "[skinny_gemm] fp8 M=%d N=%d K=%d %s split_k=%d%s\n", M, N, K,
+                     M >= sg::kFp8MfmaFromM ? "matrix cores" : "vector ALU", splits,
                      r ? " residual" : "");
     return SG_OK;
 }

@@ -202,6 +202,111 @@ __global__ __launch_bounds__(kWave * team_block_waves(S)) void fp8_rowdot_kernel
     }
 }
 
+// Matrix-core kernel (kFp8MfmaFromM <= M <= 16: x is one 16-row A tile of
+// v_mfma_f32_16x16x32_bf16, rows past M zero).  A workgroup of S waves owns
+// a 16-row tile of W; wave s takes the 128-column windows [s*chunk_w,
+// (s+1)*chunk_w), D of them in flight.  Lane (col, grp) loads the 32 codes
+// k = 128w + 32grp .. +32 of row n0 + col (two 16-byte loads); k step t of
+// the window takes codes 8t .. 8t+7 of them, converted to bf16 (exact) as
+// the B operand, against x[m][128w + 32grp + 8t .. +8) as the A operand, so
+// A and B agree on the k of every operand slot.  x of a window goes through
+// the wave's LDS tile (4 rows x 256 bytes per load instruction, the piece
+// index XOR-swizzled by row so the operand reads hit 16 different bank
+// groups).  A window lies inside one 128 x 128 scale block (the tile's rows
+// share a row block), so its 4 products are summed first and the sum is
+// multiplied by that one scale.  The S partial tiles are added in LDS in
+// ascending wave order.
+constexpr int kF8Windows = 4;  // windows in flight per wave
+
+template <int S>
+__global__ __launch_bounds__(kWave * S) void fp8_mfma_kernel(
+    const uint4* __restrict__ x, const uint4* __restrict__ Wq, const float* __restrict__ Ws,
+    int M, int N, int K16, int KB, int chunk_w, Epilogue ep) {
+    constexpr int D = kF8Windows;
+    __shared__ f32x4_t red[S > 1 ? S : 1][kWave];
+    __shared__ uint4 xtiles[S][256];  // per wave: x of one window, 16 rows x 16 pieces
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int col = lane & 15, grp = lane >> 4;
+    const int s = wave_id_in_block();
+    const int n0 = blockIdx.x * 16;
+    const int rows = min(16, N - n0);
+    const int K8 = 2 * K16;        // 16-byte pieces of an x row
+    const int KW = (K16 + 7) / 8;  // 128-column windows (8 units of 16 codes)
+    const int w0 = s * chunk_w;
+    const int w1 = min(KW, w0 + chunk_w);
+
+    // wave-uniform descriptors: codes of the tile's rows, and x (rows past M
+    // read zero)
+    const rsrc_t rw = make_rsrc(Wq + (int64_t)n0 * K16, (uint32_t)rows * K16 * 16u);
+    const rsrc_t rx = make_rsrc(x, (uint32_t)M * K8 * 16u);
+    const float* __restrict__ srow = Ws + (int64_t)(n0 / 128) * KB;
+    constexpr uint32_t kOut = 0xFFFFFFF0u;  // past any range: reads zero
+
+    uint4* xt = xtiles[s];
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int wb = w0; wb < w1; wb += D) {
+        uint4 wv[D][2], xa[D][4];
+        float sc[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int w = wb + d;
+            const bool live = w < w1;
+            const int u = 8 * w + 2 * grp;  // first unit of this lane in row col
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const bool ok = live && u + j < K16;
+                wv[d][j] = load16<kStream>(rw, ok ? (uint32_t)(col * K16 + u + j) * 16u : kOut);
+            }
+            sc[d] = live ? srow[w] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * i + grp;
+                const int piece = 16 * w + (col ^ r);  // of the x row
+                const bool ok = live && piece < K8;
+                xa[d][i] = load16<kCached>(rx, ok ? (uint32_t)(r * K8 + piece) * 16u : kOut);
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xt[(4 * i + grp) * 16 + col] = xa[d][i];
+            __builtin_amdgcn_wave_barrier();
+            const uint32_t wd[8] = {wv[d][0].x, wv[d][0].y, wv[d][0].z, wv[d][0].w,
+                                    wv[d][1].x, wv[d][1].y, wv[d][1].z, wv[d][1].w};
+            f32x4_t part = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint4 b = {
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * t], 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * t], 1.0f, true)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * t + 1], 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * t + 1], 1.0f, true))};
+                const uint4 a = xt[col * 16 + ((4 * grp + t) ^ col)];
+                part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                               __builtin_bit_cast(bf16x8_t, b),
+                                                               part, 0, 0, 0);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = fmaf(part[v], sc[d], acc[v]);
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+    if (S > 1) {
+        red[s][lane] = acc;
+        __syncthreads();
+        if (s != 0) return;
+#pragma unroll
+        for (int j = 1; j < S; ++j) acc += red[j][lane];
+    }
+    if (col >= rows) return;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int m = 4 * grp + v;
+        if (m < M) store_final(ep, (int64_t)m * N + n0 + col, acc[v]);
+    }
+}
+
 // Lane loads per row (x registers: 8*M*NCH VGPRs) allowed at batch size M.
 constexpr int fp8_nch_cap(int M) { return M == 1 ? 8 : (M == 2 ? 4 : 2); }
 
@@ -247,7 +352,10 @@ hipError_t launch_m(int nch, int S, int N, int K16, int chunk16, const void* x, 
                     const float* Ws, const Epilogue& ep, hipStream_t stream) {
     switch (nch) {
         case 1: return launch_mn<M, 1>(S, N, K16, chunk16, x, Wq, Ws, ep, stream);
-        case 2: return launch_mn<M, 2>(S, N, K16, chunk16, x, Wq, Ws, ep, stream);
+        case 2:
+            if constexpr (fp8_nch_cap(M) >= 2)
+                return launch_mn<M, 2>(S, N, K16, chunk16, x, Wq, Ws, ep, stream);
+            break;
         case 4:
             if constexpr (fp8_nch_cap(M) >= 4)
                 return launch_mn<M, 4>(S, N, K16, chunk16, x, Wq, Ws, ep, stream);
@@ -269,33 +377,76 @@ int next_pow2(int v) {
 
 }  // namespace
 
-bool fp8_size_ok(int M, int K) {
-    if (M < 1 || M > kFp8MaxM || K < 0) return false;
-    return fp8_x_in_lds(M) ? (int64_t)M * K <= kFp8MaxMK : K <= kFp8MaxKRegs;
+void fp8_mfma_split(int N, int K, int* splits, int* chunk_w) {
+    const int KW = (K / kUnitCodes + 7) / 8;
+    const int tiles = (N + 15) / 16;
+    int S = 1;
+    while (S < 8 && S < KW && tiles * S < kResident) S *= 2;
+    *splits = S;
+    *chunk_w = KW > 0 ? (KW + S - 1) / S : 0;
 }
 
-bool fp8_split(int M, int K, int* splits, int* chunk16, int* nch) {
+bool fp8_size_ok(int M, int K) {
+    if (M < 1 || M > kFp8MaxM || K < 0) return false;
+    if (M >= kFp8MfmaFromM) return true;  // matrix-core kernel: windows split over a team
+    // x in registers: a team of at most 8 waves, NCH units of 16 codes per lane
+    return fp8_x_in_lds(M) ? (int64_t)M * K <= kFp8MaxMK
+                           : K <= 8 * kWave * kUnitCodes * fp8_nch_cap(M);
+}
+
+bool fp8_split(int M, int N, int K, int* splits, int* chunk16, int* nch) {
     if (!fp8_size_ok(M, K) || K % kUnitCodes != 0) return false;
-    const int K16 = K / kUnitCodes;
-    for (int S = 1; S <= 8; S *= 2) {
-        // chunks of whole 128-byte lines (8 units)
-        const int c16 = (K16 + 8 * S - 1) / (8 * S) * 8;
-        const int n = next_pow2((c16 + kWave - 1) / kWave);
-        if (n <= fp8_nch_cap(M) && (S == 1 || (int64_t)(S - 1) * c16 < K16)) {
-            *splits = S;
-            *chunk16 = c16;
-            *nch = n < 1 ? 1 : n;
-            return true;
-        }
+    if (M >= kFp8MfmaFromM) {  // matrix-core kernel: windows of 8 units, nch unused
+        int chunk_w;
+        fp8_mfma_split(N, K, splits, &chunk_w);
+        *chunk16 = 8 * chunk_w;
+        *nch = 0;
+        return true;
     }
+    const int K16 = K / kUnitCodes;
+    // The smallest split whose chunks fit the lane loads, first among those
+    // where every wave gets a non-empty chunk; a wave past the end of K adds
+    // zeros (its loads read nothing), which some K need.
+    for (int pass = 0; pass < 2; ++pass)
+        for (int S = 1; S <= 8; S *= 2) {
+            // chunks of whole 128-byte lines (8 units)
+            const int c16 = (K16 + 8 * S - 1) / (8 * S) * 8;
+            const int n = next_pow2((c16 + kWave - 1) / kWave);
+            const bool full = S == 1 || (int64_t)(S - 1) * c16 < K16;
+            if (n <= fp8_nch_cap(M) && (full || pass == 1)) {
+                *splits = S;
+                *chunk16 = c16;
+                *nch = n < 1 ? 1 : n;
+                return true;
+            }
+        }
     return false;
 }
 
 hipError_t launch_fp8(int M, int N, int K, const void* x, const void* Wq, const float* Ws,
                       const Epilogue& ep, hipStream_t stream) {
-    int S, chunk16, nch;
-    if (!fp8_split(M, K, &S, &chunk16, &nch)) return hipErrorInvalidValue;
     const int K16 = K / kUnitCodes;
+    if (M >= kFp8MfmaFromM) {
+        if (!fp8_size_ok(M, K) || K % kUnitCodes != 0) return hipErrorInvalidValue;
+        int S, chunk_w;
+        fp8_mfma_split(N, K, &S, &chunk_w);
+        const int KB = (K + 127) / 128;
+        const int grid = (N + 15) / 16;
+        const uint4* xp = static_cast<const uint4*>(x);
+        const uint4* wp = static_cast<const uint4*>(Wq);
+        switch (S) {
+#define SG_S(v) \
+    case v: \
+        fp8_mfma_kernel<v><<<grid, kWave * v, 0, stream>>>(xp, wp, Ws, M, N, K16, KB, chunk_w, \
+                                                          ep); \
+        return hipGetLastError();
+            SG_S(1) SG_S(2) SG_S(4) SG_S(8)
+#undef SG_S
+            default: return hipErrorInvalidValue;
+        }
+    }
+    int S, chunk16, nch;
+    if (!fp8_split(M, N, K, &S, &chunk16, &nch)) return hipErrorInvalidValue;
     switch (M) {
         case 1: return launch_m<1>(nch, S, N, K16, chunk16, x, Wq, Ws, ep, stream);
         case 2: return launch_m<2>(nch, S, N, K16, chunk16, x, Wq, Ws, ep, stream);

@@ -108,16 +108,16 @@ hipError_t launch_prefetch(const void* W, size_t bytes, hipStream_t stream);
 
 // Projection with FP8 e4m3 weights: codes [N, K], fp32 scales [ceil(N/128),
 // ceil(K/128)] (one per 128 x 128 block).  1 <= M <= kFp8MaxM, K % 16 == 0;
-// at M <= 2, M * K <= kFp8MaxMK (the LDS that stages x), from M = 3,
-// K <= kFp8MaxKRegs (x in the registers of a team of at most 8 waves).
-// fp8_split: the K split (S waves a
-// team, chunk in 16-code units, loads per row) the kernel runs, false if the
-// shape is outside those limits.
-constexpr int kFp8MaxM = 4;
+// at M <= 2, M * K <= kFp8MaxMK (the LDS that stages x); at M = 3, 4 x
+// stays in the registers of a team of at most 8 waves: K <= 16384.  From
+// kFp8MfmaFromM rows the matrix-core kernel runs (any K, M <= 16).  fp8_split: the K split (S waves a team, chunk in
+// 16-code units, loads per row; 0 loads for the matrix-core kernel) the
+// kernel runs, false if the shape is outside those limits.
+constexpr int kFp8MaxM = 16;
+constexpr int kFp8MfmaFromM = 5;  // from here the matrix-core kernel
 constexpr int64_t kFp8MaxMK = 32768;
-constexpr int kFp8MaxKRegs = 16384;
 bool fp8_size_ok(int M, int K);
-bool fp8_split(int M, int K, int* splits, int* chunk16, int* nch);
+bool fp8_split(int M, int N, int K, int* splits, int* chunk16, int* nch);
 hipError_t launch_fp8(int M, int N, int K, const void* x, const void* Wq, const float* Ws,
                       const Epilogue& ep, hipStream_t stream);
 

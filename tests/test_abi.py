@@ -271,11 +271,12 @@ def test_fp8_size_limits_return_before_launch():
     def call(M, K, y=None):
         return c.skinny_gemm_fp8(M, 8, K, A, A, A, None, y, None, None)
 
-    assert call(5, 64) == 3
+    assert call(17, 64) == 3
     assert call(1, 32768) == 1 and call(1, 32784) == 3   # M * K <= 32768 (LDS) at M <= 2
     assert call(2, 16384) == 1 and call(2, 16400) == 3
     assert call(3, 16384) == 1 and call(3, 16400) == 3   # K <= 16384 (registers) at M = 3, 4
     assert call(4, 16384) == 1 and call(4, 16400) == 3
+    assert call(5, 8208) == 1 and call(16, 1 << 20) == 1  # matrix-core kernel: any K
     assert call(1, 24) == 4
     assert call(0, 64) == 0
     assert call(4, 16384, y=A + 4) == 4  # misaligned output

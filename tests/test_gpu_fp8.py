@@ -36,7 +36,11 @@ SHAPES = [(1, 40, 16), (1, 129, 112), (1, 200, 1040), (1, 77, 8192), (1, 33, 820
           (1, 300, 20000), (2, 50, 4128), (2, 130, 16384), (3, 70, 2080), (3, 129, 7168),
           (4, 96, 4160), (4, 257, 8192),
           # from M = 3 x stays in registers: K up to 16384 (8-wave teams)
-          (3, 140, 12304), (4, 129, 16384), (3, 65, 16384)]
+          (3, 140, 12304), (4, 129, 16384), (3, 65, 16384),
+          # from M = 5 the matrix-core kernel: 128-column windows split over a team,
+          # ragged last window, ragged 16-row tile, any K
+          (5, 100, 1040), (6, 131, 4112), (7, 64, 7168), (8, 257, 8192), (8, 33, 16),
+          (9, 129, 2064), (12, 300, 7168), (16, 40, 20000), (16, 1, 144), (13, 200, 30000)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -63,7 +67,9 @@ def test_fp8_small(M, N, K):
 INT_CODES = [0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50]
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 300, 4096), (2, 129, 8192), (4, 140, 2064)])
+@pytest.mark.parametrize("M,N,K", [(1, 300, 4096), (2, 129, 8192), (4, 140, 2064),
+                                   (8, 200, 8192), (6, 77, 3088), (16, 150, 8192),
+                                   (11, 64, 2064)])
 def test_fp8_integer_bit_exact(M, N, K):
     # integer activations and weights, power-of-two block scales: exact sums
     announce(f"fp8 integer M={M} N={N} K={K}")
@@ -80,14 +86,15 @@ def test_fp8_integer_bit_exact(M, N, K):
     assert np.array_equal(bits(y16), orc().encode_bf16(ref)), "bf16 output bit-exact"
 
 
-def test_fp8_nan_code_and_scale():
-    M, N, K = 2, 300, 512
-    x = si.normal_bf16((M, K), 1.0, 8900, DEV)
+@pytest.mark.parametrize("M", [2, 12])
+def test_fp8_nan_code_and_scale(M):
+    N, K = 300, 512
+    x = si.normal_bf16((M, K), 1.0, 8900 + M, DEV)
     codes, scales = si.fp8_weights(N, K, 8901, DEV)
     codes[5, 17] = 0x7F   # NaN code: row 5
     codes[200, 300] = 0xFF  # NaN code: row 200
     scales[2, 1] = float("nan")  # rows 256..299 (every k block 1 column)
-    announce("fp8 NaN code and scale")
+    announce(f"fp8 NaN code and scale M={M}")
     y32, _ = run(x, codes, scales, bf16=False)
     ref, A = orc().projection_fp8(bits(x), host(codes), host(scales))
     nan_rows = {5, 200} | set(range(256, 300))
@@ -100,11 +107,11 @@ def test_fp8_nan_code_and_scale():
 
 
 def test_fp8_rejections_touch_nothing():
-    x5 = si.normal_bf16((5, 64), 1.0, 1, DEV)
+    x17 = si.normal_bf16((17, 64), 1.0, 1, DEV)
     codes, scales = si.fp8_weights(8, 64, 2, DEV)
-    y = torch.full((5, 8), -7.0, device=DEV)
+    y = torch.full((17, 8), -7.0, device=DEV)
     with pytest.raises(sg.SkinnyGemmError) as e:
-        sg.skinny_gemm_fp8(x5, codes, scales, y_f32=y)  # M > 4
+        sg.skinny_gemm_fp8(x17, codes, scales, y_f32=y)  # M > 16
     assert e.value.status == 3
     x = si.normal_bf16((4, 16400), 1.0, 3, DEV)
     c2, s2 = si.fp8_weights(8, 16400, 4, DEV)
@@ -134,7 +141,9 @@ def test_fp8_empty():
 
 
 @pytest.mark.parametrize("M,N,K,residual", [(1, 8192, 7168, False), (2, 8192, 7168, False),
-                                            (4, 4096, 7168, False), (1, 7168, 8192, True)])
+                                            (4, 4096, 7168, False), (8, 4096, 7168, False),
+                                            (16, 4096, 7168, False), (1, 7168, 8192, True),
+                                            (8, 7168, 8192, True), (16, 7168, 8192, True)])
 def test_fp8_full_size_sampled(M, N, K, residual):
     announce(f"fp8 full M={M} N={N} K={K} residual={residual}")
     x = si.normal_bf16((M, K), 1.0, 9000 + M, DEV)
