@@ -553,7 +553,8 @@ def sweep(torch, sg, si, L, cyc, reps=40):
                 (0 if residual else M * N * 4)
             us = 1e3 * per
             gbs = nbytes / (per * 1e-3) / 1e9
-            rows.append({"workload": label, "M": M, "N": N, "K": K, "plan": "fp8_mfma" if M >= 5 else "fp8_rowdot",
+            rows.append({"workload": label, "M": M, "N": N, "K": K,
+                         "plan": "fp8_mfma" if M >= 5 else "fp8_rowdot",
                          "us": round(us, 3), "GBps": round(gbs, 1),
                          "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
         del ring
