@@ -525,7 +525,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
 
     # FP8 e4m3 weights with 128 x 128 fp32 block scales: half the bf16 weight bytes; a ring
     # of code/scale copies larger than 2 x MALL per shape
-    for label, Ms, N, K, residual in (("fp8 8192x7168", (1, 2), 8192, 7168, False),
+    for label, Ms, N, K, residual in (("fp8 8192x7168", (1, 2, 16), 8192, 7168, False),
                                       ("fp8 4096x7168", (4, 8, 16), 4096, 7168, False),
                                       ("fp8 residual 7168x8192", (1,), 7168, 8192, True)):
         codes, scales = si.fp8_weights(N, K, si.seed_for(7, si.TAG_W) + N, dev)

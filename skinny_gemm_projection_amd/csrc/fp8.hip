@@ -204,60 +204,66 @@ __global__ __launch_bounds__(kWave * team_block_waves(S)) void fp8_rowdot_kernel
 
 // Matrix-core kernel (kFp8MfmaFromM <= M <= 16: x is one 16-row A tile of
 // v_mfma_f32_16x16x32_bf16, rows past M zero).  A workgroup of S waves owns
-// a 16-row tile of W; wave s takes the 128-column windows [s*chunk_w,
+// NT 16-row tiles of W; wave s takes the 128-column windows [s*chunk_w,
 // (s+1)*chunk_w), D of them in flight.  Lane (col, grp) loads the 32 codes
-// k = 128w + 32grp .. +32 of row n0 + col (two 16-byte loads); k step t of
-// the window takes codes 8t .. 8t+7 of them, converted to bf16 (exact) as
-// the B operand, against x[m][128w + 32grp + 8t .. +8) as the A operand, so
-// A and B agree on the k of every operand slot.  x of a window goes through
-// the wave's LDS tile (4 rows x 256 bytes per load instruction, the piece
-// index XOR-swizzled by row so the operand reads hit 16 different bank
-// groups).  A window lies inside one 128 x 128 scale block (the tile's rows
-// share a row block), so its 4 products are summed first and the sum is
-// multiplied by that one scale.  The S partial tiles are added in LDS in
-// ascending wave order.
+// k = 128w + 32grp .. +32 of row n0 + 16nt + col (two 16-byte loads per row
+// tile); k step t of the window takes codes 8t .. 8t+7 of them, converted to
+// bf16 (exact) as the B operand, against x[m][128w + 32grp + 8t .. +8) as the
+// A operand, so A and B agree on the k of every operand slot.  x of a window
+// goes through the wave's LDS tile (4 rows x 256 bytes per load instruction,
+// the piece index XOR-swizzled by row so the operand reads hit 16 different
+// bank groups); with NT = 2 each A operand read serves two row tiles, halving
+// the x traffic per code byte.  A window lies inside one 128 x 128 scale
+// block (16 NT divides 128, so the tiles' rows share a row block): its 4
+// products are summed first and the sum is multiplied by that one scale.
+// The S partial tiles are added in LDS in ascending wave order.
 constexpr int kF8Windows = 4;  // windows in flight per wave
 
-template <int S>
+template <int NT, int S>
 __global__ __launch_bounds__(kWave * S) void fp8_mfma_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ Wq, const float* __restrict__ Ws,
     int M, int N, int K16, int KB, int chunk_w, Epilogue ep) {
     constexpr int D = kF8Windows;
-    __shared__ f32x4_t red[S > 1 ? S : 1][kWave];
+    __shared__ f32x4_t red[S > 1 ? S : 1][NT][kWave];
     __shared__ uint4 xtiles[S][256];  // per wave: x of one window, 16 rows x 16 pieces
 
     const int lane = threadIdx.x & (kWave - 1);
     const int col = lane & 15, grp = lane >> 4;
     const int s = wave_id_in_block();
-    const int n0 = blockIdx.x * 16;
-    const int rows = min(16, N - n0);
+    const int n0 = blockIdx.x * 16 * NT;
+    const int rows = min(16 * NT, N - n0);
     const int K8 = 2 * K16;        // 16-byte pieces of an x row
     const int KW = (K16 + 7) / 8;  // 128-column windows (8 units of 16 codes)
     const int w0 = s * chunk_w;
     const int w1 = min(KW, w0 + chunk_w);
 
-    // wave-uniform descriptors: codes of the tile's rows, and x (rows past M
-    // read zero)
+    // wave-uniform descriptors: codes of the tiles' rows (rows past N read
+    // zero), and x (rows past M read zero)
     const rsrc_t rw = make_rsrc(Wq + (int64_t)n0 * K16, (uint32_t)rows * K16 * 16u);
     const rsrc_t rx = make_rsrc(x, (uint32_t)M * K8 * 16u);
     const float* __restrict__ srow = Ws + (int64_t)(n0 / 128) * KB;
     constexpr uint32_t kOut = 0xFFFFFFF0u;  // past any range: reads zero
 
     uint4* xt = xtiles[s];
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     for (int wb = w0; wb < w1; wb += D) {
-        uint4 wv[D][2], xa[D][4];
+        uint4 wv[D][NT][2], xa[D][4];
         float sc[D];
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int w = wb + d;
             const bool live = w < w1;
-            const int u = 8 * w + 2 * grp;  // first unit of this lane in row col
+            const int u = 8 * w + 2 * grp;  // first unit of this lane in its rows
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const bool ok = live && u + j < K16;
-                wv[d][j] = load16<kStream>(rw, ok ? (uint32_t)(col * K16 + u + j) * 16u : kOut);
-            }
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const bool ok = live && u + j < K16;
+                    const uint32_t off = (uint32_t)((16 * nt + col) * K16 + u + j) * 16u;
+                    wv[d][nt][j] = load16<kStream>(rw, ok ? off : kOut);
+                }
             sc[d] = live ? srow[w] : 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -272,40 +278,63 @@ __global__ __launch_bounds__(kWave * S) void fp8_mfma_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) xt[(4 * i + grp) * 16 + col] = xa[d][i];
             __builtin_amdgcn_wave_barrier();
-            const uint32_t wd[8] = {wv[d][0].x, wv[d][0].y, wv[d][0].z, wv[d][0].w,
-                                    wv[d][1].x, wv[d][1].y, wv[d][1].z, wv[d][1].w};
-            f32x4_t part = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4_t part[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) part[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const uint4 b = {
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * t], 1.0f, false)),
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * t], 1.0f, true)),
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * t + 1], 1.0f, false)),
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * t + 1], 1.0f, true))};
                 const uint4 a = xt[col * 16 + ((4 * grp + t) ^ col)];
-                part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                               __builtin_bit_cast(bf16x8_t, b),
-                                                               part, 0, 0, 0);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    // codes 8t .. 8t+7: dwords 2t, 2t+1 of the lane's 32, low byte first
+                    const uint4 q = wv[d][nt][t / 2];
+                    const uint32_t lo = (t & 1) ? q.z : q.x;
+                    const uint32_t hi = (t & 1) ? q.w : q.y;
+                    const uint4 b = {
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+                    part[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), part[nt],
+                        0, 0, 0);
+                }
             }
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[v] = fmaf(part[v], sc[d], acc[v]);
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[nt][v] = fmaf(part[nt][v], sc[d], acc[nt][v]);
             __builtin_amdgcn_wave_barrier();
         }
     }
     if (S > 1) {
-        red[s][lane] = acc;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) red[s][nt][lane] = acc[nt];
         __syncthreads();
         if (s != 0) return;
 #pragma unroll
-        for (int j = 1; j < S; ++j) acc += red[j][lane];
-    }
-    if (col >= rows) return;
+        for (int j = 1; j < S; ++j)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int m = 4 * grp + v;
-        if (m < M) store_final(ep, (int64_t)m * N + n0 + col, acc[v]);
+            for (int nt = 0; nt < NT; ++nt) acc[nt] += red[j][nt][lane];
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int r = 16 * nt + col;
+        if (r >= rows) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = 4 * grp + v;
+            if (m < M) store_final(ep, (int64_t)m * N + n0 + r, acc[nt][v]);
+        }
     }
 }
+
+// Row tiles per wave: two once the 32-row tiles alone give every CU a
+// workgroup (measured at K = 7168: 8192 rows M = 8 18.5 -> 16.7 us, M = 16
+// 20.9 -> 17.7 us; at 4096 rows the 128 workgroups left half the CUs idle,
+// M = 8 10.8 -> 20.1 us).
+constexpr int kCus = 256;  // compute units
+int fp8_mfma_nt(int N) { return (N + 31) / 32 >= kCus ? 2 : 1; }
 
 // Lane loads per row (x registers: 8*M*NCH VGPRs) allowed at batch size M.
 constexpr int fp8_nch_cap(int M) { return M == 1 ? 8 : (M == 2 ? 4 : 2); }
@@ -379,7 +408,8 @@ int next_pow2(int v) {
 
 void fp8_mfma_split(int N, int K, int* splits, int* chunk_w) {
     const int KW = (K / kUnitCodes + 7) / 8;
-    const int tiles = (N + 15) / 16;
+    const int rows = 16 * fp8_mfma_nt(N);
+    const int tiles = (N + rows - 1) / rows;
     int S = 1;
     while (S < 8 && S < KW && tiles * S < kResident) S *= 2;
     *splits = S;
@@ -431,19 +461,19 @@ hipError_t launch_fp8(int M, int N, int K, const void* x, const void* Wq, const 
         int S, chunk_w;
         fp8_mfma_split(N, K, &S, &chunk_w);
         const int KB = (K + 127) / 128;
-        const int grid = (N + 15) / 16;
+        const int NT = fp8_mfma_nt(N);
+        const int grid = (N + 16 * NT - 1) / (16 * NT);
         const uint4* xp = static_cast<const uint4*>(x);
         const uint4* wp = static_cast<const uint4*>(Wq);
-        switch (S) {
-#define SG_S(v) \
-    case v: \
-        fp8_mfma_kernel<v><<<grid, kWave * v, 0, stream>>>(xp, wp, Ws, M, N, K16, KB, chunk_w, \
-                                                          ep); \
-        return hipGetLastError();
-            SG_S(1) SG_S(2) SG_S(4) SG_S(8)
+#define SG_S(nt, v) \
+    if (NT == nt && S == v) { \
+        fp8_mfma_kernel<nt, v><<<grid, kWave * v, 0, stream>>>(xp, wp, Ws, M, N, K16, KB, \
+                                                              chunk_w, ep); \
+        return hipGetLastError(); \
+    }
+        SG_S(1, 1) SG_S(1, 2) SG_S(1, 4) SG_S(1, 8) SG_S(2, 1) SG_S(2, 2) SG_S(2, 4) SG_S(2, 8)
 #undef SG_S
-            default: return hipErrorInvalidValue;
-        }
+        return hipErrorInvalidValue;
     }
     int S, chunk16, nch;
     if (!fp8_split(M, N, K, &S, &chunk16, &nch)) return hipErrorInvalidValue;

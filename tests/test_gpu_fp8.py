@@ -40,7 +40,9 @@ SHAPES = [(1, 40, 16), (1, 129, 112), (1, 200, 1040), (1, 77, 8192), (1, 33, 820
           # from M = 5 the matrix-core kernel: 128-column windows split over a team,
           # ragged last window, ragged 16-row tile, any K
           (5, 100, 1040), (6, 131, 4112), (7, 64, 7168), (8, 257, 8192), (8, 33, 16),
-          (9, 129, 2064), (12, 300, 7168), (16, 40, 20000), (16, 1, 144), (13, 200, 30000)]
+          (9, 129, 2064), (12, 300, 7168), (16, 40, 20000), (16, 1, 144), (13, 200, 30000),
+          # from 8161 rows two 16-row tiles per wave (ragged last 32-row tile)
+          (9, 8200, 144), (16, 8192, 1040), (5, 8177, 2064)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -86,18 +88,18 @@ def test_fp8_integer_bit_exact(M, N, K):
     assert np.array_equal(bits(y16), orc().encode_bf16(ref)), "bf16 output bit-exact"
 
 
-@pytest.mark.parametrize("M", [2, 12])
-def test_fp8_nan_code_and_scale(M):
-    N, K = 300, 512
+@pytest.mark.parametrize("M,N", [(2, 300), (12, 300), (12, 8200)])
+def test_fp8_nan_code_and_scale(M, N):
+    K = 512
     x = si.normal_bf16((M, K), 1.0, 8900 + M, DEV)
     codes, scales = si.fp8_weights(N, K, 8901, DEV)
     codes[5, 17] = 0x7F   # NaN code: row 5
     codes[200, 300] = 0xFF  # NaN code: row 200
-    scales[2, 1] = float("nan")  # rows 256..299 (every k block 1 column)
-    announce(f"fp8 NaN code and scale M={M}")
+    scales[2, 1] = float("nan")  # rows 256..383 (every k block 1 column)
+    announce(f"fp8 NaN code and scale M={M} N={N}")
     y32, _ = run(x, codes, scales, bf16=False)
     ref, A = orc().projection_fp8(bits(x), host(codes), host(scales))
-    nan_rows = {5, 200} | set(range(256, 300))
+    nan_rows = {5, 200} | set(range(256, min(N, 384)))
     got_nan = {n for n in range(N) if torch.isnan(y32[:, n]).all()}
     assert got_nan == nan_rows, sorted(got_nan ^ nan_rows)
     assert set(np.where(np.isnan(ref).all(axis=0))[0].tolist()) == nan_rows
@@ -142,7 +144,8 @@ def test_fp8_empty():
 
 @pytest.mark.parametrize("M,N,K,residual", [(1, 8192, 7168, False), (2, 8192, 7168, False),
                                             (4, 4096, 7168, False), (8, 4096, 7168, False),
-                                            (16, 4096, 7168, False), (1, 7168, 8192, True),
+                                            (16, 4096, 7168, False), (12, 8192, 7168, False),
+                                            (1, 7168, 8192, True),
                                             (8, 7168, 8192, True), (16, 7168, 8192, True)])
 def test_fp8_full_size_sampled(M, N, K, residual):
     announce(f"fp8 full M={M} N={N} K={K} residual={residual}")
