@@ -488,7 +488,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
     # MXFP4 weights (e2m1 codes + e8m0 block scales): the same shapes at a quarter of the
     # weight bytes; a ring of code/scale copies larger than 2 x MALL per shape
     c = L.c
-    for label, Ms, N, K, residual in (("mxfp4 8192x7168", (1, 2), 8192, 7168, False),
+    for label, Ms, N, K, residual in (("mxfp4 8192x7168", (1, 2, 16), 8192, 7168, False),
                                       ("mxfp4 4096x7168", (4, 8, 16), 4096, 7168, False),
                                       ("mxfp4 residual 7168x8192", (1, 8), 7168, 8192, True)):
         codes, scales = si.mxfp4_weights(N, K, si.seed_for(6, si.TAG_W) + N, dev)

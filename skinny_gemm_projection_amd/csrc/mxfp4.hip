@@ -187,30 +187,31 @@ __global__ __launch_bounds__(kWave * team_waves(S)) void mxfp4_rowdot_kernel(
     }
 }
 
-// Matrix-core kernel: one workgroup of S waves per 16-row tile of W; wave s
-// takes windows [s*chunk_w, (s+1)*chunk_w) of 128 elements (4 blocks), D of
-// them in flight at a time.
+// Matrix-core kernel: one workgroup of S waves per NT 16-row tiles of W;
+// wave s takes windows [s*chunk_w, (s+1)*chunk_w) of 128 elements (4
+// blocks), D of them in flight at a time.  With NT = 2 each x operand read
+// serves two row tiles, halving the x bytes per code byte.
 constexpr int kMfmaWindows = 8;
 
-template <int S>
+template <int NT, int S>
 __global__ __launch_bounds__(kWave * S) void mxfp4_mfma_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ Wq, const uint8_t* __restrict__ Ws,
     int M, int N, int KB, int chunk_w, Epilogue ep) {
     constexpr int D = kMfmaWindows;
-    __shared__ f32x4_t red[S > 1 ? S : 1][kWave];
+    __shared__ f32x4_t red[S > 1 ? S : 1][NT][kWave];
     __shared__ uint4 xtiles[S][256];  // per wave: x of one window, 16 rows x 16 pieces
 
     const int lane = threadIdx.x & (kWave - 1);
     const int col = lane & 15, grp = lane >> 4;
     const int s = wave_id_in_block();
-    const int n0 = blockIdx.x * 16;
-    const int rows = min(16, N - n0);
+    const int n0 = blockIdx.x * 16 * NT;
+    const int rows = min(16 * NT, N - n0);
     const int K8 = KB * 4;  // 16-byte pieces of an x row
     const int KW = (KB + 3) / 4;
     const int w0 = s * chunk_w;
     const int w1 = min(KW, w0 + chunk_w);
 
-    // wave-uniform descriptors over the tile's codes and scales and over x:
+    // wave-uniform descriptors over the tiles' codes and scales and over x:
     // rows past N and x rows past M read zero
     const rsrc_t rw = make_rsrc(Wq + (int64_t)n0 * KB, (uint32_t)rows * KB * 16u);
     const rsrc_t rs = make_rsrc(Ws + (int64_t)n0 * KB, (uint32_t)rows * KB);
@@ -222,19 +223,27 @@ __global__ __launch_bounds__(kWave * S) void mxfp4_mfma_kernel(
     // instruction), into slot col of that row; the A operand of step t,
     // piece 4*grp + t of row col, is read back from slot (4*grp + t) ^ col.
     uint4* xt = xtiles[s];
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    bool nan_scale = false;
+    f32x4_t acc[NT];
+    bool nan_scale[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        nan_scale[nt] = false;
+    }
     for (int wb = w0; wb < w1; wb += D) {
-        uint4 wv[D], xa[D][4];
-        uint32_t sc[D];
+        uint4 wv[D][NT], xa[D][4];
+        uint32_t sc[D][NT];
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int w = wb + d;
-            const int b = 4 * w + grp;  // this lane's block of row col
+            const int b = 4 * w + grp;  // this lane's block of its rows
             const bool ok = w < w1 && b < KB;
-            wv[d] = load16<kStream>(rw, ok ? (uint32_t)(col * KB + b) * 16u : kOut);
-            sc[d] = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? (uint32_t)(col * KB + b) : kOut,
-                                                        0, kStream);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const uint32_t blk = (uint32_t)((16 * nt + col) * KB + b);
+                wv[d][nt] = load16<kStream>(rw, ok ? blk * 16u : kOut);
+                sc[d][nt] = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? blk : kOut, 0, kStream);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * i + grp;
@@ -248,46 +257,72 @@ __global__ __launch_bounds__(kWave * S) void mxfp4_mfma_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) xt[(4 * i + grp) * 16 + col] = xa[d][i];
             __builtin_amdgcn_wave_barrier();
-            nan_scale |= sc[d] == 255u;
-            const float scale = as_f(sc[d] << 23);  // e8m0 code in the exponent field
-            const uint32_t wd[4] = {wv[d].x, wv[d].y, wv[d].z, wv[d].w};
+            float scale[NT];
+            uint32_t wd[NT][4];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                nan_scale[nt] |= sc[d][nt] == 255u;
+                scale[nt] = as_f(sc[d][nt] << 23);  // e8m0 code in the exponent field
+                wd[nt][0] = wv[d][nt].x;
+                wd[nt][1] = wv[d][nt].y;
+                wd[nt][2] = wv[d][nt].z;
+                wd[nt][3] = wv[d][nt].w;
+            }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const uint4 b = {
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[t], scale, 0)),
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[t], scale, 1)),
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[t], scale, 2)),
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[t], scale, 3))};
                 const uint4 a = xt[col * 16 + ((4 * grp + t) ^ col)];
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                              __builtin_bit_cast(bf16x8_t, b), acc,
-                                                              0, 0, 0);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const uint4 b = {
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], scale[nt], 0)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], scale[nt], 1)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], scale[nt], 2)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], scale[nt], 3))};
+                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), acc[nt],
+                        0, 0, 0);
+                }
             }
             __builtin_amdgcn_wave_barrier();
         }
     }
-    // a NaN scale anywhere in row col's blocks of this chunk: that row is NaN
-    const uint64_t flagged = __ballot(nan_scale);
-    const uint32_t rows_nan = (uint32_t)((flagged | flagged >> 16 | flagged >> 32 | flagged >> 48) &
-                                         0xFFFFu);
-    if ((rows_nan >> col) & 1u) {
-        const float q = __builtin_nanf("");
-        acc = f32x4_t{q, q, q, q};
+    // a NaN scale anywhere in a row's blocks of this chunk: that row is NaN
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const uint64_t flagged = __ballot(nan_scale[nt]);
+        const uint32_t rows_nan =
+            (uint32_t)((flagged | flagged >> 16 | flagged >> 32 | flagged >> 48) & 0xFFFFu);
+        if ((rows_nan >> col) & 1u) {
+            const float q = __builtin_nanf("");
+            acc[nt] = f32x4_t{q, q, q, q};
+        }
     }
     if (S > 1) {
-        red[s][lane] = acc;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) red[s][nt][lane] = acc[nt];
         __syncthreads();
         if (s != 0) return;
 #pragma unroll
-        for (int j = 1; j < S; ++j) acc += red[j][lane];
-    }
-    if (col >= rows) return;
+        for (int j = 1; j < S; ++j)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int m = 4 * grp + v;
-        if (m < M) store_final(ep, (int64_t)m * N + n0 + col, acc[v]);
+            for (int nt = 0; nt < NT; ++nt) acc[nt] += red[j][nt][lane];
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int r = 16 * nt + col;
+        if (r >= rows) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = 4 * grp + v;
+            if (m < M) store_final(ep, (int64_t)m * N + n0 + r, acc[nt][v]);
+        }
     }
 }
+
+// Row tiles per wave for the matrix-core kernel: two once the 32-row tiles
+// alone give every CU a workgroup (as in the FP8 matrix-core kernel).
+constexpr int kCus = 256;  // compute units
+int mxfp4_mfma_nt(int N) { return (N + 31) / 32 >= kCus ? 2 : 1; }
 
 constexpr int kResidentWaves = 2048;  // 256 CUs x 8 waves
 
@@ -341,7 +376,8 @@ hipError_t launch_m(int NB, int S, int N, int KB, int chunk_b, const void* x, co
 
 void mxfp4_mfma_split(int N, int K, int* splits, int* chunk_w) {
     const int KW = (K / kBlockElems + 3) / 4;
-    const int tiles = (N + 15) / 16;
+    const int rows = 16 * mxfp4_mfma_nt(N);
+    const int tiles = (N + rows - 1) / rows;
     int S = 1;
     while (S < 8 && S < KW && tiles * S < kResidentWaves) S *= 2;
     *splits = S;
@@ -376,18 +412,19 @@ hipError_t launch_mxfp4(int M, int N, int K, const void* x, const void* Wq, cons
     if (M >= kMxfp4MfmaFromM) {
         int S, chunk_w;
         mxfp4_mfma_split(N, K, &S, &chunk_w);
-        const int grid = (N + 15) / 16;
+        const int NT = mxfp4_mfma_nt(N);
+        const int grid = (N + 16 * NT - 1) / (16 * NT);
         const uint4* xp = static_cast<const uint4*>(x);
         const uint4* wp = static_cast<const uint4*>(Wq);
-        switch (S) {
-#define SG_S(v) \
-    case v: \
-        mxfp4_mfma_kernel<v><<<grid, kWave * v, 0, stream>>>(xp, wp, Ws, M, N, KB, chunk_w, ep); \
-        return hipGetLastError();
-            SG_S(1) SG_S(2) SG_S(4) SG_S(8)
+#define SG_S(nt, v) \
+    if (NT == nt && S == v) { \
+        mxfp4_mfma_kernel<nt, v><<<grid, kWave * v, 0, stream>>>(xp, wp, Ws, M, N, KB, chunk_w, \
+                                                                ep); \
+        return hipGetLastError(); \
+    }
+        SG_S(1, 1) SG_S(1, 2) SG_S(1, 4) SG_S(1, 8) SG_S(2, 1) SG_S(2, 2) SG_S(2, 4) SG_S(2, 8)
 #undef SG_S
-            default: return hipErrorInvalidValue;
-        }
+        return hipErrorInvalidValue;
     }
     int NB, S;
     if (!mxfp4_split(M, K, &NB, &S)) return hipErrorInvalidValue;

@@ -35,7 +35,10 @@ def run(x, codes, scales, r=None, f32=True, bf16=True):
 SHAPES = [(1, 40, 32), (1, 129, 96), (1, 77, 608), (1, 65, 2080), (1, 33, 8224),
           (2, 50, 4128), (2, 17, 8192), (3, 70, 2080), (4, 96, 4160), (5, 31, 640),
           (6, 64, 7168), (7, 45, 2048), (8, 130, 3200), (8, 20, 16384), (9, 40, 2080),
-          (12, 33, 608), (13, 70, 8224), (16, 100, 7168), (16, 17, 96), (16, 16, 32)]
+          (12, 33, 608), (13, 70, 8224), (16, 100, 7168), (16, 17, 96), (16, 16, 32),
+          # from 8161 rows the matrix-core kernel takes two 16-row tiles a wave
+          # (ragged last 32-row tile)
+          (9, 8200, 2080), (16, 8192, 608), (12, 8177, 96)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -59,7 +62,7 @@ def test_mxfp4_small(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 37, 4096), (2, 64, 7168), (8, 40, 8192), (5, 19, 96),
-                                   (16, 48, 4096), (11, 21, 8192)])
+                                   (16, 48, 4096), (11, 21, 8192), (16, 8200, 1024)])
 def test_mxfp4_integer_bit_exact(M, N, K):
     announce(f"mxfp4 integer M={M} N={N} K={K}")
     x = si.integer_bf16((M, K), -4, 4, 8300 + K, DEV)
@@ -72,12 +75,15 @@ def test_mxfp4_integer_bit_exact(M, N, K):
                 f"mxfp4 integer bf16 M={M}")
 
 
-def test_mxfp4_nan_scale_and_extremes():
-    announce("mxfp4 NaN scale, extreme scales, zero codes")
-    M, N, K = 3, 24, 512
-    x = si.normal_bf16((M, K), 1.0, 8400, DEV)
+@pytest.mark.parametrize("M,N", [(3, 24), (12, 24), (12, 8200)])
+def test_mxfp4_nan_scale_and_extremes(M, N):
+    # vector kernel (M = 3), matrix-core kernel with one and with two row tiles a wave
+    announce(f"mxfp4 NaN scale, extreme scales, zero codes M={M} N={N}")
+    K = 512
+    x = si.normal_bf16((M, K), 1.0, 8400 + M, DEV)
     codes, scales = si.mxfp4_weights(N, K, 8401, DEV)
     scales[5, 3] = 255      # NaN block: row 5 is NaN for every m
+    scales[N - 5, 0] = 255  # and row N - 5 (the second row tile of the last pair at N = 8200)
     scales[7, :] = 200      # large scale, 2^73 (finite fp32 sums for these x)
     scales[9, :] = 16       # small scale, 2^-111: products stay normal in fp32
     codes[11, :] = 0        # all +0 codes
@@ -85,8 +91,9 @@ def test_mxfp4_nan_scale_and_extremes():
     y32, _ = run(x, codes, scales, bf16=False)
     ref, A = orc().projection_mxfp4(bits(x), np_u8(codes), np_u8(scales))
     y = y32.cpu().numpy()
-    assert np.isnan(y[:, 5]).all() and not np.isnan(np.delete(y, 5, axis=1)).any()
-    keep = [n for n in range(N) if n != 5]
+    nan_rows = [5, N - 5]
+    assert np.isnan(y[:, nan_rows]).all() and not np.isnan(np.delete(y, nan_rows, axis=1)).any()
+    keep = [n for n in range(N) if n not in nan_rows]
     check_f32(y32[:, keep], ref[:, keep], A[:, keep], "mxfp4 extremes")
     assert (y[:, 11] == 0).all() and (y[:, 12] == 0).all()
 
@@ -122,7 +129,8 @@ def test_mxfp4_empty_and_rejected():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 8192, 7168), (2, 8192, 7168), (4, 4096, 7168),
-                                   (8, 4096, 7168), (16, 4096, 7168), (1, 7168, 8192),
+                                   (8, 4096, 7168), (16, 4096, 7168), (16, 8192, 7168),
+                                   (1, 7168, 8192),
                                    (8, 7168, 8192), (16, 7168, 8192)])
 def test_mxfp4_full_size(M, N, K):
     # the benchmark's shapes: sampled output rows against the oracle
