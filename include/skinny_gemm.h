@@ -212,9 +212,8 @@ sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int
  *   into operand layout).
  * Limits: 0 <= M <= 16 (M > 16: SG_ERR_UNSUPPORTED), 0 <= N <= 1<<20,
  * 0 <= K <= 1<<20 (else SG_ERR_SHAPE), K % 32 == 0 (SG_ERR_ALIGN); K <=
- * 65536 at M = 1, 32768 at M = 2 and 16384 for 3 <= M <= 8 (else
- * SG_ERR_UNSUPPORTED).  x,
- * W_codes, r and outputs 16-byte aligned; W_scales any alignment.  Scales
+ * 32768 at M <= 2 and 16384 for 3 <= M <= 8 (else SG_ERR_UNSUPPORTED).
+ * x, W_codes, r and outputs 16-byte aligned; W_scales any alignment.  Scales
  * whose weights fall below fp32's normal range may lose those products. */
 sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
                             const uint8_t* W_codes, const uint8_t* W_scales, const sg_bf16* r,

@@ -281,3 +281,23 @@ def test_fp8_size_limits_return_before_launch():
     assert call(0, 64) == 0
     assert call(4, 16384, y=A + 4) == 4  # misaligned output
     assert sum(sg.skinny_gemm_get_counters()) == 0
+
+
+@no_gpu_only
+def test_mxfp4_size_limits_return_before_launch():
+    # the vector kernel's team split bounds K (2 blocks of 32 a lane at M <= 2, one
+    # from M = 3, at most 8 waves); the matrix-core kernel (M >= 9) takes any K
+    c = _raw()
+    sg.skinny_gemm_reset_counters()
+    A = 0x10000
+
+    def call(M, K):
+        return c.skinny_gemm_mxfp4(M, 8, K, A, A, A, None, None, None, None)
+
+    assert call(17, 64) == 3
+    assert call(1, 32768) == 1 and call(1, 32800) == 3
+    assert call(2, 32768) == 1 and call(2, 32800) == 3
+    assert call(3, 16384) == 1 and call(8, 16416) == 3
+    assert call(9, 1 << 20) == 1
+    assert call(1, 48) == 4
+    assert sum(sg.skinny_gemm_get_counters()) == 0

@@ -114,7 +114,7 @@ def test_mxfp4_empty_and_rejected():
     s = torch.cuda.current_stream().cuda_stream
     cases = [((17, 8, 64), 3),         # batch above the 4-bit path
              ((2, 8, 48), 4),          # K not a multiple of 32
-             ((1, 8, 65568), 3),       # K over the vector-ALU split limit at M = 1
+             ((1, 8, 32800), 3),       # K over the vector-ALU split limit at M = 1
              ((2, 8, 32800), 3),       # and at M = 2
              ((5, 8, 16416), 3),       # and from M = 3
              ((2, -1, 64), 2)]
