@@ -401,6 +401,14 @@ def sweep(torch, sg, si, L, cyc, reps=40):
         y32, y16 = torch.empty((M, N), device=dev), torch.empty((M, N), device=dev, dtype=torch.bfloat16)
         per = timed_calls(torch, [L.projection(p, x, w, y32, y16) for w in ring], reps, cyc)
         record("small-batch 8192x7168", M, N, K, plan_desc(p), per, proj_bytes(M, N, K))
+    # the same matrix at larger decode batches (the planner's kernel at each M)
+    for M in (4, 8, 16, 64):
+        x = si.normal_bf16((M, K), 1.0, si.seed_for(2, si.TAG_X) + M, dev)
+        p = sg.skinny_gemm_plan(M, N, K)
+        y32, y16 = torch.empty((M, N), device=dev), torch.empty((M, N), device=dev, dtype=torch.bfloat16)
+        ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        per = timed_calls(torch, [L.projection(p, x, w, y32, y16, ws) for w in ring], reps, cyc)
+        record("8192x7168, larger batch", M, N, K, plan_desc(p), per, proj_bytes(M, N, K))
 
     # side-stream weight prefetch on the same ring: the read of one 117 MB matrix alone, and
     # what it buys the projection after it -- prefetch then project the same matrix (its
