@@ -81,6 +81,18 @@ def test_plan_kernel_by_batch_few_rows():
         assert p.kernel == want, (M, p)
 
 
+def test_plan_team_or_chunk_by_width():
+    # 8..16 rows on matrix cores: the team kernel (16-row tiles, one pass) while N/16 tiles
+    # fill the CUs, except from M = 12 once there are twice as many tiles as CUs, where the
+    # chunk kernel (128/256-row tiles, second pass) reads x fewer times
+    for M, N, team in [(8, 4096, True), (16, 4096, True), (8, 8192, True), (11, 8192, True),
+                       (12, 8192, False), (16, 8192, False), (16, 7168, True),
+                       (16, 16384, False), (17, 4096, False)]:
+        p = sg.skinny_gemm_plan(M, N, 7168)
+        assert p.kernel == sg.SG_KERNEL_SPLITK_MFMA, (M, N, p)
+        assert (p.tile_n == 16 and not p.two_pass) == team, (M, N, p)
+
+
 def test_plan_rejects():
     cases = [((65, 16, 16), 3), ((1000, 16, 16), 3), ((-1, 16, 16), 2), ((1, -1, 16), 2),
              ((1, 16, -8), 2), ((1, (1 << 20) + 1, 16), 2), ((1, 16, 12), 4), ((1, 16, 7), 4)]
