@@ -875,7 +875,7 @@ def profile_workloads(torch, sg, si, L, manifest_path, reps=3):
     del W
     torch.cuda.empty_cache()
     # MXFP4 weights
-    for label, Ms, N, K in (("mxfp4 8192x7168", (1, 2), 8192, 7168),
+    for label, Ms, N, K in (("mxfp4 8192x7168", (1, 2, 16), 8192, 7168),
                             ("mxfp4 4096x7168", (4, 8, 16), 4096, 7168)):
         codes, scales = si.mxfp4_weights(N, K, 17, dev)
         ring = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(reps - 1)]
@@ -891,7 +891,7 @@ def profile_workloads(torch, sg, si, L, manifest_path, reps=3):
                 [mx(cw, sw) for cw, sw in ring], nbytes)
         del ring
     # FP8 weights (e4m3 codes, 128 x 128 block scales)
-    for label, Ms, N, K in (("fp8 8192x7168", (1, 2), 8192, 7168),
+    for label, Ms, N, K in (("fp8 8192x7168", (1, 2, 16), 8192, 7168),
                             ("fp8 4096x7168", (4, 8, 16), 4096, 7168)):
         codes, scales = si.fp8_weights(N, K, 21, dev)
         ring = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(reps - 1)]
