@@ -434,22 +434,19 @@ bool fp8_split(int M, int N, int K, int* splits, int* chunk16, int* nch) {
         return true;
     }
     const int K16 = K / kUnitCodes;
-    // The smallest split whose chunks fit the lane loads, first among those
-    // where every wave gets a non-empty chunk; a wave past the end of K adds
-    // zeros (its loads read nothing), which some K need.
-    for (int pass = 0; pass < 2; ++pass)
-        for (int S = 1; S <= 8; S *= 2) {
-            // chunks of whole 128-byte lines (8 units)
-            const int c16 = (K16 + 8 * S - 1) / (8 * S) * 8;
-            const int n = next_pow2((c16 + kWave - 1) / kWave);
-            const bool full = S == 1 || (int64_t)(S - 1) * c16 < K16;
-            if (n <= fp8_nch_cap(M) && (full || pass == 1)) {
-                *splits = S;
-                *chunk16 = c16;
-                *nch = n < 1 ? 1 : n;
-                return true;
-            }
+    // The smallest split whose chunks fit the lane loads and leave no wave
+    // without a chunk (within the size limits above one always exists).
+    for (int S = 1; S <= 8; S *= 2) {
+        // chunks of whole 128-byte lines (8 units)
+        const int c16 = (K16 + 8 * S - 1) / (8 * S) * 8;
+        const int n = next_pow2((c16 + kWave - 1) / kWave);
+        if (n <= fp8_nch_cap(M) && (S == 1 || (int64_t)(S - 1) * c16 < K16)) {
+            *splits = S;
+            *chunk16 = c16;
+            *nch = n < 1 ? 1 : n;
+            return true;
         }
+    }
     return false;
 }
 
