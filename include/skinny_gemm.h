@@ -204,7 +204,10 @@ sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int
  *   W_scales [N, K/32] bytes: e8m0 scale of elements [32b, 32b+32) of row
  *            n, 2^(s-127); s == 255 is NaN (the row's outputs become NaN).
  *   W[n,k] = e2m1 * 2^(s-127);  y[m,n] = sum_k x[m,k] W[n,k] in fp32
- *   (products exact), then the epilogue of skinny_gemm_residual when r is
+ *   (the codes are converted at unit scale and each block's fp32 sum is
+ *   multiplied by its scale, so every scale code 0..254 is exact down to
+ *   fp32's subnormals, including weights outside bf16's range), then the
+ *   epilogue of skinny_gemm_residual when r is
  *   given (out = bf16_RNE(fp32(r) + y), r may alias y_bf16) or of
  *   skinny_gemm otherwise.  One launch, no workspace; the weight stream is a
  *   quarter of bf16's plus 1/16 for the scales.  M <= 8 runs on the vector
@@ -213,8 +216,7 @@ sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int
  * Limits: 0 <= M <= 16 (M > 16: SG_ERR_UNSUPPORTED), 0 <= N <= 1<<20,
  * 0 <= K <= 1<<20 (else SG_ERR_SHAPE), K % 32 == 0 (SG_ERR_ALIGN); K <=
  * 32768 at M <= 2 and 16384 for 3 <= M <= 8 (else SG_ERR_UNSUPPORTED).
- * x, W_codes, r and outputs 16-byte aligned; W_scales any alignment.  Scales
- * whose weights fall below fp32's normal range may lose those products. */
+ * x, W_codes, r and outputs 16-byte aligned; W_scales any alignment. */
 sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
                             const uint8_t* W_codes, const uint8_t* W_scales, const sg_bf16* r,
                             float* y_f32, sg_bf16* y_bf16, void* stream);

@@ -14,12 +14,15 @@
 // per instruction) and one byte load is its scale (64 consecutive bytes per
 // instruction).  The block's 32 activations of every x row stay in
 // registers for the wave's life.  Each code byte becomes two bf16 weights in
-// one v_cvt_scalef32_pk_bf16_fp4, which applies the block scale on the way
-// (the instruction reads its float operand's exponent field as an e8m0
-// scale; e2m1 times a power of two is exact in bf16), and the pair meets the
-// matching x pair in one v_dot2c_f32_bf16 per activation row.  A scale code
-// 255 (NaN) is handled once per row, not per element: the row's partial
-// becomes NaN before the lane reduction.
+// one v_cvt_scalef32_pk_bf16_fp4 at unit scale (every e2m1 value is exact in
+// bf16), the pair meets the matching x pair in one v_dot2c_f32_bf16 per
+// activation row, and the block's fp32 sum is then multiplied by its scale
+// 2^(s-127) in one fma into the row's total.  Scaling the sum rather than
+// the converted weights keeps every valid scale code exact: the weights of
+// codes 0..1 would be subnormal and those of codes 253..254 could overflow
+// bf16, while a power-of-two product of an fp32 sum is exact down to fp32's
+// subnormals.  The scale code 255 (NaN) becomes a NaN factor, so the row's
+// total is NaN.
 //
 // Rows are grouped R per iteration, their R*M lane partials reduced
 // together by the reduce-scatter of the bf16 kernel; S waves of a workgroup
@@ -28,19 +31,23 @@
 // From 9 rows of batch the VALU dots (16*M per block and row) outgrow the
 // weight stream, and a matrix-core kernel takes over (up to 16 rows of x,
 // one MFMA m-tile).  Lane (col, grp) of a wave on a 16-row tile loads block
-// grp of a 128-element window of row col -- the weights of one
-// v_mfma_f32_16x16x32_bf16 B operand per step t, as dword t of that block,
-// converted in 4 instructions straight into operand layout (no LDS
-// transpose).  The matching A operand is x[m][window + 32*grp + 8*t ..+8):
-// inside a 32-wide step the k order is free, A and B only have to agree.
-// x of each window is loaded as 4 rows x 256 bytes per instruction into a
-// swizzled per-wave LDS tile and read back in operand layout (reading the
-// operands straight from L2, 16 rows x 64 bytes per instruction, was 10-25%
-// slower).  S waves of a workgroup split K over the tile (8 windows in
-// flight each) and add their 16x16 tiles in LDS in ascending order.  Every
-// workgroup still reads all of x from L2 -- at 16 rows four x bytes per code
-// byte -- and that traffic, not HBM, bounds the kernel; through M = 8 the
-// VALU kernel is as fast or faster.
+// grp of a 128-element window of row col (16 bytes) and its scale byte.  Four
+// lane-row swaps (permlane32 then permlane16) transpose the 4 x 4 dwords of
+// the four lane groups of a column, so that for step t every lane of column
+// col holds 8 codes of the same block 4w + t: one v_mfma_f32_16x16x32_bf16
+// step is then exactly one scale block, converted at unit scale straight into
+// B operand layout.  Its 16x16 result is multiplied by the block scale of
+// each column and added to the accumulator in fp32 (one fma per output), the
+// same exact scaling as the vector kernel; two more swaps gather the four
+// scale bytes of a column into each of its lanes.  The matching A operand is
+// x[m][window + 32*t + 8*grp ..+8).  x of each window is loaded as 4 rows x
+// 256 bytes per instruction into a swizzled per-wave LDS tile and read back
+// in operand layout (reading the operands straight from L2, 16 rows x 64
+// bytes per instruction, was 10-25% slower).  S waves of a workgroup split K
+// over the tile (8 windows in flight each) and add their 16x16 tiles in LDS
+// in ascending order.  Every workgroup still reads all of x from L2 -- at 16
+// rows four x bytes per code byte -- and that traffic, not HBM, bounds the
+// kernel; through M = 8 the VALU kernel is as fast or faster.
 #include "launch.h"
 
 namespace sg {
@@ -49,19 +56,27 @@ namespace {
 
 constexpr int kBlockElems = 32;  // elements per scale block = per 16-byte code load
 
-// 32 products of one block: x pairs (16 dwords, xb[d] component j holds
-// elements 8d+2j, 8d+2j+1) against the 32 codes of w (dword d, byte j holds
-// the same two elements), each code pair converted with the block scale.
-__device__ __forceinline__ float dot_block(const uint4 (&xb)[4], const uint4 w, float scale,
-                                           float acc) {
+// e8m0 scale code -> its fp32 value 2^(s-127): the code is the exponent
+// field for 1 <= s <= 254, s = 0 is the fp32 subnormal 2^-127 and s = 255
+// is NaN.
+__device__ __forceinline__ float e8m0_value(uint32_t s) {
+    return as_f(s == 0u ? 0x00400000u : s == 255u ? 0x7FC00000u : s << 23);
+}
+
+// The fp32 sum of the 32 products of one block at unit scale: x pairs (16
+// dwords, xb[d] component j holds elements 8d+2j, 8d+2j+1) against the 32
+// codes of w (dword d, byte j holds the same two elements).
+__device__ __forceinline__ float dot_block(const uint4 (&xb)[4], const uint4 w) {
+    constexpr float kUnit = 1.0f;  // exponent field 127: scale 2^0
     const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    float acc = 0.0f;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const uint32_t xd[4] = {xb[d].x, xb[d].y, xb[d].z, xb[d].w};
-        const bf16x2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], scale, 0);
-        const bf16x2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], scale, 1);
-        const bf16x2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], scale, 2);
-        const bf16x2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], scale, 3);
+        const bf16x2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], kUnit, 0);
+        const bf16x2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], kUnit, 1);
+        const bf16x2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], kUnit, 2);
+        const bf16x2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], kUnit, 3);
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xd[0]), w0, acc, false);
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xd[1]), w1, acc, false);
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xd[2]), w2, acc, false);
@@ -147,19 +162,16 @@ __global__ __launch_bounds__(kWave * team_waves(S)) void mxfp4_rowdot_kernel(
 #pragma unroll
                 for (int i = 0; i < RB; ++i) {
                     const int r = q * RB + i;
-                    bool nan_scale = false;
                     float scale[NB];
 #pragma unroll
-                    for (int c = 0; c < NB; ++c) {
-                        nan_scale |= sc[r][c] == 255u;
-                        scale[c] = as_f(sc[r][c] << 23);  // e8m0 code in the exponent field
-                    }
+                    for (int c = 0; c < NB; ++c) scale[c] = e8m0_value(sc[r][c]);
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
                         float a = 0.0f;
 #pragma unroll
-                        for (int c = 0; c < NB; ++c) a = dot_block(xr[m][c], wr[r][c], scale[c], a);
-                        part[i * M + m] = nan_scale ? __builtin_nanf("") : a;
+                        for (int c = 0; c < NB; ++c)
+                            a = __builtin_fmaf(dot_block(xr[m][c], wr[r][c]), scale[c], a);
+                        part[i * M + m] = a;
                     }
                 }
             }
@@ -221,15 +233,11 @@ __global__ __launch_bounds__(kWave * S) void mxfp4_mfma_kernel(
     // x of a window goes through the wave's LDS tile: load i reads row
     // 4i + grp, piece col ^ (4i + grp) of the window (4 rows x 256 bytes per
     // instruction), into slot col of that row; the A operand of step t,
-    // piece 4*grp + t of row col, is read back from slot (4*grp + t) ^ col.
+    // piece 4t + grp of row col, is read back from slot (4t + grp) ^ col.
     uint4* xt = xtiles[s];
     f32x4_t acc[NT];
-    bool nan_scale[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        nan_scale[nt] = false;
-    }
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     for (int wb = w0; wb < w1; wb += D) {
         uint4 wv[D][NT], xa[D][4];
         uint32_t sc[D][NT];
@@ -257,44 +265,49 @@ __global__ __launch_bounds__(kWave * S) void mxfp4_mfma_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) xt[(4 * i + grp) * 16 + col] = xa[d][i];
             __builtin_amdgcn_wave_barrier();
-            float scale[NT];
             uint32_t wd[NT][4];
+            float scale[NT][4];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                nan_scale[nt] |= sc[d][nt] == 255u;
-                scale[nt] = as_f(sc[d][nt] << 23);  // e8m0 code in the exponent field
-                wd[nt][0] = wv[d][nt].x;
-                wd[nt][1] = wv[d][nt].y;
-                wd[nt][2] = wv[d][nt].z;
-                wd[nt][3] = wv[d][nt].w;
+                // lane (col, grp) holds dword t of block grp (T[grp][t]); after
+                // the swaps wd[t] holds T[t][grp]: dword grp of block t
+                const auto p02 = __builtin_amdgcn_permlane32_swap(wv[d][nt].x, wv[d][nt].z, false, false);
+                const auto p13 = __builtin_amdgcn_permlane32_swap(wv[d][nt].y, wv[d][nt].w, false, false);
+                const auto q01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
+                const auto q23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
+                wd[nt][0] = q01[0];
+                wd[nt][1] = q01[1];
+                wd[nt][2] = q23[0];
+                wd[nt][3] = q23[1];
+                // byte t of `all` = the scale code of block t of row col
+                const uint32_t mine = sc[d][nt] << (8 * grp);
+                const auto g16 = __builtin_amdgcn_permlane16_swap(mine, mine, false, false);
+                const uint32_t pair = g16[0] | g16[1];  // rows 0,1: bytes 0,1; rows 2,3: bytes 2,3
+                const auto g32 = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);
+                const uint32_t all = g32[0] | g32[1];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) scale[nt][t] = e8m0_value((all >> (8 * t)) & 0xFFu);
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const uint4 a = xt[col * 16 + ((4 * grp + t) ^ col)];
+                const uint4 a = xt[col * 16 + ((4 * t + grp) ^ col)];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
+                    constexpr float kUnit = 1.0f;  // convert at scale 2^0
                     const uint4 b = {
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], scale[nt], 0)),
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], scale[nt], 1)),
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], scale[nt], 2)),
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], scale[nt], 3))};
-                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), acc[nt],
-                        0, 0, 0);
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], kUnit, 0)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], kUnit, 1)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], kUnit, 2)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], kUnit, 3))};
+                    const f32x4_t blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                        f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc[nt][v] = __builtin_fmaf(blk[v], scale[nt][t], acc[nt][v]);
                 }
             }
             __builtin_amdgcn_wave_barrier();
-        }
-    }
-    // a NaN scale anywhere in a row's blocks of this chunk: that row is NaN
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const uint64_t flagged = __ballot(nan_scale[nt]);
-        const uint32_t rows_nan =
-            (uint32_t)((flagged | flagged >> 16 | flagged >> 32 | flagged >> 48) & 0xFFFFu);
-        if ((rows_nan >> col) & 1u) {
-            const float q = __builtin_nanf("");
-            acc[nt] = f32x4_t{q, q, q, q};
         }
     }
     if (S > 1) {

@@ -2,8 +2,10 @@
 //
 // Serves the small-matrix path (M <= 2, "Hyper Optimizing Kimi K3 in vLLM"
 // deepnotes page, Method details §1: a dedicated kernel at batch 1-2) and
-// split-K for 3 <= M <= 15 (same section: the accumulation dimension is
-// spread over more compute units), where the batch is too small for a
+// vector-ALU split-K (same section: the accumulation dimension is spread
+// over more compute units), which the planner picks for 3 <= M <= 7 (6 and 7
+// only where the matrix-core team kernel would not fill the GPU) and which a
+// forced plan can run up to M = 15: there the batch is too small for a
 // matrix-core tile to be a real dense contraction.
 //
 // Mapping (MI355X, wave64).  A wave owns one K chunk of whole W rows: lane l

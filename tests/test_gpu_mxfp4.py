@@ -76,16 +76,15 @@ def test_mxfp4_integer_bit_exact(M, N, K):
 
 
 @pytest.mark.parametrize("M,N", [(3, 24), (12, 24), (12, 8200)])
-def test_mxfp4_nan_scale_and_extremes(M, N):
+def test_mxfp4_nan_scale_and_zero_codes(M, N):
     # vector kernel (M = 3), matrix-core kernel with one and with two row tiles a wave
-    announce(f"mxfp4 NaN scale, extreme scales, zero codes M={M} N={N}")
+    announce(f"mxfp4 NaN scale, zero codes M={M} N={N}")
     K = 512
     x = si.normal_bf16((M, K), 1.0, 8400 + M, DEV)
     codes, scales = si.mxfp4_weights(N, K, 8401, DEV)
     scales[5, 3] = 255      # NaN block: row 5 is NaN for every m
     scales[N - 5, 0] = 255  # and row N - 5 (the second row tile of the last pair at N = 8200)
     scales[7, :] = 200      # large scale, 2^73 (finite fp32 sums for these x)
-    scales[9, :] = 16       # small scale, 2^-111: products stay normal in fp32
     codes[11, :] = 0        # all +0 codes
     codes[12, :] = 0x88     # all -0 codes
     y32, _ = run(x, codes, scales, bf16=False)
@@ -94,8 +93,49 @@ def test_mxfp4_nan_scale_and_extremes(M, N):
     nan_rows = [5, N - 5]
     assert np.isnan(y[:, nan_rows]).all() and not np.isnan(np.delete(y, nan_rows, axis=1)).any()
     keep = [n for n in range(N) if n not in nan_rows]
-    check_f32(y32[:, keep], ref[:, keep], A[:, keep], "mxfp4 extremes")
+    check_f32(y32[:, keep], ref[:, keep], A[:, keep], "mxfp4 NaN/zero rows")
     assert (y[:, 11] == 0).all() and (y[:, 12] == 0).all()
+
+
+# Every scale code 0..254 is a valid OCP e8m0 scale (2^-127 .. 2^127).  The
+# kernels scale each block's fp32 sum, so the products stay exact down to
+# code 0 (whose weights are below bf16's and fp32's normal range) and up to
+# code 254 (whose weights can exceed the largest bf16).
+@pytest.mark.parametrize("M,N", [(3, 40), (8, 40), (12, 40), (16, 40), (12, 8200), (16, 8192)])
+def test_mxfp4_scale_code_range(M, N):
+    # vector kernel (M = 3, 8), matrix-core kernel with one (N = 40) and two
+    # (N >= 8161) row tiles a wave
+    announce(f"mxfp4 scale codes 0..12, 120, 253, 254, mixed M={M} N={N}")
+    K = 640  # 20 blocks: 5 windows of the matrix-core kernel
+    KB = K // 32
+    codes, scales = si.mxfp4_weights(N, K, 8450 + N, DEV)
+    # low codes with x ~ N(0, 1): sums around 2^-120, some block sums subnormal
+    low = scales.clone()
+    for c in range(13):
+        low[c, :] = c                       # rows 0..12: scale code c on every block
+    low[13, :] = 120
+    low[14, :] = torch.tensor([0, 140] * (KB // 2), dtype=torch.uint8)    # 2^-127 and 2^13
+    low[15, :] = torch.tensor([(7 * b) % 41 + 100 for b in range(KB)], dtype=torch.uint8)
+    low[N - 1, :] = 1                      # the last row tile too
+    low[N - 17, :] = 0
+    x = si.normal_bf16((M, K), 1.0, 8460 + M, DEV)
+    y32, _ = run(x, codes, low, bf16=False)
+    ref, A = orc().projection_mxfp4(bits(x), np_u8(codes), np_u8(low))
+    check_f32(y32, ref, A, f"mxfp4 low scale codes M={M} N={N}")
+    assert (A[:, 0] > 0).all() and (np.abs(ref[:, 0]) < 2.0 ** -110).all()
+    # high codes with tiny x (2^-40 N(0, 1)): weights up to 6 * 2^127, above
+    # bf16's largest value, sums finite in fp32
+    high = scales.clone()
+    high[0, :] = 254
+    high[1, :] = 253
+    high[2, :] = 120
+    high[3, :] = torch.tensor([254, 200] * (KB // 2), dtype=torch.uint8)
+    high[N - 1, :] = 254
+    xs = si.normal_bf16((M, K), 2.0 ** -40, 8470 + M, DEV)
+    y32, _ = run(xs, codes, high, bf16=False)
+    ref, A = orc().projection_mxfp4(bits(xs), np_u8(codes), np_u8(high))
+    assert np.isfinite(ref).all() and np.abs(ref[:, 0]).max() > 2.0 ** 80
+    check_f32(y32, ref, A, f"mxfp4 high scale codes M={M} N={N}")
 
 
 def test_mxfp4_empty_and_rejected():
