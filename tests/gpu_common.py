@@ -9,6 +9,9 @@ inputs (both sides read the very same bf16 tensors):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -24,6 +27,26 @@ def orc() -> oracle.Oracle:
     if _ORACLE is None:
         _ORACLE = oracle.Oracle()
     return _ORACLE
+
+
+def _threads() -> int:
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, 16, int(cap) if cap.isdigit() and int(cap) > 0 else 16))
+
+
+def projection_all_rows(xb: np.ndarray, Wb: np.ndarray):
+    """oracle_projection (y and A) of every row of W, the rows split over host
+    threads: each thread runs the unchanged single-threaded oracle on its slice
+    (the C call releases the GIL)."""
+    N = Wb.shape[0]
+    t = _threads()
+    cuts = sorted({int(round(N * i / t)) for i in range(t + 1)})
+    with ThreadPoolExecutor(max_workers=t) as pool:
+        parts = list(pool.map(lambda ab: orc().projection(xb, Wb[ab[0]:ab[1]]),
+                              zip(cuts, cuts[1:])))
+    return (np.concatenate([p[0] for p in parts], axis=1),
+            np.concatenate([p[1] for p in parts], axis=1))
 
 
 def announce(msg: str) -> None:

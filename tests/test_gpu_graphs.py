@@ -111,7 +111,8 @@ def test_graph_grouped(T, tables):
     check_f32(eager[0], ref, A, f"graph grouped T={T}")
 
 
-@pytest.mark.parametrize("T,mode", [(2, "fused"), (16, "fused"), (16, "serial")])
+@pytest.mark.parametrize("T,mode", [(2, "fused"), (16, "fused"), (16, "serial"),
+                                     (2, "side_stream"), (16, "side_stream")])
 def test_graph_moe_step(T, mode):
     E, topk, N, Ns, K = 64, 8, 256, 128, 2048
     announce(f"graph moe step T={T} mode={mode}")
@@ -120,6 +121,8 @@ def test_graph_moe_step(T, mode):
     Wsh = si.normal_bf16((Ns, K), 0.02, 42002, DEV)
     if mode == "fused":
         Wr, Wsh = sg.concat_router_shared(Wr, Wsh)
+    # side_stream: the fork (event record + wait) and the join happen inside the
+    # capture, so the shared expert becomes a parallel branch of the graph
     We = si.normal_bf16((E, N, K), 0.02, 42003, DEV)
     ws = torch.empty(max(sg.skinny_moe_step_workspace(T, K, E, topk, N, Ns), 256),
                      dtype=torch.uint8, device=DEV)

@@ -156,6 +156,40 @@ def test_step_rejections_launch_nothing():
     assert counters_delta(before, sg.skinny_gemm_get_counters()) == [0] * sg.SG_NUM_COUNTERS
 
 
+@pytest.mark.parametrize("T", [1, 16])
+def test_step_side_stream_under_random_delays(T):
+    # Timing hazards of the two streams: random GPU sleeps on the caller's stream
+    # before the step (the fork waits for them) and on the side stream (the shared
+    # expert then starts anywhere from the router projection to the end of the
+    # routed experts), and x overwritten on the caller's stream right after the
+    # call (the join must hold that write back until the shared expert has read
+    # x).  Every run must equal the serial step bit for bit; the serial step is
+    # checked against the oracle.  T = 1 takes the launch that ranks the scores
+    # itself, T = 16 the separate top-k kernel.
+    K, E, N, Ns, topk = 2048, 64, 512, 2048, 8
+    x, Wr, We, Ws = weights(T, K, E, N, Ns, 7500 + T)
+    announce(f"moe step side stream under random delays T={T}: serial reference")
+    ref = sg.skinny_moe_step(x, Wr, We, Ws, topk, mode="serial")
+    torch.cuda.synchronize()
+    check_step(ref, x, Wr, We, Ws, topk, f"serial T={T}")
+    side, _, _ = sg._side_resources(x.device)
+    main = torch.cuda.current_stream()
+    g = torch.Generator().manual_seed(11 + T)
+    for it in range(12):
+        announce(f"moe step side stream T={T} iteration {it}")
+        xr = x.clone()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(int(torch.randint(0, 60000, (1,), generator=g)))
+        torch.cuda._sleep(int(torch.randint(0, 30000, (1,), generator=g)))
+        got = sg.skinny_moe_step(xr, Wr, We, Ws, topk, mode="side_stream")
+        xr.fill_(3.0)  # on the caller's stream, right after the call
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), f"iteration {it}: output {i} differs from the serial step"
+    assert main.query()
+
+
 @pytest.fixture(scope="module")
 def full_set():
     """E=384 experts of N=2048 x K=7168 (11.3 GB), the router [384, 7168] and a shared

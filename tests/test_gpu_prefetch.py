@@ -1,15 +1,23 @@
 """Side-stream weight prefetch: reads only the given weights, changes no
 result, and stays correct under random launch timing on both streams (the
-timing-dependent hazard class the pages warn about)."""
+timing-dependent hazard class the pages warn about).  The projections that
+follow a prefetch are checked against the fp64 oracle on sampled rows, and
+bit for bit against the same projection without a prefetch."""
 import pytest
 import torch
 
 import seeded_inputs as si
 import skinny_gemm_projection_amd as sg
-from gpu_common import DEV, announce, counters_delta
+from gpu_common import DEV, announce, bits, check_f32, counters_delta, orc, sample_rows
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
+
+
+def check_rows(y, x, W, what, count=64, seed=0):
+    rows = sample_rows(W.shape[0], count, seed)
+    ref, A = orc().projection(bits(x), bits(W[torch.as_tensor(rows, device=W.device)]))
+    check_f32(y[:, torch.as_tensor(rows, device=y.device)], ref, A, what)
 
 
 def test_prefetch_changes_nothing():
@@ -28,6 +36,7 @@ def test_prefetch_changes_nothing():
     torch.cuda.synchronize()
     assert counters_delta(before, sg.skinny_gemm_get_counters())[sg.SG_KERNEL_PREFETCH] == 1
     assert torch.equal(y, ref)
+    check_rows(y, x, W, "projection after a prefetch", 128, 6002)
     assert torch.equal(W, W_copy), "prefetch must not write"
     sg.skinny_gemm_prefetch(W, nbytes=4096 * 7 + 16)  # a partial range
     torch.cuda.synchronize()
@@ -44,6 +53,8 @@ def test_prefetch_on_side_stream_under_random_delays():
         sg.skinny_gemm(plan, x, W, y_f32=r)
         refs.append(r)
     torch.cuda.synchronize()
+    for i, (W, r) in enumerate(zip(Ws, refs)):
+        check_rows(r, x, W, f"projection {i} of the prefetch ring", 48, 6110 + i)
     side = torch.cuda.Stream()
     main = torch.cuda.current_stream()
     g = torch.Generator().manual_seed(3)

@@ -1,11 +1,15 @@
 """GPU parity of the projection paths through the C ABI: small-matrix kernel
-(M <= 2), VALU split-K (3 <= M <= 15), bf16 matrix-core split-K (M >= 16),
-the deterministic reduction and the fused residual epilogue.
+(M <= 2), VALU split-K (the planner's choice for 3 <= M <= 7; forced up to
+M = 15), bf16 matrix-core split-K (the planner's choice from M = 8, from M = 6
+where its workgroups fill the GPU; the in-workgroup team kernel and the chunk
+kernel with its reduction), the deterministic reduction and the fused
+residual epilogue.
 
 Every output is compared element by element with the fp64 oracle on the same
 seeded bf16 inputs: exhaustively at sizes that span several tiles and a
-ragged tail, and on sampled rows at the full workload sizes (the plan the
-benchmark times).  Integer-valued inputs make every sum exact, so there all
+ragged tail, and at the full workload sizes on the plan the planner picks
+(the plan the benchmark times) -- every output there too -- and on sampled
+rows for the forced split sweep.  Integer-valued inputs make every sum exact, so there all
 kernels, splits and output types must match the oracle bit for bit.
 """
 import numpy as np
@@ -15,7 +19,7 @@ import torch
 import seeded_inputs as si
 import skinny_gemm_projection_amd as sg
 from gpu_common import (DEV, announce, bits, check_bf16, check_exact, check_f32, counters_delta,
-                        orc, sample_rows, to_np)
+                        orc, projection_all_rows, sample_rows, to_np)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
@@ -44,11 +48,12 @@ def run(plan, x, W, r=None, f32=True, bf16=True, inplace=False):
 
 
 def oracle_rows(x, W, rows=None):
-    """Oracle y and A for all M rows of x against the chosen rows of W."""
+    """Oracle y and A for all M rows of x against the chosen rows of W (every row of W
+    when rows is None, split over host threads)."""
     Wb = bits(W)
-    if rows is not None:
-        Wb = Wb[rows]
-    return orc().projection(bits(x), Wb)
+    if rows is None:
+        return projection_all_rows(bits(x), Wb)
+    return orc().projection(bits(x), Wb[rows])
 
 
 def plan_or_skip(M, N, K, kernel, S, two_pass=-1, tile_n=0):
@@ -180,8 +185,8 @@ def _full_case(M, N, K, seed, kernel=None, S=0, rows=256, residual=False, inplac
             else plan_or_skip(M, N, K, kernel, S, tp, tile))
     announce(f"full M={M} N={N} K={K} plan={plan} residual={residual} inplace={inplace}")
     y32, y16, _ = run(plan, x, W, r=r, inplace=inplace)
-    sel = sample_rows(N, rows, seed)
-    y, A = oracle_rows(x, W, sel)
+    sel = np.arange(N) if rows is None else sample_rows(N, rows, seed)
+    y, A = oracle_rows(x, W, None if rows is None else sel)
     if residual:
         ref = orc().residual(bits(r_before)[:, sel], y)
         check_f32(y32[:, sel], ref, A, f"residual fp32 {plan}", extra=2.0 ** -23 * np.abs(ref))
@@ -206,13 +211,13 @@ def test_full_single_projection_1024():
 
 @pytest.mark.parametrize("M", [1, 2])
 def test_full_small_batch_7168x8192(M):
-    plan = _full_case(M, 8192, 7168, 2000, rows=1024)
+    plan = _full_case(M, 8192, 7168, 2000, rows=None)
     assert plan.kernel == G and plan.split_k == 1
 
 
 @pytest.mark.parametrize("M", [3, 4, 8, 12, 16, 32, 64])
 def test_full_splitk_sweep_auto(M):
-    plan = _full_case(M, 4096, 7168, 3000)
+    plan = _full_case(M, 4096, 7168, 3000, rows=None)
     assert plan.split_k > 1
 
 
@@ -233,7 +238,7 @@ def test_full_mfma_32_rows_per_wave(M, S):
 @pytest.mark.parametrize("M", [1, 8, 64])
 @pytest.mark.parametrize("inplace", [False, True])
 def test_full_residual_8192x7168(M, inplace):
-    _full_case(M, 7168, 8192, 4000, residual=True, inplace=inplace)
+    _full_case(M, 7168, 8192, 4000, residual=True, inplace=inplace, rows=None)
 
 
 # ------------------------------------------------------------------ properties and edge cases
