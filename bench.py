@@ -674,26 +674,142 @@ def sweep(torch, sg, si, L, cyc, reps=40):
 # --------------------------------------------------------------------------- CPU baseline
 
 
-def cpu_baseline(si, inputs, budget_s=10.0):
-    """The fp64 oracle, as it stands, on full projections of the same workload."""
+def _host_threads() -> int:
+    """Worker threads for the oracle: the cores this process may run on, capped by
+    OMP_NUM_THREADS when the host sets it (the share of the host one GPU gets)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rows(o, pool, threads, xb, Wb):
+    """The oracle's projection over row slices of W, one slice per thread (the C call
+    releases the GIL, so the slices run in parallel); the oracle itself is unchanged."""
+    import numpy as np
+    N = Wb.shape[0]
+    cuts = sorted({int(round(N * i / threads)) for i in range(threads + 1)})
+    futs = [pool.submit(o.projection, xb, Wb[a:b], False) for a, b in zip(cuts, cuts[1:])]
+    return np.concatenate([f.result() for f in futs], axis=1)
+
+
+def _time_loop(fn, budget_s):
+    """Calls fn until budget_s has passed (at least once); returns (calls, seconds)."""
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        calls += 1
+        if time.perf_counter() - t0 >= budget_s:
+            return calls, time.perf_counter() - t0
+
+
+def cpu_baseline(si, inputs, budget_s=8.0, sample_rows=512):
+    """The fp64 oracle, as it stands, on this host: single-threaded and over row slices
+    on every available core, on full M = 1 and M = 2 projections of the headline
+    workload; then per workload configuration (full projections on all cores,
+    single-threaded on a row sample scaled to the full matrix)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
     import oracle
+
     o = oracle.Oracle()
+    threads = _host_threads()
     x, W0 = inputs
     Wb = si.bits(W0)
     xb = {M: si.bits(x[M]) for M in M_LIST}
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        for M in M_LIST:
-            o.projection(xb[M], Wb)
-        steps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    elapsed = time.perf_counter() - t0
     step_bytes = sum(proj_bytes(M, N_MAIN, K_MAIN) for M in M_LIST)
-    return {"value": round(step_bytes * steps / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{steps} full steps (M=1 and M=2 projections, K=7168, N=8192, fp64 "
-                      f"single-threaded C) in {elapsed:.1f} s"}
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        n1, t1 = _time_loop(lambda: [o.projection(xb[M], Wb, False) for M in M_LIST],
+                            budget_s / 2)
+        nt, tt = _time_loop(lambda: [_oracle_rows(o, pool, threads, xb[M], Wb) for M in M_LIST],
+                            budget_s / 2)
+        single_gbs = step_bytes * n1 / t1 / 1e9
+        multi_gbs = step_bytes * nt / tt / 1e9
+
+        def host_bf16(shape, sigma, seed):
+            return si.bits(si.normal_bf16(shape, sigma, seed, "cpu"))
+
+        per_config = []
+
+        def add(workload, M, N, K, nbytes, full_fn, sample_fn, rows):
+            # all cores on the full projection; one core on `rows` rows, scaled to N
+            n_f, t_f = _time_loop(full_fn, 0.0)
+            n_s, t_s = _time_loop(sample_fn, 0.0)
+            ms_all = 1e3 * t_f / n_f
+            ms_one = 1e3 * t_s / n_s * N / rows
+            per_config.append({
+                "workload": workload, "M": M, "N": N, "K": K,
+                "ms_single": round(ms_one, 3), "GBps_single": round(nbytes / ms_one / 1e6, 4),
+                "ms_threads": round(ms_all, 3), "GBps_threads": round(nbytes / ms_all / 1e6, 4),
+                "single_sample_rows": rows})
+
+        # single decode projection 1024 x 1024 (every row in both legs)
+        x1, W1 = host_bf16((1, 1024), 0.02, 1000), host_bf16((1024, 1024), 0.02, 1001)
+        add("single decode projection", 1, 1024, 1024, proj_bytes(1, 1024, 1024, bf16=False),
+            lambda: _oracle_rows(o, pool, threads, x1, W1), lambda: o.projection(x1, W1, False),
+            1024)
+        # small batch 8192 x 7168 (the headline legs above, per batch size)
+        for M in M_LIST:
+            nb = proj_bytes(M, N_MAIN, K_MAIN)
+            add("small batch (headline)", M, N_MAIN, K_MAIN, nb,
+                lambda M=M: _oracle_rows(o, pool, threads, xb[M], Wb),
+                lambda M=M: o.projection(xb[M], Wb[:sample_rows], False), sample_rows)
+        # split-K sweep 4096 x 7168
+        W3 = host_bf16((4096, 7168), 0.02, 3001)
+        for M in (4, 8, 16, 32, 64):
+            x3 = host_bf16((M, 7168), 1.0, 3000 + M)
+            add("split-K sweep", M, 4096, 7168, proj_bytes(M, 4096, 7168, bf16=False),
+                lambda x3=x3: _oracle_rows(o, pool, threads, x3, W3),
+                lambda x3=x3: o.projection(x3, W3[:sample_rows], False), sample_rows)
+        del W3
+        # fused residual 7168 x 8192 (projection, then the residual add)
+        W4 = host_bf16((7168, 8192), 0.02, 4001)
+        for M in (1, 8, 64):
+            x4, r4 = host_bf16((M, 8192), 1.0, 4000 + M), host_bf16((M, 7168), 1.0, 4002 + M)
+            add("fused residual", M, 7168, 8192,
+                proj_bytes(M, 7168, 8192, f32=False, residual=True),
+                lambda x4=x4, r4=r4: o.residual(r4, _oracle_rows(o, pool, threads, x4, W4)),
+                lambda x4=x4, r4=r4: o.residual(r4[:, :sample_rows],
+                                                o.projection(x4, W4[:sample_rows], False)),
+                sample_rows)
+        del W4
+        # MoE grouped, one token routed to 8 experts of 2048 x 7168: the 8 experts'
+        # weights only (the other 376 are never read); all cores take one pair each
+        We = host_bf16((8, 2048, 7168), 0.02, 5100)
+        x5 = host_bf16((1, 7168), 1.0, 5000)
+        ids = np.arange(8, dtype=np.int32).reshape(1, 8)
+        nb5 = 8 * 2048 * 7168 * 2 + 7168 * 2 + 8 * 2048 * 4
+        add("MoE grouped E=384 top8, T=1", 1, 2048, 7168, nb5,
+            lambda: [f.result() for f in [pool.submit(o.grouped, x5, We, ids[:, j:j + 1], False)
+                                          for j in range(8)]],
+            lambda: o.grouped(x5, We, ids[:, :1], False), 2048 // 8)
+        del We
+    return {"value": round(multi_gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "single": {"value": round(single_gbs, 4), "unit": "GB/s", "cores": 1},
+            "threads": threads,
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": _cpu_model(),
+            "sample": f"headline: {nt} full steps (M=1 and M=2 projections, K=7168, N=8192) over "
+                      f"{threads} threads (row slices of W, one fp64 C oracle call each) in "
+                      f"{tt:.1f} s; single-threaded {n1} steps in {t1:.1f} s. per_config: full "
+                      f"projections on {threads} threads; single-threaded time measured on the "
+                      f"first {sample_rows} rows of W (MoE: one of the 8 pairs) and scaled to "
+                      f"the full matrix; MoE at T=1 only (larger T needs the whole 11 GB "
+                      f"expert set on the host)",
+            "per_config": per_config}
 
 
 # --------------------------------------------------------------------------- traffic (PMC)
