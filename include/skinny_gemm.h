@@ -145,6 +145,22 @@ sg_status skinny_gemm(const sg_plan* plan, const sg_bf16* x, const sg_bf16* W,
                       float* y_f32, sg_bf16* y_bf16,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* skinny_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture that must not call hipMalloc, tight serving loops, harnesses
+ * that forbid allocation).  Same plan, inputs, outputs, kernels and results
+ * as skinny_gemm; the split-K partials of two-pass plans go to a scratch
+ * array of SG_NOALLOC_MAX_WORKSPACE bytes inside the library, one per GPU,
+ * held from the first call on that GPU until the process ends (the first call
+ * on a device looks up its address there: the current device must be the
+ * one the stream and buffers belong to).  A plan whose workspace_bytes
+ * exceeds SG_NOALLOC_MAX_WORKSPACE returns SG_ERR_WORKSPACE (no launch).  The
+ * call allocates nothing.  All calls on one GPU share its scratch array:
+ * calls that overlap in time on one GPU (other streams, other host threads)
+ * race on it and must be serialised by the caller. */
+#define SG_NOALLOC_MAX_WORKSPACE ((size_t)16 << 20)
+sg_status skinny_gemm_noalloc(const sg_plan* plan, const sg_bf16* x, const sg_bf16* W,
+                              float* y_f32, sg_bf16* y_bf16, void* stream);
+
 /* Fused residual epilogue ([P] Method details §2): out = r + x W^T, with the
  * fp32 accumulator added to r in fp32 and rounded once.  out_bf16 [M,N]
  * and/or out_f32 [M,N]; out_bf16 may be the same pointer as r (in place;

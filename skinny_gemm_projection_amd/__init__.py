@@ -19,12 +19,13 @@ from . import _lib
 from ._lib import (KERNEL_NAMES, SG_KERNEL_GEMV, SG_KERNEL_GROUPED, SG_KERNEL_MOE_TABLE,
                    SG_KERNEL_FP8, SG_KERNEL_MXFP4, SG_KERNEL_NONE, SG_KERNEL_PREFETCH, SG_KERNEL_REDUCE,
                    SG_KERNEL_ROUTER_TOPK,
-                   SG_KERNEL_SPLITK_MFMA, SG_KERNEL_SPLITK_VALU, SG_NUM_COUNTERS, SgMoeStep,
+                   SG_KERNEL_SPLITK_MFMA, SG_KERNEL_SPLITK_VALU, SG_NOALLOC_MAX_WORKSPACE,
+                   SG_NUM_COUNTERS, SgMoeStep,
                    SgPlan, SkinnyGemmError)
 
 __all__ = [
     "skinny_gemm_plan", "skinny_gemm_plan_force", "skinny_gemm", "skinny_gemm_residual",
-    "grouped_skinny_gemm_workspace", "grouped_skinny_gemm", "skinny_gemm_prefetch",
+    "skinny_gemm_noalloc", "SG_NOALLOC_MAX_WORKSPACE", "grouped_skinny_gemm_workspace", "grouped_skinny_gemm", "skinny_gemm_prefetch",
     "skinny_gemm_router_topk", "router_topk", "skinny_moe_step_workspace", "skinny_moe_step",
     "concat_router_shared", "MOE_STEP_MODES", "skinny_gemm_mxfp4", "SG_KERNEL_MXFP4",
     "skinny_gemm_fp8", "SG_KERNEL_FP8",
@@ -125,6 +126,21 @@ def skinny_gemm(plan: SgPlan, x: torch.Tensor, W: torch.Tensor, y_f32=None, y_bf
                           ws_bytes, _stream(stream))
     _lib.check(st)
     return ws
+
+
+def skinny_gemm_noalloc(plan: SgPlan, x: torch.Tensor, W: torch.Tensor, y_f32=None,
+                        y_bf16=None, stream=None):
+    """skinny_gemm without a workspace: split-K partials go to the library's own
+    per-GPU scratch array (calls overlapping on one GPU race on it)."""
+    dev = x.device
+    M, N, K = plan.M, plan.N, plan.K
+    _shape(x, (M, K), "x"), _shape(W, (N, K), "W")
+    _shape(y_f32, (M, N), "y_f32"), _shape(y_bf16, (M, N), "y_bf16")
+    st = _c().skinny_gemm_noalloc(ctypes.byref(plan), _ptr(x, torch.bfloat16, "x", dev),
+                                  _ptr(W, torch.bfloat16, "W", dev),
+                                  _ptr(y_f32, torch.float32, "y_f32", dev),
+                                  _ptr(y_bf16, torch.bfloat16, "y_bf16", dev), _stream(stream))
+    _lib.check(st)
 
 
 def skinny_gemm_residual(plan: SgPlan, x: torch.Tensor, W: torch.Tensor, r: torch.Tensor,

@@ -62,6 +62,7 @@ class SgMoeStep(ctypes.Structure):
 
 
 SG_MOE_STEP_FUSED_SHARED = 1
+SG_NOALLOC_MAX_WORKSPACE = 16 << 20
 
 
 class SkinnyGemmError(RuntimeError):
@@ -90,6 +91,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.skinny_gemm_plan_force.argtypes = [i32, i32, i32, i32, i32, i32, i32, P]
     lib.skinny_gemm.argtypes = [P, p, p, p, p, p, sz, p]
     lib.skinny_gemm_residual.argtypes = [P, p, p, p, p, p, p, sz, p]
+    lib.skinny_gemm_noalloc.argtypes = [P, p, p, p, p, p]
     lib.grouped_skinny_gemm_workspace.argtypes = [i32, i32, i32, i32, i32]
     lib.grouped_skinny_gemm_workspace.restype = sz
     lib.grouped_skinny_gemm.argtypes = [p, i32, p, i32, i32, i32, p, i32, p, p, p, p, p, sz, p]
@@ -107,7 +109,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.skinny_gemm_reset_counters.argtypes = []
     lib.skinny_gemm_reset_counters.restype = None
     for name in ("skinny_gemm_plan", "skinny_gemm_plan_force", "skinny_gemm",
-                 "skinny_gemm_residual", "grouped_skinny_gemm", "skinny_gemm_prefetch",
+                 "skinny_gemm_residual", "skinny_gemm_noalloc", "grouped_skinny_gemm", "skinny_gemm_prefetch",
                  "skinny_gemm_router_topk", "skinny_moe_step", "skinny_gemm_mxfp4",
                  "skinny_gemm_fp8"):
         getattr(lib, name).restype = ctypes.c_int
