@@ -496,9 +496,9 @@ def sweep(torch, sg, si, L, cyc, reps=40):
     # MXFP4 weights (e2m1 codes + e8m0 block scales): the same shapes at a quarter of the
     # weight bytes; a ring of code/scale copies larger than 2 x MALL per shape
     c = L.c
-    for label, Ms, N, K, residual in (("mxfp4 8192x7168", (1, 2, 16), 8192, 7168, False),
-                                      ("mxfp4 4096x7168", (4, 8, 16), 4096, 7168, False),
-                                      ("mxfp4 residual 7168x8192", (1, 8), 7168, 8192, True)):
+    for label, Ms, N, K, residual in (("mxfp4 8192x7168", (1, 2, 16, 64), 8192, 7168, False),
+                                      ("mxfp4 4096x7168", (4, 8, 16, 32, 64), 4096, 7168, False),
+                                      ("mxfp4 residual 7168x8192", (1, 8, 64), 7168, 8192, True)):
         codes, scales = si.mxfp4_weights(N, K, si.seed_for(6, si.TAG_W) + N, dev)
         per_copy = codes.numel() + scales.numel()
         copies = max(1, math.ceil(RING_MIN_BYTES / per_copy))
@@ -509,10 +509,14 @@ def sweep(torch, sg, si, L, cyc, reps=40):
             y32 = None if residual else torch.empty((M, N), device=dev)
             y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
-            def mx(cw, sw, x=x, r=r, y32=y32, y16=y16, M=M, N=N, K=K):
+            wsb = sg.skinny_gemm_lowp_workspace(M, N, K)
+            ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+
+            def mx(cw, sw, x=x, r=r, y32=y32, y16=y16, M=M, N=N, K=K, ws=ws, wsb=wsb):
                 args = (M, N, K, x.data_ptr(), cw.data_ptr(), sw.data_ptr(),
                         r.data_ptr() if r is not None else None,
-                        y32.data_ptr() if y32 is not None else None, y16.data_ptr(), L.sp)
+                        y32.data_ptr() if y32 is not None else None, y16.data_ptr(),
+                        ws.data_ptr(), wsb, L.sp)
 
                 def go():
                     st = c.skinny_gemm_mxfp4(*args)
@@ -525,7 +529,8 @@ def sweep(torch, sg, si, L, cyc, reps=40):
             us = 1e3 * per
             gbs = nbytes / (per * 1e-3) / 1e9
             rows.append({"workload": label, "M": M, "N": N, "K": K,
-                         "plan": "mxfp4_mfma" if M >= 9 else "mxfp4_rowdot",
+                         "plan": ("lowp_chunk + reduce" if wsb else "lowp_chunk") if M >= 17
+                         else "mxfp4_mfma" if M >= 9 else "mxfp4_rowdot",
                          "us": round(us, 3), "GBps": round(gbs, 1),
                          "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
         del ring
@@ -533,9 +538,9 @@ def sweep(torch, sg, si, L, cyc, reps=40):
 
     # FP8 e4m3 weights with 128 x 128 fp32 block scales: half the bf16 weight bytes; a ring
     # of code/scale copies larger than 2 x MALL per shape
-    for label, Ms, N, K, residual in (("fp8 8192x7168", (1, 2, 16), 8192, 7168, False),
-                                      ("fp8 4096x7168", (4, 8, 16), 4096, 7168, False),
-                                      ("fp8 residual 7168x8192", (1,), 7168, 8192, True)):
+    for label, Ms, N, K, residual in (("fp8 8192x7168", (1, 2, 16, 64), 8192, 7168, False),
+                                      ("fp8 4096x7168", (4, 8, 16, 32, 64), 4096, 7168, False),
+                                      ("fp8 residual 7168x8192", (1, 64), 7168, 8192, True)):
         codes, scales = si.fp8_weights(N, K, si.seed_for(7, si.TAG_W) + N, dev)
         per_copy = codes.numel() + scales.numel() * 4
         copies = max(1, math.ceil(RING_MIN_BYTES / per_copy))
@@ -546,10 +551,14 @@ def sweep(torch, sg, si, L, cyc, reps=40):
             y32 = None if residual else torch.empty((M, N), device=dev)
             y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
-            def f8(cw, sw, x=x, r=r, y32=y32, y16=y16, M=M, N=N, K=K):
+            wsb = sg.skinny_gemm_lowp_workspace(M, N, K)
+            ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+
+            def f8(cw, sw, x=x, r=r, y32=y32, y16=y16, M=M, N=N, K=K, ws=ws, wsb=wsb):
                 args = (M, N, K, x.data_ptr(), cw.data_ptr(), sw.data_ptr(),
                         r.data_ptr() if r is not None else None,
-                        y32.data_ptr() if y32 is not None else None, y16.data_ptr(), L.sp)
+                        y32.data_ptr() if y32 is not None else None, y16.data_ptr(),
+                        ws.data_ptr(), wsb, L.sp)
 
                 def go():
                     st = c.skinny_gemm_fp8(*args)
@@ -562,7 +571,8 @@ def sweep(torch, sg, si, L, cyc, reps=40):
             us = 1e3 * per
             gbs = nbytes / (per * 1e-3) / 1e9
             rows.append({"workload": label, "M": M, "N": N, "K": K,
-                         "plan": "fp8_mfma" if M >= 5 else "fp8_rowdot",
+                         "plan": ("lowp_chunk + reduce" if wsb else "lowp_chunk") if M >= 17
+                         else "fp8_mfma" if M >= 5 else "fp8_rowdot",
                          "us": round(us, 3), "GBps": round(gbs, 1),
                          "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
         del ring
@@ -992,34 +1002,39 @@ def profile_workloads(torch, sg, si, L, manifest_path, reps=3):
     torch.cuda.empty_cache()
     # MXFP4 weights
     for label, Ms, N, K in (("mxfp4 8192x7168", (1, 2, 16), 8192, 7168),
-                            ("mxfp4 4096x7168", (4, 8, 16), 4096, 7168)):
+                            ("mxfp4 4096x7168", (4, 8, 16, 64), 4096, 7168)):
         codes, scales = si.mxfp4_weights(N, K, 17, dev)
         ring = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(reps - 1)]
         for M in Ms:
             x = si.normal_bf16((M, K), 1.0, 18, dev)
             y32 = torch.empty((M, N), device=dev)
             y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(max(sg.skinny_gemm_lowp_workspace(M, N, K), 256),
+                             dtype=torch.uint8, device=dev)
 
-            def mx(cw, sw, x=x, y32=y32, y16=y16, M=M, N=N, K=K):
-                return lambda: sg.skinny_gemm_mxfp4(x, cw, sw, y_f32=y32, y_bf16=y16)
+            def mx(cw, sw, x=x, y32=y32, y16=y16, ws=ws):
+                return lambda: sg.skinny_gemm_mxfp4(x, cw, sw, y_f32=y32, y_bf16=y16, workspace=ws)
             nbytes = N * K // 2 + N * K // 32 + M * K * 2 + M * N * 6
-            run(label, M, N, K, "mxfp4_mfma" if M >= 9 else "mxfp4_rowdot",
-                [mx(cw, sw) for cw, sw in ring], nbytes)
+            run(label, M, N, K, "lowp_chunk" if M >= 17 else "mxfp4_mfma" if M >= 9
+                else "mxfp4_rowdot", [mx(cw, sw) for cw, sw in ring], nbytes)
         del ring
     # FP8 weights (e4m3 codes, 128 x 128 block scales)
     for label, Ms, N, K in (("fp8 8192x7168", (1, 2, 16), 8192, 7168),
-                            ("fp8 4096x7168", (4, 8, 16), 4096, 7168)):
+                            ("fp8 4096x7168", (4, 8, 16, 64), 4096, 7168)):
         codes, scales = si.fp8_weights(N, K, 21, dev)
         ring = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(reps - 1)]
         for M in Ms:
             x = si.normal_bf16((M, K), 1.0, 22, dev)
             y32 = torch.empty((M, N), device=dev)
             y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(max(sg.skinny_gemm_lowp_workspace(M, N, K), 256),
+                             dtype=torch.uint8, device=dev)
 
-            def f8(cw, sw, x=x, y32=y32, y16=y16):
-                return lambda: sg.skinny_gemm_fp8(x, cw, sw, y_f32=y32, y_bf16=y16)
+            def f8(cw, sw, x=x, y32=y32, y16=y16, ws=ws):
+                return lambda: sg.skinny_gemm_fp8(x, cw, sw, y_f32=y32, y_bf16=y16, workspace=ws)
             nbytes = N * K + scales.numel() * 4 + M * K * 2 + M * N * 6
-            run(label, M, N, K, "fp8_mfma" if M >= 5 else "fp8_rowdot", [f8(cw, sw) for cw, sw in ring], nbytes)
+            run(label, M, N, K, "lowp_chunk" if M >= 17 else "fp8_mfma" if M >= 5 else "fp8_rowdot",
+                [f8(cw, sw) for cw, sw in ring], nbytes)
         del ring
     # router scores + top-8 (E = 384, K = 7168)
     E, K, k = 384, 7168, 8

@@ -230,20 +230,69 @@ sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int
     return sg::router_topk_call(scores, E, T, E, k, topk_ids, topk_scores, stream);
 }
 
+size_t skinny_gemm_lowp_workspace(int32_t M, int32_t N, int32_t K) {
+    if (M < sg::kLowpChunkFromM || M > sg::kLowpMaxM || N < 1 || N > (1 << 20) || K < 0 ||
+        K > (1 << 20))
+        return 0;
+    sg::LowpChunkPlan lp;
+    return sg::lowp_chunk_plan(M, N, K, &lp) ? lp.workspace : 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The 17..64-row path shared by both formats: the split plan, the workspace
+// check, then the chunk kernel (and the reduction when the plan splits K).
+sg_status lowp_chunk_call(int fmt, int32_t M, int32_t N, int32_t K, const sg_bf16* x,
+                          const void* W_codes, const void* W_scales, const sg_bf16* r,
+                          float* y_f32, sg_bf16* y_bf16, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    sg::LowpChunkPlan lp;
+    if (!sg::lowp_chunk_plan(M, N, K, &lp)) return SG_ERR_UNSUPPORTED;
+    if (lp.workspace > 0) {
+        if (!workspace || workspace_bytes < lp.workspace) return SG_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return SG_ERR_ALIGN;
+    }
+    (void)hipGetLastError();
+    const sg::Epilogue fin{nullptr, y_f32, y_bf16, r};
+    if (sg::launch_lowp_chunk(fmt, M, N, K, x, W_codes, W_scales, fin, workspace,
+                              static_cast<hipStream_t>(stream)) != hipSuccess)
+        return SG_ERR_HIP;
+    count(fmt == sg::kLowpFp8 ? SG_KERNEL_FP8 : SG_KERNEL_MXFP4);
+    if (lp.S > 1) count(SG_KERNEL_REDUCE);
+    if (log_enabled())
+        std::fprintf(stderr, "[skinny_gemm] %s M=%d N=%d K=%d chunk kernel %d-row tiles S=%d%s%s\n",
+                     fmt == sg::kLowpFp8 ? "fp8" : "mxfp4", M, N, K, 128 * lp.NT, lp.S,
+                     lp.S > 1 ? " +reduce pass" : "", r ? " residual" : "");
+    return SG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
                             const uint8_t* W_codes, const uint8_t* W_scales, const sg_bf16* r,
-                            float* y_f32, sg_bf16* y_bf16, void* stream) {
+                            float* y_f32, sg_bf16* y_bf16, void* workspace,
+                            size_t workspace_bytes, void* stream) {
     if (M < 0 || N < 0 || N > (1 << 20) || K < 0 || K > (1 << 20)) return SG_ERR_SHAPE;
-    if (M > sg::kMxfp4MaxM) return SG_ERR_UNSUPPORTED;
+    if (M > sg::kLowpMaxM) return SG_ERR_UNSUPPORTED;
     if (K % 32 != 0) return SG_ERR_ALIGN;
+    const bool chunk = M >= sg::kLowpChunkFromM;
     int nb, splits;
-    if (!sg::mxfp4_split(M, K, &nb, &splits)) return SG_ERR_UNSUPPORTED;
+    if (M > 0 && !chunk && !sg::mxfp4_split(M, K, &nb, &splits)) return SG_ERR_UNSUPPORTED;
+    sg::LowpChunkPlan lp;
+    if (chunk && N > 0 && !sg::lowp_chunk_plan(M, N, K, &lp)) return SG_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return SG_OK;
     if (!y_f32 && !y_bf16) return SG_ERR_NULL;
     if (K > 0 && (!x || !W_codes || !W_scales)) return SG_ERR_NULL;
     if (!aligned16(x) || !aligned16(W_codes) || !aligned16(r) || !aligned16(y_f32) ||
         !aligned16(y_bf16))
         return SG_ERR_ALIGN;
+    if (chunk)
+        return lowp_chunk_call(sg::kLowpMxfp4, M, N, K, x, W_codes, W_scales, r, y_f32, y_bf16,
+                               workspace, workspace_bytes, stream);
     (void)hipGetLastError();
     const sg::Epilogue ep{nullptr, y_f32, y_bf16, r};
     if (sg::launch_mxfp4(M, N, K, x, W_codes, W_scales, ep, static_cast<hipStream_t>(stream)) !=
@@ -259,10 +308,15 @@ sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
 
 sg_status skinny_gemm_fp8(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
                           const uint8_t* W_codes, const float* W_scales, const sg_bf16* r,
-                          float* y_f32, sg_bf16* y_bf16, void* stream) {
+                          float* y_f32, sg_bf16* y_bf16, void* workspace, size_t workspace_bytes,
+                          void* stream) {
     if (M < 0 || N < 0 || N > (1 << 20) || K < 0 || K > (1 << 20)) return SG_ERR_SHAPE;
     if (K % 16 != 0) return SG_ERR_ALIGN;
-    if (M > sg::kFp8MaxM || (M > 0 && !sg::fp8_size_ok(M, K))) return SG_ERR_UNSUPPORTED;
+    if (M > sg::kLowpMaxM) return SG_ERR_UNSUPPORTED;
+    const bool chunk = M >= sg::kLowpChunkFromM;
+    if (M > 0 && !chunk && !sg::fp8_size_ok(M, K)) return SG_ERR_UNSUPPORTED;
+    sg::LowpChunkPlan lp;
+    if (chunk && N > 0 && !sg::lowp_chunk_plan(M, N, K, &lp)) return SG_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return SG_OK;
     if (!y_f32 && !y_bf16) return SG_ERR_NULL;
     if (K > 0 && (!x || !W_codes || !W_scales)) return SG_ERR_NULL;
@@ -270,6 +324,9 @@ sg_status skinny_gemm_fp8(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
     if (!aligned16(x) || !aligned16(W_codes) || !aligned4(W_scales) || !aligned16(r) ||
         !aligned16(y_f32) || !aligned16(y_bf16))
         return SG_ERR_ALIGN;
+    if (chunk)
+        return lowp_chunk_call(sg::kLowpFp8, M, N, K, x, W_codes, W_scales, r, y_f32, y_bf16,
+                               workspace, workspace_bytes, stream);
     int splits, chunk16, nch;
     if (!sg::fp8_split(M, N, K, &splits, &chunk16, &nch)) return SG_ERR_UNSUPPORTED;
     (void)hipGetLastError();

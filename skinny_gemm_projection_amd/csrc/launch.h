@@ -133,6 +133,23 @@ bool mxfp4_split(int M, int K, int* nb, int* splits);
 hipError_t launch_mxfp4(int M, int N, int K, const void* x, const void* Wq, const uint8_t* Ws,
                         const Epilogue& ep, hipStream_t stream);
 
+// Projection with low-precision weights for 17 <= M <= 64 (both formats):
+// workgroups of 128 * NT weight rows x one K chunk, x staged in LDS, fp32
+// partials [S, N, 16*MT] through the workspace and the tiled reduction when
+// S > 1.  FP8: Wq [N, K] e4m3 codes, Ws fp32 [ceil(N/128), ceil(K/128)];
+// MXFP4: Wq [N, K/2], Ws [N, K/32] e8m0.
+constexpr int kLowpFp8 = 0;
+constexpr int kLowpMxfp4 = 1;
+constexpr int kLowpChunkFromM = 17;
+constexpr int kLowpMaxM = 64;
+struct LowpChunkPlan {
+    int MT, NT, S, chunk, pitch;
+    size_t lds, workspace;
+};
+bool lowp_chunk_plan(int M, int N, int K, LowpChunkPlan* p);
+hipError_t launch_lowp_chunk(int fmt, int M, int N, int K, const void* x, const void* Wq,
+                             const void* Ws, const Epilogue& fin, void* ws, hipStream_t stream);
+
 // Router top-k: ids [T,k] (and their scores) from fp32 scores, row t at
 // scores + t*ld (ld >= E); E <= 4096, k <= 32 (checked by the caller).
 hipError_t launch_router_topk(const float* scores, int64_t ld, int T, int E, int k,

@@ -1,0 +1,329 @@
+// lowp_chunk.hip -- projection with block-scaled 8-bit (FP8 e4m3) or 4-bit
+// (MXFP4) weights for batches of 17 to 64 rows, on gfx950 matrix cores.
+//
+// The decode path the pages describe covers batch 1 to 64 ("Hyper Optimizing
+// Kimi K3 in vLLM" deepnotes page, Method details: batch 1-64 decode; §1:
+// split-K at larger batch) and their later model ships low-precision weights
+// (Experimental setup and Supplementary details).  Up to 16 rows the FP8 and
+// MXFP4 kernels give each workgroup one or two 16-row weight tiles and read
+// all of x from L2 per workgroup; from 17 rows that x traffic would be one to
+// eight times the code bytes, so this kernel uses the bf16 chunk kernel's
+// shape instead:
+//
+//  * a workgroup of 8 waves owns 128 (NT = 1) or 256 (NT = 2) weight rows --
+//    16 * NT per wave -- and one K chunk (a whole number of 128-element
+//    windows); the x rows of the chunk (M padded to 16 * MT rows) are staged
+//    once in LDS, so x is read once per 128 or 256 weight rows;
+//  * each lane decodes its codes straight into B operand layout: FP8 lane
+//    (col, grp) holds 32 codes of row col per window (k 32*grp .. +32), four
+//    steps of v_mfma_f32_16x16x32_bf16 take 8 each, and the window's sum is
+//    scaled once by its 128 x 128 block scale; MXFP4 lane (col, grp) loads
+//    block grp of the window, permlane swaps transpose the four lane groups of
+//    a column so that step t is exactly block t, and each step's result is
+//    scaled by its block scale (codes converted at unit scale: exact for
+//    every scale code);
+//  * with S > 1 chunks the fp32 partials go to the workspace as
+//    [S, N, 16 * MT] and the tiled reduction kernel adds them in ascending
+//    chunk order (deterministic), as for the bf16 chunk kernel.
+#include "launch.h"
+
+namespace sg {
+
+namespace {
+
+constexpr int kLpWaves = 8;
+constexpr int kLpThreads = kWave * kLpWaves;
+constexpr int kLpWindow = 128;              // elements per window (one FP8 scale block)
+constexpr int kLpXLoads = 16;               // x staging loads per thread (at most)
+constexpr uint32_t kLpOut = 0xFFFFFFF0u;    // past any descriptor range: reads zero
+
+// e8m0 scale code -> 2^(s-127): the exponent field for 1..254, the fp32
+// subnormal 2^-127 for 0, NaN for 255.
+__device__ __forceinline__ float lp_e8m0(uint32_t s) {
+    return as_f(s == 0u ? 0x00400000u : s == 255u ? 0x7FC00000u : s << 23);
+}
+
+template <int FMT, int MT, int NT, int D>
+__global__ __launch_bounds__(kLpThreads) void lowp_chunk_kernel(
+    const uint4* __restrict__ x, const uint8_t* __restrict__ Wq, const void* __restrict__ Ws,
+    int M, int N, int K, int chunk, int pitch, Epilogue ep) {
+    constexpr bool kFp8 = FMT == kLowpFp8;
+    constexpr int XR = 16 * MT;
+    extern __shared__ uint4 xs[];  // [XR][pitch] pieces of the chunk's x rows
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wv = wave_id_in_block();
+    const int col = lane & 15, grp = lane >> 4;
+    const int K8 = K / kPiece;
+    const int k0 = blockIdx.y * chunk;
+    const int len = max(0, min(K - k0, chunk));      // elements of this chunk
+    const int windows = (len + kLpWindow - 1) / kLpWindow;
+    const int w00 = k0 / kLpWindow;                   // first window of the chunk
+    if (blockIdx.x * 128 * NT >= N) return;           // padding column of the grid
+    const int row0 = blockIdx.x * 128 * NT + wv * 16 * NT;
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16 * NT, N - row0)));
+
+    // ---- x of the chunk into LDS: row r, piece p at xs[r * pitch + p]
+    {
+        const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K8 * 16u);
+        const int P8 = chunk / kPiece;
+        const int total = XR * P8;
+        uint4 v[kLpXLoads];
+#pragma unroll
+        for (int j = 0; j < kLpXLoads; ++j) {
+            const int idx = tid + j * kLpThreads;
+            const int r = idx / P8, p = idx - r * P8;
+            const bool ok = idx < total && r < M && p * kPiece < len;
+            v[j] = load16<kCached>(rx, ok ? ((uint32_t)r * K8 + k0 / kPiece + p) * 16u : kLpOut);
+        }
+#pragma unroll
+        for (int j = 0; j < kLpXLoads; ++j) {
+            const int idx = tid + j * kLpThreads;
+            const int r = idx / P8, p = idx - r * P8;
+            if (idx < total) xs[r * pitch + p] = v[j];
+        }
+    }
+    __syncthreads();
+
+    // ---- weight codes of the wave's 16 * NT rows
+    // FP8: rows of K/16 units of 16 codes; scales [ceil(N/128)][ceil(K/128)].
+    // MXFP4: rows of K/32 blocks of 32 codes (16 bytes); scales [N][K/32].
+    const int KU = kFp8 ? K / 16 : K / 32;  // 16-byte units per row
+    const rsrc_t rw = make_rsrc(Wq + (int64_t)row0 * KU * 16, (uint32_t)rows * KU * 16u);
+    const int KB = (K + kLpWindow - 1) / kLpWindow;
+    const float* __restrict__ fsc = static_cast<const float*>(Ws) + (int64_t)(row0 / 128) * KB;
+    const uint8_t* __restrict__ bsc = static_cast<const uint8_t*>(Ws);
+    const rsrc_t rsc = make_rsrc(bsc + (int64_t)row0 * KU, (uint32_t)rows * KU);
+
+    f32x4_t acc[NT][MT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    constexpr int UPW = kFp8 ? 2 : 1;  // 16-byte code loads per lane, window and tile
+    for (int wb = 0; wb < windows; wb += D) {
+        uint4 wq[D][NT][UPW];
+        uint32_t sb[D][NT];
+        float sf[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int w = wb + d;
+            const bool live = w < windows;
+            const int gw = w00 + w;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int r = 16 * nt + col;
+#pragma unroll
+                for (int j = 0; j < UPW; ++j) {
+                    // FP8: units 8*gw + 2*grp + j; MXFP4: block 4*gw + grp
+                    const int u = kFp8 ? 8 * gw + 2 * grp + j : 4 * gw + grp;
+                    const bool ok = live && u < KU;
+                    wq[d][nt][j] =
+                        load16<kStream>(rw, ok ? ((uint32_t)r * KU + u) * 16u : kLpOut);
+                }
+                if (!kFp8) {
+                    const int b = 4 * gw + grp;
+                    sb[d][nt] = __builtin_amdgcn_raw_buffer_load_b8(
+                        rsc, live && b < KU ? (uint32_t)(r * KU + b) : kLpOut, 0, kStream);
+                }
+            }
+            if (kFp8) sf[d] = live && rows > 0 ? fsc[gw] : 0.0f;  // no scale row past N
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int w = wb + d;
+            if (w >= windows) break;  // wave-uniform
+            const uint4* xw = xs + w * (kLpWindow / kPiece);  // window's first piece
+            if constexpr (kFp8) {
+                f32x4_t part[NT][MT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) part[nt][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    uint4 a[MT];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) a[mt] = xw[(16 * mt + col) * pitch + 4 * grp + t];
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        // codes 8t .. 8t+7 of the lane's 32, low byte first
+                        const uint4 q = wq[d][nt][t / 2];
+                        const uint32_t lo = (t & 1) ? q.z : q.x;
+                        const uint32_t hi = (t & 1) ? q.w : q.y;
+                        const uint4 b = {
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+                            part[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, a[mt]), __builtin_bit_cast(bf16x8_t, b),
+                                part[nt][mt], 0, 0, 0);
+                    }
+                }
+                // a window lies in one 128 x 128 scale block of the wave's rows
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            acc[nt][mt][v] = __builtin_fmaf(part[nt][mt][v], sf[d], acc[nt][mt][v]);
+            } else {
+                uint32_t wd[NT][4];
+                float scale[NT][4];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    // lane (col, grp) holds dword t of block grp; after the
+                    // swaps wd[t] is dword grp of block t
+                    const uint4 q = wq[d][nt][0];
+                    const auto p02 = __builtin_amdgcn_permlane32_swap(q.x, q.z, false, false);
+                    const auto p13 = __builtin_amdgcn_permlane32_swap(q.y, q.w, false, false);
+                    const auto q01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
+                    const auto q23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
+                    wd[nt][0] = q01[0];
+                    wd[nt][1] = q01[1];
+                    wd[nt][2] = q23[0];
+                    wd[nt][3] = q23[1];
+                    // byte t of `all`: the scale code of block t of row col
+                    const uint32_t mine = sb[d][nt] << (8 * grp);
+                    const auto g16 = __builtin_amdgcn_permlane16_swap(mine, mine, false, false);
+                    const uint32_t pair = g16[0] | g16[1];
+                    const auto g32 = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);
+                    const uint32_t all = g32[0] | g32[1];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) scale[nt][t] = lp_e8m0((all >> (8 * t)) & 0xFFu);
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    uint4 a[MT];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) a[mt] = xw[(16 * mt + col) * pitch + 4 * t + grp];
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        constexpr float kUnit = 1.0f;
+                        const uint4 b = {
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], kUnit, 0)),
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], kUnit, 1)),
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], kUnit, 2)),
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], kUnit, 3))};
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) {
+                            const f32x4_t blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, a[mt]), __builtin_bit_cast(bf16x8_t, b),
+                                f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+                            for (int v = 0; v < 4; ++v)
+                                acc[nt][mt][v] = __builtin_fmaf(blk[v], scale[nt][t], acc[nt][mt][v]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    if (ep.partial) {
+        // partials [S, N, XR]: the 4 consecutive m a lane holds as one 16-byte store
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int r = 16 * nt + col;
+            if (r >= rows) continue;
+            f32x4_t* dst = reinterpret_cast<f32x4_t*>(
+                ep.partial + ((int64_t)blockIdx.y * N + row0 + r) * XR + grp * 4);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) dst[mt * 4] = acc[nt][mt];
+        }
+        return;
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int r = 16 * nt + col;
+        if (r >= rows) continue;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = 16 * mt + 4 * grp + v;
+                if (m < M) store_final(ep, (int64_t)m * N + row0 + r, acc[nt][mt][v]);
+            }
+    }
+}
+
+constexpr int kLpCus = 256;
+constexpr size_t kLpLdsMax = 144 * 1024;  // x staging (the kernel uses no other LDS)
+
+}  // namespace
+
+bool lowp_chunk_plan(int M, int N, int K, LowpChunkPlan* p) {
+    if (M < kLowpChunkFromM || M > kLowpMaxM || N < 1 || K < 0) return false;
+    const int MT = (M + 15) / 16;
+    const int XR = 16 * MT;
+    if (K == 0) {  // outputs are r (or zero): one launch, nothing to stage
+        *p = LowpChunkPlan{MT, 1, 1, kLpWindow, kLpWindow / kPiece + 1,
+                           (size_t)XR * (kLpWindow / kPiece + 1) * 16, 0};
+        return true;
+    }
+    // two 16-row tiles a wave while their 256-row workgroups, 8 splits each,
+    // still give three quarters of the compute units one
+    const int NT = ((N + 255) / 256) * 8 >= 3 * kLpCus / 4 ? 2 : 1;
+    const int tiles = mfma_grid_tiles(N, 128 * NT);
+    const int windows = (K + kLpWindow - 1) / kLpWindow;
+    // the smallest split whose grid fills the compute units and whose x chunk
+    // fits in LDS (and the staging registers); else the largest that fits
+    int best = 0;
+    for (int S = 1; S <= 64 && S <= windows; ++S) {
+        const int chunk = kLpWindow * ((windows + S - 1) / S);
+        if ((int64_t)(S - 1) * chunk >= K) continue;  // an empty chunk
+        const size_t lds = (size_t)XR * (chunk / kPiece + 1) * 16;
+        if (lds > kLpLdsMax || XR * (chunk / kPiece) > kLpXLoads * kLpThreads) continue;
+        best = S;
+        if (tiles * S >= kLpCus) break;
+    }
+    if (best == 0) return false;
+    const int chunk = kLpWindow * ((windows + best - 1) / best);
+    p->MT = MT;
+    p->NT = NT;
+    p->S = best;
+    p->chunk = chunk;
+    p->pitch = chunk / kPiece + 1;  // odd row pitch: the 16 rows of an operand read spread banks
+    p->lds = (size_t)XR * p->pitch * 16;
+    p->workspace = best > 1 ? ((size_t)best * N * XR * sizeof(float) + 255) / 256 * 256 : 0;
+    return true;
+}
+
+hipError_t launch_lowp_chunk(int fmt, int M, int N, int K, const void* x, const void* Wq,
+                             const void* Ws, const Epilogue& fin, void* ws, hipStream_t stream) {
+    LowpChunkPlan p;
+    if (!lowp_chunk_plan(M, N, K, &p)) return hipErrorInvalidValue;
+    const dim3 grid(mfma_grid_tiles(N, 128 * p.NT), p.S);
+    const Epilogue ep = p.S > 1 ? Epilogue{static_cast<float*>(ws), nullptr, nullptr, nullptr} : fin;
+    const uint4* xp = static_cast<const uint4*>(x);
+    const uint8_t* wp = static_cast<const uint8_t*>(Wq);
+    constexpr int kD8 = 4, kD4 = 8;  // windows in flight per wave
+#define SG_LP(f, mt, nt, d)                                                                       \
+    if (fmt == f && p.MT == mt && p.NT == nt) {                                                   \
+        auto* kern = &lowp_chunk_kernel<f, mt, nt, d>;                                            \
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),                   \
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,            \
+                                           (int)p.lds);                                           \
+        if (e != hipSuccess) return e;                                                            \
+        kern<<<grid, kLpThreads, p.lds, stream>>>(xp, wp, Ws, M, N, K, p.chunk, p.pitch, ep);    \
+        e = hipGetLastError();                                                                    \
+        if (e != hipSuccess) return e;                                                            \
+        return p.S > 1 ? launch_reduce_tiles(static_cast<const float*>(ws), p.S, M, N, 128 * nt, \
+                                             fin, stream)                                         \
+                       : hipSuccess;                                                              \
+    }
+    SG_LP(kLowpFp8, 2, 1, kD8) SG_LP(kLowpFp8, 3, 1, kD8) SG_LP(kLowpFp8, 4, 1, kD8)
+    SG_LP(kLowpFp8, 2, 2, kD8) SG_LP(kLowpFp8, 3, 2, kD8) SG_LP(kLowpFp8, 4, 2, kD8)
+    SG_LP(kLowpMxfp4, 2, 1, kD4) SG_LP(kLowpMxfp4, 3, 1, kD4) SG_LP(kLowpMxfp4, 4, 1, kD4)
+    SG_LP(kLowpMxfp4, 2, 2, kD4) SG_LP(kLowpMxfp4, 3, 2, kD4) SG_LP(kLowpMxfp4, 4, 2, kD4)
+#undef SG_LP
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sg

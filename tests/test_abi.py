@@ -280,10 +280,16 @@ def test_fp8_size_limits_return_before_launch():
     sg.skinny_gemm_reset_counters()
     A = 0x10000
 
-    def call(M, K, y=None):
-        return c.skinny_gemm_fp8(M, 8, K, A, A, A, None, y, None, None)
+    def call(M, K, y=None, N=8, ws=None, ws_bytes=0):
+        return c.skinny_gemm_fp8(M, N, K, A, A, A, None, y, None, ws, ws_bytes, None)
 
-    assert call(17, 64) == 3
+    assert call(65, 64) == 3                              # above the decode path
+    assert call(17, 64) == 1 and call(64, 65536) == 1     # chunk kernel from 17 rows
+    assert call(64, 1 << 20) == 3                         # x chunk would not fit in LDS
+    assert call(17, 7168, y=A, N=4096) == 5               # its split-K workspace is missing
+    need = sg.skinny_gemm_lowp_workspace(17, 4096, 7168)
+    assert call(17, 7168, y=A, N=4096, ws=A, ws_bytes=need - 256) == 5
+    assert call(17, 7168, y=A, N=4096, ws=A + 8, ws_bytes=need) == 4  # misaligned workspace
     assert call(1, 32768) == 1 and call(1, 32784) == 3   # M * K <= 32768 (LDS) at M <= 2
     assert call(2, 16384) == 1 and call(2, 16400) == 3
     assert call(3, 16384) == 1 and call(3, 16400) == 3   # K <= 16384 (registers) at M = 3, 4
@@ -295,6 +301,19 @@ def test_fp8_size_limits_return_before_launch():
     assert sum(sg.skinny_gemm_get_counters()) == 0
 
 
+def test_lowp_workspace_sizes():
+    # fp32 partials [S, N, 16 * ceil(M / 16)] of the low-precision chunk kernel, from 17 rows
+    assert sg.skinny_gemm_lowp_workspace(16, 4096, 7168) == 0
+    assert sg.skinny_gemm_lowp_workspace(65, 4096, 7168) == 0
+    assert sg.skinny_gemm_lowp_workspace(17, 0, 7168) == 0
+    assert sg.skinny_gemm_lowp_workspace(17, 4096, 0) == 0      # K = 0: one launch, no split
+    for M, N, K in ((17, 4096, 7168), (32, 8192, 7168), (64, 7168, 8192), (48, 200, 1024)):
+        b = sg.skinny_gemm_lowp_workspace(M, N, K)
+        mp = 16 * -(-M // 16)
+        assert b % 256 == 0 and b >= 2 * N * mp * 4, (M, N, K, b)  # at least two splits
+        assert (b // (N * mp * 4)) * N * mp * 4 <= b < (b // (N * mp * 4) + 1) * N * mp * 4
+
+
 @no_gpu_only
 def test_mxfp4_size_limits_return_before_launch():
     # the vector kernel's team split bounds K (2 blocks of 32 a lane at M <= 2, one
@@ -304,9 +323,10 @@ def test_mxfp4_size_limits_return_before_launch():
     A = 0x10000
 
     def call(M, K):
-        return c.skinny_gemm_mxfp4(M, 8, K, A, A, A, None, None, None, None)
+        return c.skinny_gemm_mxfp4(M, 8, K, A, A, A, None, None, None, None, 0, None)
 
-    assert call(17, 64) == 3
+    assert call(65, 64) == 3
+    assert call(17, 64) == 1 and call(64, 65536) == 1 and call(64, 1 << 20) == 3
     assert call(1, 32768) == 1 and call(1, 32800) == 3
     assert call(2, 32768) == 1 and call(2, 32800) == 3
     assert call(3, 16384) == 1 and call(8, 16416) == 3

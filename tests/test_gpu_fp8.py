@@ -1,6 +1,7 @@
 """GPU parity of the projection with FP8 weights (skinny_gemm_fp8: e4m3 codes, one fp32
-scale per 128 x 128 block) through the C ABI, against oracle_projection_fp8 on the same
-seeded codes and scales: fp32 |got - ref| <= 1e-3 * A, bf16 adds 2^-8 |ref|, the
+scale per 128 x 128 block) through the C ABI, M = 1..64 (vector ALU, matrix cores, and
+from 17 rows the chunk kernel with its split-K reduction), against oracle_projection_fp8
+on the same seeded codes and scales: fp32 |got - ref| <= 1e-3 * A, bf16 adds 2^-8 |ref|, the
 residual adds 2^-23 |r + y|.  Integer-valued activations and weights with power-of-two
 scales are bit-exact (every product and partial sum is exact in fp32)."""
 import numpy as np
@@ -29,6 +30,9 @@ def run(x, codes, scales, r=None, f32=True, bf16=True):
     torch.cuda.synchronize()
     d = counters_delta(before, sg.skinny_gemm_get_counters())
     assert d[sg.SG_KERNEL_FP8] == (1 if M > 0 and N > 0 else 0)
+    # from 17 rows the chunk kernel, with the reduction when it splits K
+    splits = M >= 17 and sg.skinny_gemm_lowp_workspace(M, N, x.shape[1]) > 0
+    assert d[sg.SG_KERNEL_REDUCE] == (1 if splits and N > 0 else 0)
     return y32, y16
 
 
@@ -42,7 +46,12 @@ SHAPES = [(1, 40, 16), (1, 129, 112), (1, 200, 1040), (1, 77, 8192), (1, 33, 820
           (5, 100, 1040), (6, 131, 4112), (7, 64, 7168), (8, 257, 8192), (8, 33, 16),
           (9, 129, 2064), (12, 300, 7168), (16, 40, 20000), (16, 1, 144), (13, 200, 30000),
           # from 8161 rows two 16-row tiles per wave (ragged last 32-row tile)
-          (9, 8200, 144), (16, 8192, 1040), (5, 8177, 2064)]
+          (9, 8200, 144), (16, 8192, 1040), (5, 8177, 2064),
+          # from 17 rows the chunk kernel: x rows padded to 32, 48, 64; ragged
+          # 128-row tiles and windows; one split (K = 16), several, 256-row tiles
+          (17, 200, 1040), (20, 129, 7168), (32, 300, 4112), (33, 64, 16), (47, 257, 2064),
+          (48, 1000, 8192), (64, 33, 30000), (64, 8200, 1040), (17, 6300, 4096),
+          (40, 128, 128), (64, 1, 144)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -71,7 +80,8 @@ INT_CODES = [0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50]
 
 @pytest.mark.parametrize("M,N,K", [(1, 300, 4096), (2, 129, 8192), (4, 140, 2064),
                                    (8, 200, 8192), (6, 77, 3088), (16, 150, 8192),
-                                   (11, 64, 2064)])
+                                   (11, 64, 2064), (17, 300, 8192), (32, 129, 4112),
+                                   (64, 260, 8192), (50, 8200, 2064)])
 def test_fp8_integer_bit_exact(M, N, K):
     # integer activations and weights, power-of-two block scales: exact sums
     announce(f"fp8 integer M={M} N={N} K={K}")
@@ -88,7 +98,7 @@ def test_fp8_integer_bit_exact(M, N, K):
     assert np.array_equal(bits(y16), orc().encode_bf16(ref)), "bf16 output bit-exact"
 
 
-@pytest.mark.parametrize("M,N", [(2, 300), (12, 300), (12, 8200)])
+@pytest.mark.parametrize("M,N", [(2, 300), (12, 300), (12, 8200), (20, 300), (64, 8200)])
 def test_fp8_nan_code_and_scale(M, N):
     K = 512
     x = si.normal_bf16((M, K), 1.0, 8900 + M, DEV)
@@ -109,12 +119,24 @@ def test_fp8_nan_code_and_scale(M, N):
 
 
 def test_fp8_rejections_touch_nothing():
-    x17 = si.normal_bf16((17, 64), 1.0, 1, DEV)
+    x65 = si.normal_bf16((65, 64), 1.0, 1, DEV)
     codes, scales = si.fp8_weights(8, 64, 2, DEV)
-    y = torch.full((17, 8), -7.0, device=DEV)
+    y = torch.full((65, 8), -7.0, device=DEV)
     with pytest.raises(sg.SkinnyGemmError) as e:
-        sg.skinny_gemm_fp8(x17, codes, scales, y_f32=y)  # M > 16
+        sg.skinny_gemm_fp8(x65, codes, scales, y_f32=y)  # M > 64
     assert e.value.status == 3
+    # from 17 rows: a workspace shorter than the split-K partials need
+    x20 = si.normal_bf16((20, 4096), 1.0, 6, DEV)
+    c20, s20 = si.fp8_weights(4096, 4096, 7, DEV)
+    y20 = torch.full((20, 4096), -7.0, device=DEV)
+    need = sg.skinny_gemm_lowp_workspace(20, 4096, 4096)
+    assert need > 0
+    before = sg.skinny_gemm_get_counters()
+    with pytest.raises(sg.SkinnyGemmError) as e:
+        sg.skinny_gemm_fp8(x20, c20, s20, y_f32=y20,
+                           workspace=torch.empty(need - 256, dtype=torch.uint8, device=DEV))
+    assert e.value.status == 5
+    assert counters_delta(before, sg.skinny_gemm_get_counters()) == [0] * sg.SG_NUM_COUNTERS
     x = si.normal_bf16((4, 16400), 1.0, 3, DEV)
     c2, s2 = si.fp8_weights(8, 16400, 4, DEV)
     y4 = torch.full((4, 8), -7.0, device=DEV)
@@ -127,26 +149,36 @@ def test_fp8_rejections_touch_nothing():
         sg.skinny_gemm_fp8(x2, c2, s2, y_f32=y2)  # M * K > 32768 at M = 2
     assert e.value.status == 3
     st = sg._c().skinny_gemm_fp8(1, 8, 24, x.data_ptr(), c2.data_ptr(), s2.data_ptr(), None,
-                                 y4.data_ptr(), None, None)  # K % 16
+                                 y4.data_ptr(), None, None, 0, None)  # K % 16
     assert st == 4
     torch.cuda.synchronize()
     assert (y == -7.0).all() and (y4 == -7.0).all() and (y2 == -7.0).all(), \
         "rejected calls write nothing"
+    assert (y20 == -7.0).all(), "rejected calls write nothing"
 
 
-def test_fp8_empty():
-    x = si.normal_bf16((1, 0), 1.0, 5, DEV)
+@pytest.mark.parametrize("M", [1, 20])
+def test_fp8_empty(M):
+    x = si.normal_bf16((M, 0), 1.0, 5, DEV)
     codes = torch.empty((10, 0), dtype=torch.uint8, device=DEV)
     scales = torch.empty((1, 0), dtype=torch.float32, device=DEV)
     y32, _ = run(x, codes, scales, bf16=False)
     assert (y32 == 0).all(), "K = 0: zero sums"
+    r = si.normal_bf16((M, 10), 1.0, 6, DEV)
+    out = torch.full((M, 10), -7.0, device=DEV)
+    sg.skinny_gemm_fp8(x, codes, scales, y_f32=out, r=r)
+    torch.cuda.synchronize()
+    assert torch.equal(out, r.float()), "K = 0 with a residual: out = r"
 
 
 @pytest.mark.parametrize("M,N,K,residual", [(1, 8192, 7168, False), (2, 8192, 7168, False),
                                             (4, 4096, 7168, False), (8, 4096, 7168, False),
                                             (16, 4096, 7168, False), (12, 8192, 7168, False),
+                                            (32, 4096, 7168, False), (64, 4096, 7168, False),
+                                            (64, 8192, 7168, False),
                                             (1, 7168, 8192, True),
-                                            (8, 7168, 8192, True), (16, 7168, 8192, True)])
+                                            (8, 7168, 8192, True), (16, 7168, 8192, True),
+                                            (64, 7168, 8192, True)])
 def test_fp8_full_size_sampled(M, N, K, residual):
     announce(f"fp8 full M={M} N={N} K={K} residual={residual}")
     x = si.normal_bf16((M, K), 1.0, 9000 + M, DEV)

@@ -1,5 +1,6 @@
 """GPU parity of the projection with MXFP4 weights (skinny_gemm_mxfp4) through the
-C ABI, against oracle_projection_mxfp4 on the same seeded codes and scales:
+C ABI, M = 1..64 (vector ALU, matrix cores, and from 17 rows the chunk kernel with its
+split-K reduction), against oracle_projection_mxfp4 on the same seeded codes and scales:
 fp32 |got - ref| <= 1e-3 * A, bf16 adds 2^-8 |ref|, the residual adds 2^-23 |r + y|;
 integer-valued activations with unit scales are bit-exact (every product is a
 multiple of 1/2 and every partial sum exact in fp32)."""
@@ -29,6 +30,9 @@ def run(x, codes, scales, r=None, f32=True, bf16=True):
     torch.cuda.synchronize()
     d = counters_delta(before, sg.skinny_gemm_get_counters())
     assert d[sg.SG_KERNEL_MXFP4] == (1 if M > 0 and N > 0 else 0)
+    # from 17 rows the chunk kernel, with the reduction when it splits K
+    splits = M >= 17 and sg.skinny_gemm_lowp_workspace(M, N, x.shape[1]) > 0
+    assert d[sg.SG_KERNEL_REDUCE] == (1 if splits and N > 0 else 0)
     return y32, y16
 
 
@@ -38,7 +42,11 @@ SHAPES = [(1, 40, 32), (1, 129, 96), (1, 77, 608), (1, 65, 2080), (1, 33, 8224),
           (12, 33, 608), (13, 70, 8224), (16, 100, 7168), (16, 17, 96), (16, 16, 32),
           # from 8161 rows the matrix-core kernel takes two 16-row tiles a wave
           # (ragged last 32-row tile)
-          (9, 8200, 2080), (16, 8192, 608), (12, 8177, 96)]
+          (9, 8200, 2080), (16, 8192, 608), (12, 8177, 96),
+          # from 17 rows the chunk kernel: x rows padded to 32, 48, 64, ragged
+          # 128-row tiles and windows, one split and several, 256-row tiles
+          (17, 200, 1056), (20, 129, 7168), (32, 300, 4128), (33, 64, 32), (47, 257, 2080),
+          (48, 1000, 8192), (64, 33, 30016), (64, 8200, 1056), (17, 6300, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -62,7 +70,8 @@ def test_mxfp4_small(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 37, 4096), (2, 64, 7168), (8, 40, 8192), (5, 19, 96),
-                                   (16, 48, 4096), (11, 21, 8192), (16, 8200, 1024)])
+                                   (16, 48, 4096), (11, 21, 8192), (16, 8200, 1024),
+                                   (17, 300, 8192), (40, 129, 4128), (64, 8200, 2080)])
 def test_mxfp4_integer_bit_exact(M, N, K):
     announce(f"mxfp4 integer M={M} N={N} K={K}")
     x = si.integer_bf16((M, K), -4, 4, 8300 + K, DEV)
@@ -75,7 +84,7 @@ def test_mxfp4_integer_bit_exact(M, N, K):
                 f"mxfp4 integer bf16 M={M}")
 
 
-@pytest.mark.parametrize("M,N", [(3, 24), (12, 24), (12, 8200)])
+@pytest.mark.parametrize("M,N", [(3, 24), (12, 24), (12, 8200), (20, 300), (64, 8200)])
 def test_mxfp4_nan_scale_and_zero_codes(M, N):
     # vector kernel (M = 3), matrix-core kernel with one and with two row tiles a wave
     announce(f"mxfp4 NaN scale, zero codes M={M} N={N}")
@@ -101,10 +110,11 @@ def test_mxfp4_nan_scale_and_zero_codes(M, N):
 # kernels scale each block's fp32 sum, so the products stay exact down to
 # code 0 (whose weights are below bf16's and fp32's normal range) and up to
 # code 254 (whose weights can exceed the largest bf16).
-@pytest.mark.parametrize("M,N", [(3, 40), (8, 40), (12, 40), (16, 40), (12, 8200), (16, 8192)])
+@pytest.mark.parametrize("M,N", [(3, 40), (8, 40), (12, 40), (16, 40), (12, 8200), (16, 8192),
+                                 (24, 40), (64, 8192)])
 def test_mxfp4_scale_code_range(M, N):
     # vector kernel (M = 3, 8), matrix-core kernel with one (N = 40) and two
-    # (N >= 8161) row tiles a wave
+    # (N >= 8161) row tiles a wave, chunk kernel (M = 24, 64)
     announce(f"mxfp4 scale codes 0..12, 120, 253, 254, mixed M={M} N={N}")
     K = 640  # 20 blocks: 5 windows of the matrix-core kernel
     KB = K // 32
@@ -152,7 +162,7 @@ def test_mxfp4_empty_and_rejected():
     lib = sg._c()
     y.fill_(-7.0)
     s = torch.cuda.current_stream().cuda_stream
-    cases = [((17, 8, 64), 3),         # batch above the 4-bit path
+    cases = [((65, 8, 64), 3),         # batch above the decode path
              ((2, 8, 48), 4),          # K not a multiple of 32
              ((1, 8, 32800), 3),       # K over the vector-ALU split limit at M = 1
              ((2, 8, 32800), 3),       # and at M = 2
@@ -161,7 +171,7 @@ def test_mxfp4_empty_and_rejected():
     for (M, N, K), status in cases:
         before = sg.skinny_gemm_get_counters()
         st = lib.skinny_gemm_mxfp4(M, N, K, x.data_ptr(), codes.data_ptr(), scales.data_ptr(),
-                                   None, y.data_ptr(), None, s)
+                                   None, y.data_ptr(), None, None, 0, s)
         assert st == status, ((M, N, K), st)
         assert counters_delta(before, sg.skinny_gemm_get_counters()) == [0] * sg.SG_NUM_COUNTERS
     torch.cuda.synchronize()
@@ -170,8 +180,9 @@ def test_mxfp4_empty_and_rejected():
 
 @pytest.mark.parametrize("M,N,K", [(1, 8192, 7168), (2, 8192, 7168), (4, 4096, 7168),
                                    (8, 4096, 7168), (16, 4096, 7168), (16, 8192, 7168),
+                                   (32, 4096, 7168), (64, 4096, 7168), (64, 8192, 7168),
                                    (1, 7168, 8192),
-                                   (8, 7168, 8192), (16, 7168, 8192)])
+                                   (8, 7168, 8192), (16, 7168, 8192), (64, 7168, 8192)])
 def test_mxfp4_full_size(M, N, K):
     # the benchmark's shapes: sampled output rows against the oracle
     announce(f"mxfp4 full M={M} N={N} K={K}")

@@ -76,7 +76,17 @@ def _lp_shapes(count, seed, unit):
     return out
 
 
-@pytest.mark.parametrize("i,M,N,K,residual", _lp_shapes(24, 20261203, 16))
+def _lp_shapes_wide(count, seed, unit, first):
+    """Seeded (M, N, K) with 17 <= M <= 64 (the chunk kernel), K a multiple of `unit`
+    up to 20000; numbered from `first`."""
+    rng = np.random.default_rng(seed)
+    return [(first + i, int(rng.integers(17, 65)), int(rng.integers(1, 9000)),
+             unit * int(rng.integers(1, 20000 // unit + 1)), bool(rng.integers(0, 2)))
+            for i in range(count)]
+
+
+@pytest.mark.parametrize("i,M,N,K,residual",
+                         _lp_shapes(24, 20261203, 16) + _lp_shapes_wide(16, 20261213, 16, 24))
 def test_random_shape_fp8(i, M, N, K, residual):
     announce(f"random fp8 shape {i}: M={M} N={N} K={K} residual={residual}")
     seed = 31000 + 10 * i
@@ -99,7 +109,8 @@ def test_random_shape_fp8(i, M, N, K, residual):
     assert not torch.isnan(y32).any(), "every fp32 output written"
 
 
-@pytest.mark.parametrize("i,M,N,K,residual", _lp_shapes(24, 20261204, 32))
+@pytest.mark.parametrize("i,M,N,K,residual",
+                         _lp_shapes(24, 20261204, 32) + _lp_shapes_wide(16, 20261214, 32, 24))
 def test_random_shape_mxfp4(i, M, N, K, residual):
     announce(f"random mxfp4 shape {i}: M={M} N={N} K={K} residual={residual}")
     seed = 32000 + 10 * i
