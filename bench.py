@@ -156,6 +156,17 @@ class Launcher:
         return go
 
 
+def lowp_plan_label(fmt: str, M: int, N: int, wsb: int) -> str:
+    """Kernel an FP8 / MXFP4 call runs, as the library routes it (the chunk kernel
+    from 12 rows for FP8; for MXFP4 from 17 rows, or 12 when N > 5888)."""
+    chunk = M >= 17 or (M >= 12 and (fmt == "fp8" or N > 5888))
+    if chunk:
+        return "lowp_chunk + reduce" if wsb else "lowp_chunk"
+    if fmt == "fp8":
+        return "fp8_mfma" if M >= 5 else "fp8_rowdot"
+    return "mxfp4_mfma" if M >= 9 else "mxfp4_rowdot"
+
+
 def sleep_cycles_per_ms(torch) -> float:
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -509,7 +520,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
             y32 = None if residual else torch.empty((M, N), device=dev)
             y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
-            wsb = sg.skinny_gemm_lowp_workspace(M, N, K)
+            wsb = sg.skinny_gemm_mxfp4_workspace(M, N, K)
             ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
 
             def mx(cw, sw, x=x, r=r, y32=y32, y16=y16, M=M, N=N, K=K, ws=ws, wsb=wsb):
@@ -529,8 +540,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
             us = 1e3 * per
             gbs = nbytes / (per * 1e-3) / 1e9
             rows.append({"workload": label, "M": M, "N": N, "K": K,
-                         "plan": ("lowp_chunk + reduce" if wsb else "lowp_chunk") if M >= 17
-                         else "mxfp4_mfma" if M >= 9 else "mxfp4_rowdot",
+                         "plan": lowp_plan_label("mxfp4", M, N, wsb),
                          "us": round(us, 3), "GBps": round(gbs, 1),
                          "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
         del ring
@@ -551,7 +561,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
             y32 = None if residual else torch.empty((M, N), device=dev)
             y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
-            wsb = sg.skinny_gemm_lowp_workspace(M, N, K)
+            wsb = sg.skinny_gemm_fp8_workspace(M, N, K)
             ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
 
             def f8(cw, sw, x=x, r=r, y32=y32, y16=y16, M=M, N=N, K=K, ws=ws, wsb=wsb):
@@ -571,8 +581,7 @@ def sweep(torch, sg, si, L, cyc, reps=40):
             us = 1e3 * per
             gbs = nbytes / (per * 1e-3) / 1e9
             rows.append({"workload": label, "M": M, "N": N, "K": K,
-                         "plan": ("lowp_chunk + reduce" if wsb else "lowp_chunk") if M >= 17
-                         else "fp8_mfma" if M >= 5 else "fp8_rowdot",
+                         "plan": lowp_plan_label("fp8", M, N, wsb),
                          "us": round(us, 3), "GBps": round(gbs, 1),
                          "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
         del ring
@@ -1009,14 +1018,14 @@ def profile_workloads(torch, sg, si, L, manifest_path, reps=3):
             x = si.normal_bf16((M, K), 1.0, 18, dev)
             y32 = torch.empty((M, N), device=dev)
             y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty(max(sg.skinny_gemm_lowp_workspace(M, N, K), 256),
+            ws = torch.empty(max(sg.skinny_gemm_mxfp4_workspace(M, N, K), 256),
                              dtype=torch.uint8, device=dev)
 
             def mx(cw, sw, x=x, y32=y32, y16=y16, ws=ws):
                 return lambda: sg.skinny_gemm_mxfp4(x, cw, sw, y_f32=y32, y_bf16=y16, workspace=ws)
             nbytes = N * K // 2 + N * K // 32 + M * K * 2 + M * N * 6
-            run(label, M, N, K, "lowp_chunk" if M >= 17 else "mxfp4_mfma" if M >= 9
-                else "mxfp4_rowdot", [mx(cw, sw) for cw, sw in ring], nbytes)
+            run(label, M, N, K, lowp_plan_label("mxfp4", M, N, 0),
+                [mx(cw, sw) for cw, sw in ring], nbytes)
         del ring
     # FP8 weights (e4m3 codes, 128 x 128 block scales)
     for label, Ms, N, K in (("fp8 8192x7168", (1, 2, 16), 8192, 7168),
@@ -1027,13 +1036,13 @@ def profile_workloads(torch, sg, si, L, manifest_path, reps=3):
             x = si.normal_bf16((M, K), 1.0, 22, dev)
             y32 = torch.empty((M, N), device=dev)
             y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty(max(sg.skinny_gemm_lowp_workspace(M, N, K), 256),
+            ws = torch.empty(max(sg.skinny_gemm_fp8_workspace(M, N, K), 256),
                              dtype=torch.uint8, device=dev)
 
             def f8(cw, sw, x=x, y32=y32, y16=y16, ws=ws):
                 return lambda: sg.skinny_gemm_fp8(x, cw, sw, y_f32=y32, y_bf16=y16, workspace=ws)
             nbytes = N * K + scales.numel() * 4 + M * K * 2 + M * N * 6
-            run(label, M, N, K, "lowp_chunk" if M >= 17 else "fp8_mfma" if M >= 5 else "fp8_rowdot",
+            run(label, M, N, K, lowp_plan_label("fp8", M, N, 0),
                 [f8(cw, sw) for cw, sw in ring], nbytes)
         del ring
     # router scores + top-8 (E = 384, K = 7168)

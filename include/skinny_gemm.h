@@ -227,16 +227,18 @@ sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int
  *   + y), r may alias y_bf16) or of skinny_gemm otherwise.  The weight stream
  *   is a quarter of bf16's plus 1/16 for the scales.  M <= 8 runs on the
  *   vector ALU and 9 <= M <= 16 on bf16 matrix cores (one launch, the
- *   workspace is not used); 17 <= M <= 64 runs the matrix-core chunk kernel
- *   (x staged once per 128 or 256 weight rows, K split between workgroups)
- *   and, when it splits K, the deterministic reduction: the fp32 partials
- *   need skinny_gemm_lowp_workspace(M, N, K) bytes of workspace (16-byte
+ *   workspace is not used), except 12 <= M <= 16 where N > 5888; there and
+ *   for 17 <= M <= 64 the matrix-core chunk kernel runs (x staged once per
+ *   128 or 256 weight rows, K split between workgroups) and, when it splits
+ *   K, the deterministic reduction: the fp32 partials need
+ *   skinny_gemm_mxfp4_workspace(M, N, K) bytes of workspace (16-byte
  *   aligned; NULL when that is 0), summed in ascending split order.
  * Batch 1 to 64 is the decode path of [P] Method details.
  * Limits: 0 <= M <= 64 (M > 64: SG_ERR_UNSUPPORTED), 0 <= N <= 1<<20,
  * 0 <= K <= 1<<20 (else SG_ERR_SHAPE), K % 32 == 0 (SG_ERR_ALIGN); K <=
- * 32768 at M <= 2 and 16384 for 3 <= M <= 8, and from 17 rows a split whose
- * x chunk fits in LDS (any K up to 65536) (else SG_ERR_UNSUPPORTED); a short
+ * 32768 at M <= 2 and 16384 for 3 <= M <= 8, and on the chunk kernel a
+ * split whose x chunk fits in LDS (any K up to 65536) (else
+ * SG_ERR_UNSUPPORTED); a short
  * workspace: SG_ERR_WORKSPACE.  x, W_codes, r, outputs and the workspace
  * 16-byte aligned; W_scales any alignment. */
 sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
@@ -255,13 +257,13 @@ sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
  * [M, N] (at least one); r (nullable) bf16 [M, N] gives the fused residual
  * y = r + x W^T as for skinny_gemm_residual (y_bf16 may equal r).  A NaN
  * code or scale makes its outputs NaN.  M <= 4 runs on the vector ALU,
- * 5 <= M <= 16 on bf16 matrix cores (codes converted exactly to bf16, each
- * 128-column window's sum scaled once; one launch, no workspace), 17 <= M <=
- * 64 on the matrix-core chunk kernel with the workspace and reduction of
- * skinny_gemm_mxfp4 (skinny_gemm_lowp_workspace bytes).  Limits: 0 <= M <=
+ * 5 <= M <= 11 on bf16 matrix cores (codes converted exactly to bf16, each
+ * 128-column window's sum scaled once; one launch, no workspace), 12 <= M
+ * <= 64 on the matrix-core chunk kernel with the workspace and reduction of
+ * skinny_gemm_mxfp4 (skinny_gemm_fp8_workspace bytes).  Limits: 0 <= M <=
  * 64, K % 16 == 0 (else SG_ERR_ALIGN), M * K <= 32768 at M <= 2 (x staged in
- * LDS) and K <= 16384 at M = 3, 4 (x in registers), any K for 5 <= M <= 16,
- * and from 17 rows a split whose x chunk fits in LDS (any K up to 65536)
+ * LDS) and K <= 16384 at M = 3, 4 (x in registers), any K for 5 <= M <= 11,
+ * and from 12 rows a split whose x chunk fits in LDS (any K up to 65536)
  * (else SG_ERR_UNSUPPORTED), N, K <= 1<<20; a short workspace:
  * SG_ERR_WORKSPACE.  x, W_codes, r, outputs and the workspace 16-byte
  * aligned, W_scales 4-byte aligned.  Allocates nothing. */
@@ -270,11 +272,12 @@ sg_status skinny_gemm_fp8(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
                           float* y_f32, sg_bf16* y_bf16, void* workspace, size_t workspace_bytes,
                           void* stream);
 
-/* Workspace bytes skinny_gemm_fp8 and skinny_gemm_mxfp4 need for an M x N x K
- * projection: the fp32 split-K partials [S, N, 16*ceil(M/16)] of the chunk
- * kernel when 17 <= M <= 64 and it splits K; 0 otherwise (M <= 16, one
- * split, or sizes the calls reject). */
-size_t skinny_gemm_lowp_workspace(int32_t M, int32_t N, int32_t K);
+/* Workspace bytes skinny_gemm_fp8 (resp. skinny_gemm_mxfp4) needs for an
+ * M x N x K projection: the fp32 split-K partials [S, N, 16*ceil(M/16)] of
+ * the chunk kernel when the call runs it and it splits K; 0 otherwise (the
+ * one-launch kernels, one split, or sizes the call rejects). */
+size_t skinny_gemm_fp8_workspace(int32_t M, int32_t N, int32_t K);
+size_t skinny_gemm_mxfp4_workspace(int32_t M, int32_t N, int32_t K);
 
 /* One MoE decode step of a layer on one GPU, with the shared expert on its
  * own stream ([P] Method details §3; [F] Partie 1 §3: the shared expert runs

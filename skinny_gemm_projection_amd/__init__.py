@@ -28,7 +28,7 @@ __all__ = [
     "skinny_gemm_noalloc", "SG_NOALLOC_MAX_WORKSPACE", "grouped_skinny_gemm_workspace", "grouped_skinny_gemm", "skinny_gemm_prefetch",
     "skinny_gemm_router_topk", "router_topk", "skinny_moe_step_workspace", "skinny_moe_step",
     "concat_router_shared", "MOE_STEP_MODES", "skinny_gemm_mxfp4", "SG_KERNEL_MXFP4",
-    "skinny_gemm_fp8", "SG_KERNEL_FP8", "skinny_gemm_lowp_workspace",
+    "skinny_gemm_fp8", "SG_KERNEL_FP8", "skinny_gemm_fp8_workspace", "skinny_gemm_mxfp4_workspace",
     "skinny_gemm_status_str", "skinny_gemm_get_counters", "skinny_gemm_reset_counters",
     "SgPlan", "SkinnyGemmError", "KERNEL_NAMES", "SG_KERNEL_NONE", "SG_KERNEL_GEMV",
     "SG_KERNEL_SPLITK_VALU", "SG_KERNEL_SPLITK_MFMA", "SG_KERNEL_REDUCE", "SG_KERNEL_MOE_TABLE",
@@ -260,9 +260,14 @@ def _side_resources(device):
     return res
 
 
-def skinny_gemm_lowp_workspace(M: int, N: int, K: int) -> int:
-    """Workspace bytes the FP8 / MXFP4 projections need (0 up to 16 rows)."""
-    return int(_c().skinny_gemm_lowp_workspace(M, N, K))
+def skinny_gemm_fp8_workspace(M: int, N: int, K: int) -> int:
+    """Workspace bytes skinny_gemm_fp8 needs for an M x N x K projection (0 when none)."""
+    return int(_c().skinny_gemm_fp8_workspace(M, N, K))
+
+
+def skinny_gemm_mxfp4_workspace(M: int, N: int, K: int) -> int:
+    """Workspace bytes skinny_gemm_mxfp4 needs for an M x N x K projection (0 when none)."""
+    return int(_c().skinny_gemm_mxfp4_workspace(M, N, K))
 
 
 def skinny_gemm_mxfp4(x: torch.Tensor, W_codes: torch.Tensor, W_scales: torch.Tensor,
@@ -270,8 +275,8 @@ def skinny_gemm_mxfp4(x: torch.Tensor, W_codes: torch.Tensor, W_scales: torch.Te
     """y = x W^T for MXFP4 weights: W_codes uint8 [N, K/2] (two e2m1 codes a byte, low
     nibble first), W_scales uint8 [N, K/32] (e8m0 block scales); x bf16 [M, K], M <= 64.
     Writes y_f32 and/or y_bf16 [M, N]; with r (bf16 [M, N]) the fused residual
-    y = r + x W^T.  Allocates y_f32 when no output is given, and the workspace (from
-    17 rows) when none is given; returns the outputs."""
+    y = r + x W^T.  Allocates y_f32 when no output is given, and the workspace (when
+    the chunk kernel splits K) when none is given; returns the outputs."""
     dev = x.device
     M, K = x.shape
     N = W_codes.shape[0]
@@ -282,7 +287,7 @@ def skinny_gemm_mxfp4(x: torch.Tensor, W_codes: torch.Tensor, W_scales: torch.Te
         y_f32 = torch.empty((M, N), dtype=torch.float32, device=dev)
     for t, name in ((y_f32, "y_f32"), (y_bf16, "y_bf16"), (r, "r")):
         _shape(t, (M, N), name)
-    ws, ws_bytes = _workspace(skinny_gemm_lowp_workspace(M, N, K), workspace, dev)
+    ws, ws_bytes = _workspace(skinny_gemm_mxfp4_workspace(M, N, K), workspace, dev)
     st = _c().skinny_gemm_mxfp4(
         M, N, K, _ptr(x, torch.bfloat16, "x", dev), _ptr(W_codes, torch.uint8, "W_codes", dev),
         _ptr(W_scales, torch.uint8, "W_scales", dev), _ptr(r, torch.bfloat16, "r", dev),
@@ -298,8 +303,8 @@ def skinny_gemm_fp8(x: torch.Tensor, W_codes: torch.Tensor, W_scales: torch.Tens
     """y = x W^T for FP8 weights: W_codes uint8 [N, K] (OCP E4M3 codes), W_scales float32
     [ceil(N/128), ceil(K/128)] (one scale per 128 x 128 block); x bf16 [M, K], M <= 64.
     Writes y_f32 and/or y_bf16 [M, N]; with r (bf16 [M, N]) the fused residual
-    y = r + x W^T.  Allocates y_f32 when no output is given, and the workspace (from
-    17 rows) when none is given; returns the outputs."""
+    y = r + x W^T.  Allocates y_f32 when no output is given, and the workspace (when
+    the chunk kernel splits K) when none is given; returns the outputs."""
     dev = x.device
     M, K = x.shape
     N = W_codes.shape[0]
@@ -310,7 +315,7 @@ def skinny_gemm_fp8(x: torch.Tensor, W_codes: torch.Tensor, W_scales: torch.Tens
         y_f32 = torch.empty((M, N), dtype=torch.float32, device=dev)
     for t, name in ((y_f32, "y_f32"), (y_bf16, "y_bf16"), (r, "r")):
         _shape(t, (M, N), name)
-    ws, ws_bytes = _workspace(skinny_gemm_lowp_workspace(M, N, K), workspace, dev)
+    ws, ws_bytes = _workspace(skinny_gemm_fp8_workspace(M, N, K), workspace, dev)
     st = _c().skinny_gemm_fp8(
         M, N, K, _ptr(x, torch.bfloat16, "x", dev), _ptr(W_codes, torch.uint8, "W_codes", dev),
         _ptr(W_scales, torch.float32, "W_scales", dev), _ptr(r, torch.bfloat16, "r", dev),

@@ -99,8 +99,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.skinny_gemm_router_topk.argtypes = [p, i32, i32, i32, p, p, p]
     lib.skinny_gemm_mxfp4.argtypes = [i32, i32, i32, p, p, p, p, p, p, p, sz, p]
     lib.skinny_gemm_fp8.argtypes = [i32, i32, i32, p, p, p, p, p, p, p, sz, p]
-    lib.skinny_gemm_lowp_workspace.argtypes = [i32, i32, i32]
-    lib.skinny_gemm_lowp_workspace.restype = sz
+    for name in ("skinny_gemm_fp8_workspace", "skinny_gemm_mxfp4_workspace"):
+        getattr(lib, name).argtypes = [i32, i32, i32]
+        getattr(lib, name).restype = sz
     lib.skinny_moe_step_workspace.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.skinny_moe_step_workspace.restype = sz
     lib.skinny_moe_step.argtypes = [ctypes.POINTER(SgMoeStep), p, sz, p, p, p, p]

@@ -230,20 +230,36 @@ sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int
     return sg::router_topk_call(scores, E, T, E, k, topk_ids, topk_scores, stream);
 }
 
-size_t skinny_gemm_lowp_workspace(int32_t M, int32_t N, int32_t K) {
-    if (M < sg::kLowpChunkFromM || M > sg::kLowpMaxM || N < 1 || N > (1 << 20) || K < 0 ||
-        K > (1 << 20))
+}  // extern "C"
+
+namespace {
+
+size_t lowp_workspace(int fmt, int32_t M, int32_t N, int32_t K) {
+    if (N < 1 || N > (1 << 20) || K < 0 || K > (1 << 20) || !sg::lowp_use_chunk(fmt, M, N))
         return 0;
     sg::LowpChunkPlan lp;
     return sg::lowp_chunk_plan(M, N, K, &lp) ? lp.workspace : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t skinny_gemm_fp8_workspace(int32_t M, int32_t N, int32_t K) {
+    return lowp_workspace(sg::kLowpFp8, M, N, K);
+}
+
+size_t skinny_gemm_mxfp4_workspace(int32_t M, int32_t N, int32_t K) {
+    return lowp_workspace(sg::kLowpMxfp4, M, N, K);
 }
 
 }  // extern "C"
 
 namespace {
 
-// The 17..64-row path shared by both formats: the split plan, the workspace
-// check, then the chunk kernel (and the reduction when the plan splits K).
+// The chunk-kernel path shared by both formats: the split plan, the
+// workspace check, then the chunk kernel (and the reduction when the plan
+// splits K).
 sg_status lowp_chunk_call(int fmt, int32_t M, int32_t N, int32_t K, const sg_bf16* x,
                           const void* W_codes, const void* W_scales, const sg_bf16* r,
                           float* y_f32, sg_bf16* y_bf16, void* workspace, size_t workspace_bytes,
@@ -279,7 +295,7 @@ sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
     if (M < 0 || N < 0 || N > (1 << 20) || K < 0 || K > (1 << 20)) return SG_ERR_SHAPE;
     if (M > sg::kLowpMaxM) return SG_ERR_UNSUPPORTED;
     if (K % 32 != 0) return SG_ERR_ALIGN;
-    const bool chunk = M >= sg::kLowpChunkFromM;
+    const bool chunk = sg::lowp_use_chunk(sg::kLowpMxfp4, M, N);
     int nb, splits;
     if (M > 0 && !chunk && !sg::mxfp4_split(M, K, &nb, &splits)) return SG_ERR_UNSUPPORTED;
     sg::LowpChunkPlan lp;
@@ -313,7 +329,7 @@ sg_status skinny_gemm_fp8(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
     if (M < 0 || N < 0 || N > (1 << 20) || K < 0 || K > (1 << 20)) return SG_ERR_SHAPE;
     if (K % 16 != 0) return SG_ERR_ALIGN;
     if (M > sg::kLowpMaxM) return SG_ERR_UNSUPPORTED;
-    const bool chunk = M >= sg::kLowpChunkFromM;
+    const bool chunk = sg::lowp_use_chunk(sg::kLowpFp8, M, N);
     if (M > 0 && !chunk && !sg::fp8_size_ok(M, K)) return SG_ERR_UNSUPPORTED;
     sg::LowpChunkPlan lp;
     if (chunk && N > 0 && !sg::lowp_chunk_plan(M, N, K, &lp)) return SG_ERR_UNSUPPORTED;

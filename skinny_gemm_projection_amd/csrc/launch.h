@@ -140,8 +140,10 @@ hipError_t launch_mxfp4(int M, int N, int K, const void* x, const void* Wq, cons
 // MXFP4: Wq [N, K/2], Ws [N, K/32] e8m0.
 constexpr int kLowpFp8 = 0;
 constexpr int kLowpMxfp4 = 1;
-constexpr int kLowpChunkFromM = 17;
 constexpr int kLowpMaxM = 64;
+// Whether a format's M x N projection runs the chunk kernel (else the
+// one-launch kernels of fp8.hip / mxfp4.hip, which take up to 16 rows).
+bool lowp_use_chunk(int fmt, int M, int N);
 struct LowpChunkPlan {
     int MT, NT, S, chunk, pitch;
     size_t lds, workspace;

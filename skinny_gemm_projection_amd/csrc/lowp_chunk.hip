@@ -1,14 +1,15 @@
 // lowp_chunk.hip -- projection with block-scaled 8-bit (FP8 e4m3) or 4-bit
-// (MXFP4) weights for batches of 17 to 64 rows, on gfx950 matrix cores.
+// (MXFP4) weights for batches of 12 to 64 rows, on gfx950 matrix cores.
 //
 // The decode path the pages describe covers batch 1 to 64 ("Hyper Optimizing
 // Kimi K3 in vLLM" deepnotes page, Method details: batch 1-64 decode; §1:
 // split-K at larger batch) and their later model ships low-precision weights
-// (Experimental setup and Supplementary details).  Up to 16 rows the FP8 and
-// MXFP4 kernels give each workgroup one or two 16-row weight tiles and read
-// all of x from L2 per workgroup; from 17 rows that x traffic would be one to
-// eight times the code bytes, so this kernel uses the bf16 chunk kernel's
-// shape instead:
+// (Experimental setup and Supplementary details).  The one-launch FP8 and
+// MXFP4 kernels (up to 16 rows) give each workgroup one or two 16-row weight
+// tiles and read all of x from L2 per workgroup; as M grows that x traffic
+// reaches and passes the code bytes, so from 12 rows (FP8, and MXFP4 on wide
+// matrices; MXFP4 from 17 rows otherwise) this kernel uses the bf16 chunk
+// kernel's shape instead:
 //
 //  * a workgroup of 8 waves owns 128 (NT = 1) or 256 (NT = 2) weight rows --
 //    16 * NT per wave -- and one K chunk (a whole number of 128-element
@@ -48,6 +49,7 @@ __global__ __launch_bounds__(kLpThreads) void lowp_chunk_kernel(
     const uint4* __restrict__ x, const uint8_t* __restrict__ Wq, const void* __restrict__ Ws,
     int M, int N, int K, int chunk, int pitch, Epilogue ep) {
     constexpr bool kFp8 = FMT == kLowpFp8;
+    constexpr bool kHoist = kFp8 && MT <= 2;
     constexpr int XR = 16 * MT;
     extern __shared__ uint4 xs[];  // [XR][pitch] pieces of the chunk's x rows
 
@@ -63,28 +65,6 @@ __global__ __launch_bounds__(kLpThreads) void lowp_chunk_kernel(
     if (blockIdx.x * 128 * NT >= N) return;           // padding column of the grid
     const int row0 = blockIdx.x * 128 * NT + wv * 16 * NT;
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16 * NT, N - row0)));
-
-    // ---- x of the chunk into LDS: row r, piece p at xs[r * pitch + p]
-    {
-        const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K8 * 16u);
-        const int P8 = chunk / kPiece;
-        const int total = XR * P8;
-        uint4 v[kLpXLoads];
-#pragma unroll
-        for (int j = 0; j < kLpXLoads; ++j) {
-            const int idx = tid + j * kLpThreads;
-            const int r = idx / P8, p = idx - r * P8;
-            const bool ok = idx < total && r < M && p * kPiece < len;
-            v[j] = load16<kCached>(rx, ok ? ((uint32_t)r * K8 + k0 / kPiece + p) * 16u : kLpOut);
-        }
-#pragma unroll
-        for (int j = 0; j < kLpXLoads; ++j) {
-            const int idx = tid + j * kLpThreads;
-            const int r = idx / P8, p = idx - r * P8;
-            if (idx < total) xs[r * pitch + p] = v[j];
-        }
-    }
-    __syncthreads();
 
     // ---- weight codes of the wave's 16 * NT rows
     // FP8: rows of K/16 units of 16 codes; scales [ceil(N/128)][ceil(K/128)].
@@ -103,10 +83,16 @@ __global__ __launch_bounds__(kLpThreads) void lowp_chunk_kernel(
         for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     constexpr int UPW = kFp8 ? 2 : 1;  // 16-byte code loads per lane, window and tile
-    for (int wb = 0; wb < windows; wb += D) {
+    struct Batch {
         uint4 wq[D][NT][UPW];
         uint32_t sb[D][NT];
         float sf[D];
+    };
+    // codes (and scales) of windows wb .. wb+D-1 of the chunk
+    auto load_batch = [&](Batch& bt, int wb) {
+        auto& wq = bt.wq;
+        auto& sb = bt.sb;
+        auto& sf = bt.sf;
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int w = wb + d;
@@ -131,6 +117,41 @@ __global__ __launch_bounds__(kLpThreads) void lowp_chunk_kernel(
             }
             if (kFp8) sf[d] = live && rows > 0 ? fsc[gw] : 0.0f;  // no scale row past N
         }
+    };
+
+    Batch first;  // the early batch (kHoist)
+    // ---- x of the chunk into LDS: row r, piece p at xs[r * pitch + p]
+    {
+        const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K8 * 16u);
+        const int P8 = chunk / kPiece;
+        const int total = XR * P8;
+        uint4 v[kLpXLoads];
+#pragma unroll
+        for (int j = 0; j < kLpXLoads; ++j) {
+            const int idx = tid + j * kLpThreads;
+            const int r = idx / P8, p = idx - r * P8;
+            const bool ok = idx < total && r < M && p * kPiece < len;
+            v[j] = load16<kCached>(rx, ok ? ((uint32_t)r * K8 + k0 / kPiece + p) * 16u : kLpOut);
+        }
+        // FP8 up to 32 rows: the first windows' codes are requested right
+        // behind x (only the x loads are waited for before the LDS copy and
+        // the barrier).  Measured on MI355X this pays there (4096 x 7168,
+        // M = 16: 12.1 -> 11.5 us) and loses at 64 rows and for MXFP4.
+        if constexpr (kHoist) load_batch(first, 0);
+#pragma unroll
+        for (int j = 0; j < kLpXLoads; ++j) {
+            const int idx = tid + j * kLpThreads;
+            const int r = idx / P8, p = idx - r * P8;
+            if (idx < total) xs[r * pitch + p] = v[j];
+        }
+    }
+    __syncthreads();
+
+    // windows wb .. wb+D-1 from the registers load_batch(wb) filled
+    auto compute_batch = [&](const Batch& bt, int wb) {
+        const auto& wq = bt.wq;
+        const auto& sf = bt.sf;
+        const auto& sb = bt.sb;
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int w = wb + d;
@@ -224,6 +245,15 @@ __global__ __launch_bounds__(kLpThreads) void lowp_chunk_kernel(
                 }
             }
         }
+    };
+
+    // a batch issued before the barrier is consumed outside the loop: behind
+    // a loop header the compiler would wait for all of its loads at once
+    if constexpr (kHoist) compute_batch(first, 0);
+    for (int wb = kHoist ? D : 0; wb < windows; wb += D) {
+        Batch bt;
+        load_batch(bt, wb);
+        compute_batch(bt, wb);
     }
 
     if (ep.partial) {
@@ -256,10 +286,26 @@ __global__ __launch_bounds__(kLpThreads) void lowp_chunk_kernel(
 constexpr int kLpCus = 256;
 constexpr size_t kLpLdsMax = 144 * 1024;  // x staging (the kernel uses no other LDS)
 
+// Two 16-row tiles a wave while their 256-row workgroups, 8 splits each,
+// still give three quarters of the compute units one.
+int lowp_nt(int N) { return ((N + 255) / 256) * 8 >= 3 * kLpCus / 4 ? 2 : 1; }
+
 }  // namespace
 
+// Measured on MI355X (K = 7168 or 8192, N = 4096..8192): from 12 rows the
+// chunk kernel beats the FP8 matrix-core kernel (N = 7168, K = 8192, M = 16:
+// 21.9 -> 17.8 us; N = 4096, K = 7168, M = 16: 12.3 -> 11.5 us) and, where a
+// wave takes two tiles, the MXFP4 one (N = 8192, M = 16: 19.5 -> 18.0 us); at
+// N = 4096 the one-launch MXFP4 kernels stay ahead up to 16 rows (M = 12:
+// 12.0 against 12.9 us).
+bool lowp_use_chunk(int fmt, int M, int N) {
+    if (M > kLowpMaxM || M < 12) return false;
+    if (M >= 17 || fmt == kLowpFp8) return true;
+    return lowp_nt(N) == 2;
+}
+
 bool lowp_chunk_plan(int M, int N, int K, LowpChunkPlan* p) {
-    if (M < kLowpChunkFromM || M > kLowpMaxM || N < 1 || K < 0) return false;
+    if (M < 1 || M > kLowpMaxM || N < 1 || K < 0) return false;
     const int MT = (M + 15) / 16;
     const int XR = 16 * MT;
     if (K == 0) {  // outputs are r (or zero): one launch, nothing to stage
@@ -267,9 +313,7 @@ bool lowp_chunk_plan(int M, int N, int K, LowpChunkPlan* p) {
                            (size_t)XR * (kLpWindow / kPiece + 1) * 16, 0};
         return true;
     }
-    // two 16-row tiles a wave while their 256-row workgroups, 8 splits each,
-    // still give three quarters of the compute units one
-    const int NT = ((N + 255) / 256) * 8 >= 3 * kLpCus / 4 ? 2 : 1;
+    const int NT = lowp_nt(N);
     const int tiles = mfma_grid_tiles(N, 128 * NT);
     const int windows = (K + kLpWindow - 1) / kLpWindow;
     // the smallest split whose grid fills the compute units and whose x chunk
@@ -318,10 +362,12 @@ hipError_t launch_lowp_chunk(int fmt, int M, int N, int K, const void* x, const 
                                              fin, stream)                                         \
                        : hipSuccess;                                                              \
     }
-    SG_LP(kLowpFp8, 2, 1, kD8) SG_LP(kLowpFp8, 3, 1, kD8) SG_LP(kLowpFp8, 4, 1, kD8)
-    SG_LP(kLowpFp8, 2, 2, kD8) SG_LP(kLowpFp8, 3, 2, kD8) SG_LP(kLowpFp8, 4, 2, kD8)
-    SG_LP(kLowpMxfp4, 2, 1, kD4) SG_LP(kLowpMxfp4, 3, 1, kD4) SG_LP(kLowpMxfp4, 4, 1, kD4)
-    SG_LP(kLowpMxfp4, 2, 2, kD4) SG_LP(kLowpMxfp4, 3, 2, kD4) SG_LP(kLowpMxfp4, 4, 2, kD4)
+    SG_LP(kLowpFp8, 1, 1, kD8) SG_LP(kLowpFp8, 2, 1, kD8) SG_LP(kLowpFp8, 3, 1, kD8)
+    SG_LP(kLowpFp8, 4, 1, kD8) SG_LP(kLowpFp8, 1, 2, kD8) SG_LP(kLowpFp8, 2, 2, kD8)
+    SG_LP(kLowpFp8, 3, 2, kD8) SG_LP(kLowpFp8, 4, 2, kD8)
+    SG_LP(kLowpMxfp4, 1, 1, kD4) SG_LP(kLowpMxfp4, 2, 1, kD4) SG_LP(kLowpMxfp4, 3, 1, kD4)
+    SG_LP(kLowpMxfp4, 4, 1, kD4) SG_LP(kLowpMxfp4, 1, 2, kD4) SG_LP(kLowpMxfp4, 2, 2, kD4)
+    SG_LP(kLowpMxfp4, 3, 2, kD4) SG_LP(kLowpMxfp4, 4, 2, kD4)
 #undef SG_LP
     return hipErrorInvalidValue;
 }

@@ -284,17 +284,18 @@ def test_fp8_size_limits_return_before_launch():
         return c.skinny_gemm_fp8(M, N, K, A, A, A, None, y, None, ws, ws_bytes, None)
 
     assert call(65, 64) == 3                              # above the decode path
-    assert call(17, 64) == 1 and call(64, 65536) == 1     # chunk kernel from 17 rows
-    assert call(64, 1 << 20) == 3                         # x chunk would not fit in LDS
+    assert call(12, 64) == 1 and call(64, 65536) == 1     # chunk kernel from 12 rows
+    assert call(64, 1 << 20) == 3 and call(12, 1 << 20) == 3  # x chunk would not fit in LDS
     assert call(17, 7168, y=A, N=4096) == 5               # its split-K workspace is missing
-    need = sg.skinny_gemm_lowp_workspace(17, 4096, 7168)
+    assert call(12, 7168, y=A, N=4096) == 5
+    need = sg.skinny_gemm_fp8_workspace(17, 4096, 7168)
     assert call(17, 7168, y=A, N=4096, ws=A, ws_bytes=need - 256) == 5
     assert call(17, 7168, y=A, N=4096, ws=A + 8, ws_bytes=need) == 4  # misaligned workspace
     assert call(1, 32768) == 1 and call(1, 32784) == 3   # M * K <= 32768 (LDS) at M <= 2
     assert call(2, 16384) == 1 and call(2, 16400) == 3
     assert call(3, 16384) == 1 and call(3, 16400) == 3   # K <= 16384 (registers) at M = 3, 4
     assert call(4, 16384) == 1 and call(4, 16400) == 3
-    assert call(5, 8208) == 1 and call(16, 1 << 20) == 1  # matrix-core kernel: any K
+    assert call(5, 8208) == 1 and call(11, 1 << 20) == 1  # matrix-core kernel: any K
     assert call(1, 24) == 4
     assert call(0, 64) == 0
     assert call(4, 16384, y=A + 4) == 4  # misaligned output
@@ -302,16 +303,23 @@ def test_fp8_size_limits_return_before_launch():
 
 
 def test_lowp_workspace_sizes():
-    # fp32 partials [S, N, 16 * ceil(M / 16)] of the low-precision chunk kernel, from 17 rows
-    assert sg.skinny_gemm_lowp_workspace(16, 4096, 7168) == 0
-    assert sg.skinny_gemm_lowp_workspace(65, 4096, 7168) == 0
-    assert sg.skinny_gemm_lowp_workspace(17, 0, 7168) == 0
-    assert sg.skinny_gemm_lowp_workspace(17, 4096, 0) == 0      # K = 0: one launch, no split
-    for M, N, K in ((17, 4096, 7168), (32, 8192, 7168), (64, 7168, 8192), (48, 200, 1024)):
-        b = sg.skinny_gemm_lowp_workspace(M, N, K)
-        mp = 16 * -(-M // 16)
-        assert b % 256 == 0 and b >= 2 * N * mp * 4, (M, N, K, b)  # at least two splits
-        assert (b // (N * mp * 4)) * N * mp * 4 <= b < (b // (N * mp * 4) + 1) * N * mp * 4
+    # fp32 partials [S, N, 16 * ceil(M / 16)] of the low-precision chunk kernel: FP8 from
+    # 12 rows, MXFP4 from 17 rows and from 12 where a wave takes two tiles (N > 5888)
+    fp8, mx = sg.skinny_gemm_fp8_workspace, sg.skinny_gemm_mxfp4_workspace
+    assert fp8(11, 4096, 7168) == 0 and fp8(12, 4096, 7168) > 0
+    assert mx(16, 5888, 7168) == 0 and mx(12, 5889, 7168) > 0 and mx(17, 4096, 7168) > 0
+    assert mx(11, 8192, 7168) == 0
+    for f in (fp8, mx):
+        assert f(65, 4096, 7168) == 0
+        assert f(17, 0, 7168) == 0
+        assert f(17, 4096, 0) == 0      # K = 0: one launch, no split
+        for M, N, K in ((17, 4096, 7168), (32, 8192, 7168), (64, 7168, 8192), (48, 200, 1024),
+                        (12, 8192, 7168), (16, 7168, 8192)):
+            b = f(M, N, K)
+            mp = 16 * -(-M // 16)
+            assert b % 256 == 0 and b >= 2 * N * mp * 4, (M, N, K, b)  # at least two splits
+            assert (b // (N * mp * 4)) * N * mp * 4 <= b < (b // (N * mp * 4) + 1) * N * mp * 4
+    assert fp8(20, 8192, 7168) == mx(20, 8192, 7168)  # one plan for both formats
 
 
 @no_gpu_only

@@ -1,6 +1,6 @@
 """GPU parity of the projection with FP8 weights (skinny_gemm_fp8: e4m3 codes, one fp32
 scale per 128 x 128 block) through the C ABI, M = 1..64 (vector ALU, matrix cores, and
-from 17 rows the chunk kernel with its split-K reduction), against oracle_projection_fp8
+from 12 rows the chunk kernel with its split-K reduction), against oracle_projection_fp8
 on the same seeded codes and scales: fp32 |got - ref| <= 1e-3 * A, bf16 adds 2^-8 |ref|, the
 residual adds 2^-23 |r + y|.  Integer-valued activations and weights with power-of-two
 scales are bit-exact (every product and partial sum is exact in fp32)."""
@@ -30,8 +30,8 @@ def run(x, codes, scales, r=None, f32=True, bf16=True):
     torch.cuda.synchronize()
     d = counters_delta(before, sg.skinny_gemm_get_counters())
     assert d[sg.SG_KERNEL_FP8] == (1 if M > 0 and N > 0 else 0)
-    # from 17 rows the chunk kernel, with the reduction when it splits K
-    splits = M >= 17 and sg.skinny_gemm_lowp_workspace(M, N, x.shape[1]) > 0
+    # the chunk kernel adds the reduction when it splits K (the only case with a workspace)
+    splits = sg.skinny_gemm_fp8_workspace(M, N, x.shape[1]) > 0
     assert d[sg.SG_KERNEL_REDUCE] == (1 if splits and N > 0 else 0)
     return y32, y16
 
@@ -44,11 +44,13 @@ SHAPES = [(1, 40, 16), (1, 129, 112), (1, 200, 1040), (1, 77, 8192), (1, 33, 820
           # from M = 5 the matrix-core kernel: 128-column windows split over a team,
           # ragged last window, ragged 16-row tile, any K
           (5, 100, 1040), (6, 131, 4112), (7, 64, 7168), (8, 257, 8192), (8, 33, 16),
-          (9, 129, 2064), (12, 300, 7168), (16, 40, 20000), (16, 1, 144), (13, 200, 30000),
+          (9, 129, 2064), (11, 300, 7168), (10, 40, 20000), (11, 1, 144), (11, 200, 30000),
           # from 8161 rows two 16-row tiles per wave (ragged last 32-row tile)
-          (9, 8200, 144), (16, 8192, 1040), (5, 8177, 2064),
-          # from 17 rows the chunk kernel: x rows padded to 32, 48, 64; ragged
+          (9, 8200, 144), (11, 8192, 1040), (5, 8177, 2064),
+          # from 12 rows the chunk kernel: x rows padded to 16, 32, 48, 64; ragged
           # 128-row tiles and windows; one split (K = 16), several, 256-row tiles
+          (12, 300, 7168), (16, 40, 20000), (16, 1, 144), (13, 200, 30000),
+          (16, 8192, 1040), (14, 8177, 2064),
           (17, 200, 1040), (20, 129, 7168), (32, 300, 4112), (33, 64, 16), (47, 257, 2064),
           (48, 1000, 8192), (64, 33, 30000), (64, 8200, 1040), (17, 6300, 4096),
           (40, 128, 128), (64, 1, 144)]
@@ -125,11 +127,11 @@ def test_fp8_rejections_touch_nothing():
     with pytest.raises(sg.SkinnyGemmError) as e:
         sg.skinny_gemm_fp8(x65, codes, scales, y_f32=y)  # M > 64
     assert e.value.status == 3
-    # from 17 rows: a workspace shorter than the split-K partials need
+    # chunk kernel: a workspace shorter than the split-K partials need
     x20 = si.normal_bf16((20, 4096), 1.0, 6, DEV)
     c20, s20 = si.fp8_weights(4096, 4096, 7, DEV)
     y20 = torch.full((20, 4096), -7.0, device=DEV)
-    need = sg.skinny_gemm_lowp_workspace(20, 4096, 4096)
+    need = sg.skinny_gemm_fp8_workspace(20, 4096, 4096)
     assert need > 0
     before = sg.skinny_gemm_get_counters()
     with pytest.raises(sg.SkinnyGemmError) as e:

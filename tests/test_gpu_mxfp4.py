@@ -1,6 +1,6 @@
 """GPU parity of the projection with MXFP4 weights (skinny_gemm_mxfp4) through the
-C ABI, M = 1..64 (vector ALU, matrix cores, and from 17 rows the chunk kernel with its
-split-K reduction), against oracle_projection_mxfp4 on the same seeded codes and scales:
+C ABI, M = 1..64 (vector ALU, matrix cores, and from 17 rows -- 12 where N > 5888 --
+the chunk kernel with its split-K reduction), against oracle_projection_mxfp4 on the same seeded codes and scales:
 fp32 |got - ref| <= 1e-3 * A, bf16 adds 2^-8 |ref|, the residual adds 2^-23 |r + y|;
 integer-valued activations with unit scales are bit-exact (every product is a
 multiple of 1/2 and every partial sum exact in fp32)."""
@@ -30,8 +30,8 @@ def run(x, codes, scales, r=None, f32=True, bf16=True):
     torch.cuda.synchronize()
     d = counters_delta(before, sg.skinny_gemm_get_counters())
     assert d[sg.SG_KERNEL_MXFP4] == (1 if M > 0 and N > 0 else 0)
-    # from 17 rows the chunk kernel, with the reduction when it splits K
-    splits = M >= 17 and sg.skinny_gemm_lowp_workspace(M, N, x.shape[1]) > 0
+    # the chunk kernel adds the reduction when it splits K (the only case with a workspace)
+    splits = sg.skinny_gemm_mxfp4_workspace(M, N, x.shape[1]) > 0
     assert d[sg.SG_KERNEL_REDUCE] == (1 if splits and N > 0 else 0)
     return y32, y16
 
@@ -42,7 +42,10 @@ SHAPES = [(1, 40, 32), (1, 129, 96), (1, 77, 608), (1, 65, 2080), (1, 33, 8224),
           (12, 33, 608), (13, 70, 8224), (16, 100, 7168), (16, 17, 96), (16, 16, 32),
           # from 8161 rows the matrix-core kernel takes two 16-row tiles a wave
           # (ragged last 32-row tile)
-          (9, 8200, 2080), (16, 8192, 608), (12, 8177, 96),
+          (9, 8200, 2080), (11, 8192, 608), (10, 8177, 96),
+          # 12 to 16 rows: the matrix-core kernel up to N = 5888, the chunk kernel
+          # (256-row tiles) above
+          (13, 5888, 640), (13, 5889, 640), (16, 8192, 608), (12, 8177, 96),
           # from 17 rows the chunk kernel: x rows padded to 32, 48, 64, ragged
           # 128-row tiles and windows, one split and several, 256-row tiles
           (17, 200, 1056), (20, 129, 7168), (32, 300, 4128), (33, 64, 32), (47, 257, 2080),
