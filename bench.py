@@ -115,6 +115,17 @@ class Launcher:
                 raise RuntimeError(self.sg.skinny_gemm_status_str(st))
         return go
 
+    def read_probe(self, W, rows_per_iter, grid):
+        c = self.c
+        args = (W.data_ptr(), W.shape[0], W.shape[1] * W.element_size(), rows_per_iter, grid,
+                self.sp)
+
+        def go():
+            st = c.skinny_gemm_read_probe(*args)
+            if st:
+                raise RuntimeError(self.sg.skinny_gemm_status_str(st))
+        return go
+
     def grouped(self, x, W, ids, out, ws):
         c = self.c
         T, K = x.shape
@@ -247,6 +258,10 @@ def main_workload(torch, sg, si, L, steps, warmup, cyc):
     per_m_ms = {}
     for M in M_LIST:
         per_m_ms[M] = timed_calls(torch, [calls[(M, r)] for r in range(R)], 200, cyc)
+    # the same weight stream with no arithmetic: the read probe on each plan's grid and
+    # rows per iteration, over the same ring
+    probe_ms = {M: timed_calls(torch, [L.read_probe(ring[r], plans[M].tile_n, plans[M].grid)
+                                       for r in range(R)], 200, cyc) for M in M_LIST}
     graph = graph_timing(torch, sg, lambda L2, M, r: L2.projection(plans[M], x[M], ring[r], y32[M],
                                                                     y16[M]),
                          M_LIST, R, y32)
@@ -268,6 +283,11 @@ def main_workload(torch, sg, si, L, steps, warmup, cyc):
         "value": step_bytes * steps / (total_ms * 1e-3) / 1e9,
         "us_per_projection": {str(M): round(us[M], 3) for M in M_LIST},
         "gbs_per_batch": {str(M): round(bytes_per[M] / (us[M] * 1e-6) / 1e9, 1) for M in M_LIST},
+        "read_probe": {str(M): {"grid": plans[M].grid, "rows_per_iter": plans[M].tile_n,
+                                "us": round(1e3 * probe_ms[M], 3),
+                                "GBps": round(W0.numel() * 2 / (probe_ms[M] * 1e-3) / 1e9, 1),
+                                "projection_over_probe": round(per_m_ms[M] / probe_ms[M], 4)}
+                       for M in M_LIST},
         "achieved": achieved, "avg_launch_us": 1e3 * avg_launch_ms,
         "bytes_per_launch": launch_bytes,
         "graph": graph,
@@ -456,6 +476,11 @@ def sweep(torch, sg, si, L, cyc, reps=40):
     # split-K sweep M in {4..64}, K=7168, N=4096, fp32 out
     N, K = 4096, 7168
     ring = ring_copies(torch, si.normal_bf16((N, K), 0.02, si.seed_for(3, si.TAG_W), dev))
+    # first, this matrix read with no arithmetic (the read probe on the M = 1 plan's shape)
+    p1 = sg.skinny_gemm_plan(1, N, K)
+    per = timed_calls(torch, [L.read_probe(w, p1.tile_n, p1.grid) for w in ring], reps, cyc)
+    record("read probe 4096x7168 (weights only)", 0, N, K,
+           f"read_probe rows_per_iter={p1.tile_n} grid={p1.grid}", per, N * K * 2)
     for M in (3, 4, 8, 12, 16, 32, 48, 64):
         x = si.normal_bf16((M, K), 1.0, si.seed_for(3, si.TAG_X) + M, dev)
         p = sg.skinny_gemm_plan(M, N, K)
@@ -1264,6 +1289,9 @@ def main() -> None:
             "traffic": traffic,
             "bytes_per_launch": round(res["bytes_per_launch"]),
             "avg_launch_us": round(res["avg_launch_us"], 3),
+            # the same launches with the arithmetic, reduction and stores taken out (the
+            # library's read probe): the read rate this kernel's load shape reaches here
+            "read_probe": res["read_probe"],
         },
         "cpu_baseline": cpu,
     }

@@ -344,6 +344,21 @@ sg_status skinny_moe_step(const sg_moe_step* step, void* workspace, size_t works
  * bytes a multiple of 16. */
 sg_status skinny_gemm_prefetch(const void* W, size_t bytes, void* stream);
 
+/* Read-bandwidth probe (measurement only; computes and writes nothing).
+ * Small-batch projections are bound by how fast weights stream from HBM
+ * ([P] Method details §1); this call reads W [rows, row_bytes] with the load
+ * shape of the M <= 2 projection kernel -- rows_per_iter (1 or 2) whole rows
+ * per wave and iteration, 1 KB buffer loads with the non-temporal hint, grid
+ * workgroups of 4 waves striding over the row groups -- and no arithmetic,
+ * so its time is what that kernel's loads alone take on this GPU.  Pass the
+ * plan's grid and tile_n (rows per iteration) of the projection to compare.
+ * Limits: 0 <= rows, 16 <= row_bytes <= 16384, 1 <= grid <= 65536,
+ * rows * row_bytes <= 2^40 (else SG_ERR_SHAPE); row_bytes % 16 == 0 and W
+ * 16-byte aligned (SG_ERR_ALIGN); W NULL with rows > 0: SG_ERR_NULL.  Not
+ * counted in the launch counters.  Asynchronous on `stream`. */
+sg_status skinny_gemm_read_probe(const void* W, int32_t rows, int32_t row_bytes,
+                                 int32_t rows_per_iter, int32_t grid, void* stream);
+
 /* Text for a status code (static storage). */
 const char* skinny_gemm_status_str(sg_status status);
 

@@ -25,7 +25,8 @@ from ._lib import (KERNEL_NAMES, SG_KERNEL_GEMV, SG_KERNEL_GROUPED, SG_KERNEL_MO
 
 __all__ = [
     "skinny_gemm_plan", "skinny_gemm_plan_force", "skinny_gemm", "skinny_gemm_residual",
-    "skinny_gemm_noalloc", "SG_NOALLOC_MAX_WORKSPACE", "grouped_skinny_gemm_workspace", "grouped_skinny_gemm", "skinny_gemm_prefetch",
+    "skinny_gemm_noalloc", "SG_NOALLOC_MAX_WORKSPACE", "grouped_skinny_gemm_workspace",
+    "grouped_skinny_gemm", "skinny_gemm_prefetch", "skinny_gemm_read_probe",
     "skinny_gemm_router_topk", "router_topk", "skinny_moe_step_workspace", "skinny_moe_step",
     "concat_router_shared", "MOE_STEP_MODES", "skinny_gemm_mxfp4", "SG_KERNEL_MXFP4",
     "skinny_gemm_fp8", "SG_KERNEL_FP8", "skinny_gemm_fp8_workspace", "skinny_gemm_mxfp4_workspace",
@@ -205,6 +206,16 @@ def skinny_gemm_prefetch(W: torch.Tensor, nbytes: int | None = None, stream=None
     if nbytes > total:
         raise ValueError("nbytes exceeds the tensor")
     _lib.check(_c().skinny_gemm_prefetch(W.data_ptr() or None, nbytes, _stream(stream)))
+
+
+def skinny_gemm_read_probe(W: torch.Tensor, rows_per_iter: int, grid: int, stream=None) -> None:
+    """Read W ([rows, row_bytes] contiguous device tensor) with the M <= 2 projection
+    kernel's load shape and no arithmetic (a measurement of the read rate alone)."""
+    if not W.is_cuda or not W.is_contiguous() or W.dim() != 2:
+        raise ValueError("W: must be a contiguous 2-D device tensor")
+    rows, row_bytes = W.shape[0], W.shape[1] * W.element_size()
+    _lib.check(_c().skinny_gemm_read_probe(W.data_ptr() or None, rows, row_bytes, rows_per_iter,
+                                           grid, _stream(stream)))
 
 
 def skinny_gemm_router_topk(scores: torch.Tensor, k: int, topk_ids=None, topk_scores=None,

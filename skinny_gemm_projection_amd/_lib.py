@@ -96,6 +96,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.grouped_skinny_gemm_workspace.restype = sz
     lib.grouped_skinny_gemm.argtypes = [p, i32, p, i32, i32, i32, p, i32, p, p, p, p, p, sz, p]
     lib.skinny_gemm_prefetch.argtypes = [p, sz, p]
+    lib.skinny_gemm_read_probe.argtypes = [p, i32, i32, i32, i32, p]
     lib.skinny_gemm_router_topk.argtypes = [p, i32, i32, i32, p, p, p]
     lib.skinny_gemm_mxfp4.argtypes = [i32, i32, i32, p, p, p, p, p, p, p, sz, p]
     lib.skinny_gemm_fp8.argtypes = [i32, i32, i32, p, p, p, p, p, p, p, sz, p]

@@ -23,7 +23,8 @@ LIB = os.path.join(HERE, "libskinny_gemm.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "plan.cpp", "moe_step.cpp", "rowdot.hip", "splitk_mfma.hip", "reduce.hip", "moe.hip", "router.hip", "mxfp4.hip",
-           "prefetch.hip", "fp8.hip", "noalloc.hip", "lowp_chunk.hip"]
+           "prefetch.hip", "fp8.hip", "noalloc.hip", "lowp_chunk.hip",
+           "probe.hip"]
 
 
 def hipcc() -> str:

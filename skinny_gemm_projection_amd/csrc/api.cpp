@@ -369,6 +369,23 @@ sg_status skinny_gemm_prefetch(const void* W, size_t bytes, void* stream) {
     return SG_OK;
 }
 
+sg_status skinny_gemm_read_probe(const void* W, int32_t rows, int32_t row_bytes,
+                                 int32_t rows_per_iter, int32_t grid, void* stream) {
+    if (rows < 0 || row_bytes < 16 || row_bytes > 16384 || grid < 1 || grid > 65536 ||
+        (rows_per_iter != 1 && rows_per_iter != 2) ||
+        (int64_t)rows * row_bytes > (int64_t(1) << 40))
+        return SG_ERR_SHAPE;
+    if (row_bytes % 16 != 0) return SG_ERR_ALIGN;
+    if (rows == 0) return SG_OK;
+    if (!W) return SG_ERR_NULL;
+    if (!aligned16(W)) return SG_ERR_ALIGN;
+    (void)hipGetLastError();
+    if (sg::launch_read_probe(W, rows, row_bytes, rows_per_iter, grid,
+                              static_cast<hipStream_t>(stream)) != hipSuccess)
+        return SG_ERR_HIP;
+    return SG_OK;
+}
+
 const char* skinny_gemm_status_str(sg_status status) {
     switch (status) {
         case SG_OK: return "SG_OK";

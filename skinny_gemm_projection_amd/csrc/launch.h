@@ -22,6 +22,10 @@ int rowdot_resident_waves(int M, int nch);
 // waves) by the row-streaming kernel at batch size M.
 bool rowdot_team_split_ok(int M, int S);
 int rowdot_block_threads(int S, bool two_pass);
+// Whether the unsplit small-matrix plan (M <= 2, S == 1) runs the streaming
+// kernel -- one row per step, the next row's loads in flight -- and its grid.
+constexpr int kRowstreamMaxIters = 4;
+bool rowstream_plan(int M, int N, int K, int S, bool two_pass, int* grid);
 
 // Row-streaming VALU kernel (small-matrix path and VALU split-K).
 // x [M, K], W [N, K]; split s covers pieces [s*chunk8, min(K8, (s+1)*chunk8)).
@@ -105,6 +109,10 @@ hipError_t launch_grouped(const void* x, int T, const void* W, int E, int N, int
                           const GroupedWorkspace& g, float* out, hipStream_t stream);
 
 hipError_t launch_prefetch(const void* W, size_t bytes, hipStream_t stream);
+// Read-bandwidth probe: the M <= 2 kernel's load shape over a [rows,
+// row_bytes] matrix with no arithmetic (probe.hip).
+hipError_t launch_read_probe(const void* W, int rows, int row_bytes, int rows_per_iter, int grid,
+                             hipStream_t stream);
 
 // Projection with FP8 e4m3 weights: codes [N, K], fp32 scales [ceil(N/128),
 // ceil(K/128)] (one per 128 x 128 block).  1 <= M <= kFp8MaxM, K % 16 == 0;

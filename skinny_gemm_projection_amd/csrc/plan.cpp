@@ -55,9 +55,6 @@ constexpr Tuned kTuned[] = {
     // cost model's pick of 9 splits (41.4 us) and 128-row tiles (35.7 us)
     {33, 64, 7168, 8192, SG_KERNEL_SPLITK_MFMA, 8, 256},
     {33, 64, 8192, 7168, SG_KERNEL_SPLITK_MFMA, 8, 256},
-    // one row at K = 8192: two K chunks per team (8 loads a row in flight
-    // instead of 16) measured 19.3 against 19.65 us unsplit
-    {1, 1, 7168, 8192, SG_KERNEL_GEMV, 2, 0},
 };
 
 bool split_ok(int32_t S) { return S >= 1 && S <= kMaxSplit; }
@@ -217,9 +214,14 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
             if (two_pass == 0 && !team_ok) return SG_ERR_PLAN;
             if (split_k == 1) two_pass = 0;
             p.k_chunk = chunk_of(K, split_k);
-            const int R = rowdot_rows_per_iter(M, nch_of(p.k_chunk));
-            p.tile_n = R;
-            p.grid = rowdot_grid(M, N, K, split_k, p.k_chunk, two_pass != 0);
+            int g = 0;
+            if (rowstream_plan(M, N, K, split_k, two_pass != 0, &g)) {
+                p.tile_n = 1;  // the streaming kernel: one row per step
+                p.grid = g;
+            } else {
+                p.tile_n = rowdot_rows_per_iter(M, nch_of(p.k_chunk));
+                p.grid = rowdot_grid(M, N, K, split_k, p.k_chunk, two_pass != 0);
+            }
             break;
         }
         case SG_KERNEL_SPLITK_MFMA: {

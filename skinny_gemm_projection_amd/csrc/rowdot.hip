@@ -187,6 +187,95 @@ __global__ __launch_bounds__(kWave * block_waves(S)) void rowdot_kernel(
     }
 }
 
+// x staging loads per thread of the streaming kernel (LDS slots: 256 times this).
+constexpr int rowstream_stage_loads(int M, int NCH) { return (M * NCH * kWave + kBlock - 1) / kBlock; }
+
+// Small-matrix path with one K chunk (S = 1) and x staged in LDS: a wave
+// takes ITERS rows, one per step, the grid's waves striding over N, with two
+// row buffers, so the next row's loads are in flight while the current row
+// is multiplied, reduced and stored.  Every step is unrolled: each wait is
+// for exactly the row it needs (behind a loop header the compiler would wait
+// for every load in flight).
+template <int M, int NCH, int ITERS>
+__global__ __launch_bounds__(kBlock) void rowstream_kernel(const uint4* __restrict__ x,
+                                                           const uint4* __restrict__ W, int N,
+                                                           int K8, Epilogue ep) {
+    constexpr int V = pad4(M);
+    constexpr int kStage = rowstream_stage_loads(M, NCH);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = blockIdx.x * kWavesPerBlock + wave_id_in_block();
+    const int waves = gridDim.x * kWavesPerBlock;
+    const uint32_t bytes = (uint32_t)K8 * 16u;
+    const int v = scatter_index<V>(lane);  // the output a lane stores after a row's reduction
+    // Residual values of the wave's outputs, requested first: read inside a
+    // step, each would wait for every row load in flight.  Buffer loads (no
+    // branch) keep the compiler from sinking them to their use.
+    // (converted at their use, so that nothing waits for them before then)
+    uint32_t rv[ITERS];  // 32-bit slots: packed 16-bit halves would serialize the loads
+    if (ep.r) {
+        const rsrc_t rr = make_rsrc(ep.r, (uint32_t)M * (uint32_t)N * 2u);
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+            const int n = wave + it * waves;
+            const bool mine = v >= 0 && v < M && n < N;
+            rv[it] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                rr, mine ? (uint32_t)(v * N + n) * 2u : 0xFFFFFFF0u, 0, kCached);
+        }
+    }
+    uint4 wr[2][NCH];
+    auto load_row = [&](int it, uint4 (&dst)[NCH]) {
+        const int n = wave + it * waves;
+        const rsrc_t rs = make_rsrc(W + (int64_t)min(n, N - 1) * K8, n < N ? bytes : 0u);
+        load_pieces<NCH, kStream, false>(dst, rs, NCH, lane);
+    };
+    // x: each thread stages its share; the first two rows are requested right
+    // behind it.  The LDS copy is unconditional (the buffer holds every staged
+    // slot) so that no x load moves into a branch behind the row loads.
+    extern __shared__ uint4 xs[];  // x [M, K8] pieces, then padding
+    const int pieces = M * K8;
+    const rsrc_t rx = make_rsrc(x, (uint32_t)pieces * 16u);
+    uint4 stage[kStage];
+#pragma unroll
+    for (int j = 0; j < kStage; ++j)
+        stage[j] = load16<kCached>(rx, (uint32_t)(threadIdx.x + j * kBlock) * 16u);
+    load_row(0, wr[0]);
+    if (ITERS > 1) load_row(1, wr[1]);
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) xs[threadIdx.x + j * kBlock] = stage[j];
+    __syncthreads();
+    uint4 xr[M][NCH];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int p = c * kWave + lane;
+            xr[m][c] = p < K8 ? xs[m * K8 + p] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int b = it & 1;
+        float acc[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float a = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) a = dot8(xr[m][c], wr[b][c], a);
+            acc[m] = a;
+        }
+        if (it + 2 < ITERS) load_row(it + 2, wr[b]);  // the buffer just consumed
+        const float sum = reduce_scatter<V>(acc, lane);
+        const int n = wave + it * waves;
+        if (v >= 0 && v < M && n < N) {
+            const float val = ep.r ? sum + __builtin_bit_cast(float, rv[it] << 16) : sum;
+            const int64_t i = (int64_t)v * N + n;
+            if (ep.y_f32) ep.y_f32[i] = val;
+            if (ep.y_bf16) ep.y_bf16[i] = f32_to_bf16(val);
+        }
+    }
+}
+
 int next_pow2(int v) {
     int p = 1;
     while (p < v) p <<= 1;
@@ -244,6 +333,29 @@ int rowdot_grid(int M, int N, int K, int S, int k_chunk, bool two_pass) {
     return (teams + teams_per_block - 1) / teams_per_block;
 }
 
+// Teams stage x in LDS while it fits in kStageMax (two 4-wave workgroups of
+// a CU then still fit in its 160 KB).
+constexpr size_t kStageMax = 64 * 1024;
+
+// Rows a wave of the streaming kernel takes: as many waves as the chip keeps
+// resident, each the same number of rows.
+static int rowstream_iters(int N) {
+    const int resident = rowdot_resident_waves(1, 0);
+    const int waves = N < resident ? N : resident;
+    return (N + waves - 1) / waves;
+}
+
+bool rowstream_plan(int M, int N, int K, int S, bool two_pass, int* grid) {
+    if (M < 1 || M > 2 || S != 1 || two_pass || K <= 0 || N < 1) return false;
+    const int nch = (K + kLaneSpan - 1) / kLaneSpan;
+    if (nch > 16 || (size_t)M * K * 2 > kStageMax) return false;
+    const int its = rowstream_iters(N);
+    if (its > kRowstreamMaxIters) return false;
+    const int waves = (N + its - 1) / its;
+    if (grid) *grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    return true;
+}
+
 template <int M, int NCH, int S, bool GUARD, bool XS = false>
 static hipError_t launch_mns(int N, int K, int splits, int k_chunk, int grid, bool two_pass,
                              const void* x, const void* W, const Epilogue& ep,
@@ -254,6 +366,22 @@ static hipError_t launch_mns(int N, int K, int splits, int k_chunk, int grid, bo
     const int groups = (N + R - 1) / R;
     const uint4* xp = static_cast<const uint4*>(x);
     const uint4* wp = static_cast<const uint4*>(W);
+    if constexpr (M <= 2 && S == 1 && XS && !GUARD) {
+        int g = 0;
+        if (rowstream_plan(M, N, K, splits, two_pass, &g)) {
+            const int its = rowstream_iters(N);
+            const size_t lds = (size_t)rowstream_stage_loads(M, NCH) * kBlock * 16;
+            switch (its) {
+#define SG_ITERS(i)                                                                         \
+    case i:                                                                                 \
+        rowstream_kernel<M, NCH, i><<<g, kBlock, lds, stream>>>(xp, wp, N, K8, ep);        \
+        return hipGetLastError();
+                SG_ITERS(1) SG_ITERS(2) SG_ITERS(3) SG_ITERS(4)
+#undef SG_ITERS
+                default: break;
+            }
+        }
+    }
     if (two_pass) {
         const int teams = (grid * kWavesPerBlock) / splits;
         const int iters = (groups + teams - 1) / teams;
@@ -276,9 +404,6 @@ constexpr bool team_split_compiled(int S) {
     return S == 1 || S == 2 || S == 4 || (S == 8 && M >= 5);
 }
 
-// Teams stage x in LDS while it fits in kStageMax (two 4-wave workgroups of
-// a CU then still fit in its 160 KB).
-constexpr size_t kStageMax = 64 * 1024;
 
 template <int M, int NCH, int S, bool GUARD>
 static hipError_t launch_team(int N, int K, int k_chunk, int grid, const void* x, const void* W,

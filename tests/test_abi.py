@@ -272,6 +272,22 @@ def test_grouped_and_prefetch_errors_return_before_launch():
 
 
 @no_gpu_only
+def test_read_probe_errors_return_before_launch():
+    c = _raw()
+    A = 0x10000
+    probe = c.skinny_gemm_read_probe
+    assert probe(A, -1, 14336, 2, 512, None) == 2          # negative rows
+    assert probe(A, 8, 8, 2, 512, None) == 2               # row shorter than one load
+    assert probe(A, 8, 16400, 2, 512, None) == 2           # over 16 KB a row
+    assert probe(A, 8, 14336, 3, 512, None) == 2           # 1 or 2 rows per iteration
+    assert probe(A, 8, 14336, 2, 0, None) == 2             # empty grid
+    assert probe(A, 8, 14344, 2, 512, None) == 4           # row_bytes % 16
+    assert probe(A + 8, 8, 14336, 2, 512, None) == 4       # misaligned
+    assert probe(None, 8, 14336, 2, 512, None) == 1
+    assert probe(None, 0, 14336, 2, 512, None) == 0        # nothing to read
+
+
+@no_gpu_only
 def test_fp8_size_limits_return_before_launch():
     # status 3 (unsupported) for sizes outside the kernel's x storage, 4 for K % 16;
     # a size inside the limits gets past those checks and stops at the missing

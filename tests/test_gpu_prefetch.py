@@ -77,3 +77,20 @@ def test_prefetch_on_side_stream_under_random_delays():
         torch.cuda.synchronize()
         for y, r in zip(outs, refs):
             assert torch.equal(y, r)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("rows,row_bytes,rows_per_iter,grid", [
+    (8192, 14336, 2, 512), (8192, 14336, 1, 512), (4097, 14336, 2, 512), (33, 16, 1, 1),
+    (1000, 1040, 2, 7), (300, 16384, 1, 3000), (1, 16000, 2, 2)])
+def test_read_probe_reads_only(rows, row_bytes, rows_per_iter, grid):
+    """The read probe launches once, returns SG_OK and writes nothing: the matrix it
+    reads is unchanged and the launch counters do not move."""
+    announce(f"read probe rows={rows} row_bytes={row_bytes} R={rows_per_iter} grid={grid}")
+    W = torch.randint(0, 256, (rows, row_bytes), dtype=torch.uint8, device=DEV)
+    before_w = W.clone()
+    before = sg.skinny_gemm_get_counters()
+    sg.skinny_gemm_read_probe(W, rows_per_iter, grid)
+    torch.cuda.synchronize()
+    assert torch.equal(W, before_w)
+    assert sg.skinny_gemm_get_counters() == before
