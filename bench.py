@@ -881,7 +881,7 @@ def read_traffic():
 COPY_BYTES = 1 << 30          # the calibration copy reads and writes this many bytes
 COPY_KERNEL_TAG = "MulFunctor"  # torch.mul(src, 1.0, out=dst): a plain element-wise copy
 COPY_GRID = COPY_BYTES // 16    # its launch: one thread per 4 floats
-GEMV_KERNEL_TAGS = ("rowdot_kernel<1, 14,", "rowdot_kernel<2, 14,")
+GEMV_KERNEL_TAGS = ("rowstream_kernel<1, 14, 4>", "rowstream_kernel<2, 14, 4>")
 
 
 def _pmc_dispatches(directory: str) -> list:
@@ -1281,7 +1281,7 @@ def main() -> None:
         "wall_ms_per_step": round(res["wall_ms_per_step"], 6),
         "roofline": {
             "bound": "hbm",
-            "kernel": "rowdot_kernel (small-matrix path, M=1 and M=2)",
+            "kernel": "rowstream_kernel (small-matrix path, M=1 and M=2)",
             "achieved": round(res["achieved"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
