@@ -715,6 +715,80 @@ def sweep(torch, sg, si, L, cyc, reps=40):
     return rows
 
 
+def side_stream_cu_mask(torch, sg, si, L, cyc, cus, Ts=(1, 4, 16), reps=5):
+    """The MoE step with the shared expert on a side stream restricted to the first `cus`
+    compute units (hipExtStreamCreateWithCUMask, default priority), against the
+    library's three placements on unmasked streams.  Median us over reps rounds."""
+    import statistics
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    dev = "cuda"
+    E, N, K, topk = 384, 2048, 7168, 8
+    W = si.normal_bf16((E, N, K), 0.02, si.seed_for(5, si.TAG_W), dev)
+    Wrs = torch.cat([si.normal_bf16((E, K), 0.02, si.seed_for(5, si.TAG_W) + 99, dev),
+                     si.normal_bf16((N, K), 0.02, si.seed_for(5, si.TAG_W) + 98, dev)])
+    ring_rs = ring_copies(torch, Wrs)
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+    cur = torch.cuda.current_stream()
+    fork.record(cur)  # torch creates the hipEvent_t at its first record
+    join.record(cur)
+    words = (ctypes.c_uint32 * 8)()
+    for b in range(cus):
+        words[b // 32] |= 1 << (b % 32)
+    side = ctypes.c_void_p()
+    st = hip.hipExtStreamCreateWithCUMask(ctypes.byref(side), 8, words)
+    if st != 0:
+        raise RuntimeError(f"hipExtStreamCreateWithCUMask: error {st}")
+    rows = []
+    try:
+        for T in Ts:
+            xs = [si.normal_bf16((T, K), 1.0, si.seed_for(5, si.TAG_X) + 100 * T + i, dev)
+                  for i in range(8)]
+            n_calls = max(len(ring_rs), len(xs))
+            combos = [(xs[i % len(xs)], ring_rs[i % len(ring_rs)][:E],
+                       ring_rs[i % len(ring_rs)][E:]) for i in range(n_calls)]
+            outs = (torch.empty((T, topk), dtype=torch.int32, device=dev),
+                    torch.empty((T, E + N), device=dev), torch.empty((T, topk, N), device=dev),
+                    torch.empty((T, N), device=dev))
+            ws = torch.empty(sg.skinny_moe_step_workspace(T, K, E, topk, N, N),
+                             dtype=torch.uint8, device=dev)
+            variants = {m: [L.moe_step(x, wr, W, wsh, topk, outs, ws, m) for x, wr, wsh in combos]
+                        for m in ("fused", "serial", "side_stream")}
+            steps = []
+            for x, wr, wsh in combos:
+                steps.append(sg.SgMoeStep(x.data_ptr(), wr.data_ptr(), W.data_ptr(), wsh.data_ptr(),
+                                          outs[1].data_ptr(), outs[0].data_ptr(), None,
+                                          outs[2].data_ptr(), outs[3].data_ptr(),
+                                          T, K, E, topk, N, N, 0))
+
+            def masked(step):
+                ref = ctypes.byref(step)
+
+                def go():
+                    st = L.c.skinny_moe_step(ref, ws.data_ptr(), ws.numel(), L.sp, side,
+                                             fork.cuda_event, join.cuda_event)
+                    if st:
+                        raise RuntimeError(sg.skinny_gemm_status_str(st))
+                return go
+            variants["side_stream_cu_masked"] = [masked(step) for step in steps]
+            times = {k: [] for k in variants}
+            for calls in variants.values():
+                calls[0]()
+            torch.cuda.synchronize()
+            for _ in range(reps):
+                for k, calls in variants.items():
+                    times[k].append(1e3 * timed_calls(torch, calls, n_calls, cyc))
+            rows.append({"T": T, "cus": cus,
+                         **{f"us_{k}": round(statistics.median(v), 2) for k, v in times.items()}})
+            log(json.dumps(rows[-1]))
+    finally:
+        torch.cuda.synchronize()
+        hip.hipStreamDestroy(side)
+    return rows
+
+
 # --------------------------------------------------------------------------- CPU baseline
 
 
@@ -1201,6 +1275,9 @@ def main() -> None:
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "COMMAND"))
     ap.add_argument("--profile-workloads", metavar="MANIFEST")
+    ap.add_argument("--side-stream-cu-mask", type=int, metavar="CUS",
+                    help="time the MoE step with the shared expert on a stream masked to the "
+                         "first CUS compute units, then exit")
     ap.add_argument("--summarize-workloads", nargs="+", metavar="MANIFEST_THEN_DIRS")
     args = ap.parse_args()
 
@@ -1231,6 +1308,13 @@ def main() -> None:
     cyc = sleep_cycles_per_ms(torch)
     if args.profile_workloads:
         profile_workloads(torch, sg, si, L, args.profile_workloads)
+        return
+    if args.side_stream_cu_mask:
+        if not 1 <= args.side_stream_cu_mask <= 256:
+            raise SystemExit("--side-stream-cu-mask: 1..256 compute units")
+        rows = side_stream_cu_mask(torch, sg, si, L, cyc, args.side_stream_cu_mask)
+        print(json.dumps({"experiment": "MoE step, shared expert on a CU-masked side stream",
+                          "rows": rows}), flush=True)
         return
     if args.copy_calibration:
         copy_calibration(torch)
