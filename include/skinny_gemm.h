@@ -114,7 +114,15 @@ typedef struct {
  * from a per-compute-unit byte cost model, overridable by a tuned table.  M > 64 returns
  * SG_ERR_UNSUPPORTED (prefill-sized batches fall back, [D]); M == 0 or
  * N == 0 gives kernel SG_KERNEL_NONE.  Host-only: touches no GPU state.
- * Limits: 0 <= N <= 1<<20, 0 <= K <= 1<<20 (else SG_ERR_SHAPE). */
+ * Limits: 0 <= N <= 1<<20, 0 <= K <= 1<<20 (else SG_ERR_SHAPE).
+ * The environment variable SKINNY_GEMM_TUNE_TABLE may name a text file of
+ * entries checked before the built-in tuned table, read once per process:
+ * one entry a line, "M_lo M_hi N K kernel split tile_n" (integers; 0 leaves
+ * that choice to the planner; kernel an sg_kernel value up to
+ * SG_KERNEL_SPLITK_MFMA; tile_n 0, 16, 128 or 256), '#' starts a comment.
+ * A line that does not parse rejects the whole file (one warning on
+ * stderr); an entry the planner cannot honour for a shape yields the
+ * default plan. */
 sg_status skinny_gemm_plan(int32_t M, int32_t N, int32_t K, sg_plan* out);
 
 /* Same, but with the kernel, split factor, reduction mode and (matrix cores)

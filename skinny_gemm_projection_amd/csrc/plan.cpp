@@ -17,8 +17,13 @@
 //                 per-compute-unit byte cost model, then the deterministic
 //                 reduction kernel.
 // A small table measured on MI355X overrides the split factor for known
-// shapes.  Everything here is host arithmetic; no GPU call is made.
+// shapes, and a text file named by SKINNY_GEMM_TUNE_TABLE can add entries
+// ahead of it.  Everything here is host arithmetic; no GPU call is made.
+#include <cstdio>
 #include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "launch.h"
 #include "plan_internal.h"
@@ -157,7 +162,82 @@ bool mfma_choose(int32_t M, int32_t N, int32_t K, int32_t force_split, int32_t f
     return false;
 }
 
+// Entries from the file SKINNY_GEMM_TUNE_TABLE names, read once per process.
+// One entry a line, seven integers: M_lo M_hi N K kernel split tile_n (0 for
+// "the planner's choice", as in kTuned; kernel is an sg_kernel value); text
+// after '#' is a comment.  A line that does not parse, or an entry out of
+// range, rejects the whole file: the built-in table alone applies and one
+// warning goes to stderr.
+std::vector<Tuned> g_user_tuned;
+std::once_flag g_user_tuned_once;
+
+bool parse_tuned_line(const char* line, Tuned* t, bool* empty) {
+    char buf[512];
+    std::strncpy(buf, line, sizeof buf - 1);
+    buf[sizeof buf - 1] = '\0';
+    if (char* hash = std::strchr(buf, '#')) *hash = '\0';
+    long v[7];
+    int n = 0;
+    char* p = buf;
+    while (n < 8) {
+        char* end = nullptr;
+        const long x = std::strtol(p, &end, 10);
+        if (end == p) break;
+        if (n < 7) v[n] = x;
+        ++n;
+        p = end;
+    }
+    for (; *p; ++p)
+        if (*p != ' ' && *p != '\t' && *p != '\r' && *p != '\n') return false;  // stray text
+    *empty = n == 0;
+    if (n == 0) return true;
+    if (n != 7) return false;
+    const bool ok = v[0] >= 1 && v[0] <= v[1] && v[1] <= SG_MAX_M && v[2] >= 1 &&
+                    v[2] <= kMaxNK && v[3] >= 0 && v[3] <= kMaxNK && v[4] >= 0 &&
+                    v[4] <= SG_KERNEL_SPLITK_MFMA && v[5] >= 0 && v[5] <= kMaxSplit &&
+                    (v[6] == 0 || v[6] == sg::kMfmaTeamTileN || v[6] == sg::kMfmaTileN ||
+                     v[6] == 2 * sg::kMfmaTileN);
+    if (!ok) return false;
+    *t = Tuned{(int32_t)v[0], (int32_t)v[1], (int32_t)v[2], (int32_t)v[3],
+               (int32_t)v[4], (int32_t)v[5], (int32_t)v[6]};
+    return true;
+}
+
+void load_user_tuned() {
+    const char* path = std::getenv("SKINNY_GEMM_TUNE_TABLE");
+    if (!path || !*path) return;
+    FILE* f = std::fopen(path, "r");
+    if (!f) {
+        std::fprintf(stderr, "[skinny_gemm] SKINNY_GEMM_TUNE_TABLE=%s: cannot open; ignored\n",
+                     path);
+        return;
+    }
+    std::vector<Tuned> rows;
+    char line[512];
+    int lineno = 0;
+    bool bad = false;
+    while (std::fgets(line, sizeof line, f)) {
+        ++lineno;
+        Tuned t{};
+        bool empty = false;
+        if (std::strlen(line) == sizeof line - 1 || !parse_tuned_line(line, &t, &empty)) {
+            std::fprintf(stderr, "[skinny_gemm] SKINNY_GEMM_TUNE_TABLE=%s line %d: expected "
+                                 "M_lo M_hi N K kernel split tile_n; file ignored\n",
+                         path, lineno);
+            bad = true;
+            break;
+        }
+        if (!empty) rows.push_back(t);
+    }
+    std::fclose(f);
+    if (!bad) g_user_tuned.swap(rows);
+}
+
+// The first matching entry: the user's file, then the built-in table.
 const Tuned* tuned_for(int32_t M, int32_t N, int32_t K) {
+    std::call_once(g_user_tuned_once, load_user_tuned);
+    for (const Tuned& t : g_user_tuned)
+        if (M >= t.m_lo && M <= t.m_hi && N == t.n && K == t.k) return &t;
     for (const Tuned& t : kTuned)
         if (M >= t.m_lo && M <= t.m_hi && N == t.n && K == t.k) return &t;
     return nullptr;
@@ -167,8 +247,28 @@ const Tuned* tuned_for(int32_t M, int32_t N, int32_t K) {
 
 namespace sg {
 
+namespace {
+
+sg_status make_plan_impl(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t split_k,
+                         int32_t two_pass, int32_t tile_n, bool use_tuned, sg_plan* out);
+
+}  // namespace
+
 sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t split_k,
                     int32_t two_pass, int32_t tile_n, sg_plan* out) {
+    const sg_status st = make_plan_impl(M, N, K, kernel, split_k, two_pass, tile_n, true, out);
+    // A tuned entry the planner cannot honour for this shape (a user table's
+    // split that leaves an empty chunk, say) gives way to the default plan.
+    if (st == SG_ERR_PLAN && kernel <= 0 && split_k <= 0 && tile_n <= 0 &&
+        tuned_for(M, N, K) != nullptr)
+        return make_plan_impl(M, N, K, kernel, split_k, two_pass, tile_n, false, out);
+    return st;
+}
+
+namespace {
+
+sg_status make_plan_impl(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t split_k,
+                         int32_t two_pass, int32_t tile_n, bool use_tuned, sg_plan* out) {
     if (!out) return SG_ERR_NULL;
     if (M < 0 || N < 0 || K < 0 || N > kMaxNK || K > kMaxNK) return SG_ERR_SHAPE;
     if (M > SG_MAX_M) return SG_ERR_UNSUPPORTED;
@@ -193,7 +293,7 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
         const int32_t mfma_from = team_fills ? kTeamFromM : kMfmaFromM;
         kernel = M <= 2 ? SG_KERNEL_GEMV
                         : (M < mfma_from ? SG_KERNEL_SPLITK_VALU : SG_KERNEL_SPLITK_MFMA);
-        if (const Tuned* t = tuned_for(M, N, K)) {
+        if (const Tuned* t = use_tuned ? tuned_for(M, N, K) : nullptr) {
             if (t->kernel > 0) kernel = t->kernel;
             if (split_k <= 0 && t->split > 0) split_k = t->split;
             if (tile_n <= 0 && t->tile_n > 0) tile_n = t->tile_n;
@@ -285,6 +385,8 @@ sg_status make_plan(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_t spl
     *out = p;
     return SG_OK;
 }
+
+}  // namespace
 
 bool plan_matches(const sg_plan* p) {
     // The matrix-core path has two kernels; the plan's tile width says which

@@ -6,9 +6,11 @@ Calls with made-up device pointers only run on a host without a GPU: there
 any accidental launch fails harmlessly instead of reading a stray address.
 """
 import ctypes
+import json
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 import torch
@@ -357,3 +359,73 @@ def test_mxfp4_size_limits_return_before_launch():
     assert call(9, 1 << 20) == 1
     assert call(1, 48) == 4
     assert sum(sg.skinny_gemm_get_counters()) == 0
+
+
+# plans from the C ABI in a fresh interpreter; _lib.py is loaded by path (no torch import)
+_TUNE_PROBE = r"""
+import ctypes, importlib.util, json, os, sys
+spec = importlib.util.spec_from_file_location(
+    "sg_lib", os.path.join(sys.argv[1], "skinny_gemm_projection_amd", "_lib.py"))
+lib = importlib.util.module_from_spec(spec)
+spec.loader.exec_module(lib)
+c = lib.load()
+out = []
+for M, N, K in ((4, 4096, 7168), (20, 4096, 7168), (4, 2048, 7168), (5, 4096, 7168)):
+    p = lib.SgPlan()
+    assert c.skinny_gemm_plan(M, N, K, ctypes.byref(p)) == 0
+    out.append([p.kernel, p.split_k, p.tile_n, p.two_pass])
+print(json.dumps(out))
+"""
+
+
+def _plans_with_table(tmp_path, text):
+    env = dict(os.environ)
+    if text is None:
+        env.pop("SKINNY_GEMM_TUNE_TABLE", None)
+    else:
+        f = tmp_path / "tune.txt"
+        f.write_text(text)
+        env["SKINNY_GEMM_TUNE_TABLE"] = str(f)
+    r = subprocess.run([sys.executable, "-c", _TUNE_PROBE, ROOT], env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    return json.loads(r.stdout.strip().splitlines()[-1]), r.stderr
+
+
+def test_tune_table_file_overrides_the_built_in_choices(tmp_path):
+    # the table is read once per process, so each case runs in a fresh interpreter
+    default, err = _plans_with_table(tmp_path, None)
+    assert err == ""
+    tuned, err = _plans_with_table(tmp_path, """# M_lo M_hi N K kernel split tile_n
+4 4 4096 7168 2 4 0      # VALU split-K, 4 chunks
+20 20 4096 7168 3 16 256 # chunk kernel, 16 splits, 256-row tiles
+
+4 4 2048 7168 1 0 0      # the small-matrix kernel cannot take 4 rows: default plan
+""")
+    assert err == ""
+    assert tuned[0] == [sg.SG_KERNEL_SPLITK_VALU, 4, 2, 0] != default[0]
+    assert tuned[1] == [sg.SG_KERNEL_SPLITK_MFMA, 16, 256, 1] != default[1]
+    assert tuned[2] == default[2] and tuned[3] == default[3]
+
+
+@pytest.mark.parametrize("text", ["4 4 4096 7168 2 4\n",            # six fields
+                                  "4 4 4096 7168 2 4 0 9\n",        # eight
+                                  "4 4 4096 7168 2 4 0 x\n",        # stray text
+                                  "0 4 4096 7168 2 4 0\n",          # M_lo < 1
+                                  "4 65 4096 7168 2 4 0\n",         # M_hi > 64
+                                  "4 4 4096 7168 9 4 0\n",          # no such kernel
+                                  "4 4 4096 7168 2 4 64\n"])        # no such tile width
+def test_tune_table_rejects_a_malformed_file(tmp_path, text):
+    default, _ = _plans_with_table(tmp_path, None)
+    plans, err = _plans_with_table(tmp_path, "20 20 4096 7168 3 16 256\n" + text)
+    assert "SKINNY_GEMM_TUNE_TABLE" in err and "file ignored" in err
+    assert plans == default   # the good first line is dropped with the rest
+
+
+def test_tune_table_missing_file_is_ignored(tmp_path):
+    default, _ = _plans_with_table(tmp_path, None)
+    env = dict(os.environ, SKINNY_GEMM_TUNE_TABLE=str(tmp_path / "absent.txt"))
+    r = subprocess.run([sys.executable, "-c", _TUNE_PROBE, ROOT], env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0 and "cannot open" in r.stderr
+    assert json.loads(r.stdout.strip().splitlines()[-1]) == default
