@@ -400,7 +400,48 @@ def graph_us(torch, sg, make_calls, out, per_graph=200, replays=5):
     return round(times[len(times) // 2], 3)
 
 
-def sweep(torch, sg, si, L, cyc, reps=40):
+class SweepJournal:
+    """The sweep's rows as JSON lines: every finished section appends its rows and then a
+    {"section_done": name} line, so a killed sweep run again with the same file skips the
+    sections already there (their rows are reused) and measures the rest."""
+
+    def __init__(self, path):
+        self.path = path
+        self.done = {}
+        pending = []
+        if os.path.exists(path):
+            with open(path) as f:
+                for line in f:
+                    line = line.strip()
+                    if not line:
+                        continue
+                    try:
+                        obj = json.loads(line)
+                    except json.JSONDecodeError:
+                        break  # a line cut short by the kill: the rest is measured again
+                    if "section_done" in obj:
+                        self.done[obj["section_done"]] = pending
+                        pending = []
+                    else:
+                        pending.append(obj)
+            # rewrite the file with the complete sections only
+            with open(path, "w") as f:
+                for name, rows in self.done.items():
+                    for r in rows:
+                        f.write(json.dumps(r) + "\n")
+                    f.write(json.dumps({"section_done": name}) + "\n")
+
+    def write(self, name, rows):
+        with open(self.path, "a") as f:
+            for r in rows:
+                f.write(json.dumps(r) + "\n")
+            f.write(json.dumps({"section_done": name}) + "\n")
+            f.flush()
+            os.fsync(f.fileno())
+        self.done[name] = list(rows)
+
+
+def sweep(torch, sg, si, L, cyc, reps=40, journal=None):
     dev = "cuda"
     rows = []
 
@@ -413,305 +454,343 @@ def sweep(torch, sg, si, L, cyc, reps=40):
     def plan_desc(p):
         return f"{sg.KERNEL_NAMES[p.kernel]} S={p.split_k}"
 
-    # single decode projection M=1, K=N=1024 (launch-bound)
-    N = K = 1024
-    x = si.normal_bf16((1, K), 0.02, si.seed_for(1, si.TAG_X), dev)
-    ring = ring_copies(torch, si.normal_bf16((N, K), 0.02, si.seed_for(1, si.TAG_W), dev))
-    p = sg.skinny_gemm_plan(1, N, K)
-    y = torch.empty((1, N), device=dev)
-    per = timed_calls(torch, [L.projection(p, x, w, y, None) for w in ring], 512, cyc)
-    record("single 1024x1024", 1, N, K, plan_desc(p), per, proj_bytes(1, N, K, bf16=False))
-    del ring
+    def run_section(name, fn):
+        # with --jsonl, a section already in the file is taken from it (a killed sweep
+        # resumes there); a measured one is appended to it as soon as it is done
+        if journal is not None and name in journal.done:
+            rows.extend(journal.done[name])
+            log(f"sweep: section '{name}' taken from {journal.path}")
+            return
+        start = len(rows)
+        fn()
+        if journal is not None:
+            journal.write(name, rows[start:])
 
-    # small batch M in {1,2}, K=7168, N=8192, fp32 + bf16 out
-    N, K = 8192, 7168
-    ring = ring_copies(torch, si.normal_bf16((N, K), 0.02, si.seed_for(2, si.TAG_W), dev))
-    for M in (1, 2):
-        x = si.normal_bf16((M, K), 1.0, si.seed_for(2, si.TAG_X) + M, dev)
-        p = sg.skinny_gemm_plan(M, N, K)
-        y32, y16 = torch.empty((M, N), device=dev), torch.empty((M, N), device=dev, dtype=torch.bfloat16)
-        per = timed_calls(torch, [L.projection(p, x, w, y32, y16) for w in ring], reps, cyc)
-        record("small-batch 8192x7168", M, N, K, plan_desc(p), per, proj_bytes(M, N, K))
-    # the same matrix at larger decode batches (the planner's kernel at each M)
-    for M in (4, 8, 16, 64):
-        x = si.normal_bf16((M, K), 1.0, si.seed_for(2, si.TAG_X) + M, dev)
-        p = sg.skinny_gemm_plan(M, N, K)
-        y32, y16 = torch.empty((M, N), device=dev), torch.empty((M, N), device=dev, dtype=torch.bfloat16)
-        ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
-        per = timed_calls(torch, [L.projection(p, x, w, y32, y16, ws) for w in ring], reps, cyc)
-        record("8192x7168, larger batch", M, N, K, plan_desc(p), per, proj_bytes(M, N, K))
+    def section_0():
+        # single decode projection M=1, K=N=1024 (launch-bound)
+        N = K = 1024
+        x = si.normal_bf16((1, K), 0.02, si.seed_for(1, si.TAG_X), dev)
+        ring = ring_copies(torch, si.normal_bf16((N, K), 0.02, si.seed_for(1, si.TAG_W), dev))
+        p = sg.skinny_gemm_plan(1, N, K)
+        y = torch.empty((1, N), device=dev)
+        per = timed_calls(torch, [L.projection(p, x, w, y, None) for w in ring], 512, cyc)
+        record("single 1024x1024", 1, N, K, plan_desc(p), per, proj_bytes(1, N, K, bf16=False))
+        del ring
 
-    # side-stream weight prefetch on the same ring: the read of one 117 MB matrix alone, and
-    # what it buys the projection after it -- prefetch then project the same matrix (its
-    # weights now in the Infinity Cache) against prefetch one matrix and project another
-    # that was last read two pairs earlier (cold).  Both pair streams run the same kernels;
-    # their difference is the cold-minus-warm projection time.
-    nbytes = N * K * 2
-    sp = L.sp
+    run_section("single 1024x1024", section_0)
 
-    def pf(w):
-        def go():
-            st = L.c.skinny_gemm_prefetch(w.data_ptr(), nbytes, sp)
-            if st:
-                raise RuntimeError(sg.skinny_gemm_status_str(st))
-        return go
-    x = si.normal_bf16((1, K), 1.0, si.seed_for(2, si.TAG_X) + 1, dev)
-    p = sg.skinny_gemm_plan(1, N, K)
-    y32, y16 = torch.empty((1, N), device=dev), torch.empty((1, N), device=dev, dtype=torch.bfloat16)
-    proj = [L.projection(p, x, w, y32, y16) for w in ring]
-    n = len(ring)
-    alone = timed_calls(torch, [pf(w) for w in ring], reps, cyc)
-    same = timed_calls(torch, [c for i in range(n) for c in (pf(ring[i]), proj[i])], 2 * reps, cyc)
-    other = timed_calls(torch, [c for i in range(n) for c in (pf(ring[(i + 2) % n]), proj[i])],
-                        2 * reps, cyc)
-    us = 1e3 * alone
-    rows.append({"workload": "prefetch 8192x7168 (one 117 MB matrix)", "M": 1, "N": N, "K": K,
-                 "plan": "prefetch", "us": round(us, 3),
-                 "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
-                 "pct_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
-                 "projection_after_prefetch_us": round(2e3 * same - us, 3),
-                 "projection_cold_us": round(2e3 * other - us, 3)})
-    del ring
-
-    # split-K sweep M in {4..64}, K=7168, N=4096, fp32 out
-    N, K = 4096, 7168
-    ring = ring_copies(torch, si.normal_bf16((N, K), 0.02, si.seed_for(3, si.TAG_W), dev))
-    # first, this matrix read with no arithmetic (the read probe on the M = 1 plan's shape)
-    p1 = sg.skinny_gemm_plan(1, N, K)
-    per = timed_calls(torch, [L.read_probe(w, p1.tile_n, p1.grid) for w in ring], reps, cyc)
-    record("read probe 4096x7168 (weights only)", 0, N, K,
-           f"read_probe rows_per_iter={p1.tile_n} grid={p1.grid}", per, N * K * 2)
-    for M in (3, 4, 8, 12, 16, 32, 48, 64):
-        x = si.normal_bf16((M, K), 1.0, si.seed_for(3, si.TAG_X) + M, dev)
-        p = sg.skinny_gemm_plan(M, N, K)
-        y32 = torch.empty((M, N), device=dev)
-        ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
-        per = timed_calls(torch, [L.projection(p, x, w, y32, None, ws) for w in ring], reps, cyc)
-        record("split-K 4096x7168", M, N, K, plan_desc(p), per, proj_bytes(M, N, K, bf16=False))
-        if M in (4, 16, 32, 64):  # also as 200 calls in one HIP graph (one or two launches each)
-            rows[-1]["us_graph"] = graph_us(
-                torch, sg, lambda L2, p=p, x=x, y32=y32, ws=ws:
-                [L2.projection(p, x, w, y32, None, ws) for w in ring], y32)
-    # the same shapes at each split factor the workload names, S in {2, 4, 8, 16} (vector ALU
-    # below 8 rows, matrix cores from 8; the library picks the reduction and the row tiling)
-    for M in (4, 8, 16, 32, 64):
-        x = si.normal_bf16((M, K), 1.0, si.seed_for(3, si.TAG_X) + M, dev)
-        y32 = torch.empty((M, N), device=dev)
-        kernel = sg.SG_KERNEL_SPLITK_VALU if M < 8 else sg.SG_KERNEL_SPLITK_MFMA
-        for S in (2, 4, 8, 16):
-            try:
-                p = sg.skinny_gemm_plan_force(M, N, K, kernel, S)
-            except sg.SkinnyGemmError:
-                continue
+    def section_1():
+        # small batch M in {1,2}, K=7168, N=8192, fp32 + bf16 out
+        N, K = 8192, 7168
+        ring = ring_copies(torch, si.normal_bf16((N, K), 0.02, si.seed_for(2, si.TAG_W), dev))
+        for M in (1, 2):
+            x = si.normal_bf16((M, K), 1.0, si.seed_for(2, si.TAG_X) + M, dev)
+            p = sg.skinny_gemm_plan(M, N, K)
+            y32, y16 = torch.empty((M, N), device=dev), torch.empty((M, N), device=dev, dtype=torch.bfloat16)
+            per = timed_calls(torch, [L.projection(p, x, w, y32, y16) for w in ring], reps, cyc)
+            record("small-batch 8192x7168", M, N, K, plan_desc(p), per, proj_bytes(M, N, K))
+        # the same matrix at larger decode batches (the planner's kernel at each M)
+        for M in (4, 8, 16, 64):
+            x = si.normal_bf16((M, K), 1.0, si.seed_for(2, si.TAG_X) + M, dev)
+            p = sg.skinny_gemm_plan(M, N, K)
+            y32, y16 = torch.empty((M, N), device=dev), torch.empty((M, N), device=dev, dtype=torch.bfloat16)
             ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
-            per = timed_calls(torch, [L.projection(p, x, w, y32, None, ws) for w in ring], reps,
-                              cyc)
-            record("split-K 4096x7168, forced split", M, N, K,
-                   f"{plan_desc(p)} tile={p.tile_n} two_pass={p.two_pass}", per,
-                   proj_bytes(M, N, K, bf16=False))
-    del ring
+            per = timed_calls(torch, [L.projection(p, x, w, y32, y16, ws) for w in ring], reps, cyc)
+            record("8192x7168, larger batch", M, N, K, plan_desc(p), per, proj_bytes(M, N, K))
 
-    # fused output projection + residual, K=8192, N=7168, bf16 out
-    N, K = 7168, 8192
-    ring = ring_copies(torch, si.normal_bf16((N, K), 0.02, si.seed_for(4, si.TAG_W), dev))
-    for M in (1, 8, 64):
-        x = si.normal_bf16((M, K), 1.0, si.seed_for(4, si.TAG_X) + M, dev)
-        r = si.normal_bf16((M, N), 1.0, si.seed_for(4, si.TAG_R) + M, dev)
-        p = sg.skinny_gemm_plan(M, N, K)
-        o16 = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
-        ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
-        per = timed_calls(torch, [L.residual(p, x, w, r, o16, None, ws) for w in ring], reps, cyc)
-        record("residual 7168x8192", M, N, K, plan_desc(p), per,
-               proj_bytes(M, N, K, f32=False, residual=True))
-        rows[-1]["us_graph"] = graph_us(
-            torch, sg, lambda L2, p=p, x=x, r=r, o16=o16, ws=ws:
-            [L2.residual(p, x, w, r, o16, None, ws) for w in ring], o16)
-    del ring
-    torch.cuda.empty_cache()
+        # side-stream weight prefetch on the same ring: the read of one 117 MB matrix alone, and
+        # what it buys the projection after it -- prefetch then project the same matrix (its
+        # weights now in the Infinity Cache) against prefetch one matrix and project another
+        # that was last read two pairs earlier (cold).  Both pair streams run the same kernels;
+        # their difference is the cold-minus-warm projection time.
+        nbytes = N * K * 2
+        sp = L.sp
 
-    # MXFP4 weights (e2m1 codes + e8m0 block scales): the same shapes at a quarter of the
-    # weight bytes; a ring of code/scale copies larger than 2 x MALL per shape
-    c = L.c
-    for label, Ms, N, K, residual in (("mxfp4 8192x7168", (1, 2, 16, 64), 8192, 7168, False),
-                                      ("mxfp4 4096x7168", (4, 8, 16, 32, 64), 4096, 7168, False),
-                                      ("mxfp4 residual 7168x8192", (1, 8, 64), 7168, 8192, True)):
-        codes, scales = si.mxfp4_weights(N, K, si.seed_for(6, si.TAG_W) + N, dev)
-        per_copy = codes.numel() + scales.numel()
-        copies = max(1, math.ceil(RING_MIN_BYTES / per_copy))
-        ring = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(copies - 1)]
-        for M in Ms:
-            x = si.normal_bf16((M, K), 1.0, si.seed_for(6, si.TAG_X) + M, dev)
-            r = si.normal_bf16((M, N), 1.0, si.seed_for(6, si.TAG_R) + M, dev) if residual else None
-            y32 = None if residual else torch.empty((M, N), device=dev)
-            y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-
-            wsb = sg.skinny_gemm_mxfp4_workspace(M, N, K)
-            ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-
-            def mx(cw, sw, x=x, r=r, y32=y32, y16=y16, M=M, N=N, K=K, ws=ws, wsb=wsb):
-                args = (M, N, K, x.data_ptr(), cw.data_ptr(), sw.data_ptr(),
-                        r.data_ptr() if r is not None else None,
-                        y32.data_ptr() if y32 is not None else None, y16.data_ptr(),
-                        ws.data_ptr(), wsb, L.sp)
-
-                def go():
-                    st = c.skinny_gemm_mxfp4(*args)
-                    if st:
-                        raise RuntimeError(sg.skinny_gemm_status_str(st))
-                return go
-            per = timed_calls(torch, [mx(cw, sw) for cw, sw in ring], reps, cyc)
-            nbytes = N * K // 2 + N * K // 32 + M * K * 2 + M * N * 2 * (2 if residual else 1) + \
-                (0 if residual else M * N * 4)
-            us = 1e3 * per
-            gbs = nbytes / (per * 1e-3) / 1e9
-            rows.append({"workload": label, "M": M, "N": N, "K": K,
-                         "plan": lowp_plan_label("mxfp4", M, N, wsb),
-                         "us": round(us, 3), "GBps": round(gbs, 1),
-                         "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
-        del ring
-    torch.cuda.empty_cache()
-
-    # FP8 e4m3 weights with 128 x 128 fp32 block scales: half the bf16 weight bytes; a ring
-    # of code/scale copies larger than 2 x MALL per shape
-    for label, Ms, N, K, residual in (("fp8 8192x7168", (1, 2, 16, 64), 8192, 7168, False),
-                                      ("fp8 4096x7168", (4, 8, 16, 32, 64), 4096, 7168, False),
-                                      ("fp8 residual 7168x8192", (1, 64), 7168, 8192, True)):
-        codes, scales = si.fp8_weights(N, K, si.seed_for(7, si.TAG_W) + N, dev)
-        per_copy = codes.numel() + scales.numel() * 4
-        copies = max(1, math.ceil(RING_MIN_BYTES / per_copy))
-        ring = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(copies - 1)]
-        for M in Ms:
-            x = si.normal_bf16((M, K), 1.0, si.seed_for(7, si.TAG_X) + M, dev)
-            r = si.normal_bf16((M, N), 1.0, si.seed_for(7, si.TAG_R) + M, dev) if residual else None
-            y32 = None if residual else torch.empty((M, N), device=dev)
-            y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-
-            wsb = sg.skinny_gemm_fp8_workspace(M, N, K)
-            ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-
-            def f8(cw, sw, x=x, r=r, y32=y32, y16=y16, M=M, N=N, K=K, ws=ws, wsb=wsb):
-                args = (M, N, K, x.data_ptr(), cw.data_ptr(), sw.data_ptr(),
-                        r.data_ptr() if r is not None else None,
-                        y32.data_ptr() if y32 is not None else None, y16.data_ptr(),
-                        ws.data_ptr(), wsb, L.sp)
-
-                def go():
-                    st = c.skinny_gemm_fp8(*args)
-                    if st:
-                        raise RuntimeError(sg.skinny_gemm_status_str(st))
-                return go
-            per = timed_calls(torch, [f8(cw, sw) for cw, sw in ring], reps, cyc)
-            nbytes = N * K + scales.numel() * 4 + M * K * 2 + M * N * 2 * (2 if residual else 1) + \
-                (0 if residual else M * N * 4)
-            us = 1e3 * per
-            gbs = nbytes / (per * 1e-3) / 1e9
-            rows.append({"workload": label, "M": M, "N": N, "K": K,
-                         "plan": lowp_plan_label("fp8", M, N, wsb),
-                         "us": round(us, 3), "GBps": round(gbs, 1),
-                         "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
-        del ring
-    torch.cuda.empty_cache()
-
-    # router: scores y = x W_r^T (E=384 experts, K=7168, fp32) and their top-8 per token
-    E, K, k = 384, 7168, 8
-    Wr = si.normal_bf16((E, K), 0.02, si.seed_for(5, si.TAG_W) + 99, dev)
-    ring = ring_copies(torch, Wr)
-    c = L.c
-    for T in (1, 16, 64):
-        x = si.normal_bf16((T, K), 1.0, si.seed_for(5, si.TAG_X) + T, dev)
-        p = sg.skinny_gemm_plan(T, E, K)
-        scores = torch.empty((T, E), device=dev)
-        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-        ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
-
-        def router(proj, scores=scores, ids=ids, T=T):
+        def pf(w):
             def go():
-                proj()
-                st = c.skinny_gemm_router_topk(scores.data_ptr(), T, E, k, ids.data_ptr(), None,
-                                               L.sp)
+                st = L.c.skinny_gemm_prefetch(w.data_ptr(), nbytes, sp)
                 if st:
                     raise RuntimeError(sg.skinny_gemm_status_str(st))
             return go
-        per = timed_calls(torch, [router(L.projection(p, x, w, scores, None, ws)) for w in ring],
-                          reps, cyc)
-        nbytes = proj_bytes(T, E, K, bf16=False) + T * E * 4 + T * k * 4
-        rows.append({"workload": "router top-8 E=384 K=7168", "M": T, "N": E, "K": K,
-                     "plan": f"{plan_desc(p)}+router_topk", "us": round(1e3 * per, 3),
-                     "GBps": round(nbytes / (per * 1e-3) / 1e9, 1),
-                     "pct_peak": round(100.0 * nbytes / (per * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)})
-    del ring, Wr
+        x = si.normal_bf16((1, K), 1.0, si.seed_for(2, si.TAG_X) + 1, dev)
+        p = sg.skinny_gemm_plan(1, N, K)
+        y32, y16 = torch.empty((1, N), device=dev), torch.empty((1, N), device=dev, dtype=torch.bfloat16)
+        proj = [L.projection(p, x, w, y32, y16) for w in ring]
+        n = len(ring)
+        alone = timed_calls(torch, [pf(w) for w in ring], reps, cyc)
+        same = timed_calls(torch, [c for i in range(n) for c in (pf(ring[i]), proj[i])], 2 * reps, cyc)
+        other = timed_calls(torch, [c for i in range(n) for c in (pf(ring[(i + 2) % n]), proj[i])],
+                            2 * reps, cyc)
+        us = 1e3 * alone
+        rows.append({"workload": "prefetch 8192x7168 (one 117 MB matrix)", "M": 1, "N": N, "K": K,
+                     "plan": "prefetch", "us": round(us, 3),
+                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "pct_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+                     "projection_after_prefetch_us": round(2e3 * same - us, 3),
+                     "projection_cold_us": round(2e3 * other - us, 3)})
+        del ring
 
-    # MoE grouped: E=384 experts of N=2048 x K=7168, 8 distinct experts per token,
-    # a ring of 8 routing tables per batch size
-    E, N, K, topk = 384, 2048, 7168, 8
-    W = si.normal_bf16((E, N, K), 0.02, si.seed_for(5, si.TAG_W) + 100, dev)
-    for T in (1, 16, 64):
-        x = si.normal_bf16((T, K), 1.0, si.seed_for(5, si.TAG_X) + T, dev)
-        tables = [si.routing_table(T, E, topk, si.seed_for(5, si.TAG_ROUTING) + 10 * i + 1000 * T)
+    run_section("8192x7168", section_1)
+
+    def section_2():
+        # split-K sweep M in {4..64}, K=7168, N=4096, fp32 out
+        N, K = 4096, 7168
+        ring = ring_copies(torch, si.normal_bf16((N, K), 0.02, si.seed_for(3, si.TAG_W), dev))
+        # first, this matrix read with no arithmetic (the read probe on the M = 1 plan's shape)
+        p1 = sg.skinny_gemm_plan(1, N, K)
+        per = timed_calls(torch, [L.read_probe(w, p1.tile_n, p1.grid) for w in ring], reps, cyc)
+        record("read probe 4096x7168 (weights only)", 0, N, K,
+               f"read_probe rows_per_iter={p1.tile_n} grid={p1.grid}", per, N * K * 2)
+        for M in (3, 4, 8, 12, 16, 32, 48, 64):
+            x = si.normal_bf16((M, K), 1.0, si.seed_for(3, si.TAG_X) + M, dev)
+            p = sg.skinny_gemm_plan(M, N, K)
+            y32 = torch.empty((M, N), device=dev)
+            ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+            per = timed_calls(torch, [L.projection(p, x, w, y32, None, ws) for w in ring], reps, cyc)
+            record("split-K 4096x7168", M, N, K, plan_desc(p), per, proj_bytes(M, N, K, bf16=False))
+            if M in (4, 16, 32, 64):  # also as 200 calls in one HIP graph (one or two launches each)
+                rows[-1]["us_graph"] = graph_us(
+                    torch, sg, lambda L2, p=p, x=x, y32=y32, ws=ws:
+                    [L2.projection(p, x, w, y32, None, ws) for w in ring], y32)
+        # the same shapes at each split factor the workload names, S in {2, 4, 8, 16} (vector ALU
+        # below 8 rows, matrix cores from 8; the library picks the reduction and the row tiling)
+        for M in (4, 8, 16, 32, 64):
+            x = si.normal_bf16((M, K), 1.0, si.seed_for(3, si.TAG_X) + M, dev)
+            y32 = torch.empty((M, N), device=dev)
+            kernel = sg.SG_KERNEL_SPLITK_VALU if M < 8 else sg.SG_KERNEL_SPLITK_MFMA
+            for S in (2, 4, 8, 16):
+                try:
+                    p = sg.skinny_gemm_plan_force(M, N, K, kernel, S)
+                except sg.SkinnyGemmError:
+                    continue
+                ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+                per = timed_calls(torch, [L.projection(p, x, w, y32, None, ws) for w in ring], reps,
+                                  cyc)
+                record("split-K 4096x7168, forced split", M, N, K,
+                       f"{plan_desc(p)} tile={p.tile_n} two_pass={p.two_pass}", per,
+                       proj_bytes(M, N, K, bf16=False))
+        del ring
+
+    run_section("split-K 4096x7168", section_2)
+
+    def section_3():
+        # fused output projection + residual, K=8192, N=7168, bf16 out
+        N, K = 7168, 8192
+        ring = ring_copies(torch, si.normal_bf16((N, K), 0.02, si.seed_for(4, si.TAG_W), dev))
+        for M in (1, 8, 64):
+            x = si.normal_bf16((M, K), 1.0, si.seed_for(4, si.TAG_X) + M, dev)
+            r = si.normal_bf16((M, N), 1.0, si.seed_for(4, si.TAG_R) + M, dev)
+            p = sg.skinny_gemm_plan(M, N, K)
+            o16 = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
+            ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+            per = timed_calls(torch, [L.residual(p, x, w, r, o16, None, ws) for w in ring], reps, cyc)
+            record("residual 7168x8192", M, N, K, plan_desc(p), per,
+                   proj_bytes(M, N, K, f32=False, residual=True))
+            rows[-1]["us_graph"] = graph_us(
+                torch, sg, lambda L2, p=p, x=x, r=r, o16=o16, ws=ws:
+                [L2.residual(p, x, w, r, o16, None, ws) for w in ring], o16)
+        del ring
+        torch.cuda.empty_cache()
+
+    run_section("residual 7168x8192", section_3)
+
+    def section_4():
+        # MXFP4 weights (e2m1 codes + e8m0 block scales): the same shapes at a quarter of the
+        # weight bytes; a ring of code/scale copies larger than 2 x MALL per shape
+        c = L.c
+        for label, Ms, N, K, residual in (("mxfp4 8192x7168", (1, 2, 16, 64), 8192, 7168, False),
+                                          ("mxfp4 4096x7168", (4, 8, 16, 32, 64), 4096, 7168, False),
+                                          ("mxfp4 residual 7168x8192", (1, 8, 64), 7168, 8192, True)):
+            codes, scales = si.mxfp4_weights(N, K, si.seed_for(6, si.TAG_W) + N, dev)
+            per_copy = codes.numel() + scales.numel()
+            copies = max(1, math.ceil(RING_MIN_BYTES / per_copy))
+            ring = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(copies - 1)]
+            for M in Ms:
+                x = si.normal_bf16((M, K), 1.0, si.seed_for(6, si.TAG_X) + M, dev)
+                r = si.normal_bf16((M, N), 1.0, si.seed_for(6, si.TAG_R) + M, dev) if residual else None
+                y32 = None if residual else torch.empty((M, N), device=dev)
+                y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+                wsb = sg.skinny_gemm_mxfp4_workspace(M, N, K)
+                ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+
+                def mx(cw, sw, x=x, r=r, y32=y32, y16=y16, M=M, N=N, K=K, ws=ws, wsb=wsb):
+                    args = (M, N, K, x.data_ptr(), cw.data_ptr(), sw.data_ptr(),
+                            r.data_ptr() if r is not None else None,
+                            y32.data_ptr() if y32 is not None else None, y16.data_ptr(),
+                            ws.data_ptr(), wsb, L.sp)
+
+                    def go():
+                        st = c.skinny_gemm_mxfp4(*args)
+                        if st:
+                            raise RuntimeError(sg.skinny_gemm_status_str(st))
+                    return go
+                per = timed_calls(torch, [mx(cw, sw) for cw, sw in ring], reps, cyc)
+                nbytes = N * K // 2 + N * K // 32 + M * K * 2 + M * N * 2 * (2 if residual else 1) + \
+                    (0 if residual else M * N * 4)
+                us = 1e3 * per
+                gbs = nbytes / (per * 1e-3) / 1e9
+                rows.append({"workload": label, "M": M, "N": N, "K": K,
+                             "plan": lowp_plan_label("mxfp4", M, N, wsb),
+                             "us": round(us, 3), "GBps": round(gbs, 1),
+                             "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
+            del ring
+        torch.cuda.empty_cache()
+
+    run_section("mxfp4", section_4)
+
+    def section_5():
+        c = L.c
+        # FP8 e4m3 weights with 128 x 128 fp32 block scales: half the bf16 weight bytes; a ring
+        # of code/scale copies larger than 2 x MALL per shape
+        for label, Ms, N, K, residual in (("fp8 8192x7168", (1, 2, 16, 64), 8192, 7168, False),
+                                          ("fp8 4096x7168", (4, 8, 16, 32, 64), 4096, 7168, False),
+                                          ("fp8 residual 7168x8192", (1, 64), 7168, 8192, True)):
+            codes, scales = si.fp8_weights(N, K, si.seed_for(7, si.TAG_W) + N, dev)
+            per_copy = codes.numel() + scales.numel() * 4
+            copies = max(1, math.ceil(RING_MIN_BYTES / per_copy))
+            ring = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(copies - 1)]
+            for M in Ms:
+                x = si.normal_bf16((M, K), 1.0, si.seed_for(7, si.TAG_X) + M, dev)
+                r = si.normal_bf16((M, N), 1.0, si.seed_for(7, si.TAG_R) + M, dev) if residual else None
+                y32 = None if residual else torch.empty((M, N), device=dev)
+                y16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+                wsb = sg.skinny_gemm_fp8_workspace(M, N, K)
+                ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+
+                def f8(cw, sw, x=x, r=r, y32=y32, y16=y16, M=M, N=N, K=K, ws=ws, wsb=wsb):
+                    args = (M, N, K, x.data_ptr(), cw.data_ptr(), sw.data_ptr(),
+                            r.data_ptr() if r is not None else None,
+                            y32.data_ptr() if y32 is not None else None, y16.data_ptr(),
+                            ws.data_ptr(), wsb, L.sp)
+
+                    def go():
+                        st = c.skinny_gemm_fp8(*args)
+                        if st:
+                            raise RuntimeError(sg.skinny_gemm_status_str(st))
+                    return go
+                per = timed_calls(torch, [f8(cw, sw) for cw, sw in ring], reps, cyc)
+                nbytes = N * K + scales.numel() * 4 + M * K * 2 + M * N * 2 * (2 if residual else 1) + \
+                    (0 if residual else M * N * 4)
+                us = 1e3 * per
+                gbs = nbytes / (per * 1e-3) / 1e9
+                rows.append({"workload": label, "M": M, "N": N, "K": K,
+                             "plan": lowp_plan_label("fp8", M, N, wsb),
+                             "us": round(us, 3), "GBps": round(gbs, 1),
+                             "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
+            del ring
+        torch.cuda.empty_cache()
+
+    run_section("fp8", section_5)
+
+    def section_6():
+        # router: scores y = x W_r^T (E=384 experts, K=7168, fp32) and their top-8 per token
+        E, K, k = 384, 7168, 8
+        Wr = si.normal_bf16((E, K), 0.02, si.seed_for(5, si.TAG_W) + 99, dev)
+        ring = ring_copies(torch, Wr)
+        c = L.c
+        for T in (1, 16, 64):
+            x = si.normal_bf16((T, K), 1.0, si.seed_for(5, si.TAG_X) + T, dev)
+            p = sg.skinny_gemm_plan(T, E, K)
+            scores = torch.empty((T, E), device=dev)
+            ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+            ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+
+            def router(proj, scores=scores, ids=ids, T=T):
+                def go():
+                    proj()
+                    st = c.skinny_gemm_router_topk(scores.data_ptr(), T, E, k, ids.data_ptr(), None,
+                                                   L.sp)
+                    if st:
+                        raise RuntimeError(sg.skinny_gemm_status_str(st))
+                return go
+            per = timed_calls(torch, [router(L.projection(p, x, w, scores, None, ws)) for w in ring],
+                              reps, cyc)
+            nbytes = proj_bytes(T, E, K, bf16=False) + T * E * 4 + T * k * 4
+            rows.append({"workload": "router top-8 E=384 K=7168", "M": T, "N": E, "K": K,
+                         "plan": f"{plan_desc(p)}+router_topk", "us": round(1e3 * per, 3),
+                         "GBps": round(nbytes / (per * 1e-3) / 1e9, 1),
+                         "pct_peak": round(100.0 * nbytes / (per * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)})
+        del ring, Wr
+
+    run_section("router", section_6)
+
+    def section_7():
+        # MoE grouped: E=384 experts of N=2048 x K=7168, 8 distinct experts per token,
+        # a ring of 8 routing tables per batch size
+        E, N, K, topk = 384, 2048, 7168, 8
+        W = si.normal_bf16((E, N, K), 0.02, si.seed_for(5, si.TAG_W) + 100, dev)
+        for T in (1, 16, 64):
+            x = si.normal_bf16((T, K), 1.0, si.seed_for(5, si.TAG_X) + T, dev)
+            tables = [si.routing_table(T, E, topk, si.seed_for(5, si.TAG_ROUTING) + 10 * i + 1000 * T)
+                      for i in range(8)]
+            out = torch.empty((T, topk, N), device=dev)
+            ws = torch.empty(sg.grouped_skinny_gemm_workspace(T, E, topk, N, K), dtype=torch.uint8,
+                             device=dev)
+            ids_dev = [t.to(dev) for t in tables]
+            per = timed_calls(torch, [L.grouped(x, W, ids, out, ws) for ids in ids_dev],
+                                 8 * max(1, reps // 32), cyc)
+            distinct = [len(set(t.view(-1).tolist())) for t in tables]
+            # the timed calls cycle the tables evenly (reps is a multiple of 8)
+            nbytes = sum(d * N * K * 2 + T * K * 2 + T * topk * N * 4 + T * topk * 4
+                         for d in distinct) / len(distinct)
+            us = 1e3 * per
+            gbs = nbytes / (per * 1e-3) / 1e9
+            rows.append({"workload": "MoE grouped E=384 2048x7168 top8", "M": T, "N": N, "K": K,
+                         "plan": "fused table+grouped", "us": round(us, 3), "GBps": round(gbs, 1),
+                         "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                         "distinct_experts_mean": round(sum(distinct) / len(distinct), 1)})
+
+        # one MoE decode step: router scores + top-8 + table + grouped routed experts, and a
+        # shared expert of the same shape as one routed expert (N=2048, K=7168): fused into the
+        # router's GEMM, on a side stream overlapping the routing, or serial.  Rings: inputs (8)
+        # and [router; shared expert] weight pairs (> 2 x MALL).
+        Wrs = torch.cat([si.normal_bf16((E, K), 0.02, si.seed_for(5, si.TAG_W) + 99, dev),
+                         si.normal_bf16((N, K), 0.02, si.seed_for(5, si.TAG_W) + 98, dev)])
+        ring_rs = ring_copies(torch, Wrs)
+        for T in (1, 16, 64):
+            xs = [si.normal_bf16((T, K), 1.0, si.seed_for(5, si.TAG_X) + 100 * T + i, dev)
                   for i in range(8)]
-        out = torch.empty((T, topk, N), device=dev)
-        ws = torch.empty(sg.grouped_skinny_gemm_workspace(T, E, topk, N, K), dtype=torch.uint8,
-                         device=dev)
-        ids_dev = [t.to(dev) for t in tables]
-        per = timed_calls(torch, [L.grouped(x, W, ids, out, ws) for ids in ids_dev],
-                             8 * max(1, reps // 32), cyc)
-        distinct = [len(set(t.view(-1).tolist())) for t in tables]
-        # the timed calls cycle the tables evenly (reps is a multiple of 8)
-        nbytes = sum(d * N * K * 2 + T * K * 2 + T * topk * N * 4 + T * topk * 4
-                     for d in distinct) / len(distinct)
-        us = 1e3 * per
-        gbs = nbytes / (per * 1e-3) / 1e9
-        rows.append({"workload": "MoE grouped E=384 2048x7168 top8", "M": T, "N": N, "K": K,
-                     "plan": "fused table+grouped", "us": round(us, 3), "GBps": round(gbs, 1),
-                     "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
-                     "distinct_experts_mean": round(sum(distinct) / len(distinct), 1)})
+            n_calls = max(len(ring_rs), len(xs))
+            combos = [(xs[i % len(xs)], ring_rs[i % len(ring_rs)][:E], ring_rs[i % len(ring_rs)][E:])
+                      for i in range(n_calls)]
+            outs = (torch.empty((T, topk), dtype=torch.int32, device=dev),
+                    torch.empty((T, E + N), device=dev), torch.empty((T, topk, N), device=dev),
+                    torch.empty((T, N), device=dev))
+            ws = torch.empty(sg.skinny_moe_step_workspace(T, K, E, topk, N, N), dtype=torch.uint8,
+                             device=dev)
+            distinct = []
+            for x, wr, wsh in combos:  # the experts each call routes to (same inputs as timed)
+                L.moe_step(x, wr, W, wsh, topk, outs, ws, "serial")()
+                torch.cuda.synchronize()
+                distinct.append(len(set(outs[0].view(-1).tolist())))
+            nbytes = sum(d * N * K * 2 for d in distinct) / len(distinct) + \
+                proj_bytes(T, E, K, bf16=False) + proj_bytes(T, N, K, bf16=False) - T * K * 2 + \
+                T * topk * N * 4 + T * topk * 4
+            per = {}
+            launches = {}
+            for mode in ("serial", "side_stream", "fused"):
+                calls = [L.moe_step(x, wr, W, wsh, topk, outs, ws, mode) for x, wr, wsh in combos]
+                before = sg.skinny_gemm_get_counters()
+                calls[0]()
+                torch.cuda.synchronize()
+                launches[mode] = sum(a - b for a, b in zip(sg.skinny_gemm_get_counters(), before))
+                per[mode] = timed_calls(torch, calls, n_calls, cyc)
+            gbs = nbytes / (per["fused"] * 1e-3) / 1e9
+            rows.append({"workload": "MoE step E=384 top8 2048x7168 + shared expert", "M": T,
+                         "N": N, "K": K, "plan": "router+shared fused GEMM, top8, table, grouped",
+                         "us": round(1e3 * per["fused"], 3),
+                         "us_side_stream": round(1e3 * per["side_stream"], 3),
+                         "us_serial": round(1e3 * per["serial"], 3),
+                         "launches_per_step": launches["fused"],
+                         "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                         "distinct_experts_mean": round(sum(distinct) / len(distinct), 1)})
+        del W, Wrs, ring_rs
+        torch.cuda.empty_cache()
 
-    # one MoE decode step: router scores + top-8 + table + grouped routed experts, and a
-    # shared expert of the same shape as one routed expert (N=2048, K=7168): fused into the
-    # router's GEMM, on a side stream overlapping the routing, or serial.  Rings: inputs (8)
-    # and [router; shared expert] weight pairs (> 2 x MALL).
-    Wrs = torch.cat([si.normal_bf16((E, K), 0.02, si.seed_for(5, si.TAG_W) + 99, dev),
-                     si.normal_bf16((N, K), 0.02, si.seed_for(5, si.TAG_W) + 98, dev)])
-    ring_rs = ring_copies(torch, Wrs)
-    for T in (1, 16, 64):
-        xs = [si.normal_bf16((T, K), 1.0, si.seed_for(5, si.TAG_X) + 100 * T + i, dev)
-              for i in range(8)]
-        n_calls = max(len(ring_rs), len(xs))
-        combos = [(xs[i % len(xs)], ring_rs[i % len(ring_rs)][:E], ring_rs[i % len(ring_rs)][E:])
-                  for i in range(n_calls)]
-        outs = (torch.empty((T, topk), dtype=torch.int32, device=dev),
-                torch.empty((T, E + N), device=dev), torch.empty((T, topk, N), device=dev),
-                torch.empty((T, N), device=dev))
-        ws = torch.empty(sg.skinny_moe_step_workspace(T, K, E, topk, N, N), dtype=torch.uint8,
-                         device=dev)
-        distinct = []
-        for x, wr, wsh in combos:  # the experts each call routes to (same inputs as timed)
-            L.moe_step(x, wr, W, wsh, topk, outs, ws, "serial")()
-            torch.cuda.synchronize()
-            distinct.append(len(set(outs[0].view(-1).tolist())))
-        nbytes = sum(d * N * K * 2 for d in distinct) / len(distinct) + \
-            proj_bytes(T, E, K, bf16=False) + proj_bytes(T, N, K, bf16=False) - T * K * 2 + \
-            T * topk * N * 4 + T * topk * 4
-        per = {}
-        launches = {}
-        for mode in ("serial", "side_stream", "fused"):
-            calls = [L.moe_step(x, wr, W, wsh, topk, outs, ws, mode) for x, wr, wsh in combos]
-            before = sg.skinny_gemm_get_counters()
-            calls[0]()
-            torch.cuda.synchronize()
-            launches[mode] = sum(a - b for a, b in zip(sg.skinny_gemm_get_counters(), before))
-            per[mode] = timed_calls(torch, calls, n_calls, cyc)
-        gbs = nbytes / (per["fused"] * 1e-3) / 1e9
-        rows.append({"workload": "MoE step E=384 top8 2048x7168 + shared expert", "M": T,
-                     "N": N, "K": K, "plan": "router+shared fused GEMM, top8, table, grouped",
-                     "us": round(1e3 * per["fused"], 3),
-                     "us_side_stream": round(1e3 * per["side_stream"], 3),
-                     "us_serial": round(1e3 * per["serial"], 3),
-                     "launches_per_step": launches["fused"],
-                     "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
-                     "distinct_experts_mean": round(sum(distinct) / len(distinct), 1)})
-    del W, Wrs, ring_rs
-    torch.cuda.empty_cache()
+    run_section("moe", section_7)
+
     return rows
 
 
@@ -1271,6 +1350,9 @@ def main() -> None:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--jsonl", metavar="PATH",
+                    help="write the sweep's rows to PATH as JSON lines, section by section; "
+                         "run again with the same PATH to resume a killed sweep")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "COMMAND"))
@@ -1328,7 +1410,8 @@ def main() -> None:
     sweep_rows = None
     if not args.no_sweep:
         log("sweep over batch sizes and workloads")
-        sweep_rows = sweep(torch, sg, si, L, cyc)
+        sweep_rows = sweep(torch, sg, si, L, cyc,
+                           journal=SweepJournal(args.jsonl) if args.jsonl else None)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: the fp64 oracle on this host")
