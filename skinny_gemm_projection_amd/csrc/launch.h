@@ -22,9 +22,11 @@ int rowdot_resident_waves(int M, int nch);
 // waves) by the row-streaming kernel at batch size M.
 bool rowdot_team_split_ok(int M, int S);
 int rowdot_block_threads(int S, bool two_pass);
-// Whether the unsplit small-matrix plan (M <= 2, S == 1) runs the streaming
-// kernel -- one row per step, the next row's loads in flight -- and its grid.
-constexpr int kRowstreamMaxIters = 4;
+// Whether a vector-ALU plan runs the streaming kernel -- one row per step,
+// the next row's loads in flight -- and its grid: M <= 2 with one K chunk,
+// or M = 3, 4 with teams of 2 or 4 waves on K chunks; x staged in LDS.
+constexpr int kRowstreamMaxIters = 4;      // rows a wave, M <= 2
+constexpr int kRowstreamMaxTeamIters = 8;  // rows a team, M = 3, 4
 bool rowstream_plan(int M, int N, int K, int S, bool two_pass, int* grid);
 
 // Row-streaming VALU kernel (small-matrix path and VALU split-K).

@@ -187,45 +187,66 @@ __global__ __launch_bounds__(kWave * block_waves(S)) void rowdot_kernel(
     }
 }
 
-// x staging loads per thread of the streaming kernel (LDS slots: 256 times this).
-constexpr int rowstream_stage_loads(int M, int NCH) { return (M * NCH * kWave + kBlock - 1) / kBlock; }
+// x staging loads per thread of the streaming kernel (LDS slots: 256 times
+// this): all of x, M * K8 <= M * NCH * 64 * S pieces.
+constexpr int rowstream_stage_loads(int M, int NCH, int S) {
+    return (M * NCH * kWave * S + kBlock - 1) / kBlock;
+}
 
-// Small-matrix path with one K chunk (S = 1) and x staged in LDS: a wave
-// takes ITERS rows, one per step, the grid's waves striding over N, with two
-// row buffers, so the next row's loads are in flight while the current row
-// is multiplied, reduced and stored.  Every step is unrolled: each wait is
+// Streaming projection kernel for the vector ALU with x staged in LDS.  A
+// team of S waves (S = 1, 2 or 4 in a workgroup of 4 waves) takes ITERS
+// rows, one per step, the grid's teams striding over N; member s of a team
+// covers K chunk s of each row ([s*chunk8, (s+1)*chunk8) pieces).  Two row
+// buffers keep the next row's loads in flight while the current row is
+// multiplied, reduced and stored.  Every step is unrolled, so each wait is
 // for exactly the row it needs (behind a loop header the compiler would wait
-// for every load in flight).
-template <int M, int NCH, int ITERS>
+// for every load in flight), and every load is issued: pieces past a chunk
+// or a row past N read zero through the buffer bounds (a branch around a
+// load would also make the compiler wait for all of them).  With S > 1 the
+// members' sums of a step meet in LDS and the first member adds them in
+// ascending chunk order (one barrier a step; the barrier waits for LDS
+// only, not for the row loads in flight) -- the same order on every run.
+template <int M, int NCH, int S, int ITERS>
 __global__ __launch_bounds__(kBlock) void rowstream_kernel(const uint4* __restrict__ x,
                                                            const uint4* __restrict__ W, int N,
-                                                           int K8, Epilogue ep) {
+                                                           int K8, int chunk8, Epilogue ep) {
+    static_assert(S == 1 || S == 2 || S == 4, "a team fits in the 4-wave workgroup");
     constexpr int V = pad4(M);
-    constexpr int kStage = rowstream_stage_loads(M, NCH);
+    constexpr int kTeams = kWavesPerBlock / S;  // teams per workgroup
+    constexpr int kStage = rowstream_stage_loads(M, NCH, S);
+    __shared__ float red[S > 1 ? 2 : 1][kTeams][S][V];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = blockIdx.x * kWavesPerBlock + wave_id_in_block();
-    const int waves = gridDim.x * kWavesPerBlock;
-    const uint32_t bytes = (uint32_t)K8 * 16u;
-    const int v = scatter_index<V>(lane);  // the output a lane stores after a row's reduction
-    // Residual values of the wave's outputs, requested first: read inside a
-    // step, each would wait for every row load in flight.  Buffer loads (no
-    // branch) keep the compiler from sinking them to their use.
-    // (converted at their use, so that nothing waits for them before then)
-    uint32_t rv[ITERS];  // 32-bit slots: packed 16-bit halves would serialize the loads
+    const int wib = wave_id_in_block();
+    const int team_in_block = wib / S;
+    const int member = wib - team_in_block * S;
+    const int team = blockIdx.x * kTeams + team_in_block;
+    const int teams = gridDim.x * kTeams;
+    const int k0 = member * chunk8;
+    const int len = max(0, min(K8 - k0, chunk8));  // pieces of this member's chunk
+    const uint32_t bytes = (uint32_t)len * 16u;
+    const int v = scatter_index<V>(lane);  // the output a lane holds after a row's reduction
+    const bool stores = member == 0;        // the first member finishes the outputs
+    // Residual values of the outputs this lane stores, requested first: read
+    // inside a step, each would wait for every row load in flight.  Buffer
+    // loads (no branch) keep the compiler from sinking them to their use,
+    // into 32-bit slots (packed 16-bit halves would serialise the loads), and
+    // converted at their use, so that nothing waits for them before then.
+    uint32_t rv[ITERS];
     if (ep.r) {
         const rsrc_t rr = make_rsrc(ep.r, (uint32_t)M * (uint32_t)N * 2u);
 #pragma unroll
         for (int it = 0; it < ITERS; ++it) {
-            const int n = wave + it * waves;
-            const bool mine = v >= 0 && v < M && n < N;
+            const int n = team + it * teams;
+            const bool mine = stores && v >= 0 && v < M && n < N;
             rv[it] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
                 rr, mine ? (uint32_t)(v * N + n) * 2u : 0xFFFFFFF0u, 0, kCached);
         }
     }
     uint4 wr[2][NCH];
     auto load_row = [&](int it, uint4 (&dst)[NCH]) {
-        const int n = wave + it * waves;
-        const rsrc_t rs = make_rsrc(W + (int64_t)min(n, N - 1) * K8, n < N ? bytes : 0u);
+        const int n = team + it * teams;
+        const rsrc_t rs =
+            make_rsrc(W + (int64_t)min(n, N - 1) * K8 + k0, n < N ? bytes : 0u);
         load_pieces<NCH, kStream, false>(dst, rs, NCH, lane);
     };
     // x: each thread stages its share; the first two rows are requested right
@@ -249,7 +270,7 @@ __global__ __launch_bounds__(kBlock) void rowstream_kernel(const uint4* __restri
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int p = c * kWave + lane;
-            xr[m][c] = p < K8 ? xs[m * K8 + p] : make_uint4(0, 0, 0, 0);
+            xr[m][c] = p < len ? xs[m * K8 + k0 + p] : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
@@ -265,9 +286,20 @@ __global__ __launch_bounds__(kBlock) void rowstream_kernel(const uint4* __restri
             acc[m] = a;
         }
         if (it + 2 < ITERS) load_row(it + 2, wr[b]);  // the buffer just consumed
-        const float sum = reduce_scatter<V>(acc, lane);
-        const int n = wave + it * waves;
-        if (v >= 0 && v < M && n < N) {
+        float sum = reduce_scatter<V>(acc, lane);
+        const int n = team + it * teams;
+        if constexpr (S > 1) {
+            // the step's partials meet in LDS; two buffers, so a member that
+            // runs ahead writes the other one (one barrier a step suffices)
+            if (v >= 0) red[b][team_in_block][member][v] = sum;
+            __syncthreads();
+            if (stores && v >= 0) {
+                sum = red[b][team_in_block][0][v];
+#pragma unroll
+                for (int q = 1; q < S; ++q) sum += red[b][team_in_block][q][v];
+            }
+        }
+        if (stores && v >= 0 && v < M && n < N) {
             const float val = ep.r ? sum + __builtin_bit_cast(float, rv[it] << 16) : sum;
             const int64_t i = (int64_t)v * N + n;
             if (ep.y_f32) ep.y_f32[i] = val;
@@ -337,22 +369,39 @@ int rowdot_grid(int M, int N, int K, int S, int k_chunk, bool two_pass) {
 // a CU then still fit in its 160 KB).
 constexpr size_t kStageMax = 64 * 1024;
 
-// Rows a wave of the streaming kernel takes: as many waves as the chip keeps
-// resident, each the same number of rows.
-static int rowstream_iters(int N) {
-    const int resident = rowdot_resident_waves(1, 0);
-    const int waves = N < resident ? N : resident;
-    return (N + waves - 1) / waves;
+// Rows a team of the streaming kernel takes (the unrolled step count): as
+// many teams as the chip keeps resident waves for, each the same number of
+// rows; teams of S > 1 waves round it up to a power of two (the compiled
+// step counts), with the team count then trimmed to match.
+static int rowstream_iters(int N, int S) {
+    const int resident = rowdot_resident_waves(1, 0) / S;
+    const int teams = N < resident ? N : resident;
+    const int its = (N + teams - 1) / teams;
+    return S == 1 ? its : next_pow2(its);
+}
+
+// Loads per row of a team member: exact for S = 1 (up to 16), else the
+// power of two the launch is compiled for.
+static int rowstream_nch(int K, int S) {
+    const int chunk = 64 * ((K + 64 * S - 1) / (64 * S));  // the plan's k_chunk
+    const int nch = (chunk + kLaneSpan - 1) / kLaneSpan;
+    return S == 1 ? nch : next_pow2(nch);
 }
 
 bool rowstream_plan(int M, int N, int K, int S, bool two_pass, int* grid) {
-    if (M < 1 || M > 2 || S != 1 || two_pass || K <= 0 || N < 1) return false;
-    const int nch = (K + kLaneSpan - 1) / kLaneSpan;
-    if (nch > 16 || (size_t)M * K * 2 > kStageMax) return false;
-    const int its = rowstream_iters(N);
-    if (its > kRowstreamMaxIters) return false;
-    const int waves = (N + its - 1) / its;
-    if (grid) *grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (M < 1 || two_pass || K <= 0 || N < 1 || (size_t)M * K * 2 > kStageMax) return false;
+    const int nch = rowstream_nch(K, S);
+    const int its = rowstream_iters(N, S);
+    if (M <= 2) {  // one K chunk: x of the whole row in registers
+        if (S != 1 || nch > 16 || its > kRowstreamMaxIters) return false;
+    } else {       // M = 3, 4: teams of 2 or 4 waves on K chunks
+        if (M > 4 || (S != 2 && S != 4) || nch < 2 || nch > 8 || its < 2 ||
+            its > kRowstreamMaxTeamIters)
+            return false;
+    }
+    const int teams = (N + its - 1) / its;
+    const int per_block = kWavesPerBlock / S;
+    if (grid) *grid = (teams + per_block - 1) / per_block;
     return true;
 }
 
@@ -366,18 +415,42 @@ static hipError_t launch_mns(int N, int K, int splits, int k_chunk, int grid, bo
     const int groups = (N + R - 1) / R;
     const uint4* xp = static_cast<const uint4*>(x);
     const uint4* wp = static_cast<const uint4*>(W);
-    if constexpr (M <= 2 && S == 1 && XS && !GUARD) {
+    constexpr bool kStreamOne = M <= 2 && S == 1 && XS && !GUARD;
+    constexpr bool kStreamTeam = (M == 3 || M == 4) && (S == 2 || S == 4) && XS &&
+                                 (NCH == 2 || NCH == 4 || NCH == 8);
+    if constexpr (kStreamOne || kStreamTeam) {
         int g = 0;
         if (rowstream_plan(M, N, K, splits, two_pass, &g)) {
-            const int its = rowstream_iters(N);
-            const size_t lds = (size_t)rowstream_stage_loads(M, NCH) * kBlock * 16;
+            const int its = rowstream_iters(N, S);
+            const size_t lds = (size_t)rowstream_stage_loads(M, NCH, S) * kBlock * 16;
             switch (its) {
 #define SG_ITERS(i)                                                                         \
     case i:                                                                                 \
-        rowstream_kernel<M, NCH, i><<<g, kBlock, lds, stream>>>(xp, wp, N, K8, ep);        \
+        rowstream_kernel<M, NCH, S, i><<<g, kBlock, lds, stream>>>(xp, wp, N, K8, chunk8, ep); \
         return hipGetLastError();
-                SG_ITERS(1) SG_ITERS(2) SG_ITERS(3) SG_ITERS(4)
+                SG_ITERS(2) SG_ITERS(4)
 #undef SG_ITERS
+                case 1:
+                    if constexpr (kStreamOne) {
+                        rowstream_kernel<M, NCH, S, 1><<<g, kBlock, lds, stream>>>(xp, wp, N, K8,
+                                                                                 chunk8, ep);
+                        return hipGetLastError();
+                    }
+                    break;
+                case 3:
+                    if constexpr (kStreamOne) {
+                        rowstream_kernel<M, NCH, S, 3><<<g, kBlock, lds, stream>>>(xp, wp, N, K8,
+                                                                                 chunk8, ep);
+                        return hipGetLastError();
+                    }
+                    break;
+                case 8:
+                    if constexpr (kStreamTeam) {
+                        rowstream_kernel<M, NCH, S, 8><<<g, kBlock, lds, stream>>>(xp, wp, N, K8,
+                                                                                 chunk8, ep);
+                        return hipGetLastError();
+                    }
+                    break;
                 default: break;
             }
         }
