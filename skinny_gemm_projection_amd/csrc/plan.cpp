@@ -34,7 +34,6 @@ namespace {
 constexpr int32_t kMaxNK = 1 << 20;
 constexpr int32_t kMaxSplit = 64;
 constexpr int kComputeUnits = 256;
-constexpr int32_t kWideChunkFromM = 12;  // chunk kernel from here when N/16 >= 2 CUs
 // Smallest batch planned on the matrix cores.  Measured on MI355X (K=7168,
 // N=4096): from M=8 up the VALU kernel's v_dot2 work per weight byte, M/2
 // instructions per bf16 pair, outgrows the weight stream (M=8: 15.0 us VALU
@@ -339,16 +338,16 @@ sg_status make_plan_impl(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_
             // x through the per-wave LDS tile: K=7168, N=4096, M=16 13.5 us
             // against 14.3 us for the chunk kernel and its reduction; from
             // M=20 (two row tiles) the chunk kernel wins (16.6 against 15.4).
-            // With twice as many 16-row tiles as compute units the chunk
-            // kernel fills the chip too, and from 12 rows its x read once
-            // per 128- or 256-row tile beats the team kernel's once per 16
-            // rows: K=7168, N=8192, M = 12 / 16 22.9 / 23.9 us (team) against
-            // 22.5 / 22.5 us (chunk); at M = 8 the team kernel stays faster
-            // (22.1 against 22.4 us).
+            // With twice as many 16-row tiles as compute units (N >= 8161)
+            // each wave of the team kernel takes two tiles and reads each x
+            // operand once for both; that keeps it ahead of the chunk kernel
+            // up to 16 rows: K=7168, N=8192, M = 12 / 16 22.0 / 22.2 us
+            // against 22.5 / 22.6 us (chunk); residual M = 16 22.3 against
+            // 22.9.  (With one tile a wave it lost there from 12 rows: 23.1
+            // / 24.1 us.)
             const int32_t team_tiles = (N + kMfmaTeamTileN - 1) / kMfmaTeamTileN;
-            const bool chunk_wide = M >= kWideChunkFromM && team_tiles >= 2 * kComputeUnits;
             const bool team_auto = two_pass < 0 && tile_n == 0 && M <= kTeamUpToM &&
-                                   team_tiles >= kComputeUnits && !chunk_wide &&
+                                   team_tiles >= kComputeUnits &&
                                    (split_k <= 0 || mfma_team_split_ok(split_k));
             const bool team_asked = two_pass == 0 || tile_n == kMfmaTeamTileN || team_auto;
             int32_t S = 0, t = 0;
@@ -371,7 +370,7 @@ sg_status make_plan_impl(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_
             if (!mfma_team_split_ok(split_k)) return SG_ERR_PLAN;
             p.k_chunk = chunk_of(K, split_k);
             p.tile_n = kMfmaTeamTileN;
-            p.grid = (N + kMfmaTeamTileN - 1) / kMfmaTeamTileN;
+            p.grid = mfma_team_grid(M, N);
             two_pass = 0;
             break;
         }

@@ -271,54 +271,59 @@ __global__ __launch_bounds__(kChunkThreads) void splitk_mfma_kernel(
     }
 }
 
-// Team kernel: the S waves of one workgroup share a 16-row tile of W and
+// Team kernel: the S waves of one workgroup share NT 16-row tiles of W and
 // split K between them (wave s streams chunk s).  The weights arrive as in
 // the chunk kernel -- 4 rows x 256 bytes per load, transposed through a
 // per-wave LDS tile -- while the x operands of each k step are loaded
 // straight from L2 into the same register ring (x is small and every
-// workgroup reads all of it; at MT row tiles that is MT times the weight
-// bytes, so the planner uses this kernel for M <= 16).  There is no barrier
-// in the main loop.  At the end the S partial tiles are added in LDS in
-// ascending split order (deterministic) and wave w finishes the outputs o
-// with o % S == w: no workspace and no second kernel.
-template <int MT, int S, int DR>
+// workgroup reads all of it; at MT row tiles that is MT / NT times the
+// weight bytes, so the planner uses this kernel for M <= 16).  With NT = 2
+// each x operand read serves both tiles.  There is no barrier in the main
+// loop.  At the end the S partial tiles are added in LDS in ascending split
+// order (deterministic) and wave w finishes the outputs o with o % S == w:
+// no workspace and no second kernel.
+template <int MT, int S, int DR, int NT>
 __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __restrict__ x,
                                                               const uint4* __restrict__ W, int M,
                                                               int N, int K8, int chunk8,
                                                               Epilogue ep) {
-    constexpr int OUT = MT * 4;  // accumulator floats per lane
+    constexpr int OUT = MT * 4;  // accumulator floats per lane and tile
     constexpr int RP = 16;       // pieces per row per round
     constexpr uint32_t kOff = 0xFFFFFFF0u;  // past any descriptor range: reads zero
     // x tiles in LDS too, where the workgroup's LDS allows (all but MT = 4, S = 8)
-    constexpr bool XT = (size_t)S * (kTileSlots * 16 * (1 + MT) + OUT * kWave * 4) <= kMfmaMaxLds;
-    __shared__ uint4 tiles[S][kTileSlots];
+    constexpr bool XT =
+        (size_t)S * (kTileSlots * 16 * (NT + MT) + NT * OUT * kWave * 4) <= kMfmaMaxLds;
+    __shared__ uint4 tiles[S][NT][kTileSlots];
     __shared__ uint4 xtiles[XT ? S : 1][XT ? MT : 1][XT ? kTileSlots : 1];
-    __shared__ float red[S][OUT][kWave];
+    __shared__ float red[S][NT * OUT][kWave];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int s = wave_id_in_block();
     const int col = lane & 15;
     const int grp = lane >> 4;
-    uint4* tile = tiles[s];
-    const int row0 = blockIdx.x * 16;
-    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16, N - row0)));
+    const int row0 = blockIdx.x * 16 * NT;
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16 * NT, N - row0)));
     const int k0 = s * chunk8;
     const int len = max(0, min(K8 - k0, chunk8));  // pieces of this wave's chunk
     const int rounds = (len + RP - 1) / RP;
 
     const rsrc_t wrs = make_rsrc(W + (int64_t)row0 * K8, (uint32_t)rows * (uint32_t)K8 * 16u);
     const rsrc_t xrs = make_rsrc(x, (uint32_t)M * (uint32_t)K8 * 16u);
-    // weights: load i of a round reads row 4i + grp, slot col = piece col ^ row
-    uint32_t woff[4];
+    // weights: load i of a round reads row 16*nt + 4i + grp, slot col =
+    // piece col ^ (4i + grp)
+    uint32_t woff[NT][4];
     int wpiece[4];
-    bool wrow[4];
+    bool wrow[NT][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * i + grp;
-        wpiece[i] = col ^ r;
-        wrow[i] = r < rows;
-        woff[i] = ((uint32_t)r * K8 + k0 + wpiece[i]) * 16u;
-    }
+    for (int i = 0; i < 4; ++i) wpiece[i] = col ^ (4 * i + grp);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * nt + 4 * i + grp;
+            wrow[nt][i] = r < rows;
+            woff[nt][i] = ((uint32_t)r * K8 + k0 + wpiece[i]) * 16u;
+        }
     // x goes the same way as the weights: load i of a round reads row
     // 16*mt + 4i + grp of x, slot col = piece col ^ (4i + grp), into the
     // wave's x tile; the A operand of step t (piece 4t + grp of row
@@ -337,12 +342,15 @@ __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __res
             xrow[i][mt] = m < M;
             xoff[i][mt] = ((uint32_t)m * K8 + k0 + piece) * 16u;
         }
-    auto load_round = [&](int rd, uint4 (&w)[4], uint4 (&a)[4][MT]) {
+    auto load_round = [&](int rd, uint4 (&w)[NT][4], uint4 (&a)[4][MT]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool ok = wrow[i] && (rd * RP + wpiece[i] < len);
-            w[i] = load16<kStream>(wrs, ok ? woff[i] + (uint32_t)rd * (RP * 16u) : kOff);
-        }
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = wrow[nt][i] && (rd * RP + wpiece[i] < len);
+                w[nt][i] =
+                    load16<kStream>(wrs, ok ? woff[nt][i] + (uint32_t)rd * (RP * 16u) : kOff);
+            }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -353,13 +361,15 @@ __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __res
             }
     };
 
-    uint4 wb[DR][4];
+    uint4 wb[DR][NT][4];
     uint4 xb[DR][4][MT];
 #pragma unroll
     for (int d = 0; d < DR; ++d) load_round(d, wb[d], xb[d]);
-    f32x4_t acc[MT];
+    f32x4_t acc[NT][MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     for (int r0 = 0; r0 < rounds; r0 += DR) {
 #pragma unroll
         for (int d = 0; d < DR; ++d) {
@@ -367,7 +377,9 @@ __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __res
             if (rd < rounds) {  // wave-uniform
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    tile[(4 * i + grp) * RP + col] = wb[d][i];
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        tiles[s][nt][(4 * i + grp) * RP + col] = wb[d][nt][i];
                     if constexpr (XT) {
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt)
@@ -378,14 +390,18 @@ __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __res
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int slot = col * RP + ((4 * t + grp) ^ col);
-                    const uint4 b = tile[slot];
+                    uint4 b[NT];
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) b[nt] = tiles[s][nt][slot];
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
                         const uint4 a = XT ? xtiles[XT ? s : 0][XT ? mt : 0][XT ? slot : 0]
                                            : xb[d][t][mt];
-                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                            acc[mt], 0, 0, 0);
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt)
+                            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[nt]),
+                                acc[nt][mt], 0, 0, 0);
                     }
                 }
                 __builtin_amdgcn_wave_barrier();
@@ -394,32 +410,40 @@ __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __res
         }
     }
 
-    const int n = row0 + col;
     if (S == 1) {
-        if (col >= rows) return;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int nt = 0; nt < NT; ++nt) {
+            const int r = 16 * nt + col;
+            if (r >= rows) continue;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int m = mt * 16 + grp * 4 + v;
-                if (m < M) store_final(ep, (int64_t)m * N + n, acc[mt][v]);
-            }
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = mt * 16 + grp * 4 + v;
+                    if (m < M) store_final(ep, (int64_t)m * N + row0 + r, acc[nt][mt][v]);
+                }
+        }
         return;
     }
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[s][mt * 4 + v][lane] = acc[mt][v];
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[s][nt * OUT + mt * 4 + v][lane] = acc[nt][mt][v];
     __syncthreads();
-    if (col >= rows) return;
 #pragma unroll
-    for (int o = 0; o < OUT; ++o) {
+    for (int o = 0; o < NT * OUT; ++o) {
         if (o % S != s) continue;
+        const int nt = o / OUT;
+        const int r = 16 * nt + col;
+        if (r >= rows) continue;
         float sum = red[0][o][lane];
 #pragma unroll
         for (int q = 1; q < S; ++q) sum += red[q][o][lane];
-        const int m = (o / 4) * 16 + grp * 4 + (o % 4);
-        if (m < M) store_final(ep, (int64_t)m * N + n, sum);
+        const int oo = o - nt * OUT;
+        const int m = (oo / 4) * 16 + grp * 4 + (oo % 4);
+        if (m < M) store_final(ep, (int64_t)m * N + row0 + r, sum);
     }
 }
 
@@ -427,9 +451,19 @@ __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __res
 
 bool mfma_team_split_ok(int S) { return S == 1 || S == 2 || S == 4 || S == 8; }
 
+int mfma_team_tiles_per_wave(int M, int N) {
+    return M <= 16 && N >= kMfmaTeamTwoTilesFromN ? 2 : 1;
+}
+
+int mfma_team_grid(int M, int N) {
+    const int rows = 16 * mfma_team_tiles_per_wave(M, N);
+    return (N + rows - 1) / rows;
+}
+
 hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void* x,
                             const void* W, const Epilogue& ep, hipStream_t stream) {
-    const int grid = (N + 15) / 16;
+    const int grid = mfma_team_grid(M, N);
+    const int NT = mfma_team_tiles_per_wave(M, N);
     const int K8 = K / kPiece;
     const int chunk8 = k_chunk / kPiece;
     const uint4* xp = static_cast<const uint4*>(x);
@@ -438,15 +472,16 @@ hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void*
     // rounds in flight per wave; measured on MI355X, 3 or 4 were slower (K=7168,
     // N=4096, M=8: 12.4 us at 2, 14.4 at 3, 15.0 at 4)
     constexpr int DR = 2;
-#define SG_TEAM(mt, sp) \
-    if (MT == mt && S == sp) { \
-        mfma_team_kernel<mt, sp, DR><<<grid, kWave * sp, 0, stream>>>(xp, wp, M, N, K8, chunk8, ep); \
+#define SG_TEAM(mt, sp, nt) \
+    if (MT == mt && S == sp && NT == nt) { \
+        mfma_team_kernel<mt, sp, DR, nt><<<grid, kWave * sp, 0, stream>>>(xp, wp, M, N, K8, chunk8, ep); \
         return hipGetLastError(); \
     }
-    SG_TEAM(1, 1) SG_TEAM(1, 2) SG_TEAM(1, 4) SG_TEAM(1, 8)
-    SG_TEAM(2, 1) SG_TEAM(2, 2) SG_TEAM(2, 4) SG_TEAM(2, 8)
-    SG_TEAM(3, 1) SG_TEAM(3, 2) SG_TEAM(3, 4) SG_TEAM(3, 8)
-    SG_TEAM(4, 1) SG_TEAM(4, 2) SG_TEAM(4, 4) SG_TEAM(4, 8)
+    SG_TEAM(1, 1, 1) SG_TEAM(1, 2, 1) SG_TEAM(1, 4, 1) SG_TEAM(1, 8, 1)
+    SG_TEAM(1, 1, 2) SG_TEAM(1, 2, 2) SG_TEAM(1, 4, 2) SG_TEAM(1, 8, 2)
+    SG_TEAM(2, 1, 1) SG_TEAM(2, 2, 1) SG_TEAM(2, 4, 1) SG_TEAM(2, 8, 1)
+    SG_TEAM(3, 1, 1) SG_TEAM(3, 2, 1) SG_TEAM(3, 4, 1) SG_TEAM(3, 8, 1)
+    SG_TEAM(4, 1, 1) SG_TEAM(4, 2, 1) SG_TEAM(4, 4, 1) SG_TEAM(4, 8, 1)
 #undef SG_TEAM
     return hipErrorInvalidValue;
 }

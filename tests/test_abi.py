@@ -85,14 +85,19 @@ def test_plan_kernel_by_batch_few_rows():
 
 def test_plan_team_or_chunk_by_width():
     # 8..16 rows on matrix cores: the team kernel (16-row tiles, one pass) while N/16 tiles
-    # fill the CUs, except from M = 12 once there are twice as many tiles as CUs, where the
-    # chunk kernel (128/256-row tiles, second pass) reads x fewer times
-    for M, N, team in [(8, 4096, True), (16, 4096, True), (8, 8192, True), (11, 8192, True),
-                       (12, 8192, False), (16, 8192, False), (16, 7168, True),
-                       (16, 16384, False), (17, 4096, False)]:
+    # fill the CUs (two tiles a wave from N = 8161, so its grid is N/32); the chunk kernel
+    # (128/256-row tiles, second pass) below that width and from 17 rows
+    for M, N, team, grid in [(8, 4096, True, 256), (16, 4096, True, 256), (8, 8192, True, 256),
+                             (11, 8192, True, 256), (12, 8192, True, 256),
+                             (16, 8192, True, 256), (16, 7168, True, 448),
+                             (16, 8160, True, 510), (16, 8161, True, 256),
+                             (16, 16384, True, 512), (16, 2048, False, None),
+                             (17, 4096, False, None)]:
         p = sg.skinny_gemm_plan(M, N, 7168)
         assert p.kernel == sg.SG_KERNEL_SPLITK_MFMA, (M, N, p)
         assert (p.tile_n == 16 and not p.two_pass) == team, (M, N, p)
+        if team:
+            assert p.grid == grid, (M, N, p)
 
 
 def test_plan_rejects():

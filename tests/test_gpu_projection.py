@@ -72,6 +72,10 @@ SMALL = [
     (3, 1000, 1032), (4, 513, 2056), (5, 1000, 1032), (8, 300, 4104), (9, 1000, 1032),
     (15, 257, 1032), (16, 1000, 1056), (17, 130, 520), (31, 1000, 1056), (32, 65, 2056),
     (48, 1000, 1056), (63, 200, 264), (64, 1000, 1056),
+    # wide matrices: the team kernel with two 16-row tiles a wave (ragged last pair)
+    (9, 8161, 520), (12, 8200, 1040), (16, 8177, 264), (13, 9000, 2056),
+    # the streaming vector-ALU kernel with teams: M = 3, 4, 2 to 8 rows a team
+    (3, 2101, 4104), (4, 4097, 2056), (4, 6000, 8192), (4, 3000, 7168),
 ]
 
 
@@ -213,6 +217,14 @@ def test_full_single_projection_1024():
 def test_full_small_batch_7168x8192(M):
     plan = _full_case(M, 8192, 7168, 2000, rows=None)
     assert plan.kernel == G and plan.split_k == 1
+
+
+@pytest.mark.parametrize("M", [4, 8, 16])
+def test_full_larger_batch_8192x7168(M):
+    # every output of the bench's wider-matrix rows (streaming teams at M = 4, the
+    # two-tile team kernel at M = 8 and 16)
+    plan = _full_case(M, 8192, 7168, 2500, rows=None)
+    assert plan.split_k > 1
 
 
 @pytest.mark.parametrize("M", [3, 4, 8, 12, 16, 32, 64])
