@@ -447,6 +447,116 @@ __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __res
     }
 }
 
+// Team kernel for one x row tile (M <= 16) with x in registers: each wave
+// loads the A operands of its whole K chunk once (ROUNDS rounds of 4 steps,
+// 16 bytes a lane and step) instead of reading them from L2 every round, so
+// the main loop carries only the weight loads and their LDS transpose.  The
+// rounds are unrolled (the operands are indexed by step at compile time,
+// and each wait is for exactly the round it needs); the weights go as in
+// mfma_team_kernel, NT tiles a wave, DR rounds in flight.
+template <int S, int NT, int ROUNDS>
+__global__ __launch_bounds__(kWave * S) void mfma_team_xr_kernel(const uint4* __restrict__ x,
+                                                                 const uint4* __restrict__ W,
+                                                                 int M, int N, int K8,
+                                                                 int chunk8, Epilogue ep) {
+    constexpr int DR = 2;
+    constexpr int RP = 16;
+    constexpr uint32_t kOff = 0xFFFFFFF0u;
+    __shared__ uint4 tiles[S][NT][kTileSlots];
+    __shared__ float red[S][NT * 4][kWave];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int s = wave_id_in_block();
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+    const int row0 = blockIdx.x * 16 * NT;
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16 * NT, N - row0)));
+    const int k0 = s * chunk8;
+    const int len = max(0, min(K8 - k0, chunk8));
+
+    // A operand of step t of round rd: x[col][k0 + 16 rd + 4 t + grp] (zero
+    // past M or past the chunk)
+    const rsrc_t xrs = make_rsrc(x, (uint32_t)M * (uint32_t)K8 * 16u);
+    uint4 xa[ROUNDS][4];
+#pragma unroll
+    for (int rd = 0; rd < ROUNDS; ++rd)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int piece = RP * rd + 4 * t + grp;
+            const bool ok = col < M && piece < len;
+            xa[rd][t] = load16<kCached>(xrs, ok ? ((uint32_t)col * K8 + k0 + piece) * 16u : kOff);
+        }
+
+    const rsrc_t wrs = make_rsrc(W + (int64_t)row0 * K8, (uint32_t)rows * (uint32_t)K8 * 16u);
+    uint32_t woff[NT][4];
+    int wpiece[4];
+    bool wrow[NT][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wpiece[i] = col ^ (4 * i + grp);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * nt + 4 * i + grp;
+            wrow[nt][i] = r < rows;
+            woff[nt][i] = ((uint32_t)r * K8 + k0 + wpiece[i]) * 16u;
+        }
+    auto load_round = [&](int rd, uint4 (&w)[NT][4]) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = rd < ROUNDS && wrow[nt][i] && (rd * RP + wpiece[i] < len);
+                w[nt][i] =
+                    load16<kStream>(wrs, ok ? woff[nt][i] + (uint32_t)rd * (RP * 16u) : kOff);
+            }
+    };
+    uint4 wb[DR][NT][4];
+#pragma unroll
+    for (int d = 0; d < DR; ++d) load_round(d, wb[d]);
+    f32x4_t acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int rd = 0; rd < ROUNDS; ++rd) {
+        const int d = rd % DR;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) tiles[s][nt][(4 * i + grp) * RP + col] = wb[d][nt][i];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int slot = col * RP + ((4 * t + grp) ^ col);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, xa[rd][t]),
+                    __builtin_bit_cast(bf16x8_t, tiles[s][nt][slot]), acc[nt], 0, 0, 0);
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (rd + DR < ROUNDS) load_round(rd + DR, wb[d]);
+    }
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[s][nt * 4 + v][lane] = acc[nt][v];
+    __syncthreads();
+#pragma unroll
+    for (int o = 0; o < NT * 4; ++o) {
+        if (o % S != s) continue;
+        const int nt = o / 4;
+        const int r = 16 * nt + col;
+        if (r >= rows) continue;
+        float sum = red[0][o][lane];
+#pragma unroll
+        for (int q = 1; q < S; ++q) sum += red[q][o][lane];
+        const int m = grp * 4 + (o % 4);
+        if (m < M) store_final(ep, (int64_t)m * N + row0 + r, sum);
+    }
+}
+
 }  // namespace
 
 bool mfma_team_split_ok(int S) { return S == 1 || S == 2 || S == 4 || S == 8; }
@@ -472,6 +582,23 @@ hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void*
     // rounds in flight per wave; measured on MI355X, 3 or 4 were slower (K=7168,
     // N=4096, M=8: 12.4 us at 2, 14.4 at 3, 15.0 at 4)
     constexpr int DR = 2;
+    // Two tiles a wave, up to 8 rows, 8 waves, 7 or 8 rounds a wave (K = 7168
+    // or 8192): x in registers.  Measured on MI355X (interleaved A/B),
+    // 8192x7168: M = 6 / 8 21.8 / 21.8 -> 20.9 / 21.3 us; but slower with one
+    // tile a wave (4096x7168 M = 8 / 16 12.4 / 13.5 -> 12.9 / 15.3 us;
+    // 7168x8192 M = 8 22.5 -> 27.0 us) and from 12 rows (8192x7168 M = 16
+    // 22.3 -> 23.2 us): the up-front x loads (scattered 64-byte pieces)
+    // delay the weight stream and the registers cost occupancy.
+    const int rounds = (chunk8 + 15) / 16;
+    if (MT == 1 && M <= 8 && NT == 2 && S == 8 && (rounds == 7 || rounds == 8)) {
+#define SG_XR(nt, r) \
+    if (NT == nt && rounds == r) { \
+        mfma_team_xr_kernel<8, nt, r><<<grid, kWave * 8, 0, stream>>>(xp, wp, M, N, K8, chunk8, ep); \
+        return hipGetLastError(); \
+    }
+        SG_XR(2, 7) SG_XR(2, 8)
+#undef SG_XR
+    }
 #define SG_TEAM(mt, sp, nt) \
     if (MT == mt && S == sp && NT == nt) { \
         mfma_team_kernel<mt, sp, DR, nt><<<grid, kWave * sp, 0, stream>>>(xp, wp, M, N, K8, chunk8, ep); \
