@@ -17,9 +17,11 @@
 // per workgroup in LDS and read from there; from M = 3 (K split over teams of
 // waves) each wave loads its chunk of x straight from L2, which measured
 // faster (4096 x 7168, M = 4: 9.7 -> 9.0 us; at M = 2 the LDS staging was
-// faster, 12.5 against 13.1 us at 8192 x 7168).  Except at M = 1 the first
-// row group's codes are requested right behind x.  A unit's codes become bf16
-// pairs with v_cvt_scalef32_pk_bf16_fp8
+// faster, 12.5 against 13.1 us at 8192 x 7168).  The first row group's codes
+// are requested right behind x (at M = 1 this measured 11.3 -> 10.8 us at
+// 8192 x 7168, once the LDS copy of x stopped waiting for the codes), and
+// teams of 4 or 8 waves request each next group before their reduction.  A
+// unit's codes become bf16 pairs with v_cvt_scalef32_pk_bf16_fp8
 // (scale 1: exact, every e4m3 value is a bf16 value) and meet their x pairs in
 // v_dot2; the unit's sum is multiplied by its block scale (a unit of 16 codes
 // never straddles a 128-column block) and accumulated in fp32.  R divides 128
@@ -27,6 +29,8 @@
 // row block of scales.  The R*M lane sums are reduced by the lane
 // reduce-scatter; a team of S waves (one K chunk each) adds its partials in
 // LDS in ascending chunk order, and the first wave runs the epilogue.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace sg {
@@ -60,6 +64,12 @@ __device__ __forceinline__ float dot_unit(const uint4 w, const uint4 xa, const u
     return acc;
 }
 
+// x staging loads per thread of the vector kernel (x [M, 2*K16] pieces over
+// the workgroup; LDS holds this many rounds of the workgroup's threads).
+constexpr int fp8_stage_loads(int M, int NCH, int S) {
+    return (2 * M * NCH * S + team_block_waves(S) - 1) / team_block_waves(S);
+}
+
 template <int M, int NCH, int S>
 __global__ __launch_bounds__(kWave * team_block_waves(S)) void fp8_rowdot_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ Wq, const float* __restrict__ Ws,
@@ -87,12 +97,19 @@ __global__ __launch_bounds__(kWave * team_block_waves(S)) void fp8_rowdot_kernel
     // codes and scales of the group of R rows starting at row g * R
     auto load_group = [&](int g) {
         const int n0 = g * R;
-        // the group's rows share one 128-row block of scales
-        const float* __restrict__ srow = Ws + (int64_t)(n0 / 128) * KB;
+        // the group's rows share one 128-row block of scales (a group past
+        // the end reads the last block; its sums are never stored)
+        // Chunks start on 128-column blocks (u0 is a multiple of 8 units), so
+        // the chunk's scales are the ceil(len / 8) words from u0 / 8; lanes
+        // past them read zero, and lanes past len inside the last block read
+        // its scale for codes that read zero.
+        const rsrc_t rsc = make_rsrc(Ws + (int64_t)(min(n0, N - 1) / 128) * KB + u0 / 8,
+                                     (uint32_t)((len + 7) / 8) * 4u);
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int u = c * kWave + lane;
-            sc[c] = u < len ? srow[(u0 + u) / 8] : 0.0f;  // 8 units = 128 columns
+            const int u = c * kWave + lane;  // 8 units = 128 columns
+            sc[c] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rsc, (uint32_t)(u / 8) * 4u, 0, kCached));
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -117,31 +134,23 @@ __global__ __launch_bounds__(kWave * team_block_waves(S)) void fp8_rowdot_kernel
                 xr[m][c][1] = in ? xs[m * K8 + 2 * (u0 + u) + 1] : make_uint4(0, 0, 0, 0);
             }
     };
-    if constexpr (M == 1) {
-        // x copied to LDS first, the codes requested after the barrier (the
-        // order below measured slower here: 11.2 -> 12.0 us at 8192 x 7168)
-        const int total = K8;
-        for (int i = threadIdx.x; i < total; i += kWave * kWaves) xs[i] = x[i];
-        __syncthreads();
-        read_x_lds();
-    } else if constexpr (fp8_x_in_lds(M)) {
+    if constexpr (fp8_x_in_lds(M)) {
         // x into registers first, then the first group's codes behind it:
-        // loads return in order, so the LDS copy waits for x only
-        // (8192 x 7168, M = 2: 12.4 -> 11.8 us)
+        // loads return in order, so the LDS copy waits for x only.  The copy
+        // is unconditional (the LDS buffer holds every staged slot): copied
+        // under a bounds test, an x load was moved into that branch, behind
+        // the code loads, and the barrier then waited for all of them.
         constexpr int kThreads = kWave * kWaves;
-        constexpr int kStage = (2 * M * NCH * S + kWaves - 1) / kWaves;  // >= M*K8 / kThreads
+        constexpr int kStage = fp8_stage_loads(M, NCH, S);  // >= M*K8 / kThreads
         const int total = M * K8;
         const rsrc_t rx = make_rsrc(x, (uint32_t)total * 16u);
         uint4 stage[kStage];
 #pragma unroll
         for (int j = 0; j < kStage; ++j)
             stage[j] = load16<kCached>(rx, (uint32_t)(threadIdx.x + j * kThreads) * 16u);
-        if (team < groups) load_group(team);
+        load_group(team);
 #pragma unroll
-        for (int j = 0; j < kStage; ++j) {
-            const int i = threadIdx.x + j * kThreads;
-            if (i < total) xs[i] = stage[j];
-        }
+        for (int j = 0; j < kStage; ++j) xs[threadIdx.x + j * kThreads] = stage[j];
         __syncthreads();
         read_x_lds();
     } else {
@@ -156,27 +165,36 @@ __global__ __launch_bounds__(kWave * team_block_waves(S)) void fp8_rowdot_kernel
                 xr[m][c][1] = load16<kCached>(rx, off + 16u);
             }
         }
-        if (team < groups) load_group(team);
+        load_group(team);
     }
 
-    for (int it = 0; it < iters; ++it) {
+    // One iteration over the group whose codes are in wr / sc: the dot
+    // products, then (if `next`) the next group's codes requested, then the
+    // reduction and the stores, which the new loads overlap.  A group past
+    // the end reads zero through the buffer bounds and stores nothing; no
+    // load sits behind a branch.  The codes of the first group are requested
+    // behind x, above.
+    auto iteration = [&](int it, auto next) {
         const int g = team + it * teams;
         const int n0 = g * R;
         float acc[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) acc[v] = 0.0f;
-        if (g < groups) {
-            if (M == 1 || it > 0) load_group(g);  // else requested behind x
 #pragma unroll
-            for (int r = 0; r < R; ++r)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    float a = 0.0f;
+            for (int m = 0; m < M; ++m) {
+                float a = 0.0f;
 #pragma unroll
-                    for (int c = 0; c < NCH; ++c)
-                        a = fmaf(dot_unit(wr[r][c], xr[m][c][0], xr[m][c][1]), sc[c], a);
-                    acc[r * M + m] = a;
-                }
+                for (int c = 0; c < NCH; ++c)
+                    a = fmaf(dot_unit(wr[r][c], xr[m][c][0], xr[m][c][1]), sc[c], a);
+                acc[r * M + m] = a;
+            }
+        if constexpr (decltype(next)::value) {
+            // kept behind the dot products: hoisted above them, the loads
+            // would need a second set of code registers
+            __builtin_amdgcn_sched_barrier(0);
+            load_group(g + teams);
         }
         const float tot = reduce_scatter<V>(acc, lane);
         const int v = scatter_index<V>(lane);
@@ -198,6 +216,26 @@ __global__ __launch_bounds__(kWave * team_block_waves(S)) void fp8_rowdot_kernel
                 for (int s = 1; s < S; ++s) sum += red[buf][team_in_block][s][v];
                 store_final(ep, (int64_t)m * N + n, sum);
             }
+        }
+    };
+    if constexpr (S >= 4) {
+        // The last iteration is peeled off the loop: with the loads it
+        // consumes issued either before the loop or in its last trip, each
+        // row's dot products still wait for that row's codes only.  (Separate
+        // straight-line paths for one and two iterations cost the M = 1 kernel
+        // 140 registers.)  8192 x 7168, M = 3: 13.5 -> 12.3 us.
+        for (int it = 0; it < iters - 1; ++it) iteration(it, std::true_type{});
+        iteration(iters - 1, std::false_type{});
+    } else {
+        // A lone wave or a pair: each iteration requests its own codes at the
+        // top.  The early request measured slower for a lone wave (18432 x
+        // 7168, M = 1: 23.1 against 22.1 us) and no faster for a pair (7168 x
+        // 8192, M = 2: 12.4 / 12.6 us).  The first iteration is peeled, its
+        // codes requested with x.
+        iteration(0, std::false_type{});
+        for (int it = 1; it < iters; ++it) {
+            load_group(team + it * teams);
+            iteration(it, std::false_type{});
         }
     }
 }
@@ -353,7 +391,10 @@ hipError_t launch_mns(int N, int K16, int chunk16, const void* x, const void* Wq
     const int grid = (teams + kTeams - 1) / kTeams;
     const int iters = (groups + grid * kTeams - 1) / (grid * kTeams);
     const int KB = (K16 * kUnitCodes + 127) / 128;
-    const size_t lds = fp8_x_in_lds(M) ? (size_t)M * 2 * K16 * 16 : 0;  // at most 64 KB
+    // the staged x and its padding to whole staging rounds
+    const size_t lds =
+        fp8_x_in_lds(M) ? (size_t)fp8_stage_loads(M, NCH, S) * kWave * team_block_waves(S) * 16
+                        : 0;
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&fp8_rowdot_kernel<M, NCH, S>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
