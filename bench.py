@@ -1034,7 +1034,9 @@ def read_traffic():
 COPY_BYTES = 1 << 30          # the calibration copy reads and writes this many bytes
 COPY_KERNEL_TAG = "MulFunctor"  # torch.mul(src, 1.0, out=dst): a plain element-wise copy
 COPY_GRID = COPY_BYTES // 16    # its launch: one thread per 4 floats
-GEMV_KERNEL_TAGS = ("rowstream_kernel<1, 14, 4>", "rowstream_kernel<2, 14, 4>")
+# the headline launches: rowstream_kernel<M, NCH, S, ITERS> with 14 loads a row,
+# one wave a row and 4 rows a wave (8192 rows on 2048 waves, K = 7168)
+GEMV_KERNEL_TAGS = ("rowstream_kernel<1, 14, 1, 4>", "rowstream_kernel<2, 14, 1, 4>")
 
 
 def _pmc_dispatches(directory: str) -> list:

@@ -49,3 +49,23 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_headline_kernel_tags_name_built_kernels():
+    """The kernel names bench.py looks for in rocprofv3 output (traffic and
+    trace summaries) are instantiations the library holds, and the headline
+    plan is the streaming kernel with one wave a row."""
+    import shutil
+    import skinny_gemm_projection_amd as sg
+    from skinny_gemm_projection_amd import _lib
+    nm = shutil.which("nm")
+    if nm is None:
+        import pytest
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-C", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    for tag in bench.GEMV_KERNEL_TAGS:
+        assert f"sg::(anonymous namespace)::{tag}(" in out, tag
+    for M in (1, 2):
+        p = sg.skinny_gemm_plan(M, bench.N_MAIN, bench.K_MAIN)
+        assert p.kernel == sg.SG_KERNEL_GEMV and p.split_k == 1 and p.tile_n == 1
