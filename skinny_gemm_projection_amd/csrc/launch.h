@@ -42,11 +42,13 @@ int rowdot_grid(int M, int N, int K, int S, int k_chunk, bool two_pass);
 // Team kernel: S waves (S in {1,2,4,8}) of one workgroup split K over a
 // 16-row tile and add their partials in LDS; grid ceil(N/16).
 constexpr int kMfmaTeamTileN = 16;
-// From this many rows (and up to 16 batch rows) each wave of the team kernel
-// takes two 16-row tiles, sharing every x operand read between them.
+// From this many rows, 12 to 16 batch rows and a row pitch that is not a
+// multiple of 8 KB, each wave of the team kernel takes two 16-row tiles,
+// sharing every x operand read between them.
 constexpr int kMfmaTeamTwoTilesFromN = 8161;
-int mfma_team_tiles_per_wave(int M, int N);
-int mfma_team_grid(int M, int N);  // workgroups of the team kernel's launch
+constexpr int kMfmaTeamTwoTilesFromM = 12;
+int mfma_team_tiles_per_wave(int M, int N, int K);
+int mfma_team_grid(int M, int N, int K);  // workgroups of the team kernel's launch
 bool mfma_team_split_ok(int S);
 hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void* x,
                             const void* W, const Epilogue& ep, hipStream_t stream);

@@ -41,11 +41,21 @@ constexpr int kComputeUnits = 256;
 // kernel, which needs no second pass, is faster (M=4: 12.8 against 13.8).
 constexpr int32_t kMfmaFromM = 8;
 constexpr int32_t kTeamUpToM = 16;
-// From 6 rows the matrix-core team kernel already beats the vector-ALU
-// kernel where its grid of N/16 workgroups fills the compute units
-// (interleaved A/B at K=7168, N=4096: M=6 12.3 against 12.9 us with 4 K
-// chunks, M=7 12.4 against 13.4 us; M=5 12.3 against 11.9 us).
-constexpr int32_t kTeamFromM = 6;
+// Where its grid of N/16 workgroups fills the compute units, the matrix-core
+// team kernel beats the vector-ALU kernels from 3 rows for 4096 <= K <= 8192
+// (at most 8 rounds a wave, every round unrolled).  Interleaved A/B on
+// MI355X, team against the vector-ALU plan: 4096x7168 M = 3 / 4 / 5 10.83 /
+// 10.87 / 10.87 against 11.02 / 11.39 / 12.01 us, 8192x7168 19.26 / 19.20 /
+// 19.18 against 19.53 / 20.72 / 21.00 us, 4096x4096 M = 3 7.15 against 7.61
+// us.  Outside that range it starts at 6 rows: with longer K (the loop form)
+// it lost at 5 rows (4096x7168 before the unrolling: M = 6 12.3 against
+// 12.9 us, M = 5 12.3 against 11.9 us), and at short K the streaming kernel
+// stays ahead up to 5 rows (4096x2048: M = 3 / 5 5.19 / 5.76 against 5.98 /
+// 6.01 us).
+constexpr int32_t kTeamFromM = 3;
+constexpr int32_t kTeamFromMOtherK = 6;
+constexpr int32_t kTeamFromMMinK = 4096;
+constexpr int32_t kTeamFromMMaxK = 8192;
 
 // Choices measured on MI355X for known projection shapes, overriding the
 // defaults: {M_lo, M_hi, N, K, kernel (0: default), split (0: default),
@@ -294,7 +304,9 @@ sg_status make_plan_impl(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_
 
     if (kernel <= 0) {
         const bool team_fills = (N + kMfmaTeamTileN - 1) / kMfmaTeamTileN >= kComputeUnits;
-        const int32_t mfma_from = team_fills ? kTeamFromM : kMfmaFromM;
+        const bool team_k = K >= kTeamFromMMinK && K <= kTeamFromMMaxK;
+        const int32_t mfma_from =
+            team_fills ? (team_k ? kTeamFromM : kTeamFromMOtherK) : kMfmaFromM;
         kernel = M <= 2 ? SG_KERNEL_GEMV
                         : (M < mfma_from ? SG_KERNEL_SPLITK_VALU : SG_KERNEL_SPLITK_MFMA);
         if (const Tuned* t = use_tuned ? tuned_for(M, N, K) : nullptr) {
@@ -370,7 +382,7 @@ sg_status make_plan_impl(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_
             if (!mfma_team_split_ok(split_k)) return SG_ERR_PLAN;
             p.k_chunk = chunk_of(K, split_k);
             p.tile_n = kMfmaTeamTileN;
-            p.grid = mfma_team_grid(M, N);
+            p.grid = mfma_team_grid(M, N, K);
             two_pass = 0;
             break;
         }

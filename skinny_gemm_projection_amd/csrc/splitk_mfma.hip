@@ -281,8 +281,11 @@ __global__ __launch_bounds__(kChunkThreads) void splitk_mfma_kernel(
 // each x operand read serves both tiles.  There is no barrier in the main
 // loop.  At the end the S partial tiles are added in LDS in ascending split
 // order (deterministic) and wave w finishes the outputs o with o % S == w:
-// no workspace and no second kernel.
-template <int MT, int S, int DR, int NT>
+// no workspace and no second kernel.  ROUNDS > 0 (at least the rounds of
+// any wave's chunk) unrolls every round: behind the loop header the compiler
+// waited for every load in flight (the prologue and the loop body filled the
+// round buffers in different registers), so each trip drained the stream.
+template <int MT, int S, int DR, int NT, int ROUNDS>
 __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __restrict__ x,
                                                               const uint4* __restrict__ W, int M,
                                                               int N, int K8, int chunk8,
@@ -370,43 +373,53 @@ __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __res
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int r0 = 0; r0 < rounds; r0 += DR) {
+    // One round: the weights (and x) of round rd into the wave's LDS tiles,
+    // its 4 k steps, then the loads of round rd + DR into the freed
+    // registers (past the chunk: no memory access).
+    auto round_step = [&](int rd, uint4 (&w)[NT][4], uint4 (&a)[4][MT]) {
 #pragma unroll
-        for (int d = 0; d < DR; ++d) {
-            const int rd = r0 + d;
-            if (rd < rounds) {  // wave-uniform
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+            for (int nt = 0; nt < NT; ++nt) tiles[s][nt][(4 * i + grp) * RP + col] = w[nt][i];
+            if constexpr (XT) {
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        tiles[s][nt][(4 * i + grp) * RP + col] = wb[d][nt][i];
-                    if constexpr (XT) {
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
-                            xtiles[s][mt][(4 * i + grp) * RP + col] = xb[d][i][mt];
-                    }
-                }
-                __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int slot = col * RP + ((4 * t + grp) ^ col);
-                    uint4 b[NT];
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) b[nt] = tiles[s][nt][slot];
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const uint4 a = XT ? xtiles[XT ? s : 0][XT ? mt : 0][XT ? slot : 0]
-                                           : xb[d][t][mt];
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt)
-                            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[nt]),
-                                acc[nt][mt], 0, 0, 0);
-                    }
-                }
-                __builtin_amdgcn_wave_barrier();
+                for (int mt = 0; mt < MT; ++mt)
+                    xtiles[s][mt][(4 * i + grp) * RP + col] = a[i][mt];
             }
-            load_round(rd + DR, wb[d], xb[d]);  // past the chunk: no memory access
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int slot = col * RP + ((4 * t + grp) ^ col);
+            uint4 b[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) b[nt] = tiles[s][nt][slot];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint4 av = XT ? xtiles[XT ? s : 0][XT ? mt : 0][XT ? slot : 0] : a[t][mt];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, b[nt]),
+                        acc[nt][mt], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (ROUNDS == 0 || rd + DR < ROUNDS) load_round(rd + DR, w, a);
+        // keeps the next round's LDS copy below these loads, so that it
+        // waits for its own round only
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (ROUNDS > 0) {
+#pragma unroll
+        for (int rd = 0; rd < ROUNDS; ++rd) round_step(rd, wb[rd % DR], xb[rd % DR]);
+    } else {
+        // rounds padded to whole multiples of DR: a padded round reads zero
+        // and adds exactly 0
+        const int rounds_p = (rounds + DR - 1) / DR * DR;
+        for (int r0 = 0; r0 < rounds_p; r0 += DR) {
+#pragma unroll
+            for (int d = 0; d < DR; ++d) round_step(r0 + d, wb[d], xb[d]);
         }
     }
 
@@ -447,161 +460,59 @@ __global__ __launch_bounds__(kWave * S) void mfma_team_kernel(const uint4* __res
     }
 }
 
-// Team kernel for one x row tile (M <= 16) with x in registers: each wave
-// loads the A operands of its whole K chunk once (ROUNDS rounds of 4 steps,
-// 16 bytes a lane and step) instead of reading them from L2 every round, so
-// the main loop carries only the weight loads and their LDS transpose.  The
-// rounds are unrolled (the operands are indexed by step at compile time,
-// and each wait is for exactly the round it needs); the weights go as in
-// mfma_team_kernel, NT tiles a wave, DR rounds in flight.
-template <int S, int NT, int ROUNDS>
-__global__ __launch_bounds__(kWave * S) void mfma_team_xr_kernel(const uint4* __restrict__ x,
-                                                                 const uint4* __restrict__ W,
-                                                                 int M, int N, int K8,
-                                                                 int chunk8, Epilogue ep) {
-    constexpr int DR = 2;
-    constexpr int RP = 16;
-    constexpr uint32_t kOff = 0xFFFFFFF0u;
-    __shared__ uint4 tiles[S][NT][kTileSlots];
-    __shared__ float red[S][NT * 4][kWave];
-
-    const int lane = threadIdx.x & (kWave - 1);
-    const int s = wave_id_in_block();
-    const int col = lane & 15;
-    const int grp = lane >> 4;
-    const int row0 = blockIdx.x * 16 * NT;
-    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16 * NT, N - row0)));
-    const int k0 = s * chunk8;
-    const int len = max(0, min(K8 - k0, chunk8));
-
-    // A operand of step t of round rd: x[col][k0 + 16 rd + 4 t + grp] (zero
-    // past M or past the chunk)
-    const rsrc_t xrs = make_rsrc(x, (uint32_t)M * (uint32_t)K8 * 16u);
-    uint4 xa[ROUNDS][4];
-#pragma unroll
-    for (int rd = 0; rd < ROUNDS; ++rd)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int piece = RP * rd + 4 * t + grp;
-            const bool ok = col < M && piece < len;
-            xa[rd][t] = load16<kCached>(xrs, ok ? ((uint32_t)col * K8 + k0 + piece) * 16u : kOff);
-        }
-
-    const rsrc_t wrs = make_rsrc(W + (int64_t)row0 * K8, (uint32_t)rows * (uint32_t)K8 * 16u);
-    uint32_t woff[NT][4];
-    int wpiece[4];
-    bool wrow[NT][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wpiece[i] = col ^ (4 * i + grp);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * nt + 4 * i + grp;
-            wrow[nt][i] = r < rows;
-            woff[nt][i] = ((uint32_t)r * K8 + k0 + wpiece[i]) * 16u;
-        }
-    auto load_round = [&](int rd, uint4 (&w)[NT][4]) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = rd < ROUNDS && wrow[nt][i] && (rd * RP + wpiece[i] < len);
-                w[nt][i] =
-                    load16<kStream>(wrs, ok ? woff[nt][i] + (uint32_t)rd * (RP * 16u) : kOff);
-            }
-    };
-    uint4 wb[DR][NT][4];
-#pragma unroll
-    for (int d = 0; d < DR; ++d) load_round(d, wb[d]);
-    f32x4_t acc[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int rd = 0; rd < ROUNDS; ++rd) {
-        const int d = rd % DR;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) tiles[s][nt][(4 * i + grp) * RP + col] = wb[d][nt][i];
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int slot = col * RP + ((4 * t + grp) ^ col);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, xa[rd][t]),
-                    __builtin_bit_cast(bf16x8_t, tiles[s][nt][slot]), acc[nt], 0, 0, 0);
-        }
-        __builtin_amdgcn_wave_barrier();
-        if (rd + DR < ROUNDS) load_round(rd + DR, wb[d]);
-    }
-
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) red[s][nt * 4 + v][lane] = acc[nt][v];
-    __syncthreads();
-#pragma unroll
-    for (int o = 0; o < NT * 4; ++o) {
-        if (o % S != s) continue;
-        const int nt = o / 4;
-        const int r = 16 * nt + col;
-        if (r >= rows) continue;
-        float sum = red[0][o][lane];
-#pragma unroll
-        for (int q = 1; q < S; ++q) sum += red[q][o][lane];
-        const int m = grp * 4 + (o % 4);
-        if (m < M) store_final(ep, (int64_t)m * N + row0 + r, sum);
-    }
-}
-
 }  // namespace
 
 bool mfma_team_split_ok(int S) { return S == 1 || S == 2 || S == 4 || S == 8; }
 
-int mfma_team_tiles_per_wave(int M, int N) {
-    return M <= 16 && N >= kMfmaTeamTwoTilesFromN ? 2 : 1;
+// Two tiles a wave (sharing each x operand read) measured faster only from 12
+// rows, and slower by 18-49 % at every M when the row pitch is a multiple of
+// 8 KB (K a multiple of 4096).  Interleaved A/B on MI355X, two tiles against
+// one: 8192x7168 M = 4 / 8 / 16 20.37 / 19.43 / 20.45 against 20.21 / 19.24
+// / 21.87 us; 16384x5120 M = 16 29.3 against 31.1; 8192x4096 M = 8 17.58
+// against 12.09; 8192x8192 M = 16 28.07 against 23.83.
+int mfma_team_tiles_per_wave(int M, int N, int K) {
+    return M >= kMfmaTeamTwoTilesFromM && M <= 16 && N >= kMfmaTeamTwoTilesFromN &&
+                   K % 4096 != 0
+               ? 2
+               : 1;
 }
 
-int mfma_team_grid(int M, int N) {
-    const int rows = 16 * mfma_team_tiles_per_wave(M, N);
+int mfma_team_grid(int M, int N, int K) {
+    const int rows = 16 * mfma_team_tiles_per_wave(M, N, K);
     return (N + rows - 1) / rows;
 }
 
 hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void* x,
                             const void* W, const Epilogue& ep, hipStream_t stream) {
-    const int grid = mfma_team_grid(M, N);
-    const int NT = mfma_team_tiles_per_wave(M, N);
+    const int grid = mfma_team_grid(M, N, K);
+    const int NT = mfma_team_tiles_per_wave(M, N, K);
     const int K8 = K / kPiece;
     const int chunk8 = k_chunk / kPiece;
     const uint4* xp = static_cast<const uint4*>(x);
     const uint4* wp = static_cast<const uint4*>(W);
     const int MT = (M + 15) / 16;
     // rounds in flight per wave; measured on MI355X, 3 or 4 were slower (K=7168,
-    // N=4096, M=8: 12.4 us at 2, 14.4 at 3, 15.0 at 4)
+    // N=4096, M=8: 12.4 us at 2, 14.4 at 3, 15.0 at 4, in the loop form)
     constexpr int DR = 2;
-    // Two tiles a wave, up to 8 rows, 8 waves, 7 or 8 rounds a wave (K = 7168
-    // or 8192): x in registers.  Measured on MI355X (interleaved A/B),
-    // 8192x7168: M = 6 / 8 21.8 / 21.8 -> 20.9 / 21.3 us; but slower with one
-    // tile a wave (4096x7168 M = 8 / 16 12.4 / 13.5 -> 12.9 / 15.3 us;
-    // 7168x8192 M = 8 22.5 -> 27.0 us) and from 12 rows (8192x7168 M = 16
-    // 22.3 -> 23.2 us): the up-front x loads (scattered 64-byte pieces)
-    // delay the weight stream and the registers cost occupancy.
+    // Up to 8 rounds a wave (K <= 8192 over 8 waves): every round unrolled.
+    // Measured on MI355X (interleaved A/B against the loop): 4096x7168 M = 8
+    // / 16 12.34 / 13.52 -> 10.92 / 12.19 us, 8192x7168 21.21 / 22.14 ->
+    // 19.13 / 20.33 us, 7168x8192 22.53 / 24.16 -> 20.13 / 22.70 us.  3 or 4
+    // rounds in flight stayed slower (8192x7168 M = 8: 19.4 / 19.9 us).
     const int rounds = (chunk8 + 15) / 16;
-    if (MT == 1 && M <= 8 && NT == 2 && S == 8 && (rounds == 7 || rounds == 8)) {
-#define SG_XR(nt, r) \
-    if (NT == nt && rounds == r) { \
-        mfma_team_xr_kernel<8, nt, r><<<grid, kWave * 8, 0, stream>>>(xp, wp, M, N, K8, chunk8, ep); \
+#define SG_TEAM_R(nt, r) \
+    if (MT == 1 && S == 8 && NT == nt && rounds == r) { \
+        mfma_team_kernel<1, 8, DR, nt, r><<<grid, kWave * 8, 0, stream>>>(xp, wp, M, N, K8, chunk8, ep); \
         return hipGetLastError(); \
     }
-        SG_XR(2, 7) SG_XR(2, 8)
-#undef SG_XR
-    }
+    SG_TEAM_R(1, 1) SG_TEAM_R(1, 2) SG_TEAM_R(1, 3) SG_TEAM_R(1, 4)
+    SG_TEAM_R(1, 5) SG_TEAM_R(1, 6) SG_TEAM_R(1, 7) SG_TEAM_R(1, 8)
+    SG_TEAM_R(2, 1) SG_TEAM_R(2, 2) SG_TEAM_R(2, 3) SG_TEAM_R(2, 4)
+    SG_TEAM_R(2, 5) SG_TEAM_R(2, 6) SG_TEAM_R(2, 7) SG_TEAM_R(2, 8)
+#undef SG_TEAM_R
 #define SG_TEAM(mt, sp, nt) \
     if (MT == mt && S == sp && NT == nt) { \
-        mfma_team_kernel<mt, sp, DR, nt><<<grid, kWave * sp, 0, stream>>>(xp, wp, M, N, K8, chunk8, ep); \
+        mfma_team_kernel<mt, sp, DR, nt, 0><<<grid, kWave * sp, 0, stream>>>(xp, wp, M, N, K8, chunk8, ep); \
         return hipGetLastError(); \
     }
     SG_TEAM(1, 1, 1) SG_TEAM(1, 2, 1) SG_TEAM(1, 4, 1) SG_TEAM(1, 8, 1)

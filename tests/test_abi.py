@@ -68,11 +68,17 @@ def test_status_strings():
 def test_plan_kernel_by_batch():
     for M in range(1, 65):
         p = sg.skinny_gemm_plan(M, 4096, 7168)
-        # the team kernel's 256 workgroups fill the GPU at N = 4096: matrix cores from M = 6
-        want = (sg.SG_KERNEL_GEMV if M <= 2 else
-                sg.SG_KERNEL_SPLITK_VALU if M < 6 else sg.SG_KERNEL_SPLITK_MFMA)
+        # the team kernel's 256 workgroups fill the GPU at N = 4096: matrix cores from M = 3
+        want = sg.SG_KERNEL_GEMV if M <= 2 else sg.SG_KERNEL_SPLITK_MFMA
         assert p.kernel == want, (M, p)
         assert (p.M, p.N, p.K) == (M, 4096, 7168)
+    # past K = 8192 (more than 8 rounds a wave: the team kernel's loop form) and below
+    # K = 4096 (the streaming kernel ahead) from M = 6
+    for K in (16384, 2048):
+        for M in range(3, 9):
+            p = sg.skinny_gemm_plan(M, 4096, K)
+            want = sg.SG_KERNEL_SPLITK_VALU if M < 6 else sg.SG_KERNEL_SPLITK_MFMA
+            assert p.kernel == want, (M, K, p)
 
 
 def test_plan_kernel_by_batch_few_rows():
@@ -85,19 +91,22 @@ def test_plan_kernel_by_batch_few_rows():
 
 def test_plan_team_or_chunk_by_width():
     # 8..16 rows on matrix cores: the team kernel (16-row tiles, one pass) while N/16 tiles
-    # fill the CUs (two tiles a wave from N = 8161, so its grid is N/32); the chunk kernel
-    # (128/256-row tiles, second pass) below that width and from 17 rows
-    for M, N, team, grid in [(8, 4096, True, 256), (16, 4096, True, 256), (8, 8192, True, 256),
-                             (11, 8192, True, 256), (12, 8192, True, 256),
-                             (16, 8192, True, 256), (16, 7168, True, 448),
-                             (16, 8160, True, 510), (16, 8161, True, 256),
-                             (16, 16384, True, 512), (16, 2048, False, None),
-                             (17, 4096, False, None)]:
-        p = sg.skinny_gemm_plan(M, N, 7168)
-        assert p.kernel == sg.SG_KERNEL_SPLITK_MFMA, (M, N, p)
-        assert (p.tile_n == 16 and not p.two_pass) == team, (M, N, p)
+    # fill the CUs (two tiles a wave from N = 8161 and M = 12, so its grid is N/32, unless
+    # K is a multiple of 4096); the chunk kernel (128/256-row tiles, second pass) below
+    # that width and from 17 rows
+    for M, N, K, team, grid in [(8, 4096, 7168, True, 256), (16, 4096, 7168, True, 256),
+                                (8, 8192, 7168, True, 512), (11, 8192, 7168, True, 512),
+                                (12, 8192, 7168, True, 256), (16, 8192, 7168, True, 256),
+                                (16, 7168, 7168, True, 448), (16, 8160, 7168, True, 510),
+                                (16, 8161, 7168, True, 256), (16, 16384, 7168, True, 512),
+                                (16, 8192, 8192, True, 512), (12, 8192, 4096, True, 512),
+                                (16, 8192, 6144, True, 256), (16, 2048, 7168, False, None),
+                                (17, 4096, 7168, False, None)]:
+        p = sg.skinny_gemm_plan(M, N, K)
+        assert p.kernel == sg.SG_KERNEL_SPLITK_MFMA, (M, N, K, p)
+        assert (p.tile_n == 16 and not p.two_pass) == team, (M, N, K, p)
         if team:
-            assert p.grid == grid, (M, N, p)
+            assert p.grid == grid, (M, N, K, p)
 
 
 def test_plan_rejects():

@@ -74,10 +74,10 @@ SMALL = [
     (48, 1000, 1056), (63, 200, 264), (64, 1000, 1056),
     # wide matrices: the team kernel with two 16-row tiles a wave (ragged last pair)
     (9, 8161, 520), (12, 8200, 1040), (16, 8177, 264), (13, 9000, 2056),
-    # ... and with x in registers (up to 8 rows, K = 7168 or 8192)
-    (7, 8300, 8192), (8, 8161, 7168),
-    # the streaming vector-ALU kernel with teams: M = 3, 4, 2 to 8 rows a team
-    (3, 2101, 4104), (4, 4097, 2056), (4, 6000, 8192), (4, 3000, 7168),
+    # ... with every round unrolled (K <= 8192), from 3 rows where N/16 >= 256
+    (7, 8300, 8192), (8, 8161, 7168), (3, 4097, 2056), (5, 4200, 6152), (4, 6000, 8192),
+    # the streaming vector-ALU kernel with teams (N/16 < 256): M = 3, 4, 2 to 8 rows a team
+    (3, 2101, 4104), (4, 4000, 4104), (4, 3500, 8192), (4, 3000, 7168),
 ]
 
 
