@@ -74,7 +74,7 @@ constexpr int kXLoadsMax = 16;  // x staging loads per thread and phase
 // alternate -- x of the next phase is loaded into registers while the
 // current phase is multiplied, written to the other buffer at its end, and
 // one barrier per phase publishes it.
-template <int MT, int NT, int DR, bool PHASED>
+template <int MT, int NT, int DR, bool PHASED, int ROUNDS>
 __global__ __launch_bounds__(kChunkThreads) void splitk_mfma_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ W, int M, int N, int K8, int chunk8,
     int phase, Epilogue ep) {
@@ -196,45 +196,62 @@ __global__ __launch_bounds__(kChunkThreads) void splitk_mfma_kernel(
             const int r = 16 * nt + col;
             bslot[nt][t] = r * RP + ((4 * t + grp) ^ G::swz(r));
         }
-    for (int r0 = 0; r0 < rounds; r0 += DR) {
+    // One round: the weights of round rd into the wave's LDS tile, its k
+    // steps against the staged x, then the loads of round rd + DR into the
+    // freed registers (past the chunk: no memory access).
+    auto round_step = [&](int rd, uint4 (&w)[4]) {
+        const int ph = PHASED ? rd / pr : 0;
+        const int rin = rd - ph * pr;  // round within the phase
+        const bool next = PHASED && ph + 1 < nphases;
+        if (next && rin == 0) load_x(ph + 1);
+        // Within one wave LDS operations run in order, so the tile can be
+        // rewritten right after the previous round's reads.
 #pragma unroll
-        for (int d = 0; d < DR; ++d) {
-            const int rd = r0 + d;
-            if (rd < rounds) {  // workgroup-uniform
-                const int ph = PHASED ? rd / pr : 0;
-                const int rin = rd - ph * pr;  // round within the phase
-                const bool next = PHASED && ph + 1 < nphases;
-                if (next && rin == 0) load_x(ph + 1);
-                // Within one wave LDS operations run in order, so the tile can
-                // be rewritten right after the previous round's reads.
+        for (int i = 0; i < 4; ++i) tile[(i * G::kRowsPerLoad + lrow) * RP + lslot] = w[i];
+        __builtin_amdgcn_wave_barrier();
+        const uint4* xb = xs + (ph & 1) * xslots + rin * RP;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    tile[(i * G::kRowsPerLoad + lrow) * RP + lslot] = wb[d][i];
-                __builtin_amdgcn_wave_barrier();
-                const uint4* xb = xs + (ph & 1) * xslots + rin * RP;
+        for (int t = 0; t < G::kSteps; ++t) {
+            const int p = 4 * t + grp;
+            uint4 a[MT];
 #pragma unroll
-                for (int t = 0; t < G::kSteps; ++t) {
-                    const int p = 4 * t + grp;
-                    uint4 a[MT];
+            for (int mt = 0; mt < MT; ++mt) a[mt] = xb[(mt * 16 + col) * xp + p];
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) a[mt] = xb[(mt * 16 + col) * xp + p];
+            for (int nt = 0; nt < NT; ++nt) {
+                const uint4 b = tile[bslot[nt][t]];
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        const uint4 b = tile[bslot[nt][t]];
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, a[mt]), __builtin_bit_cast(bf16x8_t, b),
+                        acc[nt][mt], 0, 0, 0);
+            }
+        }
+        if (ROUNDS == 0 || rd + DR < ROUNDS) load_round(rd + DR, w);
+        if (next && (rin == pr - 1)) {
+            // The other buffer was last read in phase ph - 1, which every wave
+            // finished before the previous phase barrier.
+            store_x((ph + 1) & 1);
+            __syncthreads();
+        }
+        // (unrolled) keeps the next round's LDS copy below these loads, so
+        // that it waits for its own round only
+        if constexpr (ROUNDS > 0) __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (ROUNDS > 0) {
+        // One x phase of ROUNDS * RP pieces a row (zeros past the chunk): a
+        // round past a shorter last chunk reads zero x and zero weights and
+        // adds exactly 0, so no round is guarded and every round is unrolled.
+        // Behind the loop header below the compiler waited for every load in
+        // flight at the top of each trip.
+        static_assert(!PHASED, "unrolled rounds need the whole chunk of x staged");
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
-                            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8_t, a[mt]), __builtin_bit_cast(bf16x8_t, b),
-                                acc[nt][mt], 0, 0, 0);
-                    }
-                }
-                load_round(rd + DR, wb[d]);  // past the chunk: no memory access
-                if (next && (rin == pr - 1)) {
-                    // The other buffer was last read in phase ph - 1, which
-                    // every wave finished before the previous phase barrier.
-                    store_x((ph + 1) & 1);
-                    __syncthreads();
-                }
+        for (int rd = 0; rd < ROUNDS; ++rd) round_step(rd, wb[rd % DR]);
+    } else {
+        for (int r0 = 0; r0 < rounds; r0 += DR) {
+#pragma unroll
+            for (int d = 0; d < DR; ++d) {
+                const int rd = r0 + d;
+                if (rd < rounds) round_step(rd, wb[d]);  // workgroup-uniform
             }
         }
     }
@@ -500,15 +517,15 @@ hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void*
     // 19.13 / 20.33 us, 7168x8192 22.53 / 24.16 -> 20.13 / 22.70 us.  3 or 4
     // rounds in flight stayed slower (8192x7168 M = 8: 19.4 / 19.9 us).
     const int rounds = (chunk8 + 15) / 16;
-#define SG_TEAM_R(nt, r) \
-    if (MT == 1 && S == 8 && NT == nt && rounds == r) { \
-        mfma_team_kernel<1, 8, DR, nt, r><<<grid, kWave * 8, 0, stream>>>(xp, wp, M, N, K8, chunk8, ep); \
+#define SG_TEAM_R(mt, nt, r) \
+    if (MT == mt && S == 8 && NT == nt && rounds == r) { \
+        mfma_team_kernel<mt, 8, DR, nt, r><<<grid, kWave * 8, 0, stream>>>(xp, wp, M, N, K8, chunk8, ep); \
         return hipGetLastError(); \
     }
-    SG_TEAM_R(1, 1) SG_TEAM_R(1, 2) SG_TEAM_R(1, 3) SG_TEAM_R(1, 4)
-    SG_TEAM_R(1, 5) SG_TEAM_R(1, 6) SG_TEAM_R(1, 7) SG_TEAM_R(1, 8)
-    SG_TEAM_R(2, 1) SG_TEAM_R(2, 2) SG_TEAM_R(2, 3) SG_TEAM_R(2, 4)
-    SG_TEAM_R(2, 5) SG_TEAM_R(2, 6) SG_TEAM_R(2, 7) SG_TEAM_R(2, 8)
+    SG_TEAM_R(1, 1, 1) SG_TEAM_R(1, 1, 2) SG_TEAM_R(1, 1, 3) SG_TEAM_R(1, 1, 4)
+    SG_TEAM_R(1, 1, 5) SG_TEAM_R(1, 1, 6) SG_TEAM_R(1, 1, 7) SG_TEAM_R(1, 1, 8)
+    SG_TEAM_R(1, 2, 1) SG_TEAM_R(1, 2, 2) SG_TEAM_R(1, 2, 3) SG_TEAM_R(1, 2, 4)
+    SG_TEAM_R(1, 2, 5) SG_TEAM_R(1, 2, 6) SG_TEAM_R(1, 2, 7) SG_TEAM_R(1, 2, 8)
 #undef SG_TEAM_R
 #define SG_TEAM(mt, sp, nt) \
     if (MT == mt && S == sp && NT == nt) { \
@@ -574,17 +591,42 @@ hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk, int tile_
     const size_t lds = mfma_chunk_lds_bytes(M, k_chunk, tile_n);
     if (phase == 0 || lds > kMfmaMaxLds) return hipErrorInvalidValue;
     // weight rounds in flight per wave (8 loads); 3 or 4 measured slower on
-    // MI355X (K=7168, N=4096, M=64: 18.5 us at 2, 18.8 at 3, 19.6 at 4)
+    // MI355X (K=7168, N=4096, M=64: 18.5 us at 2, 18.8 at 3, 19.6 at 4; with
+    // every round unrolled 17.0 / 17.0 / 18.4 us)
     constexpr int DR = 2;
     const int whole = (chunk8 + 16 / NT - 1) / (16 / NT) * (16 / NT);
     const bool phased = phase < whole;
+    // One x phase and 4 to 8 rounds (128-row tiles) or 14 / 16 rounds
+    // (256-row tiles, K = 7168 or 8192 over 8 splits): every round unrolled.
+    // Interleaved A/B on MI355X against the loop: 4096x7168 M = 17 / 32 / 64
+    // 14.98 / 15.11 / 18.23 -> 14.07 / 14.18 / 17.00 us, 8192x7168 M = 64
+    // 30.33 -> 28.96 us.
+    const int rounds = whole / (16 / NT);
+#define SG_CHUNK_R(mt, nt, r) \
+    if (MT == mt && NT == nt && !phased && rounds == r) { \
+        hipError_t e = hipFuncSetAttribute( \
+            reinterpret_cast<const void*>(&splitk_mfma_kernel<mt, nt, DR, false, r>), \
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+        if (e != hipSuccess) return e; \
+        splitk_mfma_kernel<mt, nt, DR, false, r><<<grid, kChunkThreads, lds, stream>>>( \
+            xp, wp, M, N, K8, chunk8, phase, ep); \
+        return hipGetLastError(); \
+    }
+    SG_CHUNK_R(1, 1, 4) SG_CHUNK_R(2, 1, 4) SG_CHUNK_R(3, 1, 4) SG_CHUNK_R(4, 1, 4)
+    SG_CHUNK_R(1, 1, 5) SG_CHUNK_R(2, 1, 5) SG_CHUNK_R(3, 1, 5) SG_CHUNK_R(4, 1, 5)
+    SG_CHUNK_R(1, 1, 6) SG_CHUNK_R(2, 1, 6) SG_CHUNK_R(3, 1, 6) SG_CHUNK_R(4, 1, 6)
+    SG_CHUNK_R(1, 1, 7) SG_CHUNK_R(2, 1, 7) SG_CHUNK_R(3, 1, 7) SG_CHUNK_R(4, 1, 7)
+    SG_CHUNK_R(1, 1, 8) SG_CHUNK_R(2, 1, 8) SG_CHUNK_R(3, 1, 8) SG_CHUNK_R(4, 1, 8)
+    SG_CHUNK_R(1, 2, 14) SG_CHUNK_R(2, 2, 14) SG_CHUNK_R(3, 2, 14) SG_CHUNK_R(4, 2, 14)
+    SG_CHUNK_R(1, 2, 16) SG_CHUNK_R(2, 2, 16) SG_CHUNK_R(3, 2, 16) SG_CHUNK_R(4, 2, 16)
+#undef SG_CHUNK_R
 #define SG_CHUNK(mt, nt, ph) \
     if (MT == mt && NT == nt && phased == ph) { \
         hipError_t e = hipFuncSetAttribute( \
-            reinterpret_cast<const void*>(&splitk_mfma_kernel<mt, nt, DR, ph>), \
+            reinterpret_cast<const void*>(&splitk_mfma_kernel<mt, nt, DR, ph, 0>), \
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
         if (e != hipSuccess) return e; \
-        splitk_mfma_kernel<mt, nt, DR, ph><<<grid, kChunkThreads, lds, stream>>>( \
+        splitk_mfma_kernel<mt, nt, DR, ph, 0><<<grid, kChunkThreads, lds, stream>>>( \
             xp, wp, M, N, K8, chunk8, phase, ep); \
         return hipGetLastError(); \
     }

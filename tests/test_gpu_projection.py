@@ -78,6 +78,9 @@ SMALL = [
     (7, 8300, 8192), (8, 8161, 7168), (3, 4097, 2056), (5, 4200, 6152), (4, 6000, 8192),
     # the streaming vector-ALU kernel with teams (N/16 < 256): M = 3, 4, 2 to 8 rows a team
     (3, 2101, 4104), (4, 4000, 4104), (4, 3500, 8192), (4, 3000, 7168),
+    # the chunk kernel with every round unrolled (one x phase), short last chunks:
+    # 5 and 8 rounds of 128-row tiles, 16 rounds of 256-row tiles
+    (20, 1000, 7000), (24, 4500, 6984), (48, 700, 8192), (40, 9000, 7000),
 ]
 
 
