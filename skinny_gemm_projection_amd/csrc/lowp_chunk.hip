@@ -37,6 +37,7 @@ constexpr int kLpThreads = kWave * kLpWaves;
 constexpr int kLpWindow = 128;              // elements per window (one FP8 scale block)
 constexpr int kLpXLoads = 16;               // x staging loads per thread (at most)
 constexpr uint32_t kLpOut = 0xFFFFFFF0u;    // past any descriptor range: reads zero
+constexpr int kLpPadSlots = kWave;          // LDS slots past the x rows (whole-chunk copy)
 
 // e8m0 scale code -> 2^(s-127): the exponent field for 1..254, the fp32
 // subnormal 2^-127 for 0, NaN for 255.
@@ -44,12 +45,15 @@ __device__ __forceinline__ float lp_e8m0(uint32_t s) {
     return as_f(s == 0u ? 0x00400000u : s == 255u ? 0x7FC00000u : s << 23);
 }
 
-template <int FMT, int MT, int NT, int D>
+template <int FMT, int MT, int NT, int D, bool ALL>
 __global__ __launch_bounds__(kLpThreads) void lowp_chunk_kernel(
     const uint4* __restrict__ x, const uint8_t* __restrict__ Wq, const void* __restrict__ Ws,
     int M, int N, int K, int chunk, int pitch, Epilogue ep) {
     constexpr bool kFp8 = FMT == kLowpFp8;
+    // ALL: the wave's whole chunk (at most D windows) is one batch, requested
+    // behind x and consumed with no loop (FP8, one 16-row tile a wave).
     constexpr bool kHoist = kFp8 && MT <= 2;
+    static_assert(!ALL || kHoist, "the whole-chunk batch is requested behind x");
     constexpr int XR = 16 * MT;
     extern __shared__ uint4 xs[];  // [XR][pitch] pieces of the chunk's x rows
 
@@ -125,24 +129,51 @@ __global__ __launch_bounds__(kLpThreads) void lowp_chunk_kernel(
         const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K8 * 16u);
         const int P8 = chunk / kPiece;
         const int total = XR * P8;
-        uint4 v[kLpXLoads];
+        if constexpr (ALL) {
+            // A chunk of at most D = 8 windows (1024 elements): 4 * MT loads a
+            // thread.  The copy has no branch (slots past the chunk's x go to
+            // a padding slot per lane after the rows), its slots come from a
+            // 24-bit product (with the 64-bit multiply-add the compiler chose,
+            // the unused high half of its addend was a register a code load
+            // writes, and the copy waited for that load), and scheduling
+            // barriers keep the x loads ahead of the code loads.
+            constexpr int XL = 4 * MT;
+            uint4 v[XL];
+            int dst[XL];
 #pragma unroll
-        for (int j = 0; j < kLpXLoads; ++j) {
-            const int idx = tid + j * kLpThreads;
-            const int r = idx / P8, p = idx - r * P8;
-            const bool ok = idx < total && r < M && p * kPiece < len;
-            v[j] = load16<kCached>(rx, ok ? ((uint32_t)r * K8 + k0 / kPiece + p) * 16u : kLpOut);
-        }
-        // FP8 up to 32 rows: the first windows' codes are requested right
-        // behind x (only the x loads are waited for before the LDS copy and
-        // the barrier).  Measured on MI355X this pays there (4096 x 7168,
-        // M = 16: 12.1 -> 11.5 us) and loses at 64 rows and for MXFP4.
-        if constexpr (kHoist) load_batch(first, 0);
+            for (int j = 0; j < XL; ++j) {
+                const int idx = tid + j * kLpThreads;
+                const int r = idx / P8, p = idx - r * P8;
+                const bool ok = idx < total && r < M && p * kPiece < len;
+                v[j] = load16<kCached>(rx, ok ? ((uint32_t)r * K8 + k0 / kPiece + p) * 16u : kLpOut);
+                dst[j] = idx < total ? (int)__umul24((unsigned)r, (unsigned)pitch) + p
+                                     : XR * pitch + lane;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load_batch(first, 0);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < kLpXLoads; ++j) {
-            const int idx = tid + j * kLpThreads;
-            const int r = idx / P8, p = idx - r * P8;
-            if (idx < total) xs[r * pitch + p] = v[j];
+            for (int j = 0; j < XL; ++j) xs[dst[j]] = v[j];
+        } else {
+            uint4 v[kLpXLoads];
+#pragma unroll
+            for (int j = 0; j < kLpXLoads; ++j) {
+                const int idx = tid + j * kLpThreads;
+                const int r = idx / P8, p = idx - r * P8;
+                const bool ok = idx < total && r < M && p * kPiece < len;
+                v[j] = load16<kCached>(rx, ok ? ((uint32_t)r * K8 + k0 / kPiece + p) * 16u : kLpOut);
+            }
+            // FP8 up to 32 rows: the first windows' codes are requested right
+            // behind x (only the x loads are waited for before the LDS copy and
+            // the barrier).  Measured on MI355X this pays there (4096 x 7168,
+            // M = 16: 12.1 -> 11.5 us) and loses at 64 rows and for MXFP4.
+            if constexpr (kHoist) load_batch(first, 0);
+#pragma unroll
+            for (int j = 0; j < kLpXLoads; ++j) {
+                const int idx = tid + j * kLpThreads;
+                const int r = idx / P8, p = idx - r * P8;
+                if (idx < total) xs[r * pitch + p] = v[j];
+            }
         }
     }
     __syncthreads();
@@ -250,10 +281,12 @@ __global__ __launch_bounds__(kLpThreads) void lowp_chunk_kernel(
     // a batch issued before the barrier is consumed outside the loop: behind
     // a loop header the compiler would wait for all of its loads at once
     if constexpr (kHoist) compute_batch(first, 0);
-    for (int wb = kHoist ? D : 0; wb < windows; wb += D) {
-        Batch bt;
-        load_batch(bt, wb);
-        compute_batch(bt, wb);
+    if constexpr (!ALL) {
+        for (int wb = kHoist ? D : 0; wb < windows; wb += D) {
+            Batch bt;
+            load_batch(bt, wb);
+            compute_batch(bt, wb);
+        }
     }
 
     if (ep.partial) {
@@ -310,7 +343,7 @@ bool lowp_chunk_plan(int M, int N, int K, LowpChunkPlan* p) {
     const int XR = 16 * MT;
     if (K == 0) {  // outputs are r (or zero): one launch, nothing to stage
         *p = LowpChunkPlan{MT, 1, 1, kLpWindow, kLpWindow / kPiece + 1,
-                           (size_t)XR * (kLpWindow / kPiece + 1) * 16, 0};
+                           ((size_t)XR * (kLpWindow / kPiece + 1) + kLpPadSlots) * 16, 0};
         return true;
     }
     const int NT = lowp_nt(N);
@@ -322,7 +355,7 @@ bool lowp_chunk_plan(int M, int N, int K, LowpChunkPlan* p) {
     for (int S = 1; S <= 64 && S <= windows; ++S) {
         const int chunk = kLpWindow * ((windows + S - 1) / S);
         if ((int64_t)(S - 1) * chunk >= K) continue;  // an empty chunk
-        const size_t lds = (size_t)XR * (chunk / kPiece + 1) * 16;
+        const size_t lds = ((size_t)XR * (chunk / kPiece + 1) + kLpPadSlots) * 16;
         if (lds > kLpLdsMax || XR * (chunk / kPiece) > kLpXLoads * kLpThreads) continue;
         best = S;
         if (tiles * S >= kLpCus) break;
@@ -334,7 +367,7 @@ bool lowp_chunk_plan(int M, int N, int K, LowpChunkPlan* p) {
     p->S = best;
     p->chunk = chunk;
     p->pitch = chunk / kPiece + 1;  // odd row pitch: the 16 rows of an operand read spread banks
-    p->lds = (size_t)XR * p->pitch * 16;
+    p->lds = ((size_t)XR * p->pitch + kLpPadSlots) * 16;
     p->workspace = best > 1 ? ((size_t)best * N * XR * sizeof(float) + 255) / 256 * 256 : 0;
     return true;
 }
@@ -348,9 +381,17 @@ hipError_t launch_lowp_chunk(int fmt, int M, int N, int K, const void* x, const 
     const uint4* xp = static_cast<const uint4*>(x);
     const uint8_t* wp = static_cast<const uint8_t*>(Wq);
     constexpr int kD8 = 4, kD4 = 8;  // windows in flight per wave
-#define SG_LP(f, mt, nt, d)                                                                       \
-    if (fmt == f && p.MT == mt && p.NT == nt) {                                                   \
-        auto* kern = &lowp_chunk_kernel<f, mt, nt, d>;                                            \
+    // FP8 with one 16-row tile and one x row tile a wave and 7 or 8 windows a
+    // wave (K = 7168 or 8192 over 8 splits): the whole chunk is one batch.
+    // Interleaved A/B on MI355X: 4096 x 7168 M = 12 / 16 11.41 / 11.43 ->
+    // 10.71 / 10.76 us; with two tiles a wave or from 17 rows it was slower
+    // (8192 x 7168 M = 16 17.94 -> 18.17 us, 4096 x 7168 M = 64 14.81 ->
+    // 16.00 us).
+    const int wpw = p.chunk / kLpWindow;
+    const bool all = fmt == kLowpFp8 && p.MT == 1 && p.NT == 1 && (wpw == 7 || wpw == 8);
+#define SG_LP(f, mt, nt, d, a)                                                                    \
+    if (fmt == f && p.MT == mt && p.NT == nt && all == a) {                                       \
+        auto* kern = &lowp_chunk_kernel<f, mt, nt, d, a>;                                         \
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),                   \
                                            hipFuncAttributeMaxDynamicSharedMemorySize,            \
                                            (int)p.lds);                                           \
@@ -362,12 +403,15 @@ hipError_t launch_lowp_chunk(int fmt, int M, int N, int K, const void* x, const 
                                              fin, stream)                                         \
                        : hipSuccess;                                                              \
     }
-    SG_LP(kLowpFp8, 1, 1, kD8) SG_LP(kLowpFp8, 2, 1, kD8) SG_LP(kLowpFp8, 3, 1, kD8)
-    SG_LP(kLowpFp8, 4, 1, kD8) SG_LP(kLowpFp8, 1, 2, kD8) SG_LP(kLowpFp8, 2, 2, kD8)
-    SG_LP(kLowpFp8, 3, 2, kD8) SG_LP(kLowpFp8, 4, 2, kD8)
-    SG_LP(kLowpMxfp4, 1, 1, kD4) SG_LP(kLowpMxfp4, 2, 1, kD4) SG_LP(kLowpMxfp4, 3, 1, kD4)
-    SG_LP(kLowpMxfp4, 4, 1, kD4) SG_LP(kLowpMxfp4, 1, 2, kD4) SG_LP(kLowpMxfp4, 2, 2, kD4)
-    SG_LP(kLowpMxfp4, 3, 2, kD4) SG_LP(kLowpMxfp4, 4, 2, kD4)
+    SG_LP(kLowpFp8, 1, 1, 8, true)
+    SG_LP(kLowpFp8, 1, 1, kD8, false) SG_LP(kLowpFp8, 2, 1, kD8, false)
+    SG_LP(kLowpFp8, 3, 1, kD8, false) SG_LP(kLowpFp8, 4, 1, kD8, false)
+    SG_LP(kLowpFp8, 1, 2, kD8, false) SG_LP(kLowpFp8, 2, 2, kD8, false)
+    SG_LP(kLowpFp8, 3, 2, kD8, false) SG_LP(kLowpFp8, 4, 2, kD8, false)
+    SG_LP(kLowpMxfp4, 1, 1, kD4, false) SG_LP(kLowpMxfp4, 2, 1, kD4, false)
+    SG_LP(kLowpMxfp4, 3, 1, kD4, false) SG_LP(kLowpMxfp4, 4, 1, kD4, false)
+    SG_LP(kLowpMxfp4, 1, 2, kD4, false) SG_LP(kLowpMxfp4, 2, 2, kD4, false)
+    SG_LP(kLowpMxfp4, 3, 2, kD4, false) SG_LP(kLowpMxfp4, 4, 2, kD4, false)
 #undef SG_LP
     return hipErrorInvalidValue;
 }
