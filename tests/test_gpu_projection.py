@@ -226,8 +226,8 @@ def test_full_small_batch_7168x8192(M):
 
 @pytest.mark.parametrize("M", [4, 8, 16])
 def test_full_larger_batch_8192x7168(M):
-    # every output of the bench's wider-matrix rows (streaming teams at M = 4, the
-    # two-tile team kernel at M = 8 and 16)
+    # every output of the bench's wider-matrix rows (the team kernel with one 16-row
+    # tile a wave at M = 4 and 8, two at M = 16)
     plan = _full_case(M, 8192, 7168, 2500, rows=None)
     assert plan.split_k > 1
 
