@@ -143,7 +143,8 @@ class Launcher:
     def moe_step(self, x, Wr, We, Ws, topk, outs, ws, mode):
         """skinny_moe_step: the shared expert fused into the router GEMM (Wr and Ws
         adjacent, outputs in one [T, E + N_shared] buffer), on the binding's side
-        stream, or serial after the routed experts."""
+        stream, serial after the routed experts, or inside the routed-expert launch
+        (shared_in_routed, up to 4 tokens)."""
         c, sg = self.c, self.sg
         T, K = x.shape
         E, N, _ = We.shape
@@ -153,7 +154,9 @@ class Launcher:
                             None if fused else Ws.data_ptr(), scores.data_ptr(), ids.data_ptr(),
                             None, out.data_ptr(), None if fused else shared.data_ptr(),
                             T, K, E, topk, N, Ws.shape[0],
-                            sg._lib.SG_MOE_STEP_FUSED_SHARED if fused else 0)
+                            sg._lib.SG_MOE_STEP_FUSED_SHARED if fused
+                            else sg._lib.SG_MOE_STEP_SHARED_IN_ROUTED
+                            if mode == "shared_in_routed" else 0)
         side = fork = join = None
         if mode == "side_stream":
             s_, f_, j_ = sg._side_resources(x.device)
@@ -770,7 +773,7 @@ def sweep(torch, sg, si, L, cyc, reps=40, journal=None):
                 T * topk * N * 4 + T * topk * 4
             per = {}
             launches = {}
-            for mode in ("serial", "side_stream", "fused"):
+            for mode in ("serial", "side_stream", "fused", "shared_in_routed"):
                 calls = [L.moe_step(x, wr, W, wsh, topk, outs, ws, mode) for x, wr, wsh in combos]
                 before = sg.skinny_gemm_get_counters()
                 calls[0]()
@@ -783,7 +786,9 @@ def sweep(torch, sg, si, L, cyc, reps=40, journal=None):
                          "us": round(1e3 * per["fused"], 3),
                          "us_side_stream": round(1e3 * per["side_stream"], 3),
                          "us_serial": round(1e3 * per["serial"], 3),
+                         "us_shared_in_routed": round(1e3 * per["shared_in_routed"], 3),
                          "launches_per_step": launches["fused"],
+                         "launches_shared_in_routed": launches["shared_in_routed"],
                          "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                          "distinct_experts_mean": round(sum(distinct) / len(distinct), 1)})
         del W, Wrs, ring_rs

@@ -313,6 +313,14 @@ size_t skinny_gemm_mxfp4_workspace(int32_t M, int32_t N, int32_t K);
  * [E, E+N_shared) the shared expert's output), W_shared and shared_out are
  * ignored, and no side stream is used.  Outputs equal those of the other
  * modes to the projection tolerance (the fused GEMM may take another plan).
+ * flags & SG_MOE_STEP_SHARED_IN_ROUTED: up to 4 tokens (E <= 512, N >= 1)
+ * the routed-expert launch, which ranks the scores itself, also computes
+ * shared_out: every wave streams its share of W_shared's rows while it ranks,
+ * when no routed weight can be requested yet -- the overlap of [P] Method
+ * details §3 inside one launch, two launches a step.  Larger steps run as
+ * with side_stream NULL.  Buffers as in the default mode; no side stream is
+ * used; ids and routed outputs equal the other modes' bit for bit, shared_out
+ * to the projection tolerance.  Both flags together: SG_ERR_SHAPE.
  * Shapes: x [T,K], W_router [E,K], W_experts [E,N,K], W_shared [N_shared,K]
  * (bf16); scores [T,E], topk_scores [T,topk] (nullable), out [T,topk,N],
  * shared_out [T,N_shared] (fp32); topk_ids [T,topk] int32.  Pointers whose
@@ -332,10 +340,11 @@ typedef struct {
     float* out;
     float* shared_out;
     int32_t T, K, E, topk, N, N_shared;
-    int32_t flags;  /* 0, or SG_MOE_STEP_FUSED_SHARED */
+    int32_t flags;  /* 0, SG_MOE_STEP_FUSED_SHARED or SG_MOE_STEP_SHARED_IN_ROUTED */
 } sg_moe_step;
 
 #define SG_MOE_STEP_FUSED_SHARED 1
+#define SG_MOE_STEP_SHARED_IN_ROUTED 2
 
 /* Workspace bytes skinny_moe_step needs (0 if the sizes are rejected). */
 size_t skinny_moe_step_workspace(int32_t T, int32_t K, int32_t E, int32_t topk, int32_t N,

@@ -344,7 +344,7 @@ def concat_router_shared(W_router: torch.Tensor, W_shared: torch.Tensor):
     return both[:W_router.shape[0]], both[W_router.shape[0]:]
 
 
-MOE_STEP_MODES = ("fused", "side_stream", "serial")
+MOE_STEP_MODES = ("fused", "side_stream", "serial", "shared_in_routed")
 
 
 def skinny_moe_step(x: torch.Tensor, W_router: torch.Tensor, W_experts: torch.Tensor,
@@ -354,7 +354,9 @@ def skinny_moe_step(x: torch.Tensor, W_router: torch.Tensor, W_experts: torch.Te
       "fused"       -- in the router's GEMM; W_shared must be stored right after W_router
                        (the two views concat_router_shared returns);
       "side_stream" -- on a side stream that overlaps the routing phase;
-      "serial"      -- after the routed experts on `stream`.
+      "serial"      -- after the routed experts on `stream`;
+      "shared_in_routed" -- up to 4 tokens (E <= 512), inside the routed-expert launch,
+                       streamed while it ranks the scores (else as "serial").
     Returns (topk_ids [T,topk] int32, topk_scores [T,topk], scores [T,E], out [T,topk,N],
     shared_out [T,N_shared]; fp32).  In fused mode scores and shared_out are column
     views of one [T, E + N_shared] buffer."""
@@ -395,7 +397,8 @@ def skinny_moe_step(x: torch.Tensor, W_router: torch.Tensor, W_experts: torch.Te
         _ptr(W_experts, torch.bfloat16, "W_experts", dev), w_shared_ptr, scores_ptr,
         _ptr(ids, torch.int32, "topk_ids", dev), _ptr(top, torch.float32, "topk_scores", dev),
         _ptr(out, torch.float32, "out", dev), shared_ptr, T, K, E, topk, N, N_shared,
-        _lib.SG_MOE_STEP_FUSED_SHARED if fused else 0)
+        _lib.SG_MOE_STEP_FUSED_SHARED if fused
+        else _lib.SG_MOE_STEP_SHARED_IN_ROUTED if mode == "shared_in_routed" else 0)
     side = fork = join = None
     if mode == "side_stream":
         s, f, j = _side_resources(dev)

@@ -62,6 +62,7 @@ class SgMoeStep(ctypes.Structure):
 
 
 SG_MOE_STEP_FUSED_SHARED = 1
+SG_MOE_STEP_SHARED_IN_ROUTED = 2
 SG_NOALLOC_MAX_WORKSPACE = 16 << 20
 
 

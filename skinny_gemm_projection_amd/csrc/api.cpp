@@ -142,17 +142,23 @@ bool route_grouped_ok(int32_t T, int32_t E, int32_t k, int32_t N) {
 
 sg_status route_grouped_call(const float* scores, int64_t ld, int32_t T, int32_t E, int32_t k,
                              int32_t* topk_ids, float* topk_scores, const sg_bf16* x,
-                             const sg_bf16* W, int32_t N, int32_t K, float* out, void* stream) {
-    if (!route_grouped_ok(T, E, k, N) || ld < E || K < 0 || K > 8192 || K % 8 != 0)
+                             const sg_bf16* W, int32_t N, int32_t K, float* out,
+                             const sg_bf16* W_shared, int32_t N_shared, float* shared_out,
+                             void* stream) {
+    if (!route_grouped_ok(T, E, k, N) || ld < E || K < 0 || K > 8192 || K % 8 != 0 ||
+        N_shared < 0)
         return SG_ERR_UNSUPPORTED;
     (void)hipGetLastError();
     if (launch_route_grouped(scores, ld, T, E, k, topk_ids, topk_scores, x, W, N, K, out,
+                             W_shared, N_shared, shared_out,
                              static_cast<hipStream_t>(stream)) != hipSuccess)
         return SG_ERR_HIP;
     count(SG_KERNEL_GROUPED);
     if (log_enabled())
-        std::fprintf(stderr, "[skinny_gemm] router top-k + grouped (one launch) T=%d E=%d k=%d N=%d K=%d\n",
-                     T, E, k, N, K);
+        std::fprintf(stderr,
+                     "[skinny_gemm] router top-k + grouped (one launch) T=%d E=%d k=%d N=%d K=%d "
+                     "N_shared=%d\n",
+                     T, E, k, N, K, N_shared);
     return SG_OK;
 }
 

@@ -108,12 +108,14 @@ hipError_t launch_grouped_fused(const void* x, int T, const void* W, const int32
 // Router top-k and the fused grouped projection in one launch, for a few
 // tokens: 1 <= T <= kRouteFusedMaxT, E <= kRouteFusedMaxExperts (at most 8
 // keys a lane), N >= 1.  ids [T, k] (and top [T, k] when non-null) are
-// written as by launch_router_topk.
-constexpr int kRouteFusedMaxT = 4;
+// written as by launch_router_topk.  With N_shared > 0 the launch also
+// writes shared_out [T, N_shared] = x W_shared^T, streamed while it ranks.
+constexpr int kRouteFusedMaxT = kWavesPerBlock;  // one ranking wave per token
 constexpr int kRouteFusedMaxExperts = 512;
 hipError_t launch_route_grouped(const float* scores, int64_t ld, int T, int E, int k,
                                 int32_t* ids, float* top, const void* x, const void* W, int N,
-                                int K, float* out, hipStream_t stream);
+                                int K, float* out, const void* W_shared, int N_shared,
+                                float* shared_out, hipStream_t stream);
 hipError_t launch_grouped(const void* x, int T, const void* W, int E, int N, int K, int topk,
                           const GroupedWorkspace& g, float* out, hipStream_t stream);
 

@@ -420,30 +420,81 @@ __global__ __launch_bounds__(kBlock) void grouped_fused_kernel(
 }
 
 // Router top-k and routed-expert projection in one launch, for a few tokens
-// (T <= kRouteFusedMaxT): every workgroup ranks the scores itself -- wave w
-// takes tokens w, w + 4, ... with the router kernel's wave_topk, so the ids
-// are the same bits -- and workgroup 0 also stores them (and the selected
+// (T <= kRouteFusedMaxT = kWavesPerBlock): every workgroup ranks the scores
+// itself -- wave t ranks token t with the router kernel's wave_topk, so the
+// ids are the same bits -- and workgroup 0 also stores them (and the selected
 // scores).  Then the fused table and the grouped loop as above.  This drops
 // the top-k launch and the round trip of the ids through memory.
+//
+// With Nsh > 0 the launch also computes the shared expert, shared_out[t, r] =
+// x[t] . Wsh[r] ("Hyper Optimizing Kimi K3 in vLLM" deepnotes page, Method
+// details §3: the shared expert overlaps the routing).  Its rows are split
+// evenly over every wave of the grid; each wave requests its first row right
+// behind its scores, so the row streams from HBM while the wave ranks --
+// until the ids are known no routed weight can be requested -- and finishes
+// its rows (one dot product per token, x from L2) before the table.
 template <int NCH, int PER>
 __global__ __launch_bounds__(kBlock) void route_grouped_kernel(
     const float* __restrict__ scores, int64_t ld, int T, int E, int k,
     int32_t* __restrict__ ids_out, float* __restrict__ top_out, const uint4* __restrict__ x,
-    const uint4* __restrict__ W, int N, int K8, int tiles, float* __restrict__ out) {
+    const uint4* __restrict__ W, int N, int K8, int tiles, float* __restrict__ out,
+    const uint4* __restrict__ Wsh, int Nsh, float* __restrict__ shared_out) {
     extern __shared__ int32_t lds_i[];
     __shared__ int32_t s_wave[kWavesPerBlock];
     const int lane = threadIdx.x & (kWave - 1);
+    const int wv = wave_id_in_block();
     const int P = T * k;
-    for (int t = wave_id_in_block(); t < T; t += kWavesPerBlock) {
-        const float* s = scores + t * ld;
-        const uint64_t mine = wave_topk<PER>(s, E, k, lane);
-        if (lane < k) {
+    const bool ranks = wv < T;  // wave t ranks token t
+    // The scores, then the first shared row, are requested with no branch
+    // around them (a wave with no token, or no shared row, reads through a
+    // 0-byte descriptor, which gives zeros), and every wave ranks, only the
+    // stores depending on the token: behind a branch the compiler cannot
+    // count the loads in flight and its waits for the scores drain the row's,
+    // and loads used only under a branch are moved into it, behind the row's.
+    uint32_t sv[PER];
+    wave_topk_fetch<PER>(scores + (ranks ? wv : 0) * ld, ranks ? E : 0, lane, sv);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // this wave's shared-expert rows [sr0, sr1); a row past them reads zero
+    const int nw = gridDim.x * kWavesPerBlock;
+    const int sper = (Nsh + nw - 1) / nw;
+    const int sr0 = min(Nsh, (blockIdx.x * kWavesPerBlock + wv) * sper);
+    const int sr1 = min(Nsh, sr0 + sper);
+    uint4 wsr[NCH];
+    auto load_srow = [&](int r) {
+        const bool ok = r < sr1;
+        const rsrc_t rs = make_rsrc(Wsh + (int64_t)(ok ? r : 0) * K8, ok ? (uint32_t)K8 * 16u : 0u);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            wsr[c] = load16<kStream>(rs, (uint32_t)(c * kWave + lane) * 16u);
+    };
+    load_srow(sr0);
+    __builtin_amdgcn_sched_barrier(0);  // the row's loads stay ahead of the ranking
+
+    {
+        __builtin_assume(k >= 1);  // (checked by the caller) else the scores wait behind k > 0
+        uint64_t key[PER];
+        wave_topk_keys<PER>(sv, E, lane, key);
+        const uint64_t mine = wave_topk_rank<PER>(key, k, lane);
+        if (ranks && lane < k) {
             const int id = key_id(mine);
-            lds_i[t * k + lane] = id;
+            lds_i[wv * k + lane] = id;
             if (blockIdx.x == 0) {
-                ids_out[(int64_t)t * k + lane] = id;
-                if (top_out) top_out[(int64_t)t * k + lane] = s[id];  // as given
+                ids_out[(int64_t)wv * k + lane] = id;
+                if (top_out) top_out[(int64_t)wv * k + lane] = scores[wv * ld + id];  // as given
             }
+        }
+    }
+    for (int r = sr0; r < sr1; ++r) {
+        if (r > sr0) load_srow(r);
+        for (int t = 0; t < T; ++t) {
+            const rsrc_t rx = make_rsrc(x + (int64_t)t * K8, (uint32_t)K8 * 16u);
+            uint4 xa[NCH];
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+                xa[c] = load16<kCached>(rx, (uint32_t)(c * kWave + lane) * 16u);
+            const float tot = wave_sum(dot_row<NCH>(xa, wsr));
+            if (lane == 0) shared_out[(int64_t)t * Nsh + r] = tot;
         }
     }
     grouped_lds_table<NCH>(x, W, lds_i, lds_i + P, lds_i + P + E, s_wave, P, E, N, K8, k,
@@ -515,11 +566,11 @@ template <int NCH>
 static hipError_t launch_route_nch(int per, int grid, size_t lds, hipStream_t stream,
                              const float* scores, int64_t ld, int T, int E, int k, int32_t* ids,
                              float* top, const uint4* xp, const uint4* wp, int N, int K8,
-                             int tiles, float* out) {
+                             int tiles, float* out, const uint4* wsh, int Nsh, float* sout) {
 #define SG_ROUTE(pp) \
     if (per <= pp) { \
         route_grouped_kernel<NCH, pp><<<grid, kBlock, lds, stream>>>( \
-            scores, ld, T, E, k, ids, top, xp, wp, N, K8, tiles, out); \
+            scores, ld, T, E, k, ids, top, xp, wp, N, K8, tiles, out, wsh, Nsh, sout); \
         return hipGetLastError(); \
     }
     SG_ROUTE(2) SG_ROUTE(4) SG_ROUTE(6) SG_ROUTE(8)
@@ -529,7 +580,8 @@ static hipError_t launch_route_nch(int per, int grid, size_t lds, hipStream_t st
 
 hipError_t launch_route_grouped(const float* scores, int64_t ld, int T, int E, int k,
                                 int32_t* ids, float* top, const void* x, const void* W, int N,
-                                int K, float* out, hipStream_t stream) {
+                                int K, float* out, const void* W_shared, int N_shared,
+                                float* shared_out, hipStream_t stream) {
     const int per = (E + kWave - 1) / kWave;
     if (T < 1 || T > kRouteFusedMaxT || per > kSortedPerLane || N < 1) return hipErrorInvalidValue;
     const int P = T * k;
@@ -542,23 +594,24 @@ hipError_t launch_route_grouped(const float* scores, int64_t ld, int T, int E, i
     const size_t lds = (size_t)(P + 2 * E) * sizeof(int32_t);
     const uint4* xp = static_cast<const uint4*>(x);
     const uint4* wp = static_cast<const uint4*>(W);
+    const uint4* wsh = static_cast<const uint4*>(W_shared);
     const int nch = (K + kLaneSpan - 1) / kLaneSpan;
     switch (next_pow2(nch < 1 ? 1 : nch)) {
         case 1:
             return launch_route_nch<1>(per, grid, lds, stream, scores, ld, T, E, k, ids, top, xp,
-                                        wp, N, K8, tiles, out);
+                                        wp, N, K8, tiles, out, wsh, N_shared, shared_out);
         case 2:
             return launch_route_nch<2>(per, grid, lds, stream, scores, ld, T, E, k, ids, top, xp,
-                                        wp, N, K8, tiles, out);
+                                        wp, N, K8, tiles, out, wsh, N_shared, shared_out);
         case 4:
             return launch_route_nch<4>(per, grid, lds, stream, scores, ld, T, E, k, ids, top, xp,
-                                        wp, N, K8, tiles, out);
+                                        wp, N, K8, tiles, out, wsh, N_shared, shared_out);
         case 8:
             return launch_route_nch<8>(per, grid, lds, stream, scores, ld, T, E, k, ids, top, xp,
-                                        wp, N, K8, tiles, out);
+                                        wp, N, K8, tiles, out, wsh, N_shared, shared_out);
         case 16:
             return launch_route_nch<16>(per, grid, lds, stream, scores, ld, T, E, k, ids, top, xp,
-                                        wp, N, K8, tiles, out);
+                                        wp, N, K8, tiles, out, wsh, N_shared, shared_out);
         default: return hipErrorInvalidValue;
     }
 }

@@ -21,7 +21,10 @@
 // the overlap hides at batch 1.  The fused mode therefore takes the shared
 // expert into the router's GEMM: same input, one weight stream of
 // E + N_shared rows, one launch, and the top-k kernel reads the score columns
-// through a row stride.
+// through a row stride.  The SHARED_IN_ROUTED mode instead makes the overlap
+// happen inside the routed-expert launch (up to 4 tokens): its waves stream
+// the shared expert's rows while they rank, the window in which no routed
+// weight can be requested yet.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -75,8 +78,10 @@ size_t skinny_moe_step_workspace(int32_t T, int32_t K, int32_t E, int32_t topk, 
 sg_status skinny_moe_step(const sg_moe_step* a, void* workspace, size_t workspace_bytes,
                           void* stream, void* side_stream, void* fork_event, void* join_event) {
     if (!a) return SG_ERR_NULL;
-    if (a->flags & ~SG_MOE_STEP_FUSED_SHARED) return SG_ERR_SHAPE;
+    if (a->flags & ~(SG_MOE_STEP_FUSED_SHARED | SG_MOE_STEP_SHARED_IN_ROUTED)) return SG_ERR_SHAPE;
     const bool fused = (a->flags & SG_MOE_STEP_FUSED_SHARED) != 0;
+    const bool in_routed = (a->flags & SG_MOE_STEP_SHARED_IN_ROUTED) != 0;
+    if (fused && in_routed) return SG_ERR_SHAPE;
     StepLayout L;
     sg_status st = step_layout(a->T, a->K, a->E, a->topk, a->N, a->N_shared, fused, &L);
     if (st != SG_OK) return st;
@@ -95,7 +100,7 @@ sg_status skinny_moe_step(const sg_moe_step* a, void* workspace, size_t workspac
         if (!aligned16(p)) return SG_ERR_ALIGN;
     if (!workspace || workspace_bytes < L.total) return SG_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SG_ERR_ALIGN;
-    const bool overlap = sep && side_stream && side_stream != stream;
+    const bool overlap = sep && !in_routed && side_stream && side_stream != stream;
     if (overlap && (!fork_event || !join_event)) return SG_ERR_NULL;
 
     char* base = static_cast<char*>(workspace);
@@ -121,12 +126,18 @@ sg_status skinny_moe_step(const sg_moe_step* a, void* workspace, size_t workspac
                           L.router_ws, stream)) != SG_OK)
         return st;
     const int64_t ld = fused ? (int64_t)a->E + a->N_shared : a->E;  // row stride of the scores
+    bool shared_done = false;
     if (sg::route_grouped_ok(a->T, a->E, a->topk, a->N)) {
-        // a few tokens: top-k and the routed experts in one launch
+        // a few tokens: top-k and the routed experts in one launch, and in
+        // SHARED_IN_ROUTED mode the shared expert too, streamed while it ranks
+        const bool sh = in_routed && sep;
         if ((st = sg::route_grouped_call(a->scores, ld, a->T, a->E, a->topk, a->topk_ids,
                                          a->topk_scores, a->x, a->W_experts, a->N, a->K,
-                                         a->out, stream)) != SG_OK)
+                                         a->out, sh ? a->W_shared : nullptr,
+                                         sh ? a->N_shared : 0, sh ? a->shared_out : nullptr,
+                                         stream)) != SG_OK)
             return st;
+        shared_done = sh;
     } else {
         if ((st = sg::router_topk_call(a->scores, ld, a->T, a->E, a->topk, a->topk_ids,
                                        a->topk_scores, stream)) != SG_OK)
@@ -137,7 +148,7 @@ sg_status skinny_moe_step(const sg_moe_step* a, void* workspace, size_t workspac
             return st;
     }
     if (overlap) return hipStreamWaitEvent(main_s, join, 0) == hipSuccess ? SG_OK : SG_ERR_HIP;
-    return sep ? shared_expert(stream) : SG_OK;
+    return sep && !shared_done ? shared_expert(stream) : SG_OK;
 }
 
 }  // extern "C"

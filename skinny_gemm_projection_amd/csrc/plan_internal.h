@@ -26,6 +26,8 @@ sg_status router_topk_call(const float* scores, int64_t ld, int32_t T, int32_t E
 bool route_grouped_ok(int32_t T, int32_t E, int32_t k, int32_t N);
 sg_status route_grouped_call(const float* scores, int64_t ld, int32_t T, int32_t E, int32_t k,
                              int32_t* topk_ids, float* topk_scores, const sg_bf16* x,
-                             const sg_bf16* W, int32_t N, int32_t K, float* out, void* stream);
+                             const sg_bf16* W, int32_t N, int32_t K, float* out,
+                             const sg_bf16* W_shared, int32_t N_shared, float* shared_out,
+                             void* stream);
 
 }  // namespace sg

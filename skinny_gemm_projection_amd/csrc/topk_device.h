@@ -66,22 +66,40 @@ __device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
     return v;
 }
 
-// The k first-ranked of the E scores s[0..E) (PER >= ceil(E / 64)), computed
-// by one whole wavefront: lane l holds the keys of experts l, l+64, ...; up
-// to kSortedPerLane keys a lane are sorted once and each of the k rounds
-// takes the wave maximum of the lane heads (the winning lane pops its head);
-// with more, each round every lane rescans for its best key below the
-// previous winner.  Returns, in lane r < k, the key of rank r.
+// The E scores s[0..E) a lane holds (PER >= ceil(E / 64)): lane l takes
+// experts l, l+64, ....  Buffer loads with no branch (a score past E reads
+// zero), all issued before any is used: written as a load per key under
+// `e < E`, each load sat in its own branch with a wait right behind it, so
+// the PER loads ran one after another.
 template <int PER>
-__device__ __forceinline__ uint64_t wave_topk(const float* __restrict__ s, int E, int k, int lane) {
-    // key 0 (below every real key) pads experts past E
-    uint64_t key[PER];
+__device__ __forceinline__ void wave_topk_fetch(const float* __restrict__ s, int E, int lane,
+                                                uint32_t (&v)[PER]) {
+    const rsrc_t rs = make_rsrc(s, (uint32_t)E * 4u);
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        v[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(j * kWave + lane) * 4u, 0,
+                                                    kCached);
+}
+
+// Their keys; key 0 (below every real key) pads experts past E.
+template <int PER>
+__device__ __forceinline__ void wave_topk_keys(const uint32_t (&v)[PER], int E, int lane,
+                                               uint64_t (&key)[PER]) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int e = j * kWave + lane;
-        const float v = s[e < E ? e : E - 1];
-        key[j] = e < E ? rank_key(v, e) : 0;
+        const uint64_t kj = rank_key(as_f(v[j]), e);
+        key[j] = e < E ? kj : 0;
     }
+}
+
+// The k first-ranked of the keys wave_topk_keys gave, computed by one whole
+// wavefront: up to kSortedPerLane keys a lane are sorted once and each of
+// the k rounds takes the wave maximum of the lane heads (the winning lane
+// pops its head); with more, each round every lane rescans for its best key
+// below the previous winner.  Returns, in lane r < k, the key of rank r.
+template <int PER>
+__device__ __forceinline__ uint64_t wave_topk_rank(uint64_t (&key)[PER], int k, int lane) {
     uint64_t mine = 0;
     if constexpr (PER <= kSortedPerLane) {
         // odd-even transposition sort, descending
@@ -113,6 +131,16 @@ __device__ __forceinline__ uint64_t wave_topk(const float* __restrict__ s, int E
         }
     }
     return mine;
+}
+
+// The k first-ranked of the E scores s[0..E): in lane r < k, the key of rank r.
+template <int PER>
+__device__ __forceinline__ uint64_t wave_topk(const float* __restrict__ s, int E, int k, int lane) {
+    uint32_t v[PER];
+    uint64_t key[PER];
+    wave_topk_fetch<PER>(s, E, lane, v);
+    wave_topk_keys<PER>(v, E, lane, key);
+    return wave_topk_rank<PER>(key, k, lane);
 }
 
 }  // namespace sg

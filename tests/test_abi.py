@@ -51,6 +51,17 @@ def test_library_exports_every_declared_symbol():
         assert name in exported, f"{name} missing from the dynamic symbol table"
 
 
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    consts = {n: int(v) for n, v in re.findall(r"^\s*(SG_KERNEL_\w+) = (\d+)", text, flags=re.M)}
+    consts.update({n: int(v) for n, v in
+                   re.findall(r"^#define (SG_(?:MOE_STEP_\w+|NUM_COUNTERS)) (\d+)$", text,
+                              flags=re.M)})
+    assert "SG_MOE_STEP_SHARED_IN_ROUTED" in consts and "SG_KERNEL_FP8" in consts
+    for name, value in consts.items():
+        assert getattr(_lib, name) == value, name
+
+
 def test_python_binding_has_the_same_names():
     for name in declared_functions():
         assert callable(getattr(sg, name)), name

@@ -112,7 +112,8 @@ def test_graph_grouped(T, tables):
 
 
 @pytest.mark.parametrize("T,mode", [(2, "fused"), (16, "fused"), (16, "serial"),
-                                     (2, "side_stream"), (16, "side_stream")])
+                                     (2, "side_stream"), (16, "side_stream"),
+                                     (3, "shared_in_routed")])
 def test_graph_moe_step(T, mode):
     E, topk, N, Ns, K = 64, 8, 256, 128, 2048
     announce(f"graph moe step T={T} mode={mode}")

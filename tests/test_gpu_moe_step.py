@@ -1,13 +1,15 @@
 """GPU parity of one MoE decode step through the C ABI (skinny_moe_step): router
 scores, top-k, routed-expert projection, and the shared expert's projection --
-fused into the router's GEMM, on a side stream that overlaps the routing, or
-serial.
+fused into the router's GEMM, on a side stream that overlaps the routing,
+serial, or (up to 4 tokens) inside the routed-expert launch.
 
 Each output of each mode is checked against the oracle: the router scores and
 the shared expert against oracle_projection, the ids (bit-exact) against
 oracle_router_topk of the GPU scores, the routed output against oracle_grouped
 with those ids.  The side-stream step must give bitwise the same outputs as the
-serial one (the same kernels and plans run either way)."""
+serial one (the same kernels and plans run either way), and the shared-in-routed
+step the same ids, scores and routed outputs (its shared expert is another
+kernel's sum, checked against the oracle)."""
 import ctypes
 
 import numpy as np
@@ -64,7 +66,10 @@ def check_step(res, x, Wr, We, Ws, topk, what, out_rows=None):
                                                     (16, 256, 17, 130, 0, 3),
                                                     (4, 520, 384, 40, 0, 8),
                                                     (2, 264, 500, 24, 32, 32),
-                                                    (3, 1032, 64, 0, 48, 4)])
+                                                    (3, 1032, 64, 0, 48, 4),
+                                                    (4, 520, 40, 33, 72, 6),
+                                                    (4, 7168, 256, 64, 2048, 8),
+                                                    (3, 4104, 100, 200, 7, 4)])
 def test_step_small(T, K, E, N, N_shared, topk):
     x, Wr, We, Ws = weights(T, K, E, N, N_shared, 7000 + T)
     res = {}
@@ -83,10 +88,14 @@ def test_step_small(T, K, E, N, N_shared, topk):
         assert d[sg.SG_KERNEL_GROUPED] == (1 if N > 0 else 0)
         projections = sum(d[k] for k in (sg.SG_KERNEL_GEMV, sg.SG_KERNEL_SPLITK_VALU,
                                          sg.SG_KERNEL_SPLITK_MFMA))
-        assert projections == (1 if mode == "fused" or N_shared == 0 else 2), (mode, d)
+        in_routed = mode == "shared_in_routed" and route_fused
+        one = mode == "fused" or N_shared == 0 or in_routed
+        assert projections == (1 if one else 2), (mode, d)
         check_step(res[mode], x, Wr, We, Ws, topk, f"{mode} T={T}")
     for a, b in zip(res["side_stream"], res["serial"]):
         assert torch.equal(a, b), "side-stream and serial steps bitwise identical"
+    for a, b in zip(res["shared_in_routed"][:4], res["serial"][:4]):
+        assert torch.equal(a, b), "shared-in-routed: ids, scores, routed outputs as serial"
 
 
 @pytest.mark.parametrize("T", [7, 3, 1])
@@ -138,7 +147,8 @@ def test_step_rejections_launch_nothing():
     x, Wr, We, _ = weights(65, 64, 16, 24, 0, 7200)
     cases = [(dict(T=65), 3),                        # batch above the decode path
              (dict(T=4, ws_bytes=16), 5),            # workspace too small
-             (dict(T=4, flags=2), 2)]                # unknown mode flag
+             (dict(T=4, flags=4), 2),                # unknown mode flag
+             (dict(T=4, flags=3), 2)]                # two placements of the shared expert
     for kw, status in cases:
         before = sg.skinny_gemm_get_counters()
         st, outs = raw_step(x, Wr, We, 4, **kw)
@@ -219,3 +229,5 @@ def test_step_full_size(full_set, T):
                    out_rows=rows if T <= 16 else rows[:6])
     for a, b in zip(res["side_stream"], res["serial"]):
         assert torch.equal(a, b), "side-stream and serial steps bitwise identical"
+    for a, b in zip(res["shared_in_routed"][:4], res["serial"][:4]):
+        assert torch.equal(a, b), "shared-in-routed: ids, scores, routed outputs as serial"
