@@ -158,6 +158,15 @@ __global__ __launch_bounds__(kWave * team_waves(S)) void mxfp4_rowdot_kernel(
                                 rs, (uint32_t)(c * kWave + lane), 0, kStream);
                         }
                     }
+                    // At 2 to 4 rows of x every row's loads leave before the
+                    // first dot: left to itself the scheduler issued the
+                    // later rows' loads between the earlier rows' dots,
+                    // behind their waits.  Interleaved A/B on MI355X:
+                    // 8192 x 7168 M = 2 9.60 -> 9.05 us, 4096 x 7168 M = 2 /
+                    // 4 6.13 / 7.65 -> 5.94 / 7.37 us; at M = 1 mixed
+                    // (-0.27 to +0.34 us over five shapes), at M = 8 slower
+                    // (8192 x 7168 18.43 -> 18.92 us).
+                    if constexpr (M >= 2 && M <= 4) __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
                 for (int i = 0; i < RB; ++i) {
