@@ -802,7 +802,8 @@ def sweep(torch, sg, si, L, cyc, reps=40, journal=None):
 def side_stream_cu_mask(torch, sg, si, L, cyc, cus, Ts=(1, 4, 16), reps=5):
     """The MoE step with the shared expert on a side stream restricted to the first `cus`
     compute units (hipExtStreamCreateWithCUMask, default priority), against the
-    library's three placements on unmasked streams.  Median us over reps rounds."""
+    library's fused, serial and side-stream placements on unmasked streams.  Median us over
+    reps rounds."""
     import statistics
     hip = ctypes.CDLL("libamdhip64.so")
     hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
