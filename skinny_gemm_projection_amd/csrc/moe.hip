@@ -9,6 +9,8 @@
 // expert's weight matrix is then streamed from HBM once per call, however
 // many tokens chose it.  No host synchronisation: the number of active
 // experts is only known on the device, so the grouped kernel reads it there.
+#include <algorithm>
+
 #include "launch.h"
 #include "topk_device.h"
 
@@ -590,7 +592,10 @@ hipError_t launch_route_grouped(const float* scores, int64_t ld, int T, int E, i
     const int max_active = E < P ? E : P;
     const int64_t max_items = (int64_t)max_active * tiles;
     const int resident = 512;  // 256 CUs x 2 workgroups
-    const int grid = (int)(max_items < resident ? max_items : resident);
+    // enough waves for the shared rows too (about 4 a wave): a workgroup past
+    // the routed items only ranks, streams its shared rows and finds no item
+    const int64_t want = std::max<int64_t>(max_items, ((int64_t)N_shared + 15) / 16);
+    const int grid = (int)(want < resident ? want : resident);
     const size_t lds = (size_t)(P + 2 * E) * sizeof(int32_t);
     const uint4* xp = static_cast<const uint4*>(x);
     const uint4* wp = static_cast<const uint4*>(W);

@@ -69,7 +69,8 @@ def check_step(res, x, Wr, We, Ws, topk, what, out_rows=None):
                                                     (3, 1032, 64, 0, 48, 4),
                                                     (4, 520, 40, 33, 72, 6),
                                                     (4, 7168, 256, 64, 2048, 8),
-                                                    (3, 4104, 100, 200, 7, 4)])
+                                                    (3, 4104, 100, 200, 7, 4),
+                                                    (1, 1024, 16, 8, 3000, 4)])
 def test_step_small(T, K, E, N, N_shared, topk):
     x, Wr, We, Ws = weights(T, K, E, N, N_shared, 7000 + T)
     res = {}
