@@ -38,7 +38,14 @@ namespace sg {
 namespace {
 
 constexpr int kUnitCodes = 16;  // e4m3 codes per 16-byte lane load
-constexpr int kFp8Rows = 4;     // rows per wave iteration (divides 128)
+// Rows per wave iteration (divides 128).  At one row of x, two: half the
+// codes in flight per wave at once (with four, every wave requests its whole
+// share of the matrix at the start).  Interleaved A/B on MI355X against
+// four: 8192 x 7168 10.94 -> 10.78 us, 4096 x 7168 6.72 -> 6.56 us, 18432 x
+// 7168 22.19 -> 21.38 us, 2048 x 7168 5.33 -> 4.41 us; one row was mixed
+// (7168 x 8192 11.01 -> 10.74, 4096 x 7168 6.56 -> 6.69 us).  At M = 2
+// equal, at M = 3, 4 slower (4096 x 7168 8.05 / 8.78 -> 8.42 / 9.01 us).
+constexpr int fp8_rows(int M) { return M == 1 ? 2 : 4; }
 
 constexpr int pad4(int v) { return (v + 3) / 4 * 4; }
 constexpr int team_block_waves(int S) { return S > kWavesPerBlock ? S : kWavesPerBlock; }
@@ -74,7 +81,7 @@ template <int M, int NCH, int S>
 __global__ __launch_bounds__(kWave * team_block_waves(S)) void fp8_rowdot_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ Wq, const float* __restrict__ Ws,
     int N, int K16, int KB, int chunk16, int iters, Epilogue ep) {
-    constexpr int R = kFp8Rows;
+    constexpr int R = fp8_rows(M);
     constexpr int kWaves = team_block_waves(S);
     constexpr int kTeams = kWaves / S;
     constexpr int V = pad4(R * M);
@@ -383,7 +390,7 @@ template <int M, int NCH, int S>
 hipError_t launch_mns(int N, int K16, int chunk16, const void* x, const void* Wq,
                       const float* Ws, const Epilogue& ep, hipStream_t stream) {
     constexpr int kTeams = team_block_waves(S) / S;
-    const int groups = (N + kFp8Rows - 1) / kFp8Rows;
+    const int groups = (N + fp8_rows(M) - 1) / fp8_rows(M);
     const int cap = kResident / S;
     int teams = groups < cap ? groups : cap;
     const int its = (groups + teams - 1) / teams;
