@@ -348,15 +348,22 @@ int mxfp4_mfma_nt(int N) { return (N + 31) / 32 >= kCus ? 2 : 1; }
 
 constexpr int kResidentWaves = 2048;  // 256 CUs x 8 waves
 
-// Rows per wave iteration (R * NB KB of codes in flight per wave).  Measured
-// on MI355X at K = 7168 and 8192: 8 rows at every M (4 and 16 were slower; 16
-// rows at M >= 7 also halve the resident waves).
-constexpr int mxfp4_rows(int) { return 8; }
+// Rows per wave iteration (R * NB KB of codes in flight per wave): 8, and at
+// M = 1 4 where the 8-row groups would leave resident teams without one, so
+// that a short matrix still fills the GPU.  Measured on MI355X with full
+// occupancy (K = 7168 and 8192): 8 rows at every M (4 and 16 were slower;
+// 16 rows at M >= 7 also halve the resident waves).  The 4-row rule at M = 1
+// (interleaved A/B): 2048 x 7168 4.77 -> 3.99 us, 4096 x 7168 5.40 -> 5.13
+// us, 6144 x 7168 6.75 -> 6.65 us, 4096 x 4096 4.78 -> 3.98 us, 1024 x 1024
+// 3.30 -> 2.78 us; at M = 2 mixed (2048 x 7168 5.26 -> 4.61, 4096 x 7168
+// 5.97 -> 6.26 us), at M = 4, 8 slower (2048 x 7168 5.35 -> 5.69, 7.28 ->
+// 7.93 us).
+constexpr int kMxfp4Rows = 8;
+constexpr int kMxfp4RowsShort = 4;
 
-template <int M, int NB, int S>
-hipError_t launch_mns(int N, int KB, int chunk_b, const void* x, const void* Wq,
-                      const uint8_t* Ws, const Epilogue& ep, hipStream_t stream) {
-    constexpr int kRows = mxfp4_rows(M);
+template <int M, int NB, int S, int kRows>
+hipError_t launch_mnsr(int N, int KB, int chunk_b, const void* x, const void* Wq,
+                       const uint8_t* Ws, const Epilogue& ep, hipStream_t stream) {
     constexpr int kTeams = team_waves(S) / S;
     const int groups = (N + kRows - 1) / kRows;
     const int cap = kResidentWaves / S;
@@ -368,6 +375,17 @@ hipError_t launch_mns(int N, int KB, int chunk_b, const void* x, const void* Wq,
         static_cast<const uint4*>(x), static_cast<const uint4*>(Wq), Ws, N, KB, chunk_b, iters,
         ep);
     return hipGetLastError();
+}
+
+template <int M, int NB, int S>
+hipError_t launch_mns(int N, int KB, int chunk_b, const void* x, const void* Wq,
+                      const uint8_t* Ws, const Epilogue& ep, hipStream_t stream) {
+    if constexpr (M == 1) {
+        const int cap = kResidentWaves / S;  // resident teams
+        if ((N + kMxfp4Rows - 1) / kMxfp4Rows < cap)
+            return launch_mnsr<M, NB, S, kMxfp4RowsShort>(N, KB, chunk_b, x, Wq, Ws, ep, stream);
+    }
+    return launch_mnsr<M, NB, S, kMxfp4Rows>(N, KB, chunk_b, x, Wq, Ws, ep, stream);
 }
 
 template <int M, int NB>
