@@ -228,6 +228,7 @@ __global__ __launch_bounds__(kLpThreads) void lowp_chunk_kernel(
             } else {
                 uint32_t wd[NT][4];
                 float scale[NT][4];
+                uint32_t out_of_range = 0;  // a scale code of this lane outside [64, 190]
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     // lane (col, grp) holds dword t of block grp; after the
@@ -248,8 +249,46 @@ __global__ __launch_bounds__(kLpThreads) void lowp_chunk_kernel(
                     const auto g32 = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);
                     const uint32_t all = g32[0] | g32[1];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) scale[nt][t] = lp_e8m0((all >> (8 * t)) & 0xFFu);
+                    for (int t = 0; t < 4; ++t) {
+                        const uint32_t code = (all >> (8 * t)) & 0xFFu;
+                        scale[nt][t] = lp_e8m0(code);
+                        out_of_range |= code - 64u > 126u;
+                    }
                 }
+                // Every scale of the window in [64, 190] (the wave agrees): the
+                // codes convert exactly at their block's scale (any code in
+                // [2, 252] would: 0.5 * 2^(s-127) is a normal bf16 and
+                // 6 * 2^(s-127) below bf16's largest) and the steps accumulate
+                // on the matrix cores, with no fp32 scaling after each.  The
+                // narrower range keeps the weights, and so the products and
+                // partial sums the matrix cores form, 2^60 away from fp32's
+                // subnormal and overflow limits for any x of ordinary size.
+                // Otherwise each step's sum, formed at unit scale, is scaled by
+                // its block's 2^(s-127) before it is added (exact for every
+                // scale code).
+                const bool at_scale = __builtin_amdgcn_ballot_w64(out_of_range != 0) == 0;
+                if (at_scale) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        uint4 a[MT];
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) a[mt] = xw[(16 * mt + col) * pitch + 4 * t + grp];
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) {
+                            const float sc = scale[nt][t];
+                            const uint4 b = {
+                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], sc, 0)),
+                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], sc, 1)),
+                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], sc, 2)),
+                                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[nt][t], sc, 3))};
+#pragma unroll
+                            for (int mt = 0; mt < MT; ++mt)
+                                acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8_t, a[mt]), __builtin_bit_cast(bf16x8_t, b),
+                                    acc[nt][mt], 0, 0, 0);
+                        }
+                    }
+                } else {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     uint4 a[MT];
@@ -273,6 +312,7 @@ __global__ __launch_bounds__(kLpThreads) void lowp_chunk_kernel(
                                 acc[nt][mt][v] = __builtin_fmaf(blk[v], scale[nt][t], acc[nt][mt][v]);
                         }
                     }
+                }
                 }
             }
         }
@@ -380,7 +420,7 @@ hipError_t launch_lowp_chunk(int fmt, int M, int N, int K, const void* x, const 
     const Epilogue ep = p.S > 1 ? Epilogue{static_cast<float*>(ws), nullptr, nullptr, nullptr} : fin;
     const uint4* xp = static_cast<const uint4*>(x);
     const uint8_t* wp = static_cast<const uint8_t*>(Wq);
-    constexpr int kD8 = 4, kD4 = 8;  // windows in flight per wave
+    constexpr int kD8 = 4, kD4 = 2;  // windows in flight per wave
     // FP8 with one 16-row tile and one x row tile a wave and 7 or 8 windows a
     // wave (K = 7168 or 8192 over 8 splits): the whole chunk is one batch.
     // Interleaved A/B on MI355X: 4096 x 7168 M = 12 / 16 11.41 / 11.43 ->

@@ -110,7 +110,8 @@ def test_mxfp4_nan_scale_and_zero_codes(M, N):
 
 
 # Every scale code 0..254 is a valid OCP e8m0 scale (2^-127 .. 2^127).  The
-# kernels scale each block's fp32 sum, so the products stay exact down to
+# kernels scale each block's fp32 sum, formed at unit scale (the chunk kernel
+# for codes outside [64, 190]), so the products stay exact down to
 # code 0 (whose weights are below bf16's and fp32's normal range) and up to
 # code 254 (whose weights can exceed the largest bf16).
 @pytest.mark.parametrize("M,N", [(3, 40), (8, 40), (12, 40), (16, 40), (12, 8200), (16, 8192),
@@ -149,6 +150,32 @@ def test_mxfp4_scale_code_range(M, N):
     ref, A = orc().projection_mxfp4(bits(xs), np_u8(codes), np_u8(high))
     assert np.isfinite(ref).all() and np.abs(ref[:, 0]).max() > 2.0 ** 80
     check_f32(y32, ref, A, f"mxfp4 high scale codes M={M} N={N}")
+
+
+# The chunk kernel (from 12 rows) takes a window on the matrix cores at its
+# blocks' scales when every scale code of the window's rows lies in [64, 190],
+# else at unit scale with each block's sum scaled after: one wave switching
+# between the two inside its K range, and tiles at the range's two ends (the
+# other kernels, scaling every block's sum, run the same inputs).
+@pytest.mark.parametrize("M,N", [(3, 40), (12, 40), (16, 40), (12, 8200), (16, 8192), (24, 40),
+                                 (64, 8192)])
+def test_mxfp4_scale_window_mix(M, N):
+    announce(f"mxfp4 scale windows mixed M={M} N={N}")
+    K = 640
+    KB = K // 32
+    codes, scales = si.mxfp4_weights(N, K, 8480 + N, DEV)
+    assert int(scales.min()) >= 64 and int(scales.max()) <= 190
+    scales[1, 9] = 1                        # window 2 of the first tile at unit scale
+    scales[20, 0] = 200                     # the first and last windows of the second tile
+    scales[20, KB - 1] = 63
+    scales[32:40, :] = 64                   # the range's ends, every block
+    if N > 48:
+        scales[40:48, :] = 190
+    x = si.normal_bf16((M, K), 1.0, 8490 + M, DEV)
+    y32, _ = run(x, codes, scales, bf16=False)
+    ref, A = orc().projection_mxfp4(bits(x), np_u8(codes), np_u8(scales))
+    assert np.isfinite(ref).all()
+    check_f32(y32, ref, A, f"mxfp4 scale windows mixed M={M} N={N}")
 
 
 def test_mxfp4_empty_and_rejected():
