@@ -420,7 +420,12 @@ hipError_t launch_lowp_chunk(int fmt, int M, int N, int K, const void* x, const 
     const Epilogue ep = p.S > 1 ? Epilogue{static_cast<float*>(ws), nullptr, nullptr, nullptr} : fin;
     const uint4* xp = static_cast<const uint4*>(x);
     const uint8_t* wp = static_cast<const uint8_t*>(Wq);
-    constexpr int kD8 = 4, kD4 = 2;  // windows in flight per wave
+    // windows in flight per wave: FP8 up to 32 rows 2, from 33 rows 4; MXFP4 2.
+    // Interleaved A/B on MI355X, FP8 4 -> 2 windows: 8192 x 7168 M = 32
+    // 20.32 -> 19.76 us, 4096 x 7168 M = 32 12.61 -> 12.29 us, 2048 x 7168
+    // M = 24 14.84 -> 13.85 us; at M = 64 2 was slower (4096 x 7168 14.84 ->
+    // 15.13 us, 8192 x 7168 25.33 -> 25.71 us).
+    constexpr int kD8 = 2, kD8Wide = 4, kD4 = 2;
     // FP8 with one 16-row tile and one x row tile a wave and 7 or 8 windows a
     // wave (K = 7168 or 8192 over 8 splits): the whole chunk is one batch.
     // Interleaved A/B on MI355X: 4096 x 7168 M = 12 / 16 11.41 / 11.43 ->
@@ -445,9 +450,9 @@ hipError_t launch_lowp_chunk(int fmt, int M, int N, int K, const void* x, const 
     }
     SG_LP(kLowpFp8, 1, 1, 8, true)
     SG_LP(kLowpFp8, 1, 1, kD8, false) SG_LP(kLowpFp8, 2, 1, kD8, false)
-    SG_LP(kLowpFp8, 3, 1, kD8, false) SG_LP(kLowpFp8, 4, 1, kD8, false)
+    SG_LP(kLowpFp8, 3, 1, kD8Wide, false) SG_LP(kLowpFp8, 4, 1, kD8Wide, false)
     SG_LP(kLowpFp8, 1, 2, kD8, false) SG_LP(kLowpFp8, 2, 2, kD8, false)
-    SG_LP(kLowpFp8, 3, 2, kD8, false) SG_LP(kLowpFp8, 4, 2, kD8, false)
+    SG_LP(kLowpFp8, 3, 2, kD8Wide, false) SG_LP(kLowpFp8, 4, 2, kD8Wide, false)
     SG_LP(kLowpMxfp4, 1, 1, kD4, false) SG_LP(kLowpMxfp4, 2, 1, kD4, false)
     SG_LP(kLowpMxfp4, 3, 1, kD4, false) SG_LP(kLowpMxfp4, 4, 1, kD4, false)
     SG_LP(kLowpMxfp4, 1, 2, kD4, false) SG_LP(kLowpMxfp4, 2, 2, kD4, false)
