@@ -211,8 +211,12 @@ __global__ __launch_bounds__(kWave * team_waves(S)) void mxfp4_rowdot_kernel(
 // Matrix-core kernel: one workgroup of S waves per NT 16-row tiles of W;
 // wave s takes windows [s*chunk_w, (s+1)*chunk_w) of 128 elements (4
 // blocks), D of them in flight at a time.  With NT = 2 each x operand read
-// serves two row tiles, halving the x bytes per code byte.
-constexpr int kMfmaWindows = 8;
+// serves two row tiles, halving the x bytes per code byte.  Two windows in
+// flight: interleaved A/B on MI355X against 8 (and 4), K = 7168: N = 4096
+// M = 9 / 12 / 16 11.44 / 11.98 / 12.65 -> 11.18 / 11.55 / 12.07 us (4:
+// 11.44 / 11.88 / 12.41), N = 2048 M = 16 12.02 -> 11.41 us, N = 5888
+// M = 12 21.51 -> 19.27 us (4: 18.89).
+constexpr int kMfmaWindows = 2;
 
 template <int NT, int S>
 __global__ __launch_bounds__(kWave * S) void mxfp4_mfma_kernel(
