@@ -509,7 +509,9 @@ hipError_t launch_mfma_team(int M, int N, int K, int S, int k_chunk, const void*
     const uint4* wp = static_cast<const uint4*>(W);
     const int MT = (M + 15) / 16;
     // rounds in flight per wave; measured on MI355X, 3 or 4 were slower (K=7168,
-    // N=4096, M=8: 12.4 us at 2, 14.4 at 3, 15.0 at 4, in the loop form)
+    // N=4096, M=8: 12.4 us at 2, 14.4 at 3, 15.0 at 4, in the loop form), and
+    // so was 1 (8192x7168 M = 8 19.17 -> 20.45 us, 7168x8192 M = 12 21.23 ->
+    // 22.68 us)
     constexpr int DR = 2;
     // Up to 8 rounds a wave (K <= 8192 over 8 waves): every round unrolled.
     // Measured on MI355X (interleaved A/B against the loop): 4096x7168 M = 8
@@ -592,7 +594,8 @@ hipError_t launch_splitk_mfma(int M, int N, int K, int S, int k_chunk, int tile_
     if (phase == 0 || lds > kMfmaMaxLds) return hipErrorInvalidValue;
     // weight rounds in flight per wave (8 loads); 3 or 4 measured slower on
     // MI355X (K=7168, N=4096, M=64: 18.5 us at 2, 18.8 at 3, 19.6 at 4; with
-    // every round unrolled 17.0 / 17.0 / 18.4 us)
+    // every round unrolled 17.0 / 17.0 / 18.4 us), and 1 too (M = 20 / 64
+    // 14.07 / 17.06 -> 15.09 / 18.17 us)
     constexpr int DR = 2;
     const int whole = (chunk8 + 16 / NT - 1) / (16 / NT) * (16 / NT);
     const bool phased = phase < whole;
