@@ -389,16 +389,27 @@ bool lowp_chunk_plan(int M, int N, int K, LowpChunkPlan* p) {
     const int NT = lowp_nt(N);
     const int tiles = mfma_grid_tiles(N, 128 * NT);
     const int windows = (K + kLpWindow - 1) / kLpWindow;
-    // the smallest split whose grid fills the compute units and whose x chunk
-    // fits in LDS (and the staging registers); else the largest that fits
+    // The split whose busiest compute unit has the least to stream: ceil(grid
+    // / 256) workgroups of ceil(windows / S) windows each; a tie goes to the
+    // smaller split (fewer partials).  Only splits whose x chunk fits in LDS
+    // (and the staging registers) and that leave no chunk empty.  The first
+    // split to reach 256 workgroups, taken before, overshot to 264-304 where
+    // the tiles do not divide 256, and the compute units holding two
+    // workgroups set the time (FP8, K = 7168, M = 16: N = 3072 14.1 us at
+    // S = 12 against 10.4 at S = 8; N = 6144 22.1 against 17.3 us).
     int best = 0;
+    int64_t best_cost = INT64_MAX;
     for (int S = 1; S <= 64 && S <= windows; ++S) {
-        const int chunk = kLpWindow * ((windows + S - 1) / S);
+        const int wpw = (windows + S - 1) / S;
+        const int chunk = kLpWindow * wpw;
         if ((int64_t)(S - 1) * chunk >= K) continue;  // an empty chunk
         const size_t lds = ((size_t)XR * (chunk / kPiece + 1) + kLpPadSlots) * 16;
         if (lds > kLpLdsMax || XR * (chunk / kPiece) > kLpXLoads * kLpThreads) continue;
-        best = S;
-        if (tiles * S >= kLpCus) break;
+        const int64_t cost = ((int64_t)tiles * S + kLpCus - 1) / kLpCus * wpw;
+        if (cost < best_cost) {
+            best = S;
+            best_cost = cost;
+        }
     }
     if (best == 0) return false;
     const int chunk = kLpWindow * ((windows + best - 1) / best);
