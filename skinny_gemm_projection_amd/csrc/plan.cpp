@@ -52,6 +52,16 @@ constexpr int32_t kTeamUpToM = 16;
 // 12.9 us, M = 5 12.3 against 11.9 us), and at short K the streaming kernel
 // stays ahead up to 5 rows (4096x2048: M = 3 / 5 5.19 / 5.76 against 5.98 /
 // 6.01 us).
+// The team kernel's grid of N/16 workgroups counts as filling the GPU from
+// 160 workgroups (N >= 2545), five eighths of the compute units.  Interleaved
+// A/B on MI355X, team against the plan of a 256-workgroup threshold (vector
+// ALU below 8 rows, chunk kernel from 8), K = 7168: N = 2560 M = 3 / 8 / 16
+// 9.72 / 11.02 / 11.00 -> 8.96 / 9.64 / 10.93 us, N = 3072 M = 4 / 8 10.26 /
+// 11.28 -> 9.54 / 10.00 us (M = 16 11.26 against 11.42), N = 3584 M = 6 / 8 /
+// 16 12.14 / 12.96 / 12.93 -> 10.19 / 10.42 / 11.78 us; 3072 x 4096 M = 8
+// 8.38 -> 6.74 us.  At N = 2048 (128 workgroups) the other plans stay ahead
+// (M = 3 / 16 7.56 / 9.04 against 8.59 / 10.50 us).
+constexpr int32_t kTeamMinTiles = 160;
 constexpr int32_t kTeamFromM = 3;
 constexpr int32_t kTeamFromMOtherK = 6;
 constexpr int32_t kTeamFromMMinK = 4096;
@@ -303,7 +313,7 @@ sg_status make_plan_impl(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_
     }
 
     if (kernel <= 0) {
-        const bool team_fills = (N + kMfmaTeamTileN - 1) / kMfmaTeamTileN >= kComputeUnits;
+        const bool team_fills = (N + kMfmaTeamTileN - 1) / kMfmaTeamTileN >= kTeamMinTiles;
         const bool team_k = K >= kTeamFromMMinK && K <= kTeamFromMMaxK;
         const int32_t mfma_from =
             team_fills ? (team_k ? kTeamFromM : kTeamFromMOtherK) : kMfmaFromM;
@@ -346,7 +356,7 @@ sg_status make_plan_impl(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_
             // reduced inside the workgroup).
             // Up to 16 rows (one x row tile) the team kernel -- no
             // workspace, no second launch -- when its grid of N/16
-            // workgroups fills the compute units.  Measured on MI355X with
+            // workgroups fills the compute units (kTeamMinTiles).  Measured on MI355X with
             // x through the per-wave LDS tile: K=7168, N=4096, M=16 13.5 us
             // against 14.3 us for the chunk kernel and its reduction; from
             // M=20 (two row tiles) the chunk kernel wins (16.6 against 15.4).
@@ -359,7 +369,7 @@ sg_status make_plan_impl(int32_t M, int32_t N, int32_t K, int32_t kernel, int32_
             // / 24.1 us.)
             const int32_t team_tiles = (N + kMfmaTeamTileN - 1) / kMfmaTeamTileN;
             const bool team_auto = two_pass < 0 && tile_n == 0 && M <= kTeamUpToM &&
-                                   team_tiles >= kComputeUnits &&
+                                   team_tiles >= kTeamMinTiles &&
                                    (split_k <= 0 || mfma_team_split_ok(split_k));
             const bool team_asked = two_pass == 0 || tile_n == kMfmaTeamTileN || team_auto;
             int32_t S = 0, t = 0;

@@ -74,10 +74,12 @@ SMALL = [
     (48, 1000, 1056), (63, 200, 264), (64, 1000, 1056),
     # wide matrices: the team kernel with two 16-row tiles a wave (ragged last pair)
     (9, 8161, 520), (12, 8200, 1040), (16, 8177, 264), (13, 9000, 2056),
-    # ... with every round unrolled (K <= 8192), from 3 rows where N/16 >= 256
+    # ... with every round unrolled (K <= 8192), from 3 rows where N/16 >= 160
     (7, 8300, 8192), (8, 8161, 7168), (3, 4097, 2056), (5, 4200, 6152), (4, 6000, 8192),
-    # the streaming vector-ALU kernel with teams (N/16 < 256): M = 3, 4, 2 to 8 rows a team
-    (3, 2101, 4104), (4, 4000, 4104), (4, 3500, 8192), (4, 3000, 7168),
+    # the streaming vector-ALU kernel with teams (N/16 < 160): M = 3, 4, 2 to 8 rows a team
+    (3, 2101, 4104), (4, 2400, 4104), (4, 2200, 8192), (4, 2544, 7168),
+    # the team kernel from 160 workgroups (N/16 >= 160)
+    (4, 4000, 4104), (4, 3500, 8192), (4, 3000, 7168), (8, 2560, 7168), (16, 3584, 7168),
     # the chunk kernel with every round unrolled (one x phase), short last chunks:
     # 5 and 8 rounds of 128-row tiles, 16 rounds of 256-row tiles
     (20, 1000, 7000), (24, 4500, 6984), (48, 700, 8192), (40, 9000, 7000),
