@@ -389,9 +389,11 @@ bool lowp_chunk_plan(int M, int N, int K, LowpChunkPlan* p) {
     const int NT = lowp_nt(N);
     const int tiles = mfma_grid_tiles(N, 128 * NT);
     const int windows = (K + kLpWindow - 1) / kLpWindow;
-    // The split whose busiest compute unit has the least to stream: ceil(grid
-    // / 256) workgroups of ceil(windows / S) windows each; a tie goes to the
-    // smaller split (fewer partials).  Only splits whose x chunk fits in LDS
+    // The split whose busiest compute unit has the least to do: ceil(grid /
+    // 256) workgroups of ceil(windows / S) windows each, plus one window's
+    // worth a workgroup for staging x and writing its partials (without it,
+    // N = 5888 took S = 56, one window a workgroup: MXFP4 M = 16 37.8 us);
+    // a tie goes to the smaller split (fewer partials).  Only splits whose x chunk fits in LDS
     // (and the staging registers) and that leave no chunk empty.  The first
     // split to reach 256 workgroups, taken before, overshot to 264-304 where
     // the tiles do not divide 256, and the compute units holding two
@@ -405,7 +407,7 @@ bool lowp_chunk_plan(int M, int N, int K, LowpChunkPlan* p) {
         if ((int64_t)(S - 1) * chunk >= K) continue;  // an empty chunk
         const size_t lds = ((size_t)XR * (chunk / kPiece + 1) + kLpPadSlots) * 16;
         if (lds > kLpLdsMax || XR * (chunk / kPiece) > kLpXLoads * kLpThreads) continue;
-        const int64_t cost = ((int64_t)tiles * S + kLpCus - 1) / kLpCus * wpw;
+        const int64_t cost = ((int64_t)tiles * S + kLpCus - 1) / kLpCus * (wpw + 1);
         if (cost < best_cost) {
             best = S;
             best_cost = cost;
