@@ -335,9 +335,11 @@ sg_status skinny_gemm_fp8(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
     if (M < 0 || N < 0 || N > (1 << 20) || K < 0 || K > (1 << 20)) return SG_ERR_SHAPE;
     if (K % 16 != 0) return SG_ERR_ALIGN;
     if (M > sg::kLowpMaxM) return SG_ERR_UNSUPPORTED;
-    const bool chunk = sg::lowp_use_chunk(sg::kLowpFp8, M, N);
-    if (M > 0 && !chunk && !sg::fp8_size_ok(M, K)) return SG_ERR_UNSUPPORTED;
+    bool chunk = sg::lowp_use_chunk(sg::kLowpFp8, M, N);
     sg::LowpChunkPlan lp;
+    // below 12 rows a K whose chunks do not fit in LDS goes to the matrix-core kernel
+    if (chunk && M < 12 && N > 0 && !sg::lowp_chunk_plan(M, N, K, &lp)) chunk = false;
+    if (M > 0 && !chunk && !sg::fp8_size_ok(M, K)) return SG_ERR_UNSUPPORTED;
     if (chunk && N > 0 && !sg::lowp_chunk_plan(M, N, K, &lp)) return SG_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return SG_OK;
     if (!y_f32 && !y_bf16) return SG_ERR_NULL;

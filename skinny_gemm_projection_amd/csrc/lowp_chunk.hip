@@ -371,9 +371,22 @@ int lowp_nt(int N) { return ((N + 255) / 256) * 8 >= 3 * kLpCus / 4 ? 2 : 1; }
 // wave takes two tiles, the MXFP4 one (N = 8192, M = 16: 19.5 -> 18.0 us); at
 // N = 4096 the one-launch MXFP4 kernels stay ahead up to 16 rows (M = 12:
 // 12.0 against 12.9 us).
+// FP8 from 8 rows too, except where the FP8 matrix-core kernel takes two
+// 16-row tiles a wave over a whole multiple of 256 workgroups (N = 8192):
+// there it stays ahead to 11 rows (8192 x 7168 M = 8 16.99 against 17.86
+// us); elsewhere the chunk kernel was ahead or level at 8 and 11 rows
+// (K = 7168: N = 2048 M = 8 10.39 -> 9.37 us, N = 6144 17.82 -> 15.69 us,
+// N = 4096 M = 11 11.46 -> 10.75 us, N = 18432 M = 11 41.96 -> 34.72 us,
+// N = 3072 M = 8 10.65 / 10.58 us).
 bool lowp_use_chunk(int fmt, int M, int N) {
-    if (M > kLowpMaxM || M < 12) return false;
-    if (M >= 17 || fmt == kLowpFp8) return true;
+    if (M > kLowpMaxM || M < 8) return false;
+    if (fmt == kLowpFp8) {
+        if (M >= 12) return true;
+        const bool two_tiles = (N + 31) / 32 >= kLpCus;  // the matrix-core kernel's rule
+        return !(two_tiles && ((N + 31) / 32) % kLpCus == 0);
+    }
+    if (M < 12) return false;
+    if (M >= 17) return true;
     return lowp_nt(N) == 2;
 }
 

@@ -1,6 +1,6 @@
 """GPU parity of the projection with FP8 weights (skinny_gemm_fp8: e4m3 codes, one fp32
 scale per 128 x 128 block) through the C ABI, M = 1..64 (vector ALU, matrix cores, and
-from 12 rows the chunk kernel with its split-K reduction), against oracle_projection_fp8
+from 8 or 12 rows the chunk kernel with its split-K reduction), against oracle_projection_fp8
 on the same seeded codes and scales: fp32 |got - ref| <= 1e-3 * A, bf16 adds 2^-8 |ref|, the
 residual adds 2^-23 |r + y|.  Integer-valued activations and weights with power-of-two
 scales are bit-exact (every product and partial sum is exact in fp32)."""
@@ -47,7 +47,10 @@ SHAPES = [(1, 40, 16), (1, 129, 112), (1, 200, 1040), (1, 77, 8192), (1, 33, 820
           (9, 129, 2064), (11, 300, 7168), (10, 40, 20000), (11, 1, 144), (11, 200, 30000),
           # from 8161 rows two 16-row tiles per wave (ragged last 32-row tile)
           (9, 8200, 144), (11, 8192, 1040), (5, 8177, 2064),
-          # from 12 rows the chunk kernel: x rows padded to 16, 32, 48, 64; ragged
+          # 8 to 11 rows with a K whose chunks do not fit in LDS: the matrix-core kernel
+          (9, 5, 524288),
+          # the chunk kernel (from 8 rows, from 12 where N/32 is a whole multiple of
+          # 256): x rows padded to 16, 32, 48, 64; ragged
           # 128-row tiles and windows; one split (K = 16), several, 256-row tiles
           (12, 300, 7168), (16, 40, 20000), (16, 1, 144), (13, 200, 30000),
           (16, 8192, 1040), (14, 8177, 2064),
