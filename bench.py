@@ -171,9 +171,12 @@ class Launcher:
 
 
 def lowp_plan_label(fmt: str, M: int, N: int, wsb: int) -> str:
-    """Kernel an FP8 / MXFP4 call runs, as the library routes it (the chunk kernel
-    from 12 rows for FP8; for MXFP4 from 17 rows, or 12 when N > 5888)."""
-    chunk = M >= 17 or (M >= 12 and (fmt == "fp8" or N > 5888))
+    """Kernel an FP8 / MXFP4 call runs, as the library routes it (the chunk kernel for
+    FP8 from 8 rows, from 12 where N/32 is a whole multiple of 256, K short enough for
+    its LDS; for MXFP4 from 17 rows, or 12 when N > 5888)."""
+    tiles32 = (N + 31) // 32
+    fp8_from = 12 if tiles32 >= 256 and tiles32 % 256 == 0 else 8
+    chunk = M >= 17 or (M >= 12 and N > 5888) or (fmt == "fp8" and M >= fp8_from)
     if chunk:
         return "lowp_chunk + reduce" if wsb else "lowp_chunk"
     if fmt == "fp8":

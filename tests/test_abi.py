@@ -347,9 +347,13 @@ def test_fp8_size_limits_return_before_launch():
 
 def test_lowp_workspace_sizes():
     # fp32 partials [S, N, 16 * ceil(M / 16)] of the low-precision chunk kernel: FP8 from
-    # 12 rows, MXFP4 from 17 rows and from 12 where a wave takes two tiles (N > 5888)
+    # 8 rows (from 12 where N/32 is a whole multiple of 256, and below 12 rows only while
+    # its x chunk fits in LDS), MXFP4 from 17 rows and from 12 where a wave takes two
+    # tiles (N > 5888)
     fp8, mx = sg.skinny_gemm_fp8_workspace, sg.skinny_gemm_mxfp4_workspace
-    assert fp8(11, 4096, 7168) == 0 and fp8(12, 4096, 7168) > 0
+    assert fp8(7, 4096, 7168) == 0 and fp8(8, 4096, 7168) > 0 and fp8(11, 4096, 7168) > 0
+    assert fp8(11, 8192, 7168) == 0 and fp8(12, 8192, 7168) > 0 and fp8(8, 8200, 7168) > 0
+    assert fp8(9, 5, 1 << 19) == 0  # the matrix-core kernel: no workspace
     assert mx(16, 5888, 7168) == 0 and mx(12, 5889, 7168) > 0 and mx(17, 4096, 7168) > 0
     assert mx(11, 8192, 7168) == 0
     for f in (fp8, mx):
