@@ -173,10 +173,14 @@ class Launcher:
 def lowp_plan_label(fmt: str, M: int, N: int, wsb: int) -> str:
     """Kernel an FP8 / MXFP4 call runs, as the library routes it (the chunk kernel for
     FP8 from 8 rows, from 12 where N/32 is a whole multiple of 256, K short enough for
-    its LDS; for MXFP4 from 17 rows, or 12 when N > 5888)."""
+    its LDS; for MXFP4 from 17 rows, 12 when N > 5888, 9 where its matrix-core grid is
+    not a whole multiple of 256)."""
     tiles32 = (N + 31) // 32
+    tiles = tiles32 if tiles32 >= 256 else (N + 15) // 16
     fp8_from = 12 if tiles32 >= 256 and tiles32 % 256 == 0 else 8
-    chunk = M >= 17 or (M >= 12 and N > 5888) or (fmt == "fp8" and M >= fp8_from)
+    mx_from = 9 if tiles % 256 else 17
+    chunk = M >= 17 or (M >= 12 and N > 5888) or (fmt == "fp8" and M >= fp8_from) or \
+        (fmt == "mxfp4" and M >= mx_from)
     if chunk:
         return "lowp_chunk + reduce" if wsb else "lowp_chunk"
     if fmt == "fp8":

@@ -301,10 +301,12 @@ sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
     if (M < 0 || N < 0 || N > (1 << 20) || K < 0 || K > (1 << 20)) return SG_ERR_SHAPE;
     if (M > sg::kLowpMaxM) return SG_ERR_UNSUPPORTED;
     if (K % 32 != 0) return SG_ERR_ALIGN;
-    const bool chunk = sg::lowp_use_chunk(sg::kLowpMxfp4, M, N);
+    bool chunk = sg::lowp_use_chunk(sg::kLowpMxfp4, M, N);
+    sg::LowpChunkPlan lp;
+    // up to 16 rows a K whose chunks do not fit in LDS goes to the matrix-core kernel
+    if (chunk && M <= sg::kMxfp4MaxM && N > 0 && !sg::lowp_chunk_plan(M, N, K, &lp)) chunk = false;
     int nb, splits;
     if (M > 0 && !chunk && !sg::mxfp4_split(M, K, &nb, &splits)) return SG_ERR_UNSUPPORTED;
-    sg::LowpChunkPlan lp;
     if (chunk && N > 0 && !sg::lowp_chunk_plan(M, N, K, &lp)) return SG_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return SG_OK;
     if (!y_f32 && !y_bf16) return SG_ERR_NULL;
@@ -337,8 +339,8 @@ sg_status skinny_gemm_fp8(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
     if (M > sg::kLowpMaxM) return SG_ERR_UNSUPPORTED;
     bool chunk = sg::lowp_use_chunk(sg::kLowpFp8, M, N);
     sg::LowpChunkPlan lp;
-    // below 12 rows a K whose chunks do not fit in LDS goes to the matrix-core kernel
-    if (chunk && M < 12 && N > 0 && !sg::lowp_chunk_plan(M, N, K, &lp)) chunk = false;
+    // up to 16 rows a K whose chunks do not fit in LDS goes to the matrix-core kernel
+    if (chunk && M <= sg::kFp8MaxM && N > 0 && !sg::lowp_chunk_plan(M, N, K, &lp)) chunk = false;
     if (M > 0 && !chunk && !sg::fp8_size_ok(M, K)) return SG_ERR_UNSUPPORTED;
     if (chunk && N > 0 && !sg::lowp_chunk_plan(M, N, K, &lp)) return SG_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return SG_OK;

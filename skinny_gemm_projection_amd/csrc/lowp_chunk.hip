@@ -385,9 +385,17 @@ bool lowp_use_chunk(int fmt, int M, int N) {
         const bool two_tiles = (N + 31) / 32 >= kLpCus;  // the matrix-core kernel's rule
         return !(two_tiles && ((N + 31) / 32) % kLpCus == 0);
     }
-    if (M < 12) return false;
-    if (M >= 17) return true;
-    return lowp_nt(N) == 2;
+    // MXFP4 from 17 rows, from 12 where a wave takes two tiles, and from 9
+    // where the MXFP4 matrix-core kernel's grid of 16- or 32-row tiles is not
+    // a whole multiple of 256 workgroups.  Interleaved A/B, K = 7168 unless
+    // noted, against the matrix-core kernel: N = 5888 M = 9 / 16 18.51 /
+    // 20.50 -> 15.25 / 15.34 us, N = 12288 M = 9 28.97 -> 24.31 us, 7168 x
+    // 8192 M = 9 20.07 -> 18.57 us, N = 2048 M = 16 11.42 -> 10.02 us; the
+    // one loss N = 3072 M = 9 10.86 -> 11.25 us.
+    if (M >= 17 || (M >= 12 && lowp_nt(N) == 2)) return true;
+    const int t16 = (N + 15) / 16, t32 = (N + 31) / 32;
+    const int tiles = t32 >= kLpCus ? t32 : t16;  // the matrix-core kernel's rule
+    return M >= 9 && tiles % kLpCus != 0;
 }
 
 bool lowp_chunk_plan(int M, int N, int K, LowpChunkPlan* p) {

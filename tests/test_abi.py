@@ -328,7 +328,8 @@ def test_fp8_size_limits_return_before_launch():
 
     assert call(65, 64) == 3                              # above the decode path
     assert call(12, 64) == 1 and call(64, 65536) == 1     # chunk kernel from 12 rows
-    assert call(64, 1 << 20) == 3 and call(12, 1 << 20) == 3  # x chunk would not fit in LDS
+    assert call(64, 1 << 20) == 3 and call(17, 1 << 20) == 3  # x chunk would not fit in LDS
+    assert call(12, 1 << 20) == 1  # up to 16 rows the matrix-core kernel takes that K
     assert call(17, 7168, y=A, N=4096) == 5               # its split-K workspace is missing
     assert call(12, 7168, y=A, N=4096) == 5
     need = sg.skinny_gemm_fp8_workspace(17, 4096, 7168)
@@ -348,14 +349,14 @@ def test_fp8_size_limits_return_before_launch():
 def test_lowp_workspace_sizes():
     # fp32 partials [S, N, 16 * ceil(M / 16)] of the low-precision chunk kernel: FP8 from
     # 8 rows (from 12 where N/32 is a whole multiple of 256, and below 12 rows only while
-    # its x chunk fits in LDS), MXFP4 from 17 rows and from 12 where a wave takes two
-    # tiles (N > 5888)
+    # its x chunk fits in LDS), MXFP4 from 17 rows, from 12 where a wave takes two
+    # tiles (N > 5888) and from 9 where its matrix-core grid is not a multiple of 256
     fp8, mx = sg.skinny_gemm_fp8_workspace, sg.skinny_gemm_mxfp4_workspace
     assert fp8(7, 4096, 7168) == 0 and fp8(8, 4096, 7168) > 0 and fp8(11, 4096, 7168) > 0
     assert fp8(11, 8192, 7168) == 0 and fp8(12, 8192, 7168) > 0 and fp8(8, 8200, 7168) > 0
     assert fp8(9, 5, 1 << 19) == 0  # the matrix-core kernel: no workspace
-    assert mx(16, 5888, 7168) == 0 and mx(12, 5889, 7168) > 0 and mx(17, 4096, 7168) > 0
-    assert mx(11, 8192, 7168) == 0
+    assert mx(16, 4096, 7168) == 0 and mx(12, 5889, 7168) > 0 and mx(17, 4096, 7168) > 0
+    assert mx(11, 8192, 7168) == 0 and mx(8, 5888, 7168) == 0 and mx(9, 5888, 7168) > 0
     for f in (fp8, mx):
         assert f(65, 4096, 7168) == 0
         assert f(17, 0, 7168) == 0
