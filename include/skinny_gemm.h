@@ -235,8 +235,11 @@ sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int
  *   + y), r may alias y_bf16) or of skinny_gemm otherwise.  The weight stream
  *   is a quarter of bf16's plus 1/16 for the scales.  M <= 8 runs on the
  *   vector ALU and 9 <= M <= 16 on bf16 matrix cores (one launch, the
- *   workspace is not used), except 12 <= M <= 16 where N > 5888; there and
- *   for 17 <= M <= 64 the matrix-core chunk kernel runs (x staged once per
+ *   workspace is not used) where its grid of 16-row tiles (32-row from N =
+ *   8161) is a whole multiple of 256 workgroups, and for 9 <= M <= 11 also
+ *   where N > 5888; elsewhere from 9 rows, and for 17 <= M <= 64, the
+ *   matrix-core chunk kernel runs (up to 16 rows only while its x chunk fits
+ *   in LDS; a longer K takes the one-launch kernel) (x staged once per
  *   128 or 256 weight rows, K split between workgroups) and, when it splits
  *   K, the deterministic reduction: the fp32 partials need
  *   skinny_gemm_mxfp4_workspace(M, N, K) bytes of workspace (16-byte
@@ -244,7 +247,7 @@ sg_status skinny_gemm_router_topk(const float* scores, int32_t T, int32_t E, int
  * Batch 1 to 64 is the decode path of [P] Method details.
  * Limits: 0 <= M <= 64 (M > 64: SG_ERR_UNSUPPORTED), 0 <= N <= 1<<20,
  * 0 <= K <= 1<<20 (else SG_ERR_SHAPE), K % 32 == 0 (SG_ERR_ALIGN); K <=
- * 32768 at M <= 2 and 16384 for 3 <= M <= 8, and on the chunk kernel a
+ * 32768 at M <= 2 and 16384 for 3 <= M <= 8, and from 17 rows a
  * split whose x chunk fits in LDS (any K up to 65536) (else
  * SG_ERR_UNSUPPORTED); a short
  * workspace: SG_ERR_WORKSPACE.  x, W_codes, r, outputs and the workspace
@@ -265,13 +268,16 @@ sg_status skinny_gemm_mxfp4(int32_t M, int32_t N, int32_t K, const sg_bf16* x,
  * [M, N] (at least one); r (nullable) bf16 [M, N] gives the fused residual
  * y = r + x W^T as for skinny_gemm_residual (y_bf16 may equal r).  A NaN
  * code or scale makes its outputs NaN.  M <= 4 runs on the vector ALU,
- * 5 <= M <= 11 on bf16 matrix cores (codes converted exactly to bf16, each
- * 128-column window's sum scaled once; one launch, no workspace), 12 <= M
- * <= 64 on the matrix-core chunk kernel with the workspace and reduction of
- * skinny_gemm_mxfp4 (skinny_gemm_fp8_workspace bytes).  Limits: 0 <= M <=
- * 64, K % 16 == 0 (else SG_ERR_ALIGN), M * K <= 32768 at M <= 2 (x staged in
- * LDS) and K <= 16384 at M = 3, 4 (x in registers), any K for 5 <= M <= 11,
- * and from 12 rows a split whose x chunk fits in LDS (any K up to 65536)
+ * 5 <= M <= 7 on bf16 matrix cores (codes converted exactly to bf16, each
+ * 128-column window's sum scaled once; one launch, no workspace), also 8 <=
+ * M <= 11 where N/32 is a whole multiple of 256 (N = 8192); otherwise from 8
+ * rows the matrix-core chunk kernel with the workspace and reduction of
+ * skinny_gemm_mxfp4 (skinny_gemm_fp8_workspace bytes), up to 16 rows only
+ * while its x chunk fits in LDS (a longer K takes the one-launch kernel).
+ * Limits: 0 <= M <= 64, K % 16 == 0 (else SG_ERR_ALIGN), M * K <= 32768 at
+ * M <= 2 (x staged in LDS) and K <= 16384 at M = 3, 4 (x in registers), any
+ * K for 5 <= M <= 16, and from 17 rows a split whose x chunk fits in LDS
+ * (any K up to 65536)
  * (else SG_ERR_UNSUPPORTED), N, K <= 1<<20; a short workspace:
  * SG_ERR_WORKSPACE.  x, W_codes, r, outputs and the workspace 16-byte
  * aligned, W_scales 4-byte aligned.  Allocates nothing. */
